@@ -1,0 +1,280 @@
+#!/usr/bin/env python3
+"""Monarch forward+backward throughput on one MI355X.
+
+One step = monarch_fwd + monarch_bwd (the whole hot path) over one batch of
+synthetic inputs already resident in HBM. Prints one JSON line with the
+throughput (Monarch algorithmic TFLOP/s = 6*batch*params per step), the
+roofline of the dominant kernel (timed with HIP events recorded between the
+library's kernels on the launch stream, over the timed region), the dense
+bf16 GEMM of the same shape and the fp64 CPU oracle timed on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import glob
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA, published
+
+DEFAULT_WORKLOAD = "square_n16384_b128"
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def csrc_digest() -> str:
+    h = hashlib.sha256()
+    for p in sorted(glob.glob(os.path.join(ROOT, "monarch_block_diagonal_amd", "csrc", "*"))):
+        with open(p, "rb") as f:
+            h.update(os.path.basename(p).encode())
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def kernel_bytes(name: str, pr: dict) -> float:
+    """Algorithmic HBM bytes of one launch: each tensor the kernel's role needs
+    read once and each result written once (weights and weight gradients at
+    the I/O width; partial sums are not counted)."""
+    e, B = pr["e"], pr["batch"]
+    inp, mid, out = pr["in"], pr["mid"], pr["out"]
+    p1, p2 = pr["params1"], pr["params2"]
+    relu = pr["act"] == 1
+    table = {
+        "stage1_fwd": e * B * (inp + mid) + e * p1,
+        "stage2_fwd": e * B * (mid + out) + e * p2,
+        "stage2_bwd_data": e * B * (out * (2 if relu else 1) + mid) + e * p2,
+        "stage2_bwd_weight": e * B * (out * (2 if relu else 1) + mid) + e * p2,
+        "stage2_bwd": e * B * (out * (2 if relu else 1) + 2 * mid) + 2 * e * p2,
+        "stage1_bwd_data": e * B * (mid + inp) + e * p1,
+        "stage1_bwd_weight": e * B * (mid + inp) + e * p1,
+        "stage1_bwd": e * B * (mid + 2 * inp) + 2 * e * p1,
+        "reduce_dw2": e * p2,
+        "reduce_dw1": e * p1,
+    }
+    for key in sorted(table, key=len, reverse=True):
+        if name.endswith(key):
+            return float(table[key])
+    return 0.0
+
+
+def load_traffic(kernel: str, workload: str, digest: str):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, or None
+    when absent or taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    for line in open(path):
+        if ":" in line and not line.startswith("#"):
+            k, v = line.split(":", 1)
+            kv[k.strip()] = v.strip()
+    if kv.get("csrc_sha256") != digest:
+        return None
+    try:
+        return float(kv["hbm_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def cpu_baseline(w, rows: int):
+    """The fp64 oracle as it stands, on `rows` rows of the same workload."""
+    import numpy as np
+    import oracle as O
+    from monarch_block_diagonal_amd import synthetic as S
+    layer = w.layers[0]
+    d = S.make_layer_inputs(w, batch=rows)
+    fi, fo = layer.in_features, layer.out_features
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    t0 = time.perf_counter()
+    y = O.forward(d["x"], d["w1"], d["w2"], fi, fo)
+    dx, dw1, dw2 = O.backward(d["dy"], d["x"], d["w1"], d["w2"], fi, fo)
+    dt = time.perf_counter() - t0
+    flops = 6.0 * rows * w.params
+    assert np.isfinite(y).all() and np.isfinite(dx).all()
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{rows} of {w.batch} rows of {w.name}: fp64 forward+backward through "
+                      f"dense factor matrices (built in the timed call), {dt:.2f} s",
+            "seconds": dt}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=DEFAULT_WORKLOAD)
+    ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0: auto)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on one GPU only: the Monarch path here has no multi-GPU "
+              "(sharded) implementation, so --gpus must be 1.", file=sys.stderr)
+        return 2
+
+    import torch
+    import monarch_block_diagonal_amd as M
+    from monarch_block_diagonal_amd import synthetic as S
+
+    w = S.WORKLOADS[args.workload]
+    if len(w.layers) != 1:
+        print("bench.py times single-layer workloads", file=sys.stderr)
+        return 2
+    layer = w.layers[0]
+    fi, fo, nb1, nb2, B = layer.in_features, layer.out_features, layer.nblocks1, layer.nblocks2, w.batch
+    dt_code = M.BF16 if w.dtype == "bf16" else M.F32
+    tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    e = 2 if w.dtype == "bf16" else 4
+
+    log(f"workload {w.name}: in={fi} out={fo} b1={nb1} b2={nb2} batch={B} {w.dtype}")
+    # seeded synthetic inputs drawn on the device (same distributions as the
+    # parity tests' host draws)
+    def draw(tid, shape, dist, var):
+        g = torch.Generator(device=dev)
+        g.manual_seed(S.seed_for(w.cfg, tid))
+        if dist == "normal":
+            t = torch.randn(shape, generator=g, device=dev, dtype=torch.float32)
+            if var != 1.0:
+                t.mul_(var ** 0.5)
+        else:
+            t = torch.rand(shape, generator=g, device=dev, dtype=torch.float32)
+        return t.to(tdt)
+
+    vr, vl = w.w_var[0]
+    x = draw(S.TID_X, (B, fi), w.x_dist, w.x_var)
+    w1 = draw(S.TID_W1, layer.w1_shape, "normal", vr)
+    w2 = draw(S.TID_W2, layer.w2_shape, "normal", vl)
+    dy = draw(S.TID_DY, (B, fo), "normal", w.dy_var)
+    y = torch.empty((B, fo), dtype=tdt, device=dev)
+    z = torch.empty((B, fo), dtype=tdt, device=dev)
+    dx = torch.empty_like(x)
+    dw1 = torch.empty_like(w1)
+    dw2 = torch.empty_like(w2)
+    wsb = M.monarch_bwd_workspace_bytes(fi, fo, nb1, nb2, B, dt_code)
+    ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    fnames = M.monarch_describe(0, fi, fo, nb1, nb2, B, dt_code)
+    bnames = M.monarch_describe(1, fi, fo, nb1, nb2, B, dt_code)
+    stream = torch.cuda.current_stream()
+
+    def step(evf=None, evb=None):
+        M.monarch_fwd(x, w1, w2, y, z, fi, fo, nb1, nb2, B, dt_code, M.ACT_NONE, stream, events=evf)
+        M.monarch_bwd(dy, x, w1, w2, z, None, dx, dw1, dw2, ws, wsb, fi, fo, nb1, nb2, B, dt_code,
+                      M.ACT_NONE, stream, events=evb)
+
+    log(f"warmup {args.warmup} steps; kernels fwd={fnames} bwd={bnames}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fnames) + 1)] for _ in range(K)]
+    evb = [[torch.cuda.Event(enable_timing=True) for _ in range(len(bnames) + 1)] for _ in range(K)]
+    log(f"timing {K} steps")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        step(evf[k], evb[k])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_per_step = wall * 1e3 / K
+
+    per_kernel = {}
+    for names, evs in ((fnames, evf), (bnames, evb)):
+        for i, nm in enumerate(names):
+            ts = [ev[i].elapsed_time(ev[i + 1]) for ev in evs]
+            per_kernel[nm] = sum(ts) / len(ts)
+    pr = {"e": e, "batch": B, "in": fi, "mid": fo, "out": fo, "act": 0,
+          "params1": nb1 * (fo // nb1) * (fi // nb1), "params2": nb2 * (fo // nb2) * (fo // nb2)}
+    dom = max(per_kernel, key=per_kernel.get)
+    dom_ms = per_kernel[dom]
+    dom_bytes = kernel_bytes(dom, pr)
+    digest = csrc_digest()
+    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                "traffic": load_traffic(dom, w.name, digest),
+                "algorithmic_bytes": dom_bytes, "avg_ms": round(dom_ms, 4)}
+
+    flops = 6.0 * B * w.params
+    value = flops / (ms_per_step * 1e-3) / 1e12
+    # whole-step HBM fraction against the two-pass algorithmic byte count
+    b2p = e * B * (fi + 2 * fo + fo) + e * w.params + e * B * (fo + 3 * fo + 2 * fi) + 2 * e * w.params
+    step_hbm_frac = b2p / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS
+
+    dense = None
+    if not args.no_dense:
+        log("dense bf16 GEMM baseline of the same shape")
+        Wd = torch.randn((fo, fi), device=dev, dtype=torch.float32).mul_(fi ** -0.5).to(tdt)
+
+        def dense_step():
+            yd = torch.nn.functional.linear(x, Wd)
+            dxd = dy @ Wd
+            dwd = dy.t() @ x
+            return yd, dxd, dwd
+        for _ in range(2):
+            dense_step()
+        torch.cuda.synchronize()
+        reps = 3
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            dense_step()
+        torch.cuda.synchronize()
+        dense_ms = (time.perf_counter() - t0) * 1e3 / reps
+        dense = {"ms_per_step": round(dense_ms, 3),
+                 "tflops": round(6.0 * B * fi * fo / (dense_ms * 1e-3) / 1e12, 1),
+                 "speedup_monarch_vs_dense": round(dense_ms / ms_per_step, 2)}
+        del Wd
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        # about 1.5e12 fp64 flops of dense-factor products (~10-30 s on a host)
+        rows = args.cpu_rows or min(B, max(8, int(1.5e12 / (20.0 * fo * max(fi, fo)))))
+        log(f"cpu baseline: oracle on {rows} rows")
+        cpu = cpu_baseline(w, rows)
+
+    result = {
+        "metric": "Monarch fwd+bwd TFLOP/s",
+        "value": round(value, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded, drawn on the device)",
+        "config": {"workload": w.name, "in_features": fi, "out_features": fo, "nblocks1": nb1,
+                   "nblocks2": nb2, "batch": B, "params": w.params, "passes": "fwd+bwd"},
+        "tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
+        "step_hbm_fraction_2pass": round(step_hbm_frac, 4),
+        "kernels_ms": {k: round(v, 4) for k, v in per_kernel.items()},
+        "roofline": roofline,
+        "dense_baseline": dense,
+        "cpu_baseline": cpu,
+        "csrc_sha256": digest,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,144 @@
+/*
+ * monarch.h -- C ABI of the MI355X (gfx950) Monarch multiply library.
+ *
+ * Operation (Monarch paper, abstract: a product of two block-diagonal
+ * matrices; scatterbrain issues page, "Definition C.3" thread: the block
+ * counts and the MonarchLinear parameter layout; "hypercube" thread: the
+ * stride permutation between the two products):
+ *
+ *   y = Qout · L · P · R · x        for every row x of X, i.e. Y = X · Mᵀ
+ *
+ *   in  = in_features, out = out_features, mid = out (intermediate width),
+ *   b1  = nblocks1, b2 = nblocks2,
+ *   q1i = in/b1, q1o = mid/b1, q2i = mid/b2, q2o = out/b2.
+ *
+ *   stage 1   Z[b, r*q1o + k] = sum_s w1[r, k, s] * X[b, r*q1i + s]
+ *   P         W[b, g*q2i + t] = Z[b, t*b2 + g]          (stride-b2 gather)
+ *   stage 2   V[b, g*q2o + p] = sum_t w2[g, p, t] * W[b, g*q2i + t]
+ *   Qout      Y[b, p*b2 + g]  = act(V[b, g*q2o + p])    (inverse stride scatter)
+ *
+ * Layouts (all row-major, contiguous):
+ *   x  [batch, in]            y  [batch, out]
+ *   w1 [b1, q1o, q1i]  (R)    w2 [b2, q2o, q2i]  (L)
+ *   z  batch*mid elements of the I/O dtype: stage 2's input W, in a layout
+ *      private to the library. It is written by monarch_fwd and must be
+ *      passed unchanged to monarch_bwd with the same shape arguments.
+ *   dtype MONARCH_F32: every buffer is fp32.  MONARCH_BF16: every buffer is
+ *   bfloat16; all sums accumulate in fp32 and results are rounded to
+ *   nearest-even bf16 when stored.
+ *
+ * Common rules for every entry point:
+ *   - Calls are asynchronous and ordered on `stream` (a hipStream_t; NULL is
+ *     the default stream). The library never allocates, frees or
+ *     synchronises, and keeps no state between calls (reentrant).
+ *   - The caller owns every buffer. Outputs must not alias inputs.
+ *   - Every argument is checked before any HIP call; a rejected call has no
+ *     side effects. Checks, in order:
+ *       dtype or act out of range                      -> MONARCH_ERR_DTYPE
+ *       a size <= 0 (batch < 0), a block count that
+ *       does not divide in, mid or out, or a size
+ *       beyond 2^31 elements per dimension              -> MONARCH_ERR_SHAPE
+ *       a required pointer is NULL                      -> MONARCH_ERR_NULL
+ *       a pointer not 16-byte aligned                   -> MONARCH_ERR_ALIGN
+ *       workspace smaller than required                 -> MONARCH_ERR_WORKSPACE
+ *     A failed kernel launch returns MONARCH_ERR_HIP; the HIP error text is
+ *     then available from monarch_status_string(MONARCH_ERR_HIP) on the same
+ *     thread.
+ */
+#ifndef MONARCH_H_
+#define MONARCH_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MONARCH_ABI_VERSION 1
+
+typedef enum {
+  MONARCH_OK = 0,
+  MONARCH_ERR_NULL = -1,
+  MONARCH_ERR_SHAPE = -2,
+  MONARCH_ERR_DTYPE = -3,
+  MONARCH_ERR_ALIGN = -4,
+  MONARCH_ERR_WORKSPACE = -5,
+  MONARCH_ERR_HIP = -6
+} monarch_status;
+
+typedef enum { MONARCH_F32 = 0, MONARCH_BF16 = 1 } monarch_dtype;
+
+/* Activation fused after the inverse permutation (the ReLU between the two
+ * layers of the recommender MLP, scatterbrain issues page, "efficiency
+ * testing numbers" thread). Its derivative at 0 is taken as 0. */
+typedef enum { MONARCH_ACT_NONE = 0, MONARCH_ACT_RELU = 1 } monarch_act;
+
+/* Forward pass: y = act(X · Mᵀ); also writes z (stage 2's input, kept for
+ * the backward pass). x, w1, w2 are read; y and z are overwritten.
+ * batch == 0 returns MONARCH_OK without launching anything (x, y, z may then
+ * be NULL). */
+int monarch_fwd(const void* x, const void* w1, const void* w2, void* y, void* z,
+                int64_t in_features, int64_t out_features, int64_t nblocks1,
+                int64_t nblocks2, int64_t batch, int dtype, int act, void* stream);
+
+/* Bytes of device workspace monarch_bwd needs for this problem (0 when
+ * batch == 0). Returns 0 and sets nothing for invalid shapes. */
+size_t monarch_bwd_workspace_bytes(int64_t in_features, int64_t out_features,
+                                   int64_t nblocks1, int64_t nblocks2, int64_t batch,
+                                   int dtype);
+
+/* Backward pass. Given dy = dL/dy [batch, out], computes
+ *   dx  [batch, in]        = dY_eff · M,
+ *   dw1 [b1, q1o, q1i]     = block r of (dY_eff·Qout·L·P)ᵀ · X   (sum over batch),
+ *   dw2 [b2, q2o, q2i]     = block g of (dY_eff·Qout)ᵀ · W      (sum over batch),
+ * with dY_eff = dy ⊙ 1[y > 0] when act == MONARCH_ACT_RELU (y is then the
+ * forward output and must be non-NULL) and dY_eff = dy otherwise (y unused,
+ * may be NULL). z must be the buffer monarch_fwd wrote for the same x, w1
+ * and shapes. dx, dw1 and dw2 are overwritten, never accumulated into. The
+ * batch reduction of dw1/dw2 runs in a fixed order, so results are
+ * bit-reproducible from run to run. workspace must hold
+ * monarch_bwd_workspace_bytes(...) bytes; its contents are scratch.
+ * batch == 0 writes zeros to dw1 and dw2 and touches nothing else. */
+int monarch_bwd(const void* dy, const void* x, const void* w1, const void* w2,
+                const void* z, const void* y, void* dx, void* dw1, void* dw2,
+                void* workspace, size_t workspace_bytes, int64_t in_features,
+                int64_t out_features, int64_t nblocks1, int64_t nblocks2,
+                int64_t batch, int dtype, int act, void* stream);
+
+/* Same as monarch_fwd / monarch_bwd, and in addition records events[i]
+ * (hipEvent_t) on the stream just before kernel i of the call and
+ * events[n] after the last kernel, where n is the kernel count that
+ * monarch_describe reports for the same problem. events may be NULL. Used to
+ * time single kernels inside a timed region. */
+int monarch_fwd_traced(const void* x, const void* w1, const void* w2, void* y, void* z,
+                       int64_t in_features, int64_t out_features, int64_t nblocks1,
+                       int64_t nblocks2, int64_t batch, int dtype, int act, void* stream,
+                       void* const* events, int n_events);
+int monarch_bwd_traced(const void* dy, const void* x, const void* w1, const void* w2,
+                       const void* z, const void* y, void* dx, void* dw1, void* dw2,
+                       void* workspace, size_t workspace_bytes, int64_t in_features,
+                       int64_t out_features, int64_t nblocks1, int64_t nblocks2,
+                       int64_t batch, int dtype, int act, void* stream,
+                       void* const* events, int n_events);
+
+/* Describes the kernels monarch_fwd (direction 0) or monarch_bwd (direction
+ * 1) launches for a problem: returns their count (negative status for an
+ * invalid problem) and writes their names, separated by ';', into buf
+ * (truncated to buf_len including the terminating NUL; buf may be NULL). */
+int monarch_describe(int direction, int64_t in_features, int64_t out_features,
+                     int64_t nblocks1, int64_t nblocks2, int64_t batch, int dtype,
+                     int act, char* buf, size_t buf_len);
+
+/* Static text for a status code; for MONARCH_ERR_HIP the last HIP error
+ * message recorded on the calling thread. Never NULL. */
+const char* monarch_status_string(int status);
+
+/* MONARCH_ABI_VERSION of the built library. */
+int monarch_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MONARCH_H_ */

@@ -1,0 +1,165 @@
+"""ctypes binding of the C ABI in include/monarch.h.
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libmonarch.so. Functions named like the C entry points take torch
+tensors (or raw integer device pointers / None) and a stream, pass pointers
+and sizes through, and raise MonarchError on a non-zero status. If the
+library has not been built, every call raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional, Sequence
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmonarch.so")
+
+MONARCH_OK = 0
+MONARCH_ERR_NULL = -1
+MONARCH_ERR_SHAPE = -2
+MONARCH_ERR_DTYPE = -3
+MONARCH_ERR_ALIGN = -4
+MONARCH_ERR_WORKSPACE = -5
+MONARCH_ERR_HIP = -6
+
+F32 = 0
+BF16 = 1
+ACT_NONE = 0
+ACT_RELU = 1
+
+EXPORTED = (
+    "monarch_fwd", "monarch_bwd", "monarch_bwd_workspace_bytes", "monarch_fwd_traced",
+    "monarch_bwd_traced", "monarch_describe", "monarch_status_string", "monarch_abi_version",
+)
+
+_lib = None
+
+
+class MonarchError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"monarch status {status}: {message}")
+        self.status = status
+
+
+def load_library():
+    """Loads libmonarch.so (once). Raises if it is missing."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(
+            f"{LIB_PATH} is not built; run `python -m monarch_block_diagonal_amd.build_lib` "
+            "(the Monarch path has no CPU fallback)")
+    lib = ctypes.CDLL(LIB_PATH)
+    vp, i64, c_int, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_size_t
+    shape = [i64] * 5
+    lib.monarch_fwd.argtypes = [vp] * 5 + shape + [c_int, c_int, vp]
+    lib.monarch_fwd.restype = c_int
+    lib.monarch_fwd_traced.argtypes = [vp] * 5 + shape + [c_int, c_int, vp, ctypes.POINTER(vp), c_int]
+    lib.monarch_fwd_traced.restype = c_int
+    lib.monarch_bwd_workspace_bytes.argtypes = shape + [c_int]
+    lib.monarch_bwd_workspace_bytes.restype = sz
+    lib.monarch_bwd.argtypes = [vp] * 10 + [sz] + shape + [c_int, c_int, vp]
+    lib.monarch_bwd.restype = c_int
+    lib.monarch_bwd_traced.argtypes = [vp] * 10 + [sz] + shape + [c_int, c_int, vp,
+                                                                   ctypes.POINTER(vp), c_int]
+    lib.monarch_bwd_traced.restype = c_int
+    lib.monarch_describe.argtypes = [c_int] + shape + [c_int, c_int, ctypes.c_char_p, sz]
+    lib.monarch_describe.restype = c_int
+    lib.monarch_status_string.argtypes = [c_int]
+    lib.monarch_status_string.restype = ctypes.c_char_p
+    lib.monarch_abi_version.argtypes = []
+    lib.monarch_abi_version.restype = c_int
+    _lib = lib
+    return lib
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    return t.data_ptr()
+
+
+def _stream(stream) -> Optional[int]:
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _events(events: Optional[Sequence]):
+    """Raw hipEvent_t handles. torch creates its events lazily, on first
+    record, so an uninitialised torch event is recorded once here first."""
+    if events is None:
+        return None, 0
+    handles = []
+    for e in events:
+        if hasattr(e, "cuda_event"):
+            if not e.cuda_event:
+                e.record()
+            handles.append(e.cuda_event)
+        else:
+            handles.append(e)
+    arr = (ctypes.c_void_p * len(handles))(*handles)
+    return arr, len(handles)
+
+
+def _check(status: int) -> None:
+    if status != MONARCH_OK:
+        raise MonarchError(status, load_library().monarch_status_string(status).decode())
+
+
+def monarch_status_string(status: int) -> str:
+    return load_library().monarch_status_string(status).decode()
+
+
+def monarch_abi_version() -> int:
+    return load_library().monarch_abi_version()
+
+
+def monarch_fwd(x, w1, w2, y, z, in_features, out_features, nblocks1, nblocks2, batch, dtype,
+                act=ACT_NONE, stream=None, events=None) -> None:
+    lib = load_library()
+    args = [_ptr(x), _ptr(w1), _ptr(w2), _ptr(y), _ptr(z), in_features, out_features, nblocks1,
+            nblocks2, batch, dtype, act, _stream(stream)]
+    if events is None:
+        _check(lib.monarch_fwd(*args))
+    else:
+        arr, n = _events(events)
+        _check(lib.monarch_fwd_traced(*args, arr, n))
+
+
+def monarch_bwd_workspace_bytes(in_features, out_features, nblocks1, nblocks2, batch, dtype) -> int:
+    return load_library().monarch_bwd_workspace_bytes(in_features, out_features, nblocks1,
+                                                      nblocks2, batch, dtype)
+
+
+def monarch_bwd(dy, x, w1, w2, z, y, dx, dw1, dw2, workspace, workspace_bytes, in_features,
+                out_features, nblocks1, nblocks2, batch, dtype, act=ACT_NONE, stream=None,
+                events=None) -> None:
+    lib = load_library()
+    args = [_ptr(dy), _ptr(x), _ptr(w1), _ptr(w2), _ptr(z), _ptr(y), _ptr(dx), _ptr(dw1),
+            _ptr(dw2), _ptr(workspace), workspace_bytes, in_features, out_features, nblocks1,
+            nblocks2, batch, dtype, act, _stream(stream)]
+    if events is None:
+        _check(lib.monarch_bwd(*args))
+    else:
+        arr, n = _events(events)
+        _check(lib.monarch_bwd_traced(*args, arr, n))
+
+
+def monarch_describe(direction, in_features, out_features, nblocks1, nblocks2, batch, dtype,
+                     act=ACT_NONE):
+    """Returns the list of kernel names monarch_fwd (0) / monarch_bwd (1) launches."""
+    lib = load_library()
+    buf = ctypes.create_string_buffer(1024)
+    n = lib.monarch_describe(direction, in_features, out_features, nblocks1, nblocks2, batch,
+                             dtype, act, buf, len(buf))
+    if n < 0:
+        raise MonarchError(n, monarch_status_string(n))
+    names = buf.value.decode().split(";") if n else []
+    return names

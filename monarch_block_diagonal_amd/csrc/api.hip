@@ -1,0 +1,198 @@
+// C ABI of the Monarch library: argument checks, kernel planning, launches.
+//
+// The operator and its backward pass are stated in include/monarch.h. Every
+// check runs before the first HIP call, so a rejected call has no side
+// effects and the checks work on machines without a GPU.
+#include <stdio.h>
+#include <string.h>
+
+#include "kernels.h"
+#include "monarch.h"
+#include "plan.h"
+
+namespace monarch {
+namespace {
+
+thread_local char g_hip_error[256] = "no HIP error recorded";
+
+int record_hip(hipError_t e) {
+  if (e == hipSuccess) return MONARCH_OK;
+  snprintf(g_hip_error, sizeof(g_hip_error), "HIP error %d: %s", static_cast<int>(e),
+           hipGetErrorString(e));
+  return MONARCH_ERR_HIP;
+}
+
+bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
+
+struct Tracer {
+  void* const* ev;
+  int n;
+  int idx = 0;
+  hipStream_t s;
+  hipError_t mark() {
+    hipError_t e = hipSuccess;
+    if (ev && idx < n && ev[idx]) e = hipEventRecord(static_cast<hipEvent_t>(ev[idx]), s);
+    ++idx;
+    return e;
+  }
+};
+
+int run_plan(const Plan& plan, const Problem& pr, const Buffers& b, hipStream_t s,
+             void* const* events, int n_events) {
+  Tracer tr{events, n_events, 0, s};
+  for (int i = 0; i < plan.n; ++i) {
+    int st = record_hip(tr.mark());
+    if (st) return st;
+    st = record_hip(launch_step(plan.kind[i], pr, b, s));
+    if (st) return st;
+  }
+  return record_hip(tr.mark());
+}
+
+int fwd_impl(const void* x, const void* w1, const void* w2, void* y, void* z, int64_t in_f,
+             int64_t out_f, int64_t nb1, int64_t nb2, int64_t batch, int dtype, int act,
+             void* stream, void* const* events, int n_events) {
+  Problem pr;
+  int st = make_problem(in_f, out_f, nb1, nb2, batch, dtype, act, &pr);
+  if (st) return st;
+  if (!w1 || !w2) return MONARCH_ERR_NULL;
+  if (batch > 0 && (!x || !y || !z)) return MONARCH_ERR_NULL;
+  if (misaligned(x) || misaligned(w1) || misaligned(w2) || misaligned(y) || misaligned(z))
+    return MONARCH_ERR_ALIGN;
+  if (batch == 0) return MONARCH_OK;
+  Buffers b;
+  b.x = x;
+  b.w1 = w1;
+  b.w2 = w2;
+  b.y_out = y;
+  b.z_out = z;
+  Plan plan = plan_fwd(pr);
+  return run_plan(plan, pr, b, static_cast<hipStream_t>(stream), events, n_events);
+}
+
+int bwd_impl(const void* dy, const void* x, const void* w1, const void* w2, const void* z,
+             const void* y, void* dx, void* dw1, void* dw2, void* ws, size_t ws_bytes,
+             int64_t in_f, int64_t out_f, int64_t nb1, int64_t nb2, int64_t batch, int dtype,
+             int act, void* stream, void* const* events, int n_events) {
+  Problem pr;
+  int st = make_problem(in_f, out_f, nb1, nb2, batch, dtype, act, &pr);
+  if (st) return st;
+  if (!w1 || !w2 || !dw1 || !dw2) return MONARCH_ERR_NULL;
+  if (batch > 0) {
+    if (!dy || !x || !z || !dx) return MONARCH_ERR_NULL;
+    if (act == MONARCH_ACT_RELU && !y) return MONARCH_ERR_NULL;
+  }
+  const size_t need = workspace_bytes(pr);
+  if (need > 0 && !ws) return MONARCH_ERR_NULL;
+  if (misaligned(dy) || misaligned(x) || misaligned(w1) || misaligned(w2) || misaligned(z) ||
+      misaligned(y) || misaligned(dx) || misaligned(dw1) || misaligned(dw2) || misaligned(ws))
+    return MONARCH_ERR_ALIGN;
+  if (ws_bytes < need) return MONARCH_ERR_WORKSPACE;
+  Buffers b;
+  b.dy = dy;
+  b.x = x;
+  b.w1 = w1;
+  b.w2 = w2;
+  b.z = z;
+  b.y = y;
+  b.dx = dx;
+  b.dw1 = dw1;
+  b.dw2 = dw2;
+  b.ws = ws;
+  Plan plan = plan_bwd(pr);
+  return run_plan(plan, pr, b, static_cast<hipStream_t>(stream), events, n_events);
+}
+
+}  // namespace
+}  // namespace monarch
+
+using namespace monarch;
+
+extern "C" {
+
+int monarch_fwd(const void* x, const void* w1, const void* w2, void* y, void* z,
+                int64_t in_features, int64_t out_features, int64_t nblocks1, int64_t nblocks2,
+                int64_t batch, int dtype, int act, void* stream) {
+  return fwd_impl(x, w1, w2, y, z, in_features, out_features, nblocks1, nblocks2, batch, dtype,
+                  act, stream, nullptr, 0);
+}
+
+int monarch_fwd_traced(const void* x, const void* w1, const void* w2, void* y, void* z,
+                       int64_t in_features, int64_t out_features, int64_t nblocks1,
+                       int64_t nblocks2, int64_t batch, int dtype, int act, void* stream,
+                       void* const* events, int n_events) {
+  return fwd_impl(x, w1, w2, y, z, in_features, out_features, nblocks1, nblocks2, batch, dtype,
+                  act, stream, events, n_events);
+}
+
+size_t monarch_bwd_workspace_bytes(int64_t in_features, int64_t out_features, int64_t nblocks1,
+                                   int64_t nblocks2, int64_t batch, int dtype) {
+  Problem pr;
+  if (make_problem(in_features, out_features, nblocks1, nblocks2, batch, dtype, 0, &pr))
+    return 0;
+  return workspace_bytes(pr);
+}
+
+int monarch_bwd(const void* dy, const void* x, const void* w1, const void* w2, const void* z,
+                const void* y, void* dx, void* dw1, void* dw2, void* workspace,
+                size_t workspace_bytes, int64_t in_features, int64_t out_features,
+                int64_t nblocks1, int64_t nblocks2, int64_t batch, int dtype, int act,
+                void* stream) {
+  return bwd_impl(dy, x, w1, w2, z, y, dx, dw1, dw2, workspace, workspace_bytes, in_features,
+                  out_features, nblocks1, nblocks2, batch, dtype, act, stream, nullptr, 0);
+}
+
+int monarch_bwd_traced(const void* dy, const void* x, const void* w1, const void* w2,
+                       const void* z, const void* y, void* dx, void* dw1, void* dw2,
+                       void* workspace, size_t workspace_bytes, int64_t in_features,
+                       int64_t out_features, int64_t nblocks1, int64_t nblocks2, int64_t batch,
+                       int dtype, int act, void* stream, void* const* events, int n_events) {
+  return bwd_impl(dy, x, w1, w2, z, y, dx, dw1, dw2, workspace, workspace_bytes, in_features,
+                  out_features, nblocks1, nblocks2, batch, dtype, act, stream, events, n_events);
+}
+
+int monarch_describe(int direction, int64_t in_features, int64_t out_features, int64_t nblocks1,
+                     int64_t nblocks2, int64_t batch, int dtype, int act, char* buf,
+                     size_t buf_len) {
+  Problem pr;
+  int st = make_problem(in_features, out_features, nblocks1, nblocks2, batch, dtype, act, &pr);
+  if (st) return st;
+  if (direction != 0 && direction != 1) return MONARCH_ERR_DTYPE;
+  Plan plan;
+  if (direction == 0)
+    plan = batch == 0 ? Plan{} : plan_fwd(pr);
+  else
+    plan = plan_bwd(pr);
+  if (buf && buf_len) {
+    buf[0] = '\0';
+    size_t used = 0;
+    for (int i = 0; i < plan.n; ++i) {
+      const char* nm = step_name(plan.kind[i]);
+      int w = snprintf(buf + used, buf_len - used, "%s%s", i ? ";" : "", nm);
+      if (w < 0) break;
+      used += static_cast<size_t>(w);
+      if (used >= buf_len) {
+        buf[buf_len - 1] = '\0';
+        break;
+      }
+    }
+  }
+  return plan.n;
+}
+
+const char* monarch_status_string(int status) {
+  switch (status) {
+    case MONARCH_OK: return "ok";
+    case MONARCH_ERR_NULL: return "a required pointer is NULL";
+    case MONARCH_ERR_SHAPE: return "invalid shape: sizes must be positive and divisible by the block counts";
+    case MONARCH_ERR_DTYPE: return "dtype or activation out of range";
+    case MONARCH_ERR_ALIGN: return "a pointer is not 16-byte aligned";
+    case MONARCH_ERR_WORKSPACE: return "workspace smaller than monarch_bwd_workspace_bytes()";
+    case MONARCH_ERR_HIP: return g_hip_error;
+    default: return "unknown status";
+  }
+}
+
+int monarch_abi_version(void) { return MONARCH_ABI_VERSION; }
+
+}  // extern "C"

@@ -1,0 +1,50 @@
+// Host-side launchers of the Monarch kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace monarch {
+
+// A batched GEMM over independent blocks with arbitrary element strides:
+//   C[blk](i, j) = act( sum_k A[blk](i, k) * B[blk](k, j) ),  i < M, j < N, k < K
+// with A element (blk, i, k) at A + blk*a_sb + i*a_si + k*a_sk (elements of the
+// I/O type), likewise B and C. Every step of the two-stage Monarch product and
+// of its backward pass is one such GEMM whose strides encode the block layout
+// and the stride permutation. When `mask` is set, A(blk, i, k) is replaced by
+// 0 wherever mask at the same offset is <= 0 (ReLU derivative). When
+// `partial` is set, K is cut into `splits` chunks of k_chunk and chunk s writes
+// its fp32 sum to partial[((s*nblk + blk)*M + i)*N + j] instead of C.
+struct GemmArgs {
+  const void* A = nullptr;
+  const void* B = nullptr;
+  void* C = nullptr;
+  const void* mask = nullptr;
+  float* partial = nullptr;
+  int64_t a_sb = 0, a_si = 0, a_sk = 0;
+  int64_t b_sb = 0, b_sk = 0, b_sj = 0;
+  int64_t c_sb = 0, c_si = 0, c_sj = 0;
+  int64_t M = 0, N = 0, K = 0;
+  int64_t nblk = 1;
+  int64_t splits = 1;
+  int64_t k_chunk = 0;
+  int relu = 0;
+};
+
+// Tile sizes of the generic kernel (shared with the host planner).
+constexpr int kGenBM = 64;
+constexpr int kGenBN = 64;
+constexpr int kGenBK = 32;
+
+hipError_t launch_generic_gemm(const GemmArgs& a, bool bf16, hipStream_t s);
+
+// Writes `bytes` zero bytes (a plain kernel, not hipMemsetAsync, so callers may
+// capture it in a graph). p must be 2-byte aligned and bytes a multiple of 2.
+hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
+
+// out[e] = sum_{s < splits} partial[s*n + e] in increasing s, stored in the
+// I/O type (fixed order: bit-reproducible).
+hipError_t launch_reduce_partials(const float* partial, void* out, int64_t n, int64_t splits,
+                                  bool bf16, hipStream_t s);
+
+}  // namespace monarch

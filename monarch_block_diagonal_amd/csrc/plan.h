@@ -1,0 +1,68 @@
+// Problem description, kernel plans and step launches (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace monarch {
+
+enum Path { PATH_GENERIC = 0 };
+
+struct Problem {
+  int64_t in = 0, out = 0, mid = 0, b1 = 0, b2 = 0;
+  int64_t q1i = 0, q1o = 0, q2i = 0, q2o = 0;
+  int64_t batch = 0;
+  int dtype = 0, act = 0;
+  int64_t esize = 4;
+  int path = PATH_GENERIC;
+  // batch split of the weight-gradient reductions (stage 2 and stage 1)
+  int64_t s2 = 1, kc2 = 0, s1 = 1, kc1 = 0;
+  // workspace layout (byte offsets)
+  size_t ws_dz = 0, ws_p2 = 0, ws_p1 = 0, ws_total = 0;
+};
+
+struct Buffers {
+  const void* x = nullptr;
+  const void* w1 = nullptr;
+  const void* w2 = nullptr;
+  const void* dy = nullptr;
+  const void* y = nullptr;  // forward output (read by the ReLU backward)
+  const void* z = nullptr;  // saved stage-2 input (read by the backward)
+  void* y_out = nullptr;
+  void* z_out = nullptr;
+  void* dx = nullptr;
+  void* dw1 = nullptr;
+  void* dw2 = nullptr;
+  void* ws = nullptr;
+};
+
+enum StepKind {
+  GEN_STAGE1_FWD,
+  GEN_STAGE2_FWD,
+  GEN_STAGE2_BWD_DATA,
+  GEN_STAGE2_BWD_WEIGHT,
+  GEN_STAGE1_BWD_DATA,
+  GEN_STAGE1_BWD_WEIGHT,
+  REDUCE_DW2,
+  REDUCE_DW1,
+  ZERO_DW,
+};
+
+struct Plan {
+  int n = 0;
+  StepKind kind[16];
+  void add(StepKind k) { kind[n++] = k; }
+};
+
+// Checks dtype/act/shape and fills the derived sizes, path and workspace
+// layout. Returns a monarch_status.
+int make_problem(int64_t in, int64_t out, int64_t nb1, int64_t nb2, int64_t batch, int dtype,
+                 int act, Problem* pr);
+size_t workspace_bytes(const Problem& pr);
+Plan plan_fwd(const Problem& pr);
+Plan plan_bwd(const Problem& pr);
+const char* step_name(StepKind k);
+hipError_t launch_step(StepKind k, const Problem& pr, const Buffers& b, hipStream_t s);
+
+}  // namespace monarch

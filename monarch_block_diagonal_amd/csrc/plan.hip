@@ -1,0 +1,203 @@
+// Kernel planning for one Monarch problem and the launch of each step.
+//
+// Generic path (any shape): every step is one strided batched GEMM
+// (generic.hip). With natural-order Z[b, r*q1o + k] saved by the forward:
+//   stage 1 fwd   Z(r; b, k)  = sum_s X[b, r*q1i+s] w1[r,k,s]
+//   stage 2 fwd   Y(g; b, p)  = act(sum_t Z[b, t*b2+g] w2[g,p,t])   -> Y[b, p*b2+g]
+//   stage 2 bwd   dZ(g; b, t) = sum_p dYe[b, p*b2+g] w2[g,p,t]      -> dZ[b, t*b2+g]
+//                 dw2(g; p, t) = sum_b dYe[b, p*b2+g] Z[b, t*b2+g]   (batch split)
+//   stage 1 bwd   dX(r; b, s) = sum_k dZ[b, r*q1o+k] w1[r,k,s]
+//                 dw1(r; k, s) = sum_b dZ[b, r*q1o+k] X[b, r*q1i+s]  (batch split)
+// where dYe = dY masked by Y > 0 after a fused ReLU. The index maps are the
+// stride permutation and its inverse (scatterbrain issues page, "hypercube"
+// thread) folded into the operand strides.
+#include "kernels.h"
+#include "monarch.h"
+#include "plan.h"
+
+namespace monarch {
+
+namespace {
+
+constexpr int64_t kDimLimit = int64_t(1) << 31;
+
+size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// Batch split for a weight-gradient GEMM with nblk blocks of M x N and
+// reduction length K: enough workgroups to fill the chip, chunks >= 128 rows.
+void choose_splits(int64_t nblk, int64_t M, int64_t N, int64_t K, int64_t* splits,
+                   int64_t* chunk) {
+  if (K <= 0) {
+    *splits = 1;
+    *chunk = 0;
+    return;
+  }
+  const int64_t base = nblk * ((M + kGenBM - 1) / kGenBM) * ((N + kGenBN - 1) / kGenBN);
+  int64_t s = (2048 + base - 1) / base;
+  const int64_t smax_k = (K + 127) / 128;
+  if (s > smax_k) s = smax_k;
+  if (s > 64) s = 64;
+  if (s < 1) s = 1;
+  int64_t c = (K + s - 1) / s;
+  c = (c + kGenBK - 1) / kGenBK * kGenBK;
+  *chunk = c;
+  *splits = (K + c - 1) / c;
+}
+
+}  // namespace
+
+int make_problem(int64_t in, int64_t out, int64_t nb1, int64_t nb2, int64_t batch, int dtype,
+                 int act, Problem* pr) {
+  if (dtype != MONARCH_F32 && dtype != MONARCH_BF16) return MONARCH_ERR_DTYPE;
+  if (act != MONARCH_ACT_NONE && act != MONARCH_ACT_RELU) return MONARCH_ERR_DTYPE;
+  if (in <= 0 || out <= 0 || nb1 <= 0 || nb2 <= 0 || batch < 0) return MONARCH_ERR_SHAPE;
+  if (in >= kDimLimit || out >= kDimLimit || batch >= kDimLimit) return MONARCH_ERR_SHAPE;
+  const int64_t mid = out;
+  if (in % nb1 || mid % nb1 || mid % nb2 || out % nb2) return MONARCH_ERR_SHAPE;
+  Problem p;
+  p.in = in;
+  p.out = out;
+  p.mid = mid;
+  p.b1 = nb1;
+  p.b2 = nb2;
+  p.q1i = in / nb1;
+  p.q1o = mid / nb1;
+  p.q2i = mid / nb2;
+  p.q2o = out / nb2;
+  p.batch = batch;
+  p.dtype = dtype;
+  p.act = act;
+  p.esize = dtype == MONARCH_BF16 ? 2 : 4;
+  p.path = PATH_GENERIC;
+  choose_splits(p.b2, p.q2o, p.q2i, batch, &p.s2, &p.kc2);
+  choose_splits(p.b1, p.q1o, p.q1i, batch, &p.s1, &p.kc1);
+  if (batch > 0) {
+    size_t off = 0;
+    p.ws_dz = off;
+    off = align_up(off + static_cast<size_t>(batch) * mid * p.esize, 256);
+    p.ws_p2 = off;
+    off = align_up(off + static_cast<size_t>(p.s2) * nb2 * p.q2o * p.q2i * 4, 256);
+    p.ws_p1 = off;
+    off = align_up(off + static_cast<size_t>(p.s1) * nb1 * p.q1o * p.q1i * 4, 256);
+    p.ws_total = off;
+  }
+  *pr = p;
+  return MONARCH_OK;
+}
+
+size_t workspace_bytes(const Problem& pr) { return pr.ws_total; }
+
+Plan plan_fwd(const Problem& pr) {
+  Plan p;
+  if (pr.batch == 0) return p;
+  p.add(GEN_STAGE1_FWD);
+  p.add(GEN_STAGE2_FWD);
+  return p;
+}
+
+Plan plan_bwd(const Problem& pr) {
+  Plan p;
+  if (pr.batch == 0) {
+    p.add(ZERO_DW);
+    return p;
+  }
+  p.add(GEN_STAGE2_BWD_DATA);
+  p.add(GEN_STAGE2_BWD_WEIGHT);
+  p.add(GEN_STAGE1_BWD_DATA);
+  p.add(GEN_STAGE1_BWD_WEIGHT);
+  p.add(REDUCE_DW2);
+  p.add(REDUCE_DW1);
+  return p;
+}
+
+const char* step_name(StepKind k) {
+  switch (k) {
+    case GEN_STAGE1_FWD: return "generic_stage1_fwd";
+    case GEN_STAGE2_FWD: return "generic_stage2_fwd";
+    case GEN_STAGE2_BWD_DATA: return "generic_stage2_bwd_data";
+    case GEN_STAGE2_BWD_WEIGHT: return "generic_stage2_bwd_weight";
+    case GEN_STAGE1_BWD_DATA: return "generic_stage1_bwd_data";
+    case GEN_STAGE1_BWD_WEIGHT: return "generic_stage1_bwd_weight";
+    case REDUCE_DW2: return "reduce_dw2";
+    case REDUCE_DW1: return "reduce_dw1";
+    case ZERO_DW: return "zero_dw";
+  }
+  return "?";
+}
+
+hipError_t launch_step(StepKind k, const Problem& pr, const Buffers& b, hipStream_t s) {
+  const bool bf16 = pr.dtype == MONARCH_BF16;
+  char* ws = static_cast<char*>(b.ws);
+  void* dz = ws ? ws + pr.ws_dz : nullptr;
+  float* p2 = ws ? reinterpret_cast<float*>(ws + pr.ws_p2) : nullptr;
+  float* p1 = ws ? reinterpret_cast<float*>(ws + pr.ws_p1) : nullptr;
+  const void* mask = pr.act == MONARCH_ACT_RELU ? b.y : nullptr;
+  GemmArgs a;
+  switch (k) {
+    case GEN_STAGE1_FWD:
+      a.A = b.x;
+      a.a_sb = pr.q1i, a.a_si = pr.in, a.a_sk = 1;
+      a.B = b.w1;
+      a.b_sb = pr.q1o * pr.q1i, a.b_sk = 1, a.b_sj = pr.q1i;
+      a.C = b.z_out;
+      a.c_sb = pr.q1o, a.c_si = pr.mid, a.c_sj = 1;
+      a.M = pr.batch, a.N = pr.q1o, a.K = pr.q1i, a.nblk = pr.b1;
+      return launch_generic_gemm(a, bf16, s);
+    case GEN_STAGE2_FWD:
+      a.A = b.z_out;
+      a.a_sb = 1, a.a_si = pr.mid, a.a_sk = pr.b2;
+      a.B = b.w2;
+      a.b_sb = pr.q2o * pr.q2i, a.b_sk = 1, a.b_sj = pr.q2i;
+      a.C = b.y_out;
+      a.c_sb = 1, a.c_si = pr.out, a.c_sj = pr.b2;
+      a.M = pr.batch, a.N = pr.q2o, a.K = pr.q2i, a.nblk = pr.b2;
+      a.relu = pr.act == MONARCH_ACT_RELU;
+      return launch_generic_gemm(a, bf16, s);
+    case GEN_STAGE2_BWD_DATA:
+      a.A = b.dy, a.mask = mask;
+      a.a_sb = 1, a.a_si = pr.out, a.a_sk = pr.b2;
+      a.B = b.w2;
+      a.b_sb = pr.q2o * pr.q2i, a.b_sk = pr.q2i, a.b_sj = 1;
+      a.C = dz;
+      a.c_sb = 1, a.c_si = pr.mid, a.c_sj = pr.b2;
+      a.M = pr.batch, a.N = pr.q2i, a.K = pr.q2o, a.nblk = pr.b2;
+      return launch_generic_gemm(a, bf16, s);
+    case GEN_STAGE2_BWD_WEIGHT:
+      a.A = b.dy, a.mask = mask;
+      a.a_sb = 1, a.a_si = pr.b2, a.a_sk = pr.out;
+      a.B = b.z;
+      a.b_sb = 1, a.b_sk = pr.mid, a.b_sj = pr.b2;
+      a.partial = p2, a.splits = pr.s2, a.k_chunk = pr.kc2;
+      a.M = pr.q2o, a.N = pr.q2i, a.K = pr.batch, a.nblk = pr.b2;
+      return launch_generic_gemm(a, bf16, s);
+    case GEN_STAGE1_BWD_DATA:
+      a.A = dz;
+      a.a_sb = pr.q1o, a.a_si = pr.mid, a.a_sk = 1;
+      a.B = b.w1;
+      a.b_sb = pr.q1o * pr.q1i, a.b_sk = pr.q1i, a.b_sj = 1;
+      a.C = b.dx;
+      a.c_sb = pr.q1i, a.c_si = pr.in, a.c_sj = 1;
+      a.M = pr.batch, a.N = pr.q1i, a.K = pr.q1o, a.nblk = pr.b1;
+      return launch_generic_gemm(a, bf16, s);
+    case GEN_STAGE1_BWD_WEIGHT:
+      a.A = dz;
+      a.a_sb = pr.q1o, a.a_si = 1, a.a_sk = pr.mid;
+      a.B = b.x;
+      a.b_sb = pr.q1i, a.b_sk = pr.in, a.b_sj = 1;
+      a.partial = p1, a.splits = pr.s1, a.k_chunk = pr.kc1;
+      a.M = pr.q1o, a.N = pr.q1i, a.K = pr.batch, a.nblk = pr.b1;
+      return launch_generic_gemm(a, bf16, s);
+    case REDUCE_DW2:
+      return launch_reduce_partials(p2, b.dw2, pr.b2 * pr.q2o * pr.q2i, pr.s2, bf16, s);
+    case REDUCE_DW1:
+      return launch_reduce_partials(p1, b.dw1, pr.b1 * pr.q1o * pr.q1i, pr.s1, bf16, s);
+    case ZERO_DW: {
+      hipError_t e = launch_zero(b.dw2, static_cast<size_t>(pr.b2 * pr.q2o * pr.q2i) * pr.esize, s);
+      if (e != hipSuccess) return e;
+      return launch_zero(b.dw1, static_cast<size_t>(pr.b1 * pr.q1o * pr.q1i) * pr.esize, s);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace monarch

@@ -31,9 +31,11 @@ def round_to_bf16(a: np.ndarray) -> np.ndarray:
     """Round fp32 values to the nearest bfloat16 (ties to even); returns fp32
     arrays holding exactly representable bf16 values. NaN stays NaN."""
     a32 = np.ascontiguousarray(a, dtype=np.float32)
-    u = a32.view(np.uint32).astype(np.uint64)
-    lsb = (u >> np.uint64(16)) & np.uint64(1)
-    r = ((u + np.uint64(0x7FFF) + lsb) & np.uint64(0xFFFF0000)).astype(np.uint32)
+    u = a32.view(np.uint32)
+    # finite values never wrap: the largest finite pattern 0xFF7FFFFF + 0x8000 fits in 32 bits
+    r = u + np.uint32(0x7FFF)
+    r += (u >> np.uint32(16)) & np.uint32(1)
+    r &= np.uint32(0xFFFF0000)
     nan = np.isnan(a32)
     if nan.any():
         r[nan] = (a32.view(np.uint32)[nan] | np.uint32(0x00400000)) & np.uint32(0xFFFF0000)

@@ -246,40 +246,45 @@ def backward_dx_rows(dy_rows, w1, w2, in_features, out_features, factors=None, y
 
 
 def weight_grad_entries(dy, x, w1, w2, in_features, out_features, r_k_s, g_p_t, factors=None,
-                        y=None, relu=False):
+                        y=None, relu=False, chunk: int = 8192):
     """Individual weight-gradient entries summed over the whole batch.
 
     dR[r,k,s] = Σ_b dZ[b, r*q1o+k]·X[b, r*q1i+s] with the column dZ[:, j] =
     dY_eff·(Qo·Ld·Pm)[:, j];  dL[g,p,t] = Σ_b dV[b, g*q2o+p]·W[b, g*q2i+t] with
-    dV[:, i] = dY_eff·Qo[:, i] and W[:, i] = X·(Pm·Rd)[i, :]ᵀ."""
+    dV[:, i] = dY_eff·Qo[:, i] and W[:, i] = X·(Pm·Rd)[i, :]ᵀ.
+    The batch sum runs over row chunks (fp64) so full-size inputs stay in
+    their storage precision in memory."""
     Rd, Pm, Ld, Qo = factors if factors is not None else dense_factors(w1, w2, in_features, out_features)
     s = derive_sizes(in_features, out_features, w1.shape[0], w2.shape[0])
-    X = np.asarray(x, dtype=np.float64)
-    dY = np.asarray(dy, dtype=np.float64)
-    if relu:
-        dY = dY * (np.asarray(y, dtype=np.float64) > 0)
     mid, out = s["mid"], s["out"]
-    out_r = []
+    rcols, rx = [], []
     for (r, k, sidx) in r_k_s:
-        j = r * s["q1o"] + k
         e = np.zeros((mid, 1))
-        e[j, 0] = 1.0
-        col = _mm(Qo, _mm(Ld, _mm(Pm, e)))          # (out, 1) = (Qo·Ld·Pm)[:, j]
-        dz = (dY @ col).ravel()
-        out_r.append(float(dz @ X[:, r * s["q1i"] + sidx]))
-    out_l = []
+        e[r * s["q1o"] + k, 0] = 1.0
+        rcols.append(_mm(Qo, _mm(Ld, _mm(Pm, e))).ravel())     # (Qo·Ld·Pm)[:, j]
+        rx.append(r * s["q1i"] + sidx)
+    lq, lw = [], []
     for (g, p, t) in g_p_t:
-        i_out = g * s["q2o"] + p
         e = np.zeros((out, 1))
-        e[i_out, 0] = 1.0
-        dv = (dY @ _mm(Qo, e)).ravel()
-        i_mid = g * s["q2i"] + t
+        e[g * s["q2o"] + p, 0] = 1.0
+        lq.append(_mm(Qo, e).ravel())                          # Qo[:, i_out]
         e2 = np.zeros((1, mid))
-        e2[0, i_mid] = 1.0
-        row = _mm(_mm(e2, Pm), Rd)                   # (1, in) = (Pm·Rd)[i_mid, :]
-        wcol = (X @ row.T).ravel()
-        out_l.append(float(dv @ wcol))
-    return np.array(out_r), np.array(out_l)
+        e2[0, g * s["q2i"] + t] = 1.0
+        lw.append(_mm(_mm(e2, Pm), Rd).ravel())                # (Pm·Rd)[i_mid, :]
+    acc_r = np.zeros(len(rcols))
+    acc_l = np.zeros(len(lq))
+    nrows = np.asarray(x).shape[0]
+    for b0 in range(0, nrows, chunk):
+        b1 = min(nrows, b0 + chunk)
+        dYc = np.asarray(dy[b0:b1], dtype=np.float64)
+        if relu:
+            dYc = dYc * (np.asarray(y[b0:b1], dtype=np.float64) > 0)
+        Xc = np.asarray(x[b0:b1], dtype=np.float64)
+        for i, (col, xi) in enumerate(zip(rcols, rx)):
+            acc_r[i] += (dYc @ col) @ Xc[:, xi]
+        for i, (qc, wr) in enumerate(zip(lq, lw)):
+            acc_l[i] += (dYc @ qc) @ (Xc @ wr)
+    return acc_r, acc_l
 
 
 # ----------------------------------------------------------------------------

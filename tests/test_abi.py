@@ -1,0 +1,141 @@
+"""Host-side checks of the C ABI: the library loads, exports every symbol the
+header declares, and rejects bad arguments before any HIP call (these run
+without a GPU; no call here reaches a kernel launch)."""
+import os
+import re
+
+import pytest
+
+import monarch_block_diagonal_amd as M
+from monarch_block_diagonal_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "monarch.h")
+
+A = 0x10000      # fake 16-byte-aligned device addresses (never dereferenced)
+A2 = 0x20000
+MIS = 0x10008    # 8-byte but not 16-byte aligned
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(monarch_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = M.load_library()
+    declared = header_functions()
+    assert declared, "no declarations parsed"
+    for name in declared:
+        assert hasattr(lib, name), name
+    assert set(declared) == set(B.EXPORTED)
+
+
+def test_abi_version_matches_header():
+    text = open(HEADER).read()
+    ver = int(re.search(r"#define MONARCH_ABI_VERSION (\d+)", text).group(1))
+    assert M.monarch_abi_version() == ver
+
+
+def test_status_strings():
+    for st in (0, -1, -2, -3, -4, -5, -6, 7):
+        s = M.monarch_status_string(st)
+        assert isinstance(s, str) and s
+    assert "aligned" in M.monarch_status_string(B.MONARCH_ERR_ALIGN)
+
+
+def fwd(x=A, w1=A, w2=A, y=A2, z=A2, fi=16, fo=16, nb1=4, nb2=4, b=8, dt=B.F32, act=B.ACT_NONE):
+    lib = M.load_library()
+    return lib.monarch_fwd(x, w1, w2, y, z, fi, fo, nb1, nb2, b, dt, act, None)
+
+
+def bwd(dy=A, x=A, w1=A, w2=A, z=A, y=A, dx=A2, dw1=A2, dw2=A2, ws=A2, wsb=1 << 40, fi=16,
+        fo=16, nb1=4, nb2=4, b=8, dt=B.F32, act=B.ACT_NONE):
+    lib = M.load_library()
+    return lib.monarch_bwd(dy, x, w1, w2, z, y, dx, dw1, dw2, ws, wsb, fi, fo, nb1, nb2, b, dt,
+                           act, None)
+
+
+@pytest.mark.parametrize("kw", [dict(dt=2), dict(dt=-1), dict(act=2), dict(act=-1)])
+def test_bad_dtype_or_act(kw):
+    assert fwd(**kw) == B.MONARCH_ERR_DTYPE
+    assert bwd(**kw) == B.MONARCH_ERR_DTYPE
+
+
+@pytest.mark.parametrize("kw", [
+    dict(fi=0), dict(fo=0), dict(nb1=0), dict(nb2=0), dict(b=-1), dict(fi=-16),
+    dict(fi=18),                 # in % nb1
+    dict(fo=18, nb2=2),          # mid % nb1
+    dict(fo=20, nb1=4, nb2=8),   # mid % nb2
+    dict(fi=1 << 31, nb1=1),     # per-dimension limit
+])
+def test_bad_shapes(kw):
+    assert fwd(**kw) == B.MONARCH_ERR_SHAPE
+    assert bwd(**kw) == B.MONARCH_ERR_SHAPE
+    args = {k: kw.get(k, d) for k, d in dict(fi=16, fo=16, nb1=4, nb2=4, b=8).items()}
+    assert M.monarch_bwd_workspace_bytes(args["fi"], args["fo"], args["nb1"], args["nb2"],
+                                         args["b"], 0) == 0
+
+
+@pytest.mark.parametrize("name", ["x", "w1", "w2", "y", "z"])
+def test_fwd_null_pointers(name):
+    assert fwd(**{name: None}) == B.MONARCH_ERR_NULL
+
+
+@pytest.mark.parametrize("name", ["dy", "x", "w1", "w2", "z", "dx", "dw1", "dw2", "ws"])
+def test_bwd_null_pointers(name):
+    assert bwd(**{name: None}) == B.MONARCH_ERR_NULL
+
+
+def test_bwd_relu_needs_y():
+    assert bwd(y=None, act=B.ACT_RELU) == B.MONARCH_ERR_NULL
+
+
+@pytest.mark.parametrize("name", ["x", "w1", "w2", "y", "z"])
+def test_fwd_misaligned(name):
+    assert fwd(**{name: MIS}) == B.MONARCH_ERR_ALIGN
+
+
+@pytest.mark.parametrize("name", ["dy", "x", "w1", "w2", "z", "y", "dx", "dw1", "dw2", "ws"])
+def test_bwd_misaligned(name):
+    assert bwd(**{name: MIS}) == B.MONARCH_ERR_ALIGN
+
+
+def test_bwd_workspace_too_small():
+    need = M.monarch_bwd_workspace_bytes(16, 16, 4, 4, 8, 0)
+    assert need > 0
+    assert bwd(wsb=need - 1) == B.MONARCH_ERR_WORKSPACE
+    assert bwd(wsb=0) == B.MONARCH_ERR_WORKSPACE
+
+
+def test_batch_zero_forward_is_a_no_op():
+    # no launch: null activations are accepted and nothing touches the GPU
+    assert fwd(x=None, y=None, z=None, b=0) == B.MONARCH_OK
+    assert M.monarch_bwd_workspace_bytes(16, 16, 4, 4, 0, 0) == 0
+    assert M.monarch_describe(0, 16, 16, 4, 4, 0, 0) == []
+    assert M.monarch_describe(1, 16, 16, 4, 4, 0, 0) == ["zero_dw"]
+
+
+def test_workspace_grows_with_batch_and_dtype():
+    a = M.monarch_bwd_workspace_bytes(1024, 1024, 32, 32, 4096, B.BF16)
+    b = M.monarch_bwd_workspace_bytes(1024, 1024, 32, 32, 8192, B.BF16)
+    c = M.monarch_bwd_workspace_bytes(1024, 1024, 32, 32, 4096, B.F32)
+    assert 0 < a < b and a < c
+    big = M.monarch_bwd_workspace_bytes(16384, 16384, 128, 128, 65536, B.BF16)
+    assert big >= 65536 * 16384 * 2
+
+
+def test_describe_lists_kernels():
+    f = M.monarch_describe(0, 1024, 1024, 32, 32, 4096, B.BF16)
+    b = M.monarch_describe(1, 1024, 1024, 32, 32, 4096, B.BF16)
+    assert len(f) >= 1 and len(b) >= 1
+    assert all(isinstance(n, str) and n for n in f + b)
+    with pytest.raises(M.MonarchError):
+        M.monarch_describe(0, 18, 16, 4, 4, 8, 0)
+
+
+def test_binding_raises_on_error():
+    with pytest.raises(M.MonarchError) as e:
+        M.monarch_fwd(None, A, A, A, A, 16, 16, 4, 4, 8, B.F32, B.ACT_NONE, stream=0)
+    assert e.value.status == B.MONARCH_ERR_NULL
