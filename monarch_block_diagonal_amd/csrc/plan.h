@@ -5,9 +5,11 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "square.h"
+
 namespace monarch {
 
-enum Path { PATH_GENERIC = 0 };
+enum Path { PATH_GENERIC = 0, PATH_SQ128 = 1 };
 
 struct Problem {
   int64_t in = 0, out = 0, mid = 0, b1 = 0, b2 = 0;
@@ -18,6 +20,7 @@ struct Problem {
   int path = PATH_GENERIC;
   // batch split of the weight-gradient reductions (stage 2 and stage 1)
   int64_t s2 = 1, kc2 = 0, s1 = 1, kc1 = 0;
+  SqPlan sq;  // launch geometry of PATH_SQ128
   // workspace layout (byte offsets)
   size_t ws_dz = 0, ws_p2 = 0, ws_p1 = 0, ws_total = 0;
 };
@@ -47,6 +50,11 @@ enum StepKind {
   REDUCE_DW2,
   REDUCE_DW1,
   ZERO_DW,
+  SQ_STAGE1_FWD,
+  SQ_STAGE2_FWD,
+  SQ_STAGE2_BWD_DATA,
+  SQ_STAGE2_BWD_WEIGHT,
+  SQ_STAGE1_BWD,
 };
 
 struct Plan {

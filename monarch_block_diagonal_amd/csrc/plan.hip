@@ -69,8 +69,15 @@ int make_problem(int64_t in, int64_t out, int64_t nb1, int64_t nb2, int64_t batc
   p.act = act;
   p.esize = dtype == MONARCH_BF16 ? 2 : 4;
   p.path = PATH_GENERIC;
-  choose_splits(p.b2, p.q2o, p.q2i, batch, &p.s2, &p.kc2);
-  choose_splits(p.b1, p.q1o, p.q1i, batch, &p.s1, &p.kc1);
+  if (batch > 0 && sq_applicable(in, out, nb1, nb2, dtype == MONARCH_BF16)) {
+    p.path = PATH_SQ128;
+    p.sq = sq_plan(batch, nb1);
+    p.s2 = p.sq.w2_chunks;
+    p.s1 = p.sq.b1_chunks;
+  } else {
+    choose_splits(p.b2, p.q2o, p.q2i, batch, &p.s2, &p.kc2);
+    choose_splits(p.b1, p.q1o, p.q1i, batch, &p.s1, &p.kc1);
+  }
   if (batch > 0) {
     size_t off = 0;
     p.ws_dz = off;
@@ -90,6 +97,11 @@ size_t workspace_bytes(const Problem& pr) { return pr.ws_total; }
 Plan plan_fwd(const Problem& pr) {
   Plan p;
   if (pr.batch == 0) return p;
+  if (pr.path == PATH_SQ128) {
+    p.add(SQ_STAGE1_FWD);
+    p.add(SQ_STAGE2_FWD);
+    return p;
+  }
   p.add(GEN_STAGE1_FWD);
   p.add(GEN_STAGE2_FWD);
   return p;
@@ -99,6 +111,14 @@ Plan plan_bwd(const Problem& pr) {
   Plan p;
   if (pr.batch == 0) {
     p.add(ZERO_DW);
+    return p;
+  }
+  if (pr.path == PATH_SQ128) {
+    p.add(SQ_STAGE2_BWD_DATA);
+    p.add(SQ_STAGE2_BWD_WEIGHT);
+    p.add(SQ_STAGE1_BWD);
+    p.add(REDUCE_DW2);
+    p.add(REDUCE_DW1);
     return p;
   }
   p.add(GEN_STAGE2_BWD_DATA);
@@ -121,6 +141,11 @@ const char* step_name(StepKind k) {
     case REDUCE_DW2: return "reduce_dw2";
     case REDUCE_DW1: return "reduce_dw1";
     case ZERO_DW: return "zero_dw";
+    case SQ_STAGE1_FWD: return "sq128_stage1_fwd";
+    case SQ_STAGE2_FWD: return "sq128_stage2_fwd";
+    case SQ_STAGE2_BWD_DATA: return "sq128_stage2_bwd_data";
+    case SQ_STAGE2_BWD_WEIGHT: return "sq128_stage2_bwd_weight";
+    case SQ_STAGE1_BWD: return "sq128_stage1_bwd";
   }
   return "?";
 }
@@ -191,6 +216,17 @@ hipError_t launch_step(StepKind k, const Problem& pr, const Buffers& b, hipStrea
       return launch_reduce_partials(p2, b.dw2, pr.b2 * pr.q2o * pr.q2i, pr.s2, bf16, s);
     case REDUCE_DW1:
       return launch_reduce_partials(p1, b.dw1, pr.b1 * pr.q1o * pr.q1i, pr.s1, bf16, s);
+    case SQ_STAGE1_FWD:
+      return sq_launch_stage1_fwd(b.x, b.w1, b.z_out, pr.batch, pr.b1, pr.sq, s);
+    case SQ_STAGE2_FWD:
+      return sq_launch_stage2_fwd(b.z_out, b.w2, b.y_out, pr.batch, pr.b2,
+                                  pr.act == MONARCH_ACT_RELU, pr.sq, s);
+    case SQ_STAGE2_BWD_DATA:
+      return sq_launch_stage2_bwd_data(b.dy, mask, b.w2, dz, pr.batch, pr.b2, pr.sq, s);
+    case SQ_STAGE2_BWD_WEIGHT:
+      return sq_launch_stage2_bwd_weight(b.dy, mask, b.z, p2, pr.batch, pr.b2, pr.sq, s);
+    case SQ_STAGE1_BWD:
+      return sq_launch_stage1_bwd(dz, b.x, b.w1, b.dx, p1, pr.batch, pr.b1, pr.sq, s);
     case ZERO_DW: {
       hipError_t e = launch_zero(b.dw2, static_cast<size_t>(pr.b2 * pr.q2o * pr.q2i) * pr.esize, s);
       if (e != hipSuccess) return e;

@@ -241,6 +241,11 @@ SHAPES = [
     (2048, 2048, 16, 16, 129),
     (4096, 4096, 64, 64, 65),
     (16384, 16384, 128, 128, 96),
+    # 128x128 blocks with a multiple of 8 blocks: the bf16 fast path
+    (1024, 1024, 8, 8, 1),
+    (1024, 1024, 8, 8, 77),
+    (2048, 2048, 16, 16, 129),
+    (16384, 16384, 128, 128, 1000),
     (768, 3072, 4, 4, 100),
     (250, 100, 5, 2, 45),
     (36, 36, 6, 6, 17),
@@ -258,7 +263,8 @@ def test_shapes(api, shape, dtype):
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("shape", [(256, 256, 16, 16, 300), (96, 160, 4, 8, 50),
-                                   (16384, 16384, 128, 128, 64), (1024, 512, 16, 16, 100)],
+                                   (16384, 16384, 128, 128, 64), (1024, 512, 16, 16, 100),
+                                   (2048, 2048, 16, 16, 45)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_shapes_relu(api, shape, dtype):
     inp, out, b1, b2, batch = shape
@@ -292,8 +298,11 @@ def test_permutation_blocks_bit_exact(api, shape, dtype):
         assert np.array_equal(host(y), expect), (shape, a, c)
 
 
-def test_backward_is_deterministic(api):
-    x, w1, w2, dy = rand_layer(1024, 1024, 32, 32, 4096, "bf16", seed=99)
+@pytest.mark.parametrize("shape", [(1024, 1024, 32, 32, 4096), (2048, 2048, 16, 16, 4100)],
+                         ids=lambda s: "x".join(map(str, s)))
+def test_backward_is_deterministic(api, shape):
+    inp, out, b1, b2, batch = shape
+    x, w1, w2, dy = rand_layer(inp, out, b1, b2, batch, "bf16", seed=99)
     X, W1, W2, DY = dev(x, "bf16"), dev(w1, "bf16"), dev(w2, "bf16"), dev(dy, "bf16")
     y, z = api.monarch_forward(X, W1, W2)
     a = api.monarch_backward(DY, X, W1, W2, z)
