@@ -57,6 +57,7 @@ def kernel_bytes(name: str, pr: dict) -> float:
         "stage1_bwd_data": e * B * (mid + inp) + e * p1,
         "stage1_bwd_weight": e * B * (mid + inp) + e * p1,
         "stage1_bwd": e * B * (mid + 2 * inp) + 2 * e * p1,
+        "transpose_weights": 2 * e * (p1 + p2),
         "reduce_dw2": e * p2,
         "reduce_dw1": e * p1,
     }
@@ -119,6 +120,9 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 1 GiB device copy (read 1 GiB + write 1 GiB), the "
+                         "reference for scaling HBM byte counters")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -217,6 +221,14 @@ def main() -> int:
     # whole-step HBM fraction against the two-pass algorithmic byte count
     b2p = e * B * (fi + 2 * fo + fo) + e * w.params + e * B * (fo + 3 * fo + 2 * fi) + 2 * e * w.params
     step_hbm_frac = b2p / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS
+
+    if args.copy_probe:
+        src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     dense = None
     if not args.no_dense:

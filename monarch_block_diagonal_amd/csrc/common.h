@@ -19,17 +19,26 @@ __device__ __forceinline__ float bf16_to_f32(uint16_t h) {
   return __uint_as_float(static_cast<uint32_t>(h) << 16);
 }
 
-// fp32 -> bf16, round to nearest even; NaN stays a (quiet) NaN.
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+
+// fp32 -> bf16 with the hardware conversion (v_cvt_pk_bf16_f32): round to
+// nearest even, NaN stays NaN. Branch-free, so it adds no control flow to
+// the kernels' main loops.
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<uint16_t>(u >> 16);
+  const __bf16 r = static_cast<__bf16>(f);
+  uint16_t u;
+  __builtin_memcpy(&u, &r, sizeof(u));
+  return u;
 }
 
-// two fp32 -> packed pair of bf16 (low half = a)
+// two fp32 -> packed pair of bf16 (low half = a), one conversion instruction
 __device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
-  return static_cast<uint32_t>(f32_to_bf16(a)) | (static_cast<uint32_t>(f32_to_bf16(b)) << 16);
+  const f32x2 v = {a, b};
+  const bf16x2 r = __builtin_convertvector(v, bf16x2);
+  uint32_t u;
+  __builtin_memcpy(&u, &r, sizeof(u));
+  return u;
 }
 
 template <typename T> struct Io;

@@ -69,7 +69,7 @@ int make_problem(int64_t in, int64_t out, int64_t nb1, int64_t nb2, int64_t batc
   p.act = act;
   p.esize = dtype == MONARCH_BF16 ? 2 : 4;
   p.path = PATH_GENERIC;
-  if (batch > 0 && sq_applicable(in, out, nb1, nb2, dtype == MONARCH_BF16)) {
+  if (batch > 0 && sq_applicable(in, out, nb1, nb2, batch, dtype == MONARCH_BF16)) {
     p.path = PATH_SQ128;
     p.sq = sq_plan(batch, nb1);
     p.s2 = p.sq.w2_chunks;
@@ -86,6 +86,9 @@ int make_problem(int64_t in, int64_t out, int64_t nb1, int64_t nb2, int64_t batc
     off = align_up(off + static_cast<size_t>(p.s2) * nb2 * p.q2o * p.q2i * 4, 256);
     p.ws_p1 = off;
     off = align_up(off + static_cast<size_t>(p.s1) * nb1 * p.q1o * p.q1i * 4, 256);
+    p.ws_wt = off;
+    if (p.path == PATH_SQ128)  // transposed copies of both factors
+      off = align_up(off + static_cast<size_t>(nb1 * p.q1o * p.q1i + nb2 * p.q2o * p.q2i) * 2, 256);
     p.ws_total = off;
   }
   *pr = p;
@@ -114,6 +117,7 @@ Plan plan_bwd(const Problem& pr) {
     return p;
   }
   if (pr.path == PATH_SQ128) {
+    p.add(SQ_TRANSPOSE_W);
     p.add(SQ_STAGE2_BWD_DATA);
     p.add(SQ_STAGE2_BWD_WEIGHT);
     p.add(SQ_STAGE1_BWD);
@@ -141,6 +145,7 @@ const char* step_name(StepKind k) {
     case REDUCE_DW2: return "reduce_dw2";
     case REDUCE_DW1: return "reduce_dw1";
     case ZERO_DW: return "zero_dw";
+    case SQ_TRANSPOSE_W: return "sq128_transpose_weights";
     case SQ_STAGE1_FWD: return "sq128_stage1_fwd";
     case SQ_STAGE2_FWD: return "sq128_stage2_fwd";
     case SQ_STAGE2_BWD_DATA: return "sq128_stage2_bwd_data";
@@ -157,6 +162,8 @@ hipError_t launch_step(StepKind k, const Problem& pr, const Buffers& b, hipStrea
   float* p2 = ws ? reinterpret_cast<float*>(ws + pr.ws_p2) : nullptr;
   float* p1 = ws ? reinterpret_cast<float*>(ws + pr.ws_p1) : nullptr;
   const void* mask = pr.act == MONARCH_ACT_RELU ? b.y : nullptr;
+  uint16_t* w1t = ws ? reinterpret_cast<uint16_t*>(ws + pr.ws_wt) : nullptr;
+  uint16_t* w2t = w1t ? w1t + pr.b1 * pr.q1o * pr.q1i : nullptr;
   GemmArgs a;
   switch (k) {
     case GEN_STAGE1_FWD:
@@ -216,17 +223,19 @@ hipError_t launch_step(StepKind k, const Problem& pr, const Buffers& b, hipStrea
       return launch_reduce_partials(p2, b.dw2, pr.b2 * pr.q2o * pr.q2i, pr.s2, bf16, s);
     case REDUCE_DW1:
       return launch_reduce_partials(p1, b.dw1, pr.b1 * pr.q1o * pr.q1i, pr.s1, bf16, s);
+    case SQ_TRANSPOSE_W:
+      return sq_launch_transpose_weights(b.w1, b.w2, w1t, w2t, pr.b1, s);
     case SQ_STAGE1_FWD:
       return sq_launch_stage1_fwd(b.x, b.w1, b.z_out, pr.batch, pr.b1, pr.sq, s);
     case SQ_STAGE2_FWD:
       return sq_launch_stage2_fwd(b.z_out, b.w2, b.y_out, pr.batch, pr.b2,
                                   pr.act == MONARCH_ACT_RELU, pr.sq, s);
     case SQ_STAGE2_BWD_DATA:
-      return sq_launch_stage2_bwd_data(b.dy, mask, b.w2, dz, pr.batch, pr.b2, pr.sq, s);
+      return sq_launch_stage2_bwd_data(b.dy, mask, w2t, dz, pr.batch, pr.b2, pr.sq, s);
     case SQ_STAGE2_BWD_WEIGHT:
       return sq_launch_stage2_bwd_weight(b.dy, mask, b.z, p2, pr.batch, pr.b2, pr.sq, s);
     case SQ_STAGE1_BWD:
-      return sq_launch_stage1_bwd(dz, b.x, b.w1, b.dx, p1, pr.batch, pr.b1, pr.sq, s);
+      return sq_launch_stage1_bwd(dz, b.x, w1t, b.dx, p1, pr.batch, pr.b1, pr.sq, s);
     case ZERO_DW: {
       hipError_t e = launch_zero(b.dw2, static_cast<size_t>(pr.b2 * pr.q2o * pr.q2i) * pr.esize, s);
       if (e != hipSuccess) return e;

@@ -14,24 +14,28 @@ struct SqPlan {
   int64_t b1_chunks = 0, b1_rows = 0;      // stage-1 backward: batch chunks
 };
 
-// True when the fast path covers the shape: bf16, in = out = 128*nb with
-// nb1 = nb2 = nb and nb a multiple of 8.
-bool sq_applicable(int64_t in, int64_t out, int64_t nb1, int64_t nb2, int dtype_bf16);
+// True when the fast path covers the problem: bf16, in = out = 128*nb with
+// nb1 = nb2 = nb, nb a multiple of 8, and batch*out < 2^31.
+bool sq_applicable(int64_t in, int64_t out, int64_t nb1, int64_t nb2, int64_t batch,
+                   int dtype_bf16);
 SqPlan sq_plan(int64_t batch, int64_t nb);
 
+// w1t/w2t = each 128x128 block of w1/w2 transposed (read by the backward kernels).
+hipError_t sq_launch_transpose_weights(const void* w1, const void* w2, void* w1t, void* w2t,
+                                      int64_t nb, hipStream_t s);
 // z / dz are in the panel layout: feature j of row b at ((j/8)*batch + b)*8 + j%8.
 hipError_t sq_launch_stage1_fwd(const void* x, const void* w1, void* z, int64_t batch, int64_t nb,
                                 const SqPlan& p, hipStream_t s);
 hipError_t sq_launch_stage2_fwd(const void* z, const void* w2, void* y, int64_t batch, int64_t nb,
                                 int relu, const SqPlan& p, hipStream_t s);
-hipError_t sq_launch_stage2_bwd_data(const void* dy, const void* ymask, const void* w2, void* dz,
+hipError_t sq_launch_stage2_bwd_data(const void* dy, const void* ymask, const void* w2t, void* dz,
                                      int64_t batch, int64_t nb, const SqPlan& p, hipStream_t s);
 // partial: [w2_chunks][nb][128][128] fp32
 hipError_t sq_launch_stage2_bwd_weight(const void* dy, const void* ymask, const void* z,
                                        float* partial, int64_t batch, int64_t nb, const SqPlan& p,
                                        hipStream_t s);
 // partial: [b1_chunks][nb][128][128] fp32
-hipError_t sq_launch_stage1_bwd(const void* dz, const void* x, const void* w1, void* dx,
+hipError_t sq_launch_stage1_bwd(const void* dz, const void* x, const void* w1t, void* dx,
                                 float* partial, int64_t batch, int64_t nb, const SqPlan& p,
                                 hipStream_t s);
 
