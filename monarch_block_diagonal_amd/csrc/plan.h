@@ -22,7 +22,7 @@ struct Problem {
   int64_t s2 = 1, kc2 = 0, s1 = 1, kc1 = 0;
   SqPlan sq;  // launch geometry of PATH_SQ128
   // workspace layout (byte offsets)
-  size_t ws_dz = 0, ws_p2 = 0, ws_p1 = 0, ws_wt = 0, ws_total = 0;
+  size_t ws_dz = 0, ws_p2 = 0, ws_p1 = 0, ws_wt = 0, ws_dv = 0, ws_total = 0;
 };
 
 struct Buffers {
@@ -51,6 +51,7 @@ enum StepKind {
   REDUCE_DW1,
   ZERO_DW,
   SQ_TRANSPOSE_W,
+  SQ_DV_PANELS,
   SQ_STAGE1_FWD,
   SQ_STAGE2_FWD,
   SQ_STAGE2_BWD_DATA,

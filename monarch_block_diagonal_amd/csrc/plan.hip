@@ -87,8 +87,12 @@ int make_problem(int64_t in, int64_t out, int64_t nb1, int64_t nb2, int64_t batc
     p.ws_p1 = off;
     off = align_up(off + static_cast<size_t>(p.s1) * nb1 * p.q1o * p.q1i * 4, 256);
     p.ws_wt = off;
-    if (p.path == PATH_SQ128)  // transposed copies of both factors
+    if (p.path == PATH_SQ128) {
+      // transposed copies of both factors, then the block-major dV panels
       off = align_up(off + static_cast<size_t>(nb1 * p.q1o * p.q1i + nb2 * p.q2o * p.q2i) * 2, 256);
+      p.ws_dv = off;
+      off = align_up(off + static_cast<size_t>(batch) * out * p.esize, 256);
+    }
     p.ws_total = off;
   }
   *pr = p;
@@ -118,6 +122,7 @@ Plan plan_bwd(const Problem& pr) {
   }
   if (pr.path == PATH_SQ128) {
     p.add(SQ_TRANSPOSE_W);
+    p.add(SQ_DV_PANELS);
     p.add(SQ_STAGE2_BWD_DATA);
     p.add(SQ_STAGE2_BWD_WEIGHT);
     p.add(SQ_STAGE1_BWD);
@@ -146,6 +151,7 @@ const char* step_name(StepKind k) {
     case REDUCE_DW1: return "reduce_dw1";
     case ZERO_DW: return "zero_dw";
     case SQ_TRANSPOSE_W: return "sq128_transpose_weights";
+    case SQ_DV_PANELS: return "sq128_dv_panels";
     case SQ_STAGE1_FWD: return "sq128_stage1_fwd";
     case SQ_STAGE2_FWD: return "sq128_stage2_fwd";
     case SQ_STAGE2_BWD_DATA: return "sq128_stage2_bwd_data";
@@ -164,6 +170,7 @@ hipError_t launch_step(StepKind k, const Problem& pr, const Buffers& b, hipStrea
   const void* mask = pr.act == MONARCH_ACT_RELU ? b.y : nullptr;
   uint16_t* w1t = ws ? reinterpret_cast<uint16_t*>(ws + pr.ws_wt) : nullptr;
   uint16_t* w2t = w1t ? w1t + pr.b1 * pr.q1o * pr.q1i : nullptr;
+  void* dv = ws ? ws + pr.ws_dv : nullptr;
   GemmArgs a;
   switch (k) {
     case GEN_STAGE1_FWD:
@@ -225,15 +232,17 @@ hipError_t launch_step(StepKind k, const Problem& pr, const Buffers& b, hipStrea
       return launch_reduce_partials(p1, b.dw1, pr.b1 * pr.q1o * pr.q1i, pr.s1, bf16, s);
     case SQ_TRANSPOSE_W:
       return sq_launch_transpose_weights(b.w1, b.w2, w1t, w2t, pr.b1, s);
+    case SQ_DV_PANELS:
+      return sq_launch_dv_panels(b.dy, mask, dv, pr.batch, pr.b2, s);
     case SQ_STAGE1_FWD:
       return sq_launch_stage1_fwd(b.x, b.w1, b.z_out, pr.batch, pr.b1, pr.sq, s);
     case SQ_STAGE2_FWD:
       return sq_launch_stage2_fwd(b.z_out, b.w2, b.y_out, pr.batch, pr.b2,
                                   pr.act == MONARCH_ACT_RELU, pr.sq, s);
     case SQ_STAGE2_BWD_DATA:
-      return sq_launch_stage2_bwd_data(b.dy, mask, w2t, dz, pr.batch, pr.b2, pr.sq, s);
+      return sq_launch_stage2_bwd_data(dv, w2t, dz, pr.batch, pr.b2, pr.sq, s);
     case SQ_STAGE2_BWD_WEIGHT:
-      return sq_launch_stage2_bwd_weight(b.dy, mask, b.z, p2, pr.batch, pr.b2, pr.sq, s);
+      return sq_launch_stage2_bwd_weight(dv, b.z, p2, pr.batch, pr.b2, pr.sq, s);
     case SQ_STAGE1_BWD:
       return sq_launch_stage1_bwd(dz, b.x, w1t, b.dx, p1, pr.batch, pr.b1, pr.sq, s);
     case ZERO_DW: {

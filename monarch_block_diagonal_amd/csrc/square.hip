@@ -1,5 +1,5 @@
 // Fast path for bf16 Monarch layers whose four block dimensions are all 128
-// (in = mid = out = 128*b, nblocks1 = nblocks2 = b, b a multiple of 8): the
+// (in = mid = out = 128*b, nblocks1 = nblocks2 = b, b a multiple of 32): the
 // square Definition C.3 family (scatterbrain issues page, "Definition C.3"
 // thread) at block size 128, e.g. n = 16384 with 128 blocks.
 //
@@ -10,17 +10,21 @@
 //  * The saved stage-2 input Z (and the backward's dZ) use a panel layout:
 //    feature j of row b sits at ((j/8)*B + b)*8 + j%8. A stage-1 kernel that
 //    owns one R block writes 16 whole panels (256-512 B runs); a stage-2
-//    kernel that owns 8 consecutive L blocks g0..g0+7 finds, for each t, its
-//    8 inputs Z[b, t*b2 + g0 .. +7] in one panel (the stride permutation of
-//    the "hypercube" thread becomes a panel index, no permuted copy exists).
-//  * The caller's row-major Y / dY put the 8 L blocks of a workgroup in one
-//    16-byte run per (row, p). The stage-2 workgroups that share those cache
-//    lines are mapped onto one XCD (workgroups are dispatched round-robin
-//    over the 8 XCDs) so partial lines merge in that XCD's L2.
+//    kernel that owns L blocks g0..g0+31 finds, for each t, its inputs
+//    Z[b, t*b2 + g0 .. +31] in 4 consecutive panels (the stride permutation
+//    of the "hypercube" thread becomes a panel index; no permuted copy).
+//  * The caller's row-major Y / dY hold the L blocks of one (row, p) side by
+//    side, so a workgroup that owns 32 blocks moves 64-byte runs there (16
+//    blocks: 32-byte runs for the weight gradient). Narrower runs cost up to
+//    2-3x in achieved bandwidth on this memory system. Workgroups that share
+//    cache lines are mapped onto one XCD (workgroups are dispatched
+//    round-robin over the 8 XCDs).
 //  * Weights stay in VGPRs for the whole launch (persistent workgroups over
 //    a row range); MFMA v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
 //  * Weight gradients accumulate in registers over a batch chunk per
 //    workgroup; chunks are summed afterwards in a fixed order.
+#include <type_traits>
+
 #include "common.h"
 #include "square.h"
 
@@ -88,6 +92,18 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 // minimum over its predecessors; without this, the prologue's issue order
 // would set them and drain both prefetch slots on every iteration.
 __device__ __forceinline__ void drain_prologue() { __builtin_amdgcn_s_waitcnt(0); }
+
+// 4x8 transpose of bf16 in registers: in[i] holds elements (i, e = 0..7);
+// out[e] gets elements (i = 0..3, e) packed into 8 bytes.
+__device__ __forceinline__ void transpose4x8(const u32x4 (&in)[4], u32x2 (&out)[8]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    out[2 * k][0] = (in[0][k] & 0xffffu) | (in[1][k] << 16);
+    out[2 * k][1] = (in[2][k] & 0xffffu) | (in[3][k] << 16);
+    out[2 * k + 1][0] = (in[0][k] >> 16) | (in[1][k] & 0xffff0000u);
+    out[2 * k + 1][1] = (in[2][k] >> 16) | (in[3][k] & 0xffff0000u);
+  }
+}
 
 __device__ __forceinline__ int clamp_row(int row, int64_t lim) {
   return row < lim ? row : static_cast<int>(lim - 1);
@@ -182,114 +198,202 @@ __global__ __launch_bounds__(256) void sq_stage1_fwd_kernel(const uint16_t* __re
 // --------------------------------------------------------------------------
 // stage 2 forward: Y[b, p*b2 + g] = act(sum_t L[g,p,t] Z[b, t*b2 + g])
 // --------------------------------------------------------------------------
-// 8 waves, 8 L blocks g0..g0+7 per workgroup; wave w owns block g0 + w with
-// all of L_g in VGPRs. Tile: 16 rows; two tiles of Z panels are in flight in
-// registers while a third is computed. Z panels -> LDS [g][row][t];
-// C = Vᵀ[p x b] = L[p x t] · Wᵀ[t x b]; results -> LDS [row][p][g] -> Y in
-// 16-byte runs.
+// Workgroup: 32 L blocks g0..g0+31 x a 32-wide slice of p x a row range, so
+// each (row, p) of Y gets a 64-byte run. 8 waves; wave w owns blocks
+// g0+4w..+3 for the 32 p of the slice (L fragments: 128 VGPRs). Row tile: 16
+// rows; the t contraction runs in 4 chunks of 32. Z chunk (32 t x 32 g x 16
+// rows) -> LDS [g][row][t] (double-buffered; the next chunk's panels are in
+// flight in registers). C = Vᵀ[p x b] = L[p x t] · Wᵀ[t x b]; after 4 chunks
+// the tile -> LDS [row][p][g] -> Y.
+constexpr int CLD = 32 + 8;          // pitch of [..][row][32] chunk tiles
+constexpr int Y2LD = 32 * 32 + 8;    // pitch of [row][32 p][32 g]
+
 __global__ __launch_bounds__(512) void sq_stage2_fwd_kernel(const uint16_t* __restrict__ Z,
                                                             const uint16_t* __restrict__ W2,
                                                             uint16_t* __restrict__ Y, int64_t B,
                                                             int nb2, int64_t rows_per, int relu) {
   constexpr int T = 16;
-  __shared__ __attribute__((aligned(16))) uint16_t ws[8 * T * XLD];
-  __shared__ __attribute__((aligned(16))) uint16_t ys[T * YLD];
-  const int n_groups = nb2 >> 3;
+  __shared__ __attribute__((aligned(16))) uint16_t zs[2][32 * T * CLD];
+  __shared__ __attribute__((aligned(16))) uint16_t ys[T * Y2LD];
+  const int n_gq = nb2 >> 5;
   const int logical = xcd_logical(blockIdx.x, gridDim.x);
-  const int gg = logical % n_groups;
-  const int64_t row0 = static_cast<int64_t>(logical / n_groups) * rows_per;
+  const int ps = logical & 3;
+  const int gq = (logical >> 2) % n_gq;
+  const int64_t row0 = static_cast<int64_t>((logical >> 2) / n_gq) * rows_per;
   const int64_t row1 = row0 + rows_per < B ? row0 + rows_per : B;
   if (row0 >= row1) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l15 = lane & 15, lh = lane >> 4;
-  const int g = gg * 8 + w;
   const uint32_t out = static_cast<uint32_t>(nb2) * Q;
   const uint32_t Bu = static_cast<uint32_t>(B);
   const uint32_t pstride = nb2 >> 3;  // panels between t and t+1
 
-  bf16x8 a[8][4];
-  const uint16_t* Lg = W2 + static_cast<int64_t>(g) * Q * Q;
+  // a[g][mt][ks] = L[g0+4w+g][p = 32ps + 16mt + l15][t = 32ks + 8lh ..]
+  bf16x8 a[4][2][4];
 #pragma unroll
-  for (int mt = 0; mt < 8; ++mt)
+  for (int g = 0; g < 4; ++g) {
+    const uint16_t* Lg = W2 + static_cast<int64_t>(gq * 32 + 4 * w + g) * Q * Q;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) a[mt][ks] = frag_ld(Lg + (16 * mt + l15) * Q + 32 * ks + 8 * lh);
+    for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        a[g][mt][ks] = frag_ld(Lg + (32 * ps + 16 * mt + l15) * Q + 32 * ks + 8 * lh);
+  }
 
-  // Z pieces: t = (tid>>4) + 32i, row = tid&15; Y pieces: row = (tid>>7) + 4i, p = tid&127
-  const int zt = tid >> 4, zrow = tid & 15;
-  const uint32_t zcol = (zt * pstride + gg) * Bu * 8;
-  const uint32_t zstep = 32 * pstride * Bu * 8;
-  const int yrow = tid >> 7, yp = tid & 127;
-  const uint32_t ycol = yp * nb2 + gg * 8;
+  // chunk pieces: thread (row = tid&15, q4 = (tid>>4)&3, tq = tid>>6) loads
+  // t = 4tq + i, i < 4 (consecutive lanes: consecutive rows of one panel)
+  const int crow = tid & 15, cq4 = (tid >> 4) & 3, ctq = tid >> 6;
+  const uint32_t ccol = (4 * ctq * pstride + gq * 4 + cq4) * Bu * 8;
+  const uint32_t cstep = pstride * Bu * 8;   // +1 t
+  // Y pieces: id = tid + 512i: q4 = id&3, pl = (id>>2)&31, row = id>>7 (+4i)
+  const int yq4 = tid & 3, ypl = (tid >> 2) & 31, yrow = tid >> 7;
+  const uint32_t ycol = (32 * ps + ypl) * nb2 + gq * 32 + yq4 * 8;
 
-  auto gload = [&](u32x4(&pre)[4], int64_t b0) {
+  // chunk c of the row range: tile c>>2, t chunk c&3
+  auto gload = [&](u32x4(&pre)[4], int64_t c) {
+    const int64_t b0 = row0 + (c >> 2) * T;
     const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
-    const uint16_t* base = Z + bc * 8 + clamp_row(zrow, lim) * 8;
+    const uint16_t* base = Z + bc * 8 + clamp_row(crow, lim) * 8 + ccol +
+                           static_cast<uint32_t>(c & 3) * 32 * pstride * Bu * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pre[i] = ldg16(base + zcol + i * zstep);
+    for (int i = 0; i < 4; ++i) pre[i] = ldg16(base + i * cstep);
   };
-  auto body = [&](u32x4(&cur)[4], int64_t b0) {
+  auto scatter = [&](const u32x4(&pre)[4], uint16_t* buf) {
+    u32x2 tr[8];
+    transpose4x8(pre, tr);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) ws[(e * T + zrow) * XLD + zt + 32 * i] = half_of(cur[i], e);
+    for (int e = 0; e < 8; ++e)
+      *reinterpret_cast<u32x2*>(&buf[((cq4 * 8 + e) * T + crow) * CLD + 4 * ctq]) = tr[e];
+  };
+
+  f32x4 acc[4][2];
+  const int64_t ntiles = (row1 - row0 + T - 1) / T;
+  const int64_t nchunks = ntiles * 4;
+  u32x4 pa[4], pb[4];
+  gload(pa, 0);
+  gload(pb, 1);
+  drain_prologue();
+  auto step = [&](auto tcc, u32x4(&cur)[4], int64_t tile, uint16_t* buf) {
+    constexpr int tc = decltype(tcc)::value;
+    const int64_t c = tile * 4 + tc;
+    scatter(cur, buf);
     __syncthreads();
-    gload(cur, b0 + 2 * T);
-    f32x4 acc[8];
+    gload(cur, c + 2 < nchunks ? c + 2 : nchunks - 1);
+    if constexpr (tc == 0) {
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt) acc[mt] = zero4();
+      for (int g = 0; g < 4; ++g)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 bop = frag_ld(&ws[(w * T + l15) * XLD + 32 * ks + 8 * lh]);
-#pragma unroll
-      for (int mt = 0; mt < 8; ++mt) acc[mt] = mfma(a[mt][ks], bop, acc[mt]);
+        for (int mt = 0; mt < 2; ++mt) acc[g][mt] = zero4();
     }
 #pragma unroll
-    for (int mt = 0; mt < 8; ++mt)
+    for (int g = 0; g < 4; ++g) {
+      const bf16x8 bop = frag_ld(&buf[((4 * w + g) * T + l15) * CLD + 8 * lh]);
 #pragma unroll
-      for (int v = 0; v < 4; v += 2) {
-        float v0 = acc[mt][v], v1 = acc[mt][v + 1];
-        if (relu) {
-          v0 = v0 > 0.f ? v0 : 0.f;
-          v1 = v1 > 0.f ? v1 : 0.f;
-        }
-        const uint32_t pk = pack_bf16x2(v0, v1);
-        ys[l15 * YLD + (16 * mt + 4 * lh + v) * 8 + w] = static_cast<uint16_t>(pk & 0xffffu);
-        ys[l15 * YLD + (16 * mt + 4 * lh + v + 1) * 8 + w] = static_cast<uint16_t>(pk >> 16);
-      }
-    __syncthreads();
-    const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
-    uint16_t* yb = Y + bc * out + ycol;
+      for (int mt = 0; mt < 2; ++mt) acc[g][mt] = mfma(a[g][mt][tc], bop, acc[g][mt]);
+    }
+    if constexpr (tc == 3) {
+      // tile done: results -> ys[row][p][g], then Y
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-      stg16(yb + clamp_row(yrow + 4 * i, lim) * out,
-            *reinterpret_cast<const u32x4*>(&ys[(yrow + 4 * i) * YLD + yp * 8]));
+      for (int g = 0; g < 4; ++g)
+#pragma unroll
+        for (int mt = 0; mt < 2; ++mt)
+#pragma unroll
+          for (int v = 0; v < 4; v += 2) {
+            float v0 = acc[g][mt][v], v1 = acc[g][mt][v + 1];
+            if (relu) {
+              v0 = v0 > 0.f ? v0 : 0.f;
+              v1 = v1 > 0.f ? v1 : 0.f;
+            }
+            const uint32_t pk = pack_bf16x2(v0, v1);
+            const int pl = 16 * mt + 4 * lh + v;
+            ys[l15 * Y2LD + pl * 32 + 4 * w + g] = static_cast<uint16_t>(pk & 0xffffu);
+            ys[l15 * Y2LD + (pl + 1) * 32 + 4 * w + g] = static_cast<uint16_t>(pk >> 16);
+          }
+      __syncthreads();
+      const int64_t b0 = row0 + tile * T;
+      const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
+      uint16_t* yb = Y + bc * out + ycol;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        stg16(yb + clamp_row(yrow + 4 * i, lim) * out,
+              *reinterpret_cast<const u32x4*>(&ys[(yrow + 4 * i) * Y2LD + ypl * 32 + yq4 * 8]));
+    }
   };
-
-  const int64_t npairs = (row1 - row0 + 2 * T - 1) / (2 * T);
-  u32x4 pa[4], pb[4];
-  gload(pa, row0);
-  gload(pb, row0 + T);
-  drain_prologue();
-  for (int64_t k = 0; k < npairs; ++k) {
-    body(pa, row0 + 2 * k * T);
-    body(pb, row0 + (2 * k + 1) * T);
+  for (int64_t tile = 0; tile < ntiles; ++tile) {
+    step(std::integral_constant<int, 0>{}, pa, tile, zs[0]);
+    step(std::integral_constant<int, 1>{}, pb, tile, zs[1]);
+    step(std::integral_constant<int, 2>{}, pa, tile, zs[0]);
+    step(std::integral_constant<int, 3>{}, pb, tile, zs[1]);
   }
 }
 
 // --------------------------------------------------------------------------
-// stage 2 backward, data: dZ[b, t*b2 + g] = sum_p dYe[b, p*b2 + g] L[g,p,t]
+// dV panels: dV[b, g*128 + p] = dYe[b, p*b2 + g]  (block-major gradient of
+// stage 2's output; dYe = dY masked by Y > 0 after a fused ReLU)
 // --------------------------------------------------------------------------
-// Same tiling and pipeline as the forward; wave w owns block g0 + w.
-// dY (masked) -> LDS [g][row][p]; C = dZᵀ[t x b] = Lᵀ[t x p] · dVᵀ[p x b];
-// results -> LDS [t][row][g] -> dZ panels (256 B per t). The ReLU mask is
-// read when a tile is consumed, not prefetched.
-template <bool MASK>
+// The inverse stride permutation scatters one L block's outputs with stride
+// b2 through each row of Y, so a kernel owning a few blocks would read dY in
+// short runs. This pass reads dY rows in 256-byte runs (all blocks of 16 p at
+// once), transposes 8x8 bf16 blocks in registers and writes the panel layout
+// ((i/8)*B + b)*8 + i%8, i = g*128 + p, through LDS in 256-byte runs. Both
+// backward stage-2 kernels then read dV contiguously.
+// Tile: RT = 256/GO rows x 16 p x 8*GO blocks (GO = min(16, b2/8) block
+// octets); 512 threads, one 8x8 block each; one tile per workgroup.
+__global__ __launch_bounds__(512) void sq_dv_panels_kernel(const uint16_t* __restrict__ dY,
+                                                           const uint16_t* __restrict__ Ym,
+                                                           uint16_t* __restrict__ dV, int64_t B,
+                                                           int nb2) {
+  __shared__ __attribute__((aligned(16))) u32x4 st[4096];   // [g][po][row] 16-byte pieces
+  const int GO = nb2 >= 128 ? 16 : nb2 >> 3;
+  const int RT = 256 / GO;
+  const int n_gt = nb2 / (8 * GO);            // block groups per row
+  int bid = blockIdx.x;
+  const int gt = bid % n_gt;
+  bid /= n_gt;
+  const int pt = bid & 7;                     // 16-p tile
+  const int64_t b0 = static_cast<int64_t>(bid >> 3) * RT;
+  const int tid = threadIdx.x;
+  const int go = tid % GO, po = (tid / GO) & 1, row = tid / (2 * GO);
+  const uint32_t out = static_cast<uint32_t>(nb2) * Q;
+  const int64_t b = b0 + row < B ? b0 + row : B - 1;
+  const int64_t src = b * out + static_cast<int64_t>(16 * pt + 8 * po) * nb2 + (gt * GO + go) * 8;
+  u32x4 in[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) in[i] = ldg16(dY + src + i * nb2);
+  if (Ym) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) in[i] = apply_mask(in[i], ldg16(Ym + src + i * nb2));
+  }
+  u32x2 lo[8], hi[8];
+  transpose4x8(*reinterpret_cast<const u32x4(*)[4]>(&in[0]), lo);
+  transpose4x8(*reinterpret_cast<const u32x4(*)[4]>(&in[4]), hi);
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    st[((go * 8 + e) * 2 + po) * RT + row] = u32x4{lo[e][0], lo[e][1], hi[e][0], hi[e][1]};
+  __syncthreads();
+  const int n_pieces = 8 * GO * 2 * RT;   // 4096
+  for (int id = tid; id < n_pieces; id += 512) {
+    const int r = id % RT, q = (id / RT) & 1, gl = id / (2 * RT);
+    const int64_t bb = b0 + r;
+    if (bb < B) {
+      const int64_t panel = static_cast<int64_t>(gt * GO * 8 + gl) * 16 + 2 * pt + q;
+      stg16(dV + (panel * B + bb) * 8, st[(gl * 2 + q) * RT + r]);
+    }
+  }
+}
+
+// --------------------------------------------------------------------------
+// stage 2 backward, data: dZ[b, t*b2 + g] = sum_p dV[b, g*128 + p] L[g,p,t]
+// --------------------------------------------------------------------------
+// 8 waves, 8 L blocks g0..g0+7 per workgroup; wave w owns block g0 + w (all
+// t, Lᵀ fragments from the transposed copy: 128 VGPRs). Tile: 16 rows; the
+// MFMA B operands (dV_g[b][8 p]) are 16-byte pieces of the dV panels, loaded
+// straight into registers two tiles ahead. C = dZᵀ[t x b] = Lᵀ[t x p] ·
+// dVᵀ[p x b]; results -> LDS [t][row][g] -> dZ panels (256-byte runs).
 __global__ __launch_bounds__(512) void sq_stage2_bwd_data_kernel(
-    const uint16_t* __restrict__ dY, const uint16_t* __restrict__ Ym,
-    const uint16_t* __restrict__ W2t, uint16_t* __restrict__ dZ, int64_t B, int nb2,
-    int64_t rows_per) {
+    const uint16_t* __restrict__ dV, const uint16_t* __restrict__ W2t,
+    uint16_t* __restrict__ dZ, int64_t B, int nb2, int64_t rows_per) {
   constexpr int T = 16;
-  __shared__ __attribute__((aligned(16))) uint16_t dvs[8 * T * XLD];
   __shared__ __attribute__((aligned(16))) uint16_t zs[Q * XLD];
   const int n_groups = nb2 >> 3;
   const int logical = xcd_logical(blockIdx.x, gridDim.x);
@@ -300,11 +404,10 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_data_kernel(
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l15 = lane & 15, lh = lane >> 4;
   const int g = gg * 8 + w;
-  const uint32_t out = static_cast<uint32_t>(nb2) * Q;
   const uint32_t Bu = static_cast<uint32_t>(B);
   const uint32_t pstride = nb2 >> 3;
 
-  // A = Lᵀ[t x p] from the transposed copy: lane holds L[g][p = 32ks + 8lh + e][t = 16mt + l15]
+  // A = Lᵀ[t x p]: lane holds L[g][p = 32ks + 8lh + e][t = 16mt + l15]
   bf16x8 a[8][4];
   const uint16_t* Ltg = W2t + static_cast<int64_t>(g) * Q * Q;
 #pragma unroll
@@ -312,41 +415,32 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_data_kernel(
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) a[mt][ks] = frag_ld(Ltg + (16 * mt + l15) * Q + 32 * ks + 8 * lh);
 
-  // dY pieces: row = (tid>>7) + 4i, p = tid&127; dZ pieces: t = (tid>>4) + 32i, row = tid&15
-  const int drow = tid >> 7, dp = tid & 127;
-  const uint32_t dcol = dp * nb2 + gg * 8;
+  // operand pieces: panel g*16 + 4ks + lh, row b0 + l15
+  const uint32_t vcol = ((g * 16 + lh) * Bu) * 8;
+  const uint32_t vstep = 4 * Bu * 8;   // +4 panels (next k step)
+  // dZ pieces: t = (tid>>4) + 32i, row = tid&15
   const int zt = tid >> 4, zrow = tid & 15;
   const uint32_t zcol = (zt * pstride + gg) * Bu * 8;
   const uint32_t zstep = 32 * pstride * Bu * 8;
 
   auto gload = [&](u32x4(&pre)[4], int64_t b0) {
     const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
-    const uint16_t* base = dY + bc * out + dcol;
+    const uint16_t* base = dV + bc * 8 + clamp_row(l15, lim) * 8 + vcol;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pre[i] = ldg16(base + clamp_row(drow + 4 * i, lim) * out);
+    for (int ks = 0; ks < 4; ++ks) pre[ks] = ldg16(base + ks * vstep);
   };
   auto body = [&](u32x4(&cur)[4], int64_t b0) {
-    if constexpr (MASK) {
-      const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
-      const uint16_t* mb = Ym + bc * out + dcol;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) cur[i] = apply_mask(cur[i], ldg16(mb + clamp_row(drow + 4 * i, lim) * out));
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) dvs[(e * T + drow + 4 * i) * XLD + dp] = half_of(cur[i], e);
-    __syncthreads();
-    gload(cur, b0 + 2 * T);
     f32x4 acc[8];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) acc[mt] = zero4();
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      const bf16x8 bop = frag_ld(&dvs[(w * T + l15) * XLD + 32 * ks + 8 * lh]);
+      bf16x8 bop;
+      __builtin_memcpy(&bop, &cur[ks], sizeof(bop));
 #pragma unroll
       for (int mt = 0; mt < 8; ++mt) acc[mt] = mfma(a[mt][ks], bop, acc[mt]);
     }
+    gload(cur, b0 + 2 * T);
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
@@ -361,6 +455,7 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_data_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       stg16(zb + i * zstep, *reinterpret_cast<const u32x4*>(&zs[(zt + 32 * i) * XLD + zrow * 8]));
+    __syncthreads();
   };
 
   const int64_t npairs = (row1 - row0 + 2 * T - 1) / (2 * T);
@@ -375,19 +470,18 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_data_kernel(
 }
 
 // --------------------------------------------------------------------------
-// stage 2 backward, weights: dL[g,p,t] = sum_b dYe[b, p*b2+g] Z[b, t*b2+g]
+// stage 2 backward, weights: dL[g,p,t] = sum_b dV[b, g*128 + p] Z[b, t*b2 + g]
 // --------------------------------------------------------------------------
 // Workgroup: 8 L blocks x a 32-wide slice of p x a batch chunk. 8 waves;
-// wave w owns block g0 + w, accumulators dL[32 p x 128 t] in VGPRs. Tile: 32
-// rows = one K step; two tiles in flight in registers. dY slice -> LDS
-// [g][p][row], Z panels -> LDS [g][t][row] (row-contiguous operands for
-// K = batch). Rows past the range enter as zero dY. The chunk's sum is
-// written as an fp32 partial.
-template <bool MASK>
+// wave w owns block g0 + w with accumulators dL[32 p x 128 t] in VGPRs. Tile:
+// 32 rows = one K step; the next tile's panels are in flight in registers.
+// Both operands need consecutive rows per lane (K = batch): dV panels ->
+// LDS [g][p][row] through 2x8 register transposes, Z panels -> LDS
+// [g][t][row] through 4x8 transposes. The chunk's sum is written as an fp32
+// partial.
 __global__ __launch_bounds__(512) void sq_stage2_bwd_weight_kernel(
-    const uint16_t* __restrict__ dY, const uint16_t* __restrict__ Ym,
-    const uint16_t* __restrict__ Z, float* __restrict__ partial, int64_t B, int nb2,
-    int64_t rows_per) {
+    const uint16_t* __restrict__ dV, const uint16_t* __restrict__ Z, float* __restrict__ partial,
+    int64_t B, int nb2, int64_t rows_per) {
   constexpr int T = 32;
   __shared__ __attribute__((aligned(16))) uint16_t dvs[8 * 32 * TLD];
   __shared__ __attribute__((aligned(16))) uint16_t zst[8 * Q * TLD];
@@ -400,8 +494,6 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_weight_kernel(
   const int64_t row1 = row0 + rows_per < B ? row0 + rows_per : B;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l15 = lane & 15, lh = lane >> 4;
-  const int g = gg * 8 + w;
-  const uint32_t out = static_cast<uint32_t>(nb2) * Q;
   const uint32_t Bu = static_cast<uint32_t>(B);
   const uint32_t pstride = nb2 >> 3;
 
@@ -411,39 +503,47 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_weight_kernel(
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = zero4();
 
-  // dY slice: row = (tid>>5) + 16i, pl = tid&31 (i < 2); Z: t = (tid>>5) + 16i, row = tid&31 (i < 8)
-  const int hi = tid >> 5, lo = tid & 31;
-  const uint32_t dcol = (32 * ps + lo) * nb2 + gg * 8;
-  const uint32_t zcol = (hi * pstride + gg) * Bu * 8;
-  const uint32_t zstep = 16 * pstride * Bu * 8;
+  // dV: thread (rp = tid&15, po = (tid>>4)&3, gl = tid>>6) loads rows 2rp, 2rp+1
+  // of panel (g0+gl)*16 + 4ps + po
+  const int vrp = tid & 15, vpo = (tid >> 4) & 3, vgl = tid >> 6;
+  const uint32_t vcol = ((gg * 8 + vgl) * 16 + 4 * ps + vpo) * Bu * 8;
+  // Z: thread (rq = tid&7, tl = tid>>3) loads rows 4rq..4rq+3 of t = tl + 64j
+  const int zrq = tid & 7, ztl = tid >> 3;
+  const uint32_t zcol = (ztl * pstride + gg) * Bu * 8;
+  const uint32_t zstep = 64 * pstride * Bu * 8;
 
-  auto gload = [&](u32x4(&pd)[2], u32x4(&pz)[8], int64_t b0) {
+  auto gload = [&](u32x4(&pv)[2], u32x4(&pz)[8], int64_t b0) {
     const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
-    const uint16_t* db = dY + bc * out + dcol;
+    const uint16_t* vb = dV + bc * 8 + vcol;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      pd[i] = zero_unless(b0 + hi + 16 * i < row1, ldg16(db + clamp_row(hi + 16 * i, lim) * out));
-    const uint16_t* zb = Z + bc * 8 + clamp_row(lo, lim) * 8 + zcol;
+      pv[i] = zero_unless(b0 + 2 * vrp + i < row1, ldg16(vb + clamp_row(2 * vrp + i, lim) * 8));
+    const uint16_t* zb = Z + bc * 8 + zcol;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) pz[i] = ldg16(zb + i * zstep);
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) pz[4 * j + i] = ldg16(zb + j * zstep + clamp_row(4 * zrq + i, lim) * 8);
   };
-  auto body = [&](u32x4(&pd)[2], u32x4(&pz)[8], int64_t b0) {
-    if constexpr (MASK) {
-      const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
-      const uint16_t* mb = Ym + bc * out + dcol;
+  auto body = [&](u32x4(&pv)[2], u32x4(&pz)[8], int64_t b0) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i) pd[i] = apply_mask(pd[i], ldg16(mb + clamp_row(hi + 16 * i, lim) * out));
+    for (int k = 0; k < 4; ++k) {
+      // rows 2rp, 2rp+1 of p = 8po + 2k (lo halves) and 8po + 2k + 1 (hi halves)
+      const uint32_t even = (pv[0][k] & 0xffffu) | (pv[1][k] << 16);
+      const uint32_t odd = (pv[0][k] >> 16) | (pv[1][k] & 0xffff0000u);
+      *reinterpret_cast<uint32_t*>(&dvs[(vgl * 32 + 8 * vpo + 2 * k) * TLD + 2 * vrp]) = even;
+      *reinterpret_cast<uint32_t*>(&dvs[(vgl * 32 + 8 * vpo + 2 * k + 1) * TLD + 2 * vrp]) = odd;
     }
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int j = 0; j < 2; ++j) {
+      const u32x4 blk[4] = {pz[4 * j], pz[4 * j + 1], pz[4 * j + 2], pz[4 * j + 3]};
+      u32x2 tr[8];
+      transpose4x8(blk, tr);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) dvs[(e * 32 + lo) * TLD + hi + 16 * i] = half_of(pd[i], e);
-#pragma unroll
-    for (int i = 0; i < 8; ++i)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) zst[(e * Q + hi + 16 * i) * TLD + lo] = half_of(pz[i], e);
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<u32x2*>(&zst[(e * Q + ztl + 64 * j) * TLD + 4 * zrq]) = tr[e];
+    }
     __syncthreads();
-    gload(pd, pz, b0 + 2 * T);
+    gload(pv, pz, b0 + T);
     bf16x8 A[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) A[mt] = frag_ld(&dvs[(w * 32 + 16 * mt + l15) * TLD + 8 * lh]);
@@ -457,18 +557,14 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_weight_kernel(
   };
 
   if (row0 < row1) {
-    const int64_t npairs = (row1 - row0 + 2 * T - 1) / (2 * T);
-    u32x4 da[2], za[8], db[2], zb[8];
-    gload(da, za, row0);
-    gload(db, zb, row0 + T);
+    const int64_t ntiles = (row1 - row0 + T - 1) / T;
+    u32x4 pv[2], pz[8];
+    gload(pv, pz, row0);
     drain_prologue();
-    for (int64_t k = 0; k < npairs; ++k) {
-      body(da, za, row0 + 2 * k * T);
-      body(db, zb, row0 + (2 * k + 1) * T);
-    }
+    for (int64_t k = 0; k < ntiles; ++k) body(pv, pz, row0 + k * T);
   }
   // partial[chunk][g][p][t]
-  float* P = partial + (static_cast<int64_t>(chunk) * nb2 + g) * Q * Q;
+  float* P = partial + (static_cast<int64_t>(chunk) * nb2 + gg * 8 + w) * Q * Q;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -606,7 +702,7 @@ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > h
 bool sq_applicable(int64_t in, int64_t out, int64_t nb1, int64_t nb2, int64_t batch,
                    int dtype_bf16) {
   if (!dtype_bf16) return false;
-  if (nb1 != nb2 || nb2 % 8 != 0) return false;
+  if (nb1 != nb2 || nb2 % 32 != 0) return false;
   if (in != nb1 * Q || out != nb2 * Q) return false;
   // 32-bit element offsets inside the kernels
   return batch * out < (int64_t(1) << 31);
@@ -614,17 +710,21 @@ bool sq_applicable(int64_t in, int64_t out, int64_t nb1, int64_t nb2, int64_t ba
 
 SqPlan sq_plan(int64_t batch, int64_t nb) {
   SqPlan p;
-  const int64_t groups = nb / 8;
+  const int64_t groups = nb / 32;   // 32-block groups of the stage-2 kernels
   // stage-1 forward: ~2048 workgroups of single blocks
   p.fwd1_chunks = clamp64(2048 / nb, 1, cdiv(batch, 32));
   p.fwd1_rows = round_up(cdiv(batch, p.fwd1_chunks), 32);
   p.fwd1_chunks = cdiv(batch, p.fwd1_rows);
-  // stage-2 kernels: one 1024-thread workgroup per CU (256 CUs)
-  p.s2_ranges = clamp64(256 / groups, 1, cdiv(batch, 16));
+  // stage-2 data kernels: groups x 4 slices x row ranges ~ one workgroup per CU
+  p.s2_ranges = clamp64(256 / (groups * 4), 1, cdiv(batch, 16));
   p.s2_rows = round_up(cdiv(batch, p.s2_ranges), 16);
   p.s2_ranges = cdiv(batch, p.s2_rows);
-  // stage-2 weight gradient: groups x 4 p slices x chunks ~ 256 workgroups
-  p.w2_chunks = clamp64(256 / (groups * 4), 1, cdiv(batch, 32));
+  // stage-2 backward data: nb/8 block groups x row ranges ~ one workgroup per CU
+  p.d2_ranges = clamp64(256 / (nb / 8), 1, cdiv(batch, 16));
+  p.d2_rows = round_up(cdiv(batch, p.d2_ranges), 16);
+  p.d2_ranges = cdiv(batch, p.d2_rows);
+  // stage-2 weight gradient: nb/8 block groups x 4 p slices x chunks ~ 256
+  p.w2_chunks = clamp64(256 / (nb / 8 * 4), 1, cdiv(batch, 32));
   p.w2_rows = round_up(cdiv(batch, p.w2_chunks), 32);
   p.w2_chunks = cdiv(batch, p.w2_rows);
   // stage-1 backward: 2 workgroups of 8 waves per CU
@@ -653,43 +753,39 @@ hipError_t sq_launch_stage1_fwd(const void* x, const void* w1, void* z, int64_t 
 
 hipError_t sq_launch_stage2_fwd(const void* z, const void* w2, void* y, int64_t batch, int64_t nb,
                                 int relu, const SqPlan& p, hipStream_t s) {
-  hipLaunchKernelGGL(sq_stage2_fwd_kernel, dim3(static_cast<unsigned>(nb / 8 * p.s2_ranges)),
+  hipLaunchKernelGGL(sq_stage2_fwd_kernel, dim3(static_cast<unsigned>(nb / 32 * 4 * p.s2_ranges)),
                      dim3(512), 0, s, static_cast<const uint16_t*>(z),
                      static_cast<const uint16_t*>(w2), static_cast<uint16_t*>(y), batch,
                      static_cast<int>(nb), p.s2_rows, relu);
   return hipGetLastError();
 }
 
-hipError_t sq_launch_stage2_bwd_data(const void* dy, const void* ymask, const void* w2, void* dz,
-                                     int64_t batch, int64_t nb, const SqPlan& p, hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(nb / 8 * p.s2_ranges));
-  if (ymask)
-    hipLaunchKernelGGL(sq_stage2_bwd_data_kernel<true>, grid, dim3(512), 0, s,
-                       static_cast<const uint16_t*>(dy), static_cast<const uint16_t*>(ymask),
-                       static_cast<const uint16_t*>(w2), static_cast<uint16_t*>(dz), batch,
-                       static_cast<int>(nb), p.s2_rows);
-  else
-    hipLaunchKernelGGL(sq_stage2_bwd_data_kernel<false>, grid, dim3(512), 0, s,
-                       static_cast<const uint16_t*>(dy), static_cast<const uint16_t*>(ymask),
-                       static_cast<const uint16_t*>(w2), static_cast<uint16_t*>(dz), batch,
-                       static_cast<int>(nb), p.s2_rows);
+hipError_t sq_launch_dv_panels(const void* dy, const void* ymask, void* dv, int64_t batch,
+                               int64_t nb, hipStream_t s) {
+  const int64_t GO = nb >= 128 ? 16 : nb / 8;
+  const int64_t RT = 256 / GO;
+  const int64_t grid = cdiv(batch, RT) * 8 * (nb / (8 * GO));
+  hipLaunchKernelGGL(sq_dv_panels_kernel, dim3(static_cast<unsigned>(grid)), dim3(512), 0, s,
+                     static_cast<const uint16_t*>(dy), static_cast<const uint16_t*>(ymask),
+                     static_cast<uint16_t*>(dv), batch, static_cast<int>(nb));
   return hipGetLastError();
 }
 
-hipError_t sq_launch_stage2_bwd_weight(const void* dy, const void* ymask, const void* z,
-                                       float* partial, int64_t batch, int64_t nb, const SqPlan& p,
-                                       hipStream_t s) {
-  const dim3 grid(static_cast<unsigned>(nb / 8 * 4 * p.w2_chunks));
-  if (ymask)
-    hipLaunchKernelGGL(sq_stage2_bwd_weight_kernel<true>, grid, dim3(512), 0, s,
-                       static_cast<const uint16_t*>(dy), static_cast<const uint16_t*>(ymask),
-                       static_cast<const uint16_t*>(z), partial, batch, static_cast<int>(nb),
-                       p.w2_rows);
-  else
-    hipLaunchKernelGGL(sq_stage2_bwd_weight_kernel<false>, grid, dim3(512), 0, s,
-                       static_cast<const uint16_t*>(dy), static_cast<const uint16_t*>(ymask),
-                       static_cast<const uint16_t*>(z), partial, batch, static_cast<int>(nb),
-                       p.w2_rows);
+hipError_t sq_launch_stage2_bwd_data(const void* dv, const void* w2t, void* dz, int64_t batch,
+                                     int64_t nb, const SqPlan& p, hipStream_t s) {
+  hipLaunchKernelGGL(sq_stage2_bwd_data_kernel, dim3(static_cast<unsigned>(nb / 8 * p.d2_ranges)),
+                     dim3(512), 0, s, static_cast<const uint16_t*>(dv),
+                     static_cast<const uint16_t*>(w2t), static_cast<uint16_t*>(dz), batch,
+                     static_cast<int>(nb), p.d2_rows);
+  return hipGetLastError();
+}
+
+hipError_t sq_launch_stage2_bwd_weight(const void* dv, const void* z, float* partial,
+                                       int64_t batch, int64_t nb, const SqPlan& p, hipStream_t s) {
+  hipLaunchKernelGGL(sq_stage2_bwd_weight_kernel,
+                     dim3(static_cast<unsigned>(nb / 8 * 4 * p.w2_chunks)), dim3(512), 0, s,
+                     static_cast<const uint16_t*>(dv), static_cast<const uint16_t*>(z), partial,
+                     batch, static_cast<int>(nb), p.w2_rows);
   return hipGetLastError();
 }
 

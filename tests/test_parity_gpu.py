@@ -241,11 +241,15 @@ SHAPES = [
     (2048, 2048, 16, 16, 129),
     (4096, 4096, 64, 64, 65),
     (16384, 16384, 128, 128, 96),
-    # 128x128 blocks with a multiple of 8 blocks: the bf16 fast path
-    (1024, 1024, 8, 8, 1),
+    # 128x128 blocks with a multiple of 32 blocks: the bf16 fast path
+    (4096, 4096, 32, 32, 1),
+    (4096, 4096, 32, 32, 200),
+    (8192, 8192, 64, 64, 77),
+    (16384, 16384, 128, 128, 1000),
+    (16384, 16384, 128, 128, 17),
+    # 128x128 blocks, fewer blocks: generic path
     (1024, 1024, 8, 8, 77),
     (2048, 2048, 16, 16, 129),
-    (16384, 16384, 128, 128, 1000),
     (768, 3072, 4, 4, 100),
     (250, 100, 5, 2, 45),
     (36, 36, 6, 6, 17),
@@ -264,7 +268,7 @@ def test_shapes(api, shape, dtype):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("shape", [(256, 256, 16, 16, 300), (96, 160, 4, 8, 50),
                                    (16384, 16384, 128, 128, 64), (1024, 512, 16, 16, 100),
-                                   (2048, 2048, 16, 16, 45)],
+                                   (2048, 2048, 16, 16, 45), (4096, 4096, 32, 32, 45)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_shapes_relu(api, shape, dtype):
     inp, out, b1, b2, batch = shape
@@ -279,6 +283,7 @@ def test_shapes_relu(api, shape, dtype):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("shape", [(16, 16, 4, 4, 8), (1024, 1024, 32, 32, 300),
                                    (16384, 16384, 128, 128, 64), (256, 256, 16, 16, 100),
+                                   (4096, 4096, 32, 32, 33),
                                    (48, 96, 2, 4, 10)], ids=lambda s: "x".join(map(str, s)))
 def test_permutation_blocks_bit_exact(api, shape, dtype):
     """0/1 blocks (identity and cyclic shifts) make M a permutation matrix:
@@ -298,7 +303,7 @@ def test_permutation_blocks_bit_exact(api, shape, dtype):
         assert np.array_equal(host(y), expect), (shape, a, c)
 
 
-@pytest.mark.parametrize("shape", [(1024, 1024, 32, 32, 4096), (2048, 2048, 16, 16, 4100)],
+@pytest.mark.parametrize("shape", [(1024, 1024, 32, 32, 4096), (4096, 4096, 32, 32, 4100)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_backward_is_deterministic(api, shape):
     inp, out, b1, b2, batch = shape
