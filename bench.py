@@ -256,8 +256,8 @@ def main() -> int:
 
     cpu = None
     if not args.no_cpu_baseline:
-        # about 1.5e13 fp64 flops of dense-factor products (~10-30 s on 16 host cores)
-        rows = args.cpu_rows or min(B, max(8, int(1.5e13 / (20.0 * fo * max(fi, fo)))))
+        # about 2e13 fp64 flops of dense-factor products (~10-30 s on 16 host cores)
+        rows = args.cpu_rows or min(B, max(8, int(2e13 / (20.0 * fo * max(fi, fo)))))
         log(f"cpu baseline: oracle on {rows} rows")
         cpu = cpu_baseline(w, rows)
 

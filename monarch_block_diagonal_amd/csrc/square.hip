@@ -87,11 +87,19 @@ __device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
 //  * A workgroup walks its row range in pairs of tiles (slots A and B); a
 //    trailing odd tile is a clamped duplicate.
 
-// Wait once for everything the prologue issued (weights and the first two
-// tiles). The wait counts the compiler inserts at a loop head are the
-// minimum over its predecessors; without this, the prologue's issue order
-// would set them and drain both prefetch slots on every iteration.
-__device__ __forceinline__ void drain_prologue() { __builtin_amdgcn_s_waitcnt(0); }
+// Empty asm statements that claim to modify a value: code placed after one
+// cannot be scheduled before the load that produced the value. Used to wait
+// once for everything a prologue issued (weights and the first prefetched
+// tiles): the wait counts the compiler inserts at a loop head are the minimum
+// over its predecessors, so without it the prologue's issue order would set
+// them and drain the prefetch slots on every iteration. Also placed before a
+// select on a prefetched value, which would otherwise be hoisted up to the
+// load and wait for the prefetch right after issuing it.
+template <typename T> __device__ __forceinline__ void pin(T& v) { asm volatile("" : "+v"(v)); }
+template <typename T, int N> __device__ __forceinline__ void pin(T (&v)[N]) {
+#pragma unroll
+  for (int i = 0; i < N; ++i) pin(v[i]);
+}
 
 // 4x8 transpose of bf16 in registers: in[i] holds elements (i, e = 0..7);
 // out[e] gets elements (i = 0..3, e) packed into 8 bytes.
@@ -155,6 +163,7 @@ __global__ __launch_bounds__(256) void sq_stage1_fwd_kernel(const uint16_t* __re
     for (int i = 0; i < 2; ++i) pre[i] = ldg16(base + clamp_row(lrow + 16 * i, lim) * in + xcol);
   };
   auto body = [&](u32x4(&cur)[2], int64_t b0) {
+    pin(cur);
 #pragma unroll
     for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(&xs[(lrow + 16 * i) * XLD + seg * 8]) = cur[i];
     __syncthreads();
@@ -188,7 +197,9 @@ __global__ __launch_bounds__(256) void sq_stage1_fwd_kernel(const uint16_t* __re
   u32x4 pa[2], pb[2];
   gload(pa, row0);
   gload(pb, row0 + T);
-  drain_prologue();
+  pin(a);
+  pin(pa);
+  pin(pb);
   for (int64_t k = 0; k < npairs; ++k) {
     body(pa, row0 + 2 * k * T);
     body(pb, row0 + (2 * k + 1) * T);
@@ -272,10 +283,13 @@ __global__ __launch_bounds__(512) void sq_stage2_fwd_kernel(const uint16_t* __re
   u32x4 pa[4], pb[4];
   gload(pa, 0);
   gload(pb, 1);
-  drain_prologue();
+  pin(a);
+  pin(pa);
+  pin(pb);
   auto step = [&](auto tcc, u32x4(&cur)[4], int64_t tile, uint16_t* buf) {
     constexpr int tc = decltype(tcc)::value;
     const int64_t c = tile * 4 + tc;
+    pin(cur);
     scatter(cur, buf);
     __syncthreads();
     gload(cur, c + 2 < nchunks ? c + 2 : nchunks - 1);
@@ -430,6 +444,7 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_data_kernel(
     for (int ks = 0; ks < 4; ++ks) pre[ks] = ldg16(base + ks * vstep);
   };
   auto body = [&](u32x4(&cur)[4], int64_t b0) {
+    pin(cur);
     f32x4 acc[8];
 #pragma unroll
     for (int mt = 0; mt < 8; ++mt) acc[mt] = zero4();
@@ -462,7 +477,9 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_data_kernel(
   u32x4 pa[4], pb[4];
   gload(pa, row0);
   gload(pb, row0 + T);
-  drain_prologue();
+  pin(a);
+  pin(pa);
+  pin(pb);
   for (int64_t k = 0; k < npairs; ++k) {
     body(pa, row0 + 2 * k * T);
     body(pb, row0 + (2 * k + 1) * T);
@@ -474,7 +491,7 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_data_kernel(
 // --------------------------------------------------------------------------
 // Workgroup: 8 L blocks x a 32-wide slice of p x a batch chunk. 8 waves;
 // wave w owns block g0 + w with accumulators dL[32 p x 128 t] in VGPRs. Tile:
-// 32 rows = one K step; the next tile's panels are in flight in registers.
+// 32 rows = one K step; the next two tiles' panels are in flight in registers.
 // Both operands need consecutive rows per lane (K = batch): dV panels ->
 // LDS [g][p][row] through 2x8 register transposes, Z panels -> LDS
 // [g][t][row] through 4x8 transposes. The chunk's sum is written as an fp32
@@ -516,8 +533,7 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_weight_kernel(
     const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
     const uint16_t* vb = dV + bc * 8 + vcol;
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      pv[i] = zero_unless(b0 + 2 * vrp + i < row1, ldg16(vb + clamp_row(2 * vrp + i, lim) * 8));
+    for (int i = 0; i < 2; ++i) pv[i] = ldg16(vb + clamp_row(2 * vrp + i, lim) * 8);
     const uint16_t* zb = Z + bc * 8 + zcol;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -525,6 +541,13 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_weight_kernel(
       for (int i = 0; i < 4; ++i) pz[4 * j + i] = ldg16(zb + j * zstep + clamp_row(4 * zrq + i, lim) * 8);
   };
   auto body = [&](u32x4(&pv)[2], u32x4(&pz)[8], int64_t b0) {
+    // rows past the range were loaded clamped; zero their dV here, where the
+    // values are consumed (a select right after the load would make the
+    // compiler wait for the prefetch at once)
+    pin(pv);
+    pin(pz);
+#pragma unroll
+    for (int i = 0; i < 2; ++i) pv[i] = zero_unless(b0 + 2 * vrp + i < row1, pv[i]);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
       // rows 2rp, 2rp+1 of p = 8po + 2k (lo halves) and 8po + 2k + 1 (hi halves)
@@ -543,7 +566,7 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_weight_kernel(
         *reinterpret_cast<u32x2*>(&zst[(e * Q + ztl + 64 * j) * TLD + 4 * zrq]) = tr[e];
     }
     __syncthreads();
-    gload(pv, pz, b0 + T);
+    gload(pv, pz, b0 + 2 * T);
     bf16x8 A[2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt) A[mt] = frag_ld(&dvs[(w * 32 + 16 * mt + l15) * TLD + 8 * lh]);
@@ -557,11 +580,18 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_weight_kernel(
   };
 
   if (row0 < row1) {
-    const int64_t ntiles = (row1 - row0 + T - 1) / T;
-    u32x4 pv[2], pz[8];
-    gload(pv, pz, row0);
-    drain_prologue();
-    for (int64_t k = 0; k < ntiles; ++k) body(pv, pz, row0 + k * T);
+    const int64_t npairs = (row1 - row0 + 2 * T - 1) / (2 * T);
+    u32x4 va[2], za[8], vb[2], zb[8];
+    gload(va, za, row0);
+    gload(vb, zb, row0 + T);
+    pin(va);
+    pin(za);
+    pin(vb);
+    pin(zb);
+    for (int64_t k = 0; k < npairs; ++k) {
+      body(va, za, row0 + 2 * k * T);
+      body(vb, zb, row0 + (2 * k + 1) * T);
+    }
   }
   // partial[chunk][g][p][t]
   float* P = partial + (static_cast<int64_t>(chunk) * nb2 + gg * 8 + w) * Q * Q;
@@ -580,7 +610,7 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_weight_kernel(
 // One R block and a batch chunk per workgroup, 8 waves; wave w owns dX
 // features s in [16w, +16) and dR rows k in [16w, +16). Tile: 32 rows; two
 // tiles in flight in registers. dZ panels -> LDS [row][k] and [k][row];
-// X -> LDS [s][row] (zero past the range, so dR only sums real rows).
+// X -> LDS [s][row] (zeroed past the range, so dR only sums real rows).
 __global__ __launch_bounds__(512) void sq_stage1_bwd_kernel(
     const uint16_t* __restrict__ dZ, const uint16_t* __restrict__ X,
     const uint16_t* __restrict__ W1t, uint16_t* __restrict__ dX, float* __restrict__ partial,
@@ -617,9 +647,13 @@ __global__ __launch_bounds__(512) void sq_stage1_bwd_kernel(
   auto gload = [&](u32x4& pz, u32x4& px, int64_t b0) {
     const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
     pz = ldg16(dZ + bc * 8 + clamp_row(zrow, lim) * 8 + zcol);
-    px = zero_unless(b0 + xrow < row1, ldg16(X + bc * in + clamp_row(xrow, lim) * in + xcol));
+    px = ldg16(X + bc * in + clamp_row(xrow, lim) * in + xcol);
   };
   auto body = [&](u32x4& pz, u32x4& px, int64_t b0) {
+    // X rows past the range were loaded clamped; zero them where consumed
+    pin(pz);
+    pin(px);
+    px = zero_unless(b0 + xrow < row1, px);
     *reinterpret_cast<u32x4*>(&dzs[zrow * XLD + kg * 8]) = pz;
 #pragma unroll
     for (int e = 0; e < 8; ++e) dzt[(kg * 8 + e) * TLD + zrow] = half_of(pz, e);
@@ -657,7 +691,11 @@ __global__ __launch_bounds__(512) void sq_stage1_bwd_kernel(
     u32x4 za, xa, zb, xb;
     gload(za, xa, row0);
     gload(zb, xb, row0 + T);
-    drain_prologue();
+    pin(a);
+    pin(za);
+    pin(xa);
+    pin(zb);
+    pin(xb);
     for (int64_t k = 0; k < npairs; ++k) {
       body(za, xa, row0 + 2 * k * T);
       body(zb, xb, row0 + (2 * k + 1) * T);
