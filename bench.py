@@ -57,6 +57,11 @@ def kernel_bytes(name: str, pr: dict) -> float:
         "stage1_bwd_data": e * B * (mid + inp) + e * p1,
         "stage1_bwd_weight": e * B * (mid + inp) + e * p1,
         "stage1_bwd": e * B * (mid + 2 * inp) + 2 * e * p1,
+        # square fast path: dY (and Y for the ReLU mask) -> block-major dV, then
+        # both stage-2 backward kernels read dV instead of dY
+        "sq128_dv_panels": e * B * out * (3 if relu else 2),
+        "sq128_stage2_bwd_data": e * B * (out + mid) + e * p2,
+        "sq128_stage2_bwd_weight": e * B * (out + mid) + e * p2,
         "transpose_weights": 2 * e * (p1 + p2),
         "reduce_dw2": e * p2,
         "reduce_dw1": e * p1,

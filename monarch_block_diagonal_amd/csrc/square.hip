@@ -493,9 +493,12 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_data_kernel(
 // wave w owns block g0 + w with accumulators dL[32 p x 128 t] in VGPRs. Tile:
 // 32 rows = one K step; the next two tiles' panels are in flight in registers.
 // Both operands need consecutive rows per lane (K = batch): dV panels ->
-// LDS [g][p][row] through 2x8 register transposes, Z panels -> LDS
-// [g][t][row] through 4x8 transposes. The chunk's sum is written as an fp32
-// partial.
+// LDS [g][p][pos] through 2x8 register transposes, Z panels -> LDS
+// [g][t][pos] through 4x8 transposes. A sum over rows may take them in any
+// order, so LDS position pos holds tile row (pos%4)*8 + pos/4 in both
+// operands: every load instruction then reads whole 128-byte lines (8
+// consecutive rows of a panel) and each thread still ends up with adjacent
+// positions. The chunk's sum is written as an fp32 partial.
 __global__ __launch_bounds__(512) void sq_stage2_bwd_weight_kernel(
     const uint16_t* __restrict__ dV, const uint16_t* __restrict__ Z, float* __restrict__ partial,
     int64_t B, int nb2, int64_t rows_per) {
@@ -520,11 +523,13 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_weight_kernel(
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = zero4();
 
-  // dV: thread (rp = tid&15, po = (tid>>4)&3, gl = tid>>6) loads rows 2rp, 2rp+1
-  // of panel (g0+gl)*16 + 4ps + po
+  // dV: thread (rp = tid&15, po = (tid>>4)&3, gl = tid>>6) loads positions
+  // 2rp, 2rp+1 (rows vr0 and vr0 + 8) of panel (g0+gl)*16 + 4ps + po
   const int vrp = tid & 15, vpo = (tid >> 4) & 3, vgl = tid >> 6;
+  const int vr0 = 16 * (vrp & 1) + (vrp >> 1);
   const uint32_t vcol = ((gg * 8 + vgl) * 16 + 4 * ps + vpo) * Bu * 8;
-  // Z: thread (rq = tid&7, tl = tid>>3) loads rows 4rq..4rq+3 of t = tl + 64j
+  // Z: thread (rq = tid&7, tl = tid>>3) loads positions 4rq..4rq+3 (rows
+  // rq + 8i) of t = tl + 64j
   const int zrq = tid & 7, ztl = tid >> 3;
   const uint32_t zcol = (ztl * pstride + gg) * Bu * 8;
   const uint32_t zstep = 64 * pstride * Bu * 8;
@@ -533,12 +538,12 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_weight_kernel(
     const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
     const uint16_t* vb = dV + bc * 8 + vcol;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) pv[i] = ldg16(vb + clamp_row(2 * vrp + i, lim) * 8);
+    for (int i = 0; i < 2; ++i) pv[i] = ldg16(vb + clamp_row(vr0 + 8 * i, lim) * 8);
     const uint16_t* zb = Z + bc * 8 + zcol;
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) pz[4 * j + i] = ldg16(zb + j * zstep + clamp_row(4 * zrq + i, lim) * 8);
+      for (int i = 0; i < 4; ++i) pz[4 * j + i] = ldg16(zb + j * zstep + clamp_row(zrq + 8 * i, lim) * 8);
   };
   auto body = [&](u32x4(&pv)[2], u32x4(&pz)[8], int64_t b0) {
     // rows past the range were loaded clamped; zero their dV here, where the
@@ -547,10 +552,10 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_weight_kernel(
     pin(pv);
     pin(pz);
 #pragma unroll
-    for (int i = 0; i < 2; ++i) pv[i] = zero_unless(b0 + 2 * vrp + i < row1, pv[i]);
+    for (int i = 0; i < 2; ++i) pv[i] = zero_unless(b0 + vr0 + 8 * i < row1, pv[i]);
 #pragma unroll
     for (int k = 0; k < 4; ++k) {
-      // rows 2rp, 2rp+1 of p = 8po + 2k (lo halves) and 8po + 2k + 1 (hi halves)
+      // positions 2rp, 2rp+1 of p = 8po + 2k (lo halves) and 8po + 2k + 1 (hi halves)
       const uint32_t even = (pv[0][k] & 0xffffu) | (pv[1][k] << 16);
       const uint32_t odd = (pv[0][k] >> 16) | (pv[1][k] & 0xffff0000u);
       *reinterpret_cast<uint32_t*>(&dvs[(vgl * 32 + 8 * vpo + 2 * k) * TLD + 2 * vrp]) = even;
@@ -608,23 +613,31 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_weight_kernel(
 // stage 1 backward: dX_r = dZ_r · R_r and dR_r = sum_b dZ_rᵀ X_r
 // --------------------------------------------------------------------------
 // One R block and a batch chunk per workgroup, 8 waves; wave w owns dX
-// features s in [16w, +16) and dR rows k in [16w, +16). Tile: 32 rows; two
-// tiles in flight in registers. dZ panels -> LDS [row][k] and [k][row];
-// X -> LDS [s][row] (zeroed past the range, so dR only sums real rows).
-__global__ __launch_bounds__(512) void sq_stage1_bwd_kernel(
+// features s in [16w, +16) and dR rows k in [16w, +16). Tile: 64 rows; two
+// tiles in flight in registers. Waves 0-3 load dZ, waves 4-7 load X: each
+// thread 4 rows (rq + 16i) of one 8-feature piece, so a load instruction
+// reads 256-byte runs, and a 4x8 register transpose gives 8-byte LDS writes
+// for the row-contiguous copies the dR product needs (K = batch). A sum
+// over rows may take them in any order: position 4rq + i holds row rq + 16i
+// in both dR operands. dZ also goes to LDS row-major (dX operand); X rows
+// past the range are zeroed, so dR only sums real rows.
+constexpr int T1 = 64;            // stage-1 backward row tile
+constexpr int PLD = T1 + 8;       // LDS pitch of [feature][64 positions] tiles
+
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void sq_stage1_bwd_kernel(
     const uint16_t* __restrict__ dZ, const uint16_t* __restrict__ X,
     const uint16_t* __restrict__ W1t, uint16_t* __restrict__ dX, float* __restrict__ partial,
     int64_t B, int nb1, int64_t rows_per) {
-  constexpr int T = 32;
-  __shared__ __attribute__((aligned(16))) uint16_t dzs[T * XLD];
-  __shared__ __attribute__((aligned(16))) uint16_t dzt[Q * TLD];
-  __shared__ __attribute__((aligned(16))) uint16_t xt[Q * TLD];
-  __shared__ __attribute__((aligned(16))) uint16_t dxs[T * XLD];
+  constexpr int T = T1;
+  __shared__ __attribute__((aligned(16))) uint16_t dzs[T * XLD];   // [row][k]
+  __shared__ __attribute__((aligned(16))) uint16_t dxs[T * XLD];   // [row][s]
+  __shared__ __attribute__((aligned(16))) uint16_t ts[2][Q * PLD];  // dZ: [k][pos], X: [s][pos]
   const int r = blockIdx.x % nb1;
   const int chunk = blockIdx.x / nb1;
   const int64_t row0 = static_cast<int64_t>(chunk) * rows_per;
   const int64_t row1 = row0 + rows_per < B ? row0 + rows_per : B;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l15 = lane & 15, lh = lane >> 4;
   const uint32_t in = static_cast<uint32_t>(nb1) * Q;
   const uint32_t Bu = static_cast<uint32_t>(B);
@@ -638,67 +651,79 @@ __global__ __launch_bounds__(512) void sq_stage1_bwd_kernel(
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) accr[nt] = zero4();
 
-  // dZ piece: kg = tid>>5, row = tid&31; X piece: row = tid>>4, seg = tid&15
-  const int kg = tid >> 5, zrow = tid & 31;
-  const uint32_t zcol = (r * 16 + kg) * Bu * 8;
-  const int xrow = tid >> 4, seg = tid & 15;
-  const uint32_t xcol = r * Q + seg * 8;
+  // loader role: dZ (panel r*16 + oct, 16-byte row stride) or X (columns
+  // r*128 + 8*oct, row stride in); rows rq + 16i of the tile
+  const bool is_x = w >= 4;
+  const int lt = tid & 255;
+  const int rq = is_x ? lt >> 4 : lt & 15;
+  const int oct = is_x ? lt & 15 : lt >> 4;
+  const uint16_t* src = is_x ? X + r * Q + oct * 8 : dZ + static_cast<int64_t>(r * 16 + oct) * B * 8;
+  const uint32_t rstride = is_x ? in : 8u;
+  uint16_t* tdst = &ts[is_x ? 1 : 0][(oct * 8) * PLD + 4 * rq];
+  // dX store pieces: seg = tid&15, rows (tid>>4) + 32i
+  const int xseg = tid & 15, xrow = tid >> 4;
 
-  auto gload = [&](u32x4& pz, u32x4& px, int64_t b0) {
+  auto gload = [&](u32x4(&pre)[4], int64_t b0) {
     const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
-    pz = ldg16(dZ + bc * 8 + clamp_row(zrow, lim) * 8 + zcol);
-    px = ldg16(X + bc * in + clamp_row(xrow, lim) * in + xcol);
+    const uint16_t* base = src + bc * rstride;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pre[i] = ldg16(base + clamp_row(rq + 16 * i, lim) * rstride);
   };
-  auto body = [&](u32x4& pz, u32x4& px, int64_t b0) {
-    // X rows past the range were loaded clamped; zero them where consumed
-    pin(pz);
-    pin(px);
-    px = zero_unless(b0 + xrow < row1, px);
-    *reinterpret_cast<u32x4*>(&dzs[zrow * XLD + kg * 8]) = pz;
+  auto body = [&](u32x4(&pre)[4], int64_t b0) {
+    pin(pre);
 #pragma unroll
-    for (int e = 0; e < 8; ++e) dzt[(kg * 8 + e) * TLD + zrow] = half_of(pz, e);
+    for (int i = 0; i < 4; ++i)
+      pre[i] = zero_unless(!is_x || b0 + rq + 16 * i < row1, pre[i]);
+    if (!is_x) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) xt[(seg * 8 + e) * TLD + xrow] = half_of(px, e);
+      for (int i = 0; i < 4; ++i)
+        *reinterpret_cast<u32x4*>(&dzs[(rq + 16 * i) * XLD + oct * 8]) = pre[i];
+    }
+    u32x2 tr[8];
+    transpose4x8(pre, tr);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x2*>(tdst + e * PLD) = tr[e];
     __syncthreads();
-    gload(pz, px, b0 + 2 * T);
-    // dXᵀ[s x b] = Rᵀ[s x k] · dZᵀ[k x b]
-    f32x4 accx[2] = {zero4(), zero4()};
+    gload(pre, b0 + 2 * T);
+    // dXᵀ[s x b] = Rᵀ[s x k] · dZᵀ[k x b], 4 column tiles of 16 rows
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
+    for (int nt = 0; nt < 4; ++nt) {
+      f32x4 accx = zero4();
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt)
-        accx[nt] = mfma(a[ks], frag_ld(&dzs[(16 * nt + l15) * XLD + 32 * ks + 8 * lh]), accx[nt]);
-#pragma unroll
-    for (int nt = 0; nt < 2; ++nt) {
+      for (int ks = 0; ks < 4; ++ks)
+        accx = mfma(a[ks], frag_ld(&dzs[(16 * nt + l15) * XLD + 32 * ks + 8 * lh]), accx);
       u32x2 v;
-      v[0] = pack_bf16x2(accx[nt][0], accx[nt][1]);
-      v[1] = pack_bf16x2(accx[nt][2], accx[nt][3]);
+      v[0] = pack_bf16x2(accx[0], accx[1]);
+      v[1] = pack_bf16x2(accx[2], accx[3]);
       *reinterpret_cast<u32x2*>(&dxs[(16 * nt + l15) * XLD + 16 * w + 4 * lh]) = v;
     }
-    // dR[k x s] += dZᵀ[k x b] · X[b x s]
-    const bf16x8 A = frag_ld(&dzt[(16 * w + l15) * TLD + 8 * lh]);
+    // dR[k x s] += dZᵀ[k x pos] · X[pos x s]
 #pragma unroll
-    for (int nt = 0; nt < 8; ++nt)
-      accr[nt] = mfma(A, frag_ld(&xt[(16 * nt + l15) * TLD + 8 * lh]), accr[nt]);
+    for (int kk = 0; kk < 2; ++kk) {
+      const bf16x8 A = frag_ld(&ts[0][(16 * w + l15) * PLD + 32 * kk + 8 * lh]);
+#pragma unroll
+      for (int nt = 0; nt < 8; ++nt)
+        accr[nt] = mfma(A, frag_ld(&ts[1][(16 * nt + l15) * PLD + 32 * kk + 8 * lh]), accr[nt]);
+    }
     __syncthreads();
     const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
-    stg16(dX + bc * in + clamp_row(xrow, lim) * in + xcol,
-          *reinterpret_cast<const u32x4*>(&dxs[xrow * XLD + seg * 8]));
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      stg16(dX + bc * in + clamp_row(xrow + 32 * i, lim) * in + r * Q + xseg * 8,
+            *reinterpret_cast<const u32x4*>(&dxs[(xrow + 32 * i) * XLD + xseg * 8]));
   };
 
   if (row0 < row1) {
     const int64_t npairs = (row1 - row0 + 2 * T - 1) / (2 * T);
-    u32x4 za, xa, zb, xb;
-    gload(za, xa, row0);
-    gload(zb, xb, row0 + T);
+    u32x4 pa[4], pb[4];
+    gload(pa, row0);
+    gload(pb, row0 + T);
     pin(a);
-    pin(za);
-    pin(xa);
-    pin(zb);
-    pin(xb);
+    pin(pa);
+    pin(pb);
     for (int64_t k = 0; k < npairs; ++k) {
-      body(za, xa, row0 + 2 * k * T);
-      body(zb, xb, row0 + (2 * k + 1) * T);
+      body(pa, row0 + 2 * k * T);
+      body(pb, row0 + (2 * k + 1) * T);
     }
   }
   float* P = partial + (static_cast<int64_t>(chunk) * nb1 + r) * Q * Q;
@@ -766,8 +791,8 @@ SqPlan sq_plan(int64_t batch, int64_t nb) {
   p.w2_rows = round_up(cdiv(batch, p.w2_chunks), 32);
   p.w2_chunks = cdiv(batch, p.w2_rows);
   // stage-1 backward: 2 workgroups of 8 waves per CU
-  p.b1_chunks = clamp64(512 / nb, 1, cdiv(batch, 32));
-  p.b1_rows = round_up(cdiv(batch, p.b1_chunks), 32);
+  p.b1_chunks = clamp64(512 / nb, 1, cdiv(batch, T1));
+  p.b1_rows = round_up(cdiv(batch, p.b1_chunks), T1);
   p.b1_chunks = cdiv(batch, p.b1_rows);
   return p;
 }
