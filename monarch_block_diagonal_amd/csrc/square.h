@@ -16,7 +16,7 @@ struct SqPlan {
 };
 
 // True when the fast path covers the problem: bf16, in = out = 128*nb with
-// nb1 = nb2 = nb, nb a multiple of 32, and batch*out < 2^31.
+// nb1 = nb2 = nb, nb in {32, 64, 128}, and batch*out < 2^31.
 bool sq_applicable(int64_t in, int64_t out, int64_t nb1, int64_t nb2, int64_t batch,
                    int dtype_bf16);
 SqPlan sq_plan(int64_t batch, int64_t nb);
@@ -24,7 +24,8 @@ SqPlan sq_plan(int64_t batch, int64_t nb);
 // w1t/w2t = each 128x128 block of w1/w2 transposed (read by the backward kernels).
 hipError_t sq_launch_transpose_weights(const void* w1, const void* w2, void* w1t, void* w2t,
                                       int64_t nb, hipStream_t s);
-// z / dz are in the panel layout: feature j of row b at ((j/8)*batch + b)*8 + j%8.
+// Panel layout: feature f of row b at ((f/8)*batch + b)*8 + f%8. z holds
+// stage 2's input W[b, g*128 + t] = Z[b, t*nb + g] in it; dz holds dZ (Z order).
 hipError_t sq_launch_stage1_fwd(const void* x, const void* w1, void* z, int64_t batch, int64_t nb,
                                 const SqPlan& p, hipStream_t s);
 hipError_t sq_launch_stage2_fwd(const void* z, const void* w2, void* y, int64_t batch, int64_t nb,

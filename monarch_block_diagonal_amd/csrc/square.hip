@@ -1,5 +1,5 @@
 // Fast path for bf16 Monarch layers whose four block dimensions are all 128
-// (in = mid = out = 128*b, nblocks1 = nblocks2 = b, b a multiple of 32): the
+// (in = mid = out = 128*b, nblocks1 = nblocks2 = b, b in {32, 64, 128}): the
 // square Definition C.3 family (scatterbrain issues page, "Definition C.3"
 // thread) at block size 128, e.g. n = 16384 with 128 blocks.
 //
@@ -7,20 +7,24 @@
 // I/O width against a bf16 MFMA ridge near 300), so the kernels are built
 // around data movement:
 //
-//  * The saved stage-2 input Z (and the backward's dZ) use a panel layout:
-//    feature j of row b sits at ((j/8)*B + b)*8 + j%8. A stage-1 kernel that
-//    owns one R block writes 16 whole panels (256-512 B runs); a stage-2
-//    kernel that owns L blocks g0..g0+31 finds, for each t, its inputs
-//    Z[b, t*b2 + g0 .. +31] in 4 consecutive panels (the stride permutation
-//    of the "hypercube" thread becomes a panel index; no permuted copy).
+//  * Block-major panel layout for the intermediates: feature f of row b sits
+//    at ((f/8)*B + b)*8 + f%8, so a 16-byte piece holds 8 features of one
+//    row and a panel holds those 8 features for every row. The saved stage-2
+//    input (z) is W = P·Z in this layout, W[b, g*128 + t] = Z[b, t*b2 + g]:
+//    the stride permutation of the "hypercube" thread is applied once, by the
+//    stage-1 kernel's stores, and every stage-2 kernel reads whole pieces of
+//    one L block. The gradient of stage 2's output (dV, from dY) uses the
+//    same layout; dZ, read by the stage-1 backward, is in Z order.
 //  * The caller's row-major Y / dY hold the L blocks of one (row, p) side by
-//    side, so a workgroup that owns 32 blocks moves 64-byte runs there (16
-//    blocks: 32-byte runs for the weight gradient). Narrower runs cost up to
-//    2-3x in achieved bandwidth on this memory system. Workgroups that share
-//    cache lines are mapped onto one XCD (workgroups are dispatched
-//    round-robin over the 8 XCDs).
+//    side, so the stage-2 forward owns 32 blocks to write 64-byte runs, and a
+//    transpose pass moves dY into dV panels with 256-byte runs. Narrower runs
+//    cost up to 2-3x in achieved bandwidth on this memory system. Workgroups
+//    that share cache lines are mapped onto one XCD (workgroups are
+//    dispatched round-robin over the 8 XCDs).
 //  * Weights stay in VGPRs for the whole launch (persistent workgroups over
 //    a row range); MFMA v_mfma_f32_16x16x32_bf16 with fp32 accumulation.
+//    Where a lane's MFMA operand is one 16-byte piece of a panel or a row it
+//    is loaded straight from global memory into registers.
 //  * Weight gradients accumulate in registers over a batch chunk per
 //    workgroup; chunks are summed afterwards in a fixed order.
 #include <type_traits>
@@ -34,7 +38,6 @@ namespace {
 constexpr int Q = 128;        // block size
 constexpr int XLD = Q + 8;    // LDS pitch (elements) of [row][feature] tiles
 constexpr int TLD = 32 + 8;   // LDS pitch of [feature][32 rows] tiles
-constexpr int YLD = Q * 8 + 8;
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
@@ -121,80 +124,97 @@ __device__ __forceinline__ u32x4 zero_unless(bool keep, u32x4 v) {
 }
 
 // --------------------------------------------------------------------------
-// stage 1 forward: Z_r = X_r · R_rᵀ for one R block per workgroup
+// stage 1 forward, stored in stage 2's input order:
+//   W[b, g*128 + t] = Z[b, t*b2 + g],  Z[b, r*128 + k] = sum_s R[r,k,s] X[b, r*128 + s]
 // --------------------------------------------------------------------------
-// 4 waves; wave w owns output features k in [32w, 32w+32). Tile: 32 rows.
-// C = Zᵀ[k x b] = R[k x s] · Xᵀ[s x b]; A = R fragments in VGPRs, B = X tile
-// from LDS; results go straight to the panel layout (lane pairs fill 16 B,
-// 16 lanes fill 256 B of one panel).
-__global__ __launch_bounds__(256) void sq_stage1_fwd_kernel(const uint16_t* __restrict__ X,
+// Workgroup: 8 R blocks r0..r0+7 x a row range; wave w owns block r0 + w
+// (R fragments: 128 VGPRs). Tile: 16 rows; the MFMA B operands (X[b][8 s])
+// are 16-byte pieces of X rows, loaded straight into registers two tiles
+// ahead. C = Zᵀ[k x b] = R[k x s] · Xᵀ[s x b]. Output (r, k) is W-feature
+// (g, t) = ((r*128 + k) % b2, (r*128 + k) / b2); the 8 blocks cover 1024/b2
+// consecutive t of every g, i.e. 128 whole 8-t pieces per row, staged in LDS
+// [piece][row][t%8] and stored in 256-byte runs.
+template <int LNB>
+__global__ __launch_bounds__(512) void sq_stage1_fwd_kernel(const uint16_t* __restrict__ X,
                                                             const uint16_t* __restrict__ W1,
-                                                            uint16_t* __restrict__ Z, int64_t B,
-                                                            int nb1, int64_t rows_per) {
-  constexpr int T = 32;
-  __shared__ __attribute__((aligned(16))) uint16_t xs[T * XLD];
-  const int r = blockIdx.x % nb1;
-  const int64_t row0 = static_cast<int64_t>(blockIdx.x / nb1) * rows_per;
+                                                            uint16_t* __restrict__ Wz, int64_t B,
+                                                            int64_t rows_per) {
+  constexpr int NB = 1 << LNB;
+  constexpr int NPC = Q / NB;         // 8-t pieces per g covered by one workgroup
+  constexpr int T = 16;
+  constexpr int ZP = T * 8 + 8;       // LDS pitch of one staged piece
+  constexpr uint32_t in = NB * Q;
+  __shared__ __attribute__((aligned(16))) uint16_t zs[Q * ZP];
+  constexpr int n_rg = NB / 8;
+  const int logical = xcd_logical(blockIdx.x, gridDim.x);
+  const int rg = logical % n_rg;
+  const int64_t row0 = static_cast<int64_t>(logical / n_rg) * rows_per;
   const int64_t row1 = row0 + rows_per < B ? row0 + rows_per : B;
   if (row0 >= row1) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l15 = lane & 15, lh = lane >> 4;
-  const uint32_t in = static_cast<uint32_t>(nb1) * Q;
+  const int r = rg * 8 + w;
   const uint32_t Bu = static_cast<uint32_t>(B);
 
-  bf16x8 a[2][4];
+  // A = R_r[k x s]: lane holds R[r][k = 16mt + l15][s = 32ks + 8lh ..]
+  bf16x8 a[8][4];
   const uint16_t* Rr = W1 + static_cast<int64_t>(r) * Q * Q;
 #pragma unroll
-  for (int mt = 0; mt < 2; ++mt)
+  for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks)
-      a[mt][ks] = frag_ld(Rr + (32 * w + 16 * mt + l15) * Q + 32 * ks + 8 * lh);
+    for (int ks = 0; ks < 4; ++ks) a[mt][ks] = frag_ld(Rr + (16 * mt + l15) * Q + 32 * ks + 8 * lh);
 
-  // X pieces: row = (tid>>4) + 16i, seg = tid&15
-  const int lrow = tid >> 4, seg = tid & 15;
-  const uint32_t xcol = r * Q + seg * 8;
-  // Z stores: panel r*16 + 4w + 2mt + lh/2, row 16nt + l15
-  const uint32_t zcol = (r * 16 + 4 * w + (lh >> 1)) * Bu * 8 + 4 * (lh & 1);
+  const uint32_t xcol = r * Q + 8 * lh;
+  // staged pieces: pid = (tid>>4) + 32i, row = tid&15 -> panel (pid/NPC)*16 + rg*NPC + pid%NPC
+  const int spid = tid >> 4, srow = tid & 15;
 
-  auto gload = [&](u32x4(&pre)[2], int64_t b0) {
+  auto gload = [&](u32x4(&pre)[4], int64_t b0) {
     const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
-    const uint16_t* base = X + bc * in;
+    const uint16_t* base = X + (bc + clamp_row(l15, lim)) * in + xcol;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) pre[i] = ldg16(base + clamp_row(lrow + 16 * i, lim) * in + xcol);
+    for (int ks = 0; ks < 4; ++ks) pre[ks] = ldg16(base + 32 * ks);
   };
-  auto body = [&](u32x4(&cur)[2], int64_t b0) {
+  auto body = [&](u32x4(&cur)[4], int64_t b0) {
     pin(cur);
+    f32x4 acc[8];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) *reinterpret_cast<u32x4*>(&xs[(lrow + 16 * i) * XLD + seg * 8]) = cur[i];
-    __syncthreads();
-    gload(cur, b0 + 2 * T);
-    f32x4 acc[2][2] = {{zero4(), zero4()}, {zero4(), zero4()}};
+    for (int mt = 0; mt < 8; ++mt) acc[mt] = zero4();
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) {
-      bf16x8 bop[2];
+      bf16x8 bop;
+      __builtin_memcpy(&bop, &cur[ks], sizeof(bop));
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) bop[nt] = frag_ld(&xs[(16 * nt + l15) * XLD + 32 * ks + 8 * lh]);
-#pragma unroll
-      for (int mt = 0; mt < 2; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = mfma(a[mt][ks], bop[nt], acc[mt][nt]);
+      for (int mt = 0; mt < 8; ++mt) acc[mt] = mfma(a[mt][ks], bop, acc[mt]);
     }
-    const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
-    uint16_t* zb = Z + bc * 8;
+    gload(cur, b0 + 2 * T);
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt)
+    for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) {
-        u32x2 v;
-        v[0] = pack_bf16x2(acc[mt][nt][0], acc[mt][nt][1]);
-        v[1] = pack_bf16x2(acc[mt][nt][2], acc[mt][nt][3]);
-        *reinterpret_cast<u32x2*>(zb + zcol + 2 * mt * Bu * 8 + clamp_row(16 * nt + l15, lim) * 8) = v;
+      for (int v = 0; v < 4; v += 2) {
+        const uint32_t pk = pack_bf16x2(acc[mt][v], acc[mt][v + 1]);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          const int k = 16 * mt + 4 * lh + v + h;
+          const int g = k & (NB - 1);
+          const int tl = w * NPC + (k >> LNB);       // t relative to the workgroup's first t
+          zs[(g * NPC + (tl >> 3)) * ZP + l15 * 8 + (tl & 7)] =
+              static_cast<uint16_t>(h ? pk >> 16 : pk & 0xffffu);
+        }
       }
+    __syncthreads();
+    const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
+    uint16_t* zb = Wz + (bc + clamp_row(srow, lim)) * 8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int pid = spid + 32 * i;
+      const uint32_t panel = (pid / NPC) * 16 + rg * NPC + pid % NPC;
+      stg16(zb + panel * Bu * 8, *reinterpret_cast<const u32x4*>(&zs[pid * ZP + srow * 8]));
+    }
     __syncthreads();
   };
 
   const int64_t npairs = (row1 - row0 + 2 * T - 1) / (2 * T);
-  u32x4 pa[2], pb[2];
+  u32x4 pa[4], pb[4];
   gload(pa, row0);
   gload(pb, row0 + T);
   pin(a);
@@ -207,24 +227,22 @@ __global__ __launch_bounds__(256) void sq_stage1_fwd_kernel(const uint16_t* __re
 }
 
 // --------------------------------------------------------------------------
-// stage 2 forward: Y[b, p*b2 + g] = act(sum_t L[g,p,t] Z[b, t*b2 + g])
+// stage 2 forward: Y[b, p*b2 + g] = act(sum_t L[g,p,t] W[b, g*128 + t])
 // --------------------------------------------------------------------------
 // Workgroup: 32 L blocks g0..g0+31 x a 32-wide slice of p x a row range, so
 // each (row, p) of Y gets a 64-byte run. 8 waves; wave w owns blocks
 // g0+4w..+3 for the 32 p of the slice (L fragments: 128 VGPRs). Row tile: 16
-// rows; the t contraction runs in 4 chunks of 32. Z chunk (32 t x 32 g x 16
-// rows) -> LDS [g][row][t] (double-buffered; the next chunk's panels are in
-// flight in registers). C = Vᵀ[p x b] = L[p x t] · Wᵀ[t x b]; after 4 chunks
-// the tile -> LDS [row][p][g] -> Y.
-constexpr int CLD = 32 + 8;          // pitch of [..][row][32] chunk tiles
+// rows; the t contraction runs in 4 chunks of 32. The MFMA B operands
+// (W[b][8 t] of one block) are 16-byte pieces of the W panels, loaded
+// straight into registers two chunks ahead. C = Vᵀ[p x b] = L[p x t] ·
+// Wᵀ[t x b]; after 4 chunks the tile -> LDS [row][p][g] -> Y.
 constexpr int Y2LD = 32 * 32 + 8;    // pitch of [row][32 p][32 g]
 
-__global__ __launch_bounds__(512) void sq_stage2_fwd_kernel(const uint16_t* __restrict__ Z,
+__global__ __launch_bounds__(512) void sq_stage2_fwd_kernel(const uint16_t* __restrict__ Wz,
                                                             const uint16_t* __restrict__ W2,
                                                             uint16_t* __restrict__ Y, int64_t B,
                                                             int nb2, int64_t rows_per, int relu) {
   constexpr int T = 16;
-  __shared__ __attribute__((aligned(16))) uint16_t zs[2][32 * T * CLD];
   __shared__ __attribute__((aligned(16))) uint16_t ys[T * Y2LD];
   const int n_gq = nb2 >> 5;
   const int logical = xcd_logical(blockIdx.x, gridDim.x);
@@ -237,7 +255,6 @@ __global__ __launch_bounds__(512) void sq_stage2_fwd_kernel(const uint16_t* __re
   const int l15 = lane & 15, lh = lane >> 4;
   const uint32_t out = static_cast<uint32_t>(nb2) * Q;
   const uint32_t Bu = static_cast<uint32_t>(B);
-  const uint32_t pstride = nb2 >> 3;  // panels between t and t+1
 
   // a[g][mt][ks] = L[g0+4w+g][p = 32ps + 16mt + l15][t = 32ks + 8lh ..]
   bf16x8 a[4][2][4];
@@ -251,11 +268,10 @@ __global__ __launch_bounds__(512) void sq_stage2_fwd_kernel(const uint16_t* __re
         a[g][mt][ks] = frag_ld(Lg + (32 * ps + 16 * mt + l15) * Q + 32 * ks + 8 * lh);
   }
 
-  // chunk pieces: thread (row = tid&15, q4 = (tid>>4)&3, tq = tid>>6) loads
-  // t = 4tq + i, i < 4 (consecutive lanes: consecutive rows of one panel)
-  const int crow = tid & 15, cq4 = (tid >> 4) & 3, ctq = tid >> 6;
-  const uint32_t ccol = (4 * ctq * pstride + gq * 4 + cq4) * Bu * 8;
-  const uint32_t cstep = pstride * Bu * 8;   // +1 t
+  // operand pieces: panel (g0+4w+g)*16 + 4tc + lh, row b0 + l15
+  const uint32_t wcol = ((gq * 32 + 4 * w) * 16 + lh) * Bu * 8;
+  const uint32_t gstep = 16 * Bu * 8;   // next block
+  const uint32_t tstep = 4 * Bu * 8;    // next t chunk
   // Y pieces: id = tid + 512i: q4 = id&3, pl = (id>>2)&31, row = id>>7 (+4i)
   const int yq4 = tid & 3, ypl = (tid >> 2) & 31, yrow = tid >> 7;
   const uint32_t ycol = (32 * ps + ypl) * nb2 + gq * 32 + yq4 * 8;
@@ -264,17 +280,10 @@ __global__ __launch_bounds__(512) void sq_stage2_fwd_kernel(const uint16_t* __re
   auto gload = [&](u32x4(&pre)[4], int64_t c) {
     const int64_t b0 = row0 + (c >> 2) * T;
     const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
-    const uint16_t* base = Z + bc * 8 + clamp_row(crow, lim) * 8 + ccol +
-                           static_cast<uint32_t>(c & 3) * 32 * pstride * Bu * 8;
+    const uint16_t* base = Wz + (bc + clamp_row(l15, lim)) * 8 + wcol +
+                           static_cast<uint32_t>(c & 3) * tstep;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pre[i] = ldg16(base + i * cstep);
-  };
-  auto scatter = [&](const u32x4(&pre)[4], uint16_t* buf) {
-    u32x2 tr[8];
-    transpose4x8(pre, tr);
-#pragma unroll
-    for (int e = 0; e < 8; ++e)
-      *reinterpret_cast<u32x2*>(&buf[((cq4 * 8 + e) * T + crow) * CLD + 4 * ctq]) = tr[e];
+    for (int g = 0; g < 4; ++g) pre[g] = ldg16(base + g * gstep);
   };
 
   f32x4 acc[4][2];
@@ -286,13 +295,10 @@ __global__ __launch_bounds__(512) void sq_stage2_fwd_kernel(const uint16_t* __re
   pin(a);
   pin(pa);
   pin(pb);
-  auto step = [&](auto tcc, u32x4(&cur)[4], int64_t tile, uint16_t* buf) {
+  auto step = [&](auto tcc, u32x4(&cur)[4], int64_t tile) {
     constexpr int tc = decltype(tcc)::value;
     const int64_t c = tile * 4 + tc;
     pin(cur);
-    scatter(cur, buf);
-    __syncthreads();
-    gload(cur, c + 2 < nchunks ? c + 2 : nchunks - 1);
     if constexpr (tc == 0) {
 #pragma unroll
       for (int g = 0; g < 4; ++g)
@@ -301,10 +307,12 @@ __global__ __launch_bounds__(512) void sq_stage2_fwd_kernel(const uint16_t* __re
     }
 #pragma unroll
     for (int g = 0; g < 4; ++g) {
-      const bf16x8 bop = frag_ld(&buf[((4 * w + g) * T + l15) * CLD + 8 * lh]);
+      bf16x8 bop;
+      __builtin_memcpy(&bop, &cur[g], sizeof(bop));
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) acc[g][mt] = mfma(a[g][mt][tc], bop, acc[g][mt]);
     }
+    gload(cur, c + 2 < nchunks ? c + 2 : nchunks - 1);
     if constexpr (tc == 3) {
       // tile done: results -> ys[row][p][g], then Y
 #pragma unroll
@@ -331,13 +339,14 @@ __global__ __launch_bounds__(512) void sq_stage2_fwd_kernel(const uint16_t* __re
       for (int i = 0; i < 4; ++i)
         stg16(yb + clamp_row(yrow + 4 * i, lim) * out,
               *reinterpret_cast<const u32x4*>(&ys[(yrow + 4 * i) * Y2LD + ypl * 32 + yq4 * 8]));
+      __syncthreads();
     }
   };
   for (int64_t tile = 0; tile < ntiles; ++tile) {
-    step(std::integral_constant<int, 0>{}, pa, tile, zs[0]);
-    step(std::integral_constant<int, 1>{}, pb, tile, zs[1]);
-    step(std::integral_constant<int, 2>{}, pa, tile, zs[0]);
-    step(std::integral_constant<int, 3>{}, pb, tile, zs[1]);
+    step(std::integral_constant<int, 0>{}, pa, tile);
+    step(std::integral_constant<int, 1>{}, pb, tile);
+    step(std::integral_constant<int, 2>{}, pa, tile);
+    step(std::integral_constant<int, 3>{}, pb, tile);
   }
 }
 
@@ -487,35 +496,33 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_data_kernel(
 }
 
 // --------------------------------------------------------------------------
-// stage 2 backward, weights: dL[g,p,t] = sum_b dV[b, g*128 + p] Z[b, t*b2 + g]
+// stage 2 backward, weights: dL[g,p,t] = sum_b dV[b, g*128 + p] W[b, g*128 + t]
 // --------------------------------------------------------------------------
-// Workgroup: 8 L blocks x a 32-wide slice of p x a batch chunk. 8 waves;
-// wave w owns block g0 + w with accumulators dL[32 p x 128 t] in VGPRs. Tile:
-// 32 rows = one K step; the next two tiles' panels are in flight in registers.
-// Both operands need consecutive rows per lane (K = batch): dV panels ->
-// LDS [g][p][pos] through 2x8 register transposes, Z panels -> LDS
-// [g][t][pos] through 4x8 transposes. A sum over rows may take them in any
-// order, so LDS position pos holds tile row (pos%4)*8 + pos/4 in both
-// operands: every load instruction then reads whole 128-byte lines (8
-// consecutive rows of a panel) and each thread still ends up with adjacent
-// positions. The chunk's sum is written as an fp32 partial.
-__global__ __launch_bounds__(512) void sq_stage2_bwd_weight_kernel(
-    const uint16_t* __restrict__ dV, const uint16_t* __restrict__ Z, float* __restrict__ partial,
+// Workgroup: one L block x a batch chunk, all p and t. 4 waves; wave w owns
+// p in [32w, +32): accumulators dL[32 p x 128 t] in VGPRs. Tile: 32 rows =
+// one K step; two tiles in flight in registers. dV and W are both
+// block-major panels: waves 0-1 load dV, waves 2-3 load W, each thread 4
+// rows of one panel. Both MFMA operands need consecutive batch rows per
+// lane, so a 4x8 register transpose gives 8-byte LDS writes of
+// [feature][position] tiles. A sum over rows may take them in any order:
+// position 4rq + i holds row rq + 8i in both operands, so every load
+// instruction reads whole 128-byte lines (8 consecutive rows of a panel).
+// The chunk's sum is written as an fp32 partial.
+__device__ __forceinline__ int fl_row(int f) { return f * TLD + (f >> 3) * 8; }  // LDS row of feature f
+
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void sq_stage2_bwd_weight_kernel(
+    const uint16_t* __restrict__ dV, const uint16_t* __restrict__ Wz, float* __restrict__ partial,
     int64_t B, int nb2, int64_t rows_per) {
   constexpr int T = 32;
-  __shared__ __attribute__((aligned(16))) uint16_t dvs[8 * 32 * TLD];
-  __shared__ __attribute__((aligned(16))) uint16_t zst[8 * Q * TLD];
-  const int n_groups = nb2 >> 3;
-  const int logical = xcd_logical(blockIdx.x, gridDim.x);
-  const int ps = logical & 3;
-  const int gg = (logical >> 2) % n_groups;
-  const int chunk = (logical >> 2) / n_groups;
+  constexpr int TS = Q * TLD + Q;   // one operand's [128][positions] tile (+ skew)
+  __shared__ __attribute__((aligned(16))) uint16_t ts[2 * TS];
+  const int g = blockIdx.x % nb2;
+  const int chunk = blockIdx.x / nb2;
   const int64_t row0 = static_cast<int64_t>(chunk) * rows_per;
   const int64_t row1 = row0 + rows_per < B ? row0 + rows_per : B;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l15 = lane & 15, lh = lane >> 4;
-  const uint32_t Bu = static_cast<uint32_t>(B);
-  const uint32_t pstride = nb2 >> 3;
 
   f32x4 acc[2][8];
 #pragma unroll
@@ -523,61 +530,36 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_weight_kernel(
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = zero4();
 
-  // dV: thread (rp = tid&15, po = (tid>>4)&3, gl = tid>>6) loads positions
-  // 2rp, 2rp+1 (rows vr0 and vr0 + 8) of panel (g0+gl)*16 + 4ps + po
-  const int vrp = tid & 15, vpo = (tid >> 4) & 3, vgl = tid >> 6;
-  const int vr0 = 16 * (vrp & 1) + (vrp >> 1);
-  const uint32_t vcol = ((gg * 8 + vgl) * 16 + 4 * ps + vpo) * Bu * 8;
-  // Z: thread (rq = tid&7, tl = tid>>3) loads positions 4rq..4rq+3 (rows
-  // rq + 8i) of t = tl + 64j
-  const int zrq = tid & 7, ztl = tid >> 3;
-  const uint32_t zcol = (ztl * pstride + gg) * Bu * 8;
-  const uint32_t zstep = 64 * pstride * Bu * 8;
+  // loader role: thread (rq = lt&7, pl = lt>>3) loads rows rq + 8i of panel
+  // g*16 + pl (features 8pl ..) of dV or W
+  const bool is_w = w >= 2;
+  const int lt = tid & 127, rq = lt & 7, pl = lt >> 3;
+  const uint16_t* src = (is_w ? Wz : dV) + static_cast<int64_t>(g * 16 + pl) * B * 8;
+  uint16_t* tdst = &ts[(is_w ? TS : 0) + fl_row(pl * 8) + 4 * rq];
 
-  auto gload = [&](u32x4(&pv)[2], u32x4(&pz)[8], int64_t b0) {
+  auto gload = [&](u32x4(&pre)[4], int64_t b0) {
     const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
-    const uint16_t* vb = dV + bc * 8 + vcol;
+    const uint16_t* base = src + bc * 8;
 #pragma unroll
-    for (int i = 0; i < 2; ++i) pv[i] = ldg16(vb + clamp_row(vr0 + 8 * i, lim) * 8);
-    const uint16_t* zb = Z + bc * 8 + zcol;
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) pz[4 * j + i] = ldg16(zb + j * zstep + clamp_row(zrq + 8 * i, lim) * 8);
+    for (int i = 0; i < 4; ++i) pre[i] = ldg16(base + clamp_row(rq + 8 * i, lim) * 8);
   };
-  auto body = [&](u32x4(&pv)[2], u32x4(&pz)[8], int64_t b0) {
-    // rows past the range were loaded clamped; zero their dV here, where the
-    // values are consumed (a select right after the load would make the
-    // compiler wait for the prefetch at once)
-    pin(pv);
-    pin(pz);
+  auto body = [&](u32x4(&pre)[4], int64_t b0) {
+    pin(pre);
+    // dV rows past the range were loaded clamped: zero them (W rows stay)
 #pragma unroll
-    for (int i = 0; i < 2; ++i) pv[i] = zero_unless(b0 + vr0 + 8 * i < row1, pv[i]);
+    for (int i = 0; i < 4; ++i) pre[i] = zero_unless(is_w || b0 + rq + 8 * i < row1, pre[i]);
+    u32x2 tr[8];
+    transpose4x8(pre, tr);
 #pragma unroll
-    for (int k = 0; k < 4; ++k) {
-      // positions 2rp, 2rp+1 of p = 8po + 2k (lo halves) and 8po + 2k + 1 (hi halves)
-      const uint32_t even = (pv[0][k] & 0xffffu) | (pv[1][k] << 16);
-      const uint32_t odd = (pv[0][k] >> 16) | (pv[1][k] & 0xffff0000u);
-      *reinterpret_cast<uint32_t*>(&dvs[(vgl * 32 + 8 * vpo + 2 * k) * TLD + 2 * vrp]) = even;
-      *reinterpret_cast<uint32_t*>(&dvs[(vgl * 32 + 8 * vpo + 2 * k + 1) * TLD + 2 * vrp]) = odd;
-    }
-#pragma unroll
-    for (int j = 0; j < 2; ++j) {
-      const u32x4 blk[4] = {pz[4 * j], pz[4 * j + 1], pz[4 * j + 2], pz[4 * j + 3]};
-      u32x2 tr[8];
-      transpose4x8(blk, tr);
-#pragma unroll
-      for (int e = 0; e < 8; ++e)
-        *reinterpret_cast<u32x2*>(&zst[(e * Q + ztl + 64 * j) * TLD + 4 * zrq]) = tr[e];
-    }
+    for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x2*>(tdst + e * TLD) = tr[e];
     __syncthreads();
-    gload(pv, pz, b0 + 2 * T);
+    gload(pre, b0 + 2 * T);
     bf16x8 A[2];
 #pragma unroll
-    for (int mt = 0; mt < 2; ++mt) A[mt] = frag_ld(&dvs[(w * 32 + 16 * mt + l15) * TLD + 8 * lh]);
+    for (int mt = 0; mt < 2; ++mt) A[mt] = frag_ld(&ts[fl_row(32 * w + 16 * mt + l15) + 8 * lh]);
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt) {
-      const bf16x8 Bv = frag_ld(&zst[(w * Q + 16 * nt + l15) * TLD + 8 * lh]);
+      const bf16x8 Bv = frag_ld(&ts[TS + fl_row(16 * nt + l15) + 8 * lh]);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt) acc[mt][nt] = mfma(A[mt], Bv, acc[mt][nt]);
     }
@@ -586,27 +568,25 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_weight_kernel(
 
   if (row0 < row1) {
     const int64_t npairs = (row1 - row0 + 2 * T - 1) / (2 * T);
-    u32x4 va[2], za[8], vb[2], zb[8];
-    gload(va, za, row0);
-    gload(vb, zb, row0 + T);
-    pin(va);
-    pin(za);
-    pin(vb);
-    pin(zb);
+    u32x4 pa[4], pb[4];
+    gload(pa, row0);
+    gload(pb, row0 + T);
+    pin(pa);
+    pin(pb);
     for (int64_t k = 0; k < npairs; ++k) {
-      body(va, za, row0 + 2 * k * T);
-      body(vb, zb, row0 + (2 * k + 1) * T);
+      body(pa, row0 + 2 * k * T);
+      body(pb, row0 + (2 * k + 1) * T);
     }
   }
   // partial[chunk][g][p][t]
-  float* P = partial + (static_cast<int64_t>(chunk) * nb2 + gg * 8 + w) * Q * Q;
+  float* P = partial + (static_cast<int64_t>(chunk) * nb2 + g) * Q * Q;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
     for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        P[(32 * ps + 16 * mt + 4 * lh + v) * Q + 16 * nt + l15] = acc[mt][nt][v];
+        P[(32 * w + 16 * mt + 4 * lh + v) * Q + 16 * nt + l15] = acc[mt][nt][v];
 }
 
 // --------------------------------------------------------------------------
@@ -765,7 +745,9 @@ int64_t clamp64(int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > h
 bool sq_applicable(int64_t in, int64_t out, int64_t nb1, int64_t nb2, int64_t batch,
                    int dtype_bf16) {
   if (!dtype_bf16) return false;
-  if (nb1 != nb2 || nb2 % 32 != 0) return false;
+  // the stage-1 forward writes whole 8-t pieces from 8 R blocks: 128/nb must
+  // be a whole number, and the stage-2 forward takes blocks 32 at a time
+  if (nb1 != nb2 || (nb2 != 32 && nb2 != 64 && nb2 != 128)) return false;
   if (in != nb1 * Q || out != nb2 * Q) return false;
   // 32-bit element offsets inside the kernels
   return batch * out < (int64_t(1) << 31);
@@ -774,9 +756,9 @@ bool sq_applicable(int64_t in, int64_t out, int64_t nb1, int64_t nb2, int64_t ba
 SqPlan sq_plan(int64_t batch, int64_t nb) {
   SqPlan p;
   const int64_t groups = nb / 32;   // 32-block groups of the stage-2 kernels
-  // stage-1 forward: ~2048 workgroups of single blocks
-  p.fwd1_chunks = clamp64(2048 / nb, 1, cdiv(batch, 32));
-  p.fwd1_rows = round_up(cdiv(batch, p.fwd1_chunks), 32);
+  // stage-1 forward: nb/8 block groups x row ranges ~ one workgroup per CU
+  p.fwd1_chunks = clamp64(256 / (nb / 8), 1, cdiv(batch, 16));
+  p.fwd1_rows = round_up(cdiv(batch, p.fwd1_chunks), 16);
   p.fwd1_chunks = cdiv(batch, p.fwd1_rows);
   // stage-2 data kernels: groups x 4 slices x row ranges ~ one workgroup per CU
   p.s2_ranges = clamp64(256 / (groups * 4), 1, cdiv(batch, 16));
@@ -786,8 +768,8 @@ SqPlan sq_plan(int64_t batch, int64_t nb) {
   p.d2_ranges = clamp64(256 / (nb / 8), 1, cdiv(batch, 16));
   p.d2_rows = round_up(cdiv(batch, p.d2_ranges), 16);
   p.d2_ranges = cdiv(batch, p.d2_rows);
-  // stage-2 weight gradient: nb/8 block groups x 4 p slices x chunks ~ 256
-  p.w2_chunks = clamp64(256 / (nb / 8 * 4), 1, cdiv(batch, 32));
+  // stage-2 weight gradient: nb blocks x chunks ~ three 4-wave workgroups per CU
+  p.w2_chunks = clamp64(768 / nb, 1, cdiv(batch, 32));
   p.w2_rows = round_up(cdiv(batch, p.w2_chunks), 32);
   p.w2_chunks = cdiv(batch, p.w2_rows);
   // stage-1 backward: 2 workgroups of 8 waves per CU
@@ -807,10 +789,16 @@ hipError_t sq_launch_transpose_weights(const void* w1, const void* w2, void* w1t
 
 hipError_t sq_launch_stage1_fwd(const void* x, const void* w1, void* z, int64_t batch, int64_t nb,
                                 const SqPlan& p, hipStream_t s) {
-  hipLaunchKernelGGL(sq_stage1_fwd_kernel, dim3(static_cast<unsigned>(nb * p.fwd1_chunks)),
-                     dim3(256), 0, s, static_cast<const uint16_t*>(x),
-                     static_cast<const uint16_t*>(w1), static_cast<uint16_t*>(z), batch,
-                     static_cast<int>(nb), p.fwd1_rows);
+  const dim3 grid(static_cast<unsigned>(nb / 8 * p.fwd1_chunks)), block(512);
+  const uint16_t* xp = static_cast<const uint16_t*>(x);
+  const uint16_t* wp = static_cast<const uint16_t*>(w1);
+  uint16_t* zp = static_cast<uint16_t*>(z);
+  switch (nb) {
+    case 32: hipLaunchKernelGGL(sq_stage1_fwd_kernel<5>, grid, block, 0, s, xp, wp, zp, batch, p.fwd1_rows); break;
+    case 64: hipLaunchKernelGGL(sq_stage1_fwd_kernel<6>, grid, block, 0, s, xp, wp, zp, batch, p.fwd1_rows); break;
+    case 128: hipLaunchKernelGGL(sq_stage1_fwd_kernel<7>, grid, block, 0, s, xp, wp, zp, batch, p.fwd1_rows); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 
@@ -846,7 +834,7 @@ hipError_t sq_launch_stage2_bwd_data(const void* dv, const void* w2t, void* dz, 
 hipError_t sq_launch_stage2_bwd_weight(const void* dv, const void* z, float* partial,
                                        int64_t batch, int64_t nb, const SqPlan& p, hipStream_t s) {
   hipLaunchKernelGGL(sq_stage2_bwd_weight_kernel,
-                     dim3(static_cast<unsigned>(nb / 8 * 4 * p.w2_chunks)), dim3(512), 0, s,
+                     dim3(static_cast<unsigned>(nb * p.w2_chunks)), dim3(256), 0, s,
                      static_cast<const uint16_t*>(dv), static_cast<const uint16_t*>(z), partial,
                      batch, static_cast<int>(nb), p.w2_rows);
   return hipGetLastError();

@@ -142,12 +142,13 @@ def test_binding_raises_on_error():
 
 
 def test_path_selection():
-    # 128x128 bf16 blocks with a multiple of 32 blocks take the square fast path
+    # 128x128 bf16 blocks, 32, 64 or 128 of them, take the square fast path
     for n, nb in [(16384, 128), (8192, 64), (4096, 32)]:
         assert all(k.startswith("sq128") for k in M.monarch_describe(0, n, n, nb, nb, 64, B.BF16))
         assert M.monarch_describe(1, n, n, nb, nb, 64, B.BF16)[0].startswith("sq128")
     # everything else takes the generic path
     for args in [(16384, 16384, 128, 128, 64, B.F32), (1024, 1024, 32, 32, 64, B.BF16),
                  (1024, 1024, 8, 8, 64, B.BF16), (2048, 2048, 16, 16, 64, B.BF16),
-                 (768, 3072, 4, 4, 64, B.BF16), (512, 512, 4, 4, 64, B.BF16)]:
+                 (768, 3072, 4, 4, 64, B.BF16), (512, 512, 4, 4, 64, B.BF16),
+                 (12288, 12288, 96, 96, 64, B.BF16)]:
         assert M.monarch_describe(0, *args)[0].startswith("generic")

@@ -241,7 +241,7 @@ SHAPES = [
     (2048, 2048, 16, 16, 129),
     (4096, 4096, 64, 64, 65),
     (16384, 16384, 128, 128, 96),
-    # 128x128 blocks with a multiple of 32 blocks: the bf16 fast path
+    # 128x128 blocks, 32, 64 or 128 of them: the bf16 fast path
     (4096, 4096, 32, 32, 1),
     (4096, 4096, 32, 32, 200),
     (8192, 8192, 64, 64, 77),
