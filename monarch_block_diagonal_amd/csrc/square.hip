@@ -45,6 +45,10 @@ __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
 __device__ __forceinline__ void stg16(uint16_t* p, u32x4 v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }
+// streaming store for final outputs that no later kernel of the pass reads
+__device__ __forceinline__ void stg16_nt(uint16_t* p, u32x4 v) {
+  __builtin_nontemporal_store(v, reinterpret_cast<u32x4*>(p));
+}
 __device__ __forceinline__ bf16x8 frag_ld(const uint16_t* p) {
   return as_bf16x8(*reinterpret_cast<const u16x8*>(p));
 }
@@ -337,8 +341,8 @@ __global__ __launch_bounds__(512) void sq_stage2_fwd_kernel(const uint16_t* __re
       uint16_t* yb = Y + bc * out + ycol;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
-        stg16(yb + clamp_row(yrow + 4 * i, lim) * out,
-              *reinterpret_cast<const u32x4*>(&ys[(yrow + 4 * i) * Y2LD + ypl * 32 + yq4 * 8]));
+        stg16_nt(yb + clamp_row(yrow + 4 * i, lim) * out,
+                 *reinterpret_cast<const u32x4*>(&ys[(yrow + 4 * i) * Y2LD + ypl * 32 + yq4 * 8]));
       __syncthreads();
     }
   };
@@ -689,8 +693,8 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
     const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-      stg16(dX + bc * in + clamp_row(xrow + 32 * i, lim) * in + r * Q + xseg * 8,
-            *reinterpret_cast<const u32x4*>(&dxs[(xrow + 32 * i) * XLD + xseg * 8]));
+      stg16_nt(dX + bc * in + clamp_row(xrow + 32 * i, lim) * in + r * Q + xseg * 8,
+               *reinterpret_cast<const u32x4*>(&dxs[(xrow + 32 * i) * XLD + xseg * 8]));
   };
 
   if (row0 < row1) {
