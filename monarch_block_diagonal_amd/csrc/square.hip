@@ -236,10 +236,11 @@ __global__ __launch_bounds__(512) void sq_stage1_fwd_kernel(const uint16_t* __re
 // Workgroup: 32 L blocks g0..g0+31 x a 32-wide slice of p x a row range, so
 // each (row, p) of Y gets a 64-byte run. 8 waves; wave w owns blocks
 // g0+4w..+3 for the 32 p of the slice (L fragments: 128 VGPRs). Row tile: 16
-// rows; the t contraction runs in 4 chunks of 32. The MFMA B operands
-// (W[b][8 t] of one block) are 16-byte pieces of the W panels, loaded
-// straight into registers two chunks ahead. C = Vᵀ[p x b] = L[p x t] ·
-// Wᵀ[t x b]; after 4 chunks the tile -> LDS [row][p][g] -> Y.
+// rows; the t contraction runs in 4 chunks of 32, in an order rotated by the
+// p slice. The MFMA B operands (W[b][8 t] of one block) are 16-byte pieces
+// of the W panels, loaded straight into registers two chunks ahead.
+// C = Vᵀ[p x b] = L[p x t] · Wᵀ[t x b]; after 4 chunks the tile -> LDS
+// [row][p][g] -> Y.
 constexpr int Y2LD = 32 * 32 + 8;    // pitch of [row][32 p][32 g]
 
 __global__ __launch_bounds__(512) void sq_stage2_fwd_kernel(const uint16_t* __restrict__ Wz,
@@ -260,7 +261,11 @@ __global__ __launch_bounds__(512) void sq_stage2_fwd_kernel(const uint16_t* __re
   const uint32_t out = static_cast<uint32_t>(nb2) * Q;
   const uint32_t Bu = static_cast<uint32_t>(B);
 
-  // a[g][mt][ks] = L[g0+4w+g][p = 32ps + 16mt + l15][t = 32ks + 8lh ..]
+  // The four workgroups of a block group (one per p slice) read the same W
+  // pieces. Each takes the tile's t chunks in its own rotated order (chunk j
+  // of the tile is t chunk (j + ps) % 4), so they do not request the same
+  // lines at the same moment; the lines are L2 hits for the later ones.
+  // a[g][mt][j] = L[g0+4w+g][p = 32ps + 16mt + l15][t = 32((j + ps) % 4) + 8lh ..]
   bf16x8 a[4][2][4];
 #pragma unroll
   for (int g = 0; g < 4; ++g) {
@@ -268,8 +273,8 @@ __global__ __launch_bounds__(512) void sq_stage2_fwd_kernel(const uint16_t* __re
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks)
-        a[g][mt][ks] = frag_ld(Lg + (32 * ps + 16 * mt + l15) * Q + 32 * ks + 8 * lh);
+      for (int j = 0; j < 4; ++j)
+        a[g][mt][j] = frag_ld(Lg + (32 * ps + 16 * mt + l15) * Q + 32 * ((j + ps) & 3) + 8 * lh);
   }
 
   // operand pieces: panel (g0+4w+g)*16 + 4tc + lh, row b0 + l15
@@ -280,12 +285,12 @@ __global__ __launch_bounds__(512) void sq_stage2_fwd_kernel(const uint16_t* __re
   const int yq4 = tid & 3, ypl = (tid >> 2) & 31, yrow = tid >> 7;
   const uint32_t ycol = (32 * ps + ypl) * nb2 + gq * 32 + yq4 * 8;
 
-  // chunk c of the row range: tile c>>2, t chunk c&3
+  // chunk c of the row range: tile c>>2, t chunk (c + ps) & 3
   auto gload = [&](u32x4(&pre)[4], int64_t c) {
     const int64_t b0 = row0 + (c >> 2) * T;
     const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
     const uint16_t* base = Wz + (bc + clamp_row(l15, lim)) * 8 + wcol +
-                           static_cast<uint32_t>(c & 3) * tstep;
+                           static_cast<uint32_t>((c + ps) & 3) * tstep;
 #pragma unroll
     for (int g = 0; g < 4; ++g) pre[g] = ldg16(base + g * gstep);
   };
