@@ -42,6 +42,10 @@ constexpr int TLD = 32 + 8;   // LDS pitch of [feature][32 rows] tiles
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
+// streaming load for the last reader of a tensor in the pass
+__device__ __forceinline__ u32x4 ldg16_nt(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 __device__ __forceinline__ void stg16(uint16_t* p, u32x4 v) {
   *reinterpret_cast<u32x4*>(p) = v;
 }
@@ -212,7 +216,7 @@ __global__ __launch_bounds__(512) void sq_stage1_fwd_kernel(const uint16_t* __re
     for (int i = 0; i < 4; ++i) {
       const int pid = spid + 32 * i;
       const uint32_t panel = (pid / NPC) * 16 + rg * NPC + pid % NPC;
-      stg16(zb + panel * Bu * 8, *reinterpret_cast<const u32x4*>(&zs[pid * ZP + srow * 8]));
+      stg16_nt(zb + panel * Bu * 8, *reinterpret_cast<const u32x4*>(&zs[pid * ZP + srow * 8]));
     }
     __syncthreads();
   };
@@ -391,10 +395,10 @@ __global__ __launch_bounds__(512) void sq_dv_panels_kernel(const uint16_t* __res
   const int64_t src = b * out + static_cast<int64_t>(16 * pt + 8 * po) * nb2 + (gt * GO + go) * 8;
   u32x4 in[8];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) in[i] = ldg16(dY + src + i * nb2);
+  for (int i = 0; i < 8; ++i) in[i] = ldg16_nt(dY + src + i * nb2);
   if (Ym) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) in[i] = apply_mask(in[i], ldg16(Ym + src + i * nb2));
+    for (int i = 0; i < 8; ++i) in[i] = apply_mask(in[i], ldg16_nt(Ym + src + i * nb2));
   }
   u32x2 lo[8], hi[8];
   transpose4x8(*reinterpret_cast<const u32x4(*)[4]>(&in[0]), lo);
@@ -459,7 +463,7 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_data_kernel(
     const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
     const uint16_t* base = dV + bc * 8 + clamp_row(l15, lim) * 8 + vcol;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) pre[ks] = ldg16(base + ks * vstep);
+    for (int ks = 0; ks < 4; ++ks) pre[ks] = ldg16_nt(base + ks * vstep);
   };
   auto body = [&](u32x4(&cur)[4], int64_t b0) {
     pin(cur);
@@ -487,7 +491,7 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_data_kernel(
     uint16_t* zb = dZ + bc * 8 + clamp_row(zrow, lim) * 8 + zcol;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      stg16(zb + i * zstep, *reinterpret_cast<const u32x4*>(&zs[(zt + 32 * i) * XLD + zrow * 8]));
+      stg16_nt(zb + i * zstep, *reinterpret_cast<const u32x4*>(&zs[(zt + 32 * i) * XLD + zrow * 8]));
     __syncthreads();
   };
 
@@ -550,7 +554,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
     const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
     const uint16_t* base = src + bc * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pre[i] = ldg16(base + clamp_row(rq + 8 * i, lim) * 8);
+    for (int i = 0; i < 4; ++i) pre[i] = ldg16_nt(base + clamp_row(rq + 8 * i, lim) * 8);
   };
   auto body = [&](u32x4(&pre)[4], int64_t b0) {
     pin(pre);
@@ -656,7 +660,7 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
     const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
     const uint16_t* base = src + bc * rstride;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pre[i] = ldg16(base + clamp_row(rq + 16 * i, lim) * rstride);
+    for (int i = 0; i < 4; ++i) pre[i] = ldg16_nt(base + clamp_row(rq + 16 * i, lim) * rstride);
   };
   auto body = [&](u32x4(&pre)[4], int64_t b0) {
     pin(pre);
