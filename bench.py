@@ -62,9 +62,7 @@ def kernel_bytes(name: str, pr: dict) -> float:
         "sq128_dv_panels": e * B * out * (3 if relu else 2),
         "sq128_stage2_bwd_data": e * B * (out + mid) + e * p2,
         "sq128_stage2_bwd_weight": e * B * (out + mid) + e * p2,
-        "transpose_weights": 2 * e * (p1 + p2),
-        "reduce_dw2": e * p2,
-        "reduce_dw1": e * p1,
+        "reduce_dw": e * (p1 + p2),
     }
     for key in sorted(table, key=len, reverse=True):
         if name.endswith(key):

@@ -155,15 +155,23 @@ __global__ __launch_bounds__(256) void generic_gemm_kernel(GemmArgs p, int64_t m
       }
 }
 
+// Elements [0, nA) of the flattened index space reduce partialA, the rest
+// partialB.
 template <typename T>
-__global__ __launch_bounds__(256) void reduce_partials_kernel(const float* __restrict__ ws,
-                                                              void* out, int64_t n,
-                                                              int64_t splits) {
-  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
+__global__ __launch_bounds__(256) void reduce_partials_kernel(const float* __restrict__ wsA,
+                                                              void* outA, int64_t nA,
+                                                              int64_t splitsA,
+                                                              const float* __restrict__ wsB,
+                                                              void* outB, int64_t nB,
+                                                              int64_t splitsB) {
+  for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < nA + nB;
        e += static_cast<int64_t>(gridDim.x) * 256) {
+    const bool a = e < nA;
+    const float* ws = a ? wsA : wsB;
+    const int64_t n = a ? nA : nB, i = a ? e : e - nA, splits = a ? splitsA : splitsB;
     float s = 0.f;
-    for (int64_t k = 0; k < splits; ++k) s += ws[k * n + e];
-    Io<T>::store(out, e, s);
+    for (int64_t k = 0; k < splits; ++k) s += ws[k * n + i];
+    Io<T>::store(a ? outA : outB, i, s);
   }
 }
 
@@ -204,17 +212,19 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_reduce_partials(const float* partial, void* out, int64_t n, int64_t splits,
+hipError_t launch_reduce_partials(const float* partialA, void* outA, int64_t nA, int64_t splitsA,
+                                  const float* partialB, void* outB, int64_t nB, int64_t splitsB,
                                   bool bf16, hipStream_t s) {
+  const int64_t n = nA + nB;
   if (n <= 0) return hipSuccess;
   int64_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (bf16)
     hipLaunchKernelGGL(reduce_partials_kernel<uint16_t>, dim3(static_cast<unsigned>(blocks)),
-                       dim3(256), 0, s, partial, out, n, splits);
+                       dim3(256), 0, s, partialA, outA, nA, splitsA, partialB, outB, nB, splitsB);
   else
     hipLaunchKernelGGL(reduce_partials_kernel<float>, dim3(static_cast<unsigned>(blocks)),
-                       dim3(256), 0, s, partial, out, n, splits);
+                       dim3(256), 0, s, partialA, outA, nA, splitsA, partialB, outB, nB, splitsB);
   return hipGetLastError();
 }
 

@@ -42,9 +42,11 @@ hipError_t launch_generic_gemm(const GemmArgs& a, bool bf16, hipStream_t s);
 // capture it in a graph). p must be 2-byte aligned and bytes a multiple of 2.
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
-// out[e] = sum_{s < splits} partial[s*n + e] in increasing s, stored in the
-// I/O type (fixed order: bit-reproducible).
-hipError_t launch_reduce_partials(const float* partial, void* out, int64_t n, int64_t splits,
+// Both weight gradients in one launch: outA[e] = sum_{s < splitsA} partialA[s*nA + e]
+// in increasing s (likewise B), stored in the I/O type (fixed order:
+// bit-reproducible).
+hipError_t launch_reduce_partials(const float* partialA, void* outA, int64_t nA, int64_t splitsA,
+                                  const float* partialB, void* outB, int64_t nB, int64_t splitsB,
                                   bool bf16, hipStream_t s);
 
 }  // namespace monarch

@@ -22,7 +22,7 @@ struct Problem {
   int64_t s2 = 1, kc2 = 0, s1 = 1, kc1 = 0;
   SqPlan sq;  // launch geometry of PATH_SQ128
   // workspace layout (byte offsets)
-  size_t ws_dz = 0, ws_p2 = 0, ws_p1 = 0, ws_wt = 0, ws_dv = 0, ws_total = 0;
+  size_t ws_dz = 0, ws_p2 = 0, ws_p1 = 0, ws_dv = 0, ws_total = 0;
 };
 
 struct Buffers {
@@ -47,10 +47,8 @@ enum StepKind {
   GEN_STAGE2_BWD_WEIGHT,
   GEN_STAGE1_BWD_DATA,
   GEN_STAGE1_BWD_WEIGHT,
-  REDUCE_DW2,
-  REDUCE_DW1,
+  REDUCE_DW,
   ZERO_DW,
-  SQ_TRANSPOSE_W,
   SQ_DV_PANELS,
   SQ_STAGE1_FWD,
   SQ_STAGE2_FWD,

@@ -86,10 +86,8 @@ int make_problem(int64_t in, int64_t out, int64_t nb1, int64_t nb2, int64_t batc
     off = align_up(off + static_cast<size_t>(p.s2) * nb2 * p.q2o * p.q2i * 4, 256);
     p.ws_p1 = off;
     off = align_up(off + static_cast<size_t>(p.s1) * nb1 * p.q1o * p.q1i * 4, 256);
-    p.ws_wt = off;
     if (p.path == PATH_SQ128) {
-      // transposed copies of both factors, then the block-major dV panels
-      off = align_up(off + static_cast<size_t>(nb1 * p.q1o * p.q1i + nb2 * p.q2o * p.q2i) * 2, 256);
+      // the block-major dV panels
       p.ws_dv = off;
       off = align_up(off + static_cast<size_t>(batch) * out * p.esize, 256);
     }
@@ -121,21 +119,18 @@ Plan plan_bwd(const Problem& pr) {
     return p;
   }
   if (pr.path == PATH_SQ128) {
-    p.add(SQ_TRANSPOSE_W);
     p.add(SQ_DV_PANELS);
     p.add(SQ_STAGE2_BWD_DATA);
     p.add(SQ_STAGE2_BWD_WEIGHT);
     p.add(SQ_STAGE1_BWD);
-    p.add(REDUCE_DW2);
-    p.add(REDUCE_DW1);
+    p.add(REDUCE_DW);
     return p;
   }
   p.add(GEN_STAGE2_BWD_DATA);
   p.add(GEN_STAGE2_BWD_WEIGHT);
   p.add(GEN_STAGE1_BWD_DATA);
   p.add(GEN_STAGE1_BWD_WEIGHT);
-  p.add(REDUCE_DW2);
-  p.add(REDUCE_DW1);
+  p.add(REDUCE_DW);
   return p;
 }
 
@@ -147,10 +142,8 @@ const char* step_name(StepKind k) {
     case GEN_STAGE2_BWD_WEIGHT: return "generic_stage2_bwd_weight";
     case GEN_STAGE1_BWD_DATA: return "generic_stage1_bwd_data";
     case GEN_STAGE1_BWD_WEIGHT: return "generic_stage1_bwd_weight";
-    case REDUCE_DW2: return "reduce_dw2";
-    case REDUCE_DW1: return "reduce_dw1";
+    case REDUCE_DW: return "reduce_dw";
     case ZERO_DW: return "zero_dw";
-    case SQ_TRANSPOSE_W: return "sq128_transpose_weights";
     case SQ_DV_PANELS: return "sq128_dv_panels";
     case SQ_STAGE1_FWD: return "sq128_stage1_fwd";
     case SQ_STAGE2_FWD: return "sq128_stage2_fwd";
@@ -168,8 +161,6 @@ hipError_t launch_step(StepKind k, const Problem& pr, const Buffers& b, hipStrea
   float* p2 = ws ? reinterpret_cast<float*>(ws + pr.ws_p2) : nullptr;
   float* p1 = ws ? reinterpret_cast<float*>(ws + pr.ws_p1) : nullptr;
   const void* mask = pr.act == MONARCH_ACT_RELU ? b.y : nullptr;
-  uint16_t* w1t = ws ? reinterpret_cast<uint16_t*>(ws + pr.ws_wt) : nullptr;
-  uint16_t* w2t = w1t ? w1t + pr.b1 * pr.q1o * pr.q1i : nullptr;
   void* dv = ws ? ws + pr.ws_dv : nullptr;
   GemmArgs a;
   switch (k) {
@@ -226,12 +217,9 @@ hipError_t launch_step(StepKind k, const Problem& pr, const Buffers& b, hipStrea
       a.partial = p1, a.splits = pr.s1, a.k_chunk = pr.kc1;
       a.M = pr.q1o, a.N = pr.q1i, a.K = pr.batch, a.nblk = pr.b1;
       return launch_generic_gemm(a, bf16, s);
-    case REDUCE_DW2:
-      return launch_reduce_partials(p2, b.dw2, pr.b2 * pr.q2o * pr.q2i, pr.s2, bf16, s);
-    case REDUCE_DW1:
-      return launch_reduce_partials(p1, b.dw1, pr.b1 * pr.q1o * pr.q1i, pr.s1, bf16, s);
-    case SQ_TRANSPOSE_W:
-      return sq_launch_transpose_weights(b.w1, b.w2, w1t, w2t, pr.b1, s);
+    case REDUCE_DW:
+      return launch_reduce_partials(p2, b.dw2, pr.b2 * pr.q2o * pr.q2i, pr.s2, p1, b.dw1,
+                                    pr.b1 * pr.q1o * pr.q1i, pr.s1, bf16, s);
     case SQ_DV_PANELS:
       return sq_launch_dv_panels(b.dy, mask, dv, pr.batch, pr.b2, s);
     case SQ_STAGE1_FWD:
@@ -240,11 +228,11 @@ hipError_t launch_step(StepKind k, const Problem& pr, const Buffers& b, hipStrea
       return sq_launch_stage2_fwd(b.z_out, b.w2, b.y_out, pr.batch, pr.b2,
                                   pr.act == MONARCH_ACT_RELU, pr.sq, s);
     case SQ_STAGE2_BWD_DATA:
-      return sq_launch_stage2_bwd_data(dv, w2t, dz, pr.batch, pr.b2, pr.sq, s);
+      return sq_launch_stage2_bwd_data(dv, b.w2, dz, pr.batch, pr.b2, pr.sq, s);
     case SQ_STAGE2_BWD_WEIGHT:
       return sq_launch_stage2_bwd_weight(dv, b.z, p2, pr.batch, pr.b2, pr.sq, s);
     case SQ_STAGE1_BWD:
-      return sq_launch_stage1_bwd(dz, b.x, w1t, b.dx, p1, pr.batch, pr.b1, pr.sq, s);
+      return sq_launch_stage1_bwd(dz, b.x, b.w1, b.dx, p1, pr.batch, pr.b1, pr.sq, s);
     case ZERO_DW: {
       hipError_t e = launch_zero(b.dw2, static_cast<size_t>(pr.b2 * pr.q2o * pr.q2i) * pr.esize, s);
       if (e != hipSuccess) return e;

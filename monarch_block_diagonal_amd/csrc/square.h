@@ -21,9 +21,6 @@ bool sq_applicable(int64_t in, int64_t out, int64_t nb1, int64_t nb2, int64_t ba
                    int dtype_bf16);
 SqPlan sq_plan(int64_t batch, int64_t nb);
 
-// w1t/w2t = each 128x128 block of w1/w2 transposed (read by the backward kernels).
-hipError_t sq_launch_transpose_weights(const void* w1, const void* w2, void* w1t, void* w2t,
-                                      int64_t nb, hipStream_t s);
 // Panel layout: feature f of row b at ((f/8)*batch + b)*8 + f%8. z holds
 // stage 2's input W[b, g*128 + t] = Z[b, t*nb + g] in it; dz holds dZ (Z order).
 hipError_t sq_launch_stage1_fwd(const void* x, const void* w1, void* z, int64_t batch, int64_t nb,
@@ -34,13 +31,13 @@ hipError_t sq_launch_stage2_fwd(const void* z, const void* w2, void* y, int64_t 
 // element (b, g*128 + p) at (((g*128+p)/8)*batch + b)*8 + p%8.
 hipError_t sq_launch_dv_panels(const void* dy, const void* ymask, void* dv, int64_t batch,
                                int64_t nb, hipStream_t s);
-hipError_t sq_launch_stage2_bwd_data(const void* dv, const void* w2t, void* dz, int64_t batch,
+hipError_t sq_launch_stage2_bwd_data(const void* dv, const void* w2, void* dz, int64_t batch,
                                      int64_t nb, const SqPlan& p, hipStream_t s);
 // partial: [w2_chunks][nb][128][128] fp32
 hipError_t sq_launch_stage2_bwd_weight(const void* dv, const void* z, float* partial,
                                        int64_t batch, int64_t nb, const SqPlan& p, hipStream_t s);
 // partial: [b1_chunks][nb][128][128] fp32
-hipError_t sq_launch_stage1_bwd(const void* dz, const void* x, const void* w1t, void* dx,
+hipError_t sq_launch_stage1_bwd(const void* dz, const void* x, const void* w1, void* dx,
                                 float* partial, int64_t batch, int64_t nb, const SqPlan& p,
                                 hipStream_t s);
 

@@ -56,6 +56,14 @@ __device__ __forceinline__ void stg16_nt(uint16_t* p, u32x4 v) {
 __device__ __forceinline__ bf16x8 frag_ld(const uint16_t* p) {
   return as_bf16x8(*reinterpret_cast<const u16x8*>(p));
 }
+// 8 elements at a stride of one 128-element block row: a fragment of a
+// transposed weight block, gathered once when a workgroup starts
+__device__ __forceinline__ bf16x8 frag_gather(const uint16_t* p) {
+  u16x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = p[e * 128];
+  return as_bf16x8(v);
+}
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -422,12 +430,12 @@ __global__ __launch_bounds__(512) void sq_dv_panels_kernel(const uint16_t* __res
 // stage 2 backward, data: dZ[b, t*b2 + g] = sum_p dV[b, g*128 + p] L[g,p,t]
 // --------------------------------------------------------------------------
 // 8 waves, 8 L blocks g0..g0+7 per workgroup; wave w owns block g0 + w (all
-// t, Lᵀ fragments from the transposed copy: 128 VGPRs). Tile: 16 rows; the
+// t; Lᵀ fragments gathered from L at the start: 128 VGPRs). Tile: 16 rows; the
 // MFMA B operands (dV_g[b][8 p]) are 16-byte pieces of the dV panels, loaded
 // straight into registers two tiles ahead. C = dZᵀ[t x b] = Lᵀ[t x p] ·
 // dVᵀ[p x b]; results -> LDS [t][row][g] -> dZ panels (256-byte runs).
 __global__ __launch_bounds__(512) void sq_stage2_bwd_data_kernel(
-    const uint16_t* __restrict__ dV, const uint16_t* __restrict__ W2t,
+    const uint16_t* __restrict__ dV, const uint16_t* __restrict__ W2,
     uint16_t* __restrict__ dZ, int64_t B, int nb2, int64_t rows_per) {
   constexpr int T = 16;
   __shared__ __attribute__((aligned(16))) uint16_t zs[Q * XLD];
@@ -445,11 +453,11 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_data_kernel(
 
   // A = Lᵀ[t x p]: lane holds L[g][p = 32ks + 8lh + e][t = 16mt + l15]
   bf16x8 a[8][4];
-  const uint16_t* Ltg = W2t + static_cast<int64_t>(g) * Q * Q;
+  const uint16_t* Lg = W2 + static_cast<int64_t>(g) * Q * Q;
 #pragma unroll
   for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) a[mt][ks] = frag_ld(Ltg + (16 * mt + l15) * Q + 32 * ks + 8 * lh);
+    for (int ks = 0; ks < 4; ++ks) a[mt][ks] = frag_gather(Lg + (32 * ks + 8 * lh) * Q + 16 * mt + l15);
 
   // operand pieces: panel g*16 + 4ks + lh, row b0 + l15
   const uint32_t vcol = ((g * 16 + lh) * Bu) * 8;
@@ -619,7 +627,7 @@ constexpr int PLD = T1 + 8;       // LDS pitch of [feature][64 positions] tiles
 
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void sq_stage1_bwd_kernel(
     const uint16_t* __restrict__ dZ, const uint16_t* __restrict__ X,
-    const uint16_t* __restrict__ W1t, uint16_t* __restrict__ dX, float* __restrict__ partial,
+    const uint16_t* __restrict__ W1, uint16_t* __restrict__ dX, float* __restrict__ partial,
     int64_t B, int nb1, int64_t rows_per) {
   constexpr int T = T1;
   __shared__ __attribute__((aligned(16))) uint16_t dzs[T * XLD];   // [row][k]
@@ -635,11 +643,11 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
   const uint32_t in = static_cast<uint32_t>(nb1) * Q;
   const uint32_t Bu = static_cast<uint32_t>(B);
 
-  // A = Rᵀ[s x k] from the transposed copy: lane holds R[r][k = 32ks + 8lh + e][s = 16w + l15]
+  // A = Rᵀ[s x k], gathered from R: lane holds R[r][k = 32ks + 8lh + e][s = 16w + l15]
   bf16x8 a[4];
-  const uint16_t* Rtr = W1t + static_cast<int64_t>(r) * Q * Q;
+  const uint16_t* Rr = W1 + static_cast<int64_t>(r) * Q * Q;
 #pragma unroll
-  for (int ks = 0; ks < 4; ++ks) a[ks] = frag_ld(Rtr + (16 * w + l15) * Q + 32 * ks + 8 * lh);
+  for (int ks = 0; ks < 4; ++ks) a[ks] = frag_gather(Rr + (32 * ks + 8 * lh) * Q + 16 * w + l15);
   f32x4 accr[8];
 #pragma unroll
   for (int nt = 0; nt < 8; ++nt) accr[nt] = zero4();
@@ -726,29 +734,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
     for (int v = 0; v < 4; ++v) P[(16 * w + 4 * lh + v) * Q + 16 * nt + l15] = accr[nt][v];
 }
 
-// --------------------------------------------------------------------------
-// Wt[blk][c][r] = W[blk][r][c] for 128x128 blocks (both factors in one
-// launch: blocks [0, nb1) of w1 then [0, nb2) of w2). 32x32 sub-tiles
-// through LDS; 256 threads.
-// --------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void sq_transpose_blocks_kernel(
-    const uint16_t* __restrict__ W1, const uint16_t* __restrict__ W2, uint16_t* __restrict__ W1t,
-    uint16_t* __restrict__ W2t, int nb1) {
-  __shared__ uint16_t tile[32][33];
-  const int blk = blockIdx.x >> 4, sub = blockIdx.x & 15;
-  const bool first = blk < nb1;
-  const int64_t bofs = static_cast<int64_t>(first ? blk : blk - nb1) * Q * Q;
-  const uint16_t* src = (first ? W1 : W2) + bofs;
-  uint16_t* dst = (first ? W1t : W2t) + bofs;
-  const int r0 = (sub >> 2) * 32, c0 = (sub & 3) * 32;
-  const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) tile[ty + 8 * i][tx] = src[(r0 + ty + 8 * i) * Q + c0 + tx];
-  __syncthreads();
-#pragma unroll
-  for (int i = 0; i < 4; ++i) dst[(c0 + ty + 8 * i) * Q + r0 + tx] = tile[tx][ty + 8 * i];
-}
-
 int64_t round_up(int64_t v, int64_t m) { return (v + m - 1) / m * m; }
 int64_t cdiv(int64_t a, int64_t b) { return (a + b - 1) / b; }
 int64_t clamp64(int64_t v, int64_t lo, int64_t hi) { return v < lo ? lo : (v > hi ? hi : v); }
@@ -792,14 +777,6 @@ SqPlan sq_plan(int64_t batch, int64_t nb) {
   return p;
 }
 
-hipError_t sq_launch_transpose_weights(const void* w1, const void* w2, void* w1t, void* w2t,
-                                      int64_t nb, hipStream_t s) {
-  hipLaunchKernelGGL(sq_transpose_blocks_kernel, dim3(static_cast<unsigned>(2 * nb * 16)), dim3(256),
-                     0, s, static_cast<const uint16_t*>(w1), static_cast<const uint16_t*>(w2),
-                     static_cast<uint16_t*>(w1t), static_cast<uint16_t*>(w2t), static_cast<int>(nb));
-  return hipGetLastError();
-}
-
 hipError_t sq_launch_stage1_fwd(const void* x, const void* w1, void* z, int64_t batch, int64_t nb,
                                 const SqPlan& p, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(nb / 8 * p.fwd1_chunks)), block(512);
@@ -835,11 +812,11 @@ hipError_t sq_launch_dv_panels(const void* dy, const void* ymask, void* dv, int6
   return hipGetLastError();
 }
 
-hipError_t sq_launch_stage2_bwd_data(const void* dv, const void* w2t, void* dz, int64_t batch,
+hipError_t sq_launch_stage2_bwd_data(const void* dv, const void* w2, void* dz, int64_t batch,
                                      int64_t nb, const SqPlan& p, hipStream_t s) {
   hipLaunchKernelGGL(sq_stage2_bwd_data_kernel, dim3(static_cast<unsigned>(nb / 8 * p.d2_ranges)),
                      dim3(512), 0, s, static_cast<const uint16_t*>(dv),
-                     static_cast<const uint16_t*>(w2t), static_cast<uint16_t*>(dz), batch,
+                     static_cast<const uint16_t*>(w2), static_cast<uint16_t*>(dz), batch,
                      static_cast<int>(nb), p.d2_rows);
   return hipGetLastError();
 }
