@@ -226,6 +226,60 @@ def test_square_n16384_full_size_sampled(api):
         assert abs(v - yy) <= 2e-2 * yy
 
 
+def _dot64(a, b, chunk=8192):
+    """<a, b> in fp64, accumulated over row chunks (bounded temporaries)."""
+    tot = 0.0
+    for i in range(0, a.shape[0], chunk):
+        tot += torch.sum(a[i:i + chunk].double() * b[i:i + chunk].double()).item()
+    return tot
+
+
+def test_square_size_limit_ragged(api):
+    """The fast path at its size limit: 131071 rows x 16384 (batch*out just
+    under 2^31, the kernels' 32-bit offset bound) with a ragged tail of every
+    tile size. Inputs are drawn on the device (seeded, the largest
+    configuration's distributions); sampled rows of Y and dX, including the
+    last ones, against the oracle; the weight gradients through the Euler
+    identities (dY = Y), which hold at any size."""
+    n, nb, B = 16384, 128, 131071
+    assert B * n < 2 ** 31 and (B + 1) * n == 2 ** 31
+    from monarch_block_diagonal_amd import binding as BD
+    names = BD.monarch_describe(1, n, n, nb, nb, B, BD.BF16)
+    assert all(k.startswith("sq128") or k == "reduce_dw" for k in names)
+    say("[parity] size limit: drawing inputs on the device")
+    g = torch.Generator(device="cuda:0")
+    g.manual_seed(S.seed_for(4, S.TID_X) + 7)
+    X = torch.randn((B, n), generator=g, device="cuda:0", dtype=torch.float32).to(torch.bfloat16)
+    g.manual_seed(S.seed_for(4, S.TID_DY) + 7)
+    DY = torch.randn((B, n), generator=g, device="cuda:0", dtype=torch.float32).to(torch.bfloat16)
+    w1 = S.draw(S.seed_for(4, S.TID_W1) + 7, (nb, 128, 128), "normal", 1.0 / 128, "bf16")
+    w2 = S.draw(S.seed_for(4, S.TID_W2) + 7, (nb, 128, 128), "normal", 1.0 / 128, "bf16")
+    W1, W2 = dev(w1, "bf16"), dev(w2, "bf16")
+    say("[parity] size limit: forward + backward")
+    y, z = api.monarch_forward(X, W1, W2)
+    dx, _, _ = api.monarch_backward(DY, X, W1, W2, z)
+    torch.cuda.synchronize()
+    rows = np.array([0, 31, 65536, 131039, 131040, 131056, 131070])
+    ridx = torch.from_numpy(rows).cuda()
+    xr = host(X[ridx]).astype(np.float64)
+    dyr = host(DY[ridx]).astype(np.float64)
+    fac = O.dense_factors(w1, w2, n, n, sparse=True)
+    say("[parity] size limit: oracle on sampled rows")
+    ey = O.rel_frobenius(host(y[ridx]), O.forward_rows(xr, w1, w2, n, n, factors=fac))
+    edx = O.rel_frobenius(host(dx[ridx]), O.backward_dx_rows(dyr, w1, w2, n, n, factors=fac))
+    say(f"[parity] size limit sampled errors y={ey:.3e} dx={edx:.3e}")
+    assert ey <= TOL["bf16"] and edx <= TOL["bf16"]
+    del DY, dx
+    dx2, dw1, dw2 = api.monarch_backward(y, X, W1, W2, z)
+    torch.cuda.synchronize()
+    yy = _dot64(y, y)
+    vals = [_dot64(dx2, X), torch.sum(dw1.double() * W1.double()).item(),
+            torch.sum(dw2.double() * W2.double()).item()]
+    say(f"[parity] size limit Euler: <Y,Y>={yy:.6e} others={vals}")
+    for v in vals:
+        assert abs(v - yy) <= 2e-2 * yy
+
+
 # --------------------------------------------------------------------------
 # shapes: several tiles, ragged tails, rectangular, both dtypes, ReLU
 # --------------------------------------------------------------------------
