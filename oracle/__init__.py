@@ -8,3 +8,4 @@ from .monarch_oracle import (  # noqa: F401
     dense_factors, monarch_matrix, forward, backward, mlp_forward, mlp_backward,
     forward_rows, backward_dx_rows, weight_grad_entries, rel_frobenius,
 )
+from . import monarch_projection  # noqa: F401,E402
