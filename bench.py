@@ -114,6 +114,86 @@ def cpu_baseline(w, rows: int):
             "seconds": dt}
 
 
+def bench_project(args) -> int:
+    """Dense -> Monarch projection of an n x n bf16 matrix (n = 16384, 128
+    blocks of 128 x 128 per factor: 16384 slices of 128 x 128), inputs
+    resident in HBM; one JSON line."""
+    import numpy as np
+    import torch
+    import monarch_block_diagonal_amd as M
+    from monarch_block_diagonal_amd import synthetic as S
+    n, b = 16384, 128
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q = n // b
+    log(f"projection: {n} x {n} bf16, {b} x {b} slices of {q} x {q}, {args.iters} iterations")
+    g = torch.Generator(device=dev)
+    g.manual_seed(S.seed_for(4, S.TID_X) + 99)
+    m = torch.randn((n, n), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
+    w1 = torch.empty((b, b, q), dtype=torch.bfloat16, device=dev)
+    w2 = torch.empty((b, q, b), dtype=torch.bfloat16, device=dev)
+    stream = torch.cuda.current_stream()
+
+    def run():
+        M.monarch_project(m, w1, w2, n, n, b, b, M.BF16, args.iters, stream)
+
+    for _ in range(args.warmup):
+        run()
+    torch.cuda.synchronize()
+    K = args.steps
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(stream)
+    for _ in range(K):
+        run()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / K
+    ms = e0.elapsed_time(e1) / K
+    # fp32 work per slice: column sums, (iters + 1) products A v and iters products Aᵀ u,
+    # 2 flops per multiply-add
+    flops = b * b * 2.0 * q * q * (2 * args.iters + 2)
+    hbm = 2.0 * n * n + 2 * 2.0 * b * b * q
+    tflops = flops / (ms * 1e-3) / 1e12
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import monarch_projection as PJ
+        ns = 2048
+        mh = m[:, : (ns // b) * q].float().cpu().numpy().astype(np.float64)   # slices r < ns/b
+        log(f"cpu baseline: oracle fit of {ns} of {b * b} slices")
+        t1 = time.perf_counter()
+        sl = PJ.slices(np.ascontiguousarray(mh), (ns // b) * q, n, ns // b, b)
+        for gg in range(b):
+            for rr in range(ns // b):
+                PJ.fit_slice(sl[gg, rr])
+        dt = time.perf_counter() - t1
+        try:
+            from threadpoolctl import threadpool_info
+            threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        except Exception:
+            threads = len(os.sched_getaffinity(0))
+        cpu = {"value": round(ns / dt, 1), "unit": "slices/s", "cores": int(threads),
+               "kind": "oracle",
+               "sample": f"{ns} of {b * b} slices ({q} x {q}, fp64 SVD each), {dt:.2f} s",
+               "seconds": dt}
+    result = {
+        "metric": "Monarch projection slices/s", "value": round(b * b / (ms * 1e-3), 1),
+        "unit": "slices/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "wall_ms_per_step": round(wall * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "data": "synthetic (seeded N(0,1) matrix drawn on the device, stored bf16)",
+        "config": {"workload": f"project_n{n}_b{b}", "n": n, "nblocks": b, "iters": args.iters,
+                   "input": "bf16"},
+        "roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": 157.3,
+                     "unit": "TFLOP/s", "frac": round(tflops / 157.3, 4), "traffic": None,
+                     "hbm_bytes": hbm, "hbm_frac": round(hbm / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -126,6 +206,10 @@ def main() -> int:
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (read 1 GiB + write 1 GiB), the "
                          "reference for scaling HBM byte counters")
+    ap.add_argument("--op", choices=("step", "project"), default="step",
+                    help="step: forward + backward (default); project: dense -> Monarch "
+                         "projection of an n x n matrix")
+    ap.add_argument("--iters", type=int, default=32, help="power iterations (--op project)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -133,6 +217,8 @@ def main() -> int:
         print("bench.py runs on one GPU only: the Monarch path here has no multi-GPU "
               "(sharded) implementation, so --gpus must be 1.", file=sys.stderr)
         return 2
+    if args.op == "project":
+        return bench_project(args)
 
     import torch
     import monarch_block_diagonal_amd as M

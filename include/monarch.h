@@ -130,6 +130,31 @@ int monarch_describe(int direction, int64_t in_features, int64_t out_features,
                      int64_t nblocks1, int64_t nblocks2, int64_t batch, int dtype,
                      int act, char* buf, size_t buf_len);
 
+/* Dense -> Monarch projection (scatterbrain issues page, "projection"
+ * thread: M rearranged as '(p k) (r s) -> k r p s', every (k, r) slice fitted
+ * on its own; Monarch paper, abstract: an analytical optimal solution).
+ *
+ * Defined for the Definition C.3 case out_features = nblocks1 * nblocks2 with
+ * in_features % nblocks1 == 0 (then q1o = nblocks2 and q2i = nblocks1). The
+ * Monarch matrix has M[p*b2 + g, r*q1i + s] = w2[g, p, r] * w1[r, g, s], so
+ * slice (g, r) over (p, s) is an outer product and the nearest Monarch matrix
+ * (Frobenius) takes each slice's nearest rank-one matrix.
+ *
+ *   m  [out, in] row-major, read;  w1 [b1, b2, q1i] and w2 [b2, q2o, b1],
+ *   overwritten, in the layouts monarch_fwd takes.
+ *
+ * Each slice is fitted in fp32 by `iters` power iterations (1..4096) from the
+ * column sums of the slice; the rate is (sigma2/sigma1)^2 per iteration and
+ * an exactly rank-one slice is exact after one. The factors split sqrt(sigma)
+ * evenly, with the sign making the largest-magnitude entry of w1[r, g, :]
+ * (the first on ties) positive. A slice must fit in one workgroup's LDS:
+ * q2o * (q1i + 1) + q1i + q2o + 16 <= 40960 fp32 values (128 x 128 slices
+ * fit). Errors as for monarch_fwd; shapes outside the case, iters out of
+ * range or a slice too large give MONARCH_ERR_SHAPE. */
+int monarch_project(const void* m, void* w1, void* w2, int64_t in_features,
+                    int64_t out_features, int64_t nblocks1, int64_t nblocks2, int dtype,
+                    int iters, void* stream);
+
 /* Static text for a status code; for MONARCH_ERR_HIP the last HIP error
  * message recorded on the calling thread. Never NULL. */
 const char* monarch_status_string(int status);

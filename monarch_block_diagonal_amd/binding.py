@@ -30,6 +30,7 @@ ACT_RELU = 1
 EXPORTED = (
     "monarch_fwd", "monarch_bwd", "monarch_bwd_workspace_bytes", "monarch_fwd_traced",
     "monarch_bwd_traced", "monarch_describe", "monarch_status_string", "monarch_abi_version",
+    "monarch_project",
 )
 
 _lib = None
@@ -70,6 +71,8 @@ def load_library():
     lib.monarch_status_string.restype = ctypes.c_char_p
     lib.monarch_abi_version.argtypes = []
     lib.monarch_abi_version.restype = c_int
+    lib.monarch_project.argtypes = [vp] * 3 + [i64] * 4 + [c_int, c_int, vp]
+    lib.monarch_project.restype = c_int
     _lib = lib
     return lib
 
@@ -150,6 +153,13 @@ def monarch_bwd(dy, x, w1, w2, z, y, dx, dw1, dw2, workspace, workspace_bytes, i
     else:
         arr, n = _events(events)
         _check(lib.monarch_bwd_traced(*args, arr, n))
+
+
+def monarch_project(m, w1, w2, in_features, out_features, nblocks1, nblocks2, dtype, iters=32,
+                    stream=None) -> None:
+    lib = load_library()
+    _check(lib.monarch_project(_ptr(m), _ptr(w1), _ptr(w2), in_features, out_features, nblocks1,
+                               nblocks2, dtype, iters, _stream(stream)))
 
 
 def monarch_describe(direction, in_features, out_features, nblocks1, nblocks2, batch, dtype,

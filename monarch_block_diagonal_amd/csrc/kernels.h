@@ -49,4 +49,12 @@ hipError_t launch_reduce_partials(const float* partialA, void* outA, int64_t nA,
                                   const float* partialB, void* outB, int64_t nB, int64_t splitsB,
                                   bool bf16, hipStream_t s);
 
+// Dense -> Monarch projection: one workgroup per (g, r) slice of M
+// [out = nb1*nb2, in]; writes w1 [nb1, nb2, q1i] and w2 [nb2, q2o, nb1].
+// project_lds_bytes is the dynamic LDS one workgroup needs.
+size_t project_lds_bytes(int64_t q1i, int64_t q2o);
+hipError_t launch_project(const void* m, void* w1, void* w2, int64_t in, int64_t nb1,
+                          int64_t nb2, int64_t q1i, int64_t q2o, int iters, bool bf16,
+                          hipStream_t s);
+
 }  // namespace monarch

@@ -69,6 +69,21 @@ def monarch_backward(dy, x, w1, w2, z, y=None, act: int = B.ACT_NONE, stream=Non
     return dx, dw1, dw2
 
 
+def monarch_project(m, nblocks1: int, nblocks2: int, iters: int = 32, stream=None):
+    """Nearest Monarch factors (w1 [b1, b2, in/b1], w2 [b2, out/b2, b1]) of a
+    dense [out, in] matrix; needs out = nblocks1 * nblocks2."""
+    _check(m)
+    if m.dim() != 2:
+        raise ValueError("m must be [out, in]")
+    fo, fi = m.shape
+    if nblocks1 <= 0 or nblocks2 <= 0 or fi % nblocks1 or fo % nblocks2:
+        raise ValueError("block counts must divide the matrix dimensions")
+    w1 = torch.empty((nblocks1, nblocks2, fi // nblocks1), dtype=m.dtype, device=m.device)
+    w2 = torch.empty((nblocks2, fo // nblocks2, nblocks1), dtype=m.dtype, device=m.device)
+    B.monarch_project(m, w1, w2, fi, fo, nblocks1, nblocks2, dtype_code(m), iters, stream)
+    return w1, w2
+
+
 class MonarchLinearFunction(torch.autograd.Function):
     """y = act(x · Mᵀ) with M the Monarch matrix of (w1, w2); no bias."""
 

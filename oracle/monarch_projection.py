@@ -51,6 +51,19 @@ def slices(m: np.ndarray, in_features: int, out_features: int, nblocks1: int,
     return m.transpose(1, 2, 0, 3)
 
 
+def fit_slice(a: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Nearest rank-one matrix of one p x s slice as (l, r) with l r^T the fit:
+    l = sqrt(sigma) u, r = sqrt(sigma) v from the top singular triple, signed so
+    that the entry of largest magnitude of r (the first on ties) is positive."""
+    u, sv, vt = np.linalg.svd(np.asarray(a, dtype=np.float64), full_matrices=False)
+    sigma = sv[0]
+    uu, vv = u[:, 0], vt[0, :]
+    j = int(np.argmax(np.abs(vv)))
+    if vv[j] < 0:
+        uu, vv = -uu, -vv
+    return np.sqrt(sigma) * uu, np.sqrt(sigma) * vv
+
+
 def project(m: np.ndarray, in_features: int, out_features: int, nblocks1: int,
             nblocks2: int) -> Tuple[np.ndarray, np.ndarray]:
     """Nearest Monarch factors (w1 = R, w2 = L) of a dense out x in matrix."""
@@ -64,12 +77,5 @@ def project(m: np.ndarray, in_features: int, out_features: int, nblocks1: int,
     w2 = np.zeros((b2, q2o, b1))        # L[g, p, r]  (q2i = b1)
     for g in range(b2):
         for r in range(b1):
-            u, sv, vt = np.linalg.svd(sl[g, r], full_matrices=False)
-            sigma = sv[0]
-            uu, vv = u[:, 0], vt[0, :]
-            j = int(np.argmax(np.abs(vv)))
-            if vv[j] < 0:
-                uu, vv = -uu, -vv
-            w2[g, :, r] = np.sqrt(sigma) * uu
-            w1[r, g, :] = np.sqrt(sigma) * vv
+            w2[g, :, r], w1[r, g, :] = fit_slice(sl[g, r])
     return w1, w2

@@ -152,3 +152,26 @@ def test_path_selection():
                  (768, 3072, 4, 4, 64, B.BF16), (512, 512, 4, 4, 64, B.BF16),
                  (12288, 12288, 96, 96, 64, B.BF16)]:
         assert M.monarch_describe(0, *args)[0].startswith("generic")
+
+
+def proj(m=A, w1=A2, w2=A2, fi=16, fo=16, nb1=4, nb2=4, dt=B.F32, iters=8):
+    lib = M.load_library()
+    return lib.monarch_project(m, w1, w2, fi, fo, nb1, nb2, dt, iters, None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(fo=32),                      # out != nb1 * nb2
+    dict(fi=18),                      # in % nb1
+    dict(nb1=0), dict(fi=0),
+    dict(iters=0), dict(iters=5000),
+    dict(fi=256 * 512, fo=16, nb1=4, nb2=4),   # slice 4 x 32768 does not fit in LDS
+])
+def test_project_bad_shapes(kw):
+    assert proj(**kw) == B.MONARCH_ERR_SHAPE
+
+
+def test_project_bad_dtype_null_align():
+    assert proj(dt=3) == B.MONARCH_ERR_DTYPE
+    for name in ("m", "w1", "w2"):
+        assert proj(**{name: None}) == B.MONARCH_ERR_NULL
+        assert proj(**{name: MIS}) == B.MONARCH_ERR_ALIGN
