@@ -65,4 +65,28 @@ __device__ __forceinline__ bf16x8 as_bf16x8(u16x8 v) {
   return r;
 }
 
+// Offset of output column j under the optional column split of GemmArgs
+// (kernels.h): j*lo, or (j / ns)*hi + (j % ns)*lo when ns > 0.
+__device__ __forceinline__ int64_t col_off(int64_t j, int64_t ns, int64_t hi, int64_t lo) {
+  return ns > 0 ? (j / ns) * hi + (j % ns) * lo : j * lo;
+}
+
+// 4x8 transpose of bf16 in registers: in[i] holds elements (i, e = 0..7);
+// out[e] gets elements (i = 0..3, e) packed into 8 bytes.
+__device__ __forceinline__ void transpose4x8(const u32x4 (&in)[4], u32x2 (&out)[8]) {
+#pragma unroll
+  for (int k = 0; k < 4; ++k) {
+    out[2 * k][0] = (in[0][k] & 0xffffu) | (in[1][k] << 16);
+    out[2 * k][1] = (in[2][k] & 0xffffu) | (in[3][k] << 16);
+    out[2 * k + 1][0] = (in[0][k] >> 16) | (in[1][k] & 0xffff0000u);
+    out[2 * k + 1][1] = (in[2][k] >> 16) | (in[3][k] & 0xffff0000u);
+  }
+}
+
+// 4x4 transpose of 32-bit elements: out[e][i] = in[i][e].
+__device__ __forceinline__ void transpose4x4(const u32x4 (&in)[4], u32x4 (&out)[4]) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) out[e] = u32x4{in[0][e], in[1][e], in[2][e], in[3][e]};
+}
+
 }  // namespace monarch

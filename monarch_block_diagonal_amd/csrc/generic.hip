@@ -89,7 +89,7 @@ __global__ __launch_bounds__(256) void generic_gemm_kernel(GemmArgs p, int64_t m
       }
       const int64_t gj = j0 + j, gk = k0 + k;
       T v = T(0);
-      if (gj < p.N && gk < ke) v = B[blk * p.b_sb + gk * p.b_sk + gj * p.b_sj];
+      if (gj < p.N && gk < ke) v = B[blk * p.b_sb + gk * p.b_sk + col_off(gj, p.nsplit, p.b_sj_hi, p.b_sj)];
       Bs[j * LD + k] = v;
     }
     __syncthreads();
@@ -149,7 +149,7 @@ __global__ __launch_bounds__(256) void generic_gemm_kernel(GemmArgs p, int64_t m
             p.partial[((split * p.nblk + blk) * p.M + i) * p.N + j] = val;
           } else {
             if (p.relu) val = val > 0.f ? val : 0.f;
-            Io<T>::store(p.C, blk * p.c_sb + i * p.c_si + j * p.c_sj, val);
+            Io<T>::store(p.C, blk * p.c_sb + i * p.c_si + col_off(j, p.nsplit, p.c_sj_hi, p.c_sj), val);
           }
         }
       }

@@ -15,6 +15,10 @@ namespace monarch {
 // 0 wherever mask at the same offset is <= 0 (ReLU derivative). When
 // `partial` is set, K is cut into `splits` chunks of k_chunk and chunk s writes
 // its fp32 sum to partial[((s*nblk + blk)*M + i)*N + j] instead of C.
+// When nsplit > 0 (not with `partial`), column j is split as
+// (j / nsplit, j % nsplit) and sits at (j / nsplit)*b_sj_hi + (j % nsplit)*b_sj
+// in B and (j / nsplit)*c_sj_hi + (j % nsplit)*c_sj in C: a reordering of the
+// output columns that lets stage 1 write its result in stage 2's order.
 struct GemmArgs {
   const void* A = nullptr;
   const void* B = nullptr;
@@ -24,6 +28,7 @@ struct GemmArgs {
   int64_t a_sb = 0, a_si = 0, a_sk = 0;
   int64_t b_sb = 0, b_sk = 0, b_sj = 0;
   int64_t c_sb = 0, c_si = 0, c_sj = 0;
+  int64_t nsplit = 0, b_sj_hi = 0, c_sj_hi = 0;
   int64_t M = 0, N = 0, K = 0;
   int64_t nblk = 1;
   int64_t splits = 1;
@@ -37,6 +42,25 @@ constexpr int kGenBN = 64;
 constexpr int kGenBK = 32;
 
 hipError_t launch_generic_gemm(const GemmArgs& a, bool bf16, hipStream_t s);
+
+// Reduction-chunk granularity of batch-split GEMMs (a multiple of both
+// kernels' K steps).
+constexpr int kSplitK = 64;
+
+// The tiled kernel (tiled.hip): 16-byte operand loads, for GEMMs whose A is
+// contiguous along K or M and whose B is contiguous along K or N (with
+// `nsplit`, B must be K-contiguous). tiled_gemm_applicable says whether a
+// GEMM qualifies; launch_gemm takes the tiled kernel when it does and the
+// generic one otherwise.
+bool tiled_gemm_applicable(const GemmArgs& a, bool bf16);
+hipError_t launch_tiled_gemm(const GemmArgs& a, bool bf16, hipStream_t s);
+hipError_t launch_gemm(const GemmArgs& a, bool bf16, hipStream_t s);
+
+// dV[b, g*q2o + p] = dY[b, p*b2 + g], times 1[Y > 0] when ymask is set: dY
+// (and the ReLU derivative) gathered into the block-major order of stage 2's
+// backward products. rows x out elements; out = b2 * q2o.
+hipError_t launch_dv_gather(const void* dy, const void* ymask, void* dv, int64_t rows, int64_t out,
+                            int64_t b2, int64_t q2o, bool bf16, hipStream_t s);
 
 // Writes `bytes` zero bytes (a plain kernel, not hipMemsetAsync, so callers may
 // capture it in a graph). p must be 2-byte aligned and bytes a multiple of 2.

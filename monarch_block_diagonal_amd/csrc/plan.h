@@ -18,6 +18,9 @@ struct Problem {
   int dtype = 0, act = 0;
   int64_t esize = 4;
   int path = PATH_GENERIC;
+  // generic path: z holds stage 2's input in stage 2's order,
+  // W[b, g*q2i + t] = Z[b, t*b2 + g] (needs q1o % b2 == 0; else Z's own order)
+  bool z_stage2_order = false;
   // batch split of the weight-gradient reductions (stage 2 and stage 1)
   int64_t s2 = 1, kc2 = 0, s1 = 1, kc1 = 0;
   SqPlan sq;  // launch geometry of PATH_SQ128
@@ -41,6 +44,7 @@ struct Buffers {
 };
 
 enum StepKind {
+  GEN_DV_GATHER,
   GEN_STAGE1_FWD,
   GEN_STAGE2_FWD,
   GEN_STAGE2_BWD_DATA,

@@ -1,16 +1,22 @@
 // Kernel planning for one Monarch problem and the launch of each step.
 //
 // Generic path (any shape): every step is one strided batched GEMM
-// (generic.hip). With natural-order Z[b, r*q1o + k] saved by the forward:
+// (tiled.hip when its operands are contiguous along a tile dimension,
+// generic.hip otherwise). With Z[b, r*q1o + k] the stage-1 output:
 //   stage 1 fwd   Z(r; b, k)  = sum_s X[b, r*q1i+s] w1[r,k,s]
 //   stage 2 fwd   Y(g; b, p)  = act(sum_t Z[b, t*b2+g] w2[g,p,t])   -> Y[b, p*b2+g]
-//   stage 2 bwd   dZ(g; b, t) = sum_p dYe[b, p*b2+g] w2[g,p,t]      -> dZ[b, t*b2+g]
-//                 dw2(g; p, t) = sum_b dYe[b, p*b2+g] Z[b, t*b2+g]   (batch split)
+//   dV gather     dV[b, g*q2o+p] = dYe[b, p*b2+g]
+//   stage 2 bwd   dZ(g; b, t) = sum_p dV[b, g*q2o+p] w2[g,p,t]      -> dZ[b, t*b2+g]
+//                 dw2(g; p, t) = sum_b dV[b, g*q2o+p] Z[b, t*b2+g]   (batch split)
 //   stage 1 bwd   dX(r; b, s) = sum_k dZ[b, r*q1o+k] w1[r,k,s]
 //                 dw1(r; k, s) = sum_b dZ[b, r*q1o+k] X[b, r*q1i+s]  (batch split)
 // where dYe = dY masked by Y > 0 after a fused ReLU. The index maps are the
 // stride permutation and its inverse (scatterbrain issues page, "hypercube"
-// thread) folded into the operand strides.
+// thread) folded into the operand strides. When q1o % b2 == 0 the saved z
+// holds Z in stage 2's order, W[b, g*q2i + t] = Z[b, t*b2 + g]: stage 1
+// enumerates its output columns of block r as j = g*n1 + tt (k = tt*b2 + g,
+// n1 = q1o/b2), so it writes runs of n1 consecutive elements and stage 2 and
+// the dw2 product read z contiguously.
 #include "kernels.h"
 #include "monarch.h"
 #include "plan.h"
@@ -39,7 +45,7 @@ void choose_splits(int64_t nblk, int64_t M, int64_t N, int64_t K, int64_t* split
   if (s > 64) s = 64;
   if (s < 1) s = 1;
   int64_t c = (K + s - 1) / s;
-  c = (c + kGenBK - 1) / kGenBK * kGenBK;
+  c = (c + kSplitK - 1) / kSplitK * kSplitK;
   *chunk = c;
   *splits = (K + c - 1) / c;
 }
@@ -69,6 +75,7 @@ int make_problem(int64_t in, int64_t out, int64_t nb1, int64_t nb2, int64_t batc
   p.act = act;
   p.esize = dtype == MONARCH_BF16 ? 2 : 4;
   p.path = PATH_GENERIC;
+  p.z_stage2_order = p.q1o % nb2 == 0;
   if (batch > 0 && sq_applicable(in, out, nb1, nb2, batch, dtype == MONARCH_BF16)) {
     p.path = PATH_SQ128;
     p.sq = sq_plan(batch, nb1);
@@ -86,11 +93,9 @@ int make_problem(int64_t in, int64_t out, int64_t nb1, int64_t nb2, int64_t batc
     off = align_up(off + static_cast<size_t>(p.s2) * nb2 * p.q2o * p.q2i * 4, 256);
     p.ws_p1 = off;
     off = align_up(off + static_cast<size_t>(p.s1) * nb1 * p.q1o * p.q1i * 4, 256);
-    if (p.path == PATH_SQ128) {
-      // the block-major dV panels
-      p.ws_dv = off;
-      off = align_up(off + static_cast<size_t>(batch) * out * p.esize, 256);
-    }
+    // dY in block-major order (sq path: panels, generic path: rows)
+    p.ws_dv = off;
+    off = align_up(off + static_cast<size_t>(batch) * out * p.esize, 256);
     p.ws_total = off;
   }
   *pr = p;
@@ -126,6 +131,7 @@ Plan plan_bwd(const Problem& pr) {
     p.add(REDUCE_DW);
     return p;
   }
+  p.add(GEN_DV_GATHER);
   p.add(GEN_STAGE2_BWD_DATA);
   p.add(GEN_STAGE2_BWD_WEIGHT);
   p.add(GEN_STAGE1_BWD_DATA);
@@ -136,6 +142,7 @@ Plan plan_bwd(const Problem& pr) {
 
 const char* step_name(StepKind k) {
   switch (k) {
+    case GEN_DV_GATHER: return "generic_dv_gather";
     case GEN_STAGE1_FWD: return "generic_stage1_fwd";
     case GEN_STAGE2_FWD: return "generic_stage2_fwd";
     case GEN_STAGE2_BWD_DATA: return "generic_stage2_bwd_data";
@@ -164,42 +171,61 @@ hipError_t launch_step(StepKind k, const Problem& pr, const Buffers& b, hipStrea
   void* dv = ws ? ws + pr.ws_dv : nullptr;
   GemmArgs a;
   switch (k) {
+    case GEN_DV_GATHER:
+      return launch_dv_gather(b.dy, mask, dv, pr.batch, pr.out, pr.b2, pr.q2o, bf16, s);
     case GEN_STAGE1_FWD:
       a.A = b.x;
       a.a_sb = pr.q1i, a.a_si = pr.in, a.a_sk = 1;
       a.B = b.w1;
-      a.b_sb = pr.q1o * pr.q1i, a.b_sk = 1, a.b_sj = pr.q1i;
+      a.b_sb = pr.q1o * pr.q1i, a.b_sk = 1;
       a.C = b.z_out;
-      a.c_sb = pr.q1o, a.c_si = pr.mid, a.c_sj = 1;
+      a.c_si = pr.mid;
+      if (pr.z_stage2_order) {
+        // column j = g*n1 + tt of block r is k = tt*b2 + g, stored at W
+        // position g*q2i + r*n1 + tt
+        const int64_t n1 = pr.q1o / pr.b2;
+        a.nsplit = n1;
+        a.b_sj_hi = pr.q1i, a.b_sj = pr.b2 * pr.q1i;
+        a.c_sb = n1, a.c_sj_hi = pr.q2i, a.c_sj = 1;
+      } else {
+        a.b_sj = pr.q1i;
+        a.c_sb = pr.q1o, a.c_sj = 1;
+      }
       a.M = pr.batch, a.N = pr.q1o, a.K = pr.q1i, a.nblk = pr.b1;
-      return launch_generic_gemm(a, bf16, s);
+      return launch_gemm(a, bf16, s);
     case GEN_STAGE2_FWD:
       a.A = b.z_out;
-      a.a_sb = 1, a.a_si = pr.mid, a.a_sk = pr.b2;
+      if (pr.z_stage2_order)
+        a.a_sb = pr.q2i, a.a_si = pr.mid, a.a_sk = 1;
+      else
+        a.a_sb = 1, a.a_si = pr.mid, a.a_sk = pr.b2;
       a.B = b.w2;
       a.b_sb = pr.q2o * pr.q2i, a.b_sk = 1, a.b_sj = pr.q2i;
       a.C = b.y_out;
       a.c_sb = 1, a.c_si = pr.out, a.c_sj = pr.b2;
       a.M = pr.batch, a.N = pr.q2o, a.K = pr.q2i, a.nblk = pr.b2;
       a.relu = pr.act == MONARCH_ACT_RELU;
-      return launch_generic_gemm(a, bf16, s);
+      return launch_gemm(a, bf16, s);
     case GEN_STAGE2_BWD_DATA:
-      a.A = b.dy, a.mask = mask;
-      a.a_sb = 1, a.a_si = pr.out, a.a_sk = pr.b2;
+      a.A = dv;
+      a.a_sb = pr.q2o, a.a_si = pr.out, a.a_sk = 1;
       a.B = b.w2;
       a.b_sb = pr.q2o * pr.q2i, a.b_sk = pr.q2i, a.b_sj = 1;
       a.C = dz;
       a.c_sb = 1, a.c_si = pr.mid, a.c_sj = pr.b2;
       a.M = pr.batch, a.N = pr.q2i, a.K = pr.q2o, a.nblk = pr.b2;
-      return launch_generic_gemm(a, bf16, s);
+      return launch_gemm(a, bf16, s);
     case GEN_STAGE2_BWD_WEIGHT:
-      a.A = b.dy, a.mask = mask;
-      a.a_sb = 1, a.a_si = pr.b2, a.a_sk = pr.out;
+      a.A = dv;
+      a.a_sb = pr.q2o, a.a_si = 1, a.a_sk = pr.out;
       a.B = b.z;
-      a.b_sb = 1, a.b_sk = pr.mid, a.b_sj = pr.b2;
+      if (pr.z_stage2_order)
+        a.b_sb = pr.q2i, a.b_sk = pr.mid, a.b_sj = 1;
+      else
+        a.b_sb = 1, a.b_sk = pr.mid, a.b_sj = pr.b2;
       a.partial = p2, a.splits = pr.s2, a.k_chunk = pr.kc2;
       a.M = pr.q2o, a.N = pr.q2i, a.K = pr.batch, a.nblk = pr.b2;
-      return launch_generic_gemm(a, bf16, s);
+      return launch_gemm(a, bf16, s);
     case GEN_STAGE1_BWD_DATA:
       a.A = dz;
       a.a_sb = pr.q1o, a.a_si = pr.mid, a.a_sk = 1;
@@ -208,7 +234,7 @@ hipError_t launch_step(StepKind k, const Problem& pr, const Buffers& b, hipStrea
       a.C = b.dx;
       a.c_sb = pr.q1i, a.c_si = pr.in, a.c_sj = 1;
       a.M = pr.batch, a.N = pr.q1i, a.K = pr.q1o, a.nblk = pr.b1;
-      return launch_generic_gemm(a, bf16, s);
+      return launch_gemm(a, bf16, s);
     case GEN_STAGE1_BWD_WEIGHT:
       a.A = dz;
       a.a_sb = pr.q1o, a.a_si = 1, a.a_sk = pr.mid;
@@ -216,7 +242,7 @@ hipError_t launch_step(StepKind k, const Problem& pr, const Buffers& b, hipStrea
       a.b_sb = pr.q1i, a.b_sk = pr.in, a.b_sj = 1;
       a.partial = p1, a.splits = pr.s1, a.k_chunk = pr.kc1;
       a.M = pr.q1o, a.N = pr.q1i, a.K = pr.batch, a.nblk = pr.b1;
-      return launch_generic_gemm(a, bf16, s);
+      return launch_gemm(a, bf16, s);
     case REDUCE_DW:
       return launch_reduce_partials(p2, b.dw2, pr.b2 * pr.q2o * pr.q2i, pr.s2, p1, b.dw1,
                                     pr.b1 * pr.q1o * pr.q1i, pr.s1, bf16, s);

@@ -120,18 +120,6 @@ template <typename T, int N> __device__ __forceinline__ void pin(T (&v)[N]) {
   for (int i = 0; i < N; ++i) pin(v[i]);
 }
 
-// 4x8 transpose of bf16 in registers: in[i] holds elements (i, e = 0..7);
-// out[e] gets elements (i = 0..3, e) packed into 8 bytes.
-__device__ __forceinline__ void transpose4x8(const u32x4 (&in)[4], u32x2 (&out)[8]) {
-#pragma unroll
-  for (int k = 0; k < 4; ++k) {
-    out[2 * k][0] = (in[0][k] & 0xffffu) | (in[1][k] << 16);
-    out[2 * k][1] = (in[2][k] & 0xffffu) | (in[3][k] << 16);
-    out[2 * k + 1][0] = (in[0][k] >> 16) | (in[1][k] & 0xffff0000u);
-    out[2 * k + 1][1] = (in[2][k] >> 16) | (in[3][k] & 0xffff0000u);
-  }
-}
-
 __device__ __forceinline__ int clamp_row(int row, int64_t lim) {
   return row < lim ? row : static_cast<int>(lim - 1);
 }
