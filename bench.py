@@ -70,6 +70,21 @@ def kernel_bytes(name: str, pr: dict) -> float:
     return 0.0
 
 
+def kernel_flops(name: str, pr: dict) -> float:
+    """Algorithmic flops of one launch (2 per multiply-add of the Monarch
+    products the kernel's role computes)."""
+    B, p1, p2 = pr["batch"], pr["params1"], pr["params2"]
+    table = {
+        "stage1_fwd": 2 * B * p1, "stage2_fwd": 2 * B * p2,
+        "stage2_bwd_data": 2 * B * p2, "stage2_bwd_weight": 2 * B * p2, "stage2_bwd": 4 * B * p2,
+        "stage1_bwd_data": 2 * B * p1, "stage1_bwd_weight": 2 * B * p1, "stage1_bwd": 4 * B * p1,
+    }
+    for key in sorted(table, key=len, reverse=True):
+        if name.endswith(key):
+            return float(table[key])
+    return 0.0
+
+
 def load_traffic(kernel: str, workload: str, digest: str):
     """HBM bytes per launch from committed rocprofv3 --pmc summaries, or None
     when absent or taken on other kernel sources."""
@@ -94,17 +109,18 @@ def cpu_baseline(w, rows: int):
     import numpy as np
     import oracle as O
     from monarch_block_diagonal_amd import synthetic as S
-    layer = w.layers[0]
-    d = S.make_layer_inputs(w, batch=rows)
-    fi, fo = layer.in_features, layer.out_features
+    ins = [S.make_layer_inputs(w, li, batch=rows) for li in range(len(w.layers))]
+    chain = [(d["w1"], d["w2"], l.in_features, l.out_features, l.relu)
+             for d, l in zip(ins, w.layers)]
+    x, dy = ins[0]["x"], ins[0]["dy"]
     try:
         from threadpoolctl import threadpool_info
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
     t0 = time.perf_counter()
-    y = O.forward(d["x"], d["w1"], d["w2"], fi, fo)
-    dx, dw1, dw2 = O.backward(d["dy"], d["x"], d["w1"], d["w2"], fi, fo)
+    y, _ = O.mlp_forward(x, chain)
+    dx, _ = O.mlp_backward(dy, x, chain)
     dt = time.perf_counter() - t0
     flops = 6.0 * rows * w.params
     assert np.isfinite(y).all() and np.isfinite(dx).all()
@@ -225,23 +241,24 @@ def main() -> int:
     from monarch_block_diagonal_amd import synthetic as S
 
     w = S.WORKLOADS[args.workload]
-    if len(w.layers) != 1:
-        print("bench.py times single-layer workloads", file=sys.stderr)
-        return 2
-    layer = w.layers[0]
-    fi, fo, nb1, nb2, B = layer.in_features, layer.out_features, layer.nblocks1, layer.nblocks2, w.batch
     dt_code = M.BF16 if w.dtype == "bf16" else M.F32
     tdt = torch.bfloat16 if w.dtype == "bf16" else torch.float32
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     e = 2 if w.dtype == "bf16" else 4
+    B = w.batch
+    layers = w.layers
+    multi = len(layers) > 1
 
-    log(f"workload {w.name}: in={fi} out={fo} b1={nb1} b2={nb2} batch={B} {w.dtype}")
+    log(f"workload {w.name}: " + ", ".join(
+        f"in={l.in_features} out={l.out_features} b1={l.nblocks1} b2={l.nblocks2}"
+        f"{' +relu' if l.relu else ''}" for l in layers) + f"; batch={B} {w.dtype}")
+
     # seeded synthetic inputs drawn on the device (same distributions as the
     # parity tests' host draws)
-    def draw(tid, shape, dist, var):
+    def draw(seed, shape, dist, var):
         g = torch.Generator(device=dev)
-        g.manual_seed(S.seed_for(w.cfg, tid))
+        g.manual_seed(seed)
         if dist == "normal":
             t = torch.randn(shape, generator=g, device=dev, dtype=torch.float32)
             if var != 1.0:
@@ -250,36 +267,65 @@ def main() -> int:
             t = torch.rand(shape, generator=g, device=dev, dtype=torch.float32)
         return t.to(tdt)
 
-    vr, vl = w.w_var[0]
-    x = draw(S.TID_X, (B, fi), w.x_dist, w.x_var)
-    w1 = draw(S.TID_W1, layer.w1_shape, "normal", vr)
-    w2 = draw(S.TID_W2, layer.w2_shape, "normal", vl)
-    dy = draw(S.TID_DY, (B, fo), "normal", w.dy_var)
-    y = torch.empty((B, fo), dtype=tdt, device=dev)
-    z = torch.empty((B, fo), dtype=tdt, device=dev)
-    dx = torch.empty_like(x)
-    dw1 = torch.empty_like(w1)
-    dw2 = torch.empty_like(w2)
-    wsb = M.monarch_bwd_workspace_bytes(fi, fo, nb1, nb2, B, dt_code)
+    x = draw(S.seed_for(w.cfg, S.TID_X), (B, layers[0].in_features), w.x_dist, w.x_var)
+    dy = draw(S.seed_for(w.cfg, S.TID_DY), (B, layers[-1].out_features), "normal", w.dy_var)
+    L = []
+    wsb = 0
+    for li, l in enumerate(layers):
+        t1, t2 = (S.TID_W1, S.TID_W2) if li == 0 else (S.TID_W1_L2, S.TID_W2_L2)
+        vr, vl = w.w_var[li]
+        fi, fo = l.in_features, l.out_features
+        d = {"l": l, "fi": fi, "fo": fo,
+             "w1": draw(S.seed_for(w.cfg, t1), l.w1_shape, "normal", vr),
+             "w2": draw(S.seed_for(w.cfg, t2), l.w2_shape, "normal", vl),
+             "y": torch.empty((B, fo), dtype=tdt, device=dev),
+             "z": torch.empty((B, fo), dtype=tdt, device=dev),
+             "dx": torch.empty((B, fi), dtype=tdt, device=dev),
+             "act": M.ACT_RELU if l.relu else M.ACT_NONE,
+             "fn": M.monarch_describe(0, fi, fo, l.nblocks1, l.nblocks2, B, dt_code),
+             "bn": M.monarch_describe(1, fi, fo, l.nblocks1, l.nblocks2, B, dt_code)}
+        d["dw1"] = torch.empty_like(d["w1"])
+        d["dw2"] = torch.empty_like(d["w2"])
+        d["x"] = x if li == 0 else L[li - 1]["y"]
+        wsb = max(wsb, M.monarch_bwd_workspace_bytes(fi, fo, l.nblocks1, l.nblocks2, B, dt_code))
+        L.append(d)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
-    fnames = M.monarch_describe(0, fi, fo, nb1, nb2, B, dt_code)
-    bnames = M.monarch_describe(1, fi, fo, nb1, nb2, B, dt_code)
     stream = torch.cuda.current_stream()
 
-    def step(evf=None, evb=None):
-        M.monarch_fwd(x, w1, w2, y, z, fi, fo, nb1, nb2, B, dt_code, M.ACT_NONE, stream, events=evf)
-        M.monarch_bwd(dy, x, w1, w2, z, None, dx, dw1, dw2, ws, wsb, fi, fo, nb1, nb2, B, dt_code,
-                      M.ACT_NONE, stream, events=evb)
+    def fwd(evs=None):
+        for li, d in enumerate(L):
+            l = d["l"]
+            M.monarch_fwd(d["x"], d["w1"], d["w2"], d["y"], d["z"], d["fi"], d["fo"], l.nblocks1,
+                          l.nblocks2, B, dt_code, d["act"], stream,
+                          events=None if evs is None else evs[li])
 
-    log(f"warmup {args.warmup} steps; kernels fwd={fnames} bwd={bnames}")
+    def bwd(evs=None):
+        g = dy
+        for li in range(len(L) - 1, -1, -1):
+            d, l = L[li], L[li]["l"]
+            M.monarch_bwd(g, d["x"], d["w1"], d["w2"], d["z"],
+                          d["y"] if d["act"] == M.ACT_RELU else None, d["dx"], d["dw1"], d["dw2"],
+                          ws, wsb, d["fi"], d["fo"], l.nblocks1, l.nblocks2, B, dt_code, d["act"],
+                          stream, events=None if evs is None else evs[li])
+            g = d["dx"]
+
+    def step(evf=None, evb=None):
+        fwd(evf)
+        bwd(evb)
+
+    log(f"warmup {args.warmup} steps; kernels " + " | ".join(
+        f"fwd={d['fn']} bwd={d['bn']}" for d in L))
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
 
+    def new_events(n):
+        return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
+
     K = args.steps
-    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fnames) + 1)] for _ in range(K)]
-    evb = [[torch.cuda.Event(enable_timing=True) for _ in range(len(bnames) + 1)] for _ in range(K)]
-    log(f"timing {K} steps")
+    evf = [[new_events(len(d["fn"]) + 1) for d in L] for _ in range(K)]
+    evb = [[new_events(len(d["bn"]) + 1) for d in L] for _ in range(K)]
+    log(f"timing {K} fwd+bwd steps")
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(K):
@@ -287,29 +333,68 @@ def main() -> int:
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / K
+    # per-step device times: first forward event to last backward event
+    step_ms = sorted(evf[k][0][0].elapsed_time(evb[k][0][-1]) for k in range(K))
+
+    def pct(v, q):
+        return v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
+
+    log(f"timing {K} forward-only steps")
+    evs_f = new_events(K + 1)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for k in range(K):
+        evs_f[k].record(stream)
+        fwd()
+    evs_f[K].record(stream)
+    torch.cuda.synchronize()
+    fwd_wall_ms = (time.perf_counter() - t0) * 1e3 / K
+    fwd_ms = sorted(evs_f[k].elapsed_time(evs_f[k + 1]) for k in range(K))
 
     per_kernel = {}
-    for names, evs in ((fnames, evf), (bnames, evb)):
-        for i, nm in enumerate(names):
-            ts = [ev[i].elapsed_time(ev[i + 1]) for ev in evs]
-            per_kernel[nm] = sum(ts) / len(ts)
-    pr = {"e": e, "batch": B, "in": fi, "mid": fo, "out": fo, "act": 0,
-          "params1": nb1 * (fo // nb1) * (fi // nb1), "params2": nb2 * (fo // nb2) * (fo // nb2)}
+    prs = {}
+    for li, d in enumerate(L):
+        l = d["l"]
+        pre = f"L{li + 1}:" if multi else ""
+        pr = {"e": e, "batch": B, "in": d["fi"], "mid": d["fo"], "out": d["fo"],
+              "act": 1 if l.relu else 0,
+              "params1": l.nblocks1 * (d["fo"] // l.nblocks1) * (d["fi"] // l.nblocks1),
+              "params2": l.nblocks2 * (d["fo"] // l.nblocks2) * (d["fo"] // l.nblocks2)}
+        for names, evs in ((d["fn"], [ev[li] for ev in evf]), (d["bn"], [ev[li] for ev in evb])):
+            for i, nm in enumerate(names):
+                ts = [ev[i].elapsed_time(ev[i + 1]) for ev in evs]
+                per_kernel[pre + nm] = sum(ts) / len(ts)
+                prs[pre + nm] = (nm, pr)
     dom = max(per_kernel, key=per_kernel.get)
     dom_ms = per_kernel[dom]
-    dom_bytes = kernel_bytes(dom, pr)
+    dom_name, dom_pr = prs[dom]
+    dom_bytes = kernel_bytes(dom_name, dom_pr)
+    dom_flops = kernel_flops(dom_name, dom_pr)
     digest = csrc_digest()
-    achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
-    roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                "traffic": load_traffic(dom, w.name, digest),
-                "algorithmic_bytes": dom_bytes, "avg_ms": round(dom_ms, 4)}
+    mfma_peak = MFMA_PEAK_TFLOPS[w.dtype]
+    ridge = mfma_peak * 1e12 / (HBM_PEAK_GBS * 1e9)
+    if dom_bytes > 0 and dom_flops / dom_bytes > ridge:
+        achieved = dom_flops / (dom_ms * 1e-3) / 1e12
+        roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 1),
+                    "peak": mfma_peak, "unit": "TFLOP/s", "frac": round(achieved / mfma_peak, 4)}
+    else:
+        achieved = dom_bytes / (dom_ms * 1e-3) / 1e9
+        roofline = {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                    "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4)}
+    roofline.update({"traffic": None if multi else load_traffic(dom, w.name, digest),
+                     "algorithmic_bytes": dom_bytes, "algorithmic_flops": dom_flops,
+                     "avg_ms": round(dom_ms, 4)})
 
     flops = 6.0 * B * w.params
     value = flops / (ms_per_step * 1e-3) / 1e12
-    # whole-step HBM fraction against the two-pass algorithmic byte count
-    b2p = e * B * (fi + 2 * fo + fo) + e * w.params + e * B * (fo + 3 * fo + 2 * fi) + 2 * e * w.params
-    step_hbm_frac = b2p / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS
+    # whole step against the two-pass algorithmic bytes (each stage reads its
+    # input and writes its output once, z saved; weights and gradients once)
+    b2p = sum(e * B * (d["fi"] + 3 * d["fo"]) + e * B * (4 * d["fo"] + 2 * d["fi"])
+              + 3 * e * d["l"].params for d in L)
+    t_roof = max(flops / (mfma_peak * 1e12), b2p / (HBM_PEAK_GBS * 1e9)) * 1e3
+    step_roofline = {"binds": "mfma" if flops / (mfma_peak * 1e12) > b2p / (HBM_PEAK_GBS * 1e9)
+                     else "hbm", "t_roof_ms": round(t_roof, 4), "bytes_2pass": b2p,
+                     "flops": flops, "frac": round(t_roof / ms_per_step, 4)}
 
     if args.copy_probe:
         src = torch.empty(1 << 29, dtype=torch.bfloat16, device=dev).fill_(1.0)
@@ -321,32 +406,44 @@ def main() -> int:
 
     dense = None
     if not args.no_dense:
-        log("dense bf16 GEMM baseline of the same shape")
-        Wd = torch.randn((fo, fi), device=dev, dtype=torch.float32).mul_(fi ** -0.5).to(tdt)
+        log(f"dense {w.dtype} GEMM baseline of the same shapes")
+        Wd = [torch.randn((d["fo"], d["fi"]), device=dev, dtype=torch.float32)
+              .mul_(d["fi"] ** -0.5).to(tdt) for d in L]
 
         def dense_step():
-            yd = torch.nn.functional.linear(x, Wd)
-            dxd = dy @ Wd
-            dwd = dy.t() @ x
-            return yd, dxd, dwd
+            hs = [x]
+            for i, Wl in enumerate(Wd):
+                h = torch.nn.functional.linear(hs[-1], Wl)
+                if L[i]["l"].relu:
+                    h = torch.relu(h)
+                hs.append(h)
+            g = dy
+            for i in range(len(Wd) - 1, -1, -1):
+                if L[i]["l"].relu:
+                    g = g * (hs[i + 1] > 0)
+                dw = g.t() @ hs[i]
+                g = g @ Wd[i]
+            return g, dw
         for _ in range(2):
             dense_step()
         torch.cuda.synchronize()
-        reps = 3
+        reps = 5
         t0 = time.perf_counter()
         for _ in range(reps):
             dense_step()
         torch.cuda.synchronize()
         dense_ms = (time.perf_counter() - t0) * 1e3 / reps
-        dense = {"ms_per_step": round(dense_ms, 3),
-                 "tflops": round(6.0 * B * fi * fo / (dense_ms * 1e-3) / 1e12, 1),
-                 "speedup_monarch_vs_dense": round(dense_ms / ms_per_step, 2)}
+        dflops = sum(6.0 * B * d["fi"] * d["fo"] for d in L)
+        dense = {"dtype": w.dtype, "ms_per_step": round(dense_ms, 4),
+                 "tflops": round(dflops / (dense_ms * 1e-3) / 1e12, 1),
+                 "speedup_monarch_vs_dense": round(dense_ms / ms_per_step, 3)}
         del Wd
 
     cpu = None
     if not args.no_cpu_baseline:
         # about 2e13 fp64 flops of dense-factor products (~10-30 s on 16 host cores)
-        rows = args.cpu_rows or min(B, max(8, int(2e13 / (20.0 * fo * max(fi, fo)))))
+        per_row = sum(20.0 * l.out_features * max(l.in_features, l.out_features) for l in layers)
+        rows = args.cpu_rows or min(B, max(8, int(2e13 / per_row)))
         log(f"cpu baseline: oracle on {rows} rows")
         cpu = cpu_baseline(w, rows)
 
@@ -363,10 +460,16 @@ def main() -> int:
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic (seeded, drawn on the device)",
-        "config": {"workload": w.name, "in_features": fi, "out_features": fo, "nblocks1": nb1,
-                   "nblocks2": nb2, "batch": B, "params": w.params, "passes": "fwd+bwd"},
+        "config": {"workload": w.name, "layers": [
+            {"in_features": d["fi"], "out_features": d["fo"], "nblocks1": d["l"].nblocks1,
+             "nblocks2": d["l"].nblocks2, "relu_after": d["l"].relu} for d in L],
+            "batch": B, "params": w.params, "passes": "fwd+bwd"},
         "tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
-        "step_hbm_fraction_2pass": round(step_hbm_frac, 4),
+        "step_ms_p10_p50_p90": [round(pct(step_ms, q), 4) for q in (0.1, 0.5, 0.9)],
+        "fwd_ms_per_step": round(fwd_wall_ms, 4),
+        "fwd_ms_p10_p50_p90": [round(pct(fwd_ms, q), 4) for q in (0.1, 0.5, 0.9)],
+        "fwd_tflops": round(2.0 * B * w.params / (pct(fwd_ms, 0.5) * 1e-3) / 1e12, 2),
+        "step_roofline": step_roofline,
         "kernels_ms": {k: round(v, 4) for k, v in per_kernel.items()},
         "roofline": roofline,
         "dense_baseline": dense,
@@ -375,7 +478,6 @@ def main() -> int:
     }
     print(json.dumps(result), flush=True)
     return 0
-
 
 if __name__ == "__main__":
     sys.exit(main())

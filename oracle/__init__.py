@@ -9,3 +9,4 @@ from .monarch_oracle import (  # noqa: F401
     forward_rows, backward_dx_rows, weight_grad_entries, rel_frobenius,
 )
 from . import monarch_projection  # noqa: F401,E402
+from . import monarch_linear  # noqa: F401,E402
