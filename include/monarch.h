@@ -155,6 +155,58 @@ int monarch_project(const void* m, void* w1, void* w2, int64_t in_features,
                     int64_t out_features, int64_t nblocks1, int64_t nblocks2, int dtype,
                     int iters, void* stream);
 
+/* ---------------------------------------------------------------------------
+ * General layer shapes (the MonarchLinear constructor in the "Definition C.3"
+ * thread of the scatterbrain issues page: block sizes ceil(in/nb) and
+ * ceil(out/nb), and mid = in_ext for an expanding layer, out_ext otherwise).
+ *
+ * The *_ex entry points take the intermediate width mid explicitly (divisible
+ * by both block counts) and any in and out:
+ *   q1i = ceil(in/b1), q1o = mid/b1, q2i = mid/b2, q2o = ceil(out/b2),
+ *   in_ext = b1*q1i >= in, out_ext = b2*q2o >= out.
+ * The input is zero-padded to in_ext features (the padded positions of w1
+ * take no part in the product and receive zero gradient), the two stages
+ * run at the extended sizes as above, and y keeps the first `out` of the
+ * out_ext features. An optional bias [out] is added before the activation:
+ *   y = act(Qout·L·P·R·pad(x) truncated to out + bias).
+ *   w1 [b1, q1o, q1i], w2 [b2, q2o, q2i], bias and dbias [out] in the I/O
+ *   dtype; z holds batch*mid elements. With mid = out, in % b1 == 0,
+ *   out % b2 == 0 and no bias they compute exactly what monarch_fwd and
+ *   monarch_bwd compute. Errors as for monarch_fwd/monarch_bwd, except that
+ *   in and out need not be divisible (mid must be: MONARCH_ERR_SHAPE). */
+
+/* The MonarchLinear intermediate width for one block count nb:
+ * min-of-branches rule above (in_ext if in_ext < out_ext, else out_ext).
+ * Returns MONARCH_ERR_SHAPE for non-positive or too large sizes. */
+int64_t monarch_linear_mid(int64_t in_features, int64_t out_features, int64_t nblocks);
+
+/* Forward of the general layer. bias may be NULL (no bias). events: as for
+ * monarch_fwd_traced (may be NULL, with n_events 0). */
+int monarch_fwd_ex(const void* x, const void* w1, const void* w2, const void* bias, void* y,
+                   void* z, int64_t in_features, int64_t out_features, int64_t mid_features,
+                   int64_t nblocks1, int64_t nblocks2, int64_t batch, int dtype, int act,
+                   void* stream, void* const* events, int n_events);
+
+/* Workspace bytes of monarch_bwd_ex (with_bias: whether dbias is requested). */
+size_t monarch_bwd_ex_workspace_bytes(int64_t in_features, int64_t out_features,
+                                      int64_t mid_features, int64_t nblocks1, int64_t nblocks2,
+                                      int64_t batch, int dtype, int with_bias);
+
+/* Backward of the general layer: dx [batch, in], dw1, dw2 as for
+ * monarch_bwd, and dbias[o] = sum over rows of dY_eff[b, o] when dbias is
+ * non-NULL (fixed-order sums, bit-reproducible). dx, dw1, dw2 and dbias are
+ * overwritten. batch == 0 writes zeros to dw1, dw2 and dbias. */
+int monarch_bwd_ex(const void* dy, const void* x, const void* w1, const void* w2, const void* z,
+                   const void* y, void* dx, void* dw1, void* dw2, void* dbias, void* workspace,
+                   size_t workspace_bytes, int64_t in_features, int64_t out_features,
+                   int64_t mid_features, int64_t nblocks1, int64_t nblocks2, int64_t batch,
+                   int dtype, int act, void* stream, void* const* events, int n_events);
+
+/* monarch_describe for the general layer (with_bias as above). */
+int monarch_describe_ex(int direction, int64_t in_features, int64_t out_features,
+                        int64_t mid_features, int64_t nblocks1, int64_t nblocks2, int64_t batch,
+                        int dtype, int act, int with_bias, char* buf, size_t buf_len);
+
 /* Static text for a status code; for MONARCH_ERR_HIP the last HIP error
  * message recorded on the calling thread. Never NULL. */
 const char* monarch_status_string(int status);

@@ -30,7 +30,8 @@ ACT_RELU = 1
 EXPORTED = (
     "monarch_fwd", "monarch_bwd", "monarch_bwd_workspace_bytes", "monarch_fwd_traced",
     "monarch_bwd_traced", "monarch_describe", "monarch_status_string", "monarch_abi_version",
-    "monarch_project",
+    "monarch_project", "monarch_linear_mid", "monarch_fwd_ex", "monarch_bwd_ex",
+    "monarch_bwd_ex_workspace_bytes", "monarch_describe_ex",
 )
 
 _lib = None
@@ -73,6 +74,18 @@ def load_library():
     lib.monarch_abi_version.restype = c_int
     lib.monarch_project.argtypes = [vp] * 3 + [i64] * 4 + [c_int, c_int, vp]
     lib.monarch_project.restype = c_int
+    ev = [ctypes.POINTER(vp), c_int]
+    lib.monarch_linear_mid.argtypes = [i64] * 3
+    lib.monarch_linear_mid.restype = i64
+    lib.monarch_fwd_ex.argtypes = [vp] * 6 + [i64] * 6 + [c_int, c_int, vp] + ev
+    lib.monarch_fwd_ex.restype = c_int
+    lib.monarch_bwd_ex_workspace_bytes.argtypes = [i64] * 6 + [c_int, c_int]
+    lib.monarch_bwd_ex_workspace_bytes.restype = sz
+    lib.monarch_bwd_ex.argtypes = [vp] * 11 + [sz] + [i64] * 6 + [c_int, c_int, vp] + ev
+    lib.monarch_bwd_ex.restype = c_int
+    lib.monarch_describe_ex.argtypes = [c_int] + [i64] * 6 + [c_int, c_int, c_int,
+                                                             ctypes.c_char_p, sz]
+    lib.monarch_describe_ex.restype = c_int
     _lib = lib
     return lib
 
@@ -173,3 +186,50 @@ def monarch_describe(direction, in_features, out_features, nblocks1, nblocks2, b
         raise MonarchError(n, monarch_status_string(n))
     names = buf.value.decode().split(";") if n else []
     return names
+
+
+def monarch_linear_mid(in_features, out_features, nblocks) -> int:
+    """The MonarchLinear intermediate width for one block count."""
+    v = load_library().monarch_linear_mid(in_features, out_features, nblocks)
+    if v < 0:
+        raise MonarchError(int(v), monarch_status_string(int(v)))
+    return int(v)
+
+
+def monarch_fwd_ex(x, w1, w2, bias, y, z, in_features, out_features, mid_features, nblocks1,
+                   nblocks2, batch, dtype, act=ACT_NONE, stream=None, events=None) -> None:
+    lib = load_library()
+    arr, n = _events(events)
+    _check(lib.monarch_fwd_ex(_ptr(x), _ptr(w1), _ptr(w2), _ptr(bias), _ptr(y), _ptr(z),
+                              in_features, out_features, mid_features, nblocks1, nblocks2, batch,
+                              dtype, act, _stream(stream), arr, n))
+
+
+def monarch_bwd_ex_workspace_bytes(in_features, out_features, mid_features, nblocks1, nblocks2,
+                                   batch, dtype, with_bias=False) -> int:
+    return load_library().monarch_bwd_ex_workspace_bytes(in_features, out_features, mid_features,
+                                                         nblocks1, nblocks2, batch, dtype,
+                                                         1 if with_bias else 0)
+
+
+def monarch_bwd_ex(dy, x, w1, w2, z, y, dx, dw1, dw2, dbias, workspace, workspace_bytes,
+                   in_features, out_features, mid_features, nblocks1, nblocks2, batch, dtype,
+                   act=ACT_NONE, stream=None, events=None) -> None:
+    lib = load_library()
+    arr, n = _events(events)
+    _check(lib.monarch_bwd_ex(_ptr(dy), _ptr(x), _ptr(w1), _ptr(w2), _ptr(z), _ptr(y), _ptr(dx),
+                              _ptr(dw1), _ptr(dw2), _ptr(dbias), _ptr(workspace), workspace_bytes,
+                              in_features, out_features, mid_features, nblocks1, nblocks2, batch,
+                              dtype, act, _stream(stream), arr, n))
+
+
+def monarch_describe_ex(direction, in_features, out_features, mid_features, nblocks1, nblocks2,
+                        batch, dtype, act=ACT_NONE, with_bias=False):
+    """Kernel names monarch_fwd_ex (0) / monarch_bwd_ex (1) launches."""
+    lib = load_library()
+    buf = ctypes.create_string_buffer(1024)
+    n = lib.monarch_describe_ex(direction, in_features, out_features, mid_features, nblocks1,
+                                nblocks2, batch, dtype, act, 1 if with_bias else 0, buf, len(buf))
+    if n < 0:
+        raise MonarchError(n, monarch_status_string(n))
+    return buf.value.decode().split(";") if n else []

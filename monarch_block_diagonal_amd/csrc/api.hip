@@ -49,43 +49,40 @@ int run_plan(const Plan& plan, const Problem& pr, const Buffers& b, hipStream_t 
   return record_hip(tr.mark());
 }
 
-int fwd_impl(const void* x, const void* w1, const void* w2, void* y, void* z, int64_t in_f,
-             int64_t out_f, int64_t nb1, int64_t nb2, int64_t batch, int dtype, int act,
-             void* stream, void* const* events, int n_events) {
-  Problem pr;
-  int st = make_problem(in_f, out_f, nb1, nb2, batch, dtype, act, &pr);
-  if (st) return st;
+int fwd_impl(const Problem& pr, const void* x, const void* w1, const void* w2, const void* bias,
+             void* y, void* z, void* stream, void* const* events, int n_events) {
   if (!w1 || !w2) return MONARCH_ERR_NULL;
-  if (batch > 0 && (!x || !y || !z)) return MONARCH_ERR_NULL;
-  if (misaligned(x) || misaligned(w1) || misaligned(w2) || misaligned(y) || misaligned(z))
+  if (pr.bias && !bias) return MONARCH_ERR_NULL;
+  if (pr.batch > 0 && (!x || !y || !z)) return MONARCH_ERR_NULL;
+  if (misaligned(x) || misaligned(w1) || misaligned(w2) || misaligned(y) || misaligned(z) ||
+      misaligned(bias))
     return MONARCH_ERR_ALIGN;
-  if (batch == 0) return MONARCH_OK;
+  if (pr.batch == 0) return MONARCH_OK;
   Buffers b;
   b.x = x;
   b.w1 = w1;
   b.w2 = w2;
+  b.bias = bias;
   b.y_out = y;
   b.z_out = z;
   Plan plan = plan_fwd(pr);
   return run_plan(plan, pr, b, static_cast<hipStream_t>(stream), events, n_events);
 }
 
-int bwd_impl(const void* dy, const void* x, const void* w1, const void* w2, const void* z,
-             const void* y, void* dx, void* dw1, void* dw2, void* ws, size_t ws_bytes,
-             int64_t in_f, int64_t out_f, int64_t nb1, int64_t nb2, int64_t batch, int dtype,
-             int act, void* stream, void* const* events, int n_events) {
-  Problem pr;
-  int st = make_problem(in_f, out_f, nb1, nb2, batch, dtype, act, &pr);
-  if (st) return st;
+int bwd_impl(const Problem& pr, const void* dy, const void* x, const void* w1, const void* w2,
+             const void* z, const void* y, void* dx, void* dw1, void* dw2, void* dbias, void* ws,
+             size_t ws_bytes, void* stream, void* const* events, int n_events) {
   if (!w1 || !w2 || !dw1 || !dw2) return MONARCH_ERR_NULL;
-  if (batch > 0) {
+  if (pr.bias && !dbias) return MONARCH_ERR_NULL;
+  if (pr.batch > 0) {
     if (!dy || !x || !z || !dx) return MONARCH_ERR_NULL;
-    if (act == MONARCH_ACT_RELU && !y) return MONARCH_ERR_NULL;
+    if (pr.act == MONARCH_ACT_RELU && !y) return MONARCH_ERR_NULL;
   }
   const size_t need = workspace_bytes(pr);
   if (need > 0 && !ws) return MONARCH_ERR_NULL;
   if (misaligned(dy) || misaligned(x) || misaligned(w1) || misaligned(w2) || misaligned(z) ||
-      misaligned(y) || misaligned(dx) || misaligned(dw1) || misaligned(dw2) || misaligned(ws))
+      misaligned(y) || misaligned(dx) || misaligned(dw1) || misaligned(dw2) ||
+      misaligned(dbias) || misaligned(ws))
     return MONARCH_ERR_ALIGN;
   if (ws_bytes < need) return MONARCH_ERR_WORKSPACE;
   Buffers b;
@@ -98,9 +95,34 @@ int bwd_impl(const void* dy, const void* x, const void* w1, const void* w2, cons
   b.dx = dx;
   b.dw1 = dw1;
   b.dw2 = dw2;
+  b.dbias = dbias;
   b.ws = ws;
   Plan plan = plan_bwd(pr);
   return run_plan(plan, pr, b, static_cast<hipStream_t>(stream), events, n_events);
+}
+
+int describe_plan(const Problem& pr, int direction, char* buf, size_t buf_len) {
+  if (direction != 0 && direction != 1) return MONARCH_ERR_DTYPE;
+  Plan plan;
+  if (direction == 0)
+    plan = pr.batch == 0 ? Plan{} : plan_fwd(pr);
+  else
+    plan = plan_bwd(pr);
+  if (buf && buf_len) {
+    buf[0] = '\0';
+    size_t used = 0;
+    for (int i = 0; i < plan.n; ++i) {
+      const char* nm = step_name(plan.kind[i]);
+      int w = snprintf(buf + used, buf_len - used, "%s%s", i ? ";" : "", nm);
+      if (w < 0) break;
+      used += static_cast<size_t>(w);
+      if (used >= buf_len) {
+        buf[buf_len - 1] = '\0';
+        break;
+      }
+    }
+  }
+  return plan.n;
 }
 
 }  // namespace
@@ -113,16 +135,18 @@ extern "C" {
 int monarch_fwd(const void* x, const void* w1, const void* w2, void* y, void* z,
                 int64_t in_features, int64_t out_features, int64_t nblocks1, int64_t nblocks2,
                 int64_t batch, int dtype, int act, void* stream) {
-  return fwd_impl(x, w1, w2, y, z, in_features, out_features, nblocks1, nblocks2, batch, dtype,
-                  act, stream, nullptr, 0);
+  return monarch_fwd_traced(x, w1, w2, y, z, in_features, out_features, nblocks1, nblocks2, batch,
+                            dtype, act, stream, nullptr, 0);
 }
 
 int monarch_fwd_traced(const void* x, const void* w1, const void* w2, void* y, void* z,
                        int64_t in_features, int64_t out_features, int64_t nblocks1,
                        int64_t nblocks2, int64_t batch, int dtype, int act, void* stream,
                        void* const* events, int n_events) {
-  return fwd_impl(x, w1, w2, y, z, in_features, out_features, nblocks1, nblocks2, batch, dtype,
-                  act, stream, events, n_events);
+  Problem pr;
+  int st = make_problem(in_features, out_features, nblocks1, nblocks2, batch, dtype, act, &pr);
+  if (st) return st;
+  return fwd_impl(pr, x, w1, w2, nullptr, y, z, stream, events, n_events);
 }
 
 size_t monarch_bwd_workspace_bytes(int64_t in_features, int64_t out_features, int64_t nblocks1,
@@ -138,8 +162,9 @@ int monarch_bwd(const void* dy, const void* x, const void* w1, const void* w2, c
                 size_t workspace_bytes, int64_t in_features, int64_t out_features,
                 int64_t nblocks1, int64_t nblocks2, int64_t batch, int dtype, int act,
                 void* stream) {
-  return bwd_impl(dy, x, w1, w2, z, y, dx, dw1, dw2, workspace, workspace_bytes, in_features,
-                  out_features, nblocks1, nblocks2, batch, dtype, act, stream, nullptr, 0);
+  return monarch_bwd_traced(dy, x, w1, w2, z, y, dx, dw1, dw2, workspace, workspace_bytes,
+                            in_features, out_features, nblocks1, nblocks2, batch, dtype, act,
+                            stream, nullptr, 0);
 }
 
 int monarch_bwd_traced(const void* dy, const void* x, const void* w1, const void* w2,
@@ -147,8 +172,65 @@ int monarch_bwd_traced(const void* dy, const void* x, const void* w1, const void
                        void* workspace, size_t workspace_bytes, int64_t in_features,
                        int64_t out_features, int64_t nblocks1, int64_t nblocks2, int64_t batch,
                        int dtype, int act, void* stream, void* const* events, int n_events) {
-  return bwd_impl(dy, x, w1, w2, z, y, dx, dw1, dw2, workspace, workspace_bytes, in_features,
-                  out_features, nblocks1, nblocks2, batch, dtype, act, stream, events, n_events);
+  Problem pr;
+  int st = make_problem(in_features, out_features, nblocks1, nblocks2, batch, dtype, act, &pr);
+  if (st) return st;
+  return bwd_impl(pr, dy, x, w1, w2, z, y, dx, dw1, dw2, nullptr, workspace, workspace_bytes,
+                  stream, events, n_events);
+}
+
+int64_t monarch_linear_mid(int64_t in_features, int64_t out_features, int64_t nblocks) {
+  const int64_t lim = int64_t(1) << 31;
+  if (in_features <= 0 || out_features <= 0 || nblocks <= 0 || in_features >= lim ||
+      out_features >= lim || nblocks >= lim)
+    return MONARCH_ERR_SHAPE;
+  const int64_t in_ext = (in_features + nblocks - 1) / nblocks * nblocks;
+  const int64_t out_ext = (out_features + nblocks - 1) / nblocks * nblocks;
+  return in_ext < out_ext ? in_ext : out_ext;
+}
+
+int monarch_fwd_ex(const void* x, const void* w1, const void* w2, const void* bias, void* y,
+                   void* z, int64_t in_features, int64_t out_features, int64_t mid_features,
+                   int64_t nblocks1, int64_t nblocks2, int64_t batch, int dtype, int act,
+                   void* stream, void* const* events, int n_events) {
+  Problem pr;
+  int st = make_problem_ex(in_features, out_features, mid_features, nblocks1, nblocks2, batch,
+                           dtype, act, bias != nullptr, &pr);
+  if (st) return st;
+  return fwd_impl(pr, x, w1, w2, bias, y, z, stream, events, n_events);
+}
+
+size_t monarch_bwd_ex_workspace_bytes(int64_t in_features, int64_t out_features,
+                                      int64_t mid_features, int64_t nblocks1, int64_t nblocks2,
+                                      int64_t batch, int dtype, int with_bias) {
+  Problem pr;
+  if (make_problem_ex(in_features, out_features, mid_features, nblocks1, nblocks2, batch, dtype, 0,
+                      with_bias != 0, &pr))
+    return 0;
+  return workspace_bytes(pr);
+}
+
+int monarch_bwd_ex(const void* dy, const void* x, const void* w1, const void* w2, const void* z,
+                   const void* y, void* dx, void* dw1, void* dw2, void* dbias, void* workspace,
+                   size_t workspace_bytes, int64_t in_features, int64_t out_features,
+                   int64_t mid_features, int64_t nblocks1, int64_t nblocks2, int64_t batch,
+                   int dtype, int act, void* stream, void* const* events, int n_events) {
+  Problem pr;
+  int st = make_problem_ex(in_features, out_features, mid_features, nblocks1, nblocks2, batch,
+                           dtype, act, dbias != nullptr, &pr);
+  if (st) return st;
+  return bwd_impl(pr, dy, x, w1, w2, z, y, dx, dw1, dw2, dbias, workspace, workspace_bytes, stream,
+                  events, n_events);
+}
+
+int monarch_describe_ex(int direction, int64_t in_features, int64_t out_features,
+                        int64_t mid_features, int64_t nblocks1, int64_t nblocks2, int64_t batch,
+                        int dtype, int act, int with_bias, char* buf, size_t buf_len) {
+  Problem pr;
+  int st = make_problem_ex(in_features, out_features, mid_features, nblocks1, nblocks2, batch,
+                           dtype, act, with_bias != 0, &pr);
+  if (st) return st;
+  return describe_plan(pr, direction, buf, buf_len);
 }
 
 int monarch_project(const void* m, void* w1, void* w2, int64_t in_features,
@@ -174,27 +256,7 @@ int monarch_describe(int direction, int64_t in_features, int64_t out_features, i
   Problem pr;
   int st = make_problem(in_features, out_features, nblocks1, nblocks2, batch, dtype, act, &pr);
   if (st) return st;
-  if (direction != 0 && direction != 1) return MONARCH_ERR_DTYPE;
-  Plan plan;
-  if (direction == 0)
-    plan = batch == 0 ? Plan{} : plan_fwd(pr);
-  else
-    plan = plan_bwd(pr);
-  if (buf && buf_len) {
-    buf[0] = '\0';
-    size_t used = 0;
-    for (int i = 0; i < plan.n; ++i) {
-      const char* nm = step_name(plan.kind[i]);
-      int w = snprintf(buf + used, buf_len - used, "%s%s", i ? ";" : "", nm);
-      if (w < 0) break;
-      used += static_cast<size_t>(w);
-      if (used >= buf_len) {
-        buf[buf_len - 1] = '\0';
-        break;
-      }
-    }
-  }
-  return plan.n;
+  return describe_plan(pr, direction, buf, buf_len);
 }
 
 const char* monarch_status_string(int status) {

@@ -29,6 +29,15 @@ struct GemmArgs {
   int64_t b_sb = 0, b_sk = 0, b_sj = 0;
   int64_t c_sb = 0, c_si = 0, c_sj = 0;
   int64_t nsplit = 0, b_sj_hi = 0, c_sj_hi = 0;
+  // Zero padding and truncation (all optional, -1 = none): in block blk only
+  // k < k_lim - blk*k_lim_bs takes part in the sum (A and B), only B columns
+  // j < n_lim - blk*n_lim_bs are read (others count as zero), and only C
+  // entries whose row-relative offset blk*c_sb + (column offset) is below
+  // c_cols are written.
+  int64_t k_lim = -1, k_lim_bs = 0, n_lim = -1, n_lim_bs = 0, c_cols = -1;
+  // Optional bias (I/O type) added before `relu`, indexed by the row-relative
+  // C offset.
+  const void* bias = nullptr;
   int64_t M = 0, N = 0, K = 0;
   int64_t nblk = 1;
   int64_t splits = 1;
@@ -36,41 +45,42 @@ struct GemmArgs {
   int relu = 0;
 };
 
-// Tile sizes of the generic kernel (shared with the host planner).
-constexpr int kGenBM = 64;
-constexpr int kGenBN = 64;
-constexpr int kGenBK = 32;
-
-hipError_t launch_generic_gemm(const GemmArgs& a, bool bf16, hipStream_t s);
-
 // Reduction-chunk granularity of batch-split GEMMs (a multiple of both
 // kernels' K steps).
 constexpr int kSplitK = 64;
 
-// The tiled kernel (tiled.hip): 16-byte operand loads, for GEMMs whose A is
-// contiguous along K or M and whose B is contiguous along K or N (with
-// `nsplit`, B must be K-contiguous). tiled_gemm_applicable says whether a
-// GEMM qualifies; launch_gemm takes the tiled kernel when it does and the
-// generic one otherwise.
-bool tiled_gemm_applicable(const GemmArgs& a, bool bf16);
-hipError_t launch_tiled_gemm(const GemmArgs& a, bool bf16, hipStream_t s);
+// The tiled GEMM (tiled.hip) runs every GemmArgs: operands move as 16-byte
+// pieces when they are contiguous along a tile dimension with 16-byte
+// aligned rows, element by element otherwise.
 hipError_t launch_gemm(const GemmArgs& a, bool bf16, hipStream_t s);
 
-// dV[b, g*q2o + p] = dY[b, p*b2 + g], times 1[Y > 0] when ymask is set: dY
-// (and the ReLU derivative) gathered into the block-major order of stage 2's
-// backward products. rows x out elements; out = b2 * q2o.
+// dV[b, g*q2o + p] = dY[b, p*b2 + g] for p*b2 + g < out, else 0, times
+// 1[Y > 0] when ymask is set: dY (and the ReLU derivative) gathered into the
+// block-major order of stage 2's backward products. dY and Y are rows x out,
+// dV is rows x (b2*q2o).
 hipError_t launch_dv_gather(const void* dy, const void* ymask, void* dv, int64_t rows, int64_t out,
                             int64_t b2, int64_t q2o, bool bf16, hipStream_t s);
+
+// Bias gradient partial sums: partial[c][p*b2 + g] = sum over rows
+// [c*chunk, (c+1)*chunk) of dV[b, g*q2o + p], for p*b2 + g < out (fp32,
+// rows in increasing order).
+hipError_t launch_bias_partials(const void* dv, float* partial, int64_t rows, int64_t chunk,
+                                int64_t chunks, int64_t out, int64_t b2, int64_t q2o, bool bf16,
+                                hipStream_t s);
 
 // Writes `bytes` zero bytes (a plain kernel, not hipMemsetAsync, so callers may
 // capture it in a graph). p must be 2-byte aligned and bytes a multiple of 2.
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
 
-// Both weight gradients in one launch: outA[e] = sum_{s < splitsA} partialA[s*nA + e]
-// in increasing s (likewise B), stored in the I/O type (fixed order:
-// bit-reproducible).
-hipError_t launch_reduce_partials(const float* partialA, void* outA, int64_t nA, int64_t splitsA,
-                                  const float* partialB, void* outB, int64_t nB, int64_t splitsB,
+// Up to three gradients in one launch: out[e] = sum_{s < splits} partial[s*n + e]
+// in increasing s, stored in the I/O type (fixed order: bit-reproducible).
+// An entry with n == 0 is skipped.
+struct ReduceArgs {
+  const float* partial = nullptr;
+  void* out = nullptr;
+  int64_t n = 0, splits = 1;
+};
+hipError_t launch_reduce_partials(const ReduceArgs& a, const ReduceArgs& b, const ReduceArgs& c,
                                   bool bf16, hipStream_t s);
 
 // Dense -> Monarch projection: one workgroup per (g, r) slice of M

@@ -38,7 +38,7 @@ void choose_splits(int64_t nblk, int64_t M, int64_t N, int64_t K, int64_t* split
     *chunk = 0;
     return;
   }
-  const int64_t base = nblk * ((M + kGenBM - 1) / kGenBM) * ((N + kGenBN - 1) / kGenBN);
+  const int64_t base = nblk * ((M + 63) / 64) * ((N + 63) / 64);
   int64_t s = (2048 + base - 1) / base;
   const int64_t smax_k = (K + 127) / 128;
   if (s > smax_k) s = smax_k;
@@ -52,31 +52,38 @@ void choose_splits(int64_t nblk, int64_t M, int64_t N, int64_t K, int64_t* split
 
 }  // namespace
 
-int make_problem(int64_t in, int64_t out, int64_t nb1, int64_t nb2, int64_t batch, int dtype,
-                 int act, Problem* pr) {
+int make_problem_ex(int64_t in, int64_t out, int64_t mid, int64_t nb1, int64_t nb2, int64_t batch,
+                    int dtype, int act, bool bias, Problem* pr) {
   if (dtype != MONARCH_F32 && dtype != MONARCH_BF16) return MONARCH_ERR_DTYPE;
   if (act != MONARCH_ACT_NONE && act != MONARCH_ACT_RELU) return MONARCH_ERR_DTYPE;
-  if (in <= 0 || out <= 0 || nb1 <= 0 || nb2 <= 0 || batch < 0) return MONARCH_ERR_SHAPE;
-  if (in >= kDimLimit || out >= kDimLimit || batch >= kDimLimit) return MONARCH_ERR_SHAPE;
-  const int64_t mid = out;
-  if (in % nb1 || mid % nb1 || mid % nb2 || out % nb2) return MONARCH_ERR_SHAPE;
+  if (in <= 0 || out <= 0 || mid <= 0 || nb1 <= 0 || nb2 <= 0 || batch < 0)
+    return MONARCH_ERR_SHAPE;
+  if (in >= kDimLimit || out >= kDimLimit || mid >= kDimLimit || batch >= kDimLimit ||
+      nb1 >= kDimLimit || nb2 >= kDimLimit)
+    return MONARCH_ERR_SHAPE;
+  if (mid % nb1 || mid % nb2) return MONARCH_ERR_SHAPE;
   Problem p;
   p.in = in;
   p.out = out;
   p.mid = mid;
   p.b1 = nb1;
   p.b2 = nb2;
-  p.q1i = in / nb1;
+  p.q1i = (in + nb1 - 1) / nb1;
   p.q1o = mid / nb1;
   p.q2i = mid / nb2;
-  p.q2o = out / nb2;
+  p.q2o = (out + nb2 - 1) / nb2;
+  p.in_ext = p.q1i * nb1;
+  p.out_ext = p.q2o * nb2;
+  if (p.in_ext >= kDimLimit || p.out_ext >= kDimLimit) return MONARCH_ERR_SHAPE;
+  p.bias = bias;
   p.batch = batch;
   p.dtype = dtype;
   p.act = act;
   p.esize = dtype == MONARCH_BF16 ? 2 : 4;
   p.path = PATH_GENERIC;
   p.z_stage2_order = p.q1o % nb2 == 0;
-  if (batch > 0 && sq_applicable(in, out, nb1, nb2, batch, dtype == MONARCH_BF16)) {
+  const bool whole = p.in_ext == in && p.out_ext == out && mid == out && !bias;
+  if (batch > 0 && whole && sq_applicable(in, out, nb1, nb2, batch, dtype == MONARCH_BF16)) {
     p.path = PATH_SQ128;
     p.sq = sq_plan(batch, nb1);
     p.s2 = p.sq.w2_chunks;
@@ -95,11 +102,29 @@ int make_problem(int64_t in, int64_t out, int64_t nb1, int64_t nb2, int64_t batc
     off = align_up(off + static_cast<size_t>(p.s1) * nb1 * p.q1o * p.q1i * 4, 256);
     // dY in block-major order (sq path: panels, generic path: rows)
     p.ws_dv = off;
-    off = align_up(off + static_cast<size_t>(batch) * out * p.esize, 256);
+    off = align_up(off + static_cast<size_t>(batch) * p.out_ext * p.esize, 256);
+    if (bias) {
+      // bias-gradient partials: about 256 rows per chunk, at most 256 chunks
+      int64_t chunks = (batch + 255) / 256;
+      if (chunks > 256) chunks = 256;
+      p.bias_chunk = (batch + chunks - 1) / chunks;
+      p.bias_chunks = (batch + p.bias_chunk - 1) / p.bias_chunk;
+      p.ws_pb = off;
+      off = align_up(off + static_cast<size_t>(p.bias_chunks) * out * 4, 256);
+    }
     p.ws_total = off;
   }
   *pr = p;
   return MONARCH_OK;
+}
+
+int make_problem(int64_t in, int64_t out, int64_t nb1, int64_t nb2, int64_t batch, int dtype,
+                 int act, Problem* pr) {
+  if (dtype != MONARCH_F32 && dtype != MONARCH_BF16) return MONARCH_ERR_DTYPE;
+  if (act != MONARCH_ACT_NONE && act != MONARCH_ACT_RELU) return MONARCH_ERR_DTYPE;
+  if (in <= 0 || out <= 0 || nb1 <= 0 || nb2 <= 0 || batch < 0) return MONARCH_ERR_SHAPE;
+  if (in % nb1 || out % nb1 || out % nb2) return MONARCH_ERR_SHAPE;
+  return make_problem_ex(in, out, out, nb1, nb2, batch, dtype, act, false, pr);
 }
 
 size_t workspace_bytes(const Problem& pr) { return pr.ws_total; }
@@ -132,6 +157,7 @@ Plan plan_bwd(const Problem& pr) {
     return p;
   }
   p.add(GEN_DV_GATHER);
+  if (pr.bias) p.add(GEN_BIAS_PARTIALS);
   p.add(GEN_STAGE2_BWD_DATA);
   p.add(GEN_STAGE2_BWD_WEIGHT);
   p.add(GEN_STAGE1_BWD_DATA);
@@ -143,6 +169,7 @@ Plan plan_bwd(const Problem& pr) {
 const char* step_name(StepKind k) {
   switch (k) {
     case GEN_DV_GATHER: return "generic_dv_gather";
+    case GEN_BIAS_PARTIALS: return "generic_bias_partials";
     case GEN_STAGE1_FWD: return "generic_stage1_fwd";
     case GEN_STAGE2_FWD: return "generic_stage2_fwd";
     case GEN_STAGE2_BWD_DATA: return "generic_stage2_bwd_data";
@@ -169,13 +196,19 @@ hipError_t launch_step(StepKind k, const Problem& pr, const Buffers& b, hipStrea
   float* p1 = ws ? reinterpret_cast<float*>(ws + pr.ws_p1) : nullptr;
   const void* mask = pr.act == MONARCH_ACT_RELU ? b.y : nullptr;
   void* dv = ws ? ws + pr.ws_dv : nullptr;
+  float* pb = ws && pr.bias ? reinterpret_cast<float*>(ws + pr.ws_pb) : nullptr;
   GemmArgs a;
   switch (k) {
     case GEN_DV_GATHER:
       return launch_dv_gather(b.dy, mask, dv, pr.batch, pr.out, pr.b2, pr.q2o, bf16, s);
+    case GEN_BIAS_PARTIALS:
+      return launch_bias_partials(dv, pb, pr.batch, pr.bias_chunk, pr.bias_chunks, pr.out, pr.b2,
+                                  pr.q2o, bf16, s);
     case GEN_STAGE1_FWD:
+      // X is zero-padded to whole blocks: block r sums over k < in - r*q1i
       a.A = b.x;
       a.a_sb = pr.q1i, a.a_si = pr.in, a.a_sk = 1;
+      a.k_lim = pr.in, a.k_lim_bs = pr.q1i;
       a.B = b.w1;
       a.b_sb = pr.q1o * pr.q1i, a.b_sk = 1;
       a.C = b.z_out;
@@ -194,6 +227,7 @@ hipError_t launch_step(StepKind k, const Problem& pr, const Buffers& b, hipStrea
       a.M = pr.batch, a.N = pr.q1o, a.K = pr.q1i, a.nblk = pr.b1;
       return launch_gemm(a, bf16, s);
     case GEN_STAGE2_FWD:
+      // outputs past `out` are dropped; bias and ReLU in the epilogue
       a.A = b.z_out;
       if (pr.z_stage2_order)
         a.a_sb = pr.q2i, a.a_si = pr.mid, a.a_sk = 1;
@@ -202,13 +236,14 @@ hipError_t launch_step(StepKind k, const Problem& pr, const Buffers& b, hipStrea
       a.B = b.w2;
       a.b_sb = pr.q2o * pr.q2i, a.b_sk = 1, a.b_sj = pr.q2i;
       a.C = b.y_out;
-      a.c_sb = 1, a.c_si = pr.out, a.c_sj = pr.b2;
+      a.c_sb = 1, a.c_si = pr.out, a.c_sj = pr.b2, a.c_cols = pr.out;
+      a.bias = b.bias;
       a.M = pr.batch, a.N = pr.q2o, a.K = pr.q2i, a.nblk = pr.b2;
       a.relu = pr.act == MONARCH_ACT_RELU;
       return launch_gemm(a, bf16, s);
     case GEN_STAGE2_BWD_DATA:
       a.A = dv;
-      a.a_sb = pr.q2o, a.a_si = pr.out, a.a_sk = 1;
+      a.a_sb = pr.q2o, a.a_si = pr.out_ext, a.a_sk = 1;
       a.B = b.w2;
       a.b_sb = pr.q2o * pr.q2i, a.b_sk = pr.q2i, a.b_sj = 1;
       a.C = dz;
@@ -217,7 +252,7 @@ hipError_t launch_step(StepKind k, const Problem& pr, const Buffers& b, hipStrea
       return launch_gemm(a, bf16, s);
     case GEN_STAGE2_BWD_WEIGHT:
       a.A = dv;
-      a.a_sb = pr.q2o, a.a_si = 1, a.a_sk = pr.out;
+      a.a_sb = pr.q2o, a.a_si = 1, a.a_sk = pr.out_ext;
       a.B = b.z;
       if (pr.z_stage2_order)
         a.b_sb = pr.q2i, a.b_sk = pr.mid, a.b_sj = 1;
@@ -227,25 +262,32 @@ hipError_t launch_step(StepKind k, const Problem& pr, const Buffers& b, hipStrea
       a.M = pr.q2o, a.N = pr.q2i, a.K = pr.batch, a.nblk = pr.b2;
       return launch_gemm(a, bf16, s);
     case GEN_STAGE1_BWD_DATA:
+      // dX of the padded input positions is dropped
       a.A = dz;
       a.a_sb = pr.q1o, a.a_si = pr.mid, a.a_sk = 1;
       a.B = b.w1;
       a.b_sb = pr.q1o * pr.q1i, a.b_sk = pr.q1i, a.b_sj = 1;
       a.C = b.dx;
-      a.c_sb = pr.q1i, a.c_si = pr.in, a.c_sj = 1;
+      a.c_sb = pr.q1i, a.c_si = pr.in, a.c_sj = 1, a.c_cols = pr.in;
       a.M = pr.batch, a.N = pr.q1i, a.K = pr.q1o, a.nblk = pr.b1;
       return launch_gemm(a, bf16, s);
     case GEN_STAGE1_BWD_WEIGHT:
+      // padded input positions read as zero: their weight gradient is 0
       a.A = dz;
       a.a_sb = pr.q1o, a.a_si = 1, a.a_sk = pr.mid;
       a.B = b.x;
       a.b_sb = pr.q1i, a.b_sk = pr.in, a.b_sj = 1;
+      a.n_lim = pr.in, a.n_lim_bs = pr.q1i;
       a.partial = p1, a.splits = pr.s1, a.k_chunk = pr.kc1;
       a.M = pr.q1o, a.N = pr.q1i, a.K = pr.batch, a.nblk = pr.b1;
       return launch_gemm(a, bf16, s);
-    case REDUCE_DW:
-      return launch_reduce_partials(p2, b.dw2, pr.b2 * pr.q2o * pr.q2i, pr.s2, p1, b.dw1,
-                                    pr.b1 * pr.q1o * pr.q1i, pr.s1, bf16, s);
+    case REDUCE_DW: {
+      ReduceArgs r2, r1, rb;
+      r2.partial = p2, r2.out = b.dw2, r2.n = pr.b2 * pr.q2o * pr.q2i, r2.splits = pr.s2;
+      r1.partial = p1, r1.out = b.dw1, r1.n = pr.b1 * pr.q1o * pr.q1i, r1.splits = pr.s1;
+      if (pr.bias) rb.partial = pb, rb.out = b.dbias, rb.n = pr.out, rb.splits = pr.bias_chunks;
+      return launch_reduce_partials(r2, r1, rb, bf16, s);
+    }
     case SQ_DV_PANELS:
       return sq_launch_dv_panels(b.dy, mask, dv, pr.batch, pr.b2, s);
     case SQ_STAGE1_FWD:
@@ -262,7 +304,9 @@ hipError_t launch_step(StepKind k, const Problem& pr, const Buffers& b, hipStrea
     case ZERO_DW: {
       hipError_t e = launch_zero(b.dw2, static_cast<size_t>(pr.b2 * pr.q2o * pr.q2i) * pr.esize, s);
       if (e != hipSuccess) return e;
-      return launch_zero(b.dw1, static_cast<size_t>(pr.b1 * pr.q1o * pr.q1i) * pr.esize, s);
+      e = launch_zero(b.dw1, static_cast<size_t>(pr.b1 * pr.q1o * pr.q1i) * pr.esize, s);
+      if (e != hipSuccess || !pr.bias) return e;
+      return launch_zero(b.dbias, static_cast<size_t>(pr.out) * pr.esize, s);
     }
   }
   return hipErrorInvalidValue;

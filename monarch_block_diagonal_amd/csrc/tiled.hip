@@ -45,11 +45,16 @@ __device__ __forceinline__ void pin(u32x4& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *static_cast<const u32x4*>(p); }
 
 // One operand tile (A: rows = M, B: rows = N) of ROWS x TK elements.
-//   mode 1 (K-contiguous): unit = one 16-byte piece (row r, k piece kp);
-//   mode 2 (row-contiguous): unit = four k rows of one 16-byte row piece.
-// init() resolves each unit's row address once (rows past `lim` are clamped
-// to an in-range row and later stored as zeros); `sk` is the K stride.
-template <typename T, int MODE, int ROWS>
+//   mode 1 (K-major units): unit = VEC consecutive k of one row;
+//   mode 2 (row-major units): unit = four consecutive k of VEC consecutive rows.
+// With `vec` a unit's VEC elements are one 16-byte load (the operand is
+// contiguous along the unit with 16-byte aligned starts, and every limit is
+// a multiple of VEC); otherwise they are loaded one by one with any strides.
+// init() resolves each unit's row address once; elements past the row limit
+// or the K range are loaded from a clamped in-range address and stored as
+// zeros. An operand row sits at base + (r / ns)*hi + (r % ns)*lo (ns > 0,
+// mode 1 only) or base + r*lo; `sk` is the K stride.
+template <typename T, int MODE, int ROWS, bool EW>
 struct Tile {
   using C = Cfg<T>;
   static constexpr int VEC = C::VEC, TK = C::TK;
@@ -57,12 +62,17 @@ struct Tile {
   static constexpr int NU = (UNITS + TT - 1) / TT;
   static constexpr int NR = MODE == 1 ? NU : 4 * NU;
   static constexpr int LDS = C::rowoff(ROWS);
-  static_assert(MODE == 1 || ROWS % VEC == 0, "row pieces");
+  static_assert(ROWS % VEC == 0, "row pieces");
 
-  const T* row[NU];   // row address of each unit (k = 0)
-  bool rowok[NU];
-  int64_t sk, kb, ke;
+  const T* row[NU];   // address of the unit's first element at k = 0
+  int nrow[NU];       // valid rows of the unit (mode 1: 0 or 1; mode 2: 0..VEC)
+  int eclamp[NU];     // mode 2: largest row offset loads may use
+  int64_t lo, sk, kb, ke;
+  bool vec_;
   u32x4 reg[NR];
+
+  // without EW every operand of the launch moves as 16-byte pieces
+  __device__ __forceinline__ bool vec() const { return EW ? vec_ : true; }
 
   __device__ __forceinline__ static bool active(int q) {
     return UNITS % TT == 0 || static_cast<int>(threadIdx.x) + TT * q < UNITS;
@@ -75,19 +85,32 @@ struct Tile {
     const int id = threadIdx.x + TT * q;
     return MODE == 1 ? (id % (TK / VEC)) * VEC : 4 * (id / (ROWS / VEC));
   }
+  __device__ __forceinline__ static u32x4 pack(const T (&v)[VEC]) {
+    u32x4 r;
+    __builtin_memcpy(&r, v, sizeof(r));
+    return r;
+  }
 
-  // row r of the operand sits at base + (r / ns)*hi + (r % ns)*lo (ns > 0)
-  // or base + r*lo
-  __device__ __forceinline__ void init(const T* base, int64_t r0, int64_t lim, int64_t lo,
+  // lim >= 1 rows are valid (callers skip the K loop when an operand has none)
+  __device__ __forceinline__ void init(const T* base, int64_t r0, int64_t lim, int64_t lo_,
                                        int64_t hi, int64_t ns, int64_t sk_, int64_t kb_,
-                                       int64_t ke_) {
-    sk = sk_, kb = kb_, ke = ke_;
+                                       int64_t ke_, bool vec_in) {
+    lo = lo_, sk = sk_, kb = kb_, ke = ke_, vec_ = vec_in;
 #pragma unroll
     for (int q = 0; q < NU; ++q) {
       const int64_t gr = r0 + unit_row(q);
-      rowok[q] = gr < lim;
-      const int64_t r = rowok[q] ? gr : 0;
-      row[q] = base + (ns > 0 ? (r / ns) * hi + (r % ns) * lo : r * lo);
+      if constexpr (MODE == 1) {
+        nrow[q] = gr < lim ? 1 : 0;
+        eclamp[q] = 0;
+        const int64_t r = gr < lim ? gr : 0;
+        row[q] = base + (ns > 0 ? (r / ns) * hi + (r % ns) * lo : r * lo);
+      } else {
+        const int64_t nv = lim - gr;
+        nrow[q] = nv <= 0 ? 0 : (nv >= VEC ? VEC : static_cast<int>(nv));
+        const int64_t room = nv > 0 ? nv : lim;           // rows loads may touch
+        eclamp[q] = room >= VEC ? VEC - 1 : static_cast<int>(room - 1);
+        row[q] = base + (nv > 0 ? gr : 0) * lo;
+      }
     }
   }
 
@@ -95,22 +118,53 @@ struct Tile {
 #pragma unroll
     for (int q = 0; q < NU; ++q) {
       if (!active(q)) continue;
+      const int k = unit_k(q);
       if constexpr (MODE == 1) {
-        int64_t gk = k0 + unit_k(q);
-        gk = gk < ke ? gk : kb;
-        reg[q] = ld16(row[q] + gk);
+        if (vec()) {
+          int64_t gk = k0 + k;
+          gk = gk < ke ? gk : kb;
+          reg[q] = ld16(row[q] + gk);
+        } else {
+          T v[VEC];
+#pragma unroll
+          for (int e = 0; e < VEC; ++e) {
+            int64_t gk = k0 + k + e;
+            gk = gk < ke ? gk : ke - 1;
+            v[e] = row[q][gk * sk];
+          }
+          reg[q] = pack(v);
+        }
       } else {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          int64_t gk = k0 + unit_k(q) + i;
-          gk = gk < ke ? gk : kb;
-          reg[4 * q + i] = ld16(row[q] + gk * sk);
+          int64_t gk = k0 + k + i;
+          gk = gk < ke ? gk : ke - 1;
+          if (vec()) {
+            reg[4 * q + i] = ld16(row[q] + gk * sk);
+          } else {
+            T v[VEC];
+#pragma unroll
+            for (int e = 0; e < VEC; ++e) v[e] = row[q][(e < eclamp[q] ? e : eclamp[q]) * lo + gk * sk];
+            reg[4 * q + i] = pack(v);
+          }
         }
       }
     }
   }
 
-  // units loaded clamped (row past `lim`, k past `ke`) are stored as zeros
+  // keep element e of a loaded unit piece only where keep_e holds
+  __device__ __forceinline__ static u32x4 mask_elems(u32x4 v, int nvalid_rows, bool kok_all,
+                                                     int64_t kfirst, int64_t ke_) {
+    T el[VEC];
+    __builtin_memcpy(el, &v, sizeof(v));
+#pragma unroll
+    for (int e = 0; e < VEC; ++e) {
+      const bool keep = MODE == 1 ? (nvalid_rows > 0 && kfirst + e < ke_) : (e < nvalid_rows && kok_all);
+      if (!keep) el[e] = T(0);
+    }
+    return pack(el);
+  }
+
   __device__ __forceinline__ void store(T* s, int64_t k0) {
 #pragma unroll
     for (int q = 0; q < NU; ++q) {
@@ -118,16 +172,24 @@ struct Tile {
       const int r = unit_row(q), k = unit_k(q);
       if constexpr (MODE == 1) {
         pin(reg[q]);
-        const bool keep = rowok[q] && k0 + k < ke;
-        const u32x4 v = keep ? reg[q] : u32x4{0u, 0u, 0u, 0u};
+        u32x4 v;
+        if (vec()) {
+          const bool keep = nrow[q] > 0 && k0 + k < ke;
+          v = keep ? reg[q] : u32x4{0u, 0u, 0u, 0u};
+        } else {
+          v = mask_elems(reg[q], nrow[q], true, k0 + k, ke);
+        }
         *reinterpret_cast<u32x4*>(s + C::rowoff(r) + k) = v;
       } else {
         u32x4 v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           pin(reg[4 * q + i]);
-          const bool keep = rowok[q] && k0 + k + i < ke;
-          v[i] = keep ? reg[4 * q + i] : u32x4{0u, 0u, 0u, 0u};
+          const bool kok = k0 + k + i < ke;
+          if (vec())
+            v[i] = (nrow[q] > 0 && kok) ? reg[4 * q + i] : u32x4{0u, 0u, 0u, 0u};
+          else
+            v[i] = mask_elems(reg[4 * q + i], nrow[q], kok, 0, 0);
         }
         if constexpr (C::kBf16) {
           u32x2 tr[8];
@@ -147,14 +209,15 @@ struct Tile {
   }
 };
 
-template <typename T, int AM, int BMD, int WM, int WN, int FM, int FN>
+template <typename T, int AM, int BMD, int WM, int WN, int FM, int FN, bool EW>
 __global__ __launch_bounds__(TT) void tiled_gemm_kernel(GemmArgs p, int64_t m_tiles,
-                                                        int64_t n_tiles, int remap) {
+                                                        int64_t n_tiles, int remap, int avec,
+                                                        int bvec) {
   using C = Cfg<T>;
   constexpr int TM = WM * FM * 16, TN = WN * FN * 16, TK = C::TK;
   static_assert(WM * WN == 4, "four waves");
-  using TA = Tile<T, AM, TM>;
-  using TB = Tile<T, BMD, TN>;
+  using TA = Tile<T, AM, TM, EW>;
+  using TB = Tile<T, BMD, TN, EW>;
   __shared__ __attribute__((aligned(16))) T As[TA::LDS];
   __shared__ __attribute__((aligned(16))) T Bs[TB::LDS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -170,15 +233,26 @@ __global__ __launch_bounds__(TT) void tiled_gemm_kernel(GemmArgs p, int64_t m_ti
   const int64_t mt = t % m_tiles;
   const int64_t split = t / m_tiles;
   const int64_t kb = p.partial ? split * p.k_chunk : 0;
-  const int64_t ke = p.partial ? (kb + p.k_chunk < p.K ? kb + p.k_chunk : p.K) : p.K;
+  int64_t ke = p.partial ? (kb + p.k_chunk < p.K ? kb + p.k_chunk : p.K) : p.K;
+  // zero padding: this block's valid K range and B columns
+  if (p.k_lim >= 0) {
+    const int64_t kv = p.k_lim - blk * p.k_lim_bs;
+    ke = ke < kv ? ke : kv;
+  }
+  int64_t nlim = p.N;
+  if (p.n_lim >= 0) {
+    const int64_t nv = p.n_lim - blk * p.n_lim_bs;
+    nlim = nlim < nv ? nlim : nv;
+  }
+  if (nlim <= 0 || ke < kb) ke = kb;   // nothing to sum: the K loop is skipped
   const int64_t i0 = mt * TM, j0 = nt * TN;
 
   TA a;
-  a.init(static_cast<const T*>(p.A) + blk * p.a_sb, i0, p.M, AM == 1 ? p.a_si : 1, 0, 0, p.a_sk,
-         kb, ke);
+  a.init(static_cast<const T*>(p.A) + blk * p.a_sb, i0, p.M, p.a_si, 0, 0, p.a_sk, kb, ke,
+         avec != 0);
   TB b;
-  b.init(static_cast<const T*>(p.B) + blk * p.b_sb, j0, p.N, BMD == 1 ? p.b_sj : 1, p.b_sj_hi,
-         BMD == 1 ? p.nsplit : 0, p.b_sk, kb, ke);
+  b.init(static_cast<const T*>(p.B) + blk * p.b_sb, j0, nlim > 0 ? nlim : 1, p.b_sj, p.b_sj_hi,
+         BMD == 1 ? p.nsplit : 0, p.b_sk, kb, ke, bvec != 0);
 
   f32x4 acc[FM][FN];
 #pragma unroll
@@ -245,7 +319,7 @@ __global__ __launch_bounds__(TT) void tiled_gemm_kernel(GemmArgs p, int64_t m_ti
 #pragma unroll
   for (int ni = 0; ni < FN; ++ni) {
     const int64_t j = j0 + (wn * FN + ni) * 16 + l15;
-    const int64_t joff = col_off(j, p.nsplit, p.c_sj_hi, p.c_sj);
+    const int64_t cpos = blk * p.c_sb + col_off(j, p.nsplit, p.c_sj_hi, p.c_sj);   // in-row offset
 #pragma unroll
     for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
@@ -255,9 +329,10 @@ __global__ __launch_bounds__(TT) void tiled_gemm_kernel(GemmArgs p, int64_t m_ti
           float val = acc[mi][ni][v];
           if (p.partial) {
             p.partial[((split * p.nblk + blk) * p.M + i) * p.N + j] = val;
-          } else {
+          } else if (p.c_cols < 0 || cpos < p.c_cols) {
+            if (p.bias) val += Io<T>::load(p.bias, cpos);
             if (p.relu) val = val > 0.f ? val : 0.f;
-            Io<T>::store(p.C, blk * p.c_sb + i * p.c_si + joff, val);
+            Io<T>::store(p.C, i * p.c_si + cpos, val);
           }
         }
       }
@@ -290,7 +365,7 @@ __device__ __forceinline__ u32x4 mask_piece(u32x4 v, u32x4 m) {
 // dV rows from dY rows through LDS: each workgroup takes rpw whole rows,
 // reads them with 16-byte loads (masking on the way), and writes the
 // permuted rows with 16-byte stores. dV position o = g*q2o + p takes dY
-// position p*b2 + g.
+// position p*b2 + g when that is below out (truncated outputs: 0).
 template <typename T>
 __global__ __launch_bounds__(256) void dv_gather_lds_kernel(const T* __restrict__ dY,
                                                             const T* __restrict__ Ym,
@@ -300,26 +375,28 @@ __global__ __launch_bounds__(256) void dv_gather_lds_kernel(const T* __restrict_
   constexpr int VEC = 16 / static_cast<int>(sizeof(T));
   extern __shared__ __attribute__((aligned(16))) unsigned char dv_smem[];
   T* s = reinterpret_cast<T*>(dv_smem);
+  const int64_t oext = b2 * q2o;
   const int64_t row0 = static_cast<int64_t>(blockIdx.x) * rpw;
   const int64_t nr = rows - row0 < rpw ? rows - row0 : rpw;
-  const int64_t pieces = nr * out / VEC;
+  const int64_t in_pieces = nr * out / VEC, out_pieces = nr * oext / VEC;
   const T* src = dY + row0 * out;
   const T* msk = Ym ? Ym + row0 * out : nullptr;
-  for (int64_t e = threadIdx.x; e < pieces; e += 256) {
+  for (int64_t e = threadIdx.x; e < in_pieces; e += 256) {
     u32x4 v = ld16(src + e * VEC);
     if (msk) v = mask_piece<T>(v, ld16(msk + e * VEC));
     *reinterpret_cast<u32x4*>(s + e * VEC) = v;
   }
   __syncthreads();
-  T* dst = dV + row0 * out;
-  for (int64_t e = threadIdx.x; e < pieces; e += 256) {
-    const int64_t r = (e * VEC) / out, o0 = e * VEC - r * out;
+  T* dst = dV + row0 * oext;
+  for (int64_t e = threadIdx.x; e < out_pieces; e += 256) {
+    const int64_t r = (e * VEC) / oext, o0 = e * VEC - r * oext;
     T vals[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
       const int64_t o = o0 + i;
       const int64_t g = o / q2o, pp = o - g * q2o;
-      vals[i] = s[r * out + pp * b2 + g];
+      const int64_t so = pp * b2 + g;
+      vals[i] = so < out ? s[r * out + so] : T(0);
     }
     u32x4 w;
     __builtin_memcpy(&w, vals, sizeof(w));
@@ -327,22 +404,46 @@ __global__ __launch_bounds__(256) void dv_gather_lds_kernel(const T* __restrict_
   }
 }
 
-// Element-wise fallback for rows that are too long for LDS or not a whole
+// Element-wise form for rows that are too long for LDS or not a whole
 // number of 16-byte pieces.
 template <typename T>
 __global__ __launch_bounds__(256) void dv_gather_kernel(const T* __restrict__ dY,
                                                         const T* __restrict__ Ym,
                                                         T* __restrict__ dV, int64_t rows,
                                                         int64_t out, int64_t b2, int64_t q2o) {
-  const int64_t n = rows * out;
+  const int64_t oext = b2 * q2o;
+  const int64_t n = rows * oext;
   for (int64_t e = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e < n;
        e += static_cast<int64_t>(gridDim.x) * 256) {
-    const int64_t b = e / out, o = e - b * out;
-    const int64_t src = b * out + (o % q2o) * b2 + o / q2o;
-    T v = dY[src];
-    if (Ym && !(Io<T>::load(Ym, src) > 0.f)) v = T(0);
+    const int64_t b = e / oext, o = e - b * oext;
+    const int64_t so = (o % q2o) * b2 + o / q2o;
+    T v = T(0);
+    if (so < out) {
+      const int64_t src = b * out + so;
+      v = dY[src];
+      if (Ym && !(Io<T>::load(Ym, src) > 0.f)) v = T(0);
+    }
     dV[e] = v;
   }
+}
+
+// partial[c][p*b2 + g] = sum over rows of chunk c of dV[b, g*q2o + p]: one
+// thread per dV column, rows in increasing order (deterministic).
+template <typename T>
+__global__ __launch_bounds__(256) void bias_partials_kernel(const T* __restrict__ dV,
+                                                            float* __restrict__ partial,
+                                                            int64_t rows, int64_t chunk,
+                                                            int64_t out, int64_t b2, int64_t q2o) {
+  const int64_t oext = b2 * q2o;
+  const int64_t col = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
+  const int64_t c = blockIdx.y;
+  if (col >= oext) return;
+  const int64_t g = col / q2o, pp = col - g * q2o, o = pp * b2 + g;
+  if (o >= out) return;
+  const int64_t r0 = c * chunk, r1 = r0 + chunk < rows ? r0 + chunk : rows;
+  float acc = 0.f;
+  for (int64_t b = r0; b < r1; ++b) acc += Io<T>::load(dV, b * oext + col);
+  partial[c * out + o] = acc;
 }
 
 // Tile shapes (TM x TN) and their wave grids
@@ -354,6 +455,7 @@ Shape pick_shape(int64_t M, int64_t N) {
     if (N > 32) return S256x64;
     return S256x32;
   }
+  if (M <= 32) return S32x32;
   if (M > 64 && N > 64) return S128x128;
   if (M > 32 || N > 32) return S64x64;
   return S32x32;
@@ -369,18 +471,20 @@ void shape_tiles(Shape s, int* tm, int* tn) {
   }
 }
 
-bool mode1_ok(int64_t s_contig, int64_t s_row, int64_t s_blk, int64_t kdim, int vec) {
-  return s_contig == 1 && s_row % vec == 0 && s_blk % vec == 0 && kdim % vec == 0;
-}
-bool mode2_ok(int64_t s_contig, int64_t s_k, int64_t s_blk, int64_t rows, int vec) {
-  return s_contig == 1 && s_k % vec == 0 && s_blk % vec == 0 && rows % vec == 0;
+bool lim_ok(int64_t lim, int64_t lim_bs, int vec) {
+  return lim < 0 || (lim % vec == 0 && lim_bs % vec == 0);
 }
 
 template <typename T, int AM, int BMD>
 hipError_t launch_modes(const GemmArgs& a, Shape sh, dim3 g, int64_t mt, int64_t nt, int remap,
-                        hipStream_t s) {
-#define MONARCH_TILED(WM, WN, FM, FN) \
-  hipLaunchKernelGGL((tiled_gemm_kernel<T, AM, BMD, WM, WN, FM, FN>), g, dim3(TT), 0, s, a, mt, nt, remap)
+                        int avec, int bvec, hipStream_t s) {
+#define MONARCH_TILED(WM, WN, FM, FN)                                                         \
+  if (avec && bvec)                                                                             \
+    hipLaunchKernelGGL((tiled_gemm_kernel<T, AM, BMD, WM, WN, FM, FN, false>), g, dim3(TT), 0, s, \
+                       a, mt, nt, remap, 1, 1);                                                 \
+  else                                                                                          \
+    hipLaunchKernelGGL((tiled_gemm_kernel<T, AM, BMD, WM, WN, FM, FN, true>), g, dim3(TT), 0, s,  \
+                       a, mt, nt, remap, avec, bvec)
   switch (sh) {
     case S128x128: MONARCH_TILED(2, 2, 4, 4); break;
     case S256x64: MONARCH_TILED(4, 1, 4, 4); break;
@@ -392,27 +496,28 @@ hipError_t launch_modes(const GemmArgs& a, Shape sh, dim3 g, int64_t mt, int64_t
   return hipGetLastError();
 }
 
+int64_t iabs(int64_t v) { return v < 0 ? -v : v; }
+
 }  // namespace
 
-bool tiled_gemm_applicable(const GemmArgs& a, bool bf16) {
+hipError_t launch_gemm(const GemmArgs& a, bool bf16, hipStream_t s) {
   const int vec = bf16 ? 8 : 4;
-  if (a.M < 16 || a.N < 16 || a.K < 16) return false;  // tiny blocks: the generic kernel
-  if (a.partial && (a.k_chunk % kSplitK != 0 || a.nsplit > 0)) return false;
-  const bool a1 = mode1_ok(a.a_sk, a.a_si, a.a_sb, a.K, vec);
-  const bool a2 = mode2_ok(a.a_si, a.a_sk, a.a_sb, a.M, vec);
-  const bool b1 = a.nsplit > 0
-                      ? (a.b_sk == 1 && a.b_sj % vec == 0 && a.b_sj_hi % vec == 0 &&
-                         a.b_sb % vec == 0 && a.K % vec == 0)
-                      : mode1_ok(a.b_sk, a.b_sj, a.b_sb, a.K, vec);
-  const bool b2 = a.nsplit == 0 && mode2_ok(a.b_sj, a.b_sk, a.b_sb, a.N, vec);
-  return (a1 || a2) && (b1 || b2);
-}
-
-hipError_t launch_tiled_gemm(const GemmArgs& a, bool bf16, hipStream_t s) {
-  if (!tiled_gemm_applicable(a, bf16)) return hipErrorInvalidValue;
-  const int vec = bf16 ? 8 : 4;
-  const bool a1 = mode1_ok(a.a_sk, a.a_si, a.a_sb, a.K, vec);
-  const bool b1 = a.nsplit > 0 || mode1_ok(a.b_sk, a.b_sj, a.b_sb, a.K, vec);
+  // A: K-major units when K is its faster dimension, row-major otherwise
+  const int am = a.a_sk == 1 ? 1 : (a.a_si == 1 ? 2 : (iabs(a.a_sk) <= iabs(a.a_si) ? 1 : 2));
+  const bool klim = lim_ok(a.k_lim, a.k_lim_bs, vec);
+  const bool avec = am == 1 ? (a.a_sk == 1 && a.a_si % vec == 0 && a.a_sb % vec == 0 &&
+                               a.K % vec == 0 && klim)
+                            : (a.a_si == 1 && a.a_sk % vec == 0 && a.a_sb % vec == 0 &&
+                               a.M % vec == 0);
+  // B: the column split needs K-major units
+  const int bm = a.nsplit > 0 ? 1
+                              : (a.b_sk == 1 ? 1 : (a.b_sj == 1 ? 2 : (iabs(a.b_sk) <= iabs(a.b_sj) ? 1 : 2)));
+  const bool bvec = bm == 1 ? (a.b_sk == 1 && a.b_sj % vec == 0 &&
+                               (a.nsplit == 0 || a.b_sj_hi % vec == 0) && a.b_sb % vec == 0 &&
+                               a.K % vec == 0 && klim)
+                            : (a.b_sj == 1 && a.b_sk % vec == 0 && a.b_sb % vec == 0 &&
+                               a.N % vec == 0 && lim_ok(a.n_lim, a.n_lim_bs, vec));
+  if (a.partial && (a.k_chunk % kSplitK != 0 || a.nsplit > 0)) return hipErrorInvalidValue;
   const Shape sh = pick_shape(a.M, a.N);
   int tm, tn;
   shape_tiles(sh, &tm, &tn);
@@ -422,31 +527,27 @@ hipError_t launch_tiled_gemm(const GemmArgs& a, bool bf16, hipStream_t s) {
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   const int remap = grid % 8 == 0 ? 1 : 0;
   const dim3 g(static_cast<unsigned>(grid));
+  const int av = avec ? 1 : 0, bv = bvec ? 1 : 0;
   if (bf16) {
-    if (a1 && b1) return launch_modes<uint16_t, 1, 1>(a, sh, g, mt, nt, remap, s);
-    if (a1) return launch_modes<uint16_t, 1, 2>(a, sh, g, mt, nt, remap, s);
-    if (b1) return launch_modes<uint16_t, 2, 1>(a, sh, g, mt, nt, remap, s);
-    return launch_modes<uint16_t, 2, 2>(a, sh, g, mt, nt, remap, s);
+    if (am == 1 && bm == 1) return launch_modes<uint16_t, 1, 1>(a, sh, g, mt, nt, remap, av, bv, s);
+    if (am == 1) return launch_modes<uint16_t, 1, 2>(a, sh, g, mt, nt, remap, av, bv, s);
+    if (bm == 1) return launch_modes<uint16_t, 2, 1>(a, sh, g, mt, nt, remap, av, bv, s);
+    return launch_modes<uint16_t, 2, 2>(a, sh, g, mt, nt, remap, av, bv, s);
   }
-  if (a1 && b1) return launch_modes<float, 1, 1>(a, sh, g, mt, nt, remap, s);
-  if (a1) return launch_modes<float, 1, 2>(a, sh, g, mt, nt, remap, s);
-  if (b1) return launch_modes<float, 2, 1>(a, sh, g, mt, nt, remap, s);
-  return launch_modes<float, 2, 2>(a, sh, g, mt, nt, remap, s);
-}
-
-hipError_t launch_gemm(const GemmArgs& a, bool bf16, hipStream_t s) {
-  return tiled_gemm_applicable(a, bf16) ? launch_tiled_gemm(a, bf16, s)
-                                        : launch_generic_gemm(a, bf16, s);
+  if (am == 1 && bm == 1) return launch_modes<float, 1, 1>(a, sh, g, mt, nt, remap, av, bv, s);
+  if (am == 1) return launch_modes<float, 1, 2>(a, sh, g, mt, nt, remap, av, bv, s);
+  if (bm == 1) return launch_modes<float, 2, 1>(a, sh, g, mt, nt, remap, av, bv, s);
+  return launch_modes<float, 2, 2>(a, sh, g, mt, nt, remap, av, bv, s);
 }
 
 hipError_t launch_dv_gather(const void* dy, const void* ymask, void* dv, int64_t rows, int64_t out,
                             int64_t b2, int64_t q2o, bool bf16, hipStream_t s) {
-  const int64_t n = rows * out;
-  if (n <= 0) return hipSuccess;
+  const int64_t oext = b2 * q2o;
+  if (rows <= 0 || oext <= 0) return hipSuccess;
   const int esz = bf16 ? 2 : 4, vec = 16 / esz;
   constexpr int64_t kLds = 32768;
   const int64_t row_bytes = out * esz;
-  if (out % vec == 0 && row_bytes <= kLds) {
+  if (out % vec == 0 && oext % vec == 0 && row_bytes <= kLds) {
     const int rpw = static_cast<int>(kLds / row_bytes);
     const int64_t blocks = (rows + rpw - 1) / rpw;
     if (blocks <= 0x7fffffffLL) {
@@ -464,7 +565,7 @@ hipError_t launch_dv_gather(const void* dy, const void* ymask, void* dv, int64_t
       return hipGetLastError();
     }
   }
-  int64_t blocks = (n + 255) / 256;
+  int64_t blocks = (rows * oext + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (bf16)
     hipLaunchKernelGGL(dv_gather_kernel<uint16_t>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0,
@@ -474,6 +575,23 @@ hipError_t launch_dv_gather(const void* dy, const void* ymask, void* dv, int64_t
     hipLaunchKernelGGL(dv_gather_kernel<float>, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
                        static_cast<const float*>(dy), static_cast<const float*>(ymask),
                        static_cast<float*>(dv), rows, out, b2, q2o);
+  return hipGetLastError();
+}
+
+hipError_t launch_bias_partials(const void* dv, float* partial, int64_t rows, int64_t chunk,
+                                int64_t chunks, int64_t out, int64_t b2, int64_t q2o, bool bf16,
+                                hipStream_t s) {
+  const int64_t oext = b2 * q2o;
+  if (rows <= 0 || chunks <= 0) return hipSuccess;
+  const int64_t gx = (oext + 255) / 256;
+  if (gx > 0x7fffffffLL || chunks > 65535) return hipErrorInvalidConfiguration;
+  const dim3 g(static_cast<unsigned>(gx), static_cast<unsigned>(chunks));
+  if (bf16)
+    hipLaunchKernelGGL(bias_partials_kernel<uint16_t>, g, dim3(256), 0, s,
+                       static_cast<const uint16_t*>(dv), partial, rows, chunk, out, b2, q2o);
+  else
+    hipLaunchKernelGGL(bias_partials_kernel<float>, g, dim3(256), 0, s,
+                       static_cast<const float*>(dv), partial, rows, chunk, out, b2, q2o);
   return hipGetLastError();
 }
 

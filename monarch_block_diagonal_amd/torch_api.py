@@ -5,7 +5,9 @@ supplies the stream; the library's kernels do all the arithmetic.
     dx, dw1, dw2 = monarch_backward(dy, x, w1, w2, z)
 
 MonarchLinearFunction wraps the pair as an autograd function, so the operator
-can stand in for a dense linear layer.
+can stand in for a dense linear layer. The *_ex helpers and the MonarchLinear
+module take the general layer (any in/out, zero-padded to whole blocks, an
+explicit intermediate width, optional bias).
 """
 from __future__ import annotations
 
@@ -100,3 +102,105 @@ class MonarchLinearFunction(torch.autograd.Function):
         x, w1, w2, z, y = ctx.saved_tensors
         dx, dw1, dw2 = monarch_backward(dy.contiguous(), x, w1, w2, z, y, ctx.act)
         return dx, dw1, dw2, None
+
+
+def ex_problem(x, w1, w2, out_features: int):
+    """(in, out, mid, nb1, nb2, batch) of the general layer from tensor shapes."""
+    if x.dim() != 2 or w1.dim() != 3 or w2.dim() != 3:
+        raise ValueError("x must be [batch, in], w1 [b1, q1o, q1i], w2 [b2, q2o, q2i]")
+    nb1, q1o, q1i = w1.shape
+    nb2, q2o, q2i = w2.shape
+    mid = nb1 * q1o
+    if nb2 * q2i != mid:
+        raise ValueError("w1 and w2 disagree on the intermediate width")
+    return x.shape[1], out_features, mid, nb1, nb2, x.shape[0]
+
+
+def monarch_forward_ex(x, w1, w2, out_features: int, bias=None, act: int = B.ACT_NONE,
+                       stream=None):
+    """y = act(pad(x) · Mᵀ truncated to out_features + bias); returns (y, z)."""
+    _check(x, w1, w2, bias)
+    fi, fo, mid, nb1, nb2, b = ex_problem(x, w1, w2, out_features)
+    y = torch.empty((b, fo), dtype=x.dtype, device=x.device)
+    z = torch.empty((b, mid), dtype=x.dtype, device=x.device)
+    B.monarch_fwd_ex(x, w1, w2, bias, y, z, fi, fo, mid, nb1, nb2, b, dtype_code(x), act, stream)
+    return y, z
+
+
+def monarch_backward_ex(dy, x, w1, w2, z, y=None, with_bias: bool = False,
+                        act: int = B.ACT_NONE, stream=None):
+    """(dx, dw1, dw2, dbias or None) of the general layer."""
+    _check(dy, x, w1, w2, z, y)
+    fi, fo, mid, nb1, nb2, b = ex_problem(x, w1, w2, dy.shape[1])
+    code = dtype_code(x)
+    dx = torch.empty_like(x)
+    dw1 = torch.empty_like(w1)
+    dw2 = torch.empty_like(w2)
+    db = torch.empty((fo,), dtype=x.dtype, device=x.device) if with_bias else None
+    need = B.monarch_bwd_ex_workspace_bytes(fi, fo, mid, nb1, nb2, b, code, with_bias)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    B.monarch_bwd_ex(dy, x, w1, w2, z, y, dx, dw1, dw2, db, ws, need, fi, fo, mid, nb1, nb2, b,
+                     code, act, stream)
+    return dx, dw1, dw2, db
+
+
+class MonarchLinearExFunction(torch.autograd.Function):
+    """y = act(pad(x) · Mᵀ truncated to out_features + bias)."""
+
+    @staticmethod
+    def forward(ctx, x, w1, w2, bias, out_features: int, act: int = B.ACT_NONE):
+        x, w1, w2 = x.contiguous(), w1.contiguous(), w2.contiguous()
+        bias = bias.contiguous() if bias is not None else None
+        y, z = monarch_forward_ex(x, w1, w2, out_features, bias, act)
+        ctx.act = act
+        ctx.with_bias = bias is not None
+        ctx.save_for_backward(x, w1, w2, z, y if act == B.ACT_RELU else None)
+        return y
+
+    @staticmethod
+    def backward(ctx, dy):
+        x, w1, w2, z, y = ctx.saved_tensors
+        dx, dw1, dw2, db = monarch_backward_ex(dy.contiguous(), x, w1, w2, z, y, ctx.with_bias,
+                                               ctx.act)
+        return dx, dw1, dw2, db, None, None
+
+
+class MonarchLinear(torch.nn.Module):
+    """Drop-in for a dense linear layer with the MonarchLinear sizes of the
+    "Definition C.3" thread of the scatterbrain issues page: block sizes
+    ceil(in/nblocks) and ceil(out/nblocks), intermediate width in_ext for an
+    expanding layer and out_ext otherwise; the input is zero-padded to whole
+    blocks and the output keeps the first out_features. Optional bias and
+    fused ReLU (act)."""
+
+    def __init__(self, in_features: int, out_features: int, nblocks: int = 4, bias: bool = True,
+                 act: int = B.ACT_NONE, device=None, dtype=torch.float32):
+        super().__init__()
+        self.in_features, self.out_features, self.nblocks, self.act = (
+            in_features, out_features, nblocks, act)
+        mid = B.monarch_linear_mid(in_features, out_features, nblocks)
+        q1i = -(-in_features // nblocks)
+        q2o = -(-out_features // nblocks)
+        self.mid = mid
+        self.w1 = torch.nn.Parameter(torch.empty((nblocks, mid // nblocks, q1i), device=device,
+                                                 dtype=dtype))
+        self.w2 = torch.nn.Parameter(torch.empty((nblocks, q2o, mid // nblocks), device=device,
+                                                 dtype=dtype))
+        self.bias = (torch.nn.Parameter(torch.empty(out_features, device=device, dtype=dtype))
+                     if bias else None)
+        self.reset_parameters()
+
+    @torch.no_grad()
+    def reset_parameters(self):
+        # each factor block is a small dense layer: uniform(+-1/sqrt(fan_in))
+        for w in (self.w1, self.w2):
+            bound = w.shape[2] ** -0.5
+            w.uniform_(-bound, bound)
+        if self.bias is not None:
+            self.bias.uniform_(-self.in_features ** -0.5, self.in_features ** -0.5)
+
+    def forward(self, x):
+        shape = x.shape
+        y = MonarchLinearExFunction.apply(x.reshape(-1, shape[-1]), self.w1, self.w2, self.bias,
+                                          self.out_features, self.act)
+        return y.reshape(*shape[:-1], self.out_features)

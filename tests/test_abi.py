@@ -175,3 +175,69 @@ def test_project_bad_dtype_null_align():
     for name in ("m", "w1", "w2"):
         assert proj(**{name: None}) == B.MONARCH_ERR_NULL
         assert proj(**{name: MIS}) == B.MONARCH_ERR_ALIGN
+
+
+# ---------------------------------------------------------------------------
+# general layer (*_ex): explicit mid, zero padding, truncation, bias
+
+def fwd_ex(x=A, w1=A, w2=A, bias=None, y=A2, z=A2, fi=10, fo=7, mid=8, nb1=4, nb2=4, b=5,
+           dt=B.F32, act=B.ACT_NONE):
+    lib = M.load_library()
+    return lib.monarch_fwd_ex(x, w1, w2, bias, y, z, fi, fo, mid, nb1, nb2, b, dt, act, None,
+                              None, 0)
+
+
+def bwd_ex(dy=A, x=A, w1=A, w2=A, z=A, y=A, dx=A2, dw1=A2, dw2=A2, db=None, ws=A2, wsb=1 << 40,
+           fi=10, fo=7, mid=8, nb1=4, nb2=4, b=5, dt=B.F32, act=B.ACT_NONE):
+    lib = M.load_library()
+    return lib.monarch_bwd_ex(dy, x, w1, w2, z, y, dx, dw1, dw2, db, ws, wsb, fi, fo, mid, nb1,
+                              nb2, b, dt, act, None, None, 0)
+
+
+def test_linear_mid_follows_the_constructor_rule():
+    # ceil block sizes; mid = in_ext when in_ext < out_ext, else out_ext
+    assert M.monarch_linear_mid(768, 3072, 4) == 768
+    assert M.monarch_linear_mid(3072, 768, 4) == 768
+    assert M.monarch_linear_mid(10, 7, 4) == 8
+    assert M.monarch_linear_mid(5, 13, 4) == 8
+    assert M.monarch_linear_mid(10000, 1024, 16) == 1024
+    with pytest.raises(M.MonarchError):
+        M.monarch_linear_mid(0, 8, 4)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(mid=10),                 # mid % nb1
+    dict(mid=12, nb2=8),          # mid % nb2
+    dict(mid=0), dict(fi=0), dict(fo=0), dict(b=-1), dict(nb1=0),
+    dict(fi=1 << 31, nb1=1),
+])
+def test_ex_bad_shapes(kw):
+    assert fwd_ex(**kw) == B.MONARCH_ERR_SHAPE
+    assert bwd_ex(**kw) == B.MONARCH_ERR_SHAPE
+
+
+def test_ex_accepts_padded_sizes_and_checks_pointers():
+    # padded in/out are valid shapes: the pointer checks decide
+    assert fwd_ex(x=0) == B.MONARCH_ERR_NULL
+    assert fwd_ex(bias=MIS) == B.MONARCH_ERR_ALIGN
+    assert bwd_ex(db=MIS) == B.MONARCH_ERR_ALIGN
+    assert bwd_ex(wsb=0) == B.MONARCH_ERR_WORKSPACE
+    assert bwd_ex(act=B.ACT_RELU, y=None) == B.MONARCH_ERR_NULL
+    assert fwd_ex(b=0, x=None, y=None, z=None) == B.MONARCH_OK
+
+
+def test_ex_workspace_and_plan():
+    need = M.monarch_bwd_ex_workspace_bytes(10, 7, 8, 4, 4, 5, B.F32, True)
+    need_nb = M.monarch_bwd_ex_workspace_bytes(10, 7, 8, 4, 4, 5, B.F32, False)
+    assert need > need_nb > 0
+    names = M.monarch_describe_ex(1, 10, 7, 8, 4, 4, 5, B.F32, B.ACT_NONE, True)
+    assert "generic_bias_partials" in names and names[-1] == "reduce_dw"
+    # whole blocks, mid = out, no bias: the same plan as monarch_describe
+    for d in (0, 1):
+        assert (M.monarch_describe_ex(d, 16384, 16384, 16384, 128, 128, 4096, B.BF16)
+                == M.monarch_describe(d, 16384, 16384, 128, 128, 4096, B.BF16))
+    # a bias moves even the square shape to the generic path
+    names = M.monarch_describe_ex(0, 16384, 16384, 16384, 128, 128, 4096, B.BF16, B.ACT_NONE, True)
+    assert all(n.startswith("generic_") for n in names)
+    assert M.monarch_bwd_ex_workspace_bytes(16, 16, 16, 4, 4, 8, B.F32) == \
+        M.monarch_bwd_workspace_bytes(16, 16, 4, 4, 8, B.F32)
