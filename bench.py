@@ -118,9 +118,19 @@ def cpu_baseline(w, rows: int):
         threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         threads = len(os.sched_getaffinity(0))
+    general = [l for l in w.layers if l.mid != l.out_features or l.bias
+               or l.in_features % l.nblocks1 or l.out_features % l.nblocks2]
     t0 = time.perf_counter()
-    y, _ = O.mlp_forward(x, chain)
-    dx, _ = O.mlp_backward(dy, x, chain)
+    if general:
+        # one general layer (explicit mid, padding, bias): the MonarchLinear-variant oracle
+        from oracle import monarch_linear as ML
+        l, d = w.layers[0], ins[0]
+        bias = d.get("bias")
+        y = ML.forward_ex(x, d["w1"], d["w2"], l.in_features, l.out_features, l.mid, bias)
+        dx = ML.backward_ex(dy, x, d["w1"], d["w2"], l.in_features, l.out_features, l.mid, bias)[0]
+    else:
+        y, _ = O.mlp_forward(x, chain)
+        dx, _ = O.mlp_backward(dy, x, chain)
     dt = time.perf_counter() - t0
     flops = 6.0 * rows * w.params
     assert np.isfinite(y).all() and np.isfinite(dx).all()
@@ -236,6 +246,7 @@ def main() -> int:
     if args.op == "project":
         return bench_project(args)
 
+    import numpy as np
     import torch
     import monarch_block_diagonal_amd as M
     from monarch_block_diagonal_amd import synthetic as S
@@ -274,20 +285,26 @@ def main() -> int:
     for li, l in enumerate(layers):
         t1, t2 = (S.TID_W1, S.TID_W2) if li == 0 else (S.TID_W1_L2, S.TID_W2_L2)
         vr, vl = w.w_var[li]
-        fi, fo = l.in_features, l.out_features
-        d = {"l": l, "fi": fi, "fo": fo,
+        fi, fo, mid = l.in_features, l.out_features, l.mid
+        d = {"l": l, "fi": fi, "fo": fo, "mid": mid,
              "w1": draw(S.seed_for(w.cfg, t1), l.w1_shape, "normal", vr),
              "w2": draw(S.seed_for(w.cfg, t2), l.w2_shape, "normal", vl),
              "y": torch.empty((B, fo), dtype=tdt, device=dev),
-             "z": torch.empty((B, fo), dtype=tdt, device=dev),
+             "z": torch.empty((B, mid), dtype=tdt, device=dev),
+             "bias": (draw(S.seed_for(w.cfg, S.TID_BIAS + 10 * li), (fo,), "normal", 0.25)
+                      if l.bias else None),
              "dx": torch.empty((B, fi), dtype=tdt, device=dev),
              "act": M.ACT_RELU if l.relu else M.ACT_NONE,
-             "fn": M.monarch_describe(0, fi, fo, l.nblocks1, l.nblocks2, B, dt_code),
-             "bn": M.monarch_describe(1, fi, fo, l.nblocks1, l.nblocks2, B, dt_code)}
+             "fn": M.monarch_describe_ex(0, fi, fo, mid, l.nblocks1, l.nblocks2, B, dt_code,
+                                         M.ACT_RELU if l.relu else M.ACT_NONE, l.bias),
+             "bn": M.monarch_describe_ex(1, fi, fo, mid, l.nblocks1, l.nblocks2, B, dt_code,
+                                         M.ACT_RELU if l.relu else M.ACT_NONE, l.bias)}
         d["dw1"] = torch.empty_like(d["w1"])
         d["dw2"] = torch.empty_like(d["w2"])
+        d["db"] = torch.empty_like(d["bias"]) if l.bias else None
         d["x"] = x if li == 0 else L[li - 1]["y"]
-        wsb = max(wsb, M.monarch_bwd_workspace_bytes(fi, fo, l.nblocks1, l.nblocks2, B, dt_code))
+        wsb = max(wsb, M.monarch_bwd_ex_workspace_bytes(fi, fo, mid, l.nblocks1, l.nblocks2, B,
+                                                        dt_code, l.bias))
         L.append(d)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
     stream = torch.cuda.current_stream()
@@ -295,18 +312,19 @@ def main() -> int:
     def fwd(evs=None):
         for li, d in enumerate(L):
             l = d["l"]
-            M.monarch_fwd(d["x"], d["w1"], d["w2"], d["y"], d["z"], d["fi"], d["fo"], l.nblocks1,
-                          l.nblocks2, B, dt_code, d["act"], stream,
-                          events=None if evs is None else evs[li])
+            M.monarch_fwd_ex(d["x"], d["w1"], d["w2"], d["bias"], d["y"], d["z"], d["fi"],
+                             d["fo"], d["mid"], l.nblocks1, l.nblocks2, B, dt_code, d["act"],
+                             stream, events=None if evs is None else evs[li])
 
     def bwd(evs=None):
         g = dy
         for li in range(len(L) - 1, -1, -1):
             d, l = L[li], L[li]["l"]
-            M.monarch_bwd(g, d["x"], d["w1"], d["w2"], d["z"],
-                          d["y"] if d["act"] == M.ACT_RELU else None, d["dx"], d["dw1"], d["dw2"],
-                          ws, wsb, d["fi"], d["fo"], l.nblocks1, l.nblocks2, B, dt_code, d["act"],
-                          stream, events=None if evs is None else evs[li])
+            M.monarch_bwd_ex(g, d["x"], d["w1"], d["w2"], d["z"],
+                             d["y"] if d["act"] == M.ACT_RELU else None, d["dx"], d["dw1"],
+                             d["dw2"], d["db"], ws, wsb, d["fi"], d["fo"], d["mid"], l.nblocks1,
+                             l.nblocks2, B, dt_code, d["act"], stream,
+                             events=None if evs is None else evs[li])
             g = d["dx"]
 
     def step(evf=None, evb=None):
@@ -356,10 +374,9 @@ def main() -> int:
     for li, d in enumerate(L):
         l = d["l"]
         pre = f"L{li + 1}:" if multi else ""
-        pr = {"e": e, "batch": B, "in": d["fi"], "mid": d["fo"], "out": d["fo"],
+        pr = {"e": e, "batch": B, "in": d["fi"], "mid": d["mid"], "out": d["fo"],
               "act": 1 if l.relu else 0,
-              "params1": l.nblocks1 * (d["fo"] // l.nblocks1) * (d["fi"] // l.nblocks1),
-              "params2": l.nblocks2 * (d["fo"] // l.nblocks2) * (d["fo"] // l.nblocks2)}
+              "params1": int(np.prod(l.w1_shape)), "params2": int(np.prod(l.w2_shape))}
         for names, evs in ((d["fn"], [ev[li] for ev in evf]), (d["bn"], [ev[li] for ev in evb])):
             for i, nm in enumerate(names):
                 ts = [ev[i].elapsed_time(ev[i + 1]) for ev in evs]
@@ -389,7 +406,7 @@ def main() -> int:
     value = flops / (ms_per_step * 1e-3) / 1e12
     # whole step against the two-pass algorithmic bytes (each stage reads its
     # input and writes its output once, z saved; weights and gradients once)
-    b2p = sum(e * B * (d["fi"] + 3 * d["fo"]) + e * B * (4 * d["fo"] + 2 * d["fi"])
+    b2p = sum(e * B * (d["fi"] + 2 * d["mid"] + d["fo"]) + e * B * (d["fo"] + 3 * d["mid"] + 2 * d["fi"])
               + 3 * e * d["l"].params for d in L)
     t_roof = max(flops / (mfma_peak * 1e12), b2p / (HBM_PEAK_GBS * 1e9)) * 1e3
     step_roofline = {"binds": "mfma" if flops / (mfma_peak * 1e12) > b2p / (HBM_PEAK_GBS * 1e9)
@@ -461,8 +478,9 @@ def main() -> int:
         "dtype": w.dtype,
         "data": "synthetic (seeded, drawn on the device)",
         "config": {"workload": w.name, "layers": [
-            {"in_features": d["fi"], "out_features": d["fo"], "nblocks1": d["l"].nblocks1,
-             "nblocks2": d["l"].nblocks2, "relu_after": d["l"].relu} for d in L],
+            {"in_features": d["fi"], "out_features": d["fo"], "mid_features": d["mid"],
+             "nblocks1": d["l"].nblocks1, "nblocks2": d["l"].nblocks2, "relu_after": d["l"].relu,
+             "bias": d["l"].bias} for d in L],
             "batch": B, "params": w.params, "passes": "fwd+bwd"},
         "tokens_per_s": round(B / (ms_per_step * 1e-3), 1),
         "step_ms_p10_p50_p90": [round(pct(step_ms, q), 4) for q in (0.1, 0.5, 0.9)],

@@ -25,6 +25,7 @@ BASE_SEED = 20220401
 # tensor ids used in the seed formula
 TID_X, TID_W1, TID_W2, TID_DY = 0, 1, 2, 3
 TID_W1_L2, TID_W2_L2 = 11, 12
+TID_BIAS = 4
 
 
 def round_to_bf16(a: np.ndarray) -> np.ndarray:
@@ -60,14 +61,20 @@ class Layer:
     nblocks1: int
     nblocks2: int
     relu: bool = False            # activation fused after this layer
+    mid_features: int = 0         # intermediate width (0: out_features)
+    bias: bool = False
+
+    @property
+    def mid(self) -> int:
+        return self.mid_features or self.out_features
 
     @property
     def w1_shape(self) -> Tuple[int, int, int]:
-        return (self.nblocks1, self.out_features // self.nblocks1, self.in_features // self.nblocks1)
+        return (self.nblocks1, self.mid // self.nblocks1, -(-self.in_features // self.nblocks1))
 
     @property
     def w2_shape(self) -> Tuple[int, int, int]:
-        return (self.nblocks2, self.out_features // self.nblocks2, self.out_features // self.nblocks2)
+        return (self.nblocks2, -(-self.out_features // self.nblocks2), self.mid // self.nblocks2)
 
     @property
     def params(self) -> int:
@@ -119,6 +126,12 @@ _add(Workload("gpt2_ffn_up_768x3072_nb4", 2, (Layer(768, 3072, 4, 4),), 16 * 102
 for _nb in (4, 16):
     for _b in (10, 1000, 10000):
         _add(_recsys(_nb, _b))
+# the same FFN up-projection with the MonarchLinear sizes (expanding branch:
+# mid = in = 768, stage-1 blocks 4 x (192 x 192), stage-2 blocks 4 x (768 x 192))
+# and a bias
+_add(Workload("gpt2_ffn_up_monarchlinear_768x3072_nb4_bias", 2,
+              (Layer(768, 3072, 4, 4, mid_features=768, bias=True),), 16 * 1024, "bf16",
+              "normal", 1.0, ((1.0 / 192, 1.0 / 192),)))
 _add(Workload("square_n16384_b128", 4, (Layer(16384, 16384, 128, 128),), 65536, "bf16",
               "normal", 1.0, ((1.0 / 128, 1.0 / 128),)))
 
@@ -160,6 +173,9 @@ def make_layer_inputs(w: Workload, layer_index: int = 0, batch: int | None = Non
         "w1": draw(seed_for(w.cfg, t1), layer.w1_shape, "normal", vr, w.dtype),
         "w2": draw(seed_for(w.cfg, t2), layer.w2_shape, "normal", vl, w.dtype),
     }
+    if layer.bias:
+        out["bias"] = draw(seed_for(w.cfg, TID_BIAS + 10 * layer_index), (layer.out_features,),
+                           "normal", 0.25, w.dtype)
     if layer_index == 0:
         out["x"] = draw(seed_for(w.cfg, TID_X), (b, layer.in_features), w.x_dist, w.x_var, w.dtype)
     if with_dy:
