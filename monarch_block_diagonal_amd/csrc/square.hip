@@ -67,10 +67,6 @@ __device__ __forceinline__ bf16x8 frag_gather(const uint16_t* p) {
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-__device__ __forceinline__ uint16_t half_of(u32x4 v, int e) {
-  const uint32_t w = v[e >> 1];
-  return static_cast<uint16_t>((e & 1) ? (w >> 16) : (w & 0xffffu));
-}
 // bf16 bit pattern strictly greater than zero (NaN excluded)
 __device__ __forceinline__ bool bf16_pos(uint32_t h) {
   return (h & 0x8000u) == 0 && (h & 0x7fffu) != 0 && (h & 0x7fffu) <= 0x7f80u;
@@ -370,7 +366,9 @@ __global__ __launch_bounds__(512) void sq_stage2_fwd_kernel(const uint16_t* __re
 // ((i/8)*B + b)*8 + i%8, i = g*128 + p, through LDS in 256-byte runs. Both
 // backward stage-2 kernels then read dV contiguously.
 // Tile: RT = 256/GO rows x 16 p x 8*GO blocks (GO = min(16, b2/8) block
-// octets); 512 threads, one 8x8 block each; one tile per workgroup.
+// octets); 512 threads, one 8x8 block each; one tile per workgroup. The
+// staging row is XOR-swizzled with the block octet, so the 16-byte stores of
+// lanes with consecutive octets land on distinct banks.
 __global__ __launch_bounds__(512) void sq_dv_panels_kernel(const uint16_t* __restrict__ dY,
                                                            const uint16_t* __restrict__ Ym,
                                                            uint16_t* __restrict__ dV, int64_t B,
@@ -401,7 +399,7 @@ __global__ __launch_bounds__(512) void sq_dv_panels_kernel(const uint16_t* __res
   transpose4x8(*reinterpret_cast<const u32x4(*)[4]>(&in[4]), hi);
 #pragma unroll
   for (int e = 0; e < 8; ++e)
-    st[((go * 8 + e) * 2 + po) * RT + row] = u32x4{lo[e][0], lo[e][1], hi[e][0], hi[e][1]};
+    st[((go * 8 + e) * 2 + po) * RT + (row ^ go)] = u32x4{lo[e][0], lo[e][1], hi[e][0], hi[e][1]};
   __syncthreads();
   const int n_pieces = 8 * GO * 2 * RT;   // 4096
   for (int id = tid; id < n_pieces; id += 512) {
@@ -409,7 +407,7 @@ __global__ __launch_bounds__(512) void sq_dv_panels_kernel(const uint16_t* __res
     const int64_t bb = b0 + r;
     if (bb < B) {
       const int64_t panel = static_cast<int64_t>(gt * GO * 8 + gl) * 16 + 2 * pt + q;
-      stg16(dV + (panel * B + bb) * 8, st[(gl * 2 + q) * RT + r]);
+      stg16(dV + (panel * B + bb) * 8, st[(gl * 2 + q) * RT + (r ^ (gl >> 3))]);
     }
   }
 }
@@ -629,7 +627,6 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l15 = lane & 15, lh = lane >> 4;
   const uint32_t in = static_cast<uint32_t>(nb1) * Q;
-  const uint32_t Bu = static_cast<uint32_t>(B);
 
   // A = Rᵀ[s x k], gathered from R: lane holds R[r][k = 32ks + 8lh + e][s = 16w + l15]
   bf16x8 a[4];
