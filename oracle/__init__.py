@@ -10,3 +10,4 @@ from .monarch_oracle import (  # noqa: F401
 )
 from . import monarch_projection  # noqa: F401,E402
 from . import monarch_linear  # noqa: F401,E402
+from . import monarch_hypercube  # noqa: F401,E402
