@@ -207,6 +207,43 @@ int monarch_describe_ex(int direction, int64_t in_features, int64_t out_features
                         int64_t mid_features, int64_t nblocks1, int64_t nblocks2, int64_t batch,
                         int dtype, int act, int with_bias, char* buf, size_t buf_len);
 
+/* ---------------------------------------------------------------------------
+ * k-factor ("hypercube") Monarch layer (scatterbrain issues page, "hypercube"
+ * thread: the N units of a layer as a lattice, one round of block products
+ * per lattice dimension).
+ *
+ * dims[0..ndims-1] (1 <= ndims <= 4, N = prod dims < 2^31) is a row-major
+ * lattice: unit u has multi-index (a_1..a_k), u = ((a_1*n_2 + a_2)*n_3 + ...).
+ * Round j (in axis order j = 1..k) multiplies along axis j with one
+ * n_j x n_j matrix per combination of the other axes' indices:
+ *   w[j] [N/n_j, n_j, n_j], w[j][f][o, i] the weight from position i to o,
+ *   f = the other axes' indices flattened row-major in axis order.
+ * y = F_k ... F_1 x for every row (x, y [batch, N]). The forward also writes
+ * the outputs of rounds 1..k-1 to `saved` (monarch_hyper_saved_elems
+ * elements of the I/O dtype, a layout private to the library), which the
+ * backward reads. w and dw are host arrays of ndims device pointers.
+ * dtype, streams, ownership, alignment and errors as for monarch_fwd
+ * (a bad lattice gives MONARCH_ERR_SHAPE). */
+size_t monarch_hyper_saved_elems(int ndims, const int64_t* dims, int64_t batch);
+
+int monarch_hyper_fwd(const void* x, const void* const* w, void* y, void* saved, int ndims,
+                      const int64_t* dims, int64_t batch, int dtype, void* stream,
+                      void* const* events, int n_events);
+
+size_t monarch_hyper_bwd_workspace_bytes(int ndims, const int64_t* dims, int64_t batch,
+                                         int dtype);
+
+/* dx [batch, N] and dw[j] [N/n_j, n_j, n_j] (overwritten; fixed-order batch
+ * sums) from dy, x, w and the forward's `saved`. batch == 0 zeroes dw. */
+int monarch_hyper_bwd(const void* dy, const void* x, const void* const* w, const void* saved,
+                      void* dx, void* const* dw, void* workspace, size_t workspace_bytes,
+                      int ndims, const int64_t* dims, int64_t batch, int dtype, void* stream,
+                      void* const* events, int n_events);
+
+/* Kernel names of monarch_hyper_fwd (direction 0) / monarch_hyper_bwd (1). */
+int monarch_hyper_describe(int direction, int ndims, const int64_t* dims, int64_t batch,
+                           int dtype, char* buf, size_t buf_len);
+
 /* Static text for a status code; for MONARCH_ERR_HIP the last HIP error
  * message recorded on the calling thread. Never NULL. */
 const char* monarch_status_string(int status);

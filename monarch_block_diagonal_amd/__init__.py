@@ -11,5 +11,7 @@ from .binding import (  # noqa: F401
     ACT_NONE, ACT_RELU, BF16, F32, LIB_PATH, MonarchError, load_library, monarch_abi_version,
     monarch_bwd, monarch_bwd_workspace_bytes, monarch_describe, monarch_fwd, monarch_project,
     monarch_status_string, monarch_linear_mid, monarch_fwd_ex, monarch_bwd_ex,
-    monarch_bwd_ex_workspace_bytes, monarch_describe_ex,
+    monarch_bwd_ex_workspace_bytes, monarch_describe_ex, monarch_hyper_saved_elems,
+    monarch_hyper_fwd, monarch_hyper_bwd_workspace_bytes, monarch_hyper_bwd,
+    monarch_hyper_describe,
 )

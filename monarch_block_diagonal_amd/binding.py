@@ -31,7 +31,9 @@ EXPORTED = (
     "monarch_fwd", "monarch_bwd", "monarch_bwd_workspace_bytes", "monarch_fwd_traced",
     "monarch_bwd_traced", "monarch_describe", "monarch_status_string", "monarch_abi_version",
     "monarch_project", "monarch_linear_mid", "monarch_fwd_ex", "monarch_bwd_ex",
-    "monarch_bwd_ex_workspace_bytes", "monarch_describe_ex",
+    "monarch_bwd_ex_workspace_bytes", "monarch_describe_ex", "monarch_hyper_saved_elems",
+    "monarch_hyper_fwd", "monarch_hyper_bwd_workspace_bytes", "monarch_hyper_bwd",
+    "monarch_hyper_describe",
 )
 
 _lib = None
@@ -86,6 +88,18 @@ def load_library():
     lib.monarch_describe_ex.argtypes = [c_int] + [i64] * 6 + [c_int, c_int, c_int,
                                                              ctypes.c_char_p, sz]
     lib.monarch_describe_ex.restype = c_int
+    pp, pi64 = ctypes.POINTER(vp), ctypes.POINTER(i64)
+    lib.monarch_hyper_saved_elems.argtypes = [c_int, pi64, i64]
+    lib.monarch_hyper_saved_elems.restype = sz
+    lib.monarch_hyper_fwd.argtypes = [vp, pp, vp, vp, c_int, pi64, i64, c_int, vp] + ev
+    lib.monarch_hyper_fwd.restype = c_int
+    lib.monarch_hyper_bwd_workspace_bytes.argtypes = [c_int, pi64, i64, c_int]
+    lib.monarch_hyper_bwd_workspace_bytes.restype = sz
+    lib.monarch_hyper_bwd.argtypes = [vp, vp, pp, vp, vp, pp, vp, sz, c_int, pi64, i64, c_int,
+                                      vp] + ev
+    lib.monarch_hyper_bwd.restype = c_int
+    lib.monarch_hyper_describe.argtypes = [c_int, c_int, pi64, i64, c_int, ctypes.c_char_p, sz]
+    lib.monarch_hyper_describe.restype = c_int
     _lib = lib
     return lib
 
@@ -230,6 +244,52 @@ def monarch_describe_ex(direction, in_features, out_features, mid_features, nblo
     buf = ctypes.create_string_buffer(1024)
     n = lib.monarch_describe_ex(direction, in_features, out_features, mid_features, nblocks1,
                                 nblocks2, batch, dtype, act, 1 if with_bias else 0, buf, len(buf))
+    if n < 0:
+        raise MonarchError(n, monarch_status_string(n))
+    return buf.value.decode().split(";") if n else []
+
+
+def _dims(dims):
+    return (ctypes.c_int64 * len(dims))(*[int(d) for d in dims]), len(dims)
+
+
+def _ptrs(ts):
+    return (ctypes.c_void_p * len(ts))(*[_ptr(t) for t in ts])
+
+
+def monarch_hyper_saved_elems(dims, batch) -> int:
+    d, k = _dims(dims)
+    return load_library().monarch_hyper_saved_elems(k, d, batch)
+
+
+def monarch_hyper_fwd(x, ws, y, saved, dims, batch, dtype, stream=None, events=None) -> None:
+    lib = load_library()
+    d, k = _dims(dims)
+    arr, n = _events(events)
+    _check(lib.monarch_hyper_fwd(_ptr(x), _ptrs(ws), _ptr(y), _ptr(saved), k, d, batch, dtype,
+                                 _stream(stream), arr, n))
+
+
+def monarch_hyper_bwd_workspace_bytes(dims, batch, dtype) -> int:
+    d, k = _dims(dims)
+    return load_library().monarch_hyper_bwd_workspace_bytes(k, d, batch, dtype)
+
+
+def monarch_hyper_bwd(dy, x, ws, saved, dx, dws, workspace, workspace_bytes, dims, batch, dtype,
+                      stream=None, events=None) -> None:
+    lib = load_library()
+    d, k = _dims(dims)
+    arr, n = _events(events)
+    _check(lib.monarch_hyper_bwd(_ptr(dy), _ptr(x), _ptrs(ws), _ptr(saved), _ptr(dx), _ptrs(dws),
+                                 _ptr(workspace), workspace_bytes, k, d, batch, dtype,
+                                 _stream(stream), arr, n))
+
+
+def monarch_hyper_describe(direction, dims, batch, dtype):
+    lib = load_library()
+    d, k = _dims(dims)
+    buf = ctypes.create_string_buffer(1024)
+    n = lib.monarch_hyper_describe(direction, k, d, batch, dtype, buf, len(buf))
     if n < 0:
         raise MonarchError(n, monarch_status_string(n))
     return buf.value.decode().split(";") if n else []

@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include "hyper.h"
 #include "kernels.h"
 #include "monarch.h"
 #include "plan.h"
@@ -99,6 +100,35 @@ int bwd_impl(const Problem& pr, const void* dy, const void* x, const void* w1, c
   b.ws = ws;
   Plan plan = plan_bwd(pr);
   return run_plan(plan, pr, b, static_cast<hipStream_t>(stream), events, n_events);
+}
+
+int run_hyper(const HyperStep* steps, int n, bool bf16, hipStream_t s, void* const* events,
+              int n_events) {
+  Tracer tr{events, n_events, 0, s};
+  for (int i = 0; i < n; ++i) {
+    int st = record_hip(tr.mark());
+    if (st) return st;
+    st = record_hip(hyper_launch(steps[i], bf16, s));
+    if (st) return st;
+  }
+  return record_hip(tr.mark());
+}
+
+int write_names(const char* const* names, int n, char* buf, size_t buf_len) {
+  if (buf && buf_len) {
+    buf[0] = '\0';
+    size_t used = 0;
+    for (int i = 0; i < n; ++i) {
+      int w = snprintf(buf + used, buf_len - used, "%s%s", i ? ";" : "", names[i]);
+      if (w < 0) break;
+      used += static_cast<size_t>(w);
+      if (used >= buf_len) {
+        buf[buf_len - 1] = '\0';
+        break;
+      }
+    }
+  }
+  return n;
 }
 
 int describe_plan(const Problem& pr, int direction, char* buf, size_t buf_len) {
@@ -257,6 +287,90 @@ int monarch_describe(int direction, int64_t in_features, int64_t out_features, i
   int st = make_problem(in_features, out_features, nblocks1, nblocks2, batch, dtype, act, &pr);
   if (st) return st;
   return describe_plan(pr, direction, buf, buf_len);
+}
+
+size_t monarch_hyper_saved_elems(int ndims, const int64_t* dims, int64_t batch) {
+  HyperProblem hp;
+  if (make_hyper(ndims, dims, batch, MONARCH_F32, &hp)) return 0;
+  return static_cast<size_t>(hp.k - 1) * hp.batch * hp.N;
+}
+
+int monarch_hyper_fwd(const void* x, const void* const* w, void* y, void* saved, int ndims,
+                      const int64_t* dims, int64_t batch, int dtype, void* stream,
+                      void* const* events, int n_events) {
+  HyperProblem hp;
+  int st = make_hyper(ndims, dims, batch, dtype, &hp);
+  if (st) return st;
+  if (!w) return MONARCH_ERR_NULL;
+  HyperBuffers b;
+  for (int j = 0; j < hp.k; ++j) {
+    if (!w[j]) return MONARCH_ERR_NULL;
+    if (misaligned(w[j])) return MONARCH_ERR_ALIGN;
+    b.w[j] = w[j];
+  }
+  if (batch > 0 && (!x || !y || (hp.k > 1 && !saved))) return MONARCH_ERR_NULL;
+  if (misaligned(x) || misaligned(y) || misaligned(saved)) return MONARCH_ERR_ALIGN;
+  if (batch == 0) return MONARCH_OK;
+  b.x = x;
+  b.y = y;
+  b.saved = saved;
+  HyperStep steps[kHyperMaxSteps];
+  const int n = hyper_plan_fwd(hp, b, steps);
+  return run_hyper(steps, n, dtype == MONARCH_BF16, static_cast<hipStream_t>(stream), events,
+                   n_events);
+}
+
+size_t monarch_hyper_bwd_workspace_bytes(int ndims, const int64_t* dims, int64_t batch,
+                                         int dtype) {
+  HyperProblem hp;
+  if (make_hyper(ndims, dims, batch, dtype, &hp)) return 0;
+  return hp.ws_total;
+}
+
+int monarch_hyper_bwd(const void* dy, const void* x, const void* const* w, const void* saved,
+                      void* dx, void* const* dw, void* workspace, size_t workspace_bytes,
+                      int ndims, const int64_t* dims, int64_t batch, int dtype, void* stream,
+                      void* const* events, int n_events) {
+  HyperProblem hp;
+  int st = make_hyper(ndims, dims, batch, dtype, &hp);
+  if (st) return st;
+  if (!w || !dw) return MONARCH_ERR_NULL;
+  HyperBuffers b;
+  for (int j = 0; j < hp.k; ++j) {
+    if (!w[j] || !dw[j]) return MONARCH_ERR_NULL;
+    if (misaligned(w[j]) || misaligned(dw[j])) return MONARCH_ERR_ALIGN;
+    b.w[j] = w[j];
+    b.dw[j] = dw[j];
+  }
+  if (batch > 0 && (!dy || !x || !dx || (hp.k > 1 && !saved))) return MONARCH_ERR_NULL;
+  if (hp.ws_total > 0 && !workspace) return MONARCH_ERR_NULL;
+  if (misaligned(dy) || misaligned(x) || misaligned(saved) || misaligned(dx) ||
+      misaligned(workspace))
+    return MONARCH_ERR_ALIGN;
+  if (workspace_bytes < hp.ws_total) return MONARCH_ERR_WORKSPACE;
+  b.dy = dy;
+  b.x = x;
+  b.saved_in = saved;
+  b.dx = dx;
+  b.ws = workspace;
+  HyperStep steps[kHyperMaxSteps];
+  const int n = hyper_plan_bwd(hp, b, steps);
+  return run_hyper(steps, n, dtype == MONARCH_BF16, static_cast<hipStream_t>(stream), events,
+                   n_events);
+}
+
+int monarch_hyper_describe(int direction, int ndims, const int64_t* dims, int64_t batch,
+                           int dtype, char* buf, size_t buf_len) {
+  HyperProblem hp;
+  int st = make_hyper(ndims, dims, batch, dtype, &hp);
+  if (st) return st;
+  if (direction != 0 && direction != 1) return MONARCH_ERR_DTYPE;
+  HyperBuffers b;
+  HyperStep steps[kHyperMaxSteps];
+  const int n = direction == 0 ? hyper_plan_fwd(hp, b, steps) : hyper_plan_bwd(hp, b, steps);
+  const char* names[kHyperMaxSteps];
+  for (int i = 0; i < n; ++i) names[i] = steps[i].name;
+  return write_names(names, n, buf, buf_len);
 }
 
 const char* monarch_status_string(int status) {

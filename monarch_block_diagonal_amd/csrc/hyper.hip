@@ -1,0 +1,226 @@
+// k-factor ("hypercube") Monarch layer: planning of its rounds as batched
+// GEMMs (scatterbrain issues page, "hypercube" thread: the N units form a
+// lattice [n_1, ..., n_k]; round j multiplies along axis j with one matrix per
+// index of the other axes, rounds in axis order).
+//
+// Every round is one launch of the tiled GEMM (tiled.hip) with one block per
+// fiber of its axis. Layouts: L_j denotes the lattice with axis j moved to
+// the end (the other axes in order), so a fiber of round j is a contiguous
+// run of n_j elements and the fiber index equals the weight index; L_{k-1} is
+// the natural row-major layout. Round j reads its input in L_j (round 0 reads
+// the caller's natural x with stride N/n_0) and writes its output in L_{j+1}
+// through a mixed-radix block offset; the last round writes y in natural
+// order. The forward keeps each round's output (k-1 saved tensors). The
+// backward walks the rounds in reverse: the weight gradient of round j sums
+// g_{j+1}[fiber]ᵀ · input_j[fiber] over the batch (split in chunks, summed in
+// a fixed order), and the data gradient g_j = F_jᵀ g_{j+1} is written in
+// L_{j-1} (round 0: natural order, i.e. dx).
+#include "hyper.h"
+#include "monarch.h"
+
+namespace monarch {
+namespace {
+
+constexpr int64_t kLimit = int64_t(1) << 31;
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+// batch split of a weight-gradient GEMM with nblk blocks of n x n: about
+// 2048 tiles of 64 x 64 in flight, chunks of at least 128 rows, multiples of
+// kSplitK
+void splits_for(int64_t nblk, int64_t n, int64_t K, int64_t* splits, int64_t* chunk) {
+  if (K <= 0) {
+    *splits = 1;
+    *chunk = kSplitK;
+    return;
+  }
+  const int64_t t = (n + 63) / 64;
+  const int64_t base = nblk * t * t;
+  int64_t s = (2048 + base - 1) / base;
+  const int64_t smax = (K + 127) / 128;
+  if (s > smax) s = smax;
+  if (s > 64) s = 64;
+  if (s < 1) s = 1;
+  int64_t c = (K + s - 1) / s;
+  c = (c + kSplitK - 1) / kSplitK * kSplitK;
+  *chunk = c;
+  *splits = (K + c - 1) / c;
+}
+
+int64_t prod(const int64_t* d, int lo, int hi) {
+  int64_t p = 1;
+  for (int i = lo; i < hi; ++i) p *= d[i];
+  return p;
+}
+
+// output of forward round j (j < k-1) in layout L_{j+1}
+void set_out_next(GemmArgs& a, const HyperProblem& hp, int j) {
+  const int64_t R = prod(hp.dims, j + 2, hp.k), nn = hp.dims[j + 1];
+  a.cb_r0 = R, a.cb_r1 = nn;
+  a.cb_s0 = nn, a.cb_s1 = 1, a.cb_s2 = hp.dims[j] * nn * R;
+  a.c_sj = R * nn;
+}
+
+// data gradient of round j (j > 0) in layout L_{j-1}
+void set_out_prev(GemmArgs& a, const HyperProblem& hp, int j) {
+  const int64_t R = prod(hp.dims, j + 1, hp.k), np = hp.dims[j - 1];
+  a.cb_r0 = R, a.cb_r1 = np;
+  a.cb_s0 = np, a.cb_s1 = 1, a.cb_s2 = hp.dims[j] * R * np;
+  a.c_sj = R * np;
+}
+
+}  // namespace
+
+int make_hyper(int ndims, const int64_t* dims, int64_t batch, int dtype, HyperProblem* hp) {
+  if (dtype != MONARCH_F32 && dtype != MONARCH_BF16) return MONARCH_ERR_DTYPE;
+  if (ndims < 1 || ndims > kHyperMaxDims || !dims || batch < 0 || batch >= kLimit)
+    return MONARCH_ERR_SHAPE;
+  HyperProblem p;
+  p.k = ndims;
+  int64_t n = 1;
+  for (int i = 0; i < ndims; ++i) {
+    if (dims[i] <= 0 || dims[i] >= kLimit) return MONARCH_ERR_SHAPE;
+    p.dims[i] = dims[i];
+    n *= dims[i];
+    if (n >= kLimit) return MONARCH_ERR_SHAPE;
+  }
+  p.N = n;
+  p.batch = batch;
+  p.dtype = dtype;
+  p.esize = dtype == MONARCH_BF16 ? 2 : 4;
+  size_t off = 0;
+  if (batch > 0) {
+    for (int g = 0; g < 2; ++g) {
+      p.ws_g[g] = off;
+      off = align256(off + static_cast<size_t>(batch) * n * p.esize);
+    }
+    for (int j = 0; j < ndims; ++j) {
+      const int64_t nj = p.dims[j];
+      splits_for(n / nj, nj, batch, &p.splits[j], &p.chunk[j]);
+      p.ws_part[j] = off;
+      off = align256(off + static_cast<size_t>(p.splits[j]) * (n / nj) * nj * nj * 4);
+    }
+  }
+  p.ws_total = off;
+  *hp = p;
+  return MONARCH_OK;
+}
+
+int hyper_plan_fwd(const HyperProblem& hp, const HyperBuffers& b, HyperStep* steps) {
+  if (hp.batch == 0) return 0;
+  const int k = hp.k;
+  const int64_t BN = hp.batch * hp.N;
+  const char* bytes_saved = static_cast<const char*>(b.saved);
+  for (int j = 0; j < k; ++j) {
+    const int64_t n = hp.dims[j];
+    HyperStep& st = steps[j];
+    st.kind = HYPER_GEMM;
+    st.name = "hyper_round_fwd";
+    GemmArgs& a = st.g;
+    if (j == 0) {
+      a.A = b.x;
+      a.a_sb = 1, a.a_sk = prod(hp.dims, 1, k);       // natural layout: stride N/n_0
+    } else {
+      a.A = bytes_saved + (j - 1) * BN * hp.esize;
+      a.a_sb = n, a.a_sk = 1;                          // L_j
+    }
+    a.a_si = hp.N;
+    a.B = b.w[j];
+    a.b_sb = n * n, a.b_sk = 1, a.b_sj = n;
+    a.c_si = hp.N;
+    if (j == k - 1) {
+      a.C = b.y;
+      a.c_sb = n, a.c_sj = 1;                          // natural = L_{k-1}
+    } else {
+      a.C = static_cast<char*>(b.saved) + j * BN * hp.esize;
+      set_out_next(a, hp, j);
+    }
+    a.M = hp.batch, a.N = n, a.K = n, a.nblk = hp.N / n;
+  }
+  return k;
+}
+
+int hyper_plan_bwd(const HyperProblem& hp, const HyperBuffers& b, HyperStep* steps) {
+  const int k = hp.k;
+  int ns = 0;
+  if (hp.batch == 0) {
+    for (int j = 0; j < k; ++j) {
+      HyperStep& st = steps[ns++];
+      st.kind = HYPER_ZERO;
+      st.name = "zero_dw";
+      st.zero_ptr = b.dw[j];
+      st.zero_bytes = static_cast<size_t>(hp.N) * hp.dims[j] * hp.esize;
+    }
+    return ns;
+  }
+  const int64_t BN = hp.batch * hp.N;
+  char* ws = static_cast<char*>(b.ws);
+  const char* saved = static_cast<const char*>(b.saved_in);
+  for (int j = k - 1; j >= 0; --j) {
+    const int64_t n = hp.dims[j], nf = hp.N / n;
+    // gradient w.r.t. round j's output, in L_j
+    const void* g = j == k - 1 ? b.dy : ws + hp.ws_g[(k - 2 - j) & 1];
+    {
+      HyperStep& st = steps[ns++];
+      st.kind = HYPER_GEMM;
+      st.name = "hyper_round_bwd_weight";
+      GemmArgs& a = st.g;
+      a.A = g;
+      a.a_sb = n, a.a_si = 1, a.a_sk = hp.N;
+      if (j == 0) {
+        a.B = b.x;
+        a.b_sb = 1, a.b_sk = hp.N, a.b_sj = prod(hp.dims, 1, k);
+      } else {
+        a.B = saved + (j - 1) * BN * hp.esize;
+        a.b_sb = n, a.b_sk = hp.N, a.b_sj = 1;
+      }
+      a.partial = reinterpret_cast<float*>(ws + hp.ws_part[j]);
+      a.splits = hp.splits[j], a.k_chunk = hp.chunk[j];
+      a.M = n, a.N = n, a.K = hp.batch, a.nblk = nf;
+    }
+    {
+      HyperStep& st = steps[ns++];
+      st.kind = HYPER_GEMM;
+      st.name = "hyper_round_bwd_data";
+      GemmArgs& a = st.g;
+      a.A = g;
+      a.a_sb = n, a.a_si = hp.N, a.a_sk = 1;
+      a.B = b.w[j];
+      a.b_sb = n * n, a.b_sk = n, a.b_sj = 1;
+      a.c_si = hp.N;
+      if (j == 0) {
+        a.C = b.dx;
+        a.c_sb = 1, a.c_sj = prod(hp.dims, 1, k);    // natural layout
+      } else {
+        a.C = ws + hp.ws_g[(k - 1 - j) & 1];
+        set_out_prev(a, hp, j);
+      }
+      a.M = hp.batch, a.N = n, a.K = n, a.nblk = nf;
+    }
+  }
+  // fixed-order sums of the weight-gradient chunks, three rounds per launch
+  for (int j0 = 0; j0 < k; j0 += 3) {
+    HyperStep& st = steps[ns++];
+    st.kind = HYPER_REDUCE;
+    st.name = "reduce_dw";
+    for (int i = 0; i < 3 && j0 + i < k; ++i) {
+      const int j = j0 + i;
+      st.r[i].partial = reinterpret_cast<const float*>(ws + hp.ws_part[j]);
+      st.r[i].out = b.dw[j];
+      st.r[i].n = hp.N * hp.dims[j];
+      st.r[i].splits = hp.splits[j];
+    }
+  }
+  return ns;
+}
+
+hipError_t hyper_launch(const HyperStep& st, bool bf16, hipStream_t s) {
+  switch (st.kind) {
+    case HYPER_GEMM: return launch_gemm(st.g, bf16, s);
+    case HYPER_REDUCE: return launch_reduce_partials(st.r[0], st.r[1], st.r[2], bf16, s);
+    case HYPER_ZERO: return launch_zero(st.zero_ptr, st.zero_bytes, s);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace monarch

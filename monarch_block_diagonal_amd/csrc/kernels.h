@@ -38,6 +38,11 @@ struct GemmArgs {
   // Optional bias (I/O type) added before `relu`, indexed by the row-relative
   // C offset.
   const void* bias = nullptr;
+  // Optional mixed-radix block offset of C (cb_r0 > 0): block blk splits as
+  // d0 = blk % cb_r0, d1 = (blk / cb_r0) % cb_r1, d2 = blk / (cb_r0*cb_r1)
+  // and its entries sit at d0*cb_s0 + d1*cb_s1 + d2*cb_s2 in place of
+  // blk*c_sb (a lattice axis moved between layouts).
+  int64_t cb_r0 = 0, cb_r1 = 1, cb_s0 = 0, cb_s1 = 0, cb_s2 = 0;
   int64_t M = 0, N = 0, K = 0;
   int64_t nblk = 1;
   int64_t splits = 1;

@@ -316,10 +316,15 @@ __global__ __launch_bounds__(TT) void tiled_gemm_kernel(GemmArgs p, int64_t m_ti
   }
 
   // 16x16 result layout: lane holds rows 4*(lane/16)+v, column lane%16
+  int64_t cblk = blk * p.c_sb;
+  if (p.cb_r0 > 0) {
+    const int64_t d0 = blk % p.cb_r0, t1 = blk / p.cb_r0;
+    cblk = d0 * p.cb_s0 + (t1 % p.cb_r1) * p.cb_s1 + (t1 / p.cb_r1) * p.cb_s2;
+  }
 #pragma unroll
   for (int ni = 0; ni < FN; ++ni) {
     const int64_t j = j0 + (wn * FN + ni) * 16 + l15;
-    const int64_t cpos = blk * p.c_sb + col_off(j, p.nsplit, p.c_sj_hi, p.c_sj);   // in-row offset
+    const int64_t cpos = cblk + col_off(j, p.nsplit, p.c_sj_hi, p.c_sj);   // in-row offset
 #pragma unroll
     for (int mi = 0; mi < FM; ++mi)
 #pragma unroll

@@ -204,3 +204,28 @@ class MonarchLinear(torch.nn.Module):
         y = MonarchLinearExFunction.apply(x.reshape(-1, shape[-1]), self.w1, self.w2, self.bias,
                                           self.out_features, self.act)
         return y.reshape(*shape[:-1], self.out_features)
+
+
+def hyper_forward(x, ws, dims, stream=None):
+    """k-factor (hypercube) layer: x [batch, N], ws[j] [N/n_j, n_j, n_j];
+    returns (y, saved)."""
+    _check(x, *ws)
+    b, n = x.shape
+    saved = torch.empty((max(B.monarch_hyper_saved_elems(dims, b), 1),), dtype=x.dtype,
+                        device=x.device)
+    y = torch.empty_like(x)
+    B.monarch_hyper_fwd(x, ws, y, saved, dims, b, dtype_code(x), stream)
+    return y, saved
+
+
+def hyper_backward(dy, x, ws, saved, dims, stream=None):
+    """(dx, [dw_j]) of the hypercube layer."""
+    _check(dy, x, *ws)
+    b = x.shape[0]
+    code = dtype_code(x)
+    dx = torch.empty_like(x)
+    dws = [torch.empty_like(w) for w in ws]
+    need = B.monarch_hyper_bwd_workspace_bytes(dims, b, code)
+    ws_buf = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    B.monarch_hyper_bwd(dy, x, ws, saved, dx, dws, ws_buf, need, dims, b, code, stream)
+    return dx, dws

@@ -117,3 +117,35 @@ def backward(dy, x, ws, dims):
         grads[j] = dw
         g = g @ round_matrix(ws[j], dims, j)
     return g, grads
+
+
+def forward_fibers(x, ws, dims, keep: bool = False):
+    """The same rounds without dense N x N matrices: gather every fiber of
+    axis j, multiply by its matrix, scatter back (for large lattices)."""
+    dims = check_dims(dims)
+    h = np.asarray(x, dtype=np.float64)
+    acts = [h]
+    for j, w in enumerate(ws):
+        pos = fiber_positions(dims, j)
+        out = np.empty_like(h)
+        out[:, pos] = np.einsum("bfi,foi->bfo", h[:, pos], np.asarray(w, dtype=np.float64))
+        h = out
+        acts.append(h)
+    return (h, acts) if keep else h
+
+
+def backward_fibers(dy, x, ws, dims):
+    """backward() evaluated fiber by fiber (no dense matrices)."""
+    dims = check_dims(dims)
+    _, acts = forward_fibers(x, ws, dims, keep=True)
+    g = np.asarray(dy, dtype=np.float64)
+    grads = [None] * len(dims)
+    for j in range(len(dims) - 1, -1, -1):
+        pos = fiber_positions(dims, j)
+        w = np.asarray(ws[j], dtype=np.float64)
+        gf, xf = g[:, pos], acts[j][:, pos]
+        grads[j] = np.einsum("bfo,bfi->foi", gf, xf)
+        gin = np.empty_like(g)
+        gin[:, pos] = np.einsum("bfo,foi->bfi", gf, w)
+        g = gin
+    return g, grads

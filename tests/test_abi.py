@@ -1,6 +1,7 @@
 """Host-side checks of the C ABI: the library loads, exports every symbol the
 header declares, and rejects bad arguments before any HIP call (these run
 without a GPU; no call here reaches a kernel launch)."""
+import ctypes
 import os
 import re
 
@@ -241,3 +242,42 @@ def test_ex_workspace_and_plan():
     assert all(n.startswith("generic_") for n in names)
     assert M.monarch_bwd_ex_workspace_bytes(16, 16, 16, 4, 4, 8, B.F32) == \
         M.monarch_bwd_workspace_bytes(16, 16, 4, 4, 8, B.F32)
+
+
+# ---------------------------------------------------------------------------
+# k-factor (hypercube) layer
+
+def test_hyper_sizes_and_plan():
+    dims = (16, 24, 32)
+    assert M.monarch_hyper_saved_elems(dims, 10) == 2 * 10 * 12288
+    assert M.monarch_hyper_saved_elems((64,), 10) == 0
+    assert M.monarch_hyper_describe(0, dims, 10, B.BF16) == ["hyper_round_fwd"] * 3
+    names = M.monarch_hyper_describe(1, dims, 10, B.BF16)
+    assert names == ["hyper_round_bwd_weight", "hyper_round_bwd_data"] * 3 + ["reduce_dw"]
+    assert M.monarch_hyper_describe(1, (2, 2, 2, 2), 10, B.F32)[-2:] == ["reduce_dw", "reduce_dw"]
+    assert M.monarch_hyper_describe(1, dims, 0, B.BF16) == ["zero_dw"] * 3
+    assert M.monarch_hyper_bwd_workspace_bytes(dims, 1000, B.BF16) > 0
+
+
+@pytest.mark.parametrize("dims", [(), (2, 2, 2, 2, 2), (0, 4), (4, -1), (1 << 16, 1 << 16)])
+def test_hyper_bad_lattice(dims):
+    lib = M.load_library()
+    d = (ctypes.c_int64 * max(len(dims), 1))(*dims)
+    w = (ctypes.c_void_p * 5)(*([A] * 5))
+    assert lib.monarch_hyper_fwd(A, w, A2, A2, len(dims), d, 4, B.F32, None, None, 0) == \
+        B.MONARCH_ERR_SHAPE
+
+
+def test_hyper_pointer_checks():
+    lib = M.load_library()
+    d = (ctypes.c_int64 * 2)(4, 8)
+    w = (ctypes.c_void_p * 2)(A, A)
+    wnull = (ctypes.c_void_p * 2)(A, None)
+    wmis = (ctypes.c_void_p * 2)(A, MIS)
+    assert lib.monarch_hyper_fwd(A, wnull, A2, A2, 2, d, 4, B.F32, None, None, 0) == B.MONARCH_ERR_NULL
+    assert lib.monarch_hyper_fwd(A, wmis, A2, A2, 2, d, 4, B.F32, None, None, 0) == B.MONARCH_ERR_ALIGN
+    assert lib.monarch_hyper_fwd(A, w, A2, None, 2, d, 4, B.F32, None, None, 0) == B.MONARCH_ERR_NULL
+    assert lib.monarch_hyper_fwd(A, w, A2, A2, 2, d, 4, 7, None, None, 0) == B.MONARCH_ERR_DTYPE
+    dw = (ctypes.c_void_p * 2)(A2, A2)
+    assert lib.monarch_hyper_bwd(A, A, w, A, A2, dw, A2, 0, 2, d, 4, B.F32, None, None, 0) == \
+        B.MONARCH_ERR_WORKSPACE

@@ -1,0 +1,86 @@
+"""GPU parity of the k-factor (hypercube) layer against the fp64 oracle.
+Bars: relative Frobenius error <= 1e-5 (fp32) and <= 2e-2 (bf16) for y, dx
+and every round's weight gradient; bit-exact for identity weights."""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import monarch_hypercube as H
+from oracle.monarch_oracle import rel_frobenius
+from monarch_block_diagonal_amd import synthetic as S
+
+pytestmark = pytest.mark.gpu
+torch = pytest.importorskip("torch")
+
+TOL = {"f32": 1e-5, "bf16": 2e-2}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def api():
+    if not torch.cuda.is_available():
+        pytest.fail("a GPU is required for the gpu-marked tests")
+    from monarch_block_diagonal_amd import torch_api
+    return torch_api
+
+
+def dev(a, dtype):
+    t = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).to("cuda:0")
+    return t if dtype == "f32" else t.to(torch.bfloat16)
+
+
+def host(t):
+    return t.detach().float().cpu().numpy().astype(np.float64)
+
+
+def check(api, dims, batch, dtype, seed=8100):
+    n = int(np.prod(dims))
+    say(f"[hyper] dims={dims} batch={batch} {dtype}")
+    ws = [S.draw(seed + 1 + j, s, "normal", 1.0 / s[2], dtype)
+          for j, s in enumerate(H.weight_shapes(dims))]
+    x = S.draw(seed, (batch, n), "normal", 1.0, dtype)
+    dy = S.draw(seed + 9, (batch, n), "normal", 1.0, dtype)
+    X, DY, W = dev(x, dtype), dev(dy, dtype), [dev(w, dtype) for w in ws]
+    y, saved = api.hyper_forward(X, W, dims)
+    dx, dws = api.hyper_backward(DY, X, W, saved, dims)
+    torch.cuda.synchronize()
+    y_ref = H.forward_fibers(x, ws, dims)
+    rx, rws = H.backward_fibers(dy, x, ws, dims)
+    errs = {"y": rel_frobenius(host(y), y_ref), "dx": rel_frobenius(host(dx), rx)}
+    for j, (g, r) in enumerate(zip(dws, rws)):
+        errs[f"dw{j + 1}"] = rel_frobenius(host(g), r)
+    say(f"[hyper]   errors {errs}")
+    for k, e in errs.items():
+        assert e <= TOL[dtype], (k, e)
+
+
+@pytest.mark.parametrize("dims,batch,dtype", [
+    ((2, 3, 4), 5, "f32"), ((4, 8), 33, "bf16"), ((8, 4, 2), 40, "f32"),
+    ((16, 2, 2, 3), 7, "bf16"), ((6,), 9, "f32"), ((32, 16), 300, "bf16"),
+    ((16, 16, 16), 130, "f32"), ((5, 7, 3), 257, "f32"),
+])
+def test_hyper_small(api, dims, batch, dtype):
+    check(api, dims, batch, dtype)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_hyper_page_lattice(api, dtype):
+    """The page's 12288-unit lattice 16 x 24 x 32."""
+    check(api, (16, 24, 32), 256, dtype, seed=8200)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_hyper_identity_is_exact(api, dtype):
+    dims = (8, 4, 6)
+    n = int(np.prod(dims))
+    ws = [np.broadcast_to(np.eye(d), s).copy() for d, s in zip(dims, H.weight_shapes(dims))]
+    x = S.draw(8300, (70, n), "normal", 1.0, dtype)
+    X = dev(x, dtype)
+    y, saved = api.hyper_forward(X, [dev(w, dtype) for w in ws], dims)
+    torch.cuda.synchronize()
+    assert torch.equal(y, X)

@@ -155,3 +155,18 @@ def test_round_order_matters():
     M = H.hyper_matrix(ws, dims)
     Fs = [H.round_matrix(w, dims, j) for j, w in enumerate(ws)]
     assert not np.allclose(M, Fs[0] @ Fs[1] @ Fs[2])
+
+
+@pytest.mark.parametrize("dims", DIMS)
+def test_fiber_form_matches_the_dense_form(dims):
+    rng = np.random.default_rng(7)
+    ws = rand_ws(rng, dims)
+    n = int(np.prod(dims))
+    x = rng.standard_normal((3, n))
+    dy = rng.standard_normal((3, n))
+    assert np.allclose(H.forward_fibers(x, ws, dims), H.forward(x, ws, dims), atol=1e-12)
+    gx, gws = H.backward_fibers(dy, x, ws, dims)
+    rx, rws = H.backward(dy, x, ws, dims)
+    assert np.allclose(gx, rx, atol=1e-12)
+    for a, b in zip(gws, rws):
+        assert np.allclose(a, b, atol=1e-12)
