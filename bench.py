@@ -220,6 +220,123 @@ def bench_project(args) -> int:
     return 0
 
 
+def bench_hyper(args) -> int:
+    """k-factor (hypercube) layer: forward + backward over a lattice (default
+    the page's 16 x 24 x 32 = 12288 units) at `--rows` tokens, inputs resident
+    in HBM; one JSON line."""
+    import numpy as np
+    import torch
+    import monarch_block_diagonal_amd as M
+    from monarch_block_diagonal_amd import synthetic as S
+    dims = tuple(int(v) for v in args.dims.split("x"))
+    N = int(np.prod(dims))
+    B = args.rows
+    bf16 = args.dtype == "bf16"
+    tdt = torch.bfloat16 if bf16 else torch.float32
+    code = M.BF16 if bf16 else M.F32
+    e = 2 if bf16 else 4
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    params = N * sum(dims)
+    log(f"hypercube {dims} (N={N}, {params} params), {B} rows, {args.dtype}")
+    g = torch.Generator(device=dev)
+    g.manual_seed(S.seed_for(5, S.TID_X))
+    x = torch.randn((B, N), generator=g, device=dev).to(tdt)
+    dy = torch.randn((B, N), generator=g, device=dev).to(tdt)
+    ws = [torch.randn((N // d, d, d), generator=g, device=dev).mul_(d ** -0.5).to(tdt) for d in dims]
+    y = torch.empty_like(x)
+    dx = torch.empty_like(x)
+    dws = [torch.empty_like(w) for w in ws]
+    saved = torch.empty((max(M.monarch_hyper_saved_elems(dims, B), 1),), dtype=tdt, device=dev)
+    need = M.monarch_hyper_bwd_workspace_bytes(dims, B, code)
+    wsb = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    fn = M.monarch_hyper_describe(0, dims, B, code)
+    bn = M.monarch_hyper_describe(1, dims, B, code)
+    stream = torch.cuda.current_stream()
+
+    def step(evf=None, evb=None):
+        M.monarch_hyper_fwd(x, ws, y, saved, dims, B, code, stream, events=evf)
+        M.monarch_hyper_bwd(dy, x, ws, saved, dx, dws, wsb, need, dims, B, code, stream, events=evb)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fn) + 1)] for _ in range(K)]
+    evb = [[torch.cuda.Event(enable_timing=True) for _ in range(len(bn) + 1)] for _ in range(K)]
+    t0 = time.perf_counter()
+    for k in range(K):
+        step(evf[k], evb[k])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / K
+    step_ms = sorted(evf[k][0].elapsed_time(evb[k][-1]) for k in range(K))
+    kern = {}
+    for names, evs, pre in ((fn, evf, "fwd"), (bn, evb, "bwd")):
+        for i, nm in enumerate(names):
+            key = f"{pre}{i}:{nm}"
+            kern[key] = sum(ev[i].elapsed_time(ev[i + 1]) for ev in evs) / K
+    flops = 6.0 * B * params
+    value = flops / (ms * 1e-3) / 1e12
+    # every round reads its input and writes its output once (fwd), the
+    # backward reads two tensors per weight product and one + writes one per
+    # data product; weights and gradients once
+    act = e * B * N
+    bytes_step = len(dims) * 2 * act + len(dims) * (2 * act + 2 * act) + 3 * e * params
+    dom = max(kern, key=kern.get)
+    dom_bytes = 2.0 * act + e * params / len(dims)
+    achieved = dom_bytes / (kern[dom] * 1e-3) / 1e9
+    dense = None
+    if not args.no_dense:
+        Wd = torch.randn((N, N), device=dev).mul_(N ** -0.5).to(tdt)
+
+        def dense_step():
+            yd = x @ Wd.t()
+            return yd, dy @ Wd, dy.t() @ x
+        for _ in range(2):
+            dense_step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(3):
+            dense_step()
+        torch.cuda.synchronize()
+        dms = (time.perf_counter() - t1) * 1e3 / 3
+        dense = {"dtype": args.dtype, "ms_per_step": round(dms, 4),
+                 "tflops": round(6.0 * B * N * N / (dms * 1e-3) / 1e12, 1),
+                 "speedup_monarch_vs_dense": round(dms / ms, 3)}
+        del Wd
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import monarch_hypercube as H
+        rows = args.cpu_rows or 256
+        xs, dys = x[:rows].float().cpu().numpy(), dy[:rows].float().cpu().numpy()
+        wn = [w.float().cpu().numpy() for w in ws]
+        t1 = time.perf_counter()
+        H.forward_fibers(xs, wn, dims)
+        H.backward_fibers(dys, xs, wn, dims)
+        dt = time.perf_counter() - t1
+        cpu = {"value": round(6.0 * rows * params / dt / 1e12, 5), "unit": "TFLOP/s",
+               "cores": len(os.sched_getaffinity(0)), "kind": "oracle",
+               "sample": f"{rows} of {B} rows, fp64 fiber-by-fiber rounds, {dt:.2f} s",
+               "seconds": dt}
+    result = {
+        "metric": "hypercube Monarch fwd+bwd TFLOP/s", "value": round(value, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": args.dtype, "data": "synthetic (seeded, drawn on the device)",
+        "config": {"workload": f"hypercube_{args.dims}_rows{B}", "dims": list(dims), "N": N,
+                   "rows": B, "params": params},
+        "step_ms_p10_p50_p90": [round(step_ms[int(q * (K - 1))], 4) for q in (0.1, 0.5, 0.9)],
+        "step_hbm_frac": round(bytes_step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(achieved, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": None, "algorithmic_bytes": dom_bytes, "avg_ms": round(kern[dom], 4)},
+        "dense_baseline": dense, "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -232,9 +349,12 @@ def main() -> int:
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (read 1 GiB + write 1 GiB), the "
                          "reference for scaling HBM byte counters")
-    ap.add_argument("--op", choices=("step", "project"), default="step",
+    ap.add_argument("--op", choices=("step", "project", "hyper"), default="step",
                     help="step: forward + backward (default); project: dense -> Monarch "
-                         "projection of an n x n matrix")
+                         "projection of an n x n matrix; hyper: k-factor lattice layer")
+    ap.add_argument("--dims", default="16x24x32", help="lattice of --op hyper")
+    ap.add_argument("--rows", type=int, default=16384, help="tokens of --op hyper")
+    ap.add_argument("--dtype", choices=("bf16", "f32"), default="bf16", help="--op hyper dtype")
     ap.add_argument("--iters", type=int, default=32, help="power iterations (--op project)")
     args = ap.parse_args()
 
@@ -245,6 +365,8 @@ def main() -> int:
         return 2
     if args.op == "project":
         return bench_project(args)
+    if args.op == "hyper":
+        return bench_hyper(args)
 
     import numpy as np
     import torch

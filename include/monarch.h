@@ -219,9 +219,9 @@ int monarch_describe_ex(int direction, int64_t in_features, int64_t out_features
  *   w[j] [N/n_j, n_j, n_j], w[j][f][o, i] the weight from position i to o,
  *   f = the other axes' indices flattened row-major in axis order.
  * y = F_k ... F_1 x for every row (x, y [batch, N]). The forward also writes
- * the outputs of rounds 1..k-1 to `saved` (monarch_hyper_saved_elems
- * elements of the I/O dtype, a layout private to the library), which the
- * backward reads. w and dw are host arrays of ndims device pointers.
+ * what the backward reads to `saved` (monarch_hyper_saved_elems elements of
+ * the I/O dtype, k * batch * N for k >= 2: x and the outputs of rounds
+ * 1..k-1, in layouts private to the library). w and dw are host arrays of ndims device pointers.
  * dtype, streams, ownership, alignment and errors as for monarch_fwd
  * (a bad lattice gives MONARCH_ERR_SHAPE). */
 size_t monarch_hyper_saved_elems(int ndims, const int64_t* dims, int64_t batch);

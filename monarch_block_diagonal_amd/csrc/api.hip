@@ -292,7 +292,7 @@ int monarch_describe(int direction, int64_t in_features, int64_t out_features, i
 size_t monarch_hyper_saved_elems(int ndims, const int64_t* dims, int64_t batch) {
   HyperProblem hp;
   if (make_hyper(ndims, dims, batch, MONARCH_F32, &hp)) return 0;
-  return static_cast<size_t>(hp.k - 1) * hp.batch * hp.N;
+  return static_cast<size_t>(hyper_saved_elems(hp));
 }
 
 int monarch_hyper_fwd(const void* x, const void* const* w, void* y, void* saved, int ndims,

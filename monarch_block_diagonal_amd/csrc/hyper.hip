@@ -7,14 +7,15 @@
 // fiber of its axis. Layouts: L_j denotes the lattice with axis j moved to
 // the end (the other axes in order), so a fiber of round j is a contiguous
 // run of n_j elements and the fiber index equals the weight index; L_{k-1} is
-// the natural row-major layout. Round j reads its input in L_j (round 0 reads
-// the caller's natural x with stride N/n_0) and writes its output in L_{j+1}
-// through a mixed-radix block offset; the last round writes y in natural
-// order. The forward keeps each round's output (k-1 saved tensors). The
-// backward walks the rounds in reverse: the weight gradient of round j sums
-// g_{j+1}[fiber]ᵀ · input_j[fiber] over the batch (split in chunks, summed in
-// a fixed order), and the data gradient g_j = F_jᵀ g_{j+1} is written in
-// L_{j-1} (round 0: natural order, i.e. dx).
+// the natural row-major layout. The forward first transposes x into L_0 (each
+// row is an n_0 x N/n_0 matrix); round j reads its input in L_j and writes
+// its output in L_{j+1} through a mixed-radix block offset; the last round
+// writes y in natural order. It keeps x in L_0 and the outputs of rounds
+// 0..k-2 (k saved tensors). The backward walks the rounds in reverse: the
+// weight gradient of round j sums g_{j+1}[fiber]ᵀ · input_j[fiber] over the
+// batch (split in chunks, summed in a fixed order), and the data gradient
+// g_j = F_jᵀ g_{j+1} is written in L_{j-1}; g_0, in L_0, is transposed back
+// into dx. A one-dimensional lattice needs no transposes.
 #include "hyper.h"
 #include "monarch.h"
 
@@ -106,24 +107,30 @@ int make_hyper(int ndims, const int64_t* dims, int64_t batch, int dtype, HyperPr
   return MONARCH_OK;
 }
 
+int64_t hyper_saved_elems(const HyperProblem& hp) { return hp.k > 1 ? hp.k * hp.batch * hp.N : 0; }
+
 int hyper_plan_fwd(const HyperProblem& hp, const HyperBuffers& b, HyperStep* steps) {
   if (hp.batch == 0) return 0;
   const int k = hp.k;
   const int64_t BN = hp.batch * hp.N;
-  const char* bytes_saved = static_cast<const char*>(b.saved);
+  // saved slot s: slot 0 = x in L_0, slot j + 1 = output of round j
+  auto slot = [&](int sidx) { return static_cast<char*>(b.saved) + sidx * BN * hp.esize; };
+  int ns = 0;
+  if (k > 1) {
+    HyperStep& st = steps[ns++];
+    st.kind = HYPER_TRANSPOSE;
+    st.name = "hyper_transpose";
+    st.t_in = b.x, st.t_out = slot(0);
+    st.t_rows = hp.batch, st.t_R = hp.dims[0], st.t_C = hp.N / hp.dims[0];
+  }
   for (int j = 0; j < k; ++j) {
     const int64_t n = hp.dims[j];
-    HyperStep& st = steps[j];
+    HyperStep& st = steps[ns++];
     st.kind = HYPER_GEMM;
     st.name = "hyper_round_fwd";
     GemmArgs& a = st.g;
-    if (j == 0) {
-      a.A = b.x;
-      a.a_sb = 1, a.a_sk = prod(hp.dims, 1, k);       // natural layout: stride N/n_0
-    } else {
-      a.A = bytes_saved + (j - 1) * BN * hp.esize;
-      a.a_sb = n, a.a_sk = 1;                          // L_j
-    }
+    a.A = k > 1 ? static_cast<const void*>(slot(j)) : b.x;   // L_j
+    a.a_sb = n, a.a_sk = 1;
     a.a_si = hp.N;
     a.B = b.w[j];
     a.b_sb = n * n, a.b_sk = 1, a.b_sj = n;
@@ -132,12 +139,12 @@ int hyper_plan_fwd(const HyperProblem& hp, const HyperBuffers& b, HyperStep* ste
       a.C = b.y;
       a.c_sb = n, a.c_sj = 1;                          // natural = L_{k-1}
     } else {
-      a.C = static_cast<char*>(b.saved) + j * BN * hp.esize;
+      a.C = slot(j + 1);
       set_out_next(a, hp, j);
     }
     a.M = hp.batch, a.N = n, a.K = n, a.nblk = hp.N / n;
   }
-  return k;
+  return ns;
 }
 
 int hyper_plan_bwd(const HyperProblem& hp, const HyperBuffers& b, HyperStep* steps) {
@@ -156,6 +163,9 @@ int hyper_plan_bwd(const HyperProblem& hp, const HyperBuffers& b, HyperStep* ste
   const int64_t BN = hp.batch * hp.N;
   char* ws = static_cast<char*>(b.ws);
   const char* saved = static_cast<const char*>(b.saved_in);
+  // input of round j in L_j: the saved copies (slot j), or x itself when the
+  // lattice has one dimension
+  auto input = [&](int j) -> const void* { return k > 1 ? saved + j * BN * hp.esize : b.x; };
   for (int j = k - 1; j >= 0; --j) {
     const int64_t n = hp.dims[j], nf = hp.N / n;
     // gradient w.r.t. round j's output, in L_j
@@ -167,13 +177,8 @@ int hyper_plan_bwd(const HyperProblem& hp, const HyperBuffers& b, HyperStep* ste
       GemmArgs& a = st.g;
       a.A = g;
       a.a_sb = n, a.a_si = 1, a.a_sk = hp.N;
-      if (j == 0) {
-        a.B = b.x;
-        a.b_sb = 1, a.b_sk = hp.N, a.b_sj = prod(hp.dims, 1, k);
-      } else {
-        a.B = saved + (j - 1) * BN * hp.esize;
-        a.b_sb = n, a.b_sk = hp.N, a.b_sj = 1;
-      }
+      a.B = input(j);
+      a.b_sb = n, a.b_sk = hp.N, a.b_sj = 1;
       a.partial = reinterpret_cast<float*>(ws + hp.ws_part[j]);
       a.splits = hp.splits[j], a.k_chunk = hp.chunk[j];
       a.M = n, a.N = n, a.K = hp.batch, a.nblk = nf;
@@ -189,14 +194,22 @@ int hyper_plan_bwd(const HyperProblem& hp, const HyperBuffers& b, HyperStep* ste
       a.b_sb = n * n, a.b_sk = n, a.b_sj = 1;
       a.c_si = hp.N;
       if (j == 0) {
-        a.C = b.dx;
-        a.c_sb = 1, a.c_sj = prod(hp.dims, 1, k);    // natural layout
+        // g_0 in L_0 (dx itself for a one-dimensional lattice)
+        a.C = k > 1 ? static_cast<void*>(ws + hp.ws_g[(k - 1) & 1]) : b.dx;
+        a.c_sb = n, a.c_sj = 1;
       } else {
         a.C = ws + hp.ws_g[(k - 1 - j) & 1];
         set_out_prev(a, hp, j);
       }
       a.M = hp.batch, a.N = n, a.K = n, a.nblk = nf;
     }
+  }
+  if (k > 1) {
+    HyperStep& st = steps[ns++];
+    st.kind = HYPER_TRANSPOSE;
+    st.name = "hyper_transpose";
+    st.t_in = ws + hp.ws_g[(k - 1) & 1], st.t_out = b.dx;
+    st.t_rows = hp.batch, st.t_R = hp.N / hp.dims[0], st.t_C = hp.dims[0];
   }
   // fixed-order sums of the weight-gradient chunks, three rounds per launch
   for (int j0 = 0; j0 < k; j0 += 3) {
@@ -219,6 +232,8 @@ hipError_t hyper_launch(const HyperStep& st, bool bf16, hipStream_t s) {
     case HYPER_GEMM: return launch_gemm(st.g, bf16, s);
     case HYPER_REDUCE: return launch_reduce_partials(st.r[0], st.r[1], st.r[2], bf16, s);
     case HYPER_ZERO: return launch_zero(st.zero_ptr, st.zero_bytes, s);
+    case HYPER_TRANSPOSE:
+      return launch_row_transpose(st.t_in, st.t_out, st.t_rows, st.t_R, st.t_C, bf16, s);
   }
   return hipErrorInvalidValue;
 }

@@ -66,6 +66,11 @@ hipError_t launch_gemm(const GemmArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_dv_gather(const void* dy, const void* ymask, void* dv, int64_t rows, int64_t out,
                             int64_t b2, int64_t q2o, bool bf16, hipStream_t s);
 
+// Per-row matrix transpose: every one of `rows` rows of `in` holds an R x C
+// row-major matrix, stored to `out` as C x R (lattice layout changes).
+hipError_t launch_row_transpose(const void* in, void* out, int64_t rows, int64_t R, int64_t C,
+                                bool bf16, hipStream_t s);
+
 // Bias gradient partial sums: partial[c][p*b2 + g] = sum over rows
 // [c*chunk, (c+1)*chunk) of dV[b, g*q2o + p], for p*b2 + g < out (fp32,
 // rows in increasing order).
