@@ -11,3 +11,4 @@ from .monarch_oracle import (  # noqa: F401
 from . import monarch_projection  # noqa: F401,E402
 from . import monarch_linear  # noqa: F401,E402
 from . import monarch_hypercube  # noqa: F401,E402
+from . import dyad  # noqa: F401,E402
