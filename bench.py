@@ -337,6 +337,90 @@ def bench_hyper(args) -> int:
     return 0
 
 
+def bench_dyad(args) -> int:
+    """DYAD-style layer (two block-sparse terms) forward + backward at
+    `--n` x `--n`, `--nb` blocks, `--rows` tokens; one JSON line."""
+    import torch
+    import monarch_block_diagonal_amd as M
+    n, nb, B = args.n, args.nb, args.rows
+    bf16 = args.dtype == "bf16"
+    tdt = torch.bfloat16 if bf16 else torch.float32
+    code = M.BF16 if bf16 else M.F32
+    e = 2 if bf16 else 4
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    q = n // nb
+    log(f"dyad n={n} nb={nb} rows={B} {args.dtype}")
+    g = torch.Generator(device=dev)
+    g.manual_seed(20220401 + 600)
+    x = torch.randn((B, n), generator=g, device=dev).to(tdt)
+    dy = torch.randn((B, n), generator=g, device=dev).to(tdt)
+    wa = torch.randn((nb, q, q), generator=g, device=dev).mul_((2 * q) ** -0.5).to(tdt)
+    wb = torch.randn((nb, q, q), generator=g, device=dev).mul_((2 * q) ** -0.5).to(tdt)
+    y, dx, dwa, dwb = torch.empty_like(x), torch.empty_like(x), torch.empty_like(wa), torch.empty_like(wb)
+    need = M.monarch_dyad_bwd_workspace_bytes(n, n, nb, B, code)
+    ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    fn = M.monarch_dyad_describe(0, n, n, nb, B, code)
+    bn = M.monarch_dyad_describe(1, n, n, nb, B, code)
+    stream = torch.cuda.current_stream()
+
+    def step(evf=None, evb=None):
+        M.monarch_dyad_fwd(x, wa, wb, y, n, n, nb, B, code, stream, events=evf)
+        M.monarch_dyad_bwd(dy, x, wa, wb, dx, dwa, dwb, ws, need, n, n, nb, B, code, stream,
+                           events=evb)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    K = args.steps
+    evf = [[torch.cuda.Event(enable_timing=True) for _ in range(len(fn) + 1)] for _ in range(K)]
+    evb = [[torch.cuda.Event(enable_timing=True) for _ in range(len(bn) + 1)] for _ in range(K)]
+    t0 = time.perf_counter()
+    for k in range(K):
+        step(evf[k], evb[k])
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - t0) * 1e3 / K
+    kern = {}
+    for names, evs in ((fn, evf), (bn, evb)):
+        for i, nm in enumerate(names):
+            kern[nm] = sum(ev[i].elapsed_time(ev[i + 1]) for ev in evs) / K
+    params = 2 * nb * q * q
+    flops = 6.0 * B * params
+    act = e * B * n
+    # fwd: x read twice, y written and read back once; bwd: dy and x read
+    # twice each (two weight products), dy twice and dx twice (data products)
+    bytes_step = 4 * act + 8 * act + 3 * e * params
+    dense = None
+    if not args.no_dense:
+        Wd = torch.randn((n, n), device=dev).mul_(n ** -0.5).to(tdt)
+
+        def dense_step():
+            return x @ Wd.t(), dy @ Wd, dy.t() @ x
+        for _ in range(2):
+            dense_step()
+        torch.cuda.synchronize()
+        t1 = time.perf_counter()
+        for _ in range(3):
+            dense_step()
+        torch.cuda.synchronize()
+        dms = (time.perf_counter() - t1) * 1e3 / 3
+        dense = {"dtype": args.dtype, "ms_per_step": round(dms, 4),
+                 "speedup_dyad_vs_dense": round(dms / ms, 3)}
+    result = {
+        "metric": "DYAD fwd+bwd TFLOP/s", "value": round(flops / (ms * 1e-3) / 1e12, 2),
+        "unit": "TFLOP/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": args.dtype, "data": "synthetic (seeded, drawn on the device)",
+        "config": {"workload": f"dyad_n{n}_nb{nb}_rows{B}", "n": n, "nblocks": nb, "rows": B,
+                   "params": params},
+        "step_hbm_frac": round(bytes_step / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "kernels_ms": {k: round(v, 4) for k, v in kern.items()},
+        "dense_baseline": dense,
+    }
+    print(json.dumps(result), flush=True)
+    return 0
+
+
 def main() -> int:
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
@@ -349,12 +433,16 @@ def main() -> int:
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (read 1 GiB + write 1 GiB), the "
                          "reference for scaling HBM byte counters")
-    ap.add_argument("--op", choices=("step", "project", "hyper"), default="step",
+    ap.add_argument("--op", choices=("step", "project", "hyper", "dyad"), default="step",
                     help="step: forward + backward (default); project: dense -> Monarch "
-                         "projection of an n x n matrix; hyper: k-factor lattice layer")
+                         "projection of an n x n matrix; hyper: k-factor lattice layer; "
+                         "dyad: DYAD-style two-term layer")
+    ap.add_argument("--n", type=int, default=4096, help="features of --op dyad")
+    ap.add_argument("--nb", type=int, default=16, help="blocks of --op dyad")
     ap.add_argument("--dims", default="16x24x32", help="lattice of --op hyper")
-    ap.add_argument("--rows", type=int, default=16384, help="tokens of --op hyper")
-    ap.add_argument("--dtype", choices=("bf16", "f32"), default="bf16", help="--op hyper dtype")
+    ap.add_argument("--rows", type=int, default=16384, help="tokens of --op hyper / dyad")
+    ap.add_argument("--dtype", choices=("bf16", "f32"), default="bf16",
+                    help="dtype of --op hyper / dyad")
     ap.add_argument("--iters", type=int, default=32, help="power iterations (--op project)")
     args = ap.parse_args()
 
@@ -367,6 +455,8 @@ def main() -> int:
         return bench_project(args)
     if args.op == "hyper":
         return bench_hyper(args)
+    if args.op == "dyad":
+        return bench_dyad(args)
 
     import numpy as np
     import torch

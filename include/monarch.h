@@ -244,6 +244,33 @@ int monarch_hyper_bwd(const void* dy, const void* x, const void* const* w, const
 int monarch_hyper_describe(int direction, int ndims, const int64_t* dims, int64_t batch,
                            int dtype, char* buf, size_t buf_len);
 
+/* ---------------------------------------------------------------------------
+ * DYAD-style layer (DYAD page, abstract: the weight matrix is the sum of two
+ * matrices, each a permutation of a block-sparse one, stored as 3D tensors).
+ * With nb = nblocks, qi = in/nb, qo = out/nb (both divisible):
+ *   y = (BD(A) + Qout · BD(B) · P) x            for every row,
+ *   Y[b, r*qo + k] += sum_s A[r, k, s] X[b, r*qi + s]     (contiguous blocks)
+ *   Y[b, p*nb + g] += sum_t B[g, p, t] X[b, t*nb + g]     (stride-nb features)
+ * w_a = A and w_b = B are [nb, qo, qi]; x [batch, in], y [batch, out]. No
+ * saved intermediate. The second term is added to the rounded first one
+ * (two roundings of y in bf16). Errors and conventions as for monarch_fwd. */
+int monarch_dyad_fwd(const void* x, const void* w_a, const void* w_b, void* y,
+                     int64_t in_features, int64_t out_features, int64_t nblocks, int64_t batch,
+                     int dtype, void* stream, void* const* events, int n_events);
+
+size_t monarch_dyad_bwd_workspace_bytes(int64_t in_features, int64_t out_features,
+                                        int64_t nblocks, int64_t batch, int dtype);
+
+/* dx = dy · M, dw_a / dw_b = the block gradients (fixed-order batch sums),
+ * all overwritten. batch == 0 zeroes dw_a and dw_b. */
+int monarch_dyad_bwd(const void* dy, const void* x, const void* w_a, const void* w_b, void* dx,
+                     void* dw_a, void* dw_b, void* workspace, size_t workspace_bytes,
+                     int64_t in_features, int64_t out_features, int64_t nblocks, int64_t batch,
+                     int dtype, void* stream, void* const* events, int n_events);
+
+int monarch_dyad_describe(int direction, int64_t in_features, int64_t out_features,
+                          int64_t nblocks, int64_t batch, int dtype, char* buf, size_t buf_len);
+
 /* Static text for a status code; for MONARCH_ERR_HIP the last HIP error
  * message recorded on the calling thread. Never NULL. */
 const char* monarch_status_string(int status);

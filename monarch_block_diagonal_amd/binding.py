@@ -33,7 +33,8 @@ EXPORTED = (
     "monarch_project", "monarch_linear_mid", "monarch_fwd_ex", "monarch_bwd_ex",
     "monarch_bwd_ex_workspace_bytes", "monarch_describe_ex", "monarch_hyper_saved_elems",
     "monarch_hyper_fwd", "monarch_hyper_bwd_workspace_bytes", "monarch_hyper_bwd",
-    "monarch_hyper_describe",
+    "monarch_hyper_describe", "monarch_dyad_fwd", "monarch_dyad_bwd_workspace_bytes",
+    "monarch_dyad_bwd", "monarch_dyad_describe",
 )
 
 _lib = None
@@ -100,6 +101,14 @@ def load_library():
     lib.monarch_hyper_bwd.restype = c_int
     lib.monarch_hyper_describe.argtypes = [c_int, c_int, pi64, i64, c_int, ctypes.c_char_p, sz]
     lib.monarch_hyper_describe.restype = c_int
+    lib.monarch_dyad_fwd.argtypes = [vp] * 4 + [i64] * 4 + [c_int, vp] + ev
+    lib.monarch_dyad_fwd.restype = c_int
+    lib.monarch_dyad_bwd_workspace_bytes.argtypes = [i64] * 4 + [c_int]
+    lib.monarch_dyad_bwd_workspace_bytes.restype = sz
+    lib.monarch_dyad_bwd.argtypes = [vp] * 8 + [sz] + [i64] * 4 + [c_int, vp] + ev
+    lib.monarch_dyad_bwd.restype = c_int
+    lib.monarch_dyad_describe.argtypes = [c_int] + [i64] * 4 + [c_int, ctypes.c_char_p, sz]
+    lib.monarch_dyad_describe.restype = c_int
     _lib = lib
     return lib
 
@@ -290,6 +299,38 @@ def monarch_hyper_describe(direction, dims, batch, dtype):
     d, k = _dims(dims)
     buf = ctypes.create_string_buffer(1024)
     n = lib.monarch_hyper_describe(direction, k, d, batch, dtype, buf, len(buf))
+    if n < 0:
+        raise MonarchError(n, monarch_status_string(n))
+    return buf.value.decode().split(";") if n else []
+
+
+def monarch_dyad_fwd(x, wa, wb, y, in_features, out_features, nblocks, batch, dtype, stream=None,
+                     events=None) -> None:
+    lib = load_library()
+    arr, n = _events(events)
+    _check(lib.monarch_dyad_fwd(_ptr(x), _ptr(wa), _ptr(wb), _ptr(y), in_features, out_features,
+                                nblocks, batch, dtype, _stream(stream), arr, n))
+
+
+def monarch_dyad_bwd_workspace_bytes(in_features, out_features, nblocks, batch, dtype) -> int:
+    return load_library().monarch_dyad_bwd_workspace_bytes(in_features, out_features, nblocks,
+                                                           batch, dtype)
+
+
+def monarch_dyad_bwd(dy, x, wa, wb, dx, dwa, dwb, workspace, workspace_bytes, in_features,
+                     out_features, nblocks, batch, dtype, stream=None, events=None) -> None:
+    lib = load_library()
+    arr, n = _events(events)
+    _check(lib.monarch_dyad_bwd(_ptr(dy), _ptr(x), _ptr(wa), _ptr(wb), _ptr(dx), _ptr(dwa),
+                                _ptr(dwb), _ptr(workspace), workspace_bytes, in_features,
+                                out_features, nblocks, batch, dtype, _stream(stream), arr, n))
+
+
+def monarch_dyad_describe(direction, in_features, out_features, nblocks, batch, dtype):
+    lib = load_library()
+    buf = ctypes.create_string_buffer(1024)
+    n = lib.monarch_dyad_describe(direction, in_features, out_features, nblocks, batch, dtype, buf,
+                                  len(buf))
     if n < 0:
         raise MonarchError(n, monarch_status_string(n))
     return buf.value.decode().split(";") if n else []

@@ -6,6 +6,7 @@
 #include <stdio.h>
 #include <string.h>
 
+#include "dyad.h"
 #include "hyper.h"
 #include "kernels.h"
 #include "monarch.h"
@@ -102,13 +103,13 @@ int bwd_impl(const Problem& pr, const void* dy, const void* x, const void* w1, c
   return run_plan(plan, pr, b, static_cast<hipStream_t>(stream), events, n_events);
 }
 
-int run_hyper(const HyperStep* steps, int n, bool bf16, hipStream_t s, void* const* events,
+int run_seq(const SeqStep* steps, int n, bool bf16, hipStream_t s, void* const* events,
               int n_events) {
   Tracer tr{events, n_events, 0, s};
   for (int i = 0; i < n; ++i) {
     int st = record_hip(tr.mark());
     if (st) return st;
-    st = record_hip(hyper_launch(steps[i], bf16, s));
+    st = record_hip(seq_launch(steps[i], bf16, s));
     if (st) return st;
   }
   return record_hip(tr.mark());
@@ -314,9 +315,9 @@ int monarch_hyper_fwd(const void* x, const void* const* w, void* y, void* saved,
   b.x = x;
   b.y = y;
   b.saved = saved;
-  HyperStep steps[kHyperMaxSteps];
+  SeqStep steps[kHyperMaxSteps];
   const int n = hyper_plan_fwd(hp, b, steps);
-  return run_hyper(steps, n, dtype == MONARCH_BF16, static_cast<hipStream_t>(stream), events,
+  return run_seq(steps, n, dtype == MONARCH_BF16, static_cast<hipStream_t>(stream), events,
                    n_events);
 }
 
@@ -353,9 +354,9 @@ int monarch_hyper_bwd(const void* dy, const void* x, const void* const* w, const
   b.saved_in = saved;
   b.dx = dx;
   b.ws = workspace;
-  HyperStep steps[kHyperMaxSteps];
+  SeqStep steps[kHyperMaxSteps];
   const int n = hyper_plan_bwd(hp, b, steps);
-  return run_hyper(steps, n, dtype == MONARCH_BF16, static_cast<hipStream_t>(stream), events,
+  return run_seq(steps, n, dtype == MONARCH_BF16, static_cast<hipStream_t>(stream), events,
                    n_events);
 }
 
@@ -366,9 +367,71 @@ int monarch_hyper_describe(int direction, int ndims, const int64_t* dims, int64_
   if (st) return st;
   if (direction != 0 && direction != 1) return MONARCH_ERR_DTYPE;
   HyperBuffers b;
-  HyperStep steps[kHyperMaxSteps];
+  SeqStep steps[kHyperMaxSteps];
   const int n = direction == 0 ? hyper_plan_fwd(hp, b, steps) : hyper_plan_bwd(hp, b, steps);
   const char* names[kHyperMaxSteps];
+  for (int i = 0; i < n; ++i) names[i] = steps[i].name;
+  return write_names(names, n, buf, buf_len);
+}
+
+int monarch_dyad_fwd(const void* x, const void* w_a, const void* w_b, void* y,
+                     int64_t in_features, int64_t out_features, int64_t nblocks, int64_t batch,
+                     int dtype, void* stream, void* const* events, int n_events) {
+  DyadProblem dp;
+  int st = make_dyad(in_features, out_features, nblocks, batch, dtype, &dp);
+  if (st) return st;
+  if (!w_a || !w_b) return MONARCH_ERR_NULL;
+  if (batch > 0 && (!x || !y)) return MONARCH_ERR_NULL;
+  if (misaligned(x) || misaligned(w_a) || misaligned(w_b) || misaligned(y)) return MONARCH_ERR_ALIGN;
+  if (batch == 0) return MONARCH_OK;
+  DyadBuffers b;
+  b.x = x, b.wa = w_a, b.wb = w_b, b.y = y;
+  SeqStep steps[kDyadMaxSteps];
+  const int n = dyad_plan_fwd(dp, b, steps);
+  return run_seq(steps, n, dtype == MONARCH_BF16, static_cast<hipStream_t>(stream), events,
+                 n_events);
+}
+
+size_t monarch_dyad_bwd_workspace_bytes(int64_t in_features, int64_t out_features,
+                                        int64_t nblocks, int64_t batch, int dtype) {
+  DyadProblem dp;
+  if (make_dyad(in_features, out_features, nblocks, batch, dtype, &dp)) return 0;
+  return dp.ws_total;
+}
+
+int monarch_dyad_bwd(const void* dy, const void* x, const void* w_a, const void* w_b, void* dx,
+                     void* dw_a, void* dw_b, void* workspace, size_t workspace_bytes,
+                     int64_t in_features, int64_t out_features, int64_t nblocks, int64_t batch,
+                     int dtype, void* stream, void* const* events, int n_events) {
+  DyadProblem dp;
+  int st = make_dyad(in_features, out_features, nblocks, batch, dtype, &dp);
+  if (st) return st;
+  if (!w_a || !w_b || !dw_a || !dw_b) return MONARCH_ERR_NULL;
+  if (batch > 0 && (!dy || !x || !dx)) return MONARCH_ERR_NULL;
+  if (dp.ws_total > 0 && !workspace) return MONARCH_ERR_NULL;
+  if (misaligned(dy) || misaligned(x) || misaligned(w_a) || misaligned(w_b) || misaligned(dx) ||
+      misaligned(dw_a) || misaligned(dw_b) || misaligned(workspace))
+    return MONARCH_ERR_ALIGN;
+  if (workspace_bytes < dp.ws_total) return MONARCH_ERR_WORKSPACE;
+  DyadBuffers b;
+  b.dy = dy, b.x = x, b.wa = w_a, b.wb = w_b, b.dx = dx, b.dwa = dw_a, b.dwb = dw_b;
+  b.ws = workspace;
+  SeqStep steps[kDyadMaxSteps];
+  const int n = dyad_plan_bwd(dp, b, steps);
+  return run_seq(steps, n, dtype == MONARCH_BF16, static_cast<hipStream_t>(stream), events,
+                 n_events);
+}
+
+int monarch_dyad_describe(int direction, int64_t in_features, int64_t out_features,
+                          int64_t nblocks, int64_t batch, int dtype, char* buf, size_t buf_len) {
+  DyadProblem dp;
+  int st = make_dyad(in_features, out_features, nblocks, batch, dtype, &dp);
+  if (st) return st;
+  if (direction != 0 && direction != 1) return MONARCH_ERR_DTYPE;
+  DyadBuffers b;
+  SeqStep steps[kDyadMaxSteps];
+  const int n = direction == 0 ? dyad_plan_fwd(dp, b, steps) : dyad_plan_bwd(dp, b, steps);
+  const char* names[kDyadMaxSteps];
   for (int i = 0; i < n; ++i) names[i] = steps[i].name;
   return write_names(names, n, buf, buf_len);
 }

@@ -1,0 +1,147 @@
+// DYAD-style layer (DYAD page, abstract: a weight matrix that is the sum of
+// two matrices, each a permutation of a block-sparse one, stored as 3D
+// tensors): with nb blocks, qi = in/nb, qo = out/nb,
+//   Y = X · (BD(A) + Q_out · BD(B) · P_in)ᵀ,
+//   term A: Y[b, r*qo + k] += sum_s A[r,k,s] X[b, r*qi + s]   (contiguous blocks)
+//   term B: Y[b, p*nb + g] += sum_t B[g,p,t] X[b, t*nb + g]   (residue-g features)
+// Each term is one launch of the tiled GEMM (tiled.hip); the second adds to
+// the first's result. The backward mirrors it: dX = dY·BD(A) + (term B's
+// transpose, accumulated), and the two weight gradients are batch-split sums
+// reduced in a fixed order.
+#include "dyad.h"
+#include "monarch.h"
+
+namespace monarch {
+namespace {
+
+constexpr int64_t kLimit = int64_t(1) << 31;
+
+size_t align256(size_t v) { return (v + 255) / 256 * 256; }
+
+void splits_for(int64_t nblk, int64_t M, int64_t N, int64_t K, int64_t* splits, int64_t* chunk) {
+  const int64_t base = nblk * ((M + 63) / 64) * ((N + 63) / 64);
+  int64_t s = (2048 + base - 1) / base;
+  const int64_t smax = (K + 127) / 128;
+  if (s > smax) s = smax;
+  if (s > 64) s = 64;
+  if (s < 1) s = 1;
+  int64_t c = (K + s - 1) / s;
+  c = (c + kSplitK - 1) / kSplitK * kSplitK;
+  *chunk = c;
+  *splits = (K + c - 1) / c;
+}
+
+// term A and term B GEMMs of the forward / the data backward
+void term_a_fwd(GemmArgs& a, const DyadProblem& dp, const void* x, const void* wa, void* y) {
+  a.A = x, a.a_sb = dp.qi, a.a_si = dp.in, a.a_sk = 1;
+  a.B = wa, a.b_sb = dp.qo * dp.qi, a.b_sk = 1, a.b_sj = dp.qi;
+  a.C = y, a.c_sb = dp.qo, a.c_si = dp.out, a.c_sj = 1;
+  a.M = dp.batch, a.N = dp.qo, a.K = dp.qi, a.nblk = dp.nb;
+}
+void term_b_fwd(GemmArgs& a, const DyadProblem& dp, const void* x, const void* wb, void* y) {
+  a.A = x, a.a_sb = 1, a.a_si = dp.in, a.a_sk = dp.nb;
+  a.B = wb, a.b_sb = dp.qo * dp.qi, a.b_sk = 1, a.b_sj = dp.qi;
+  a.C = y, a.c_sb = 1, a.c_si = dp.out, a.c_sj = dp.nb;
+  a.accum = 1;
+  a.M = dp.batch, a.N = dp.qo, a.K = dp.qi, a.nblk = dp.nb;
+}
+
+}  // namespace
+
+int make_dyad(int64_t in, int64_t out, int64_t nb, int64_t batch, int dtype, DyadProblem* dp) {
+  if (dtype != MONARCH_F32 && dtype != MONARCH_BF16) return MONARCH_ERR_DTYPE;
+  if (in <= 0 || out <= 0 || nb <= 0 || batch < 0) return MONARCH_ERR_SHAPE;
+  if (in >= kLimit || out >= kLimit || batch >= kLimit || in % nb || out % nb)
+    return MONARCH_ERR_SHAPE;
+  DyadProblem p;
+  p.in = in, p.out = out, p.nb = nb, p.qi = in / nb, p.qo = out / nb, p.batch = batch;
+  p.dtype = dtype;
+  p.esize = dtype == MONARCH_BF16 ? 2 : 4;
+  if (batch > 0) {
+    splits_for(nb, p.qo, p.qi, batch, &p.splits, &p.chunk);
+    const size_t part = static_cast<size_t>(p.splits) * nb * p.qo * p.qi * 4;
+    p.ws_pa = 0;
+    p.ws_pb = align256(part);
+    p.ws_total = align256(p.ws_pb + part);
+  }
+  *dp = p;
+  return MONARCH_OK;
+}
+
+int dyad_plan_fwd(const DyadProblem& dp, const DyadBuffers& b, SeqStep* steps) {
+  if (dp.batch == 0) return 0;
+  steps[0].kind = SEQ_GEMM;
+  steps[0].name = "dyad_term_a_fwd";
+  term_a_fwd(steps[0].g, dp, b.x, b.wa, b.y);
+  steps[1].kind = SEQ_GEMM;
+  steps[1].name = "dyad_term_b_fwd";
+  term_b_fwd(steps[1].g, dp, b.x, b.wb, b.y);
+  return 2;
+}
+
+int dyad_plan_bwd(const DyadProblem& dp, const DyadBuffers& b, SeqStep* steps) {
+  const size_t wbytes = static_cast<size_t>(dp.nb * dp.qo * dp.qi) * dp.esize;
+  if (dp.batch == 0) {
+    steps[0].kind = SEQ_ZERO, steps[0].name = "zero_dw";
+    steps[0].zero_ptr = b.dwa, steps[0].zero_bytes = wbytes;
+    steps[1].kind = SEQ_ZERO, steps[1].name = "zero_dw";
+    steps[1].zero_ptr = b.dwb, steps[1].zero_bytes = wbytes;
+    return 2;
+  }
+  char* ws = static_cast<char*>(b.ws);
+  float* pa = reinterpret_cast<float*>(ws + dp.ws_pa);
+  float* pb = reinterpret_cast<float*>(ws + dp.ws_pb);
+  int n = 0;
+  {
+    // dA[r] = sum_b dY[b, r-block]ᵀ X[b, r-block]
+    SeqStep& st = steps[n++];
+    st.name = "dyad_term_a_bwd_weight";
+    GemmArgs& a = st.g;
+    a.A = b.dy, a.a_sb = dp.qo, a.a_si = 1, a.a_sk = dp.out;
+    a.B = b.x, a.b_sb = dp.qi, a.b_sk = dp.in, a.b_sj = 1;
+    a.partial = pa, a.splits = dp.splits, a.k_chunk = dp.chunk;
+    a.M = dp.qo, a.N = dp.qi, a.K = dp.batch, a.nblk = dp.nb;
+  }
+  {
+    // dB[g] = sum_b dY[b, p*nb + g] X[b, t*nb + g]
+    SeqStep& st = steps[n++];
+    st.name = "dyad_term_b_bwd_weight";
+    GemmArgs& a = st.g;
+    a.A = b.dy, a.a_sb = 1, a.a_si = dp.nb, a.a_sk = dp.out;
+    a.B = b.x, a.b_sb = 1, a.b_sk = dp.in, a.b_sj = dp.nb;
+    a.partial = pb, a.splits = dp.splits, a.k_chunk = dp.chunk;
+    a.M = dp.qo, a.N = dp.qi, a.K = dp.batch, a.nblk = dp.nb;
+  }
+  {
+    // dX[b, r*qi + s] = sum_k dY[b, r*qo + k] A[r,k,s]
+    SeqStep& st = steps[n++];
+    st.name = "dyad_term_a_bwd_data";
+    GemmArgs& a = st.g;
+    a.A = b.dy, a.a_sb = dp.qo, a.a_si = dp.out, a.a_sk = 1;
+    a.B = b.wa, a.b_sb = dp.qo * dp.qi, a.b_sk = dp.qi, a.b_sj = 1;
+    a.C = b.dx, a.c_sb = dp.qi, a.c_si = dp.in, a.c_sj = 1;
+    a.M = dp.batch, a.N = dp.qi, a.K = dp.qo, a.nblk = dp.nb;
+  }
+  {
+    // dX[b, t*nb + g] += sum_p dY[b, p*nb + g] B[g,p,t]
+    SeqStep& st = steps[n++];
+    st.name = "dyad_term_b_bwd_data";
+    GemmArgs& a = st.g;
+    a.A = b.dy, a.a_sb = 1, a.a_si = dp.out, a.a_sk = dp.nb;
+    a.B = b.wb, a.b_sb = dp.qo * dp.qi, a.b_sk = dp.qi, a.b_sj = 1;
+    a.C = b.dx, a.c_sb = 1, a.c_si = dp.in, a.c_sj = dp.nb;
+    a.accum = 1;
+    a.M = dp.batch, a.N = dp.qi, a.K = dp.qo, a.nblk = dp.nb;
+  }
+  {
+    SeqStep& st = steps[n++];
+    st.kind = SEQ_REDUCE;
+    st.name = "reduce_dw";
+    const int64_t nw = dp.nb * dp.qo * dp.qi;
+    st.r[0].partial = pa, st.r[0].out = b.dwa, st.r[0].n = nw, st.r[0].splits = dp.splits;
+    st.r[1].partial = pb, st.r[1].out = b.dwb, st.r[1].n = nw, st.r[1].splits = dp.splits;
+  }
+  return n;
+}
+
+}  // namespace monarch

@@ -6,6 +6,7 @@
 #include <stdint.h>
 
 #include "kernels.h"
+#include "steps.h"
 
 namespace monarch {
 
@@ -33,21 +34,6 @@ struct HyperBuffers {
   void* ws = nullptr;
 };
 
-enum HyperKind { HYPER_GEMM, HYPER_REDUCE, HYPER_ZERO, HYPER_TRANSPOSE };
-
-struct HyperStep {
-  HyperKind kind = HYPER_GEMM;
-  const char* name = "";
-  GemmArgs g;
-  ReduceArgs r[3];
-  void* zero_ptr = nullptr;
-  size_t zero_bytes = 0;
-  // HYPER_TRANSPOSE: every row of `rows` is an R x C matrix, written as C x R
-  const void* t_in = nullptr;
-  void* t_out = nullptr;
-  int64_t t_rows = 0, t_R = 0, t_C = 0;
-};
-
 constexpr int kHyperMaxSteps = 3 * kHyperMaxDims + 4;
 
 // Checks the lattice (1..4 dimensions, positive, N < 2^31), batch and dtype;
@@ -55,8 +41,7 @@ constexpr int kHyperMaxSteps = 3 * kHyperMaxDims + 4;
 int make_hyper(int ndims, const int64_t* dims, int64_t batch, int dtype, HyperProblem* hp);
 int64_t hyper_saved_elems(const HyperProblem& hp);
 // Steps of the forward / backward pass; returns their count.
-int hyper_plan_fwd(const HyperProblem& hp, const HyperBuffers& b, HyperStep* steps);
-int hyper_plan_bwd(const HyperProblem& hp, const HyperBuffers& b, HyperStep* steps);
-hipError_t hyper_launch(const HyperStep& st, bool bf16, hipStream_t s);
+int hyper_plan_fwd(const HyperProblem& hp, const HyperBuffers& b, SeqStep* steps);
+int hyper_plan_bwd(const HyperProblem& hp, const HyperBuffers& b, SeqStep* steps);
 
 }  // namespace monarch

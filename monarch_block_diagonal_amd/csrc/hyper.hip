@@ -109,7 +109,7 @@ int make_hyper(int ndims, const int64_t* dims, int64_t batch, int dtype, HyperPr
 
 int64_t hyper_saved_elems(const HyperProblem& hp) { return hp.k > 1 ? hp.k * hp.batch * hp.N : 0; }
 
-int hyper_plan_fwd(const HyperProblem& hp, const HyperBuffers& b, HyperStep* steps) {
+int hyper_plan_fwd(const HyperProblem& hp, const HyperBuffers& b, SeqStep* steps) {
   if (hp.batch == 0) return 0;
   const int k = hp.k;
   const int64_t BN = hp.batch * hp.N;
@@ -117,16 +117,16 @@ int hyper_plan_fwd(const HyperProblem& hp, const HyperBuffers& b, HyperStep* ste
   auto slot = [&](int sidx) { return static_cast<char*>(b.saved) + sidx * BN * hp.esize; };
   int ns = 0;
   if (k > 1) {
-    HyperStep& st = steps[ns++];
-    st.kind = HYPER_TRANSPOSE;
+    SeqStep& st = steps[ns++];
+    st.kind = SEQ_TRANSPOSE;
     st.name = "hyper_transpose";
     st.t_in = b.x, st.t_out = slot(0);
     st.t_rows = hp.batch, st.t_R = hp.dims[0], st.t_C = hp.N / hp.dims[0];
   }
   for (int j = 0; j < k; ++j) {
     const int64_t n = hp.dims[j];
-    HyperStep& st = steps[ns++];
-    st.kind = HYPER_GEMM;
+    SeqStep& st = steps[ns++];
+    st.kind = SEQ_GEMM;
     st.name = "hyper_round_fwd";
     GemmArgs& a = st.g;
     a.A = k > 1 ? static_cast<const void*>(slot(j)) : b.x;   // L_j
@@ -147,13 +147,13 @@ int hyper_plan_fwd(const HyperProblem& hp, const HyperBuffers& b, HyperStep* ste
   return ns;
 }
 
-int hyper_plan_bwd(const HyperProblem& hp, const HyperBuffers& b, HyperStep* steps) {
+int hyper_plan_bwd(const HyperProblem& hp, const HyperBuffers& b, SeqStep* steps) {
   const int k = hp.k;
   int ns = 0;
   if (hp.batch == 0) {
     for (int j = 0; j < k; ++j) {
-      HyperStep& st = steps[ns++];
-      st.kind = HYPER_ZERO;
+      SeqStep& st = steps[ns++];
+      st.kind = SEQ_ZERO;
       st.name = "zero_dw";
       st.zero_ptr = b.dw[j];
       st.zero_bytes = static_cast<size_t>(hp.N) * hp.dims[j] * hp.esize;
@@ -171,8 +171,8 @@ int hyper_plan_bwd(const HyperProblem& hp, const HyperBuffers& b, HyperStep* ste
     // gradient w.r.t. round j's output, in L_j
     const void* g = j == k - 1 ? b.dy : ws + hp.ws_g[(k - 2 - j) & 1];
     {
-      HyperStep& st = steps[ns++];
-      st.kind = HYPER_GEMM;
+      SeqStep& st = steps[ns++];
+      st.kind = SEQ_GEMM;
       st.name = "hyper_round_bwd_weight";
       GemmArgs& a = st.g;
       a.A = g;
@@ -184,8 +184,8 @@ int hyper_plan_bwd(const HyperProblem& hp, const HyperBuffers& b, HyperStep* ste
       a.M = n, a.N = n, a.K = hp.batch, a.nblk = nf;
     }
     {
-      HyperStep& st = steps[ns++];
-      st.kind = HYPER_GEMM;
+      SeqStep& st = steps[ns++];
+      st.kind = SEQ_GEMM;
       st.name = "hyper_round_bwd_data";
       GemmArgs& a = st.g;
       a.A = g;
@@ -205,16 +205,16 @@ int hyper_plan_bwd(const HyperProblem& hp, const HyperBuffers& b, HyperStep* ste
     }
   }
   if (k > 1) {
-    HyperStep& st = steps[ns++];
-    st.kind = HYPER_TRANSPOSE;
+    SeqStep& st = steps[ns++];
+    st.kind = SEQ_TRANSPOSE;
     st.name = "hyper_transpose";
     st.t_in = ws + hp.ws_g[(k - 1) & 1], st.t_out = b.dx;
     st.t_rows = hp.batch, st.t_R = hp.N / hp.dims[0], st.t_C = hp.dims[0];
   }
   // fixed-order sums of the weight-gradient chunks, three rounds per launch
   for (int j0 = 0; j0 < k; j0 += 3) {
-    HyperStep& st = steps[ns++];
-    st.kind = HYPER_REDUCE;
+    SeqStep& st = steps[ns++];
+    st.kind = SEQ_REDUCE;
     st.name = "reduce_dw";
     for (int i = 0; i < 3 && j0 + i < k; ++i) {
       const int j = j0 + i;
@@ -227,12 +227,12 @@ int hyper_plan_bwd(const HyperProblem& hp, const HyperBuffers& b, HyperStep* ste
   return ns;
 }
 
-hipError_t hyper_launch(const HyperStep& st, bool bf16, hipStream_t s) {
+hipError_t seq_launch(const SeqStep& st, bool bf16, hipStream_t s) {
   switch (st.kind) {
-    case HYPER_GEMM: return launch_gemm(st.g, bf16, s);
-    case HYPER_REDUCE: return launch_reduce_partials(st.r[0], st.r[1], st.r[2], bf16, s);
-    case HYPER_ZERO: return launch_zero(st.zero_ptr, st.zero_bytes, s);
-    case HYPER_TRANSPOSE:
+    case SEQ_GEMM: return launch_gemm(st.g, bf16, s);
+    case SEQ_REDUCE: return launch_reduce_partials(st.r[0], st.r[1], st.r[2], bf16, s);
+    case SEQ_ZERO: return launch_zero(st.zero_ptr, st.zero_bytes, s);
+    case SEQ_TRANSPOSE:
       return launch_row_transpose(st.t_in, st.t_out, st.t_rows, st.t_R, st.t_C, bf16, s);
   }
   return hipErrorInvalidValue;

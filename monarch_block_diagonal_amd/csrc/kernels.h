@@ -43,6 +43,8 @@ struct GemmArgs {
   // and its entries sit at d0*cb_s0 + d1*cb_s1 + d2*cb_s2 in place of
   // blk*c_sb (a lattice axis moved between layouts).
   int64_t cb_r0 = 0, cb_r1 = 1, cb_s0 = 0, cb_s1 = 0, cb_s2 = 0;
+  // accum: C += the product (C read back before the store; not with `partial`)
+  int accum = 0;
   int64_t M = 0, N = 0, K = 0;
   int64_t nblk = 1;
   int64_t splits = 1;

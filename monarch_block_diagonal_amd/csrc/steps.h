@@ -1,0 +1,31 @@
+// A launch sequence of the library: the layers that are not the two-stage
+// Monarch product (the k-factor lattice, the DYAD sum) run as lists of these
+// steps (internal).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "kernels.h"
+
+namespace monarch {
+
+enum SeqKind { SEQ_GEMM, SEQ_REDUCE, SEQ_ZERO, SEQ_TRANSPOSE };
+
+struct SeqStep {
+  SeqKind kind = SEQ_GEMM;
+  const char* name = "";
+  GemmArgs g;
+  ReduceArgs r[3];
+  void* zero_ptr = nullptr;
+  size_t zero_bytes = 0;
+  // SEQ_TRANSPOSE: every row of `rows` is an R x C matrix, written as C x R
+  const void* t_in = nullptr;
+  void* t_out = nullptr;
+  int64_t t_rows = 0, t_R = 0, t_C = 0;
+};
+
+hipError_t seq_launch(const SeqStep& st, bool bf16, hipStream_t s);
+
+}  // namespace monarch

@@ -335,6 +335,7 @@ __global__ __launch_bounds__(TT) void tiled_gemm_kernel(GemmArgs p, int64_t m_ti
           if (p.partial) {
             p.partial[((split * p.nblk + blk) * p.M + i) * p.N + j] = val;
           } else if (p.c_cols < 0 || cpos < p.c_cols) {
+            if (p.accum) val += Io<T>::load(p.C, i * p.c_si + cpos);
             if (p.bias) val += Io<T>::load(p.bias, cpos);
             if (p.relu) val = val > 0.f ? val : 0.f;
             Io<T>::store(p.C, i * p.c_si + cpos, val);

@@ -229,3 +229,27 @@ def hyper_backward(dy, x, ws, saved, dims, stream=None):
     ws_buf = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     B.monarch_hyper_bwd(dy, x, ws, saved, dx, dws, ws_buf, need, dims, b, code, stream)
     return dx, dws
+
+
+def dyad_forward(x, wa, wb, stream=None):
+    """DYAD-style layer: y = x · (BD(A) + Q·BD(B)·P)ᵀ; wa, wb [nb, out/nb, in/nb]."""
+    _check(x, wa, wb)
+    nb, qo, qi = wa.shape
+    b = x.shape[0]
+    y = torch.empty((b, nb * qo), dtype=x.dtype, device=x.device)
+    B.monarch_dyad_fwd(x, wa, wb, y, x.shape[1], nb * qo, nb, b, dtype_code(x), stream)
+    return y
+
+
+def dyad_backward(dy, x, wa, wb, stream=None):
+    """(dx, dwa, dwb) of the DYAD-style layer."""
+    _check(dy, x, wa, wb)
+    nb, qo, qi = wa.shape
+    b = x.shape[0]
+    code = dtype_code(x)
+    dx, dwa, dwb = torch.empty_like(x), torch.empty_like(wa), torch.empty_like(wb)
+    need = B.monarch_dyad_bwd_workspace_bytes(x.shape[1], nb * qo, nb, b, code)
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    B.monarch_dyad_bwd(dy, x, wa, wb, dx, dwa, dwb, ws, need, x.shape[1], nb * qo, nb, b, code,
+                       stream)
+    return dx, dwa, dwb
