@@ -21,14 +21,16 @@ bool sq_applicable(int64_t in, int64_t out, int64_t nb1, int64_t nb2, int64_t ba
                    int dtype_bf16);
 SqPlan sq_plan(int64_t batch, int64_t nb);
 
-// Panel layout: feature f of row b at ((f/8)*batch + b)*8 + f%8. z holds
+// Tile-major panel layout (F features per row): feature f of row b at
+// (b - b%16)*F + ((f/8)*rt + b%16)*8 + f%8, rt = rows of b's 16-row tile
+// (16, or batch%16 in a last partial tile). z holds
 // stage 2's input W[b, g*128 + t] = Z[b, t*nb + g] in it; dz holds dZ (Z order).
 hipError_t sq_launch_stage1_fwd(const void* x, const void* w1, void* z, int64_t batch, int64_t nb,
                                 const SqPlan& p, hipStream_t s);
 hipError_t sq_launch_stage2_fwd(const void* z, const void* w2, void* y, int64_t batch, int64_t nb,
                                 int relu, const SqPlan& p, hipStream_t s);
 // dv = dY (masked by ymask > 0 when ymask is set) in block-major panels:
-// element (b, g*128 + p) at (((g*128+p)/8)*batch + b)*8 + p%8.
+// feature g*128 + p of row b in the panel layout.
 hipError_t sq_launch_dv_panels(const void* dy, const void* ymask, void* dv, int64_t batch,
                                int64_t nb, hipStream_t s);
 hipError_t sq_launch_stage2_bwd_data(const void* dv, const void* w2, void* dz, int64_t batch,

@@ -7,9 +7,15 @@
 // I/O width against a bf16 MFMA ridge near 300), so the kernels are built
 // around data movement:
 //
-//  * Block-major panel layout for the intermediates: feature f of row b sits
-//    at ((f/8)*B + b)*8 + f%8, so a 16-byte piece holds 8 features of one
-//    row and a panel holds those 8 features for every row. The saved stage-2
+//  * Tile-major panel layout for the intermediates: the batch is cut into
+//    16-row tiles, and a tile stores each 8-feature panel as one run of its
+//    rows: feature f of row b sits at (b - b%16)*F + ((f/8)*rt + b%16)*8 +
+//    f%8 (F features per row, rt = 16 rows, fewer in a last partial tile).
+//    A 16-byte piece holds 8 features of one row, one panel of a tile is a
+//    256-byte run, and the runs a kernel reads together lie within one
+//    tile's F*32 bytes whatever the batch: with a panel-major order (stride
+//    B*16 bytes between panels) some batch sizes map those runs onto few
+//    memory channels and cache sets. The saved stage-2
 //    input (z) is W = P·Z in this layout, W[b, g*128 + t] = Z[b, t*b2 + g]:
 //    the stride permutation of the "hypercube" thread is applied once, by the
 //    stage-1 kernel's stores, and every stage-2 kernel reads whole pieces of
@@ -123,6 +129,18 @@ __device__ __forceinline__ u32x4 zero_unless(bool keep, u32x4 v) {
   return keep ? v : u32x4{0u, 0u, 0u, 0u};
 }
 
+// Row b of the tile-major panel layout (F features per row, B rows): piece
+// (b, panel P) is at base + P*rt8 elements.
+struct PanelRow {
+  uint32_t base;   // tile start * F + (b % 16) * 8
+  uint32_t rt8;    // 8 * rows of b's tile
+};
+__device__ __forceinline__ PanelRow panel_row(int64_t b, uint32_t F, uint32_t Bu) {
+  const uint32_t bu = static_cast<uint32_t>(b), t0 = bu & ~15u;
+  const uint32_t rt = Bu - t0 < 16u ? Bu - t0 : 16u;
+  return PanelRow{t0 * F + (bu & 15u) * 8u, rt * 8u};
+}
+
 // --------------------------------------------------------------------------
 // stage 1 forward, stored in stage 2's input order:
 //   W[b, g*128 + t] = Z[b, t*b2 + g],  Z[b, r*128 + k] = sum_s R[r,k,s] X[b, r*128 + s]
@@ -203,12 +221,13 @@ __global__ __launch_bounds__(512) void sq_stage1_fwd_kernel(const uint16_t* __re
       }
     __syncthreads();
     const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
-    uint16_t* zb = Wz + (bc + clamp_row(srow, lim)) * 8;
+    const PanelRow pr = panel_row(bc + clamp_row(srow, lim), in, Bu);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int pid = spid + 32 * i;
       const uint32_t panel = (pid / NPC) * 16 + rg * NPC + pid % NPC;
-      stg16_nt(zb + panel * Bu * 8, *reinterpret_cast<const u32x4*>(&zs[pid * ZP + srow * 8]));
+      stg16_nt(Wz + pr.base + panel * pr.rt8,
+               *reinterpret_cast<const u32x4*>(&zs[pid * ZP + srow * 8]));
     }
     __syncthreads();
   };
@@ -274,9 +293,7 @@ __global__ __launch_bounds__(512) void sq_stage2_fwd_kernel(const uint16_t* __re
   }
 
   // operand pieces: panel (g0+4w+g)*16 + 4tc + lh, row b0 + l15
-  const uint32_t wcol = ((gq * 32 + 4 * w) * 16 + lh) * Bu * 8;
-  const uint32_t gstep = 16 * Bu * 8;   // next block
-  const uint32_t tstep = 4 * Bu * 8;    // next t chunk
+  const uint32_t wpanel = (gq * 32 + 4 * w) * 16 + lh;
   // Y pieces: id = tid + 512i: q4 = id&3, pl = (id>>2)&31, row = id>>7 (+4i)
   const int yq4 = tid & 3, ypl = (tid >> 2) & 31, yrow = tid >> 7;
   const uint32_t ycol = (32 * ps + ypl) * nb2 + gq * 32 + yq4 * 8;
@@ -285,10 +302,10 @@ __global__ __launch_bounds__(512) void sq_stage2_fwd_kernel(const uint16_t* __re
   auto gload = [&](u32x4(&pre)[4], int64_t c) {
     const int64_t b0 = row0 + (c >> 2) * T;
     const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
-    const uint16_t* base = Wz + (bc + clamp_row(l15, lim)) * 8 + wcol +
-                           static_cast<uint32_t>((c + ps) & 3) * tstep;
+    const PanelRow pr = panel_row(bc + clamp_row(l15, lim), out, Bu);
+    const uint16_t* base = Wz + pr.base + (wpanel + 4 * static_cast<uint32_t>((c + ps) & 3)) * pr.rt8;
 #pragma unroll
-    for (int g = 0; g < 4; ++g) pre[g] = ldg16(base + g * gstep);
+    for (int g = 0; g < 4; ++g) pre[g] = ldg16(base + g * 16 * pr.rt8);   // next block: +16 panels
   };
 
   f32x4 acc[4][2];
@@ -362,8 +379,8 @@ __global__ __launch_bounds__(512) void sq_stage2_fwd_kernel(const uint16_t* __re
 // The inverse stride permutation scatters one L block's outputs with stride
 // b2 through each row of Y, so a kernel owning a few blocks would read dY in
 // short runs. This pass reads dY rows in 256-byte runs (all blocks of 16 p at
-// once), transposes 8x8 bf16 blocks in registers and writes the panel layout
-// ((i/8)*B + b)*8 + i%8, i = g*128 + p, through LDS in 256-byte runs. Both
+// once), transposes 8x8 bf16 blocks in registers and writes dV (feature
+// i = g*128 + p) in the panel layout through LDS in 256-byte runs. Both
 // backward stage-2 kernels then read dV contiguously.
 // Tile: RT = 256/GO rows x 16 p x 8*GO blocks (GO = min(16, b2/8) block
 // octets); 512 threads, one 8x8 block each; one tile per workgroup. The
@@ -406,8 +423,9 @@ __global__ __launch_bounds__(512) void sq_dv_panels_kernel(const uint16_t* __res
     const int r = id % RT, q = (id / RT) & 1, gl = id / (2 * RT);
     const int64_t bb = b0 + r;
     if (bb < B) {
-      const int64_t panel = static_cast<int64_t>(gt * GO * 8 + gl) * 16 + 2 * pt + q;
-      stg16(dV + (panel * B + bb) * 8, st[(gl * 2 + q) * RT + (r ^ (gl >> 3))]);
+      const uint32_t panel = static_cast<uint32_t>(gt * GO * 8 + gl) * 16 + 2 * pt + q;
+      const PanelRow pr = panel_row(bb, out, static_cast<uint32_t>(B));
+      stg16(dV + pr.base + panel * pr.rt8, st[(gl * 2 + q) * RT + (r ^ (gl >> 3))]);
     }
   }
 }
@@ -445,19 +463,20 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_data_kernel(
 #pragma unroll
     for (int ks = 0; ks < 4; ++ks) a[mt][ks] = frag_gather(Lg + (32 * ks + 8 * lh) * Q + 16 * mt + l15);
 
+  const uint32_t F = static_cast<uint32_t>(nb2) * Q;
   // operand pieces: panel g*16 + 4ks + lh, row b0 + l15
-  const uint32_t vcol = ((g * 16 + lh) * Bu) * 8;
-  const uint32_t vstep = 4 * Bu * 8;   // +4 panels (next k step)
-  // dZ pieces: t = (tid>>4) + 32i, row = tid&15
+  const uint32_t vpanel = g * 16 + lh;
+  // dZ pieces: t = (tid>>4) + 32i, row = tid&15; panel (t*b2 + g0)/8
   const int zt = tid >> 4, zrow = tid & 15;
-  const uint32_t zcol = (zt * pstride + gg) * Bu * 8;
-  const uint32_t zstep = 32 * pstride * Bu * 8;
+  const uint32_t zpanel = zt * pstride + gg;
+  const uint32_t zstep = 32 * pstride;   // panels
 
   auto gload = [&](u32x4(&pre)[4], int64_t b0) {
     const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
-    const uint16_t* base = dV + bc * 8 + clamp_row(l15, lim) * 8 + vcol;
+    const PanelRow pr = panel_row(bc + clamp_row(l15, lim), F, Bu);
+    const uint16_t* base = dV + pr.base + vpanel * pr.rt8;
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) pre[ks] = ldg16_nt(base + ks * vstep);
+    for (int ks = 0; ks < 4; ++ks) pre[ks] = ldg16_nt(base + 4 * ks * pr.rt8);   // +4 panels
   };
   auto body = [&](u32x4(&cur)[4], int64_t b0) {
     pin(cur);
@@ -482,10 +501,12 @@ __global__ __launch_bounds__(512) void sq_stage2_bwd_data_kernel(
       }
     __syncthreads();
     const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
-    uint16_t* zb = dZ + bc * 8 + clamp_row(zrow, lim) * 8 + zcol;
+    const PanelRow pr = panel_row(bc + clamp_row(zrow, lim), F, Bu);
+    uint16_t* zb = dZ + pr.base + zpanel * pr.rt8;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
-      stg16_nt(zb + i * zstep, *reinterpret_cast<const u32x4*>(&zs[(zt + 32 * i) * XLD + zrow * 8]));
+      stg16_nt(zb + i * zstep * pr.rt8,
+               *reinterpret_cast<const u32x4*>(&zs[(zt + 32 * i) * XLD + zrow * 8]));
     __syncthreads();
   };
 
@@ -541,14 +562,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void s
   // g*16 + pl (features 8pl ..) of dV or W
   const bool is_w = w >= 2;
   const int lt = tid & 127, rq = lt & 7, pl = lt >> 3;
-  const uint16_t* src = (is_w ? Wz : dV) + static_cast<int64_t>(g * 16 + pl) * B * 8;
+  const uint16_t* src = is_w ? Wz : dV;
+  const uint32_t panel = g * 16 + pl;
+  const uint32_t F = static_cast<uint32_t>(nb2) * Q, Bu = static_cast<uint32_t>(B);
   uint16_t* tdst = &ts[(is_w ? TS : 0) + fl_row(pl * 8) + 4 * rq];
 
   auto gload = [&](u32x4(&pre)[4], int64_t b0) {
     const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
-    const uint16_t* base = src + bc * 8;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pre[i] = ldg16_nt(base + clamp_row(rq + 8 * i, lim) * 8);
+    for (int i = 0; i < 4; ++i) {
+      const PanelRow pr = panel_row(bc + clamp_row(rq + 8 * i, lim), F, Bu);
+      pre[i] = ldg16_nt(src + pr.base + panel * pr.rt8);
+    }
   };
   auto body = [&](u32x4(&pre)[4], int64_t b0) {
     pin(pre);
@@ -643,17 +668,21 @@ __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(4))) void s
   const int lt = tid & 255;
   const int rq = is_x ? lt >> 4 : lt & 15;
   const int oct = is_x ? lt & 15 : lt >> 4;
-  const uint16_t* src = is_x ? X + r * Q + oct * 8 : dZ + static_cast<int64_t>(r * 16 + oct) * B * 8;
-  const uint32_t rstride = is_x ? in : 8u;
+  const uint16_t* src = is_x ? X + r * Q + oct * 8 : dZ;
+  const uint32_t zpanel = r * 16 + oct, Bu = static_cast<uint32_t>(B);
   uint16_t* tdst = &ts[is_x ? 1 : 0][(oct * 8) * PLD + 4 * rq];
   // dX store pieces: seg = tid&15, rows (tid>>4) + 32i
   const int xseg = tid & 15, xrow = tid >> 4;
 
   auto gload = [&](u32x4(&pre)[4], int64_t b0) {
     const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
-    const uint16_t* base = src + bc * rstride;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pre[i] = ldg16_nt(base + clamp_row(rq + 16 * i, lim) * rstride);
+    for (int i = 0; i < 4; ++i) {
+      const int64_t row = bc + clamp_row(rq + 16 * i, lim);
+      const PanelRow pr = panel_row(row, in, Bu);
+      const uint32_t off = is_x ? static_cast<uint32_t>(row) * in : pr.base + zpanel * pr.rt8;
+      pre[i] = ldg16_nt(src + off);
+    }
   };
   auto body = [&](u32x4(&pre)[4], int64_t b0) {
     pin(pre);
