@@ -71,6 +71,24 @@ __device__ __forceinline__ int64_t col_off(int64_t j, int64_t ns, int64_t hi, in
   return ns > 0 ? (j / ns) * hi + (j % ns) * lo : j * lo;
 }
 
+// Keeps the bf16 halves of v whose mask half is > 0 (the ReLU derivative,
+// taken as 0 at 0): sign clear, not zero, not NaN.
+__device__ __forceinline__ u32x4 relu_mask_bf16(u32x4 v, u32x4 m) {
+  u32x4 r;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    uint32_t keep = 0;
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const uint32_t x = (m[i] >> (16 * h)) & 0xffffu;
+      const bool pos = (x & 0x8000u) == 0 && x != 0 && x <= 0x7f80u;
+      keep |= pos ? (0xffffu << (16 * h)) : 0u;
+    }
+    r[i] = v[i] & keep;
+  }
+  return r;
+}
+
 // 4x8 transpose of bf16 in registers: in[i] holds elements (i, e = 0..7);
 // out[e] gets elements (i = 0..3, e) packed into 8 bytes.
 __device__ __forceinline__ void transpose4x8(const u32x4 (&in)[4], u32x2 (&out)[8]) {

@@ -5,11 +5,12 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include "small.h"
 #include "square.h"
 
 namespace monarch {
 
-enum Path { PATH_GENERIC = 0, PATH_SQ128 = 1 };
+enum Path { PATH_GENERIC = 0, PATH_SQ128 = 1, PATH_SM32 = 2 };
 
 struct Problem {
   int64_t in = 0, out = 0, mid = 0, b1 = 0, b2 = 0;
@@ -68,6 +69,8 @@ enum StepKind {
   SQ_STAGE2_BWD_DATA,
   SQ_STAGE2_BWD_WEIGHT,
   SQ_STAGE1_BWD,
+  SM_FWD,
+  SM_BWD_DATA,
 };
 
 struct Plan {

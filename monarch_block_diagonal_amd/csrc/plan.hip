@@ -17,6 +17,11 @@
 // enumerates its output columns of block r as j = g*n1 + tt (k = tt*b2 + g,
 // n1 = q1o/b2), so it writes runs of n1 consecutive elements and stage 2 and
 // the dw2 product read z contiguously.
+//
+// Fused path (bf16, 32 x 32 blocks, at most 1024 features, small.hip): the
+// forward and the data part of the backward are one launch each; the weight
+// gradients are the generic path's batch-split GEMMs on the dV and dZ the
+// fused backward stores.
 #include "kernels.h"
 #include "monarch.h"
 #include "plan.h"
@@ -89,6 +94,8 @@ int make_problem_ex(int64_t in, int64_t out, int64_t mid, int64_t nb1, int64_t n
     p.s2 = p.sq.w2_chunks;
     p.s1 = p.sq.b1_chunks;
   } else {
+    if (batch > 0 && whole && sm_applicable(in, out, nb1, nb2, batch, dtype == MONARCH_BF16))
+      p.path = PATH_SM32;
     choose_splits(p.b2, p.q2o, p.q2i, batch, &p.s2, &p.kc2);
     choose_splits(p.b1, p.q1o, p.q1i, batch, &p.s1, &p.kc1);
   }
@@ -137,6 +144,10 @@ Plan plan_fwd(const Problem& pr) {
     p.add(SQ_STAGE2_FWD);
     return p;
   }
+  if (pr.path == PATH_SM32) {
+    p.add(SM_FWD);
+    return p;
+  }
   p.add(GEN_STAGE1_FWD);
   p.add(GEN_STAGE2_FWD);
   return p;
@@ -153,6 +164,13 @@ Plan plan_bwd(const Problem& pr) {
     p.add(SQ_STAGE2_BWD_DATA);
     p.add(SQ_STAGE2_BWD_WEIGHT);
     p.add(SQ_STAGE1_BWD);
+    p.add(REDUCE_DW);
+    return p;
+  }
+  if (pr.path == PATH_SM32) {
+    p.add(SM_BWD_DATA);
+    p.add(GEN_STAGE2_BWD_WEIGHT);
+    p.add(GEN_STAGE1_BWD_WEIGHT);
     p.add(REDUCE_DW);
     return p;
   }
@@ -184,6 +202,8 @@ const char* step_name(StepKind k) {
     case SQ_STAGE2_BWD_DATA: return "sq128_stage2_bwd_data";
     case SQ_STAGE2_BWD_WEIGHT: return "sq128_stage2_bwd_weight";
     case SQ_STAGE1_BWD: return "sq128_stage1_bwd";
+    case SM_FWD: return "sm32_fwd";
+    case SM_BWD_DATA: return "sm32_bwd_data";
   }
   return "?";
 }
@@ -301,6 +321,11 @@ hipError_t launch_step(StepKind k, const Problem& pr, const Buffers& b, hipStrea
       return sq_launch_stage2_bwd_weight(dv, b.z, p2, pr.batch, pr.b2, pr.sq, s);
     case SQ_STAGE1_BWD:
       return sq_launch_stage1_bwd(dz, b.x, b.w1, b.dx, p1, pr.batch, pr.b1, pr.sq, s);
+    case SM_FWD:
+      return sm_launch_fwd(b.x, b.w1, b.w2, b.y_out, b.z_out, pr.batch, pr.b1,
+                           pr.act == MONARCH_ACT_RELU, s);
+    case SM_BWD_DATA:
+      return sm_launch_bwd_data(b.dy, mask, b.w1, b.w2, b.dx, dv, dz, pr.batch, pr.b1, s);
     case ZERO_DW: {
       hipError_t e = launch_zero(b.dw2, static_cast<size_t>(pr.b2 * pr.q2o * pr.q2i) * pr.esize, s);
       if (e != hipSuccess) return e;

@@ -73,21 +73,6 @@ __device__ __forceinline__ bf16x8 frag_gather(const uint16_t* p) {
 __device__ __forceinline__ f32x4 mfma(bf16x8 a, bf16x8 b, f32x4 c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
-// bf16 bit pattern strictly greater than zero (NaN excluded)
-__device__ __forceinline__ bool bf16_pos(uint32_t h) {
-  return (h & 0x8000u) == 0 && (h & 0x7fffu) != 0 && (h & 0x7fffu) <= 0x7f80u;
-}
-// zero the halves of v whose mask half is not > 0 (ReLU derivative)
-__device__ __forceinline__ u32x4 apply_mask(u32x4 v, u32x4 m) {
-  u32x4 r;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    uint32_t keep = (bf16_pos(m[i] & 0xffffu) ? 0xffffu : 0u) |
-                    (bf16_pos(m[i] >> 16) ? 0xffff0000u : 0u);
-    r[i] = v[i] & keep;
-  }
-  return r;
-}
 // workgroups are dispatched round-robin over the 8 XCDs: give consecutive
 // logical ids to one XCD
 __device__ __forceinline__ int xcd_logical(int bid, int grid) {
@@ -409,7 +394,7 @@ __global__ __launch_bounds__(512) void sq_dv_panels_kernel(const uint16_t* __res
   for (int i = 0; i < 8; ++i) in[i] = ldg16_nt(dY + src + i * nb2);
   if (Ym) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) in[i] = apply_mask(in[i], ldg16_nt(Ym + src + i * nb2));
+    for (int i = 0; i < 8; ++i) in[i] = relu_mask_bf16(in[i], ldg16_nt(Ym + src + i * nb2));
   }
   u32x2 lo[8], hi[8];
   transpose4x8(*reinterpret_cast<const u32x4(*)[4]>(&in[0]), lo);

@@ -348,24 +348,14 @@ __global__ __launch_bounds__(TT) void tiled_gemm_kernel(GemmArgs p, int64_t m_ti
 // keep v where m > 0 (ReLU derivative), element-wise on a 16-byte piece
 template <typename T>
 __device__ __forceinline__ u32x4 mask_piece(u32x4 v, u32x4 m) {
-  u32x4 r;
+  if constexpr (std::is_same<T, uint16_t>::value) {
+    return relu_mask_bf16(v, m);
+  } else {
+    u32x4 r;
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if constexpr (std::is_same<T, uint16_t>::value) {
-      uint32_t keep = 0;
-#pragma unroll
-      for (int h = 0; h < 2; ++h) {
-        const uint32_t x = (m[i] >> (16 * h)) & 0xffffu;
-        // bf16 > 0: sign clear, not zero, not NaN
-        const bool pos = (x & 0x8000u) == 0 && x != 0 && x <= 0x7f80u;
-        keep |= pos ? (0xffffu << (16 * h)) : 0u;
-      }
-      r[i] = v[i] & keep;
-    } else {
-      r[i] = __uint_as_float(m[i]) > 0.f ? v[i] : 0u;
-    }
+    for (int i = 0; i < 4; ++i) r[i] = __uint_as_float(m[i]) > 0.f ? v[i] : 0u;
+    return r;
   }
-  return r;
 }
 
 // dV rows from dY rows through LDS: each workgroup takes rpw whole rows,

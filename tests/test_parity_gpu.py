@@ -301,6 +301,11 @@ SHAPES = [
     (8192, 8192, 64, 64, 77),
     (16384, 16384, 128, 128, 1000),
     (16384, 16384, 128, 128, 17),
+    # 32x32 blocks, 8, 16 or 32 of them: the fused bf16 path
+    (256, 256, 8, 8, 77),
+    (512, 512, 16, 16, 130),
+    (1024, 1024, 32, 32, 1),
+    (1024, 1024, 32, 32, 4113),
     # 128x128 blocks, fewer blocks: generic path
     (1024, 1024, 8, 8, 77),
     (2048, 2048, 16, 16, 129),
@@ -322,7 +327,8 @@ def test_shapes(api, shape, dtype):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("shape", [(256, 256, 16, 16, 300), (96, 160, 4, 8, 50),
                                    (16384, 16384, 128, 128, 64), (1024, 512, 16, 16, 100),
-                                   (2048, 2048, 16, 16, 45), (4096, 4096, 32, 32, 45)],
+                                   (2048, 2048, 16, 16, 45), (4096, 4096, 32, 32, 45),
+                                   (512, 512, 16, 16, 50), (1024, 1024, 32, 32, 129)],
                          ids=lambda s: "x".join(map(str, s)))
 def test_shapes_relu(api, shape, dtype):
     inp, out, b1, b2, batch = shape
@@ -337,7 +343,7 @@ def test_shapes_relu(api, shape, dtype):
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("shape", [(16, 16, 4, 4, 8), (1024, 1024, 32, 32, 300),
                                    (16384, 16384, 128, 128, 64), (256, 256, 16, 16, 100),
-                                   (4096, 4096, 32, 32, 33),
+                                   (4096, 4096, 32, 32, 33), (512, 512, 16, 16, 70),
                                    (48, 96, 2, 4, 10)], ids=lambda s: "x".join(map(str, s)))
 def test_permutation_blocks_bit_exact(api, shape, dtype):
     """0/1 blocks (identity and cyclic shifts) make M a permutation matrix:
