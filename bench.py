@@ -3,10 +3,13 @@
 
 One step = monarch_fwd + monarch_bwd (the whole hot path) over one batch of
 synthetic inputs already resident in HBM. Prints one JSON line with the
-throughput (Monarch algorithmic TFLOP/s = 6*batch*params per step), the
-roofline of the dominant kernel (timed with HIP events recorded between the
-library's kernels on the launch stream, over the timed region), the dense
-bf16 GEMM of the same shape and the fp64 CPU oracle timed on a bounded sample.
+throughput (Monarch algorithmic TFLOP/s = 6*batch*params per step, timed
+over eager steps with no events between kernels), the roofline of the
+dominant kernel (timed with HIP events recorded between the library's
+kernels on the launch stream, over a second run of the same steps), the step
+replayed from a HIP graph (checked bit for bit against the eager step), the
+dense bf16 GEMM of the same shape and the fp64 CPU oracle timed on a bounded
+sample.
 """
 from __future__ import annotations
 
@@ -435,6 +438,8 @@ def main() -> int:
     ap.add_argument("--cpu-rows", type=int, default=0, help="oracle sample rows (0: auto)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the HIP-graph replay of the step")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 1 GiB device copy (read 1 GiB + write 1 GiB), the "
                          "reference for scaling HBM byte counters")
@@ -524,14 +529,17 @@ def main() -> int:
                                                         dt_code, l.bias))
         L.append(d)
     ws = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
+
+    def strm():
+        # looked up per call, so that a graph capture sees its capture stream
+        return torch.cuda.current_stream()
 
     def fwd(evs=None):
         for li, d in enumerate(L):
             l = d["l"]
             M.monarch_fwd_ex(d["x"], d["w1"], d["w2"], d["bias"], d["y"], d["z"], d["fi"],
                              d["fo"], d["mid"], l.nblocks1, l.nblocks2, B, dt_code, d["act"],
-                             stream, events=None if evs is None else evs[li])
+                             strm(), events=None if evs is None else evs[li])
 
     def bwd(evs=None):
         g = dy
@@ -540,7 +548,7 @@ def main() -> int:
             M.monarch_bwd_ex(g, d["x"], d["w1"], d["w2"], d["z"],
                              d["y"] if d["act"] == M.ACT_RELU else None, d["dx"], d["dw1"],
                              d["dw2"], d["db"], ws, wsb, d["fi"], d["fo"], d["mid"], l.nblocks1,
-                             l.nblocks2, B, dt_code, d["act"], stream,
+                             l.nblocks2, B, dt_code, d["act"], strm(),
                              events=None if evs is None else evs[li])
             g = d["dx"]
 
@@ -558,18 +566,67 @@ def main() -> int:
         return [torch.cuda.Event(enable_timing=True) for _ in range(n)]
 
     K = args.steps
-    evf = [[new_events(len(d["fn"]) + 1) for d in L] for _ in range(K)]
-    evb = [[new_events(len(d["bn"]) + 1) for d in L] for _ in range(K)]
+    stream = strm()
+    # timed steps: no events between kernels, one pair around each step
     log(f"timing {K} fwd+bwd steps")
+    evs_s = new_events(K + 1)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for k in range(K):
-        step(evf[k], evb[k])
+        evs_s[k].record(stream)
+        step()
+    evs_s[K].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_per_step = wall * 1e3 / K
-    # per-step device times: first forward event to last backward event
-    step_ms = sorted(evf[k][0][0].elapsed_time(evb[k][0][-1]) for k in range(K))
+    step_ms = sorted(evs_s[k].elapsed_time(evs_s[k + 1]) for k in range(K))
+
+    # per-kernel times: the same steps again with an event between kernels
+    log(f"timing {K} fwd+bwd steps kernel by kernel")
+    evf = [[new_events(len(d["fn"]) + 1) for d in L] for _ in range(K)]
+    evb = [[new_events(len(d["bn"]) + 1) for d in L] for _ in range(K)]
+    for k in range(K):
+        step(evf[k], evb[k])
+    torch.cuda.synchronize()
+
+    # the whole step captured once as a HIP graph and replayed: the same
+    # kernels with the host launch path taken out; the replay's results must
+    # equal the eager step's bit for bit
+    graph = None
+    if not args.no_graph:
+        log(f"timing {K} fwd+bwd steps replayed from a HIP graph")
+        outs = [d["dx"] for d in L] + [d["dw1"] for d in L] + [d["dw2"] for d in L] + [L[-1]["y"]]
+        step()
+        torch.cuda.synchronize()
+        ref = [t.clone() for t in outs]
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            step()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            step()
+        for t in outs:
+            t.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        same = all(torch.equal(a, b) for a, b in zip(outs, ref))
+        evs_g = new_events(K + 1)
+        t0 = time.perf_counter()
+        for k in range(K):
+            evs_g[k].record(stream)
+            g.replay()
+        evs_g[K].record(stream)
+        torch.cuda.synchronize()
+        g_wall = (time.perf_counter() - t0) * 1e3 / K
+        g_ms = sorted(evs_g[k].elapsed_time(evs_g[k + 1]) for k in range(K))
+        graph = {"ms_per_step": round(g_wall, 4),
+                 "step_ms_p50": round(g_ms[len(g_ms) // 2], 4),
+                 "value": round(6.0 * B * w.params / (g_wall * 1e-3) / 1e12, 2),
+                 "replay_equals_eager": same}
+        del g, ref
 
     def pct(v, q):
         return v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
@@ -671,6 +728,25 @@ def main() -> int:
         dense = {"dtype": w.dtype, "ms_per_step": round(dense_ms, 4),
                  "tflops": round(dflops / (dense_ms * 1e-3) / 1e12, 1),
                  "speedup_monarch_vs_dense": round(dense_ms / ms_per_step, 3)}
+        if graph is not None:
+            side = torch.cuda.Stream()
+            side.wait_stream(torch.cuda.current_stream())
+            with torch.cuda.stream(side):
+                dense_step()
+            torch.cuda.current_stream().wait_stream(side)
+            gd = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gd):
+                dense_step()
+            gd.replay()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(reps):
+                gd.replay()
+            torch.cuda.synchronize()
+            dg_ms = (time.perf_counter() - t0) * 1e3 / reps
+            dense["graph_ms_per_step"] = round(dg_ms, 4)
+            graph["speedup_monarch_vs_dense"] = round(dg_ms / graph["ms_per_step"], 3)
+            del gd
         del Wd
 
     cpu = None
@@ -705,6 +781,7 @@ def main() -> int:
         "fwd_ms_p10_p50_p90": [round(pct(fwd_ms, q), 4) for q in (0.1, 0.5, 0.9)],
         "fwd_tflops": round(2.0 * B * w.params / (pct(fwd_ms, 0.5) * 1e-3) / 1e12, 2),
         "step_roofline": step_roofline,
+        "graph": graph,
         "kernels_ms": {k: round(v, 4) for k, v in per_kernel.items()},
         "roofline": roofline,
         "dense_baseline": dense,

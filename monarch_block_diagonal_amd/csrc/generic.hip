@@ -27,8 +27,17 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(ReduceArgs a, Redu
     const int64_t n = in_a ? a.n : (in_b ? b.n : c.n);
     const int64_t splits = in_a ? a.splits : (in_b ? b.splits : c.splits);
     const int64_t i = in_a ? e : (in_b ? e - a.n : e - a.n - b.n);
+    // eight chunks' loads in flight, added in chunk order
     float s = 0.f;
-    for (int64_t k = 0; k < splits; ++k) s += part[k * n + i];
+    int64_t k = 0;
+    for (; k + 8 <= splits; k += 8) {
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = part[(k + j) * n + i];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s += v[j];
+    }
+    for (; k < splits; ++k) s += part[k * n + i];
     Io<T>::store(out, i, s);
   }
 }
