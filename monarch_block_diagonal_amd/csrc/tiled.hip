@@ -36,9 +36,10 @@ struct Cfg {
   static constexpr int VEC = 16 / static_cast<int>(sizeof(T));  // elements per 16-byte piece
   static constexpr int TK = kBf16 ? 64 : 32;                     // K step
   static constexpr int LD = TK + VEC;                             // LDS row pitch (elements)
-  // LDS offset of tile row r: pitch plus a 16-byte skew per 8 rows, which
-  // spreads the transposed stores and the fragment reads over the banks
-  static __device__ __host__ constexpr int rowoff(int r) { return r * LD + (r >> 3) * VEC; }
+  // LDS offset of tile row r: a 144-byte pitch puts the 16 rows of a
+  // fragment read on distinct bank groups, and a 16-byte skew per 16 rows
+  // does the same for the transposed stores (rows 8 apart)
+  static __device__ __host__ constexpr int rowoff(int r) { return r * LD + (r >> 4) * VEC; }
 };
 
 __device__ __forceinline__ void pin(u32x4& v) { asm volatile("" : "+v"(v)); }
@@ -54,7 +55,7 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *static_cast<const
 // or the K range are loaded from a clamped in-range address and stored as
 // zeros. An operand row sits at base + (r / ns)*hi + (r % ns)*lo (ns > 0,
 // mode 1 only) or base + r*lo; `sk` is the K stride.
-template <typename T, int MODE, int ROWS, bool EW>
+template <typename T, int MODE, int ROWS, bool EW, int SLOTS>
 struct Tile {
   using C = Cfg<T>;
   static constexpr int VEC = C::VEC, TK = C::TK;
@@ -69,7 +70,7 @@ struct Tile {
   int eclamp[NU];     // mode 2: largest row offset loads may use
   int64_t lo, sk, kb, ke;
   bool vec_;
-  u32x4 reg[NR];
+  u32x4 reg[SLOTS][NR];   // K tiles in flight
 
   // without EW every operand of the launch moves as 16-byte pieces
   __device__ __forceinline__ bool vec() const { return EW ? vec_ : true; }
@@ -114,6 +115,7 @@ struct Tile {
     }
   }
 
+  template <int S>
   __device__ __forceinline__ void load(int64_t k0) {
 #pragma unroll
     for (int q = 0; q < NU; ++q) {
@@ -123,7 +125,7 @@ struct Tile {
         if (vec()) {
           int64_t gk = k0 + k;
           gk = gk < ke ? gk : kb;
-          reg[q] = ld16(row[q] + gk);
+          reg[S][q] = ld16(row[q] + gk);
         } else {
           T v[VEC];
 #pragma unroll
@@ -132,7 +134,7 @@ struct Tile {
             gk = gk < ke ? gk : ke - 1;
             v[e] = row[q][gk * sk];
           }
-          reg[q] = pack(v);
+          reg[S][q] = pack(v);
         }
       } else {
 #pragma unroll
@@ -140,12 +142,12 @@ struct Tile {
           int64_t gk = k0 + k + i;
           gk = gk < ke ? gk : ke - 1;
           if (vec()) {
-            reg[4 * q + i] = ld16(row[q] + gk * sk);
+            reg[S][4 * q + i] = ld16(row[q] + gk * sk);
           } else {
             T v[VEC];
 #pragma unroll
             for (int e = 0; e < VEC; ++e) v[e] = row[q][(e < eclamp[q] ? e : eclamp[q]) * lo + gk * sk];
-            reg[4 * q + i] = pack(v);
+            reg[S][4 * q + i] = pack(v);
           }
         }
       }
@@ -165,31 +167,32 @@ struct Tile {
     return pack(el);
   }
 
+  template <int S>
   __device__ __forceinline__ void store(T* s, int64_t k0) {
 #pragma unroll
     for (int q = 0; q < NU; ++q) {
       if (!active(q)) continue;
       const int r = unit_row(q), k = unit_k(q);
       if constexpr (MODE == 1) {
-        pin(reg[q]);
+        pin(reg[S][q]);
         u32x4 v;
         if (vec()) {
           const bool keep = nrow[q] > 0 && k0 + k < ke;
-          v = keep ? reg[q] : u32x4{0u, 0u, 0u, 0u};
+          v = keep ? reg[S][q] : u32x4{0u, 0u, 0u, 0u};
         } else {
-          v = mask_elems(reg[q], nrow[q], true, k0 + k, ke);
+          v = mask_elems(reg[S][q], nrow[q], true, k0 + k, ke);
         }
         *reinterpret_cast<u32x4*>(s + C::rowoff(r) + k) = v;
       } else {
         u32x4 v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          pin(reg[4 * q + i]);
+          pin(reg[S][4 * q + i]);
           const bool kok = k0 + k + i < ke;
           if (vec())
-            v[i] = (nrow[q] > 0 && kok) ? reg[4 * q + i] : u32x4{0u, 0u, 0u, 0u};
+            v[i] = (nrow[q] > 0 && kok) ? reg[S][4 * q + i] : u32x4{0u, 0u, 0u, 0u};
           else
-            v[i] = mask_elems(reg[4 * q + i], nrow[q], kok, 0, 0);
+            v[i] = mask_elems(reg[S][4 * q + i], nrow[q], kok, 0, 0);
         }
         if constexpr (C::kBf16) {
           u32x2 tr[8];
@@ -209,15 +212,22 @@ struct Tile {
   }
 };
 
+// K tiles kept in flight in registers: two, or one for the 256-row tiles,
+// whose A tile alone takes as many registers as two slots of the others.
+template <int TM>
+constexpr int kSlots = TM > 128 ? 1 : 2;
+
 template <typename T, int AM, int BMD, int WM, int WN, int FM, int FN, bool EW>
-__global__ __launch_bounds__(TT) void tiled_gemm_kernel(GemmArgs p, int64_t m_tiles,
+__global__ __launch_bounds__(TT) __attribute__((amdgpu_waves_per_eu(2)))
+void tiled_gemm_kernel(GemmArgs p, int64_t m_tiles,
                                                         int64_t n_tiles, int remap, int avec,
                                                         int bvec) {
   using C = Cfg<T>;
   constexpr int TM = WM * FM * 16, TN = WN * FN * 16, TK = C::TK;
   static_assert(WM * WN == 4, "four waves");
-  using TA = Tile<T, AM, TM, EW>;
-  using TB = Tile<T, BMD, TN, EW>;
+  constexpr int SL = kSlots<TM>;
+  using TA = Tile<T, AM, TM, EW, SL>;
+  using TB = Tile<T, BMD, TN, EW, SL>;
   __shared__ __attribute__((aligned(16))) T As[TA::LDS];
   __shared__ __attribute__((aligned(16))) T Bs[TB::LDS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -260,17 +270,28 @@ __global__ __launch_bounds__(TT) void tiled_gemm_kernel(GemmArgs p, int64_t m_ti
 #pragma unroll
     for (int ni = 0; ni < FN; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  if (kb < ke) {
-    a.load(kb);
-    b.load(kb);
+  // K tile t is loaded into register slot t % SL, SL tiles ahead of its
+  // use: step t stores slot t % SL to LDS, then reloads it with tile t + SL
+  const int64_t nsteps = kb < ke ? (ke - kb + TK - 1) / TK : 0;
+  if (nsteps > 0) {
+    a.template load<0>(kb);
+    b.template load<0>(kb);
   }
-  for (int64_t k0 = kb; k0 < ke; k0 += TK) {
-    a.store(As, k0);
-    b.store(Bs, k0);
+  if constexpr (SL > 1) {
+    if (nsteps > 1) {
+      a.template load<SL - 1>(kb + TK);
+      b.template load<SL - 1>(kb + TK);
+    }
+  }
+  auto step = [&](auto slot, int64_t t) {
+    constexpr int S = decltype(slot)::value;
+    const int64_t k0 = kb + t * TK;
+    a.template store<S>(As, k0);
+    b.template store<S>(Bs, k0);
     __syncthreads();
-    if (k0 + TK < ke) {
-      a.load(k0 + TK);
-      b.load(k0 + TK);
+    if (t + SL < nsteps) {
+      a.template load<S>(k0 + SL * TK);
+      b.template load<S>(k0 + SL * TK);
     }
     if constexpr (C::kBf16) {
 #pragma unroll
@@ -313,6 +334,12 @@ __global__ __launch_bounds__(TT) void tiled_gemm_kernel(GemmArgs p, int64_t m_ti
       }
     }
     __syncthreads();
+  };
+  for (int64_t t = 0; t < nsteps; t += SL) {
+    step(std::integral_constant<int, 0>{}, t);
+    if constexpr (SL > 1) {
+      if (t + 1 < nsteps) step(std::integral_constant<int, SL - 1>{}, t + 1);
+    }
   }
 
   // 16x16 result layout: lane holds rows 4*(lane/16)+v, column lane%16
