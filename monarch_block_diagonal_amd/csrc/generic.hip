@@ -1,6 +1,6 @@
 // Small helper kernels of the Monarch library (gfx950): the fixed-order
-// reduction of batch-split gradient partial sums, a per-row transpose and a
-// zero fill.
+// reduction of batch-split gradient partial sums, axis swaps of batches of
+// 3-D arrays and a zero fill.
 //
 // The weight gradients of both block-diagonal factors are sums over the
 // batch (each block's gradient is its output gradient transposed times its
@@ -42,29 +42,94 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(ReduceArgs a, Redu
   }
 }
 
-// 32 x 32 tiles through LDS: reads and writes run along rows of 32.
+// Axis swaps out[b][c][m][a] = in[b][a][m][c] of batches of A x M x C
+// arrays (the transposes and the layout changes between the rounds of the
+// k-factor layer).
+//
+// Whole arrays through LDS (A*M*C elements fit): the array is read with
+// 16-byte pieces and written as runs of consecutive a, 16-byte pieces when
+// A allows, so both sides move whole lines however small A, M and C are.
+// The LDS copy has one pad word per 64 words: the reads of a piece's
+// elements step by M*C elements, which is often a multiple of 256 bytes.
 template <typename T>
-__global__ __launch_bounds__(256) void row_transpose_kernel(const T* __restrict__ in,
-                                                            T* __restrict__ out, int64_t R,
-                                                            int64_t C, int64_t tiles_r,
-                                                            int64_t tiles_c) {
+__device__ __forceinline__ int swap_pos(int i) {
+  constexpr int EPW = 4 / sizeof(T);   // elements per 4-byte word
+  return i + (i / (64 * EPW)) * EPW;
+}
+template <typename T>
+constexpr int swap_lds_elems(int n) {
+  return n + (n / (64 * (4 / static_cast<int>(sizeof(T)))) + 1) * (4 / static_cast<int>(sizeof(T)));
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void swap_lds_kernel(const T* __restrict__ in,
+                                                      T* __restrict__ out, int A, int M, int C,
+                                                      int vec) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  T* s = reinterpret_cast<T*>(smem);
+  constexpr int V = 16 / sizeof(T);
+  const int n = A * M * C;
+  const int64_t base = static_cast<int64_t>(blockIdx.x) * n;
+  const T* src = in + base;
+  T* dst = out + base;
+  const int tid = threadIdx.x;
+  if (vec) {
+    // a piece never straddles a pad (64*EPW is a multiple of V); its words
+    // are stored one by one (the padded position is only word-aligned)
+    for (int q = tid; q < n / V; q += 256) {
+      const u32x4 v = reinterpret_cast<const u32x4*>(src)[q];
+      uint32_t* w = reinterpret_cast<uint32_t*>(s + swap_pos<T>(q * V));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) w[e] = v[e];
+    }
+  } else {
+    for (int i = tid; i < n; i += 256) s[swap_pos<T>(i)] = src[i];
+  }
+  __syncthreads();
+  if (vec) {
+    // output piece o = V consecutive a of one (c, m)
+    for (int q = tid; q < n / V; q += 256) {
+      const int o = q * V, a0 = o % A, cm = o / A, m = cm % M, c = cm / M;
+      T v[V];
+#pragma unroll
+      for (int e = 0; e < V; ++e) v[e] = s[swap_pos<T>(((a0 + e) * M + m) * C + c)];
+      u32x4 r;
+      __builtin_memcpy(&r, v, sizeof(r));
+      reinterpret_cast<u32x4*>(dst)[q] = r;
+    }
+  } else {
+    for (int o = tid; o < n; o += 256) {
+      const int a = o % A, cm = o / A, m = cm % M, c = cm / M;
+      dst[o] = s[swap_pos<T>((a * M + m) * C + c)];
+    }
+  }
+}
+
+// Larger arrays: 32 x 32 (a, c) tiles of one (b, m) through LDS; reads run
+// along c and writes along a.
+template <typename T>
+__global__ __launch_bounds__(256) void swap_tiled_kernel(const T* __restrict__ in,
+                                                        T* __restrict__ out, int64_t A, int64_t M,
+                                                        int64_t C, int64_t tiles_a,
+                                                        int64_t tiles_c) {
   __shared__ T t[32][33];
   int64_t bid = blockIdx.x;
-  const int64_t tcol = bid % tiles_c;
+  const int64_t tc = bid % tiles_c;
   bid /= tiles_c;
-  const int64_t trow = bid % tiles_r;
-  const int64_t b = bid / tiles_r;
-  const T* src = in + b * R * C;
-  T* dst = out + b * R * C;
+  const int64_t ta = bid % tiles_a;
+  bid /= tiles_a;
+  const int64_t m = bid % M, b = bid / M;
+  const T* src = in + b * A * M * C + m * C;    // (a, c) at a*M*C + c
+  T* dst = out + b * A * M * C + m * A;         // (c, a) at c*M*A + a
   const int tx = threadIdx.x & 31, ty = threadIdx.x >> 5;
   for (int i = ty; i < 32; i += 8) {
-    const int64_t r = trow * 32 + i, c = tcol * 32 + tx;
-    if (r < R && c < C) t[i][tx] = src[r * C + c];
+    const int64_t a = ta * 32 + i, c = tc * 32 + tx;
+    if (a < A && c < C) t[i][tx] = src[a * M * C + c];
   }
   __syncthreads();
   for (int i = ty; i < 32; i += 8) {
-    const int64_t c = tcol * 32 + i, r = trow * 32 + tx;
-    if (c < C && r < R) dst[c * R + r] = t[tx][i];
+    const int64_t c = tc * 32 + i, a = ta * 32 + tx;
+    if (c < C && a < A) dst[c * M * A + a] = t[tx][i];
   }
 }
 
@@ -86,19 +151,40 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_row_transpose(const void* in, void* out, int64_t rows, int64_t R, int64_t C,
-                                bool bf16, hipStream_t s) {
-  if (rows <= 0 || R <= 0 || C <= 0) return hipSuccess;
-  const int64_t tr = (R + 31) / 32, tc = (C + 31) / 32;
-  const int64_t grid = rows * tr * tc;
+hipError_t launch_swap(const void* in, void* out, int64_t rows, int64_t A, int64_t M, int64_t C,
+                       bool bf16, hipStream_t s) {
+  if (rows <= 0 || A <= 0 || M <= 0 || C <= 0) return hipSuccess;
+  const int64_t esz = bf16 ? 2 : 4, V = 16 / esz, n = A * M * C;
+  constexpr int64_t kLds = 49 * 1024;
+  const int64_t lds_elems =
+      n < (int64_t(1) << 20) ? (bf16 ? swap_lds_elems<uint16_t>(static_cast<int>(n))
+                                     : swap_lds_elems<float>(static_cast<int>(n)))
+                             : n;
+  if (lds_elems * esz <= kLds && rows <= 0x7fffffffLL) {
+    const int vec = n % V == 0 && A % V == 0 ? 1 : 0;
+    const size_t lds = static_cast<size_t>(lds_elems * esz);
+    const dim3 g(static_cast<unsigned>(rows));
+    if (bf16)
+      hipLaunchKernelGGL(swap_lds_kernel<uint16_t>, g, dim3(256), lds, s,
+                         static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out),
+                         static_cast<int>(A), static_cast<int>(M), static_cast<int>(C), vec);
+    else
+      hipLaunchKernelGGL(swap_lds_kernel<float>, g, dim3(256), lds, s,
+                         static_cast<const float*>(in), static_cast<float*>(out),
+                         static_cast<int>(A), static_cast<int>(M), static_cast<int>(C), vec);
+    return hipGetLastError();
+  }
+  const int64_t ta = (A + 31) / 32, tc = (C + 31) / 32;
+  const int64_t grid = rows * M * ta * tc;
   if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
   if (bf16)
-    hipLaunchKernelGGL(row_transpose_kernel<uint16_t>, dim3(static_cast<unsigned>(grid)), dim3(256),
-                       0, s, static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), R, C,
-                       tr, tc);
+    hipLaunchKernelGGL(swap_tiled_kernel<uint16_t>, dim3(static_cast<unsigned>(grid)), dim3(256),
+                       0, s, static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), A, M,
+                       C, ta, tc);
   else
-    hipLaunchKernelGGL(row_transpose_kernel<float>, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
-                       s, static_cast<const float*>(in), static_cast<float*>(out), R, C, tr, tc);
+    hipLaunchKernelGGL(swap_tiled_kernel<float>, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
+                       s, static_cast<const float*>(in), static_cast<float*>(out), A, M, C, ta,
+                       tc);
   return hipGetLastError();
 }
 

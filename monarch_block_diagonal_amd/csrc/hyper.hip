@@ -7,15 +7,19 @@
 // fiber of its axis. Layouts: L_j denotes the lattice with axis j moved to
 // the end (the other axes in order), so a fiber of round j is a contiguous
 // run of n_j elements and the fiber index equals the weight index; L_{k-1} is
-// the natural row-major layout. The forward first transposes x into L_0 (each
-// row is an n_0 x N/n_0 matrix); round j reads its input in L_j and writes
-// its output in L_{j+1} through a mixed-radix block offset; the last round
-// writes y in natural order. It keeps x in L_0 and the outputs of rounds
-// 0..k-2 (k saved tensors). The backward walks the rounds in reverse: the
-// weight gradient of round j sums g_{j+1}[fiber]ᵀ · input_j[fiber] over the
-// batch (split in chunks, summed in a fixed order), and the data gradient
-// g_j = F_jᵀ g_{j+1} is written in L_{j-1}; g_0, in L_0, is transposed back
-// into dx. A one-dimensional lattice needs no transposes.
+// the natural row-major layout. A round reads and writes L_j, and an axis
+// swap moves the result on: L_j = [pre][n_{j+1}][mid][n_j] and L_{j+1} =
+// [pre][n_j][mid][n_{j+1}] (pre = axes before j, mid = axes after j+1), so
+// the change is the swap of the outer and inner axis of [n_{j+1}][mid][n_j],
+// a pass at copy speed where writing L_{j+1} from the GEMM would scatter
+// every element. The forward transposes x into L_0, runs round j into y
+// (scratch until the last round) and swaps it into the saved slot j + 1; it
+// keeps x in L_0 and the inputs of rounds 1..k-1 (k saved tensors). The
+// backward walks the rounds in reverse: the weight gradient of round j sums
+// g_{j+1}[fiber]ᵀ · input_j[fiber] over the batch (split in chunks, summed in
+// a fixed order), and the data gradient g_j = F_jᵀ g_{j+1}, written in L_j,
+// is swapped into L_{j-1}; g_0 is transposed back into dx. A one-dimensional
+// lattice needs no layout change.
 #include "hyper.h"
 #include "monarch.h"
 
@@ -54,20 +58,17 @@ int64_t prod(const int64_t* d, int lo, int hi) {
   return p;
 }
 
-// output of forward round j (j < k-1) in layout L_{j+1}
-void set_out_next(GemmArgs& a, const HyperProblem& hp, int j) {
-  const int64_t R = prod(hp.dims, j + 2, hp.k), nn = hp.dims[j + 1];
-  a.cb_r0 = R, a.cb_r1 = nn;
-  a.cb_s0 = nn, a.cb_s1 = 1, a.cb_s2 = hp.dims[j] * nn * R;
-  a.c_sj = R * nn;
-}
-
-// data gradient of round j (j > 0) in layout L_{j-1}
-void set_out_prev(GemmArgs& a, const HyperProblem& hp, int j) {
-  const int64_t R = prod(hp.dims, j + 1, hp.k), np = hp.dims[j - 1];
-  a.cb_r0 = R, a.cb_r1 = np;
-  a.cb_s0 = np, a.cb_s1 = 1, a.cb_s2 = hp.dims[j] * R * np;
-  a.c_sj = R * np;
+// the axis swap L_j -> L_{j+1} (up = true) or L_j -> L_{j-1} (up = false)
+void set_swap(SeqStep& st, const HyperProblem& hp, int j, bool up, const void* in, void* out) {
+  const int lo = up ? j : j - 1;   // the swap exchanges axes lo and lo + 1
+  st.kind = SEQ_SWAP;
+  st.name = "hyper_permute";
+  st.t_in = in, st.t_out = out;
+  st.t_rows = hp.batch * prod(hp.dims, 0, lo);
+  st.t_M = prod(hp.dims, lo + 2, hp.k);
+  // L_lo = [pre][n_{lo+1}][mid][n_lo], L_{lo+1} = [pre][n_lo][mid][n_{lo+1}]
+  st.t_A = up ? hp.dims[lo + 1] : hp.dims[lo];
+  st.t_C = up ? hp.dims[lo] : hp.dims[lo + 1];
 }
 
 }  // namespace
@@ -113,15 +114,15 @@ int hyper_plan_fwd(const HyperProblem& hp, const HyperBuffers& b, SeqStep* steps
   if (hp.batch == 0) return 0;
   const int k = hp.k;
   const int64_t BN = hp.batch * hp.N;
-  // saved slot s: slot 0 = x in L_0, slot j + 1 = output of round j
+  // saved slot j: the input of round j in L_j (slot 0 = x)
   auto slot = [&](int sidx) { return static_cast<char*>(b.saved) + sidx * BN * hp.esize; };
   int ns = 0;
   if (k > 1) {
     SeqStep& st = steps[ns++];
-    st.kind = SEQ_TRANSPOSE;
+    st.kind = SEQ_SWAP;
     st.name = "hyper_transpose";
     st.t_in = b.x, st.t_out = slot(0);
-    st.t_rows = hp.batch, st.t_R = hp.dims[0], st.t_C = hp.N / hp.dims[0];
+    st.t_rows = hp.batch, st.t_A = hp.dims[0], st.t_M = 1, st.t_C = hp.N / hp.dims[0];
   }
   for (int j = 0; j < k; ++j) {
     const int64_t n = hp.dims[j];
@@ -130,19 +131,13 @@ int hyper_plan_fwd(const HyperProblem& hp, const HyperBuffers& b, SeqStep* steps
     st.name = "hyper_round_fwd";
     GemmArgs& a = st.g;
     a.A = k > 1 ? static_cast<const void*>(slot(j)) : b.x;   // L_j
-    a.a_sb = n, a.a_sk = 1;
-    a.a_si = hp.N;
+    a.a_sb = n, a.a_sk = 1, a.a_si = hp.N;
     a.B = b.w[j];
     a.b_sb = n * n, a.b_sk = 1, a.b_sj = n;
-    a.c_si = hp.N;
-    if (j == k - 1) {
-      a.C = b.y;
-      a.c_sb = n, a.c_sj = 1;                          // natural = L_{k-1}
-    } else {
-      a.C = slot(j + 1);
-      set_out_next(a, hp, j);
-    }
+    a.C = b.y;                                                // L_j
+    a.c_sb = n, a.c_sj = 1, a.c_si = hp.N;
     a.M = hp.batch, a.N = n, a.K = n, a.nblk = hp.N / n;
+    if (j < k - 1) set_swap(steps[ns++], hp, j, true, b.y, slot(j + 1));
   }
   return ns;
 }
@@ -166,10 +161,14 @@ int hyper_plan_bwd(const HyperProblem& hp, const HyperBuffers& b, SeqStep* steps
   // input of round j in L_j: the saved copies (slot j), or x itself when the
   // lattice has one dimension
   auto input = [&](int j) -> const void* { return k > 1 ? saved + j * BN * hp.esize : b.x; };
+  // g_{j+1} (gradient w.r.t. round j's output, in L_j) is dy for the last
+  // round, else buffer 1; round j's data gradient goes to buffer 0 (in L_j)
+  // and is swapped into buffer 1 (in L_{j-1})
+  void* g0 = ws + hp.ws_g[0];
+  void* g1 = ws + hp.ws_g[1];
   for (int j = k - 1; j >= 0; --j) {
     const int64_t n = hp.dims[j], nf = hp.N / n;
-    // gradient w.r.t. round j's output, in L_j
-    const void* g = j == k - 1 ? b.dy : ws + hp.ws_g[(k - 2 - j) & 1];
+    const void* g = j == k - 1 ? b.dy : g1;
     {
       SeqStep& st = steps[ns++];
       st.kind = SEQ_GEMM;
@@ -192,24 +191,18 @@ int hyper_plan_bwd(const HyperProblem& hp, const HyperBuffers& b, SeqStep* steps
       a.a_sb = n, a.a_si = hp.N, a.a_sk = 1;
       a.B = b.w[j];
       a.b_sb = n * n, a.b_sk = n, a.b_sj = 1;
-      a.c_si = hp.N;
-      if (j == 0) {
-        // g_0 in L_0 (dx itself for a one-dimensional lattice)
-        a.C = k > 1 ? static_cast<void*>(ws + hp.ws_g[(k - 1) & 1]) : b.dx;
-        a.c_sb = n, a.c_sj = 1;
-      } else {
-        a.C = ws + hp.ws_g[(k - 1 - j) & 1];
-        set_out_prev(a, hp, j);
-      }
+      a.C = k > 1 ? g0 : b.dx;                     // L_j
+      a.c_sb = n, a.c_sj = 1, a.c_si = hp.N;
       a.M = hp.batch, a.N = n, a.K = n, a.nblk = nf;
     }
+    if (j > 0) set_swap(steps[ns++], hp, j, false, g0, g1);
   }
   if (k > 1) {
     SeqStep& st = steps[ns++];
-    st.kind = SEQ_TRANSPOSE;
+    st.kind = SEQ_SWAP;
     st.name = "hyper_transpose";
-    st.t_in = ws + hp.ws_g[(k - 1) & 1], st.t_out = b.dx;
-    st.t_rows = hp.batch, st.t_R = hp.N / hp.dims[0], st.t_C = hp.dims[0];
+    st.t_in = g0, st.t_out = b.dx;
+    st.t_rows = hp.batch, st.t_A = hp.N / hp.dims[0], st.t_M = 1, st.t_C = hp.dims[0];
   }
   // fixed-order sums of the weight-gradient chunks, three rounds per launch
   for (int j0 = 0; j0 < k; j0 += 3) {
@@ -232,8 +225,8 @@ hipError_t seq_launch(const SeqStep& st, bool bf16, hipStream_t s) {
     case SEQ_GEMM: return launch_gemm(st.g, bf16, s);
     case SEQ_REDUCE: return launch_reduce_partials(st.r[0], st.r[1], st.r[2], bf16, s);
     case SEQ_ZERO: return launch_zero(st.zero_ptr, st.zero_bytes, s);
-    case SEQ_TRANSPOSE:
-      return launch_row_transpose(st.t_in, st.t_out, st.t_rows, st.t_R, st.t_C, bf16, s);
+    case SEQ_SWAP:
+      return launch_swap(st.t_in, st.t_out, st.t_rows, st.t_A, st.t_M, st.t_C, bf16, s);
   }
   return hipErrorInvalidValue;
 }

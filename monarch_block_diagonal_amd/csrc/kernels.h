@@ -38,11 +38,6 @@ struct GemmArgs {
   // Optional bias (I/O type) added before `relu`, indexed by the row-relative
   // C offset.
   const void* bias = nullptr;
-  // Optional mixed-radix block offset of C (cb_r0 > 0): block blk splits as
-  // d0 = blk % cb_r0, d1 = (blk / cb_r0) % cb_r1, d2 = blk / (cb_r0*cb_r1)
-  // and its entries sit at d0*cb_s0 + d1*cb_s1 + d2*cb_s2 in place of
-  // blk*c_sb (a lattice axis moved between layouts).
-  int64_t cb_r0 = 0, cb_r1 = 1, cb_s0 = 0, cb_s1 = 0, cb_s2 = 0;
   // accum: C += the product (C read back before the store; not with `partial`)
   int accum = 0;
   int64_t M = 0, N = 0, K = 0;
@@ -68,10 +63,10 @@ hipError_t launch_gemm(const GemmArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_dv_gather(const void* dy, const void* ymask, void* dv, int64_t rows, int64_t out,
                             int64_t b2, int64_t q2o, bool bf16, hipStream_t s);
 
-// Per-row matrix transpose: every one of `rows` rows of `in` holds an R x C
-// row-major matrix, stored to `out` as C x R (lattice layout changes).
-hipError_t launch_row_transpose(const void* in, void* out, int64_t rows, int64_t R, int64_t C,
-                                bool bf16, hipStream_t s);
+// Axis swap of `rows` row-major A x M x C arrays: out[b][c][m][a] =
+// in[b][a][m][c] (M = 1: a per-row transpose; lattice layout changes).
+hipError_t launch_swap(const void* in, void* out, int64_t rows, int64_t A, int64_t M, int64_t C,
+                       bool bf16, hipStream_t s);
 
 // Bias gradient partial sums: partial[c][p*b2 + g] = sum over rows
 // [c*chunk, (c+1)*chunk) of dV[b, g*q2o + p], for p*b2 + g < out (fp32,

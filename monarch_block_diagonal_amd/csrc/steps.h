@@ -11,7 +11,7 @@
 
 namespace monarch {
 
-enum SeqKind { SEQ_GEMM, SEQ_REDUCE, SEQ_ZERO, SEQ_TRANSPOSE };
+enum SeqKind { SEQ_GEMM, SEQ_REDUCE, SEQ_ZERO, SEQ_SWAP };
 
 struct SeqStep {
   SeqKind kind = SEQ_GEMM;
@@ -20,10 +20,10 @@ struct SeqStep {
   ReduceArgs r[3];
   void* zero_ptr = nullptr;
   size_t zero_bytes = 0;
-  // SEQ_TRANSPOSE: every row of `rows` is an R x C matrix, written as C x R
+  // SEQ_SWAP: `rows` A x M x C arrays, written as C x M x A
   const void* t_in = nullptr;
   void* t_out = nullptr;
-  int64_t t_rows = 0, t_R = 0, t_C = 0;
+  int64_t t_rows = 0, t_A = 0, t_M = 1, t_C = 0;
 };
 
 hipError_t seq_launch(const SeqStep& st, bool bf16, hipStream_t s);

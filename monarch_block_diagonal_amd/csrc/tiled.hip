@@ -343,11 +343,7 @@ void tiled_gemm_kernel(GemmArgs p, int64_t m_tiles,
   }
 
   // 16x16 result layout: lane holds rows 4*(lane/16)+v, column lane%16
-  int64_t cblk = blk * p.c_sb;
-  if (p.cb_r0 > 0) {
-    const int64_t d0 = blk % p.cb_r0, t1 = blk / p.cb_r0;
-    cblk = d0 * p.cb_s0 + (t1 % p.cb_r1) * p.cb_s1 + (t1 / p.cb_r1) * p.cb_s2;
-  }
+  const int64_t cblk = blk * p.c_sb;
 #pragma unroll
   for (int ni = 0; ni < FN; ++ni) {
     const int64_t j = j0 + (wn * FN + ni) * 16 + l15;

@@ -256,11 +256,16 @@ def test_hyper_sizes_and_plan():
     dims = (16, 24, 32)
     assert M.monarch_hyper_saved_elems(dims, 10) == 3 * 10 * 12288
     assert M.monarch_hyper_saved_elems((64,), 10) == 0
-    assert M.monarch_hyper_describe(0, dims, 10, B.BF16) == ["hyper_transpose"] + ["hyper_round_fwd"] * 3
+    assert M.monarch_hyper_describe(0, dims, 10, B.BF16) == (
+        ["hyper_transpose"] + ["hyper_round_fwd", "hyper_permute"] * 2 + ["hyper_round_fwd"])
     assert M.monarch_hyper_describe(0, (64,), 10, B.BF16) == ["hyper_round_fwd"]
     names = M.monarch_hyper_describe(1, dims, 10, B.BF16)
-    assert names == (["hyper_round_bwd_weight", "hyper_round_bwd_data"] * 3 + ["hyper_transpose"]
+    assert names == (["hyper_round_bwd_weight", "hyper_round_bwd_data", "hyper_permute"] * 2
+                     + ["hyper_round_bwd_weight", "hyper_round_bwd_data", "hyper_transpose"]
                      + ["reduce_dw"])
+    assert M.monarch_hyper_describe(1, (64,), 10, B.BF16) == [
+        "hyper_round_bwd_weight", "hyper_round_bwd_data", "reduce_dw"]
+    assert len(M.monarch_hyper_describe(1, (2, 3, 4, 5), 10, B.BF16)) == 14
     assert M.monarch_hyper_describe(1, (2, 2, 2, 2), 10, B.F32)[-2:] == ["reduce_dw", "reduce_dw"]
     assert M.monarch_hyper_describe(1, dims, 0, B.BF16) == ["zero_dw"] * 3
     assert M.monarch_hyper_bwd_workspace_bytes(dims, 1000, B.BF16) > 0
