@@ -367,13 +367,14 @@ def bench_dyad(args) -> int:
     wb = torch.randn((nb, q, q), generator=g, device=dev).mul_((2 * q) ** -0.5).to(tdt)
     y, dx, dwa, dwb = torch.empty_like(x), torch.empty_like(x), torch.empty_like(wa), torch.empty_like(wb)
     need = M.monarch_dyad_bwd_workspace_bytes(n, n, nb, B, code)
-    ws = torch.empty((max(need, 1),), dtype=torch.uint8, device=dev)
+    need_f = M.monarch_dyad_fwd_workspace_bytes(n, n, nb, B, code)
+    ws = torch.empty((max(need, need_f, 1),), dtype=torch.uint8, device=dev)
     fn = M.monarch_dyad_describe(0, n, n, nb, B, code)
     bn = M.monarch_dyad_describe(1, n, n, nb, B, code)
     stream = torch.cuda.current_stream()
 
     def step(evf=None, evb=None):
-        M.monarch_dyad_fwd(x, wa, wb, y, n, n, nb, B, code, stream, events=evf)
+        M.monarch_dyad_fwd(x, wa, wb, y, ws, need_f, n, n, nb, B, code, stream, events=evf)
         M.monarch_dyad_bwd(dy, x, wa, wb, dx, dwa, dwb, ws, need, n, n, nb, B, code, stream,
                            events=evb)
 

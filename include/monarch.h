@@ -55,7 +55,7 @@
 extern "C" {
 #endif
 
-#define MONARCH_ABI_VERSION 1
+#define MONARCH_ABI_VERSION 2
 
 typedef enum {
   MONARCH_OK = 0,
@@ -252,11 +252,17 @@ int monarch_hyper_describe(int direction, int ndims, const int64_t* dims, int64_
  *   Y[b, r*qo + k] += sum_s A[r, k, s] X[b, r*qi + s]     (contiguous blocks)
  *   Y[b, p*nb + g] += sum_t B[g, p, t] X[b, t*nb + g]     (stride-nb features)
  * w_a = A and w_b = B are [nb, qo, qi]; x [batch, in], y [batch, out]. No
- * saved intermediate. The second term is added to the rounded first one
- * (two roundings of y in bf16). Errors and conventions as for monarch_fwd. */
-int monarch_dyad_fwd(const void* x, const void* w_a, const void* w_b, void* y,
-                     int64_t in_features, int64_t out_features, int64_t nblocks, int64_t batch,
-                     int dtype, void* stream, void* const* events, int n_events);
+ * saved intermediate. The second term is computed first and the first is
+ * added to its rounded value (two roundings of y in bf16). The caller's
+ * workspace (monarch_dyad_fwd_workspace_bytes, 16-byte aligned, contents
+ * unspecified on return) holds x in block-major order. Errors and
+ * conventions as for monarch_bwd. */
+size_t monarch_dyad_fwd_workspace_bytes(int64_t in_features, int64_t out_features,
+                                        int64_t nblocks, int64_t batch, int dtype);
+int monarch_dyad_fwd(const void* x, const void* w_a, const void* w_b, void* y, void* workspace,
+                     size_t workspace_bytes, int64_t in_features, int64_t out_features,
+                     int64_t nblocks, int64_t batch, int dtype, void* stream,
+                     void* const* events, int n_events);
 
 size_t monarch_dyad_bwd_workspace_bytes(int64_t in_features, int64_t out_features,
                                         int64_t nblocks, int64_t batch, int dtype);

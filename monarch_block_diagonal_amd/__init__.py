@@ -13,6 +13,6 @@ from .binding import (  # noqa: F401
     monarch_status_string, monarch_linear_mid, monarch_fwd_ex, monarch_bwd_ex,
     monarch_bwd_ex_workspace_bytes, monarch_describe_ex, monarch_hyper_saved_elems,
     monarch_hyper_fwd, monarch_hyper_bwd_workspace_bytes, monarch_hyper_bwd,
-    monarch_hyper_describe, monarch_dyad_fwd, monarch_dyad_bwd_workspace_bytes,
-    monarch_dyad_bwd, monarch_dyad_describe,
+    monarch_hyper_describe, monarch_dyad_fwd_workspace_bytes, monarch_dyad_fwd,
+    monarch_dyad_bwd_workspace_bytes, monarch_dyad_bwd, monarch_dyad_describe,
 )

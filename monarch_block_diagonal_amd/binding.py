@@ -33,7 +33,8 @@ EXPORTED = (
     "monarch_project", "monarch_linear_mid", "monarch_fwd_ex", "monarch_bwd_ex",
     "monarch_bwd_ex_workspace_bytes", "monarch_describe_ex", "monarch_hyper_saved_elems",
     "monarch_hyper_fwd", "monarch_hyper_bwd_workspace_bytes", "monarch_hyper_bwd",
-    "monarch_hyper_describe", "monarch_dyad_fwd", "monarch_dyad_bwd_workspace_bytes",
+    "monarch_hyper_describe", "monarch_dyad_fwd_workspace_bytes", "monarch_dyad_fwd",
+    "monarch_dyad_bwd_workspace_bytes",
     "monarch_dyad_bwd", "monarch_dyad_describe",
 )
 
@@ -101,7 +102,9 @@ def load_library():
     lib.monarch_hyper_bwd.restype = c_int
     lib.monarch_hyper_describe.argtypes = [c_int, c_int, pi64, i64, c_int, ctypes.c_char_p, sz]
     lib.monarch_hyper_describe.restype = c_int
-    lib.monarch_dyad_fwd.argtypes = [vp] * 4 + [i64] * 4 + [c_int, vp] + ev
+    lib.monarch_dyad_fwd_workspace_bytes.argtypes = [i64] * 4 + [c_int]
+    lib.monarch_dyad_fwd_workspace_bytes.restype = sz
+    lib.monarch_dyad_fwd.argtypes = [vp] * 5 + [sz] + [i64] * 4 + [c_int, vp] + ev
     lib.monarch_dyad_fwd.restype = c_int
     lib.monarch_dyad_bwd_workspace_bytes.argtypes = [i64] * 4 + [c_int]
     lib.monarch_dyad_bwd_workspace_bytes.restype = sz
@@ -304,12 +307,18 @@ def monarch_hyper_describe(direction, dims, batch, dtype):
     return buf.value.decode().split(";") if n else []
 
 
-def monarch_dyad_fwd(x, wa, wb, y, in_features, out_features, nblocks, batch, dtype, stream=None,
-                     events=None) -> None:
+def monarch_dyad_fwd_workspace_bytes(in_features, out_features, nblocks, batch, dtype) -> int:
+    return load_library().monarch_dyad_fwd_workspace_bytes(in_features, out_features, nblocks,
+                                                           batch, dtype)
+
+
+def monarch_dyad_fwd(x, wa, wb, y, workspace, workspace_bytes, in_features, out_features, nblocks,
+                     batch, dtype, stream=None, events=None) -> None:
     lib = load_library()
     arr, n = _events(events)
-    _check(lib.monarch_dyad_fwd(_ptr(x), _ptr(wa), _ptr(wb), _ptr(y), in_features, out_features,
-                                nblocks, batch, dtype, _stream(stream), arr, n))
+    _check(lib.monarch_dyad_fwd(_ptr(x), _ptr(wa), _ptr(wb), _ptr(y), _ptr(workspace),
+                                workspace_bytes, in_features, out_features, nblocks, batch, dtype,
+                                _stream(stream), arr, n))
 
 
 def monarch_dyad_bwd_workspace_bytes(in_features, out_features, nblocks, batch, dtype) -> int:

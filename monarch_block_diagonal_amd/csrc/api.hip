@@ -374,18 +374,30 @@ int monarch_hyper_describe(int direction, int ndims, const int64_t* dims, int64_
   return write_names(names, n, buf, buf_len);
 }
 
-int monarch_dyad_fwd(const void* x, const void* w_a, const void* w_b, void* y,
-                     int64_t in_features, int64_t out_features, int64_t nblocks, int64_t batch,
-                     int dtype, void* stream, void* const* events, int n_events) {
+size_t monarch_dyad_fwd_workspace_bytes(int64_t in_features, int64_t out_features,
+                                        int64_t nblocks, int64_t batch, int dtype) {
+  DyadProblem dp;
+  if (make_dyad(in_features, out_features, nblocks, batch, dtype, &dp)) return 0;
+  return dp.ws_fwd;
+}
+
+int monarch_dyad_fwd(const void* x, const void* w_a, const void* w_b, void* y, void* workspace,
+                     size_t workspace_bytes, int64_t in_features, int64_t out_features,
+                     int64_t nblocks, int64_t batch, int dtype, void* stream,
+                     void* const* events, int n_events) {
   DyadProblem dp;
   int st = make_dyad(in_features, out_features, nblocks, batch, dtype, &dp);
   if (st) return st;
   if (!w_a || !w_b) return MONARCH_ERR_NULL;
   if (batch > 0 && (!x || !y)) return MONARCH_ERR_NULL;
-  if (misaligned(x) || misaligned(w_a) || misaligned(w_b) || misaligned(y)) return MONARCH_ERR_ALIGN;
+  if (dp.ws_fwd > 0 && !workspace) return MONARCH_ERR_NULL;
+  if (misaligned(x) || misaligned(w_a) || misaligned(w_b) || misaligned(y) ||
+      misaligned(workspace))
+    return MONARCH_ERR_ALIGN;
+  if (workspace_bytes < dp.ws_fwd) return MONARCH_ERR_WORKSPACE;
   if (batch == 0) return MONARCH_OK;
   DyadBuffers b;
-  b.x = x, b.wa = w_a, b.wb = w_b, b.y = y;
+  b.x = x, b.wa = w_a, b.wb = w_b, b.y = y, b.ws = workspace;
   SeqStep steps[kDyadMaxSteps];
   const int n = dyad_plan_fwd(dp, b, steps);
   return run_seq(steps, n, dtype == MONARCH_BF16, static_cast<hipStream_t>(stream), events,

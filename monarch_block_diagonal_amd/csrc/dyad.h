@@ -13,7 +13,9 @@ struct DyadProblem {
   int dtype = 0;
   int64_t esize = 4;
   int64_t splits = 1, chunk = 0;   // batch split of both weight gradients
-  size_t ws_pa = 0, ws_pb = 0, ws_total = 0;
+  // backward workspace: partial sums of dA and dB, block-major X and dY;
+  // forward workspace: block-major X (ws_fwd bytes)
+  size_t ws_pa = 0, ws_pb = 0, ws_xp = 0, ws_dyp = 0, ws_total = 0, ws_fwd = 0;
 };
 
 struct DyadBuffers {
@@ -28,7 +30,7 @@ struct DyadBuffers {
   void* ws = nullptr;
 };
 
-constexpr int kDyadMaxSteps = 6;
+constexpr int kDyadMaxSteps = 8;
 
 // Checks the shape (in and out divisible by nb), batch and dtype; returns a
 // monarch_status.

@@ -4,10 +4,13 @@
 //   Y = X · (BD(A) + Q_out · BD(B) · P_in)ᵀ,
 //   term A: Y[b, r*qo + k] += sum_s A[r,k,s] X[b, r*qi + s]   (contiguous blocks)
 //   term B: Y[b, p*nb + g] += sum_t B[g,p,t] X[b, t*nb + g]   (residue-g features)
-// Each term is one launch of the tiled GEMM (tiled.hip); the second adds to
-// the first's result. The backward mirrors it: dX = dY·BD(A) + (term B's
-// transpose, accumulated), and the two weight gradients are batch-split sums
-// reduced in a fixed order.
+// Term B's operands are strided by nb. An axis swap (generic.hip) first
+// gathers X into block-major order, Xp[b, g*qi + t] = X[b, t*nb + g] (and the
+// backward also dY, dYp[b, g*qo + p] = dY[b, p*nb + g]), so that every GEMM
+// reads 16-byte pieces; term B's results are stored at their stride-nb
+// positions by the GEMM epilogue. The forward runs term B into Y and adds
+// term A to it; the backward takes both weight gradients as batch-split sums
+// (reduced in a fixed order), writes term B's dX and adds term A's.
 #include "dyad.h"
 #include "monarch.h"
 
@@ -31,19 +34,26 @@ void splits_for(int64_t nblk, int64_t M, int64_t N, int64_t K, int64_t* splits, 
   *splits = (K + c - 1) / c;
 }
 
-// term A and term B GEMMs of the forward / the data backward
+// term A and term B GEMMs of the forward
 void term_a_fwd(GemmArgs& a, const DyadProblem& dp, const void* x, const void* wa, void* y) {
   a.A = x, a.a_sb = dp.qi, a.a_si = dp.in, a.a_sk = 1;
   a.B = wa, a.b_sb = dp.qo * dp.qi, a.b_sk = 1, a.b_sj = dp.qi;
   a.C = y, a.c_sb = dp.qo, a.c_si = dp.out, a.c_sj = 1;
   a.M = dp.batch, a.N = dp.qo, a.K = dp.qi, a.nblk = dp.nb;
 }
-void term_b_fwd(GemmArgs& a, const DyadProblem& dp, const void* x, const void* wb, void* y) {
-  a.A = x, a.a_sb = 1, a.a_si = dp.in, a.a_sk = dp.nb;
+void term_b_fwd(GemmArgs& a, const DyadProblem& dp, const void* xp, const void* wb, void* y) {
+  a.A = xp, a.a_sb = dp.qi, a.a_si = dp.in, a.a_sk = 1;
   a.B = wb, a.b_sb = dp.qo * dp.qi, a.b_sk = 1, a.b_sj = dp.qi;
   a.C = y, a.c_sb = 1, a.c_si = dp.out, a.c_sj = dp.nb;
-  a.accum = 1;
   a.M = dp.batch, a.N = dp.qo, a.K = dp.qi, a.nblk = dp.nb;
+}
+// [rows][a][c] -> [rows][c][a], one row of `cols` = a*c elements per batch row
+void gather(SeqStep& st, const char* name, const void* in, void* out, int64_t rows, int64_t a,
+            int64_t c) {
+  st.kind = SEQ_SWAP;
+  st.name = name;
+  st.t_in = in, st.t_out = out;
+  st.t_rows = rows, st.t_A = a, st.t_M = 1, st.t_C = c;
 }
 
 }  // namespace
@@ -62,7 +72,10 @@ int make_dyad(int64_t in, int64_t out, int64_t nb, int64_t batch, int dtype, Dya
     const size_t part = static_cast<size_t>(p.splits) * nb * p.qo * p.qi * 4;
     p.ws_pa = 0;
     p.ws_pb = align256(part);
-    p.ws_total = align256(p.ws_pb + part);
+    p.ws_xp = align256(p.ws_pb + part);
+    p.ws_dyp = align256(p.ws_xp + static_cast<size_t>(batch) * in * p.esize);
+    p.ws_total = align256(p.ws_dyp + static_cast<size_t>(batch) * out * p.esize);
+    p.ws_fwd = align256(static_cast<size_t>(batch) * in * p.esize);
   }
   *dp = p;
   return MONARCH_OK;
@@ -70,13 +83,16 @@ int make_dyad(int64_t in, int64_t out, int64_t nb, int64_t batch, int dtype, Dya
 
 int dyad_plan_fwd(const DyadProblem& dp, const DyadBuffers& b, SeqStep* steps) {
   if (dp.batch == 0) return 0;
-  steps[0].kind = SEQ_GEMM;
-  steps[0].name = "dyad_term_a_fwd";
-  term_a_fwd(steps[0].g, dp, b.x, b.wa, b.y);
+  void* xp = b.ws;   // the forward's workspace: Xp
+  gather(steps[0], "dyad_gather_x", b.x, xp, dp.batch, dp.qi, dp.nb);
   steps[1].kind = SEQ_GEMM;
   steps[1].name = "dyad_term_b_fwd";
-  term_b_fwd(steps[1].g, dp, b.x, b.wb, b.y);
-  return 2;
+  term_b_fwd(steps[1].g, dp, xp, b.wb, b.y);
+  steps[2].kind = SEQ_GEMM;
+  steps[2].name = "dyad_term_a_fwd";
+  term_a_fwd(steps[2].g, dp, b.x, b.wa, b.y);
+  steps[2].g.accum = 1;
+  return 3;
 }
 
 int dyad_plan_bwd(const DyadProblem& dp, const DyadBuffers& b, SeqStep* steps) {
@@ -91,7 +107,11 @@ int dyad_plan_bwd(const DyadProblem& dp, const DyadBuffers& b, SeqStep* steps) {
   char* ws = static_cast<char*>(b.ws);
   float* pa = reinterpret_cast<float*>(ws + dp.ws_pa);
   float* pb = reinterpret_cast<float*>(ws + dp.ws_pb);
+  void* xp = ws + dp.ws_xp;
+  void* dyp = ws + dp.ws_dyp;
   int n = 0;
+  gather(steps[n++], "dyad_gather_x", b.x, xp, dp.batch, dp.qi, dp.nb);
+  gather(steps[n++], "dyad_gather_dy", b.dy, dyp, dp.batch, dp.qo, dp.nb);
   {
     // dA[r] = sum_b dY[b, r-block]ᵀ X[b, r-block]
     SeqStep& st = steps[n++];
@@ -103,33 +123,33 @@ int dyad_plan_bwd(const DyadProblem& dp, const DyadBuffers& b, SeqStep* steps) {
     a.M = dp.qo, a.N = dp.qi, a.K = dp.batch, a.nblk = dp.nb;
   }
   {
-    // dB[g] = sum_b dY[b, p*nb + g] X[b, t*nb + g]
+    // dB[g] = sum_b dYp[b, g*qo + p] Xp[b, g*qi + t]
     SeqStep& st = steps[n++];
     st.name = "dyad_term_b_bwd_weight";
     GemmArgs& a = st.g;
-    a.A = b.dy, a.a_sb = 1, a.a_si = dp.nb, a.a_sk = dp.out;
-    a.B = b.x, a.b_sb = 1, a.b_sk = dp.in, a.b_sj = dp.nb;
+    a.A = dyp, a.a_sb = dp.qo, a.a_si = 1, a.a_sk = dp.out;
+    a.B = xp, a.b_sb = dp.qi, a.b_sk = dp.in, a.b_sj = 1;
     a.partial = pb, a.splits = dp.splits, a.k_chunk = dp.chunk;
     a.M = dp.qo, a.N = dp.qi, a.K = dp.batch, a.nblk = dp.nb;
   }
   {
-    // dX[b, r*qi + s] = sum_k dY[b, r*qo + k] A[r,k,s]
+    // dX[b, t*nb + g] = sum_p dYp[b, g*qo + p] B[g,p,t]
+    SeqStep& st = steps[n++];
+    st.name = "dyad_term_b_bwd_data";
+    GemmArgs& a = st.g;
+    a.A = dyp, a.a_sb = dp.qo, a.a_si = dp.out, a.a_sk = 1;
+    a.B = b.wb, a.b_sb = dp.qo * dp.qi, a.b_sk = dp.qi, a.b_sj = 1;
+    a.C = b.dx, a.c_sb = 1, a.c_si = dp.in, a.c_sj = dp.nb;
+    a.M = dp.batch, a.N = dp.qi, a.K = dp.qo, a.nblk = dp.nb;
+  }
+  {
+    // dX[b, r*qi + s] += sum_k dY[b, r*qo + k] A[r,k,s]
     SeqStep& st = steps[n++];
     st.name = "dyad_term_a_bwd_data";
     GemmArgs& a = st.g;
     a.A = b.dy, a.a_sb = dp.qo, a.a_si = dp.out, a.a_sk = 1;
     a.B = b.wa, a.b_sb = dp.qo * dp.qi, a.b_sk = dp.qi, a.b_sj = 1;
     a.C = b.dx, a.c_sb = dp.qi, a.c_si = dp.in, a.c_sj = 1;
-    a.M = dp.batch, a.N = dp.qi, a.K = dp.qo, a.nblk = dp.nb;
-  }
-  {
-    // dX[b, t*nb + g] += sum_p dY[b, p*nb + g] B[g,p,t]
-    SeqStep& st = steps[n++];
-    st.name = "dyad_term_b_bwd_data";
-    GemmArgs& a = st.g;
-    a.A = b.dy, a.a_sb = 1, a.a_si = dp.out, a.a_sk = dp.nb;
-    a.B = b.wb, a.b_sb = dp.qo * dp.qi, a.b_sk = dp.qi, a.b_sj = 1;
-    a.C = b.dx, a.c_sb = 1, a.c_si = dp.in, a.c_sj = dp.nb;
     a.accum = 1;
     a.M = dp.batch, a.N = dp.qi, a.K = dp.qo, a.nblk = dp.nb;
   }

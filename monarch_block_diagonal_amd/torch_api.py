@@ -237,7 +237,9 @@ def dyad_forward(x, wa, wb, stream=None):
     nb, qo, qi = wa.shape
     b = x.shape[0]
     y = torch.empty((b, nb * qo), dtype=x.dtype, device=x.device)
-    B.monarch_dyad_fwd(x, wa, wb, y, x.shape[1], nb * qo, nb, b, dtype_code(x), stream)
+    need = B.monarch_dyad_fwd_workspace_bytes(x.shape[1], nb * qo, nb, b, dtype_code(x))
+    ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    B.monarch_dyad_fwd(x, wa, wb, y, ws, need, x.shape[1], nb * qo, nb, b, dtype_code(x), stream)
     return y
 
 

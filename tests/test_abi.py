@@ -299,18 +299,32 @@ def test_hyper_pointer_checks():
 # DYAD-style layer
 
 def test_dyad_plan_and_checks():
-    assert M.monarch_dyad_describe(0, 64, 32, 4, 10, B.BF16) == ["dyad_term_a_fwd", "dyad_term_b_fwd"]
+    assert M.monarch_dyad_describe(0, 64, 32, 4, 10, B.BF16) == [
+        "dyad_gather_x", "dyad_term_b_fwd", "dyad_term_a_fwd"]
     assert M.monarch_dyad_describe(1, 64, 32, 4, 10, B.BF16) == [
-        "dyad_term_a_bwd_weight", "dyad_term_b_bwd_weight", "dyad_term_a_bwd_data",
-        "dyad_term_b_bwd_data", "reduce_dw"]
+        "dyad_gather_x", "dyad_gather_dy", "dyad_term_a_bwd_weight", "dyad_term_b_bwd_weight",
+        "dyad_term_b_bwd_data", "dyad_term_a_bwd_data", "reduce_dw"]
     assert M.monarch_dyad_describe(1, 64, 32, 4, 0, B.BF16) == ["zero_dw", "zero_dw"]
     assert M.monarch_dyad_bwd_workspace_bytes(64, 32, 4, 1000, B.F32) > 0
     assert M.monarch_dyad_bwd_workspace_bytes(63, 32, 4, 1000, B.F32) == 0
+    # the forward's workspace holds x in block-major order
+    assert M.monarch_dyad_fwd_workspace_bytes(64, 32, 4, 1000, B.F32) >= 1000 * 64 * 4
+    assert M.monarch_dyad_fwd_workspace_bytes(64, 32, 4, 0, B.F32) == 0
     lib = M.load_library()
-    assert lib.monarch_dyad_fwd(A, A, A, A2, 63, 32, 4, 8, B.F32, None, None, 0) == B.MONARCH_ERR_SHAPE
-    assert lib.monarch_dyad_fwd(A, A, A, A2, 64, 32, 0, 8, B.F32, None, None, 0) == B.MONARCH_ERR_SHAPE
-    assert lib.monarch_dyad_fwd(A, None, A, A2, 64, 32, 4, 8, B.F32, None, None, 0) == B.MONARCH_ERR_NULL
-    assert lib.monarch_dyad_fwd(MIS, A, A, A2, 64, 32, 4, 8, B.F32, None, None, 0) == B.MONARCH_ERR_ALIGN
-    assert lib.monarch_dyad_fwd(A, A, A, A2, 64, 32, 4, 8, 5, None, None, 0) == B.MONARCH_ERR_DTYPE
+    big = 1 << 20
+    assert lib.monarch_dyad_fwd(A, A, A, A2, A2, big, 63, 32, 4, 8, B.F32, None, None,
+                                0) == B.MONARCH_ERR_SHAPE
+    assert lib.monarch_dyad_fwd(A, A, A, A2, A2, big, 64, 32, 0, 8, B.F32, None, None,
+                                0) == B.MONARCH_ERR_SHAPE
+    assert lib.monarch_dyad_fwd(A, None, A, A2, A2, big, 64, 32, 4, 8, B.F32, None, None,
+                                0) == B.MONARCH_ERR_NULL
+    assert lib.monarch_dyad_fwd(A, A, A, A2, None, big, 64, 32, 4, 8, B.F32, None, None,
+                                0) == B.MONARCH_ERR_NULL
+    assert lib.monarch_dyad_fwd(MIS, A, A, A2, A2, big, 64, 32, 4, 8, B.F32, None, None,
+                                0) == B.MONARCH_ERR_ALIGN
+    assert lib.monarch_dyad_fwd(A, A, A, A2, A2, 16, 64, 32, 4, 8, B.F32, None, None,
+                                0) == B.MONARCH_ERR_WORKSPACE
+    assert lib.monarch_dyad_fwd(A, A, A, A2, A2, big, 64, 32, 4, 8, 5, None, None,
+                                0) == B.MONARCH_ERR_DTYPE
     assert lib.monarch_dyad_bwd(A, A, A, A, A2, A2, A2, A2, 0, 64, 32, 4, 8, B.F32, None, None,
                                 0) == B.MONARCH_ERR_WORKSPACE
