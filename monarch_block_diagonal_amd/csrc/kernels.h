@@ -45,6 +45,9 @@ struct GemmArgs {
   int64_t splits = 1;
   int64_t k_chunk = 0;
   int relu = 0;
+  // set by launch_gemm: C columns are contiguous and every 4-column group is
+  // aligned and inside or outside the limits as a whole (4-wide epilogue)
+  int cvec = 0;
 };
 
 // Reduction-chunk granularity of batch-split GEMMs (a multiple of both

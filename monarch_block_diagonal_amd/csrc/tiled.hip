@@ -217,6 +217,29 @@ struct Tile {
 template <int TM>
 constexpr int kSlots = TM > 128 ? 1 : 2;
 
+// Four consecutive elements of the I/O type as fp32 (8-byte bf16 or 16-byte
+// fp32 accesses; offsets are multiples of four).
+template <typename T> struct Vec4;
+template <> struct Vec4<float> {
+  static __device__ __forceinline__ f32x4 load(const void* p, int64_t i) {
+    return *reinterpret_cast<const f32x4*>(static_cast<const float*>(p) + i);
+  }
+  static __device__ __forceinline__ void store(void* p, int64_t i, f32x4 v) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(p) + i) = v;
+  }
+};
+template <> struct Vec4<uint16_t> {
+  static __device__ __forceinline__ f32x4 load(const void* p, int64_t i) {
+    const u32x2 w = *reinterpret_cast<const u32x2*>(static_cast<const uint16_t*>(p) + i);
+    return f32x4{__uint_as_float(w[0] << 16), __uint_as_float(w[0] & 0xffff0000u),
+                 __uint_as_float(w[1] << 16), __uint_as_float(w[1] & 0xffff0000u)};
+  }
+  static __device__ __forceinline__ void store(void* p, int64_t i, f32x4 v) {
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(p) + i) =
+        u32x2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+  }
+};
+
 template <typename T, int AM, int BMD, int WM, int WN, int FM, int FN, bool EW>
 __global__ __launch_bounds__(TT) __attribute__((amdgpu_waves_per_eu(2)))
 void tiled_gemm_kernel(GemmArgs p, int64_t m_tiles,
@@ -344,6 +367,47 @@ void tiled_gemm_kernel(GemmArgs p, int64_t m_tiles,
 
   // 16x16 result layout: lane holds rows 4*(lane/16)+v, column lane%16
   const int64_t cblk = blk * p.c_sb;
+  if (p.cvec) {
+    // a 4x4 transpose within each quad of lanes (columns 4c..4c+3) leaves
+    // lane 4c+u with row 4*(lane/16)+u, columns 4c..4c+3: one 4-element
+    // load/store per row instead of four single elements
+    const int u = l15 & 3;
+#pragma unroll
+    for (int ni = 0; ni < FN; ++ni) {
+      const int64_t jb = j0 + (wn * FN + ni) * 16 + (l15 & ~3);
+      const int64_t cpos = cblk + jb;
+#pragma unroll
+      for (int mi = 0; mi < FM; ++mi) {
+        const f32x4 in = acc[mi][ni];
+        f32x4 o;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          // send my row (u - r) & 3 to the lane whose column I hold it for,
+          // receive row u of column (u + r) & 3
+          const int sr = (u - r) & 3;
+          const float send = sr == 0 ? in[0] : sr == 1 ? in[1] : sr == 2 ? in[2] : in[3];
+          const float got = __shfl(send, (lane & ~3) | ((u + r) & 3), 64);
+          const int dc = (u + r) & 3;
+          o[0] = dc == 0 ? got : o[0];
+          o[1] = dc == 1 ? got : o[1];
+          o[2] = dc == 2 ? got : o[2];
+          o[3] = dc == 3 ? got : o[3];
+        }
+        const int64_t i = i0 + (wm * FM + mi) * 16 + 4 * lh + u;
+        if (i < p.M && jb < p.N && (p.c_cols < 0 || cpos < p.c_cols)) {
+          const int64_t off = i * p.c_si + cpos;
+          if (p.accum) o += Vec4<T>::load(p.C, off);
+          if (p.bias) o += Vec4<T>::load(p.bias, cpos);
+          if (p.relu) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = o[e] > 0.f ? o[e] : 0.f;
+          }
+          Vec4<T>::store(p.C, off, o);
+        }
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int ni = 0; ni < FN; ++ni) {
     const int64_t j = j0 + (wn * FN + ni) * 16 + l15;
@@ -537,6 +601,9 @@ hipError_t launch_gemm(const GemmArgs& a, bool bf16, hipStream_t s) {
                             : (a.b_sj == 1 && a.b_sk % vec == 0 && a.b_sb % vec == 0 &&
                                a.N % vec == 0 && lim_ok(a.n_lim, a.n_lim_bs, vec));
   if (a.partial && (a.k_chunk % kSplitK != 0 || a.nsplit > 0)) return hipErrorInvalidValue;
+  GemmArgs g4 = a;
+  g4.cvec = !a.partial && a.nsplit == 0 && a.c_sj == 1 && a.c_sb % 4 == 0 && a.c_si % 4 == 0 &&
+            a.N % 4 == 0 && (a.c_cols < 0 || a.c_cols % 4 == 0);
   const Shape sh = pick_shape(a.M, a.N);
   int tm, tn;
   shape_tiles(sh, &tm, &tn);
@@ -548,15 +615,15 @@ hipError_t launch_gemm(const GemmArgs& a, bool bf16, hipStream_t s) {
   const dim3 g(static_cast<unsigned>(grid));
   const int av = avec ? 1 : 0, bv = bvec ? 1 : 0;
   if (bf16) {
-    if (am == 1 && bm == 1) return launch_modes<uint16_t, 1, 1>(a, sh, g, mt, nt, remap, av, bv, s);
-    if (am == 1) return launch_modes<uint16_t, 1, 2>(a, sh, g, mt, nt, remap, av, bv, s);
-    if (bm == 1) return launch_modes<uint16_t, 2, 1>(a, sh, g, mt, nt, remap, av, bv, s);
-    return launch_modes<uint16_t, 2, 2>(a, sh, g, mt, nt, remap, av, bv, s);
+    if (am == 1 && bm == 1) return launch_modes<uint16_t, 1, 1>(g4, sh, g, mt, nt, remap, av, bv, s);
+    if (am == 1) return launch_modes<uint16_t, 1, 2>(g4, sh, g, mt, nt, remap, av, bv, s);
+    if (bm == 1) return launch_modes<uint16_t, 2, 1>(g4, sh, g, mt, nt, remap, av, bv, s);
+    return launch_modes<uint16_t, 2, 2>(g4, sh, g, mt, nt, remap, av, bv, s);
   }
-  if (am == 1 && bm == 1) return launch_modes<float, 1, 1>(a, sh, g, mt, nt, remap, av, bv, s);
-  if (am == 1) return launch_modes<float, 1, 2>(a, sh, g, mt, nt, remap, av, bv, s);
-  if (bm == 1) return launch_modes<float, 2, 1>(a, sh, g, mt, nt, remap, av, bv, s);
-  return launch_modes<float, 2, 2>(a, sh, g, mt, nt, remap, av, bv, s);
+  if (am == 1 && bm == 1) return launch_modes<float, 1, 1>(g4, sh, g, mt, nt, remap, av, bv, s);
+  if (am == 1) return launch_modes<float, 1, 2>(g4, sh, g, mt, nt, remap, av, bv, s);
+  if (bm == 1) return launch_modes<float, 2, 1>(g4, sh, g, mt, nt, remap, av, bv, s);
+  return launch_modes<float, 2, 2>(g4, sh, g, mt, nt, remap, av, bv, s);
 }
 
 hipError_t launch_dv_gather(const void* dy, const void* ymask, void* dv, int64_t rows, int64_t out,
