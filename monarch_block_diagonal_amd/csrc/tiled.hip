@@ -251,8 +251,9 @@ void tiled_gemm_kernel(GemmArgs p, int64_t m_tiles,
   constexpr int SL = kSlots<TM>;
   using TA = Tile<T, AM, TM, EW, SL>;
   using TB = Tile<T, BMD, TN, EW, SL>;
-  __shared__ __attribute__((aligned(16))) T As[TA::LDS];
-  __shared__ __attribute__((aligned(16))) T Bs[TB::LDS];
+  // two LDS buffers when two K tiles are in flight in registers
+  __shared__ __attribute__((aligned(16))) T As[SL][TA::LDS];
+  __shared__ __attribute__((aligned(16))) T Bs[SL][TB::LDS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int l15 = lane & 15, lh = lane >> 4;
@@ -293,29 +294,14 @@ void tiled_gemm_kernel(GemmArgs p, int64_t m_tiles,
 #pragma unroll
     for (int ni = 0; ni < FN; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // K tile t is loaded into register slot t % SL, SL tiles ahead of its
-  // use: step t stores slot t % SL to LDS, then reloads it with tile t + SL
+  // K tile t sits in register slot t % SL and LDS buffer t % SL.
+  //  * One slot (256-row tiles): step t stores slot 0 to LDS, reloads it with
+  //    tile t + 1, multiplies, and waits twice.
+  //  * Two slots: step t multiplies buffer t % 2 while it stores tile t + 1
+  //    (slot (t + 1) % 2) into the other buffer and reloads that slot with
+  //    tile t + 3; one barrier per step, and a load has two steps to land.
   const int64_t nsteps = kb < ke ? (ke - kb + TK - 1) / TK : 0;
-  if (nsteps > 0) {
-    a.template load<0>(kb);
-    b.template load<0>(kb);
-  }
-  if constexpr (SL > 1) {
-    if (nsteps > 1) {
-      a.template load<SL - 1>(kb + TK);
-      b.template load<SL - 1>(kb + TK);
-    }
-  }
-  auto step = [&](auto slot, int64_t t) {
-    constexpr int S = decltype(slot)::value;
-    const int64_t k0 = kb + t * TK;
-    a.template store<S>(As, k0);
-    b.template store<S>(Bs, k0);
-    __syncthreads();
-    if (t + SL < nsteps) {
-      a.template load<S>(k0 + SL * TK);
-      b.template load<S>(k0 + SL * TK);
-    }
+  auto mult = [&](const T* as, const T* bs) {
     if constexpr (C::kBf16) {
 #pragma unroll
       for (int ks = 0; ks < TK; ks += 32) {
@@ -323,11 +309,11 @@ void tiled_gemm_kernel(GemmArgs p, int64_t m_tiles,
 #pragma unroll
         for (int mi = 0; mi < FM; ++mi)
           fa[mi] = as_bf16x8(*reinterpret_cast<const u16x8*>(
-              &As[C::rowoff((wm * FM + mi) * 16 + l15) + ks + 8 * lh]));
+              &as[C::rowoff((wm * FM + mi) * 16 + l15) + ks + 8 * lh]));
 #pragma unroll
         for (int ni = 0; ni < FN; ++ni)
           fb[ni] = as_bf16x8(*reinterpret_cast<const u16x8*>(
-              &Bs[C::rowoff((wn * FN + ni) * 16 + l15) + ks + 8 * lh]));
+              &bs[C::rowoff((wn * FN + ni) * 16 + l15) + ks + 8 * lh]));
 #pragma unroll
         for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
@@ -343,10 +329,10 @@ void tiled_gemm_kernel(GemmArgs p, int64_t m_tiles,
         f32x4 fa[FM], fb[FN];
 #pragma unroll
         for (int mi = 0; mi < FM; ++mi)
-          fa[mi] = *reinterpret_cast<const f32x4*>(&As[C::rowoff((wm * FM + mi) * 16 + l15) + ks + 4 * lh]);
+          fa[mi] = *reinterpret_cast<const f32x4*>(&as[C::rowoff((wm * FM + mi) * 16 + l15) + ks + 4 * lh]);
 #pragma unroll
         for (int ni = 0; ni < FN; ++ni)
-          fb[ni] = *reinterpret_cast<const f32x4*>(&Bs[C::rowoff((wn * FN + ni) * 16 + l15) + ks + 4 * lh]);
+          fb[ni] = *reinterpret_cast<const f32x4*>(&bs[C::rowoff((wn * FN + ni) * 16 + l15) + ks + 4 * lh]);
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
@@ -356,12 +342,57 @@ void tiled_gemm_kernel(GemmArgs p, int64_t m_tiles,
               acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x4f32(fa[mi][j], fb[ni][j], acc[mi][ni], 0, 0, 0);
       }
     }
-    __syncthreads();
   };
-  for (int64_t t = 0; t < nsteps; t += SL) {
-    step(std::integral_constant<int, 0>{}, t);
-    if constexpr (SL > 1) {
-      if (t + 1 < nsteps) step(std::integral_constant<int, SL - 1>{}, t + 1);
+  if constexpr (SL == 1) {
+    if (nsteps > 0) {
+      a.template load<0>(kb);
+      b.template load<0>(kb);
+    }
+    for (int64_t t = 0; t < nsteps; ++t) {
+      const int64_t k0 = kb + t * TK;
+      a.template store<0>(As[0], k0);
+      b.template store<0>(Bs[0], k0);
+      __syncthreads();
+      if (t + 1 < nsteps) {
+        a.template load<0>(k0 + TK);
+        b.template load<0>(k0 + TK);
+      }
+      mult(As[0], Bs[0]);
+      __syncthreads();
+    }
+  } else {
+    if (nsteps > 0) {
+      a.template load<0>(kb);
+      b.template load<0>(kb);
+      if (nsteps > 1) {
+        a.template load<1>(kb + TK);
+        b.template load<1>(kb + TK);
+      }
+      a.template store<0>(As[0], kb);
+      b.template store<0>(Bs[0], kb);
+      if (nsteps > 2) {
+        a.template load<0>(kb + 2 * TK);
+        b.template load<0>(kb + 2 * TK);
+      }
+      __syncthreads();
+    }
+    auto step = [&](auto buf, int64_t t) {
+      constexpr int S = decltype(buf)::value, S1 = 1 - S;
+      const int64_t k1 = kb + (t + 1) * TK;
+      mult(As[S], Bs[S]);
+      if (t + 1 < nsteps) {
+        a.template store<S1>(As[S1], k1);
+        b.template store<S1>(Bs[S1], k1);
+        if (t + 3 < nsteps) {
+          a.template load<S1>(k1 + 2 * TK);
+          b.template load<S1>(k1 + 2 * TK);
+        }
+      }
+      __syncthreads();
+    };
+    for (int64_t t = 0; t < nsteps; t += 2) {
+      step(std::integral_constant<int, 0>{}, t);
+      if (t + 1 < nsteps) step(std::integral_constant<int, 1>{}, t + 1);
     }
   }
 
