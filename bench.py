@@ -69,6 +69,7 @@ def kernel_bytes(name: str, pr: dict) -> float:
         # dX, plus dV and dZ for the weight-gradient GEMMs
         "sm32_fwd": e * B * (inp + mid + out) + e * (p1 + p2),
         "sm32_bwd_data": e * B * (out * (2 if relu else 1) + out + mid + inp) + e * (p1 + p2),
+        "sm32_bwd_weight": e * B * (out + 2 * mid + inp),
         "reduce_dw": e * (p1 + p2),
     }
     for key in sorted(table, key=len, reverse=True):
@@ -86,6 +87,7 @@ def kernel_flops(name: str, pr: dict) -> float:
         "stage2_bwd_data": 2 * B * p2, "stage2_bwd_weight": 2 * B * p2, "stage2_bwd": 4 * B * p2,
         "stage1_bwd_data": 2 * B * p1, "stage1_bwd_weight": 2 * B * p1, "stage1_bwd": 4 * B * p1,
         "sm32_fwd": 2 * B * (p1 + p2), "sm32_bwd_data": 2 * B * (p1 + p2),
+        "sm32_bwd_weight": 2 * B * (p1 + p2),
     }
     for key in sorted(table, key=len, reverse=True):
         if name.endswith(key):

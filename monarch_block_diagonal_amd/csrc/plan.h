@@ -71,6 +71,7 @@ enum StepKind {
   SQ_STAGE1_BWD,
   SM_FWD,
   SM_BWD_DATA,
+  SM_WGRAD,
 };
 
 struct Plan {

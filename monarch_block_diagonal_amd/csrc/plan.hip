@@ -19,9 +19,9 @@
 // the dw2 product read z contiguously.
 //
 // Fused path (bf16, 32 x 32 blocks, at most 1024 features, small.hip): the
-// forward and the data part of the backward are one launch each; the weight
-// gradients are the generic path's batch-split GEMMs on the dV and dZ the
-// fused backward stores.
+// forward, the data part of the backward and both weight gradients are one
+// launch each (the weight gradients as batch-chunk partials from the dV and
+// dZ the data kernel stores), then the shared reduction.
 #include "kernels.h"
 #include "monarch.h"
 #include "plan.h"
@@ -94,10 +94,14 @@ int make_problem_ex(int64_t in, int64_t out, int64_t mid, int64_t nb1, int64_t n
     p.s2 = p.sq.w2_chunks;
     p.s1 = p.sq.b1_chunks;
   } else {
-    if (batch > 0 && whole && sm_applicable(in, out, nb1, nb2, batch, dtype == MONARCH_BF16))
+    if (batch > 0 && whole && sm_applicable(in, out, nb1, nb2, batch, dtype == MONARCH_BF16)) {
       p.path = PATH_SM32;
-    choose_splits(p.b2, p.q2o, p.q2i, batch, &p.s2, &p.kc2);
-    choose_splits(p.b1, p.q1o, p.q1i, batch, &p.s1, &p.kc1);
+      sm_wgrad_split(batch, &p.s2, &p.kc2);
+      p.s1 = p.s2, p.kc1 = p.kc2;
+    } else {
+      choose_splits(p.b2, p.q2o, p.q2i, batch, &p.s2, &p.kc2);
+      choose_splits(p.b1, p.q1o, p.q1i, batch, &p.s1, &p.kc1);
+    }
   }
   if (batch > 0) {
     size_t off = 0;
@@ -169,8 +173,7 @@ Plan plan_bwd(const Problem& pr) {
   }
   if (pr.path == PATH_SM32) {
     p.add(SM_BWD_DATA);
-    p.add(GEN_STAGE2_BWD_WEIGHT);
-    p.add(GEN_STAGE1_BWD_WEIGHT);
+    p.add(SM_WGRAD);
     p.add(REDUCE_DW);
     return p;
   }
@@ -204,6 +207,7 @@ const char* step_name(StepKind k) {
     case SQ_STAGE1_BWD: return "sq128_stage1_bwd";
     case SM_FWD: return "sm32_fwd";
     case SM_BWD_DATA: return "sm32_bwd_data";
+    case SM_WGRAD: return "sm32_bwd_weight";
   }
   return "?";
 }
@@ -326,6 +330,8 @@ hipError_t launch_step(StepKind k, const Problem& pr, const Buffers& b, hipStrea
                            pr.act == MONARCH_ACT_RELU, s);
     case SM_BWD_DATA:
       return sm_launch_bwd_data(b.dy, mask, b.w1, b.w2, b.dx, dv, dz, pr.batch, pr.b1, s);
+    case SM_WGRAD:
+      return sm_launch_wgrad(dv, b.z, dz, b.x, p2, p1, pr.batch, pr.b1, s);
     case ZERO_DW: {
       hipError_t e = launch_zero(b.dw2, static_cast<size_t>(pr.b2 * pr.q2o * pr.q2i) * pr.esize, s);
       if (e != hipSuccess) return e;

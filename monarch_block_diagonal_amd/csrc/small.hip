@@ -14,8 +14,11 @@
 //    Y; HBM traffic is X read once, z and Y written once.
 //  * Backward data (one launch): dY (masked by Y > 0 after a fused ReLU) ->
 //    dV[b, g*32 + p] = dY[b, p*b + g] in LDS -> dZ = dV·L per block, stored
-//    in Z order -> dX = dZ·R per block. It also stores dV and dZ (row-major)
-//    for the weight-gradient GEMMs, which run as batch-split tiled GEMMs.
+//    in Z order -> dX = dZ·R per block. It also stores dV and dZ (row-major).
+//  * Weight gradients (one launch for both factors): dL[g] = sum_b
+//    dV[b, g-block]ᵀ z[b, g-block] and dR[r] = sum_b dZ[b, r-block]ᵀ
+//    X[b, r-block] over batch chunks, one fp32 partial per chunk, summed in a
+//    fixed order afterwards.
 //
 // Each of the 8 waves owns b/8 blocks of each factor; a block's 32 x 32
 // weights are two MFMA operands (v_mfma_f32_16x16x32_bf16: K = 32 is one
@@ -148,7 +151,7 @@ __global__ __launch_bounds__(512) void sm_fwd_kernel(const uint16_t* __restrict_
 // with the activation tile as the A operand (8 consecutive features of one
 // row, read from LDS) and a transposed weight block as the B operand
 // (gathered once per launch). dV and dZ are also stored row-major for the
-// weight-gradient GEMMs; the dV tile's LDS is reused for dX.
+// weight gradients; the dV tile's LDS is reused for dX.
 template <int NB>
 __global__ __launch_bounds__(512) void sm_bwd_data_kernel(
     const uint16_t* __restrict__ dY, const uint16_t* __restrict__ Ym,
@@ -221,6 +224,62 @@ __global__ __launch_bounds__(512) void sm_bwd_data_kernel(
   }
 }
 
+// --------------------------------------------------------------------------
+// weight gradients: partial[c][blk][i][j] = sum over the rows of chunk c of
+// A[b, blk*32 + i] Bm[b, blk*32 + j], with (A, Bm) = (dV, z) for dL and
+// (dZ, X) for dR
+// --------------------------------------------------------------------------
+// Workgroup: one factor, one block, one chunk of rows; 4 waves, wave w owns
+// the 16 x 16 output tile (w / 2, w % 2). K step: 32 rows. Threads 0-127
+// load the A rows and 128-255 the Bm rows (one 16-byte piece of 8 features
+// each, the next step's piece in flight) and store them transposed,
+// [feature][row], so that both MFMA operands (8 consecutive rows of one
+// feature) are 16-byte LDS reads.
+template <int NB>
+__global__ __launch_bounds__(256) void sm_wgrad_kernel(
+    const uint16_t* __restrict__ dV, const uint16_t* __restrict__ Zs,
+    const uint16_t* __restrict__ dZ, const uint16_t* __restrict__ X,
+    float* __restrict__ part_l, float* __restrict__ part_r, int64_t B, int64_t chunk) {
+  constexpr int N = NB * SB, KT = 32, TP = KT + 8;
+  __shared__ __attribute__((aligned(16))) uint16_t ts[2][SB * TP];
+  int bid = blockIdx.x;
+  const int blk = bid % NB;
+  bid /= NB;
+  const int fac = bid & 1;
+  const int64_t split = bid >> 1;
+  const int64_t r0 = split * chunk;
+  const int64_t r1 = r0 + chunk < B ? r0 + chunk : B;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l15 = lane & 15, lh = lane >> 4;
+  const int op = tid >> 7, lrow = (tid & 127) >> 2, lcol = (tid & 3) * 8;
+  const uint16_t* src = (op ? (fac ? X : Zs) : (fac ? dZ : dV)) + blk * SB + lcol;
+  uint16_t* dst = &ts[op][lcol * TP + lrow];
+  const int mi = w >> 1, ni = w & 1;
+
+  // rows past the chunk read as zero (they add nothing to the sums)
+  auto load = [&](int64_t b0) -> u32x4 {
+    const int64_t row = b0 + lrow;
+    return row < r1 ? *reinterpret_cast<const u32x4*>(src + row * N) : u32x4{0u, 0u, 0u, 0u};
+  };
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  u32x4 cur = load(r0);
+  for (int64_t b0 = r0; b0 < r1; b0 += KT) {
+    const u32x4 nxt = b0 + KT < r1 ? load(b0 + KT) : cur;
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      dst[e * TP] = static_cast<uint16_t>(cur[e >> 1] >> (16 * (e & 1)));
+    __syncthreads();
+    const bf16x8 a = ld_op(&ts[0][(16 * mi + l15) * TP + 8 * lh]);
+    const bf16x8 b = ld_op(&ts[1][(16 * ni + l15) * TP + 8 * lh]);
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
+    __syncthreads();
+    cur = nxt;
+  }
+  float* part = (fac ? part_r : part_l) + (split * NB + blk) * SB * SB;
+#pragma unroll
+  for (int v = 0; v < 4; ++v) part[(16 * mi + 4 * lh + v) * SB + 16 * ni + l15] = acc[v];
+}
+
 // about two workgroups per CU (each holds two 16-row tiles of LDS)
 int64_t grid_for(int64_t batch) {
   const int64_t tiles = (batch + ST - 1) / ST;
@@ -249,6 +308,34 @@ hipError_t sm_launch_fwd(const void* x, const void* w1, const void* w2, void* y,
     case 8: hipLaunchKernelGGL(sm_fwd_kernel<8>, grid, block, 0, s, xp, r, l, yp, zp, batch, relu); break;
     case 16: hipLaunchKernelGGL(sm_fwd_kernel<16>, grid, block, 0, s, xp, r, l, yp, zp, batch, relu); break;
     case 32: hipLaunchKernelGGL(sm_fwd_kernel<32>, grid, block, 0, s, xp, r, l, yp, zp, batch, relu); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+void sm_wgrad_split(int64_t batch, int64_t* splits, int64_t* chunk) {
+  // chunks of at least 256 rows (a multiple of the 32-row step), at most 64
+  int64_t c = (batch + 63) / 64;
+  if (c < 256) c = 256;
+  c = (c + 31) / 32 * 32;
+  *chunk = c;
+  *splits = (batch + c - 1) / c;
+}
+
+hipError_t sm_launch_wgrad(const void* dv, const void* z, const void* dz, const void* x,
+                           float* part_l, float* part_r, int64_t batch, int64_t nb,
+                           hipStream_t s) {
+  int64_t splits, chunk;
+  sm_wgrad_split(batch, &splits, &chunk);
+  const dim3 grid(static_cast<unsigned>(2 * nb * splits)), block(256);
+  const uint16_t* a = static_cast<const uint16_t*>(dv);
+  const uint16_t* b = static_cast<const uint16_t*>(z);
+  const uint16_t* c = static_cast<const uint16_t*>(dz);
+  const uint16_t* d = static_cast<const uint16_t*>(x);
+  switch (nb) {
+    case 8: hipLaunchKernelGGL(sm_wgrad_kernel<8>, grid, block, 0, s, a, b, c, d, part_l, part_r, batch, chunk); break;
+    case 16: hipLaunchKernelGGL(sm_wgrad_kernel<16>, grid, block, 0, s, a, b, c, d, part_l, part_r, batch, chunk); break;
+    case 32: hipLaunchKernelGGL(sm_wgrad_kernel<32>, grid, block, 0, s, a, b, c, d, part_l, part_r, batch, chunk); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

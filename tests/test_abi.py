@@ -151,7 +151,7 @@ def test_path_selection():
     for n, nb in [(1024, 32), (512, 16), (256, 8)]:
         assert M.monarch_describe(0, n, n, nb, nb, 64, B.BF16) == ["sm32_fwd"]
         assert M.monarch_describe(1, n, n, nb, nb, 64, B.BF16, B.ACT_RELU) == [
-            "sm32_bwd_data", "generic_stage2_bwd_weight", "generic_stage1_bwd_weight", "reduce_dw"]
+            "sm32_bwd_data", "sm32_bwd_weight", "reduce_dw"]
     # everything else takes the generic path
     for args in [(16384, 16384, 128, 128, 64, B.F32), (1024, 1024, 32, 32, 64, B.F32),
                  (2048, 2048, 64, 64, 64, B.BF16), (1024, 1024, 8, 8, 64, B.BF16), (2048, 2048, 16, 16, 64, B.BF16),
