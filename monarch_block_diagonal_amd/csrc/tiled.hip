@@ -502,19 +502,24 @@ __global__ __launch_bounds__(256) void dv_gather_lds_kernel(const T* __restrict_
   }
   __syncthreads();
   T* dst = dV + row0 * oext;
-  for (int64_t e = threadIdx.x; e < out_pieces; e += 256) {
-    const int64_t r = (e * VEC) / oext, o0 = e * VEC - r * oext;
+  // offsets inside the staged rows fit 32 bits (at most 32 KB of them); one
+  // division per piece, then (g, p) steps along the piece
+  const uint32_t oe = static_cast<uint32_t>(oext), q = static_cast<uint32_t>(q2o);
+  const uint32_t nb = static_cast<uint32_t>(b2), ou = static_cast<uint32_t>(out);
+  for (uint32_t e = threadIdx.x; e < static_cast<uint32_t>(out_pieces); e += 256) {
+    const uint32_t r = (e * VEC) / oe, o0 = e * VEC - r * oe;
+    uint32_t g = o0 / q, pp = o0 - g * q;
+    const T* srow = s + r * ou;
     T vals[VEC];
 #pragma unroll
     for (int i = 0; i < VEC; ++i) {
-      const int64_t o = o0 + i;
-      const int64_t g = o / q2o, pp = o - g * q2o;
-      const int64_t so = pp * b2 + g;
-      vals[i] = so < out ? s[r * out + so] : T(0);
+      const uint32_t so = pp * nb + g;
+      vals[i] = so < ou ? srow[so] : T(0);
+      if (++pp == q) pp = 0, ++g;
     }
     u32x4 w;
     __builtin_memcpy(&w, vals, sizeof(w));
-    *reinterpret_cast<u32x4*>(dst + e * VEC) = w;
+    *reinterpret_cast<u32x4*>(dst + static_cast<int64_t>(e) * VEC) = w;
   }
 }
 
@@ -555,8 +560,18 @@ __global__ __launch_bounds__(256) void bias_partials_kernel(const T* __restrict_
   const int64_t g = col / q2o, pp = col - g * q2o, o = pp * b2 + g;
   if (o >= out) return;
   const int64_t r0 = c * chunk, r1 = r0 + chunk < rows ? r0 + chunk : rows;
+  // eight rows' loads in flight, added in row order
   float acc = 0.f;
-  for (int64_t b = r0; b < r1; ++b) acc += Io<T>::load(dV, b * oext + col);
+  const T* src = dV + col;
+  int64_t b = r0;
+  for (; b + 8 <= r1; b += 8) {
+    float v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = Io<T>::load(src, (b + i) * oext);
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc += v[i];
+  }
+  for (; b < r1; ++b) acc += Io<T>::load(src, b * oext);
   partial[c * out + o] = acc;
 }
 
