@@ -36,6 +36,8 @@ def host(t):
     (16, 16, 4, 9, "f32"), (64, 32, 4, 300, "bf16"), (96, 192, 3, 70, "f32"),
     (48, 48, 6, 33, "bf16"), (8, 12, 1, 5, "f32"), (1024, 1024, 32, 1000, "bf16"),
     (768, 3072, 4, 512, "bf16"), (1000, 500, 10, 257, "f32"),
+    # rows longer than one workgroup's LDS: the gathers take the tiled swap
+    (32768, 256, 16, 6, "bf16"), (16000, 160, 16, 5, "f32"),
 ])
 def test_dyad(api, inp, out, nb, batch, dtype):
     print(f"[dyad] in={inp} out={out} nb={nb} batch={batch} {dtype}", flush=True)

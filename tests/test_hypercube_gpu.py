@@ -69,6 +69,14 @@ def test_hyper_small(api, dims, batch, dtype):
 
 
 @pytest.mark.parametrize("dtype", ["bf16", "f32"])
+def test_hyper_large_arrays(api, dtype):
+    """38400 units: the transposes and the first layout swap exceed one
+    workgroup's LDS and take the 32 x 32-tile swap kernel (partial tiles on
+    both axes)."""
+    check(api, (64, 20, 30), 6, dtype, seed=8300)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "f32"])
 def test_hyper_page_lattice(api, dtype):
     """The page's 12288-unit lattice 16 x 24 x 32."""
     check(api, (16, 24, 32), 256, dtype, seed=8200)
