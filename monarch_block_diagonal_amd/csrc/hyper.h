@@ -19,7 +19,9 @@ struct HyperProblem {
   int dtype = 0;
   int64_t esize = 4;
   int64_t splits[kHyperMaxDims] = {}, chunk[kHyperMaxDims] = {};   // batch split of dw_j
-  size_t ws_g[2] = {}, ws_part[kHyperMaxDims] = {}, ws_total = 0;
+  // backward workspace: two gradient buffers, the weight-gradient partials
+  // and per-fiber transposed weights for the fiber kernel's data products
+  size_t ws_g[2] = {}, ws_part[kHyperMaxDims] = {}, ws_wt = 0, ws_total = 0;
 };
 
 struct HyperBuffers {
@@ -34,7 +36,7 @@ struct HyperBuffers {
   void* ws = nullptr;
 };
 
-constexpr int kHyperMaxSteps = 3 * kHyperMaxDims + 4;
+constexpr int kHyperMaxSteps = 4 * kHyperMaxDims + 4;
 
 // Checks the lattice (1..4 dimensions, positive, N < 2^31), batch and dtype;
 // returns a monarch_status. hyper_saved_elems: elements the forward keeps.

@@ -58,6 +58,14 @@ int64_t prod(const int64_t* d, int lo, int hi) {
   return p;
 }
 
+// round j on fibers of n_j by the fiber kernel (inputs and outputs in L_j)
+void set_fiber(SeqStep& st, const HyperProblem& hp, int j, const void* in, const void* w,
+               void* out) {
+  st.kind = SEQ_FIBER;
+  st.t_in = in, st.t_out = out, st.f_w = w;
+  st.t_rows = hp.batch, st.f_N = hp.N, st.f_n = hp.dims[j];
+}
+
 // the axis swap L_j -> L_{j+1} (up = true) or L_j -> L_{j-1} (up = false)
 void set_swap(SeqStep& st, const HyperProblem& hp, int j, bool up, const void* in, void* out) {
   const int lo = up ? j : j - 1;   // the swap exchanges axes lo and lo + 1
@@ -102,6 +110,12 @@ int make_hyper(int ndims, const int64_t* dims, int64_t batch, int dtype, HyperPr
       p.ws_part[j] = off;
       off = align256(off + static_cast<size_t>(p.splits[j]) * (n / nj) * nj * nj * 4);
     }
+    size_t wt = 0;
+    for (int j = 0; j < ndims; ++j)
+      if (fiber_applicable(p.dims[j], dtype == MONARCH_BF16))
+        wt = static_cast<size_t>(n) * p.dims[j] * p.esize > wt ? static_cast<size_t>(n) * p.dims[j] * p.esize : wt;
+    p.ws_wt = off;
+    off = align256(off + wt);
   }
   p.ws_total = off;
   *hp = p;
@@ -126,17 +140,22 @@ int hyper_plan_fwd(const HyperProblem& hp, const HyperBuffers& b, SeqStep* steps
   }
   for (int j = 0; j < k; ++j) {
     const int64_t n = hp.dims[j];
+    const void* in = k > 1 ? static_cast<const void*>(slot(j)) : b.x;   // L_j
     SeqStep& st = steps[ns++];
-    st.kind = SEQ_GEMM;
     st.name = "hyper_round_fwd";
-    GemmArgs& a = st.g;
-    a.A = k > 1 ? static_cast<const void*>(slot(j)) : b.x;   // L_j
-    a.a_sb = n, a.a_sk = 1, a.a_si = hp.N;
-    a.B = b.w[j];
-    a.b_sb = n * n, a.b_sk = 1, a.b_sj = n;
-    a.C = b.y;                                                // L_j
-    a.c_sb = n, a.c_sj = 1, a.c_si = hp.N;
-    a.M = hp.batch, a.N = n, a.K = n, a.nblk = hp.N / n;
+    if (fiber_applicable(n, hp.dtype == MONARCH_BF16)) {
+      set_fiber(st, hp, j, in, b.w[j], b.y);
+    } else {
+      st.kind = SEQ_GEMM;
+      GemmArgs& a = st.g;
+      a.A = in;
+      a.a_sb = n, a.a_sk = 1, a.a_si = hp.N;
+      a.B = b.w[j];
+      a.b_sb = n * n, a.b_sk = 1, a.b_sj = n;
+      a.C = b.y;                                                // L_j
+      a.c_sb = n, a.c_sj = 1, a.c_si = hp.N;
+      a.M = hp.batch, a.N = n, a.K = n, a.nblk = hp.N / n;
+    }
     if (j < k - 1) set_swap(steps[ns++], hp, j, true, b.y, slot(j + 1));
   }
   return ns;
@@ -182,7 +201,19 @@ int hyper_plan_bwd(const HyperProblem& hp, const HyperBuffers& b, SeqStep* steps
       a.splits = hp.splits[j], a.k_chunk = hp.chunk[j];
       a.M = n, a.N = n, a.K = hp.batch, a.nblk = nf;
     }
-    {
+    void* gout = k > 1 ? g0 : b.dx;                // L_j
+    if (fiber_applicable(n, hp.dtype == MONARCH_BF16)) {
+      // per-fiber transposed weights, then the fiber products with them
+      void* wt = ws + hp.ws_wt;
+      SeqStep& sw = steps[ns++];
+      sw.kind = SEQ_SWAP;
+      sw.name = "hyper_weight_transpose";
+      sw.t_in = b.w[j], sw.t_out = wt;
+      sw.t_rows = nf, sw.t_A = n, sw.t_M = 1, sw.t_C = n;
+      SeqStep& st = steps[ns++];
+      st.name = "hyper_round_bwd_data";
+      set_fiber(st, hp, j, g, wt, gout);
+    } else {
       SeqStep& st = steps[ns++];
       st.kind = SEQ_GEMM;
       st.name = "hyper_round_bwd_data";
@@ -191,7 +222,7 @@ int hyper_plan_bwd(const HyperProblem& hp, const HyperBuffers& b, SeqStep* steps
       a.a_sb = n, a.a_si = hp.N, a.a_sk = 1;
       a.B = b.w[j];
       a.b_sb = n * n, a.b_sk = n, a.b_sj = 1;
-      a.C = k > 1 ? g0 : b.dx;                     // L_j
+      a.C = gout;
       a.c_sb = n, a.c_sj = 1, a.c_si = hp.N;
       a.M = hp.batch, a.N = n, a.K = n, a.nblk = nf;
     }
@@ -227,6 +258,8 @@ hipError_t seq_launch(const SeqStep& st, bool bf16, hipStream_t s) {
     case SEQ_ZERO: return launch_zero(st.zero_ptr, st.zero_bytes, s);
     case SEQ_SWAP:
       return launch_swap(st.t_in, st.t_out, st.t_rows, st.t_A, st.t_M, st.t_C, bf16, s);
+    case SEQ_FIBER:
+      return launch_fiber(st.t_in, st.f_w, st.t_out, st.t_rows, st.f_N, st.f_n, bf16, s);
   }
   return hipErrorInvalidValue;
 }

@@ -66,6 +66,13 @@ hipError_t launch_gemm(const GemmArgs& a, bool bf16, hipStream_t s);
 hipError_t launch_dv_gather(const void* dy, const void* ymask, void* dv, int64_t rows, int64_t out,
                             int64_t b2, int64_t q2o, bool bf16, hipStream_t s);
 
+// Per-fiber products of a lattice round on fibers of n (bf16, n in
+// {16, 24, 32}): out[b, f*n + p] = sum_t w[f][p][t] in[b, f*n + t] for
+// `batch` rows of N elements (fiber.hip).
+bool fiber_applicable(int64_t n, bool bf16);
+hipError_t launch_fiber(const void* in, const void* w, void* out, int64_t batch, int64_t N,
+                        int64_t n, bool bf16, hipStream_t s);
+
 // Axis swap of `rows` row-major A x M x C arrays: out[b][c][m][a] =
 // in[b][a][m][c] (M = 1: a per-row transpose; lattice layout changes).
 hipError_t launch_swap(const void* in, void* out, int64_t rows, int64_t A, int64_t M, int64_t C,

@@ -11,7 +11,7 @@
 
 namespace monarch {
 
-enum SeqKind { SEQ_GEMM, SEQ_REDUCE, SEQ_ZERO, SEQ_SWAP };
+enum SeqKind { SEQ_GEMM, SEQ_REDUCE, SEQ_ZERO, SEQ_SWAP, SEQ_FIBER };
 
 struct SeqStep {
   SeqKind kind = SEQ_GEMM;
@@ -24,6 +24,10 @@ struct SeqStep {
   const void* t_in = nullptr;
   void* t_out = nullptr;
   int64_t t_rows = 0, t_A = 0, t_M = 1, t_C = 0;
+  // SEQ_FIBER: t_out[b, f*f_n + p] = sum_t f_w[f][p][t] t_in[b, f*f_n + t]
+  // for t_rows rows of f_N elements
+  const void* f_w = nullptr;
+  int64_t f_N = 0, f_n = 0;
 };
 
 hipError_t seq_launch(const SeqStep& st, bool bf16, hipStream_t s);

@@ -259,10 +259,15 @@ def test_hyper_sizes_and_plan():
     assert M.monarch_hyper_describe(0, dims, 10, B.BF16) == (
         ["hyper_transpose"] + ["hyper_round_fwd", "hyper_permute"] * 2 + ["hyper_round_fwd"])
     assert M.monarch_hyper_describe(0, (64,), 10, B.BF16) == ["hyper_round_fwd"]
-    names = M.monarch_hyper_describe(1, dims, 10, B.BF16)
+    names = M.monarch_hyper_describe(1, dims, 10, B.F32)
     assert names == (["hyper_round_bwd_weight", "hyper_round_bwd_data", "hyper_permute"] * 2
                      + ["hyper_round_bwd_weight", "hyper_round_bwd_data", "hyper_transpose"]
                      + ["reduce_dw"])
+    # bf16 fibers of 16, 24 or 32 units take the fiber kernel, whose data
+    # products use per-fiber transposed weights
+    names = M.monarch_hyper_describe(1, dims, 10, B.BF16)
+    step = ["hyper_round_bwd_weight", "hyper_weight_transpose", "hyper_round_bwd_data"]
+    assert names == (step + ["hyper_permute"]) * 2 + step + ["hyper_transpose", "reduce_dw"]
     assert M.monarch_hyper_describe(1, (64,), 10, B.BF16) == [
         "hyper_round_bwd_weight", "hyper_round_bwd_data", "reduce_dw"]
     assert len(M.monarch_hyper_describe(1, (2, 3, 4, 5), 10, B.BF16)) == 14
