@@ -61,15 +61,20 @@ constexpr int swap_lds_elems(int n) {
   return n + (n / (64 * (4 / static_cast<int>(sizeof(T)))) + 1) * (4 / static_cast<int>(sizeof(T)));
 }
 
+// A workgroup takes `per` consecutive arrays (the last one may take fewer),
+// so that small arrays still give each workgroup a few KB to move.
 template <typename T>
 __global__ __launch_bounds__(256) void swap_lds_kernel(const T* __restrict__ in,
                                                       T* __restrict__ out, int A, int M, int C,
-                                                      int vec) {
+                                                      int vec, int64_t rows, int per) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   T* s = reinterpret_cast<T*>(smem);
   constexpr int V = 16 / sizeof(T);
-  const int n = A * M * C;
-  const int64_t base = static_cast<int64_t>(blockIdx.x) * n;
+  const int na = A * M * C;
+  const int64_t a0 = static_cast<int64_t>(blockIdx.x) * per;
+  const int cnt = rows - a0 < per ? static_cast<int>(rows - a0) : per;
+  const int n = na * cnt;
+  const int64_t base = a0 * na;
   const T* src = in + base;
   T* dst = out + base;
   const int tid = threadIdx.x;
@@ -87,20 +92,22 @@ __global__ __launch_bounds__(256) void swap_lds_kernel(const T* __restrict__ in,
   }
   __syncthreads();
   if (vec) {
-    // output piece o = V consecutive a of one (c, m)
+    // output piece o = V consecutive a of one (c, m) of array k
     for (int q = tid; q < n / V; q += 256) {
-      const int o = q * V, a0 = o % A, cm = o / A, m = cm % M, c = cm / M;
+      const int k = (q * V) / na, o = q * V - k * na;
+      const int a0 = o % A, cm = o / A, m = cm % M, c = cm / M;
       T v[V];
 #pragma unroll
-      for (int e = 0; e < V; ++e) v[e] = s[swap_pos<T>(((a0 + e) * M + m) * C + c)];
+      for (int e = 0; e < V; ++e) v[e] = s[swap_pos<T>(k * na + ((a0 + e) * M + m) * C + c)];
       u32x4 r;
       __builtin_memcpy(&r, v, sizeof(r));
       reinterpret_cast<u32x4*>(dst)[q] = r;
     }
   } else {
-    for (int o = tid; o < n; o += 256) {
+    for (int oo = tid; oo < n; oo += 256) {
+      const int k = oo / na, o = oo - k * na;
       const int a = o % A, cm = o / A, m = cm % M, c = cm / M;
-      dst[o] = s[swap_pos<T>((a * M + m) * C + c)];
+      dst[oo] = s[swap_pos<T>(k * na + (a * M + m) * C + c)];
     }
   }
 }
@@ -156,22 +163,29 @@ hipError_t launch_swap(const void* in, void* out, int64_t rows, int64_t A, int64
   if (rows <= 0 || A <= 0 || M <= 0 || C <= 0) return hipSuccess;
   const int64_t esz = bf16 ? 2 : 4, V = 16 / esz, n = A * M * C;
   constexpr int64_t kLds = 49 * 1024;
+  // arrays per workgroup: about 4K elements of them (fewer, larger
+  // workgroups lose more than they save on bigger arrays)
+  const int64_t per = n < 4096 ? (4096 / n < rows ? 4096 / n : rows) : 1;
+  const int64_t chunk = n * per;
   const int64_t lds_elems =
-      n < (int64_t(1) << 20) ? (bf16 ? swap_lds_elems<uint16_t>(static_cast<int>(n))
-                                     : swap_lds_elems<float>(static_cast<int>(n)))
-                             : n;
-  if (lds_elems * esz <= kLds && rows <= 0x7fffffffLL) {
+      chunk < (int64_t(1) << 20) ? (bf16 ? swap_lds_elems<uint16_t>(static_cast<int>(chunk))
+                                         : swap_lds_elems<float>(static_cast<int>(chunk)))
+                                 : chunk;
+  const int64_t groups = (rows + per - 1) / per;
+  if (lds_elems * esz <= kLds && groups <= 0x7fffffffLL) {
     const int vec = n % V == 0 && A % V == 0 ? 1 : 0;
     const size_t lds = static_cast<size_t>(lds_elems * esz);
-    const dim3 g(static_cast<unsigned>(rows));
+    const dim3 g(static_cast<unsigned>(groups));
     if (bf16)
       hipLaunchKernelGGL(swap_lds_kernel<uint16_t>, g, dim3(256), lds, s,
                          static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out),
-                         static_cast<int>(A), static_cast<int>(M), static_cast<int>(C), vec);
+                         static_cast<int>(A), static_cast<int>(M), static_cast<int>(C), vec, rows,
+                         static_cast<int>(per));
     else
       hipLaunchKernelGGL(swap_lds_kernel<float>, g, dim3(256), lds, s,
                          static_cast<const float*>(in), static_cast<float*>(out),
-                         static_cast<int>(A), static_cast<int>(M), static_cast<int>(C), vec);
+                         static_cast<int>(A), static_cast<int>(M), static_cast<int>(C), vec, rows,
+                         static_cast<int>(per));
     return hipGetLastError();
   }
   const int64_t ta = (A + 31) / 32, tc = (C + 31) / 32;
