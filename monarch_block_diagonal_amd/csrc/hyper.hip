@@ -106,7 +106,10 @@ int make_hyper(int ndims, const int64_t* dims, int64_t batch, int dtype, HyperPr
     }
     for (int j = 0; j < ndims; ++j) {
       const int64_t nj = p.dims[j];
-      splits_for(n / nj, nj, batch, &p.splits[j], &p.chunk[j]);
+      if (fiber_applicable(nj, dtype == MONARCH_BF16))
+        fiber_wgrad_split(batch, n, nj, &p.splits[j], &p.chunk[j]);
+      else
+        splits_for(n / nj, nj, batch, &p.splits[j], &p.chunk[j]);
       p.ws_part[j] = off;
       off = align256(off + static_cast<size_t>(p.splits[j]) * (n / nj) * nj * nj * 4);
     }
@@ -188,7 +191,15 @@ int hyper_plan_bwd(const HyperProblem& hp, const HyperBuffers& b, SeqStep* steps
   for (int j = k - 1; j >= 0; --j) {
     const int64_t n = hp.dims[j], nf = hp.N / n;
     const void* g = j == k - 1 ? b.dy : g1;
-    {
+    const bool fib = fiber_applicable(n, hp.dtype == MONARCH_BF16);
+    if (fib) {
+      SeqStep& st = steps[ns++];
+      st.kind = SEQ_FIBER_WGRAD;
+      st.name = "hyper_round_bwd_weight";
+      st.t_in = g, st.f_in2 = input(j);
+      st.f_part = reinterpret_cast<float*>(ws + hp.ws_part[j]);
+      st.t_rows = hp.batch, st.f_N = hp.N, st.f_n = n, st.f_chunk = hp.chunk[j];
+    } else {
       SeqStep& st = steps[ns++];
       st.kind = SEQ_GEMM;
       st.name = "hyper_round_bwd_weight";
@@ -202,7 +213,7 @@ int hyper_plan_bwd(const HyperProblem& hp, const HyperBuffers& b, SeqStep* steps
       a.M = n, a.N = n, a.K = hp.batch, a.nblk = nf;
     }
     void* gout = k > 1 ? g0 : b.dx;                // L_j
-    if (fiber_applicable(n, hp.dtype == MONARCH_BF16)) {
+    if (fib) {
       // per-fiber transposed weights, then the fiber products with them
       void* wt = ws + hp.ws_wt;
       SeqStep& sw = steps[ns++];
@@ -260,6 +271,9 @@ hipError_t seq_launch(const SeqStep& st, bool bf16, hipStream_t s) {
       return launch_swap(st.t_in, st.t_out, st.t_rows, st.t_A, st.t_M, st.t_C, bf16, s);
     case SEQ_FIBER:
       return launch_fiber(st.t_in, st.f_w, st.t_out, st.t_rows, st.f_N, st.f_n, bf16, s);
+    case SEQ_FIBER_WGRAD:
+      return launch_fiber_wgrad(st.t_in, st.f_in2, st.f_part, st.t_rows, st.f_N, st.f_n,
+                                st.f_chunk, bf16, s);
   }
   return hipErrorInvalidValue;
 }

@@ -72,6 +72,12 @@ hipError_t launch_dv_gather(const void* dy, const void* ymask, void* dv, int64_t
 bool fiber_applicable(int64_t n, bool bf16);
 hipError_t launch_fiber(const void* in, const void* w, void* out, int64_t batch, int64_t N,
                         int64_t n, bool bf16, hipStream_t s);
+// Weight gradient of such a round as fp32 partials [splits][N/n][n][n]:
+// partial[c][f][p][t] = sum over the rows of chunk c of g[b, f*n + p]
+// in[b, f*n + t]; fiber_wgrad_split picks the chunks (multiples of 32 rows).
+void fiber_wgrad_split(int64_t batch, int64_t N, int64_t n, int64_t* splits, int64_t* chunk);
+hipError_t launch_fiber_wgrad(const void* g, const void* in, float* partial, int64_t batch,
+                              int64_t N, int64_t n, int64_t chunk, bool bf16, hipStream_t s);
 
 // Axis swap of `rows` row-major A x M x C arrays: out[b][c][m][a] =
 // in[b][a][m][c] (M = 1: a per-row transpose; lattice layout changes).

@@ -63,6 +63,9 @@ def check(api, dims, batch, dtype, seed=8100):
     ((2, 3, 4), 5, "f32"), ((4, 8), 33, "bf16"), ((8, 4, 2), 40, "f32"),
     ((16, 2, 2, 3), 7, "bf16"), ((6,), 9, "f32"), ((32, 16), 300, "bf16"),
     ((16, 16, 16), 130, "f32"), ((5, 7, 3), 257, "f32"),
+    # bf16 fibers of 24 with a partial segment (15 fibers: 8 + 7) and weight
+    # gradients over several row chunks, the last one ragged
+    ((24, 5, 3), 1000, "bf16"), ((3, 16, 32), 1500, "bf16"),
 ])
 def test_hyper_small(api, dims, batch, dtype):
     check(api, dims, batch, dtype)
