@@ -10,7 +10,9 @@
 // is kept in stage 2's order and dY is gathered into block-major order (both
 // arranged by the planner), so operand tiles move as 16-byte pieces.
 //
-// Workgroup: 256 threads = 4 waves in a WM x WN grid; each wave owns FM x FN
+// Workgroup: 256 threads = 4 waves in a WM x WN grid (512 threads = 8 waves
+// for the bf16 256 x 256 tile, 128 x 64 per wave: half the operand bytes
+// per product of the 128 x 128 tile); each wave owns FM x FN
 // 16x16 MFMA tiles (bf16: v_mfma_f32_16x16x32_bf16, fp32:
 // v_mfma_f32_16x16x4_f32; fp32 accumulation). K step: 64 (bf16) or 32
 // (fp32). Both operand tiles sit in LDS as [row][k] with a 16-byte skew per
@@ -28,7 +30,6 @@
 namespace monarch {
 namespace {
 
-constexpr int TT = 256;
 
 template <typename T>
 struct Cfg {
@@ -55,7 +56,7 @@ __device__ __forceinline__ u32x4 ld16(const void* p) { return *static_cast<const
 // or the K range are loaded from a clamped in-range address and stored as
 // zeros. An operand row sits at base + (r / ns)*hi + (r % ns)*lo (ns > 0,
 // mode 1 only) or base + r*lo; `sk` is the K stride.
-template <typename T, int MODE, int ROWS, bool EW, int SLOTS>
+template <typename T, int MODE, int ROWS, bool EW, int SLOTS, int TT>
 struct Tile {
   using C = Cfg<T>;
   static constexpr int VEC = C::VEC, TK = C::TK;
@@ -213,9 +214,13 @@ struct Tile {
 };
 
 // K tiles kept in flight in registers: two, or one for the 256-row tiles,
-// whose A tile alone takes as many registers as two slots of the others.
+// whose A tile alone takes as many registers as two slots of the others; LDS
+// buffers: two, or one for the 256 x 64 and 256 x 32 tiles (the 256 x 256
+// tile keeps one register slot and two buffers).
 template <int TM>
 constexpr int kSlots = TM > 128 ? 1 : 2;
+template <int TM, int TN>
+constexpr int kBufs = TM > 128 && TN < 256 ? 1 : 2;
 
 // Four consecutive elements of the I/O type as fp32 (8-byte bf16 or 16-byte
 // fp32 accesses; offsets are multiples of four).
@@ -241,19 +246,19 @@ template <> struct Vec4<uint16_t> {
 };
 
 template <typename T, int AM, int BMD, int WM, int WN, int FM, int FN, bool EW>
-__global__ __launch_bounds__(TT) __attribute__((amdgpu_waves_per_eu(2)))
+__global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void tiled_gemm_kernel(GemmArgs p, int64_t m_tiles,
                                                         int64_t n_tiles, int remap, int avec,
                                                         int bvec) {
   using C = Cfg<T>;
   constexpr int TM = WM * FM * 16, TN = WN * FN * 16, TK = C::TK;
-  static_assert(WM * WN == 4, "four waves");
-  constexpr int SL = kSlots<TM>;
-  using TA = Tile<T, AM, TM, EW, SL>;
-  using TB = Tile<T, BMD, TN, EW, SL>;
-  // two LDS buffers when two K tiles are in flight in registers
-  __shared__ __attribute__((aligned(16))) T As[SL][TA::LDS];
-  __shared__ __attribute__((aligned(16))) T Bs[SL][TB::LDS];
+  static_assert(WM * WN == 4 || WM * WN == 8, "four or eight waves");
+  constexpr int TT = WM * WN * 64;
+  constexpr int SL = kSlots<TM>, LB = kBufs<TM, TN>;
+  using TA = Tile<T, AM, TM, EW, SL, TT>;
+  using TB = Tile<T, BMD, TN, EW, SL, TT>;
+  __shared__ __attribute__((aligned(16))) T As[LB][TA::LDS];
+  __shared__ __attribute__((aligned(16))) T Bs[LB][TB::LDS];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int l15 = lane & 15, lh = lane >> 4;
@@ -300,6 +305,10 @@ void tiled_gemm_kernel(GemmArgs p, int64_t m_tiles,
   //  * Two slots: step t multiplies buffer t % 2 while it stores tile t + 1
   //    (slot (t + 1) % 2) into the other buffer and reloads that slot with
   //    tile t + 3; one barrier per step, and a load has two steps to land.
+  //  * One slot, two buffers (256 x 256): step t multiplies buffer t % 2,
+  //    stores tile t + 1 from the slot into the other buffer and reloads the
+  //    slot with tile t + 2; one barrier per step, and a load has one
+  //    multiply of eight waves to land.
   const int64_t nsteps = kb < ke ? (ke - kb + TK - 1) / TK : 0;
   auto mult = [&](const T* as, const T* bs) {
     if constexpr (C::kBf16) {
@@ -343,7 +352,37 @@ void tiled_gemm_kernel(GemmArgs p, int64_t m_tiles,
       }
     }
   };
-  if constexpr (SL == 1) {
+  if constexpr (SL == 1 && LB == 2) {
+    if (nsteps > 0) {
+      a.template load<0>(kb);
+      b.template load<0>(kb);
+      a.template store<0>(As[0], kb);
+      b.template store<0>(Bs[0], kb);
+      if (nsteps > 1) {
+        a.template load<0>(kb + TK);
+        b.template load<0>(kb + TK);
+      }
+      __syncthreads();
+    }
+    auto step = [&](auto buf, int64_t t) {
+      constexpr int S = decltype(buf)::value, S1 = 1 - S;
+      const int64_t k1 = kb + (t + 1) * TK;
+      mult(As[S], Bs[S]);
+      if (t + 1 < nsteps) {
+        a.template store<0>(As[S1], k1);
+        b.template store<0>(Bs[S1], k1);
+        if (t + 2 < nsteps) {
+          a.template load<0>(k1 + TK);
+          b.template load<0>(k1 + TK);
+        }
+      }
+      __syncthreads();
+    };
+    for (int64_t t = 0; t < nsteps; t += 2) {
+      step(std::integral_constant<int, 0>{}, t);
+      if (t + 1 < nsteps) step(std::integral_constant<int, 1>{}, t + 1);
+    }
+  } else if constexpr (SL == 1) {
     if (nsteps > 0) {
       a.template load<0>(kb);
       b.template load<0>(kb);
@@ -406,7 +445,8 @@ void tiled_gemm_kernel(GemmArgs p, int64_t m_tiles,
 #pragma unroll
     for (int ni = 0; ni < FN; ++ni) {
       const int64_t jb = j0 + (wn * FN + ni) * 16 + (l15 & ~3);
-      const int64_t cpos = cblk + jb;
+      // with a column split the four columns stay within one piece
+      const int64_t cpos = cblk + (p.nsplit > 0 ? col_off(jb, p.nsplit, p.c_sj_hi, 1) : jb);
 #pragma unroll
       for (int mi = 0; mi < FM; ++mi) {
         const f32x4 in = acc[mi][ni];
@@ -576,9 +616,12 @@ __global__ __launch_bounds__(256) void bias_partials_kernel(const T* __restrict_
 }
 
 // Tile shapes (TM x TN) and their wave grids
-enum Shape { S128x128, S256x64, S256x32, S64x64, S32x32 };
+enum Shape { S256x256, S128x128, S256x64, S256x32, S64x64, S32x32 };
 
-Shape pick_shape(int64_t M, int64_t N) {
+// 256 x 256 only for bf16 products without a batch split: a split product
+// would need four times the splits (and fp32 partials) to fill the chip
+Shape pick_shape(int64_t M, int64_t N, bool bf16, bool split) {
+  if (bf16 && !split && M >= 256 && N >= 256) return S256x256;
   if (M >= 256) {
     if (N > 64) return S128x128;
     if (N > 32) return S256x64;
@@ -592,6 +635,7 @@ Shape pick_shape(int64_t M, int64_t N) {
 
 void shape_tiles(Shape s, int* tm, int* tn) {
   switch (s) {
+    case S256x256: *tm = 256, *tn = 256; return;
     case S128x128: *tm = 128, *tn = 128; return;
     case S256x64: *tm = 256, *tn = 64; return;
     case S256x32: *tm = 256, *tn = 32; return;
@@ -609,12 +653,19 @@ hipError_t launch_modes(const GemmArgs& a, Shape sh, dim3 g, int64_t mt, int64_t
                         int avec, int bvec, hipStream_t s) {
 #define MONARCH_TILED(WM, WN, FM, FN)                                                         \
   if (avec && bvec)                                                                             \
-    hipLaunchKernelGGL((tiled_gemm_kernel<T, AM, BMD, WM, WN, FM, FN, false>), g, dim3(TT), 0, s, \
-                       a, mt, nt, remap, 1, 1);                                                 \
+    hipLaunchKernelGGL((tiled_gemm_kernel<T, AM, BMD, WM, WN, FM, FN, false>), g,              \
+                       dim3(WM * WN * 64), 0, s, a, mt, nt, remap, 1, 1);                        \
   else                                                                                          \
-    hipLaunchKernelGGL((tiled_gemm_kernel<T, AM, BMD, WM, WN, FM, FN, true>), g, dim3(TT), 0, s,  \
-                       a, mt, nt, remap, avec, bvec)
+    hipLaunchKernelGGL((tiled_gemm_kernel<T, AM, BMD, WM, WN, FM, FN, true>), g,               \
+                       dim3(WM * WN * 64), 0, s, a, mt, nt, remap, avec, bvec)
   switch (sh) {
+    case S256x256:
+      if constexpr (std::is_same<T, uint16_t>::value) {
+        MONARCH_TILED(2, 4, 8, 4);
+      } else {
+        return hipErrorInvalidValue;
+      }
+      break;
     case S128x128: MONARCH_TILED(2, 2, 4, 4); break;
     case S256x64: MONARCH_TILED(4, 1, 4, 4); break;
     case S256x32: MONARCH_TILED(4, 1, 4, 2); break;
@@ -648,9 +699,10 @@ hipError_t launch_gemm(const GemmArgs& a, bool bf16, hipStream_t s) {
                                a.N % vec == 0 && lim_ok(a.n_lim, a.n_lim_bs, vec));
   if (a.partial && (a.k_chunk % kSplitK != 0 || a.nsplit > 0)) return hipErrorInvalidValue;
   GemmArgs g4 = a;
-  g4.cvec = !a.partial && a.nsplit == 0 && a.c_sj == 1 && a.c_sb % 4 == 0 && a.c_si % 4 == 0 &&
+  g4.cvec = !a.partial && (a.nsplit == 0 || (a.nsplit % 4 == 0 && a.c_sj_hi % 4 == 0)) &&
+            a.c_sj == 1 && a.c_sb % 4 == 0 && a.c_si % 4 == 0 &&
             a.N % 4 == 0 && (a.c_cols < 0 || a.c_cols % 4 == 0);
-  const Shape sh = pick_shape(a.M, a.N);
+  const Shape sh = pick_shape(a.M, a.N, bf16, a.partial != nullptr);
   int tm, tn;
   shape_tiles(sh, &tm, &tn);
   const int64_t mt = (a.M + tm - 1) / tm, nt = (a.N + tn - 1) / tn;
@@ -676,6 +728,9 @@ hipError_t launch_dv_gather(const void* dy, const void* ymask, void* dv, int64_t
                             int64_t b2, int64_t q2o, bool bf16, hipStream_t s) {
   const int64_t oext = b2 * q2o;
   if (rows <= 0 || oext <= 0) return hipSuccess;
+  // unmasked and untruncated: each row's [q2o][b2] becomes [b2][q2o], the
+  // axis swap (padded LDS tiles, several rows per workgroup)
+  if (!ymask && out == oext) return launch_swap(dy, dv, rows, q2o, 1, b2, bf16, s);
   const int esz = bf16 ? 2 : 4, vec = 16 / esz;
   constexpr int64_t kLds = 32768;
   const int64_t row_bytes = out * esz;

@@ -310,6 +310,11 @@ SHAPES = [
     (1024, 1024, 8, 8, 77),
     (2048, 2048, 16, 16, 129),
     (768, 3072, 4, 4, 100),
+    # bf16 256 x 256 tiles with ragged rows, ragged columns (520) and a K of
+    # 300 (element-wise operand loads)
+    (768, 3072, 4, 4, 1000),
+    (600, 1040, 2, 2, 600),
+    (1024, 2048, 2, 2, 513),
     (250, 100, 5, 2, 45),
     (36, 36, 6, 6, 17),
     (8, 8, 2, 4, 3),
