@@ -245,6 +245,38 @@ template <> struct Vec4<uint16_t> {
   }
 };
 
+// Row (u - r) & 3 of a lane's four values, chosen on the bits of the lane
+// index u within its quad.
+__device__ __forceinline__ float pick4(const f32x4& v, int k) {
+  const float lo = (k & 1) ? v[1] : v[0];
+  const float hi = (k & 1) ? v[3] : v[2];
+  return (k & 2) ? hi : lo;
+}
+template <int CTRL>
+__device__ __forceinline__ float quad_read(float v) {
+  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+// 4x4 transpose within a quad of lanes: lane u holds rows 0..3 of column u
+// of a 4x4 block and returns row u, columns 0..3. Rotation r moves, by a
+// quad permutation where lane u reads lane (u + r) & 3, the value each lane
+// holds for the lane that reads it.
+__device__ __forceinline__ f32x4 quad_transpose4(const f32x4& in, int u) {
+  const float g0 = pick4(in, u);
+  const float g1 = quad_read<0x39>(pick4(in, (u - 1) & 3));   // quad_perm [1,2,3,0]
+  const float g2 = quad_read<0x4e>(pick4(in, (u - 2) & 3));   // quad_perm [2,3,0,1]
+  const float g3 = quad_read<0x93>(pick4(in, (u - 3) & 3));   // quad_perm [3,0,1,2]
+  // g_r is column (u + r) & 3
+  f32x4 o;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) {
+    const int r = (c - u) & 3;
+    const float lo = (r & 1) ? g1 : g0;
+    const float hi = (r & 1) ? g3 : g2;
+    o[c] = (r & 2) ? hi : lo;
+  }
+  return o;
+}
+
 template <typename T, int AM, int BMD, int WM, int WN, int FM, int FN, bool EW>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void tiled_gemm_kernel(GemmArgs p, int64_t m_tiles,
@@ -437,10 +469,56 @@ void tiled_gemm_kernel(GemmArgs p, int64_t m_tiles,
 
   // 16x16 result layout: lane holds rows 4*(lane/16)+v, column lane%16
   const int64_t cblk = blk * p.c_sb;
+  // a whole tile of plain stores (the common case) skips the per-element
+  // range checks and flags and steps row offsets by the row stride
+  const bool plain = !p.partial && !p.accum && !p.bias && !p.relu && p.c_cols < 0 &&
+                     i0 + TM <= p.M && j0 + TN <= p.N;
+  // offset of this lane's first row (v = 0 of tile row 0)
+  const int64_t rb = (i0 + wm * FM * 16 + 4 * lh) * p.c_si;
+  if (p.cvec && plain) {
+    const int u = l15 & 3;
+#pragma unroll
+    for (int ni = 0; ni < FN; ++ni) {
+      const int64_t jb = j0 + (wn * FN + ni) * 16 + (l15 & ~3);
+      const int64_t cpos = cblk + (p.nsplit > 0 ? col_off(jb, p.nsplit, p.c_sj_hi, 1) : jb);
+      T* c = static_cast<T*>(p.C) + rb + u * p.c_si + cpos;
+#pragma unroll
+      for (int mi = 0; mi < FM; ++mi)
+        Vec4<T>::store(c, mi * 16 * p.c_si, quad_transpose4(acc[mi][ni], u));
+    }
+    return;
+  }
+  if (p.partial && i0 + TM <= p.M && j0 + TN <= p.N) {
+    float* P = p.partial + ((split * p.nblk + blk) * p.M + i0 + wm * FM * 16 + 4 * lh) * p.N + j0 +
+               wn * FN * 16 + l15;
+#pragma unroll
+    for (int ni = 0; ni < FN; ++ni)
+#pragma unroll
+      for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) P[(mi * 16 + v) * p.N + ni * 16] = acc[mi][ni][v];
+    return;
+  }
+  if (plain) {
+#pragma unroll
+    for (int ni = 0; ni < FN; ++ni) {
+      const int64_t j = j0 + (wn * FN + ni) * 16 + l15;
+      T* c = static_cast<T*>(p.C) + rb + cblk + col_off(j, p.nsplit, p.c_sj_hi, p.c_sj);
+#pragma unroll
+      for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) Io<T>::store(c, (mi * 16 + v) * p.c_si, acc[mi][ni][v]);
+    }
+    return;
+  }
   if (p.cvec) {
     // a 4x4 transpose within each quad of lanes (columns 4c..4c+3) leaves
     // lane 4c+u with row 4*(lane/16)+u, columns 4c..4c+3: one 4-element
-    // load/store per row instead of four single elements
+    // load/store per row instead of four single elements. In rotation r
+    // lane u sends its row (u - r) & 3 and receives, by a DPP quad
+    // permutation (lane u reads lane (u + r) & 3), row u of column
+    // (u + r) & 3; the selections are two-level on the bits of a
+    // loop-invariant lane index, so they stay selects, not branches.
     const int u = l15 & 3;
 #pragma unroll
     for (int ni = 0; ni < FN; ++ni) {
@@ -449,21 +527,7 @@ void tiled_gemm_kernel(GemmArgs p, int64_t m_tiles,
       const int64_t cpos = cblk + (p.nsplit > 0 ? col_off(jb, p.nsplit, p.c_sj_hi, 1) : jb);
 #pragma unroll
       for (int mi = 0; mi < FM; ++mi) {
-        const f32x4 in = acc[mi][ni];
-        f32x4 o;
-#pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          // send my row (u - r) & 3 to the lane whose column I hold it for,
-          // receive row u of column (u + r) & 3
-          const int sr = (u - r) & 3;
-          const float send = sr == 0 ? in[0] : sr == 1 ? in[1] : sr == 2 ? in[2] : in[3];
-          const float got = __shfl(send, (lane & ~3) | ((u + r) & 3), 64);
-          const int dc = (u + r) & 3;
-          o[0] = dc == 0 ? got : o[0];
-          o[1] = dc == 1 ? got : o[1];
-          o[2] = dc == 2 ? got : o[2];
-          o[3] = dc == 3 ? got : o[3];
-        }
+        f32x4 o = quad_transpose4(acc[mi][ni], u);
         const int64_t i = i0 + (wm * FM + mi) * 16 + 4 * lh + u;
         if (i < p.M && jb < p.N && (p.c_cols < 0 || cpos < p.c_cols)) {
           const int64_t off = i * p.c_si + cpos;

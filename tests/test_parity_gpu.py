@@ -315,6 +315,8 @@ SHAPES = [
     (768, 3072, 4, 4, 1000),
     (600, 1040, 2, 2, 600),
     (1024, 2048, 2, 2, 513),
+    # K = 520 (a last K tile of 8) on the direct-load 256 x 256 path
+    (1040, 1040, 2, 2, 600),
     (250, 100, 5, 2, 45),
     (36, 36, 6, 6, 17),
     (8, 8, 2, 4, 3),
