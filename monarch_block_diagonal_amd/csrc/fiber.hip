@@ -37,25 +37,6 @@ __device__ __forceinline__ bf16x8 as_op(u32x4 v) {
   return r;
 }
 
-// 4x4 transpose within lane quads: lane 4c+u holds column 4c+u of rows
-// 4*lh + (0..3) in `in`; returns row 4*lh + u, columns 4c..4c+3.
-__device__ __forceinline__ f32x4 quad_transpose(f32x4 in, int lane) {
-  const int u = lane & 3;
-  f32x4 o;
-#pragma unroll
-  for (int r = 0; r < 4; ++r) {
-    const int sr = (u - r) & 3;
-    const float send = sr == 0 ? in[0] : sr == 1 ? in[1] : sr == 2 ? in[2] : in[3];
-    const float got = __shfl(send, (lane & ~3) | ((u + r) & 3), 64);
-    const int dc = (u + r) & 3;
-    o[0] = dc == 0 ? got : o[0];
-    o[1] = dc == 1 ? got : o[1];
-    o[2] = dc == 2 ? got : o[2];
-    o[3] = dc == 3 ? got : o[3];
-  }
-  return o;
-}
-
 constexpr int kSeg = 256;          // elements of a fiber segment (at most)
 constexpr int kSegPitch = kSeg + 8;
 
@@ -111,9 +92,9 @@ __global__ __launch_bounds__(256) void fiber_kernel(const uint16_t* __restrict__
       f32x4 o[NT];
 #pragma unroll
       for (int j = 0; j < NT; ++j)
-        o[j] = quad_transpose(__builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                                  as_op(av), as_op(bv[fl][j]), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0),
-                              lane);
+        o[j] = quad_transpose4(__builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                   as_op(av), as_op(bv[fl][j]), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0),
+                               lane & 3);
       // every lane has read this fiber's inputs (one instruction above)
       // before any lane writes its outputs over them
 #pragma unroll

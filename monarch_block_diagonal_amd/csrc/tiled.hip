@@ -245,38 +245,6 @@ template <> struct Vec4<uint16_t> {
   }
 };
 
-// Row (u - r) & 3 of a lane's four values, chosen on the bits of the lane
-// index u within its quad.
-__device__ __forceinline__ float pick4(const f32x4& v, int k) {
-  const float lo = (k & 1) ? v[1] : v[0];
-  const float hi = (k & 1) ? v[3] : v[2];
-  return (k & 2) ? hi : lo;
-}
-template <int CTRL>
-__device__ __forceinline__ float quad_read(float v) {
-  return __int_as_float(__builtin_amdgcn_mov_dpp(__float_as_int(v), CTRL, 0xf, 0xf, false));
-}
-// 4x4 transpose within a quad of lanes: lane u holds rows 0..3 of column u
-// of a 4x4 block and returns row u, columns 0..3. Rotation r moves, by a
-// quad permutation where lane u reads lane (u + r) & 3, the value each lane
-// holds for the lane that reads it.
-__device__ __forceinline__ f32x4 quad_transpose4(const f32x4& in, int u) {
-  const float g0 = pick4(in, u);
-  const float g1 = quad_read<0x39>(pick4(in, (u - 1) & 3));   // quad_perm [1,2,3,0]
-  const float g2 = quad_read<0x4e>(pick4(in, (u - 2) & 3));   // quad_perm [2,3,0,1]
-  const float g3 = quad_read<0x93>(pick4(in, (u - 3) & 3));   // quad_perm [3,0,1,2]
-  // g_r is column (u + r) & 3
-  f32x4 o;
-#pragma unroll
-  for (int c = 0; c < 4; ++c) {
-    const int r = (c - u) & 3;
-    const float lo = (r & 1) ? g1 : g0;
-    const float hi = (r & 1) ? g3 : g2;
-    o[c] = (r & 2) ? hi : lo;
-  }
-  return o;
-}
-
 template <typename T, int AM, int BMD, int WM, int WN, int FM, int FN, bool EW>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void tiled_gemm_kernel(GemmArgs p, int64_t m_tiles,
