@@ -21,9 +21,17 @@ constexpr int64_t kLimit = int64_t(1) << 31;
 
 size_t align256(size_t v) { return (v + 255) / 256 * 256; }
 
-void splits_for(int64_t nblk, int64_t M, int64_t N, int64_t K, int64_t* splits, int64_t* chunk) {
-  const int64_t base = nblk * ((M + 63) / 64) * ((N + 63) / 64);
-  int64_t s = (2048 + base - 1) / base;
+void splits_for(int64_t nblk, int64_t M, int64_t N, int64_t K, bool bf16, int64_t* splits,
+                int64_t* chunk) {
+  int64_t s;
+  if (bf16 && M >= 256 && N >= 256) {
+    // 256 x 256 tiles, one workgroup per CU: about one wave of 256 of them
+    const int64_t base = nblk * ((M + 255) / 256) * ((N + 255) / 256);
+    s = 256 / base;
+  } else {
+    const int64_t base = nblk * ((M + 63) / 64) * ((N + 63) / 64);
+    s = (2048 + base - 1) / base;
+  }
   const int64_t smax = (K + 127) / 128;
   if (s > smax) s = smax;
   if (s > 64) s = 64;
@@ -68,7 +76,7 @@ int make_dyad(int64_t in, int64_t out, int64_t nb, int64_t batch, int dtype, Dya
   p.dtype = dtype;
   p.esize = dtype == MONARCH_BF16 ? 2 : 4;
   if (batch > 0) {
-    splits_for(nb, p.qo, p.qi, batch, &p.splits, &p.chunk);
+    splits_for(nb, p.qo, p.qi, batch, dtype == MONARCH_BF16, &p.splits, &p.chunk);
     const size_t part = static_cast<size_t>(p.splits) * nb * p.qo * p.qi * 4;
     p.ws_pa = 0;
     p.ws_pb = align256(part);

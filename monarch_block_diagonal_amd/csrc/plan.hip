@@ -36,15 +36,22 @@ size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 
 // Batch split for a weight-gradient GEMM with nblk blocks of M x N and
 // reduction length K: enough workgroups to fill the chip, chunks >= 128 rows.
-void choose_splits(int64_t nblk, int64_t M, int64_t N, int64_t K, int64_t* splits,
+void choose_splits(int64_t nblk, int64_t M, int64_t N, int64_t K, bool bf16, int64_t* splits,
                    int64_t* chunk) {
   if (K <= 0) {
     *splits = 1;
     *chunk = 0;
     return;
   }
-  const int64_t base = nblk * ((M + 63) / 64) * ((N + 63) / 64);
-  int64_t s = (2048 + base - 1) / base;
+  int64_t s;
+  if (bf16 && M >= 256 && N >= 256) {
+    // 256 x 256 tiles, one workgroup per CU: about one wave of 256 of them
+    const int64_t base = nblk * ((M + 255) / 256) * ((N + 255) / 256);
+    s = 256 / base;
+  } else {
+    const int64_t base = nblk * ((M + 63) / 64) * ((N + 63) / 64);
+    s = (2048 + base - 1) / base;
+  }
   const int64_t smax_k = (K + 127) / 128;
   if (s > smax_k) s = smax_k;
   if (s > 64) s = 64;
@@ -99,8 +106,8 @@ int make_problem_ex(int64_t in, int64_t out, int64_t mid, int64_t nb1, int64_t n
       sm_wgrad_split(batch, &p.s2, &p.kc2);
       p.s1 = p.s2, p.kc1 = p.kc2;
     } else {
-      choose_splits(p.b2, p.q2o, p.q2i, batch, &p.s2, &p.kc2);
-      choose_splits(p.b1, p.q1o, p.q1i, batch, &p.s1, &p.kc1);
+      choose_splits(p.b2, p.q2o, p.q2i, batch, dtype == MONARCH_BF16, &p.s2, &p.kc2);
+      choose_splits(p.b1, p.q1o, p.q1i, batch, dtype == MONARCH_BF16, &p.s1, &p.kc1);
     }
   }
   if (batch > 0) {

@@ -650,10 +650,10 @@ __global__ __launch_bounds__(256) void bias_partials_kernel(const T* __restrict_
 // Tile shapes (TM x TN) and their wave grids
 enum Shape { S256x256, S128x128, S256x64, S256x32, S64x64, S32x32 };
 
-// 256 x 256 only for bf16 products without a batch split: a split product
-// would need four times the splits (and fp32 partials) to fill the chip
-Shape pick_shape(int64_t M, int64_t N, bool bf16, bool split) {
-  if (bf16 && !split && M >= 256 && N >= 256) return S256x256;
+// 256 x 256 for bf16 products of at least 256 x 256 (batch splits of such
+// products are sized for this tile by the planner)
+Shape pick_shape(int64_t M, int64_t N, bool bf16) {
+  if (bf16 && M >= 256 && N >= 256) return S256x256;
   if (M >= 256) {
     if (N > 64) return S128x128;
     if (N > 32) return S256x64;
@@ -734,7 +734,7 @@ hipError_t launch_gemm(const GemmArgs& a, bool bf16, hipStream_t s) {
   g4.cvec = !a.partial && (a.nsplit == 0 || (a.nsplit % 4 == 0 && a.c_sj_hi % 4 == 0)) &&
             a.c_sj == 1 && a.c_sb % 4 == 0 && a.c_si % 4 == 0 &&
             a.N % 4 == 0 && (a.c_cols < 0 || a.c_cols % 4 == 0);
-  const Shape sh = pick_shape(a.M, a.N, bf16, a.partial != nullptr);
+  const Shape sh = pick_shape(a.M, a.N, bf16);
   int tm, tn;
   shape_tiles(sh, &tm, &tn);
   const int64_t mt = (a.M + tm - 1) / tm, nt = (a.N + tn - 1) / tn;
