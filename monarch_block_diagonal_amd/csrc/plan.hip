@@ -44,8 +44,9 @@ void choose_splits(int64_t nblk, int64_t M, int64_t N, int64_t K, bool bf16, int
     return;
   }
   int64_t s;
-  if (bf16 && M >= 256 && N >= 256) {
-    // 256 x 256 tiles, one workgroup per CU: about one wave of 256 of them
+  if (bf16 && M >= 256 && (N >= 256 || (N > 128 && N <= 192))) {
+    // 256 x 256 (or 256 x 192) tiles, one workgroup per CU: about one wave
+    // of 256 of them
     const int64_t base = nblk * ((M + 255) / 256) * ((N + 255) / 256);
     s = 256 / base;
   } else {

@@ -220,7 +220,7 @@ struct Tile {
 template <int TM>
 constexpr int kSlots = TM > 128 ? 1 : 2;
 template <int TM, int TN>
-constexpr int kBufs = TM > 128 && TN < 256 ? 1 : 2;
+constexpr int kBufs = TM > 128 && TN < 192 ? 1 : 2;
 
 // Four consecutive elements of the I/O type as fp32 (8-byte bf16 or 16-byte
 // fp32 accesses; offsets are multiples of four).
@@ -648,12 +648,14 @@ __global__ __launch_bounds__(256) void bias_partials_kernel(const T* __restrict_
 }
 
 // Tile shapes (TM x TN) and their wave grids
-enum Shape { S256x256, S128x128, S256x64, S256x32, S64x64, S32x32 };
+enum Shape { S256x256, S256x192, S128x128, S256x64, S256x32, S64x64, S32x32 };
 
-// 256 x 256 for bf16 products of at least 256 x 256 (batch splits of such
-// products are sized for this tile by the planner)
+// 256 x 256 for bf16 products of at least 256 x 256, 256 x 192 for those
+// 129 to 192 columns wide (batch splits of such products are sized for these
+// tiles by the planner)
 Shape pick_shape(int64_t M, int64_t N, bool bf16) {
   if (bf16 && M >= 256 && N >= 256) return S256x256;
+  if (bf16 && M >= 256 && N > 128 && N <= 192) return S256x192;
   if (M >= 256) {
     if (N > 64) return S128x128;
     if (N > 32) return S256x64;
@@ -668,6 +670,7 @@ Shape pick_shape(int64_t M, int64_t N, bool bf16) {
 void shape_tiles(Shape s, int* tm, int* tn) {
   switch (s) {
     case S256x256: *tm = 256, *tn = 256; return;
+    case S256x192: *tm = 256, *tn = 192; return;
     case S128x128: *tm = 128, *tn = 128; return;
     case S256x64: *tm = 256, *tn = 64; return;
     case S256x32: *tm = 256, *tn = 32; return;
@@ -694,6 +697,13 @@ hipError_t launch_modes(const GemmArgs& a, Shape sh, dim3 g, int64_t mt, int64_t
     case S256x256:
       if constexpr (std::is_same<T, uint16_t>::value) {
         MONARCH_TILED(2, 4, 8, 4);
+      } else {
+        return hipErrorInvalidValue;
+      }
+      break;
+    case S256x192:
+      if constexpr (std::is_same<T, uint16_t>::value) {
+        MONARCH_TILED(2, 4, 8, 3);
       } else {
         return hipErrorInvalidValue;
       }

@@ -315,8 +315,11 @@ SHAPES = [
     (768, 3072, 4, 4, 1000),
     (600, 1040, 2, 2, 600),
     (1024, 2048, 2, 2, 513),
-    # K = 520 (a last K tile of 8) on the direct-load 256 x 256 path
+    # K = 520 (a last K tile of 8) on the 256 x 256 tile
     (1040, 1040, 2, 2, 600),
+    # 256 x 192 tiles with ragged columns (170: element-wise loads, 176)
+    (340, 680, 2, 2, 700),
+    (352, 704, 2, 2, 700),
     (250, 100, 5, 2, 45),
     (36, 36, 6, 6, 17),
     (8, 8, 2, 4, 3),
