@@ -216,9 +216,147 @@ __global__ __launch_bounds__(256) void fiber_wgrad_kernel(const uint16_t* __rest
   }
 }
 
+// A round fused with the layout swap that follows it, for arrays small
+// enough for LDS: a row holds N/S arrays of S = A*M*n elements, [A][M][n] in
+// the round's layout (fibers of n along the last axis), and each output
+// array takes the same place as [n][M][A]. A workgroup takes array p of 32
+// consecutive rows: it loads them into LDS (16-byte pieces, row pitch S + 8
+// elements), multiplies every fiber in place (wave w takes fibers w, w + 4,
+// ...; all of its fibers' weight fragments in registers, requested before
+// the arrays; one MFMA per 16 outputs and the lane-quad transpose, as
+// fiber_kernel) and writes the arrays out transposed in 16-byte pieces of 8
+// consecutive a.
+// Input and output arrays cover the same bytes of a row, so `in` may equal
+// `out`: a workgroup reads all of its region before it writes any of it.
+constexpr int kFsRows = 32;
+constexpr int64_t kFsMaxArray = 1024;   // elements: 32 rows of LDS in 66 KB
+
+template <int NN>
+__global__ __launch_bounds__(256) void fiber_swap_kernel(const uint16_t* in,
+                                                        const uint16_t* __restrict__ w,
+                                                        uint16_t* out, int64_t B, int64_t N,
+                                                        int S, int A, int M, int npre) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char fs_smem[];
+  uint16_t* sm = reinterpret_cast<uint16_t*>(fs_smem);
+  constexpr int NT = (NN + 15) / 16;
+  const int pitch = S + 8;
+  const int p = static_cast<int>(blockIdx.x % npre);
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x / npre) * kFsRows;
+  const int nr = static_cast<int>(B - r0 < kFsRows ? B - r0 : kFsRows);
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int l15 = lane & 15, lh = lane >> 4;
+  const int64_t off = static_cast<int64_t>(p) * S;
+  const int pieces = S / 8;
+  const int nfib = A * M;
+  const bool kin = 8 * lh < NN;   // this lane's k are real
+
+  // weight fragments of this wave's fibers w + 4i, requested before the
+  // arrays so that both are in flight together
+  constexpr int FMAX = static_cast<int>((kFsMaxArray / NN + 3) / 4);
+  u32x4 bv[FMAX][NT];
+#pragma unroll
+  for (int i = 0; i < FMAX; ++i) {
+    const int f = wv + 4 * i;
+    const int64_t gf = static_cast<int64_t>(p) * nfib + f;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int pr = 16 * j + l15;
+      bv[i][j] = f < nfib && kin && pr < NN
+                     ? *reinterpret_cast<const u32x4*>(w + (gf * NN + pr) * NN + 8 * lh)
+                     : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+
+  // rows past the batch read the last row (never stored)
+  for (int q = tid; q < kFsRows * pieces; q += 256) {
+    const int r = q / pieces, pc = q - r * pieces;
+    const int64_t row = r0 + (r < nr ? r : nr - 1);
+    *reinterpret_cast<u32x4*>(sm + r * pitch + pc * 8) =
+        *reinterpret_cast<const u32x4*>(in + row * N + off + pc * 8);
+  }
+  __syncthreads();
+
+#pragma unroll
+  for (int i = 0; i < FMAX; ++i) {
+    const int f = wv + 4 * i;
+    if (f >= nfib) break;
+#pragma unroll
+    for (int rg = 0; rg < kFsRows / 16; ++rg) {
+      uint16_t* base = sm + (16 * rg) * pitch + f * NN;
+      const u32x4 av = kin ? *reinterpret_cast<const u32x4*>(base + l15 * pitch + 8 * lh)
+                           : u32x4{0u, 0u, 0u, 0u};
+      f32x4 o[NT];
+#pragma unroll
+      for (int j = 0; j < NT; ++j)
+        o[j] = quad_transpose4(__builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                   as_op(av), as_op(bv[i][j]), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0),
+                               lane & 3);
+      // the fiber's inputs were read (above) before its outputs overwrite
+      // them; other waves own other fibers
+#pragma unroll
+      for (int j = 0; j < NT; ++j) {
+        const int p0 = 16 * j + (l15 & ~3);
+        if (p0 < NN)
+          *reinterpret_cast<u32x2*>(base + (4 * lh + (lane & 3)) * pitch + p0) =
+              u32x2{pack_bf16x2(o[j][0], o[j][1]), pack_bf16x2(o[j][2], o[j][3])};
+      }
+    }
+  }
+  __syncthreads();
+
+  // two output pieces per pass: 8 consecutive a of (c, m) and of (c + 1, m),
+  // from 4-byte LDS reads of the element pairs (c, c + 1) of each a (c even)
+  const int na8 = A / 8, dpr = S / 16;
+  for (int q = tid; q < nr * dpr; q += 256) {
+    const int r = q / dpr, dp = q - r * dpr;
+    const int a0 = (dp % na8) * 8, rest = dp / na8, m = rest % M, c = 2 * (rest / M);
+    const uint32_t* src =
+        reinterpret_cast<const uint32_t*>(sm + r * pitch + (a0 * M + m) * NN + c);
+    uint32_t x[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) x[e] = src[e * M * NN / 2];
+    u32x4 lo, hi;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      lo[e] = (x[2 * e] & 0xffffu) | (x[2 * e + 1] << 16);
+      hi[e] = (x[2 * e] >> 16) | (x[2 * e + 1] & 0xffff0000u);
+    }
+    uint16_t* dst = out + (r0 + r) * N + off + a0;
+    *reinterpret_cast<u32x4*>(dst + (c * M + m) * A) = lo;
+    *reinterpret_cast<u32x4*>(dst + ((c + 1) * M + m) * A) = hi;
+  }
+}
+
 }  // namespace
 
 bool fiber_applicable(int64_t n, bool bf16) { return bf16 && (n == 16 || n == 24 || n == 32); }
+
+bool fiber_swap_applicable(int64_t n, int64_t A, int64_t M, bool bf16) {
+  return fiber_applicable(n, bf16) && A > 0 && M > 0 && A % 8 == 0 && A * M * n <= kFsMaxArray;
+}
+
+hipError_t launch_fiber_swap(const void* in, const void* w, void* out, int64_t batch, int64_t N,
+                             int64_t n, int64_t A, int64_t M, bool bf16, hipStream_t s) {
+  const int64_t S = A * M * n;
+  if (!fiber_swap_applicable(n, A, M, bf16) || N % S) return hipErrorInvalidValue;
+  if (batch <= 0) return hipSuccess;
+  const int64_t npre = N / S;
+  const int64_t grid = npre * ((batch + kFsRows - 1) / kFsRows);
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const size_t lds = static_cast<size_t>(kFsRows) * (S + 8) * 2;
+  const uint16_t* ip = static_cast<const uint16_t*>(in);
+  const uint16_t* wp = static_cast<const uint16_t*>(w);
+  uint16_t* op = static_cast<uint16_t*>(out);
+  const dim3 gd(static_cast<unsigned>(grid));
+  const int Si = static_cast<int>(S), Ai = static_cast<int>(A), Mi = static_cast<int>(M),
+            Pi = static_cast<int>(npre);
+  switch (n) {
+    case 16: hipLaunchKernelGGL(fiber_swap_kernel<16>, gd, dim3(256), lds, s, ip, wp, op, batch, N, Si, Ai, Mi, Pi); break;
+    case 24: hipLaunchKernelGGL(fiber_swap_kernel<24>, gd, dim3(256), lds, s, ip, wp, op, batch, N, Si, Ai, Mi, Pi); break;
+    default: hipLaunchKernelGGL(fiber_swap_kernel<32>, gd, dim3(256), lds, s, ip, wp, op, batch, N, Si, Ai, Mi, Pi); break;
+  }
+  return hipGetLastError();
+}
 
 hipError_t launch_fiber(const void* in, const void* w, void* out, int64_t batch, int64_t N,
                         int64_t n, bool bf16, hipStream_t s) {

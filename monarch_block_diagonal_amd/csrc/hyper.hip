@@ -66,6 +66,27 @@ void set_fiber(SeqStep& st, const HyperProblem& hp, int j, const void* in, const
   st.t_rows = hp.batch, st.f_N = hp.N, st.f_n = hp.dims[j];
 }
 
+// arrays of the swap after round j: L_j = [pre][A][M][n_j] with A = n_{j+1}
+// (up) or n_{j-1} (down) and M the product of the axes after the pair
+void swap_array(const HyperProblem& hp, int j, bool up, int64_t* A, int64_t* M) {
+  const int lo = up ? j : j - 1;
+  *A = up ? hp.dims[lo + 1] : hp.dims[lo];
+  *M = prod(hp.dims, lo + 2, hp.k);
+}
+
+// round j on fibers together with the swap that follows it, when the
+// swap's arrays fit the fused kernel
+bool set_fiber_swap(SeqStep& st, const HyperProblem& hp, int j, bool up, const void* in,
+                    const void* w, void* out) {
+  int64_t A, M;
+  swap_array(hp, j, up, &A, &M);
+  if (!fiber_swap_applicable(hp.dims[j], A, M, hp.dtype == MONARCH_BF16)) return false;
+  st.kind = SEQ_FIBER_SWAP;
+  st.t_in = in, st.t_out = out, st.f_w = w;
+  st.t_rows = hp.batch, st.f_N = hp.N, st.f_n = hp.dims[j], st.t_A = A, st.t_M = M;
+  return true;
+}
+
 // the axis swap L_j -> L_{j+1} (up = true) or L_j -> L_{j-1} (up = false)
 void set_swap(SeqStep& st, const HyperProblem& hp, int j, bool up, const void* in, void* out) {
   const int lo = up ? j : j - 1;   // the swap exchanges axes lo and lo + 1
@@ -144,6 +165,10 @@ int hyper_plan_fwd(const HyperProblem& hp, const HyperBuffers& b, SeqStep* steps
   for (int j = 0; j < k; ++j) {
     const int64_t n = hp.dims[j];
     const void* in = k > 1 ? static_cast<const void*>(slot(j)) : b.x;   // L_j
+    if (j < k - 1 && set_fiber_swap(steps[ns], hp, j, true, in, b.w[j], slot(j + 1))) {
+      steps[ns++].name = "hyper_round_fwd_swap";
+      continue;
+    }
     SeqStep& st = steps[ns++];
     st.name = "hyper_round_fwd";
     if (fiber_applicable(n, hp.dtype == MONARCH_BF16)) {
@@ -221,6 +246,12 @@ int hyper_plan_bwd(const HyperProblem& hp, const HyperBuffers& b, SeqStep* steps
       sw.name = "hyper_weight_transpose";
       sw.t_in = b.w[j], sw.t_out = wt;
       sw.t_rows = nf, sw.t_A = n, sw.t_M = 1, sw.t_C = n;
+      // g1 may be both the input and the output: the fused kernel reads
+      // each region before writing it
+      if (j > 0 && set_fiber_swap(steps[ns], hp, j, false, g, wt, g1)) {
+        steps[ns++].name = "hyper_round_bwd_data_swap";
+        continue;
+      }
       SeqStep& st = steps[ns++];
       st.name = "hyper_round_bwd_data";
       set_fiber(st, hp, j, g, wt, gout);
@@ -271,6 +302,9 @@ hipError_t seq_launch(const SeqStep& st, bool bf16, hipStream_t s) {
       return launch_swap(st.t_in, st.t_out, st.t_rows, st.t_A, st.t_M, st.t_C, bf16, s);
     case SEQ_FIBER:
       return launch_fiber(st.t_in, st.f_w, st.t_out, st.t_rows, st.f_N, st.f_n, bf16, s);
+    case SEQ_FIBER_SWAP:
+      return launch_fiber_swap(st.t_in, st.f_w, st.t_out, st.t_rows, st.f_N, st.f_n, st.t_A,
+                               st.t_M, bf16, s);
     case SEQ_FIBER_WGRAD:
       return launch_fiber_wgrad(st.t_in, st.f_in2, st.f_part, st.t_rows, st.f_N, st.f_n,
                                 st.f_chunk, bf16, s);

@@ -76,6 +76,13 @@ hipError_t launch_fiber(const void* in, const void* w, void* out, int64_t batch,
 // partial[c][f][p][t] = sum over the rows of chunk c of g[b, f*n + p]
 // in[b, f*n + t]; fiber_wgrad_split picks the chunks (multiples of 32 rows).
 void fiber_wgrad_split(int64_t batch, int64_t N, int64_t n, int64_t* splits, int64_t* chunk);
+// A round followed by its layout swap, fused: rows of N/S arrays of
+// S = A*M*n elements, [A][M][n] in (fibers of n), each written in place as
+// [n][M][A]; w as for launch_fiber. Needs A % 8 == 0 and S <= 1024; in may
+// equal out.
+bool fiber_swap_applicable(int64_t n, int64_t A, int64_t M, bool bf16);
+hipError_t launch_fiber_swap(const void* in, const void* w, void* out, int64_t batch, int64_t N,
+                             int64_t n, int64_t A, int64_t M, bool bf16, hipStream_t s);
 hipError_t launch_fiber_wgrad(const void* g, const void* in, float* partial, int64_t batch,
                               int64_t N, int64_t n, int64_t chunk, bool bf16, hipStream_t s);
 

@@ -66,6 +66,10 @@ def check(api, dims, batch, dtype, seed=8100):
     # bf16 fibers of 24 with a partial segment (15 fibers: 8 + 7) and weight
     # gradients over several row chunks, the last one ragged
     ((24, 5, 3), 1000, "bf16"), ((3, 16, 32), 1500, "bf16"),
+    # bf16 rounds fused with their layout swap: several arrays per row
+    # ((4, 16, 8): forward round 1), an axis after the pair ((2, 24, 8, 2)),
+    # the backward direction ((8, 32, 2)), batches not a multiple of 32
+    ((4, 16, 8), 77, "bf16"), ((2, 24, 8, 2), 100, "bf16"), ((8, 32, 2), 45, "bf16"),
 ])
 def test_hyper_small(api, dims, batch, dtype):
     check(api, dims, batch, dtype)
