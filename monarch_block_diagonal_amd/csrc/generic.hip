@@ -42,6 +42,37 @@ __global__ __launch_bounds__(256) void reduce_partials_kernel(ReduceArgs a, Redu
   }
 }
 
+// The same with four consecutive elements per thread (every n a multiple of
+// 4): 16-byte partial loads, eight chunks in flight, the same chunk order
+// for every element.
+template <typename T>
+__global__ __launch_bounds__(256) void reduce_partials4_kernel(ReduceArgs a, ReduceArgs b,
+                                                               ReduceArgs c) {
+  const int64_t total = (a.n + b.n + c.n) / 4;
+  for (int64_t e4 = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; e4 < total;
+       e4 += static_cast<int64_t>(gridDim.x) * 256) {
+    const int64_t e = 4 * e4;
+    const bool in_a = e < a.n, in_b = !in_a && e < a.n + b.n;
+    const float* part = in_a ? a.partial : (in_b ? b.partial : c.partial);
+    void* out = in_a ? a.out : (in_b ? b.out : c.out);
+    const int64_t n = in_a ? a.n : (in_b ? b.n : c.n);
+    const int64_t splits = in_a ? a.splits : (in_b ? b.splits : c.splits);
+    const int64_t i = in_a ? e : (in_b ? e - a.n : e - a.n - b.n);
+    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+    int64_t k = 0;
+    for (; k + 8 <= splits; k += 8) {
+      f32x4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = *reinterpret_cast<const f32x4*>(part + (k + j) * n + i);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) s += v[j];
+    }
+    for (; k < splits; ++k) s += *reinterpret_cast<const f32x4*>(part + k * n + i);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) Io<T>::store(out, i + q, s[q]);
+  }
+}
+
 // Axis swaps out[b][c][m][a] = in[b][a][m][c] of batches of A x M x C
 // arrays (the transposes and the layout changes between the rounds of the
 // k-factor layer).
@@ -206,6 +237,18 @@ hipError_t launch_reduce_partials(const ReduceArgs& a, const ReduceArgs& b, cons
                                   bool bf16, hipStream_t s) {
   const int64_t n = a.n + b.n + c.n;
   if (n <= 0) return hipSuccess;
+  // partial buffers are 256-byte aligned workspace regions
+  if (a.n % 4 == 0 && b.n % 4 == 0 && c.n % 4 == 0) {
+    int64_t blocks = (n / 4 + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    if (bf16)
+      hipLaunchKernelGGL(reduce_partials4_kernel<uint16_t>, dim3(static_cast<unsigned>(blocks)),
+                         dim3(256), 0, s, a, b, c);
+    else
+      hipLaunchKernelGGL(reduce_partials4_kernel<float>, dim3(static_cast<unsigned>(blocks)),
+                         dim3(256), 0, s, a, b, c);
+    return hipGetLastError();
+  }
   int64_t blocks = (n + 255) / 256;
   if (blocks > 4096) blocks = 4096;
   if (bf16)
