@@ -229,32 +229,34 @@ __global__ __launch_bounds__(512) void sm_bwd_data_kernel(
 // A[b, blk*32 + i] Bm[b, blk*32 + j], with (A, Bm) = (dV, z) for dL and
 // (dZ, X) for dR
 // --------------------------------------------------------------------------
-// Workgroup: one factor, one block, one chunk of rows; 4 waves, wave w owns
-// the 16 x 16 output tile (w / 2, w % 2). K step: 32 rows. Threads 0-127
-// load the A rows and 128-255 the Bm rows (one 16-byte piece of 8 features
-// each, the next step's piece in flight) and store them transposed,
-// [feature][row], so that both MFMA operands (8 consecutive rows of one
-// feature) are 16-byte LDS reads.
+// Workgroup: one factor, two adjacent blocks (so that every row is read as
+// one 128-byte run), one chunk of rows; 8 waves, wave w owns the 16 x 16
+// output tile ((w / 2) % 2, w % 2) of block w / 4 of the pair. K step: 32
+// rows. Threads 0-255 load the A rows and 256-511 the Bm rows (one 16-byte
+// piece of 8 features each, the next step's piece in flight) and store them
+// transposed, [feature][row], so that both MFMA operands (8 consecutive rows
+// of one feature) are 16-byte LDS reads.
 template <int NB>
-__global__ __launch_bounds__(256) void sm_wgrad_kernel(
+__global__ __launch_bounds__(512) void sm_wgrad_kernel(
     const uint16_t* __restrict__ dV, const uint16_t* __restrict__ Zs,
     const uint16_t* __restrict__ dZ, const uint16_t* __restrict__ X,
     float* __restrict__ part_l, float* __restrict__ part_r, int64_t B, int64_t chunk) {
+  static_assert(NB % 2 == 0, "block pairs");
   constexpr int N = NB * SB, KT = 32, TP = KT + 8;
-  __shared__ __attribute__((aligned(16))) uint16_t ts[2][SB * TP];
+  __shared__ __attribute__((aligned(16))) uint16_t ts[2][2 * SB * TP];
   int bid = blockIdx.x;
-  const int blk = bid % NB;
-  bid /= NB;
+  const int blk = (bid % (NB / 2)) * 2;   // first block of the pair
+  bid /= NB / 2;
   const int fac = bid & 1;
   const int64_t split = bid >> 1;
   const int64_t r0 = split * chunk;
   const int64_t r1 = r0 + chunk < B ? r0 + chunk : B;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l15 = lane & 15, lh = lane >> 4;
-  const int op = tid >> 7, lrow = (tid & 127) >> 2, lcol = (tid & 3) * 8;
+  const int op = tid >> 8, lrow = (tid & 255) >> 3, lcol = (tid & 7) * 8;
   const uint16_t* src = (op ? (fac ? X : Zs) : (fac ? dZ : dV)) + blk * SB + lcol;
   uint16_t* dst = &ts[op][lcol * TP + lrow];
-  const int mi = w >> 1, ni = w & 1;
+  const int pb = w >> 2, mi = (w >> 1) & 1, ni = w & 1;   // block of the pair, tile
 
   // rows past the chunk read as zero (they add nothing to the sums)
   auto load = [&](int64_t b0) -> u32x4 {
@@ -269,13 +271,13 @@ __global__ __launch_bounds__(256) void sm_wgrad_kernel(
     for (int e = 0; e < 8; ++e)
       dst[e * TP] = static_cast<uint16_t>(cur[e >> 1] >> (16 * (e & 1)));
     __syncthreads();
-    const bf16x8 a = ld_op(&ts[0][(16 * mi + l15) * TP + 8 * lh]);
-    const bf16x8 b = ld_op(&ts[1][(16 * ni + l15) * TP + 8 * lh]);
+    const bf16x8 a = ld_op(&ts[0][(SB * pb + 16 * mi + l15) * TP + 8 * lh]);
+    const bf16x8 b = ld_op(&ts[1][(SB * pb + 16 * ni + l15) * TP + 8 * lh]);
     acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc, 0, 0, 0);
     __syncthreads();
     cur = nxt;
   }
-  float* part = (fac ? part_r : part_l) + (split * NB + blk) * SB * SB;
+  float* part = (fac ? part_r : part_l) + (split * NB + blk + pb) * SB * SB;
 #pragma unroll
   for (int v = 0; v < 4; ++v) part[(16 * mi + 4 * lh + v) * SB + 16 * ni + l15] = acc[v];
 }
@@ -327,7 +329,7 @@ hipError_t sm_launch_wgrad(const void* dv, const void* z, const void* dz, const 
                            hipStream_t s) {
   int64_t splits, chunk;
   sm_wgrad_split(batch, &splits, &chunk);
-  const dim3 grid(static_cast<unsigned>(2 * nb * splits)), block(256);
+  const dim3 grid(static_cast<unsigned>(2 * (nb / 2) * splits)), block(512);
   const uint16_t* a = static_cast<const uint16_t*>(dv);
   const uint16_t* b = static_cast<const uint16_t*>(z);
   const uint16_t* c = static_cast<const uint16_t*>(dz);
