@@ -1,10 +1,11 @@
-// k-factor ("hypercube") Monarch layer: planning of its rounds as batched
-// GEMMs (scatterbrain issues page, "hypercube" thread: the N units form a
-// lattice [n_1, ..., n_k]; round j multiplies along axis j with one matrix per
-// index of the other axes, rounds in axis order).
+// k-factor ("hypercube") Monarch layer: planning of its rounds (scatterbrain
+// issues page, "hypercube" thread: the N units form a lattice [n_1, ..., n_k];
+// round j multiplies along axis j with one matrix per index of the other
+// axes, rounds in axis order).
 //
-// Every round is one launch of the tiled GEMM (tiled.hip) with one block per
-// fiber of its axis. Layouts: L_j denotes the lattice with axis j moved to
+// A round is one launch: the fiber kernel (fiber.hip) for bf16 fibers of 16,
+// 24 or 32 units, else the tiled GEMM (tiled.hip) with one block per fiber of
+// its axis; the weight gradients likewise. Layouts: L_j denotes the lattice with axis j moved to
 // the end (the other axes in order), so a fiber of round j is a contiguous
 // run of n_j elements and the fiber index equals the weight index; L_{k-1} is
 // the natural row-major layout. A round reads and writes L_j, and an axis
@@ -19,7 +20,9 @@
 // g_{j+1}[fiber]ᵀ · input_j[fiber] over the batch (split in chunks, summed in
 // a fixed order), and the data gradient g_j = F_jᵀ g_{j+1}, written in L_j,
 // is swapped into L_{j-1}; g_0 is transposed back into dx. A one-dimensional
-// lattice needs no layout change.
+// lattice needs no layout change. Where a swap's arrays are small, a bf16
+// fiber round and the swap after it are one kernel (fiber_swap_kernel), in
+// place in the backward.
 #include "hyper.h"
 #include "monarch.h"
 

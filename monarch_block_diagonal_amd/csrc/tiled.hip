@@ -1,7 +1,7 @@
 // Tiled strided batched GEMM for the generic Monarch path (gfx950).
 //
-// Same contract as generic_gemm_kernel (GemmArgs in kernels.h: a batch of
-// independent block products at affine offsets, ReLU on the result, fp32
+// Contract: GemmArgs in kernels.h (a batch of independent block products at
+// affine offsets, ReLU, bias and accumulation on the result, fp32
 // batch-split partials, the optional column split), for operands whose
 // elements are contiguous along one tile dimension:
 //   A: K-contiguous (mode 1) or M-contiguous (mode 2),
@@ -11,12 +11,12 @@
 // arranged by the planner), so operand tiles move as 16-byte pieces.
 //
 // Workgroup: 256 threads = 4 waves in a WM x WN grid (512 threads = 8 waves
-// for the bf16 256 x 256 tile, 128 x 64 per wave: half the operand bytes
-// per product of the 128 x 128 tile); each wave owns FM x FN
-// 16x16 MFMA tiles (bf16: v_mfma_f32_16x16x32_bf16, fp32:
+// for the bf16 256 x 256 and 256 x 192 tiles, 128 x 64 or 128 x 48 per wave:
+// about half the operand bytes per product of the 128 x 128 tile); each
+// wave owns FM x FN 16x16 MFMA tiles (bf16: v_mfma_f32_16x16x32_bf16, fp32:
 // v_mfma_f32_16x16x4_f32; fp32 accumulation). K step: 64 (bf16) or 32
 // (fp32). Both operand tiles sit in LDS as [row][k] with a 16-byte skew per
-// 8 rows. A mode-1 piece is one 16-byte store; a mode-2 thread loads four
+// 16 rows. A mode-1 piece is one 16-byte store; a mode-2 thread loads four
 // consecutive k rows of one 16-byte piece and transposes them in registers,
 // so it also writes 8- or 16-byte [row][k] runs. The next K tile is loaded
 // into registers while the current one is multiplied. Consecutive workgroups
