@@ -96,3 +96,87 @@ def test_graph_replays_equal_eager(lib, case):
         for name, got, want in zip(("y", "z", "dx", "dw1", "dw2"), outs, ref):
             assert torch.equal(got, want), f"replay {rep}: {name} differs from the eager step"
     say(f"graph case {case}: 3 replays equal the eager step")
+
+
+def replay_equals_eager(step, outs, label):
+    """Eager step, then capture and three replays (after unrelated eager work
+    and with the outputs cleared), each equal to the eager step bit for bit."""
+    step()
+    torch.cuda.synchronize()
+    ref = [t.clone() for t in outs]
+    for t in ref:
+        assert torch.isfinite(t.float()).all()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    other = torch.randn(1 << 20, device="cuda:0")
+    for rep in range(3):
+        other.mul_(1.5).add_(float(rep))
+        torch.cuda.synchronize()
+        for t in outs:
+            t.fill_(float("nan"))
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        for i, (got, want) in enumerate(zip(outs, ref)):
+            assert torch.equal(got, want), f"{label} replay {rep}: output {i} differs from eager"
+    say(f"{label}: 3 replays equal the eager step")
+
+
+def test_graph_hypercube(lib):
+    """bf16 16 x 24 x 32 lattice: fiber rounds, the fused round-and-swap
+    steps (one of them in place), fiber weight gradients and the swaps."""
+    M = lib
+    dims, B = (16, 24, 32), 100
+    N = 16 * 24 * 32
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(77)
+    x = torch.randn((B, N), generator=gen, device="cuda:0").to(torch.bfloat16)
+    dy = torch.randn((B, N), generator=gen, device="cuda:0").to(torch.bfloat16)
+    ws = [torch.randn((N // d, d, d), generator=gen, device="cuda:0").mul_(d ** -0.5)
+          .to(torch.bfloat16) for d in dims]
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+    dws = [torch.empty_like(w) for w in ws]
+    saved = torch.empty((M.monarch_hyper_saved_elems(dims, B),), dtype=torch.bfloat16,
+                        device="cuda:0")
+    need = M.monarch_hyper_bwd_workspace_bytes(dims, B, M.BF16)
+    wsb = torch.empty((need,), dtype=torch.uint8, device="cuda:0")
+    assert "hyper_round_bwd_data_swap" in M.monarch_hyper_describe(1, dims, B, M.BF16)
+
+    def step():
+        M.monarch_hyper_fwd(x, ws, y, saved, dims, B, M.BF16)
+        M.monarch_hyper_bwd(dy, x, ws, saved, dx, dws, wsb, need, dims, B, M.BF16)
+
+    replay_equals_eager(step, [y, saved, dx] + dws, "hypercube 16x24x32")
+
+
+def test_graph_dyad(lib):
+    """bf16 DYAD layer, 512 features in 8 blocks: gathers, both terms and the
+    weight-gradient reduction."""
+    M = lib
+    n, nb, B = 512, 8, 77
+    q = n // nb
+    gen = torch.Generator(device="cuda:0")
+    gen.manual_seed(78)
+    bf = torch.bfloat16
+    x = torch.randn((B, n), generator=gen, device="cuda:0").to(bf)
+    dy = torch.randn((B, n), generator=gen, device="cuda:0").to(bf)
+    wa = torch.randn((nb, q, q), generator=gen, device="cuda:0").mul_(q ** -0.5).to(bf)
+    wb = torch.randn((nb, q, q), generator=gen, device="cuda:0").mul_(q ** -0.5).to(bf)
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+    dwa, dwb = torch.empty_like(wa), torch.empty_like(wb)
+    need = M.monarch_dyad_bwd_workspace_bytes(n, n, nb, B, M.BF16)
+    need_f = M.monarch_dyad_fwd_workspace_bytes(n, n, nb, B, M.BF16)
+    ws = torch.empty((max(need, need_f),), dtype=torch.uint8, device="cuda:0")
+
+    def step():
+        M.monarch_dyad_fwd(x, wa, wb, y, ws, need_f, n, n, nb, B, M.BF16)
+        M.monarch_dyad_bwd(dy, x, wa, wb, dx, dwa, dwb, ws, need, n, n, nb, B, M.BF16)
+
+    replay_equals_eager(step, [y, dx, dwa, dwb], "dyad 512/8")
