@@ -101,6 +101,16 @@ __device__ __forceinline__ void transpose4x8(const u32x4 (&in)[4], u32x2 (&out)[
   }
 }
 
+// 8x8 transpose of bf16 in registers: in[i] holds elements (i, e = 0..7);
+// out[e] gets elements (i = 0..7, e).
+__device__ __forceinline__ void transpose8x8(const u32x4 (&in)[8], u32x4 (&out)[8]) {
+  u32x2 lo[8], hi[8];
+  transpose4x8(*reinterpret_cast<const u32x4(*)[4]>(&in[0]), lo);
+  transpose4x8(*reinterpret_cast<const u32x4(*)[4]>(&in[4]), hi);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = u32x4{lo[e][0], lo[e][1], hi[e][0], hi[e][1]};
+}
+
 // 4x4 transpose of 32-bit elements: out[e][i] = in[i][e].
 __device__ __forceinline__ void transpose4x4(const u32x4 (&in)[4], u32x4 (&out)[4]) {
 #pragma unroll

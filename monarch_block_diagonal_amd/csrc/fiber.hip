@@ -327,9 +327,172 @@ __global__ __launch_bounds__(256) void fiber_swap_kernel(const uint16_t* in,
   }
 }
 
+// Round 0 of a lattice joined with the transposes between the natural
+// layout and L_0 (axis 0 last): fiber f of axis 0 (f < R = N/n, the index of
+// the other axes) has its n elements at c*R + f in the natural layout and at
+// f*n + c in L_0. A workgroup takes 16 rows and 64 consecutive fibers (fewer
+// in a last chunk, a multiple of 8), held in LDS as [row][fiber][n] (row
+// pitch 64n + 8 elements). Forward (DIR 0): x is read in 16-byte pieces of 8
+// consecutive fibers of one element, 8 pieces per task (128-byte runs across
+// the tasks of a wave), and turned by 8x8 register transposes into LDS; the
+// L_0 copy of x (the weight gradient's input) is written, the fibers are
+// multiplied in place (wave w: fibers 16w .. 16w + 15, weights preloaded;
+// one MFMA per 16 outputs and the lane-quad transpose) and the results are
+// written in L_0. Backward (DIR 1): the gradient in L_0 is read straight
+// into LDS, multiplied with the per-fiber transposed weights, and written to
+// dx in the natural layout through the same transposes.
+constexpr int kStRows = 16, kStFib = 64;
+
+template <int NN, int DIR>
+__global__ __launch_bounds__(256) void fiber_strided_kernel(const uint16_t* __restrict__ in,
+                                                           const uint16_t* __restrict__ w,
+                                                           uint16_t* __restrict__ out,
+                                                           uint16_t* __restrict__ save, int64_t B,
+                                                           int64_t N, int nchunks) {
+  extern __shared__ __attribute__((aligned(16))) unsigned char st_smem[];
+  uint16_t* sm = reinterpret_cast<uint16_t*>(st_smem);
+  constexpr int NT = (NN + 15) / 16;
+  constexpr int PITCH = kStFib * NN + 8;
+  constexpr int FW = kStFib / 4;   // fibers per wave
+  constexpr int NG = NN / 8;       // 8-element groups of a fiber
+  const int64_t R = N / NN;
+  const int fc = static_cast<int>(blockIdx.x % nchunks);
+  const int64_t r0 = static_cast<int64_t>(blockIdx.x / nchunks) * kStRows;
+  const int nr = static_cast<int>(B - r0 < kStRows ? B - r0 : kStRows);
+  const int64_t f0 = static_cast<int64_t>(fc) * kStFib;
+  const int nfb = static_cast<int>(R - f0 < kStFib ? R - f0 : kStFib);
+  const int nf8 = nfb / 8;
+  const int per = nfb * NG;        // 16-byte pieces of a row's chunk in L_0
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int l15 = lane & 15, lh = lane >> 4;
+  const bool kin = 8 * lh < NN;
+
+  u32x4 bv[FW][NT];
+#pragma unroll
+  for (int i = 0; i < FW; ++i) {
+    const int f = FW * wv + i;
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int pr = 16 * j + l15;
+      bv[i][j] = f < nfb && kin && pr < NN
+                     ? *reinterpret_cast<const u32x4*>(w + ((f0 + f) * NN + pr) * NN + 8 * lh)
+                     : u32x4{0u, 0u, 0u, 0u};
+    }
+  }
+  // rows past the batch read the last row (never stored)
+  auto copy_out = [&](uint16_t* dst) {
+    for (int q = tid; q < nr * per; q += 256) {
+      const int r = q / per, pc = q - r * per;
+      *reinterpret_cast<u32x4*>(dst + (r0 + r) * N + f0 * NN + pc * 8) =
+          *reinterpret_cast<const u32x4*>(sm + r * PITCH + pc * 8);
+    }
+  };
+  if constexpr (DIR == 0) {
+    // task (row r, element group cg, fiber group fg), fg fastest
+    for (int t = tid; t < kStRows * NG * nf8; t += 256) {
+      const int fg = t % nf8, rest = t / nf8, cg = rest % NG, r = rest / NG;
+      const int64_t row = r0 + (r < nr ? r : nr - 1);
+      const uint16_t* src = in + row * N + static_cast<int64_t>(cg * 8) * R + f0 + fg * 8;
+      u32x4 v[8], tr[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = *reinterpret_cast<const u32x4*>(src + i * R);
+      transpose8x8(v, tr);
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        *reinterpret_cast<u32x4*>(sm + r * PITCH + (fg * 8 + e) * NN + cg * 8) = tr[e];
+    }
+    __syncthreads();
+    copy_out(save);
+    __syncthreads();
+  } else {
+    for (int q = tid; q < kStRows * per; q += 256) {
+      const int r = q / per, pc = q - r * per;
+      const int64_t row = r0 + (r < nr ? r : nr - 1);
+      *reinterpret_cast<u32x4*>(sm + r * PITCH + pc * 8) =
+          *reinterpret_cast<const u32x4*>(in + row * N + f0 * NN + pc * 8);
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < FW; ++i) {
+    const int f = FW * wv + i;
+    if (f >= nfb) break;
+    uint16_t* base = sm + f * NN;
+    const u32x4 av = kin ? *reinterpret_cast<const u32x4*>(base + l15 * PITCH + 8 * lh)
+                         : u32x4{0u, 0u, 0u, 0u};
+    f32x4 o[NT];
+#pragma unroll
+    for (int j = 0; j < NT; ++j)
+      o[j] = quad_transpose4(__builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                                 as_op(av), as_op(bv[i][j]), f32x4{0.f, 0.f, 0.f, 0.f}, 0, 0, 0),
+                             lane & 3);
+    // the fiber's inputs were read (above) before its outputs overwrite them
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int p0 = 16 * j + (l15 & ~3);
+      if (p0 < NN)
+        *reinterpret_cast<u32x2*>(base + (4 * lh + (lane & 3)) * PITCH + p0) =
+            u32x2{pack_bf16x2(o[j][0], o[j][1]), pack_bf16x2(o[j][2], o[j][3])};
+    }
+  }
+  __syncthreads();
+  if constexpr (DIR == 0) {
+    copy_out(out);
+  } else {
+    // task (row r, output group pg, fiber group fg): outputs pg*8 + i of
+    // fibers fg*8 .. fg*8 + 7 -> dx[row, (pg*8 + i)*R + f0 + fg*8 ..]
+    for (int t = tid; t < nr * NG * nf8; t += 256) {
+      const int fg = t % nf8, rest = t / nf8, pg = rest % NG, r = rest / NG;
+      u32x4 v[8], tr[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        v[e] = *reinterpret_cast<const u32x4*>(sm + r * PITCH + (fg * 8 + e) * NN + pg * 8);
+      transpose8x8(v, tr);
+      uint16_t* dst = out + (r0 + r) * N + static_cast<int64_t>(pg * 8) * R + f0 + fg * 8;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) *reinterpret_cast<u32x4*>(dst + i * R) = tr[i];
+    }
+  }
+}
+
 }  // namespace
 
 bool fiber_applicable(int64_t n, bool bf16) { return bf16 && (n == 16 || n == 24 || n == 32); }
+
+bool fiber_strided_applicable(int64_t n, int64_t N, bool bf16) {
+  return fiber_applicable(n, bf16) && N % n == 0 && (N / n) % 8 == 0;
+}
+
+hipError_t launch_fiber_strided(const void* in, const void* w, void* out, void* save,
+                                int64_t batch, int64_t N, int64_t n, int dir, bool bf16,
+                                hipStream_t s) {
+  if (!fiber_strided_applicable(n, N, bf16) || (dir == 0 && !save)) return hipErrorInvalidValue;
+  if (batch <= 0) return hipSuccess;
+  const int64_t R = N / n, nchunks = (R + kStFib - 1) / kStFib;
+  const int64_t grid = nchunks * ((batch + kStRows - 1) / kStRows);
+  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const size_t lds = static_cast<size_t>(kStRows) * (kStFib * n + 8) * 2;
+  const uint16_t* ip = static_cast<const uint16_t*>(in);
+  const uint16_t* wp = static_cast<const uint16_t*>(w);
+  uint16_t* op = static_cast<uint16_t*>(out);
+  uint16_t* sp = static_cast<uint16_t*>(save);
+  const dim3 gd(static_cast<unsigned>(grid));
+  const int nc = static_cast<int>(nchunks);
+#define MONARCH_STRIDED(NN)                                                                     \
+  if (dir == 0)                                                                                 \
+    hipLaunchKernelGGL((fiber_strided_kernel<NN, 0>), gd, dim3(256), lds, s, ip, wp, op, sp,    \
+                       batch, N, nc);                                                           \
+  else                                                                                          \
+    hipLaunchKernelGGL((fiber_strided_kernel<NN, 1>), gd, dim3(256), lds, s, ip, wp, op, sp,    \
+                       batch, N, nc)
+  switch (n) {
+    case 16: MONARCH_STRIDED(16); break;
+    case 24: MONARCH_STRIDED(24); break;
+    default: MONARCH_STRIDED(32); break;
+  }
+#undef MONARCH_STRIDED
+  return hipGetLastError();
+}
 
 bool fiber_swap_applicable(int64_t n, int64_t A, int64_t M, bool bf16) {
   return fiber_applicable(n, bf16) && A > 0 && M > 0 && A % 8 == 0 && A * M * n <= kFsMaxArray;

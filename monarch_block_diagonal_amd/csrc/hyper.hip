@@ -90,6 +90,18 @@ bool set_fiber_swap(SeqStep& st, const HyperProblem& hp, int j, bool up, const v
   return true;
 }
 
+// round 0 joined with the layout change natural <-> L_0 (bf16 fibers of 16,
+// 24 or 32 units, a multiple of 8 of them)
+bool strided_round0(const HyperProblem& hp) {
+  return hp.k > 1 && fiber_strided_applicable(hp.dims[0], hp.N, hp.dtype == MONARCH_BF16);
+}
+void set_strided(SeqStep& st, const HyperProblem& hp, int dir, const void* in, const void* w,
+                 void* out, void* save) {
+  st.kind = SEQ_FIBER_STRIDED;
+  st.t_in = in, st.t_out = out, st.f_w = w, st.f_save = save, st.f_dir = dir;
+  st.t_rows = hp.batch, st.f_N = hp.N, st.f_n = hp.dims[0];
+}
+
 // the axis swap L_j -> L_{j+1} (up = true) or L_j -> L_{j-1} (up = false)
 void set_swap(SeqStep& st, const HyperProblem& hp, int j, bool up, const void* in, void* out) {
   const int lo = up ? j : j - 1;   // the swap exchanges axes lo and lo + 1
@@ -158,7 +170,8 @@ int hyper_plan_fwd(const HyperProblem& hp, const HyperBuffers& b, SeqStep* steps
   // saved slot j: the input of round j in L_j (slot 0 = x)
   auto slot = [&](int sidx) { return static_cast<char*>(b.saved) + sidx * BN * hp.esize; };
   int ns = 0;
-  if (k > 1) {
+  const bool strided = strided_round0(hp);
+  if (k > 1 && !strided) {
     SeqStep& st = steps[ns++];
     st.kind = SEQ_SWAP;
     st.name = "hyper_transpose";
@@ -168,6 +181,13 @@ int hyper_plan_fwd(const HyperProblem& hp, const HyperBuffers& b, SeqStep* steps
   for (int j = 0; j < k; ++j) {
     const int64_t n = hp.dims[j];
     const void* in = k > 1 ? static_cast<const void*>(slot(j)) : b.x;   // L_j
+    if (j == 0 && strided) {
+      // x (natural) -> its L_0 copy in slot 0 and round 0's output in L_0
+      set_strided(steps[ns], hp, 0, b.x, b.w[0], b.y, slot(0));
+      steps[ns++].name = "hyper_transpose_round_fwd";
+      set_swap(steps[ns++], hp, j, true, b.y, slot(j + 1));
+      continue;
+    }
     if (j < k - 1 && set_fiber_swap(steps[ns], hp, j, true, in, b.w[j], slot(j + 1))) {
       steps[ns++].name = "hyper_round_fwd_swap";
       continue;
@@ -249,6 +269,12 @@ int hyper_plan_bwd(const HyperProblem& hp, const HyperBuffers& b, SeqStep* steps
       sw.name = "hyper_weight_transpose";
       sw.t_in = b.w[j], sw.t_out = wt;
       sw.t_rows = nf, sw.t_A = n, sw.t_M = 1, sw.t_C = n;
+      if (j == 0 && strided_round0(hp)) {
+        // round 0's data product straight into dx (natural layout)
+        set_strided(steps[ns], hp, 1, g, wt, b.dx, nullptr);
+        steps[ns++].name = "hyper_round_bwd_data_transpose";
+        continue;
+      }
       // g1 may be both the input and the output: the fused kernel reads
       // each region before writing it
       if (j > 0 && set_fiber_swap(steps[ns], hp, j, false, g, wt, g1)) {
@@ -273,7 +299,7 @@ int hyper_plan_bwd(const HyperProblem& hp, const HyperBuffers& b, SeqStep* steps
     }
     if (j > 0) set_swap(steps[ns++], hp, j, false, g0, g1);
   }
-  if (k > 1) {
+  if (k > 1 && !strided_round0(hp)) {
     SeqStep& st = steps[ns++];
     st.kind = SEQ_SWAP;
     st.name = "hyper_transpose";
@@ -308,6 +334,9 @@ hipError_t seq_launch(const SeqStep& st, bool bf16, hipStream_t s) {
     case SEQ_FIBER_SWAP:
       return launch_fiber_swap(st.t_in, st.f_w, st.t_out, st.t_rows, st.f_N, st.f_n, st.t_A,
                                st.t_M, bf16, s);
+    case SEQ_FIBER_STRIDED:
+      return launch_fiber_strided(st.t_in, st.f_w, st.t_out, st.f_save, st.t_rows, st.f_N, st.f_n,
+                                  st.f_dir, bf16, s);
     case SEQ_FIBER_WGRAD:
       return launch_fiber_wgrad(st.t_in, st.f_in2, st.f_part, st.t_rows, st.f_N, st.f_n,
                                 st.f_chunk, bf16, s);

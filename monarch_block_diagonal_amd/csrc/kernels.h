@@ -81,6 +81,15 @@ void fiber_wgrad_split(int64_t batch, int64_t N, int64_t n, int64_t* splits, int
 // [n][M][A]; w as for launch_fiber. Needs A % 8 == 0 and S <= 1024; in may
 // equal out.
 bool fiber_swap_applicable(int64_t n, int64_t A, int64_t M, bool bf16);
+// Round 0 (fibers of n at stride N/n in the natural layout) joined with the
+// layout change: dir 0 reads natural rows, writes the L_0 copy of the input
+// to `save` and the results in L_0 to `out`; dir 1 reads L_0 rows and writes
+// the results in the natural layout. w as for launch_fiber. Needs N/n a
+// multiple of 8.
+bool fiber_strided_applicable(int64_t n, int64_t N, bool bf16);
+hipError_t launch_fiber_strided(const void* in, const void* w, void* out, void* save,
+                                int64_t batch, int64_t N, int64_t n, int dir, bool bf16,
+                                hipStream_t s);
 hipError_t launch_fiber_swap(const void* in, const void* w, void* out, int64_t batch, int64_t N,
                              int64_t n, int64_t A, int64_t M, bool bf16, hipStream_t s);
 hipError_t launch_fiber_wgrad(const void* g, const void* in, float* partial, int64_t batch,

@@ -11,7 +11,10 @@
 
 namespace monarch {
 
-enum SeqKind { SEQ_GEMM, SEQ_REDUCE, SEQ_ZERO, SEQ_SWAP, SEQ_FIBER, SEQ_FIBER_WGRAD, SEQ_FIBER_SWAP };
+enum SeqKind {
+  SEQ_GEMM, SEQ_REDUCE, SEQ_ZERO, SEQ_SWAP, SEQ_FIBER, SEQ_FIBER_WGRAD, SEQ_FIBER_SWAP,
+  SEQ_FIBER_STRIDED
+};
 
 struct SeqStep {
   SeqKind kind = SEQ_GEMM;
@@ -30,6 +33,11 @@ struct SeqStep {
   int64_t f_N = 0, f_n = 0;
   // SEQ_FIBER_SWAP: SEQ_FIBER on rows of [t_A][t_M][f_n] arrays, each written
   // as [f_n][t_M][t_A] in the same place (t_out may equal t_in)
+  // SEQ_FIBER_STRIDED: round 0 with the change between the natural layout and
+  // L_0 (f_dir 0: natural -> L_0, the L_0 input copy to f_save; 1: L_0 ->
+  // natural)
+  void* f_save = nullptr;
+  int f_dir = 0;
   // SEQ_FIBER_WGRAD: f_part[c][f][p][t] = sum over chunk c (f_chunk rows) of
   // t_in[b, f*f_n + p] f_in2[b, f*f_n + t], for t_rows rows
   const void* f_in2 = nullptr;

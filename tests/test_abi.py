@@ -258,11 +258,11 @@ def test_hyper_sizes_and_plan():
     assert M.monarch_hyper_saved_elems((64,), 10) == 0
     assert M.monarch_hyper_describe(0, dims, 10, B.F32) == (
         ["hyper_transpose"] + ["hyper_round_fwd", "hyper_permute"] * 2 + ["hyper_round_fwd"])
-    # bf16: round 1's swap arrays ([32][24], 768 elements) are small enough
-    # for the fused round-and-swap kernel, round 0's (12288) are not
+    # bf16: round 0 reads x in its natural layout (joined with the transpose),
+    # round 1's swap arrays ([32][24], 768 elements) are small enough for the
+    # fused round-and-swap kernel, round 0's (12288) are not
     assert M.monarch_hyper_describe(0, dims, 10, B.BF16) == (
-        ["hyper_transpose", "hyper_round_fwd", "hyper_permute", "hyper_round_fwd_swap",
-         "hyper_round_fwd"])
+        ["hyper_transpose_round_fwd", "hyper_permute", "hyper_round_fwd_swap", "hyper_round_fwd"])
     assert M.monarch_hyper_describe(0, (64,), 10, B.BF16) == ["hyper_round_fwd"]
     names = M.monarch_hyper_describe(1, dims, 10, B.F32)
     assert names == (["hyper_round_bwd_weight", "hyper_round_bwd_data", "hyper_permute"] * 2
@@ -272,8 +272,8 @@ def test_hyper_sizes_and_plan():
     # products use per-fiber transposed weights
     names = M.monarch_hyper_describe(1, dims, 10, B.BF16)
     step = ["hyper_round_bwd_weight", "hyper_weight_transpose", "hyper_round_bwd_data"]
-    assert names == (step[:2] + ["hyper_round_bwd_data_swap"] + step + ["hyper_permute"] + step
-                     + ["hyper_transpose", "reduce_dw"])
+    assert names == (step[:2] + ["hyper_round_bwd_data_swap"] + step + ["hyper_permute"]
+                     + step[:2] + ["hyper_round_bwd_data_transpose", "reduce_dw"])
     assert M.monarch_hyper_describe(1, (64,), 10, B.BF16) == [
         "hyper_round_bwd_weight", "hyper_round_bwd_data", "reduce_dw"]
     assert len(M.monarch_hyper_describe(1, (2, 3, 4, 5), 10, B.BF16)) == 14

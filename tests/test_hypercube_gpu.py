@@ -70,6 +70,9 @@ def check(api, dims, batch, dtype, seed=8100):
     # ((4, 16, 8): forward round 1), an axis after the pair ((2, 24, 8, 2)),
     # the backward direction ((8, 32, 2)), batches not a multiple of 32
     ((4, 16, 8), 77, "bf16"), ((2, 24, 8, 2), 100, "bf16"), ((8, 32, 2), 45, "bf16"),
+    # bf16 round 0 joined with the transposes: a partial chunk of 40 fibers,
+    # 72 fibers (64 + 8), three axes
+    ((16, 40), 77, "bf16"), ((24, 72), 33, "bf16"), ((32, 8, 3), 100, "bf16"),
 ])
 def test_hyper_small(api, dims, batch, dtype):
     check(api, dims, batch, dtype)
