@@ -45,6 +45,13 @@ struct Cfg {
 
 __device__ __forceinline__ void pin(u32x4& v) { asm volatile("" : "+v"(v)); }
 __device__ __forceinline__ u32x4 ld16(const void* p) { return *static_cast<const u32x4*>(p); }
+// 16 bytes at 4-byte alignment (global loads of this width need only
+// dword alignment): fp32 operands whose blocks start off a 16-byte boundary
+typedef uint32_t u32x4u __attribute__((ext_vector_type(4), aligned(4)));
+__device__ __forceinline__ u32x4 ld16u(const void* p) {
+  const u32x4u v = *static_cast<const u32x4u*>(p);
+  return u32x4{v[0], v[1], v[2], v[3]};
+}
 
 // One operand tile (A: rows = M, B: rows = N) of ROWS x TK elements.
 //   mode 1 (K-major units): unit = VEC consecutive k of one row;
@@ -127,6 +134,9 @@ struct Tile {
           int64_t gk = k0 + k;
           gk = gk < ke ? gk : kb;
           reg[S][q] = ld16(row[q] + gk);
+        } else if (!C::kBf16 && sk == 1 && k0 + k + VEC <= ke) {
+          // fp32, K-contiguous, the whole piece in range
+          reg[S][q] = ld16u(row[q] + k0 + k);
         } else {
           T v[VEC];
 #pragma unroll
@@ -144,6 +154,9 @@ struct Tile {
           gk = gk < ke ? gk : ke - 1;
           if (vec()) {
             reg[S][4 * q + i] = ld16(row[q] + gk * sk);
+          } else if (!C::kBf16 && lo == 1 && nrow[q] == VEC) {
+            // fp32, row-contiguous, all VEC rows valid
+            reg[S][4 * q + i] = ld16u(row[q] + gk * sk);
           } else {
             T v[VEC];
 #pragma unroll
