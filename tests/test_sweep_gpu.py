@@ -2,8 +2,9 @@
 
 Covers the three paths with shapes the hand-picked cases do not: random
 block counts and block sizes, padded inputs and truncated outputs, bias,
-ReLU and ragged batches on the generic path; random batches on the fused
-32x32-block and square 128x128-block paths. The shapes come from a fixed
+ReLU and ragged batches on the generic path (small layers, and bf16 layers
+of 256-1536 features that take the large tiles); random batches on the
+fused 32x32-block and square 128x128-block paths. The shapes come from a fixed
 seed, so every run checks the same cases; the ids name them.
 """
 import math
@@ -67,11 +68,26 @@ def _square_cases():
     return cases
 
 
+def _large_cases():
+    # bf16 layers wide enough for the 256 x 256 and 256 x 192 tiles, with
+    # ragged rows, columns and K and batch-split weight gradients
+    rng = random.Random(20221205)
+    cases = []
+    for _ in range(12):
+        b1, b2 = rng.randint(1, 4), rng.randint(1, 4)
+        lcm = b1 * b2 // math.gcd(b1, b2)
+        mid = lcm * rng.randint(max(1, 256 // lcm), 1536 // lcm)
+        cases.append((rng.randint(256, 1536), rng.randint(256, 1536), mid, b1, b2,
+                      rng.randint(256, 1500), "bf16", rng.random() < 0.3, rng.random() < 0.3))
+    return cases
+
+
 GENERAL = _general_cases()
 SQUARE = _square_cases()
+LARGE = _large_cases()
 
 
-@pytest.mark.parametrize("case", GENERAL, ids=lambda c: "in%d-out%d-mid%d-b%dx%d-B%d-%s-bias%d-relu%d" % (
+@pytest.mark.parametrize("case", GENERAL + LARGE, ids=lambda c: "in%d-out%d-mid%d-b%dx%d-B%d-%s-bias%d-relu%d" % (
     c[0], c[1], c[2], c[3], c[4], c[5], c[6], c[7], c[8]))
 def test_sweep_general(api, case):
     inp, out, mid, b1, b2, batch, dtype, with_bias, relu = case
