@@ -187,9 +187,11 @@ def bench_project(args) -> int:
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / K
     ms = e0.elapsed_time(e1) / K
-    # fp32 work per slice: column sums, (iters + 1) products A v and iters products Aᵀ u,
-    # 2 flops per multiply-add
-    flops = b * b * 2.0 * q * q * (2 * args.iters + 2)
+    # work per slice (bf16 128 x 128 slices): B = AᵀA on MFMA (2 q³ flops), then
+    # on the vector ALU the column sums, one product B v per iteration and the
+    # final A v (2 flops per multiply-add)
+    flops = b * b * 2.0 * q * q * (args.iters + 2)
+    mfma_flops = b * b * 2.0 * q * q * q
     hbm = 2.0 * n * n + 2 * 2.0 * b * b * q
     tflops = flops / (ms * 1e-3) / 1e12
     cpu = None
@@ -223,7 +225,8 @@ def bench_project(args) -> int:
                    "input": "bf16"},
         "roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": 157.3,
                      "unit": "TFLOP/s", "frac": round(tflops / 157.3, 4), "traffic": None,
-                     "hbm_bytes": hbm, "hbm_frac": round(hbm / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
+                     "hbm_bytes": hbm, "hbm_frac": round(hbm / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                     "mfma_tflops": round(mfma_flops / (ms * 1e-3) / 1e12, 2)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)

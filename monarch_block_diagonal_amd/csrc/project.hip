@@ -18,6 +18,8 @@
 // after one iteration.
 #include <math.h>
 
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -200,7 +202,11 @@ __global__ __launch_bounds__(PT) void project_slices_kernel(const T* __restrict_
 //    so one barrier per iteration); every thread then holds its E entries of
 //    v, and |v|² is a shuffle sum over the 16 column strips of its wave.
 // Same start, iteration count, normalisation and sign rule as the general
-// kernel.
+// kernel. bf16 slices of 64 or 128 instead form B = AᵀA once with MFMAs
+// (the slice written transposed to LDS; exact products, fp32 sums) and take
+// each power step as one product with B: w = B v by row strips, v = B w by
+// column strips (B is symmetric), so an exchange round through LDS covers
+// two steps; the final A v reads the bf16 copy in LDS.
 template <typename T, int Qs>
 __global__ __launch_bounds__(PT) void project_square_kernel(const T* __restrict__ M,
                                                             T* __restrict__ W1,
@@ -289,15 +295,158 @@ __global__ __launch_bounds__(PT) void project_square_kernel(const T* __restrict_
       for (int j = 0; j < E; ++j) v[j] = (tc * E + j == 0) ? 1.f : 0.f;
     }
   }
-  for (int it = 0; it < iters; ++it) {
-    rowprod(v, u);                             // u = A v
-    colprod(u, v);                             // v = Aᵀ u
-    const float nrm = norm2(v);
-    const float inv = nrm > 0.f ? 1.f / sqrtf(nrm) : 0.f;
+  if constexpr (std::is_same<T, uint16_t>::value && Qs >= 64) {
+    // bf16: B = AᵀA once on MFMA (exact products, fp32 sums), then power
+    // steps v <- B v, two per exchange round. Wave w keeps rows
+    // [32w, 32w + 32) (Q = 128; [16w, 16w + 16) for 64) of B in the MFMA
+    // result layout: lane holds B[16mt + 4lh + e][16nt + l15]. v lives by
+    // columns (lane: v[16nt + l15]); w = B v by rows (lane: w[16mt + 4lh + e],
+    // a 16-lane row sum); v = B w (B symmetric) sums over the wave's rows
+    // with shuffles and over the waves through LDS.
+    constexpr int AP = Qs + 8;           // LDS pitch of Aᵀ (bf16)
+    constexpr int NT = Qs / 16, MTW = NT / 4;
+    __shared__ __attribute__((aligned(16))) uint16_t ast[Qs * AP];   // Aᵀ[col][row]
+    __shared__ float vs[Qs];
+    const int l15 = lane & 15, lh = lane >> 4;
+    // Aᵀ: column tc*E + j, rows tr*E .. tr*E + E - 1 (the bf16 values exactly)
 #pragma unroll
-    for (int j = 0; j < E; ++j) v[j] *= inv;
+    for (int j = 0; j < E; ++j) {
+      uint32_t pk[E / 2];
+#pragma unroll
+      for (int i = 0; i < E / 2; ++i)
+        pk[i] = (__float_as_uint(a[2 * i][j]) >> 16) | (__float_as_uint(a[2 * i + 1][j]) & 0xffff0000u);
+      uint16_t* dst = &ast[(tc * E + j) * AP + tr * E];
+      if constexpr (E == 8)
+        *reinterpret_cast<u32x4*>(dst) = u32x4{pk[0], pk[1], pk[2], pk[3]};
+      else
+        *reinterpret_cast<u32x2*>(dst) = u32x2{pk[0], pk[1]};
+    }
+    if (tr == 0) {
+#pragma unroll
+      for (int j = 0; j < E; ++j) vs[tc * E + j] = v[j];
+    }
+    __syncthreads();
+    f32x4 bacc[MTW][NT];
+#pragma unroll
+    for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) bacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < Qs / 32; ++ks) {
+      bf16x8 fa[MTW], fb[NT];
+#pragma unroll
+      for (int mt = 0; mt < MTW; ++mt)
+        fa[mt] = as_bf16x8(*reinterpret_cast<const u16x8*>(
+            &ast[(16 * (MTW * wv + mt) + l15) * AP + 32 * ks + 8 * lh]));
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt)
+        fb[nt] = as_bf16x8(*reinterpret_cast<const u16x8*>(&ast[(16 * nt + l15) * AP + 32 * ks + 8 * lh]));
+#pragma unroll
+      for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt)
+          bacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mt], fb[nt], bacc[mt][nt], 0, 0, 0);
+    }
+    float vc[NT], wr[MTW][4];
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) vc[nt] = vs[16 * nt + l15];
+    auto rowprod_b = [&]() {   // wr = B vc, rows of this wave
+#pragma unroll
+      for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          float acc = 0.f;
+#pragma unroll
+          for (int nt = 0; nt < NT; ++nt) acc += bacc[mt][nt][e] * vc[nt];
+          wr[mt][e] = row16_sum(acc);
+        }
+    };
+    auto colprod_b = [&]() {   // vc = B wr (B symmetric), then normalised
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        float acc = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+          for (int e = 0; e < 4; ++e) acc += bacc[mt][nt][e] * wr[mt][e];
+        acc += __shfl_xor(acc, 16);
+        acc += __shfl_xor(acc, 32);
+        vc[nt] = acc;
+      }
+      if (lane < 16) {
+#pragma unroll
+        for (int nt = 0; nt < NT; ++nt) part[buf][wv][16 * nt + l15] = vc[nt];
+      }
+      __syncthreads();
+      float p2 = 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const int c = 16 * nt + l15;
+        vc[nt] = part[buf][0][c] + part[buf][1][c] + part[buf][2][c] + part[buf][3][c];
+        p2 += vc[nt] * vc[nt];
+      }
+      buf ^= 1;
+      const float nrm = row16_sum(p2);
+      const float inv = nrm > 0.f ? 1.f / sqrtf(nrm) : 0.f;
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) vc[nt] *= inv;
+    };
+    int left = iters;
+    for (; left >= 2; left -= 2) {
+      rowprod_b();   // w = B v (not normalised: one step's growth)
+      colprod_b();   // v = B w, normalised
+    }
+    if (left == 1) {
+      // one step: v by rows from the lanes that hold it by columns
+#pragma unroll
+      for (int mt = 0; mt < MTW; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) wr[mt][e] = __shfl(vc[MTW * wv + mt], (lane & 48) | (4 * lh + e));
+      colprod_b();
+    }
+    __syncthreads();   // every lane has read vs
+    if (wv == 0 && lane < 16) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) vs[16 * nt + l15] = vc[nt];
+    }
+    __syncthreads();
+#pragma unroll
+    for (int j = 0; j < E; ++j) v[j] = vs[tc * E + j];
+    // u = A v from the bf16 copy (A's registers are free after the start):
+    // A[tr*E + i][tc*E + j] = Aᵀ[tc*E + j][tr*E + i]
+    float pu[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) pu[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      const uint16_t* col = &ast[(tc * E + j) * AP + tr * E];
+      uint32_t w32[E / 2];
+      if constexpr (E == 8) {
+        const u32x4 q = *reinterpret_cast<const u32x4*>(col);
+        w32[0] = q[0], w32[1] = q[1], w32[2] = q[2], w32[3] = q[3];
+      } else {
+        const u32x2 q = *reinterpret_cast<const u32x2*>(col);
+        w32[0] = q[0], w32[1] = q[1];
+      }
+#pragma unroll
+      for (int i = 0; i < E / 2; ++i) {
+        pu[2 * i] += __uint_as_float(w32[i] << 16) * v[j];
+        pu[2 * i + 1] += __uint_as_float(w32[i] & 0xffff0000u) * v[j];
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < E; ++i) u[i] = row16_sum(pu[i]);
+  } else {
+    for (int it = 0; it < iters; ++it) {
+      rowprod(v, u);                             // u = A v
+      colprod(u, v);                             // v = Aᵀ u
+      const float nrm = norm2(v);
+      const float inv = nrm > 0.f ? 1.f / sqrtf(nrm) : 0.f;
+#pragma unroll
+      for (int j = 0; j < E; ++j) v[j] *= inv;
+    }
+    rowprod(v, u);
   }
-  rowprod(v, u);
   // sigma = |u|: this wave's 4 row strips, then the 4 waves
   float p2 = 0.f;
 #pragma unroll
