@@ -252,10 +252,10 @@ int monarch_hyper_describe(int direction, int ndims, const int64_t* dims, int64_
  *   Y[b, r*qo + k] += sum_s A[r, k, s] X[b, r*qi + s]     (contiguous blocks)
  *   Y[b, p*nb + g] += sum_t B[g, p, t] X[b, t*nb + g]     (stride-nb features)
  * w_a = A and w_b = B are [nb, qo, qi]; x [batch, in], y [batch, out]. No
- * saved intermediate. The second term is computed first and the first is
- * added to its rounded value (two roundings of y in bf16). The caller's
- * workspace (monarch_dyad_fwd_workspace_bytes, 16-byte aligned, contents
- * unspecified on return) holds x in block-major order. Errors and
+ * saved intermediate. Each term is rounded to the I/O type and their sum is
+ * rounded again (three roundings of y in bf16). The caller's workspace
+ * (monarch_dyad_fwd_workspace_bytes, 16-byte aligned, contents unspecified
+ * on return) holds x and the second term in block-major order. Errors and
  * conventions as for monarch_bwd. */
 size_t monarch_dyad_fwd_workspace_bytes(int64_t in_features, int64_t out_features,
                                         int64_t nblocks, int64_t batch, int dtype);

@@ -14,8 +14,10 @@ struct DyadProblem {
   int64_t esize = 4;
   int64_t splits = 1, chunk = 0;   // batch split of both weight gradients
   // backward workspace: partial sums of dA and dB, block-major X and dY;
-  // forward workspace: block-major X (ws_fwd bytes)
+  // forward workspace: block-major X and term B's block-major rows (ws_fwd
+  // bytes)
   size_t ws_pa = 0, ws_pb = 0, ws_xp = 0, ws_dyp = 0, ws_total = 0, ws_fwd = 0;
+  size_t ws_fwd_yp = 0;   // forward: term B's block-major rows after Xp
 };
 
 struct DyadBuffers {

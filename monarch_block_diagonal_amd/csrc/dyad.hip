@@ -7,10 +7,13 @@
 // Term B's operands are strided by nb. An axis swap (generic.hip) first
 // gathers X into block-major order, Xp[b, g*qi + t] = X[b, t*nb + g] (and the
 // backward also dY, dYp[b, g*qo + p] = dY[b, p*nb + g]), so that every GEMM
-// reads 16-byte pieces; term B's results are stored at their stride-nb
-// positions by the GEMM epilogue. The forward runs term B into Y and adds
-// term A to it; the backward takes both weight gradients as batch-split sums
-// (reduced in a fixed order), writes term B's dX and adds term A's.
+// reads 16-byte pieces. Term B's results are written block-major too (the
+// stride-nb positions would take element-by-element stores) and added into
+// the output by an accumulating axis swap. The forward runs term B into its
+// block-major rows, term A into Y, and adds term B; the backward takes both
+// weight gradients as batch-split sums (reduced in a fixed order), term B's
+// data product into block-major rows (in Xp's place), term A's into dX, and
+// adds term B's.
 #include "dyad.h"
 #include "monarch.h"
 
@@ -50,10 +53,12 @@ void term_a_fwd(GemmArgs& a, const DyadProblem& dp, const void* x, const void* w
   a.C = y, a.c_sb = dp.qo, a.c_si = dp.out, a.c_sj = 1;
   a.M = dp.batch, a.N = dp.qo, a.K = dp.qi, a.nblk = dp.nb;
 }
-void term_b_fwd(GemmArgs& a, const DyadProblem& dp, const void* xp, const void* wb, void* y) {
+// term B into block-major rows, yp[b, g*qo + p] (added into Y by an axis
+// swap: its stride-nb positions would be written element by element)
+void term_b_fwd(GemmArgs& a, const DyadProblem& dp, const void* xp, const void* wb, void* yp) {
   a.A = xp, a.a_sb = dp.qi, a.a_si = dp.in, a.a_sk = 1;
   a.B = wb, a.b_sb = dp.qo * dp.qi, a.b_sk = 1, a.b_sj = dp.qi;
-  a.C = y, a.c_sb = 1, a.c_si = dp.out, a.c_sj = dp.nb;
+  a.C = yp, a.c_sb = dp.qo, a.c_si = dp.out, a.c_sj = 1;
   a.M = dp.batch, a.N = dp.qo, a.K = dp.qi, a.nblk = dp.nb;
 }
 // [rows][a][c] -> [rows][c][a], one row of `cols` = a*c elements per batch row
@@ -84,7 +89,8 @@ int make_dyad(int64_t in, int64_t out, int64_t nb, int64_t batch, int dtype, Dya
     p.ws_xp = align256(p.ws_pb + part);
     p.ws_dyp = align256(p.ws_xp + static_cast<size_t>(batch) * in * p.esize);
     p.ws_total = align256(p.ws_dyp + static_cast<size_t>(batch) * out * p.esize);
-    p.ws_fwd = align256(static_cast<size_t>(batch) * in * p.esize);
+    p.ws_fwd_yp = align256(static_cast<size_t>(batch) * in * p.esize);
+    p.ws_fwd = align256(p.ws_fwd_yp + static_cast<size_t>(batch) * out * p.esize);
   }
   *dp = p;
   return MONARCH_OK;
@@ -92,16 +98,19 @@ int make_dyad(int64_t in, int64_t out, int64_t nb, int64_t batch, int dtype, Dya
 
 int dyad_plan_fwd(const DyadProblem& dp, const DyadBuffers& b, SeqStep* steps) {
   if (dp.batch == 0) return 0;
-  void* xp = b.ws;   // the forward's workspace: Xp
+  void* xp = b.ws;   // the forward's workspace: Xp, then term B's block-major rows
+  void* yp = static_cast<char*>(b.ws) + dp.ws_fwd_yp;
   gather(steps[0], "dyad_gather_x", b.x, xp, dp.batch, dp.qi, dp.nb);
   steps[1].kind = SEQ_GEMM;
   steps[1].name = "dyad_term_b_fwd";
-  term_b_fwd(steps[1].g, dp, xp, b.wb, b.y);
+  term_b_fwd(steps[1].g, dp, xp, b.wb, yp);
   steps[2].kind = SEQ_GEMM;
   steps[2].name = "dyad_term_a_fwd";
   term_a_fwd(steps[2].g, dp, b.x, b.wa, b.y);
-  steps[2].g.accum = 1;
-  return 3;
+  // Y[b, p*nb + g] += yp[b, g*qo + p]
+  gather(steps[3], "dyad_add_term_b", yp, b.y, dp.batch, dp.nb, dp.qo);
+  steps[3].t_accum = 1;
+  return 4;
 }
 
 int dyad_plan_bwd(const DyadProblem& dp, const DyadBuffers& b, SeqStep* steps) {
@@ -141,27 +150,32 @@ int dyad_plan_bwd(const DyadProblem& dp, const DyadBuffers& b, SeqStep* steps) {
     a.partial = pb, a.splits = dp.splits, a.k_chunk = dp.chunk;
     a.M = dp.qo, a.N = dp.qi, a.K = dp.batch, a.nblk = dp.nb;
   }
+  // term B's data product goes to block-major rows in Xp's place (both
+  // weight products, which read Xp, come first)
+  void* dxp = xp;
   {
-    // dX[b, t*nb + g] = sum_p dYp[b, g*qo + p] B[g,p,t]
+    // dXp[b, g*qi + t] = sum_p dYp[b, g*qo + p] B[g,p,t]
     SeqStep& st = steps[n++];
     st.name = "dyad_term_b_bwd_data";
     GemmArgs& a = st.g;
     a.A = dyp, a.a_sb = dp.qo, a.a_si = dp.out, a.a_sk = 1;
     a.B = b.wb, a.b_sb = dp.qo * dp.qi, a.b_sk = dp.qi, a.b_sj = 1;
-    a.C = b.dx, a.c_sb = 1, a.c_si = dp.in, a.c_sj = dp.nb;
+    a.C = dxp, a.c_sb = dp.qi, a.c_si = dp.in, a.c_sj = 1;
     a.M = dp.batch, a.N = dp.qi, a.K = dp.qo, a.nblk = dp.nb;
   }
   {
-    // dX[b, r*qi + s] += sum_k dY[b, r*qo + k] A[r,k,s]
+    // dX[b, r*qi + s] = sum_k dY[b, r*qo + k] A[r,k,s]
     SeqStep& st = steps[n++];
     st.name = "dyad_term_a_bwd_data";
     GemmArgs& a = st.g;
     a.A = b.dy, a.a_sb = dp.qo, a.a_si = dp.out, a.a_sk = 1;
     a.B = b.wa, a.b_sb = dp.qo * dp.qi, a.b_sk = dp.qi, a.b_sj = 1;
     a.C = b.dx, a.c_sb = dp.qi, a.c_si = dp.in, a.c_sj = 1;
-    a.accum = 1;
     a.M = dp.batch, a.N = dp.qi, a.K = dp.qo, a.nblk = dp.nb;
   }
+  // dX[b, t*nb + g] += dXp[b, g*qi + t]
+  gather(steps[n], "dyad_add_term_b", dxp, b.dx, dp.batch, dp.nb, dp.qi);
+  steps[n++].t_accum = 1;
   {
     SeqStep& st = steps[n++];
     st.kind = SEQ_REDUCE;

@@ -92,12 +92,30 @@ constexpr int swap_lds_elems(int n) {
   return n + (n / (64 * (4 / static_cast<int>(sizeof(T)))) + 1) * (4 / static_cast<int>(sizeof(T)));
 }
 
+// out + v (accumulating swaps), in fp32, rounded once to the I/O type
+__device__ __forceinline__ float add_io(float v, float o) { return v + o; }
+__device__ __forceinline__ uint16_t add_io(uint16_t v, uint16_t o) {
+  return f32_to_bf16(bf16_to_f32(v) + bf16_to_f32(o));
+}
+template <typename T>
+__device__ __forceinline__ u32x4 add_piece(u32x4 v, u32x4 o) {
+  T a[16 / sizeof(T)], b[16 / sizeof(T)];
+  __builtin_memcpy(a, &v, 16);
+  __builtin_memcpy(b, &o, 16);
+#pragma unroll
+  for (int e = 0; e < static_cast<int>(16 / sizeof(T)); ++e) a[e] = add_io(a[e], b[e]);
+  u32x4 r;
+  __builtin_memcpy(&r, a, 16);
+  return r;
+}
+
 // A workgroup takes `per` consecutive arrays (the last one may take fewer),
-// so that small arrays still give each workgroup a few KB to move.
+// so that small arrays still give each workgroup a few KB to move. With
+// `accum` the swapped values are added to what `out` holds.
 template <typename T>
 __global__ __launch_bounds__(256) void swap_lds_kernel(const T* __restrict__ in,
                                                       T* __restrict__ out, int A, int M, int C,
-                                                      int vec, int64_t rows, int per) {
+                                                      int vec, int64_t rows, int per, int accum) {
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   T* s = reinterpret_cast<T*>(smem);
   constexpr int V = 16 / sizeof(T);
@@ -132,13 +150,15 @@ __global__ __launch_bounds__(256) void swap_lds_kernel(const T* __restrict__ in,
       for (int e = 0; e < V; ++e) v[e] = s[swap_pos<T>(k * na + ((a0 + e) * M + m) * C + c)];
       u32x4 r;
       __builtin_memcpy(&r, v, sizeof(r));
+      if (accum) r = add_piece<T>(r, reinterpret_cast<const u32x4*>(dst)[q]);
       reinterpret_cast<u32x4*>(dst)[q] = r;
     }
   } else {
     for (int oo = tid; oo < n; oo += 256) {
       const int k = oo / na, o = oo - k * na;
       const int a = o % A, cm = o / A, m = cm % M, c = cm / M;
-      dst[oo] = s[swap_pos<T>(k * na + (a * M + m) * C + c)];
+      const T v = s[swap_pos<T>(k * na + (a * M + m) * C + c)];
+      dst[oo] = accum ? add_io(v, dst[oo]) : v;
     }
   }
 }
@@ -149,7 +169,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void swap_tiled_kernel(const T* __restrict__ in,
                                                         T* __restrict__ out, int64_t A, int64_t M,
                                                         int64_t C, int64_t tiles_a,
-                                                        int64_t tiles_c) {
+                                                        int64_t tiles_c, int accum) {
   __shared__ T t[32][33];
   int64_t bid = blockIdx.x;
   const int64_t tc = bid % tiles_c;
@@ -167,7 +187,7 @@ __global__ __launch_bounds__(256) void swap_tiled_kernel(const T* __restrict__ i
   __syncthreads();
   for (int i = ty; i < 32; i += 8) {
     const int64_t c = tc * 32 + i, a = ta * 32 + tx;
-    if (c < C && a < A) dst[c * M * A + a] = t[tx][i];
+    if (c < C && a < A) dst[c * M * A + a] = accum ? add_io(t[tx][i], dst[c * M * A + a]) : t[tx][i];
   }
 }
 
@@ -190,7 +210,8 @@ hipError_t launch_zero(void* p, size_t bytes, hipStream_t s) {
 }
 
 hipError_t launch_swap(const void* in, void* out, int64_t rows, int64_t A, int64_t M, int64_t C,
-                       bool bf16, hipStream_t s) {
+                       bool bf16, hipStream_t s, bool accum) {
+  const int acc = accum ? 1 : 0;
   if (rows <= 0 || A <= 0 || M <= 0 || C <= 0) return hipSuccess;
   const int64_t esz = bf16 ? 2 : 4, V = 16 / esz, n = A * M * C;
   constexpr int64_t kLds = 49 * 1024;
@@ -211,12 +232,12 @@ hipError_t launch_swap(const void* in, void* out, int64_t rows, int64_t A, int64
       hipLaunchKernelGGL(swap_lds_kernel<uint16_t>, g, dim3(256), lds, s,
                          static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out),
                          static_cast<int>(A), static_cast<int>(M), static_cast<int>(C), vec, rows,
-                         static_cast<int>(per));
+                         static_cast<int>(per), acc);
     else
       hipLaunchKernelGGL(swap_lds_kernel<float>, g, dim3(256), lds, s,
                          static_cast<const float*>(in), static_cast<float*>(out),
                          static_cast<int>(A), static_cast<int>(M), static_cast<int>(C), vec, rows,
-                         static_cast<int>(per));
+                         static_cast<int>(per), acc);
     return hipGetLastError();
   }
   const int64_t ta = (A + 31) / 32, tc = (C + 31) / 32;
@@ -225,11 +246,11 @@ hipError_t launch_swap(const void* in, void* out, int64_t rows, int64_t A, int64
   if (bf16)
     hipLaunchKernelGGL(swap_tiled_kernel<uint16_t>, dim3(static_cast<unsigned>(grid)), dim3(256),
                        0, s, static_cast<const uint16_t*>(in), static_cast<uint16_t*>(out), A, M,
-                       C, ta, tc);
+                       C, ta, tc, acc);
   else
     hipLaunchKernelGGL(swap_tiled_kernel<float>, dim3(static_cast<unsigned>(grid)), dim3(256), 0,
                        s, static_cast<const float*>(in), static_cast<float*>(out), A, M, C, ta,
-                       tc);
+                       tc, acc);
   return hipGetLastError();
 }
 

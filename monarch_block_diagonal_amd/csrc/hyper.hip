@@ -328,7 +328,8 @@ hipError_t seq_launch(const SeqStep& st, bool bf16, hipStream_t s) {
     case SEQ_REDUCE: return launch_reduce_partials(st.r[0], st.r[1], st.r[2], bf16, s);
     case SEQ_ZERO: return launch_zero(st.zero_ptr, st.zero_bytes, s);
     case SEQ_SWAP:
-      return launch_swap(st.t_in, st.t_out, st.t_rows, st.t_A, st.t_M, st.t_C, bf16, s);
+      return launch_swap(st.t_in, st.t_out, st.t_rows, st.t_A, st.t_M, st.t_C, bf16, s,
+                         st.t_accum != 0);
     case SEQ_FIBER:
       return launch_fiber(st.t_in, st.f_w, st.t_out, st.t_rows, st.f_N, st.f_n, bf16, s);
     case SEQ_FIBER_SWAP:

@@ -96,9 +96,10 @@ hipError_t launch_fiber_wgrad(const void* g, const void* in, float* partial, int
                               int64_t N, int64_t n, int64_t chunk, bool bf16, hipStream_t s);
 
 // Axis swap of `rows` row-major A x M x C arrays: out[b][c][m][a] =
-// in[b][a][m][c] (M = 1: a per-row transpose; lattice layout changes).
+// in[b][a][m][c] (M = 1: a per-row transpose; lattice layout changes); with
+// accum, out[b][c][m][a] += in[b][a][m][c] (fp32 sum, one rounding).
 hipError_t launch_swap(const void* in, void* out, int64_t rows, int64_t A, int64_t M, int64_t C,
-                       bool bf16, hipStream_t s);
+                       bool bf16, hipStream_t s, bool accum = false);
 
 // Bias gradient partial sums: partial[c][p*b2 + g] = sum over rows
 // [c*chunk, (c+1)*chunk) of dV[b, g*q2o + p], for p*b2 + g < out (fp32,

@@ -27,6 +27,7 @@ struct SeqStep {
   const void* t_in = nullptr;
   void* t_out = nullptr;
   int64_t t_rows = 0, t_A = 0, t_M = 1, t_C = 0;
+  int t_accum = 0;   // SEQ_SWAP: add into t_out
   // SEQ_FIBER: t_out[b, f*f_n + p] = sum_t f_w[f][p][t] t_in[b, f*f_n + t]
   // for t_rows rows of f_N elements
   const void* f_w = nullptr;

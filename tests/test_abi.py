@@ -310,11 +310,14 @@ def test_hyper_pointer_checks():
 # DYAD-style layer
 
 def test_dyad_plan_and_checks():
+    # term B goes through block-major rows, added in by an accumulating swap
     assert M.monarch_dyad_describe(0, 64, 32, 4, 10, B.BF16) == [
-        "dyad_gather_x", "dyad_term_b_fwd", "dyad_term_a_fwd"]
+        "dyad_gather_x", "dyad_term_b_fwd", "dyad_term_a_fwd", "dyad_add_term_b"]
     assert M.monarch_dyad_describe(1, 64, 32, 4, 10, B.BF16) == [
         "dyad_gather_x", "dyad_gather_dy", "dyad_term_a_bwd_weight", "dyad_term_b_bwd_weight",
-        "dyad_term_b_bwd_data", "dyad_term_a_bwd_data", "reduce_dw"]
+        "dyad_term_b_bwd_data", "dyad_term_a_bwd_data", "dyad_add_term_b", "reduce_dw"]
+    # the forward workspace holds block-major x and term B's rows
+    assert M.monarch_dyad_fwd_workspace_bytes(64, 32, 4, 1000, B.F32) >= 1000 * (64 + 32) * 4
     assert M.monarch_dyad_describe(1, 64, 32, 4, 0, B.BF16) == ["zero_dw", "zero_dw"]
     assert M.monarch_dyad_bwd_workspace_bytes(64, 32, 4, 1000, B.F32) > 0
     assert M.monarch_dyad_bwd_workspace_bytes(63, 32, 4, 1000, B.F32) == 0
