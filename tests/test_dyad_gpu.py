@@ -38,6 +38,11 @@ def host(t):
     (768, 3072, 4, 512, "bf16"), (1000, 500, 10, 257, "f32"),
     # rows longer than one workgroup's LDS: the gathers take the tiled swap
     (32768, 256, 16, 6, "bf16"), (16000, 160, 16, 5, "f32"),
+    # bf16 with 256 x 256 blocks: the block-diagonal kernel that keeps a
+    # weight block in registers (one row, ragged tiles, several row ranges
+    # per block, a short last range)
+    (512, 512, 2, 1, "bf16"), (1024, 1024, 4, 100, "bf16"),
+    (4096, 4096, 16, 1000, "bf16"), (2048, 2048, 8, 4133, "bf16"),
 ])
 def test_dyad(api, inp, out, nb, batch, dtype):
     print(f"[dyad] in={inp} out={out} nb={nb} batch={batch} {dtype}", flush=True)

@@ -156,11 +156,12 @@ def test_graph_hypercube(lib):
     replay_equals_eager(step, [y, saved, dx] + dws, "hypercube 16x24x32")
 
 
-def test_graph_dyad(lib):
-    """bf16 DYAD layer, 512 features in 8 blocks: gathers, both terms and the
+@pytest.mark.parametrize("n,nb", [(512, 8), (1024, 4)])
+def test_graph_dyad(lib, n, nb):
+    """bf16 DYAD layer (blocks of 64, then of 256): gathers, both terms and the
     weight-gradient reduction."""
     M = lib
-    n, nb, B = 512, 8, 77
+    B = 77
     q = n // nb
     gen = torch.Generator(device="cuda:0")
     gen.manual_seed(78)
@@ -179,4 +180,4 @@ def test_graph_dyad(lib):
         M.monarch_dyad_fwd(x, wa, wb, y, ws, need_f, n, n, nb, B, M.BF16)
         M.monarch_dyad_bwd(dy, x, wa, wb, dx, dwa, dwb, ws, need, n, n, nb, B, M.BF16)
 
-    replay_equals_eager(step, [y, dx, dwa, dwb], "dyad 512/8")
+    replay_equals_eager(step, [y, dx, dwa, dwb], f"dyad {n}/{nb}")
