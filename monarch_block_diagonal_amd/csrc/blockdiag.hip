@@ -111,7 +111,7 @@ void bd256_kernel(const uint16_t* __restrict__ A, int64_t a_sb, int64_t a_si,
     for (int i = 0; i < 2; ++i) {
       int64_t row = r0 + t * BT + prow + 16 * i;
       row = row < r1 ? row : r1 - 1;
-      pre[i] = *reinterpret_cast<const u32x4*>(Ab + row * a_si);
+      pre[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Ab + row * a_si));
     }
   };
   auto lstore = [&](uint16_t* x) {
@@ -162,8 +162,8 @@ void bd256_kernel(const uint16_t* __restrict__ A, int64_t a_sb, int64_t a_si,
     for (int i = 0; i < 2; ++i) {
       const int64_t row = r0 + t * BT + prow + 16 * i;
       if (row < r1)
-        *reinterpret_cast<u32x4*>(Cb + row * c_si) =
-            *reinterpret_cast<const u32x4*>(&y[(prow + 16 * i) * BP + pcol]);
+        __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(&y[(prow + 16 * i) * BP + pcol]),
+                                    reinterpret_cast<u32x4*>(Cb + row * c_si));
     }
   }
 }
