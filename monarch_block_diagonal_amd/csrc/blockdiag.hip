@@ -1,13 +1,14 @@
-// Block-diagonal products with 256 x 256 weight blocks in bf16 (the two
-// terms of the DYAD page's layer, section 3: each term multiplies nb
-// independent 256-feature segments of a row by one dense block):
+// Block-diagonal products with 256 x 256 weight blocks in bf16: the two
+// block-sparse terms of the DYAD-style layer (DYAD page, abstract) once
+// term B's operands are in block-major order, each multiplying nb
+// independent 256-feature segments of a row by one dense block:
 //   C[b, blk*cs + j] = sum_k A[b, blk*as + k] W_blk(k, j),   j, k < 256,
 // with W_blk(k, j) = W[blk][j][k] (the forward: rows of the stored block are
 // output features) or W[blk][k][j] (the data gradient: its transpose).
 //
-// At K = N = 256 a product moves 1 KB per row for 256 Ki multiply-adds:
-// 256 flop per byte at the I/O width, under the bf16 MFMA ridge of about
-// 300, so it is bound by HBM. The generic tiled GEMM covers it with 256 x 256
+// At K = N = 256 a product moves 1 KB per row (512 bytes in, 512 out) for
+// 64 Ki multiply-adds: 128 flop per byte, under the bf16 MFMA ridge of about
+// 310 (2.5 PFLOP/s over 8 TB/s), so it is bound by HBM. The generic tiled GEMM covers it with 256 x 256
 // tiles whose eight waves fill a CU's registers: a workgroup then loads,
 // multiplies and stores in turn (4 K steps) with nothing to overlap.
 // Here a workgroup owns one block and a row range:
@@ -17,7 +18,9 @@
 //    ahead), results are staged in LDS and leave as whole 512-byte row
 //    segments, one barrier per tile;
 //  * 66 KB of LDS and at most 128 VGPRs per lane, so two workgroups share a
-//    CU and one's loads overlap the other's stores.
+//    CU and one's loads overlap the other's stores;
+//  * activations and results stream with non-temporal loads and stores
+//    (each is touched once per launch, far beyond the L2).
 // MFMA v_mfma_f32_16x16x32_bf16 computes Cᵀ[j x b] = Wᵀ-slice[j x k] · Aᵀ[k x b]
 // with fp32 accumulation; each result is rounded once to bf16.
 #include <stdint.h>
