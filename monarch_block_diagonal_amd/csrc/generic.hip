@@ -127,14 +127,25 @@ __global__ __launch_bounds__(256) void swap_lds_kernel(const T* __restrict__ in,
   const T* src = in + base;
   T* dst = out + base;
   const int tid = threadIdx.x;
+  // vector pieces go U at a time per thread, every load issued before the
+  // first wait
+  constexpr int U = 4;
+  const int nq = n / V;
   if (vec) {
     // a piece never straddles a pad (64*EPW is a multiple of V); its words
     // are stored one by one (the padded position is only word-aligned)
-    for (int q = tid; q < n / V; q += 256) {
-      const u32x4 v = reinterpret_cast<const u32x4*>(src)[q];
-      uint32_t* w = reinterpret_cast<uint32_t*>(s + swap_pos<T>(q * V));
+    for (int q0 = tid; q0 < nq; q0 += 256 * U) {
+      u32x4 v[U];
 #pragma unroll
-      for (int e = 0; e < 4; ++e) w[e] = v[e];
+      for (int j = 0; j < U; ++j)
+        if (q0 + 256 * j < nq) v[j] = reinterpret_cast<const u32x4*>(src)[q0 + 256 * j];
+#pragma unroll
+      for (int j = 0; j < U; ++j)
+        if (q0 + 256 * j < nq) {
+          uint32_t* w = reinterpret_cast<uint32_t*>(s + swap_pos<T>((q0 + 256 * j) * V));
+#pragma unroll
+          for (int e = 0; e < 4; ++e) w[e] = v[j][e];
+        }
     }
   } else {
     for (int i = tid; i < n; i += 256) s[swap_pos<T>(i)] = src[i];
@@ -142,16 +153,27 @@ __global__ __launch_bounds__(256) void swap_lds_kernel(const T* __restrict__ in,
   __syncthreads();
   if (vec) {
     // output piece o = V consecutive a of one (c, m) of array k
-    for (int q = tid; q < n / V; q += 256) {
-      const int k = (q * V) / na, o = q * V - k * na;
-      const int a0 = o % A, cm = o / A, m = cm % M, c = cm / M;
-      T v[V];
+    for (int q0 = tid; q0 < nq; q0 += 256 * U) {
+      u32x4 old[U];
 #pragma unroll
-      for (int e = 0; e < V; ++e) v[e] = s[swap_pos<T>(k * na + ((a0 + e) * M + m) * C + c)];
-      u32x4 r;
-      __builtin_memcpy(&r, v, sizeof(r));
-      if (accum) r = add_piece<T>(r, reinterpret_cast<const u32x4*>(dst)[q]);
-      reinterpret_cast<u32x4*>(dst)[q] = r;
+      for (int j = 0; j < U; ++j) {
+        old[j] = u32x4{0u, 0u, 0u, 0u};
+        if (accum && q0 + 256 * j < nq) old[j] = reinterpret_cast<const u32x4*>(dst)[q0 + 256 * j];
+      }
+#pragma unroll
+      for (int j = 0; j < U; ++j) {
+        const int q = q0 + 256 * j;
+        if (q >= nq) continue;
+        const int k = (q * V) / na, o = q * V - k * na;
+        const int a0 = o % A, cm = o / A, m = cm % M, c = cm / M;
+        T v[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) v[e] = s[swap_pos<T>(k * na + ((a0 + e) * M + m) * C + c)];
+        u32x4 r;
+        __builtin_memcpy(&r, v, sizeof(r));
+        if (accum) r = add_piece<T>(r, old[j]);
+        reinterpret_cast<u32x4*>(dst)[q] = r;
+      }
     }
   } else {
     for (int oo = tid; oo < n; oo += 256) {
