@@ -24,13 +24,33 @@ def dtype_code(t: torch.Tensor) -> int:
     raise TypeError(f"unsupported dtype {t.dtype}; use float32 or bfloat16")
 
 
+def _expect(t, shape, name: str):
+    """Raise ValueError unless tensor t (if given) has exactly this shape; the
+    kernels derive every extent from the sizes passed to the library, so a
+    tensor of another shape would be read or written out of its bounds."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(int(v) for v in shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+
+
+def _cdiv(a: int, b: int) -> int:
+    return -(-a // b)
+
+
 def problem_of(x: torch.Tensor, w1: torch.Tensor, w2: torch.Tensor):
-    """(in_features, out_features, nblocks1, nblocks2, batch) from tensor shapes."""
+    """(in_features, out_features, nblocks1, nblocks2, batch) from tensor shapes,
+    after checking w1 == [b1, out/b1, in/b1] and w2 == [b2, out/b2, out/b2]
+    (mid = out)."""
     if x.dim() != 2 or w1.dim() != 3 or w2.dim() != 3:
         raise ValueError("x must be [batch, in], w1 [b1, q1o, q1i], w2 [b2, q2o, q2i]")
-    nb1, q1o, q1i = w1.shape
-    nb2, q2o, q2i = w2.shape
-    return x.shape[1], nb2 * q2o, nb1, nb2, x.shape[0]
+    nb1, nb2 = int(w1.shape[0]), int(w2.shape[0])
+    fi, fo, b = int(x.shape[1]), nb2 * int(w2.shape[1]), int(x.shape[0])
+    if nb1 <= 0 or nb2 <= 0 or fi % nb1 or fo % nb1:
+        raise ValueError(f"in={fi} and out={fo} must be divisible by nblocks1={nb1}")
+    _expect(w1, (nb1, fo // nb1, fi // nb1), "w1")
+    _expect(w2, (nb2, fo // nb2, fo // nb2), "w2")
+    return fi, fo, nb1, nb2, b
 
 
 def _check(*ts):
@@ -47,8 +67,8 @@ def _check(*ts):
 
 
 def monarch_forward(x, w1, w2, act: int = B.ACT_NONE, stream=None):
-    _check(x, w1, w2)
     fi, fo, nb1, nb2, b = problem_of(x, w1, w2)
+    _check(x, w1, w2)
     y = torch.empty((b, fo), dtype=x.dtype, device=x.device)
     z = torch.empty((b, fo), dtype=x.dtype, device=x.device)
     B.monarch_fwd(x, w1, w2, y, z, fi, fo, nb1, nb2, b, dtype_code(x), act, stream)
@@ -57,8 +77,12 @@ def monarch_forward(x, w1, w2, act: int = B.ACT_NONE, stream=None):
 
 def monarch_backward(dy, x, w1, w2, z, y=None, act: int = B.ACT_NONE, stream=None,
                      workspace: torch.Tensor | None = None):
-    _check(dy, x, w1, w2, z, y)
     fi, fo, nb1, nb2, b = problem_of(x, w1, w2)
+    for t, name in ((dy, "dy"), (z, "z"), (y, "y")):
+        _expect(t, (b, fo), name)
+    if act == B.ACT_RELU and y is None:
+        raise ValueError("the ReLU backward needs the forward output y")
+    _check(dy, x, w1, w2, z, y)
     code = dtype_code(x)
     dx = torch.empty_like(x)
     dw1 = torch.empty_like(w1)
@@ -104,23 +128,30 @@ class MonarchLinearFunction(torch.autograd.Function):
         return dx, dw1, dw2, None
 
 
-def ex_problem(x, w1, w2, out_features: int):
-    """(in, out, mid, nb1, nb2, batch) of the general layer from tensor shapes."""
+def ex_problem(x, w1, w2, out_features: int, bias=None):
+    """(in, out, mid, nb1, nb2, batch) of the general layer from tensor shapes,
+    after checking w1 == [b1, mid/b1, ceil(in/b1)], w2 == [b2, ceil(out/b2),
+    mid/b2] and bias == [out]."""
     if x.dim() != 2 or w1.dim() != 3 or w2.dim() != 3:
         raise ValueError("x must be [batch, in], w1 [b1, q1o, q1i], w2 [b2, q2o, q2i]")
-    nb1, q1o, q1i = w1.shape
-    nb2, q2o, q2i = w2.shape
+    nb1, q1o = int(w1.shape[0]), int(w1.shape[1])
+    nb2 = int(w2.shape[0])
     mid = nb1 * q1o
-    if nb2 * q2i != mid:
-        raise ValueError("w1 and w2 disagree on the intermediate width")
-    return x.shape[1], out_features, mid, nb1, nb2, x.shape[0]
+    fi, fo, b = int(x.shape[1]), int(out_features), int(x.shape[0])
+    if nb1 <= 0 or nb2 <= 0 or fi <= 0 or fo <= 0 or mid % nb2:
+        raise ValueError(f"mid={mid} must be divisible by nblocks2={nb2}; sizes must be positive")
+    _expect(w1, (nb1, q1o, _cdiv(fi, nb1)), "w1")
+    _expect(w2, (nb2, _cdiv(fo, nb2), mid // nb2), "w2")
+    if bias is not None and (bias.dim() != 1 or bias.numel() != fo):
+        raise ValueError(f"bias has shape {tuple(bias.shape)}, expected ({fo},)")
+    return fi, fo, mid, nb1, nb2, b
 
 
 def monarch_forward_ex(x, w1, w2, out_features: int, bias=None, act: int = B.ACT_NONE,
                        stream=None):
     """y = act(pad(x) · Mᵀ truncated to out_features + bias); returns (y, z)."""
+    fi, fo, mid, nb1, nb2, b = ex_problem(x, w1, w2, out_features, bias)
     _check(x, w1, w2, bias)
-    fi, fo, mid, nb1, nb2, b = ex_problem(x, w1, w2, out_features)
     y = torch.empty((b, fo), dtype=x.dtype, device=x.device)
     z = torch.empty((b, mid), dtype=x.dtype, device=x.device)
     B.monarch_fwd_ex(x, w1, w2, bias, y, z, fi, fo, mid, nb1, nb2, b, dtype_code(x), act, stream)
@@ -130,8 +161,15 @@ def monarch_forward_ex(x, w1, w2, out_features: int, bias=None, act: int = B.ACT
 def monarch_backward_ex(dy, x, w1, w2, z, y=None, with_bias: bool = False,
                         act: int = B.ACT_NONE, stream=None):
     """(dx, dw1, dw2, dbias or None) of the general layer."""
-    _check(dy, x, w1, w2, z, y)
+    if dy.dim() != 2:
+        raise ValueError("dy must be [batch, out]")
     fi, fo, mid, nb1, nb2, b = ex_problem(x, w1, w2, dy.shape[1])
+    _expect(dy, (b, fo), "dy")
+    _expect(y, (b, fo), "y")
+    _expect(z, (b, mid), "z")
+    if act == B.ACT_RELU and y is None:
+        raise ValueError("the ReLU backward needs the forward output y")
+    _check(dy, x, w1, w2, z, y)
     code = dtype_code(x)
     dx = torch.empty_like(x)
     dw1 = torch.empty_like(w1)
@@ -206,11 +244,25 @@ class MonarchLinear(torch.nn.Module):
         return y.reshape(*shape[:-1], self.out_features)
 
 
+def _hyper_shapes(x, ws, dims):
+    """Check x == [batch, N] and ws[j] == [N/n_j, n_j, n_j] (N = prod dims)."""
+    dims = [int(d) for d in dims]
+    if x.dim() != 2 or len(ws) != len(dims) or not dims or min(dims) <= 0:
+        raise ValueError("x must be [batch, N] with one weight tensor per lattice axis")
+    n = 1
+    for d in dims:
+        n *= d
+    _expect(x, (x.shape[0], n), "x")
+    for j, (w, d) in enumerate(zip(ws, dims)):
+        _expect(w, (n // d, d, d), f"ws[{j}]")
+    return int(x.shape[0]), n
+
+
 def hyper_forward(x, ws, dims, stream=None):
     """k-factor (hypercube) layer: x [batch, N], ws[j] [N/n_j, n_j, n_j];
     returns (y, saved)."""
+    b, n = _hyper_shapes(x, ws, dims)
     _check(x, *ws)
-    b, n = x.shape
     saved = torch.empty((max(B.monarch_hyper_saved_elems(dims, b), 1),), dtype=x.dtype,
                         device=x.device)
     y = torch.empty_like(x)
@@ -220,8 +272,11 @@ def hyper_forward(x, ws, dims, stream=None):
 
 def hyper_backward(dy, x, ws, saved, dims, stream=None):
     """(dx, [dw_j]) of the hypercube layer."""
+    b, n = _hyper_shapes(x, ws, dims)
+    _expect(dy, (b, n), "dy")
+    if saved.numel() < B.monarch_hyper_saved_elems(dims, b):
+        raise ValueError("saved is smaller than the forward pass writes")
     _check(dy, x, *ws)
-    b = x.shape[0]
     code = dtype_code(x)
     dx = torch.empty_like(x)
     dws = [torch.empty_like(w) for w in ws]
@@ -231,11 +286,20 @@ def hyper_backward(dy, x, ws, saved, dims, stream=None):
     return dx, dws
 
 
+def _dyad_shapes(x, wa, wb):
+    """Check wb == wa == [nb, qo, qi] and x == [batch, nb*qi]."""
+    if x.dim() != 2 or wa.dim() != 3:
+        raise ValueError("x must be [batch, in], wa and wb [nb, out/nb, in/nb]")
+    nb, qo, qi = (int(v) for v in wa.shape)
+    _expect(wb, (nb, qo, qi), "wb")
+    _expect(x, (x.shape[0], nb * qi), "x")
+    return nb, qo, qi, int(x.shape[0])
+
+
 def dyad_forward(x, wa, wb, stream=None):
     """DYAD-style layer: y = x · (BD(A) + Q·BD(B)·P)ᵀ; wa, wb [nb, out/nb, in/nb]."""
+    nb, qo, qi, b = _dyad_shapes(x, wa, wb)
     _check(x, wa, wb)
-    nb, qo, qi = wa.shape
-    b = x.shape[0]
     y = torch.empty((b, nb * qo), dtype=x.dtype, device=x.device)
     need = B.monarch_dyad_fwd_workspace_bytes(x.shape[1], nb * qo, nb, b, dtype_code(x))
     ws = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
@@ -245,9 +309,9 @@ def dyad_forward(x, wa, wb, stream=None):
 
 def dyad_backward(dy, x, wa, wb, stream=None):
     """(dx, dwa, dwb) of the DYAD-style layer."""
+    nb, qo, qi, b = _dyad_shapes(x, wa, wb)
+    _expect(dy, (b, nb * qo), "dy")
     _check(dy, x, wa, wb)
-    nb, qo, qi = wa.shape
-    b = x.shape[0]
     code = dtype_code(x)
     dx, dwa, dwb = torch.empty_like(x), torch.empty_like(wa), torch.empty_like(wb)
     need = B.monarch_dyad_bwd_workspace_bytes(x.shape[1], nb * qo, nb, b, code)

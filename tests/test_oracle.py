@@ -345,23 +345,57 @@ def test_finite_differences(inp, out, b1, b2, relu):
     check_finite_differences(inp, out, b1, b2, relu)
 
 
-def test_mlp_chain_matches_finite_differences():
-    # two layers with ReLU between, as the recommender MLP (shapes scaled down)
-    l1 = _rand_factors(40, 16, 4, 4, seed=20) + (40, 16, True)
-    l2 = _rand_factors(16, 8, 4, 4, seed=21) + (16, 8, False)
+def check_mlp_chain(seed=20):
+    """Central finite differences through the two-layer chain with a ReLU
+    between (the recommender MLP of the "efficiency testing numbers" thread,
+    shapes scaled down): dX and sampled entries of both layers' dw1 and dw2.
+    The weight gradients of each layer must see that layer's own input (the
+    previous layer's post-ReLU output) and the gradient arriving from the
+    layer above, masked where the ReLU was inactive."""
+    l1 = _rand_factors(40, 16, 4, 4, seed=seed) + (40, 16, True)
+    l2 = _rand_factors(16, 8, 4, 4, seed=seed + 1) + (16, 8, False)
     layers = [l1, l2]
-    X = _rng(22).random((3, 40))
-    dY = _rng(23).standard_normal((3, 8))
+    X = _rng(seed + 2).random((3, 40))
+    dY = _rng(seed + 3).standard_normal((3, 8))
     dX, grads = O.mlp_backward(dY, X, layers)
     h = 1e-6
 
-    def f(Xv):
-        return np.vdot(dY, O.mlp_forward(Xv, layers)[0])
-    for idx in [(0, 0), (1, 17), (2, 39)]:
+    def f(Xv, lay):
+        return np.vdot(dY, O.mlp_forward(Xv, lay)[0])
+
+    def fd_x(idx):
         Xp, Xm = X.copy(), X.copy()
         Xp[idx] += h
         Xm[idx] -= h
-        assert abs((f(Xp) - f(Xm)) / (2 * h) - dX[idx]) < 1e-6
+        return (f(Xp, layers) - f(Xm, layers)) / (2 * h)
+
+    def fd_w(li, wi, idx):
+        def with_shift(d):
+            lay = [list(l) for l in layers]
+            w = lay[li][wi].copy()
+            w[idx] += d
+            lay[li][wi] = w
+            return [tuple(l) for l in lay]
+        return (f(X, with_shift(h)) - f(X, with_shift(-h))) / (2 * h)
+
+    for idx in [(0, 0), (1, 17), (2, 39)]:
+        fd = fd_x(idx)
+        assert abs(fd - dX[idx]) < 1e-6 * (1 + abs(fd)), ("x", idx, fd, dX[idx])
+    pick = _rng(seed + 4)
+    for li in range(2):
+        for wi in range(2):
+            g = grads[li][wi]
+            for _ in range(8):
+                idx = tuple(int(pick.integers(0, d)) for d in g.shape)
+                fd = fd_w(li, wi, idx)
+                assert abs(fd - g[idx]) < 1e-6 * (1 + abs(fd)), (li, wi, idx, fd, g[idx])
+    # every weight gradient is exercised (not all zero by a dead ReLU)
+    assert all(np.abs(g).max() > 1e-3 for lg in grads for g in lg)
+
+
+def test_mlp_chain_matches_finite_differences():
+    check_mlp_chain(20)
+    check_mlp_chain(50)
 
 
 def test_sampled_helpers_match_full():
@@ -487,3 +521,40 @@ def test_planted_relu_mask_slip_is_caught(monkeypatch):
         return orig(dy, x, w1, w2, inp, out, relu=False, y=None, factors=factors)
     monkeypatch.setattr(O, "backward", no_mask)
     _expect_fail(check_finite_differences, 64, 32, 4, 4, True)
+
+
+def test_planted_mlp_wrong_activation_is_caught(monkeypatch):
+    # layer 2's weight gradients computed from layer 1's pre-ReLU output
+    # (the wrong activation) instead of its post-ReLU input
+    def bad_mlp_backward(dy, x, layers):
+        h = np.asarray(x, dtype=np.float64)
+        acts, pre = [h], [h]
+        for (w1, w2, fi, fo, relu) in layers:
+            z = O.forward(h, w1, w2, fi, fo, relu=False)
+            h = np.maximum(z, 0) if relu else z
+            pre.append(z)
+            acts.append(h)
+        g = np.asarray(dy, dtype=np.float64)
+        grads = [None] * len(layers)
+        for i in range(len(layers) - 1, -1, -1):
+            w1, w2, fi, fo, relu = layers[i]
+            src = pre[i] if i > 0 else acts[i]
+            _, dw1, dw2 = O.backward(g, src, w1, w2, fi, fo, relu=relu,
+                                     y=acts[i + 1] if relu else None)
+            g, _, _ = O.backward(g, acts[i], w1, w2, fi, fo, relu=relu,
+                                 y=acts[i + 1] if relu else None)
+            grads[i] = (dw1, dw2)
+        return g, grads
+    monkeypatch.setattr(O, "mlp_backward", bad_mlp_backward)
+    _expect_fail(check_mlp_chain, 20)
+
+
+def test_planted_mlp_unmasked_gradient_is_caught(monkeypatch):
+    # layer 1's weight gradients taken from the gradient above the ReLU,
+    # without its mask
+    orig = O.monarch_oracle.backward
+
+    def bad_backward(dy, x, w1, w2, inp, out, relu=False, y=None, factors=None):
+        return orig(dy, x, w1, w2, inp, out, relu=False, factors=factors)
+    monkeypatch.setattr(O.monarch_oracle, "backward", bad_backward)
+    _expect_fail(check_mlp_chain, 20)
