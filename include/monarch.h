@@ -30,7 +30,8 @@
  * Common rules for every entry point:
  *   - Calls are asynchronous and ordered on `stream` (a hipStream_t; NULL is
  *     the default stream). The library never allocates, frees or
- *     synchronises, and keeps no state between calls (reentrant).
+ *     synchronises, and keeps no state between calls (reentrant); the one
+ *     exception is monarch_bwd_noalloc's static scratch, described there.
  *   - The caller owns every buffer. Outputs must not alias inputs.
  *   - Every argument is checked before any HIP call; a rejected call has no
  *     side effects. Checks, in order:
@@ -55,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MONARCH_ABI_VERSION 2
+#define MONARCH_ABI_VERSION 3
 
 typedef enum {
   MONARCH_OK = 0,
@@ -64,7 +65,8 @@ typedef enum {
   MONARCH_ERR_DTYPE = -3,
   MONARCH_ERR_ALIGN = -4,
   MONARCH_ERR_WORKSPACE = -5,
-  MONARCH_ERR_HIP = -6
+  MONARCH_ERR_HIP = -6,
+  MONARCH_ERR_SCRATCH = -7   /* monarch_bwd_noalloc: problem too large for its scratch */
 } monarch_status;
 
 typedef enum { MONARCH_F32 = 0, MONARCH_BF16 = 1 } monarch_dtype;
@@ -154,6 +156,27 @@ int monarch_describe(int direction, int64_t in_features, int64_t out_features,
 int monarch_project(const void* m, void* w1, void* w2, int64_t in_features,
                     int64_t out_features, int64_t nblocks1, int64_t nblocks2, int dtype,
                     int iters, void* stream);
+
+/* ---------------------------------------------------------------------------
+ * monarch_bwd without a workspace argument, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid hipMalloc). Arguments, layouts, results and errors as for
+ * monarch_bwd; the same kernels run. The intermediates and partial sums live
+ * in a static array of MONARCH_NOALLOC_SCRATCH_BYTES bytes per GPU, which
+ * the library holds on each GPU it runs on until the process ends (its
+ * address is looked up on the first call on a device, with the calling
+ * thread's current device, which must be the stream's). A problem whose
+ * monarch_bwd_workspace_bytes() exceeds that size returns
+ * MONARCH_ERR_SCRATCH before any HIP call. No allocating call is made. The
+ * array is shared by every call on one GPU: calls that overlap in time on
+ * one GPU (other streams, other threads) race and must be serialised by the
+ * caller. */
+#define MONARCH_NOALLOC_SCRATCH_BYTES (256ull << 20)
+
+int monarch_bwd_noalloc(const void* dy, const void* x, const void* w1, const void* w2,
+                        const void* z, const void* y, void* dx, void* dw1, void* dw2,
+                        int64_t in_features, int64_t out_features, int64_t nblocks1,
+                        int64_t nblocks2, int64_t batch, int dtype, int act, void* stream);
 
 /* ---------------------------------------------------------------------------
  * General layer shapes (the MonarchLinear constructor in the "Definition C.3"

@@ -21,6 +21,9 @@ MONARCH_ERR_DTYPE = -3
 MONARCH_ERR_ALIGN = -4
 MONARCH_ERR_WORKSPACE = -5
 MONARCH_ERR_HIP = -6
+MONARCH_ERR_SCRATCH = -7
+# static scratch of monarch_bwd_noalloc per GPU (MONARCH_NOALLOC_SCRATCH_BYTES)
+NOALLOC_SCRATCH_BYTES = 256 << 20
 
 F32 = 0
 BF16 = 1
@@ -35,7 +38,7 @@ EXPORTED = (
     "monarch_hyper_fwd", "monarch_hyper_bwd_workspace_bytes", "monarch_hyper_bwd",
     "monarch_hyper_describe", "monarch_dyad_fwd_workspace_bytes", "monarch_dyad_fwd",
     "monarch_dyad_bwd_workspace_bytes",
-    "monarch_dyad_bwd", "monarch_dyad_describe",
+    "monarch_dyad_bwd", "monarch_dyad_describe", "monarch_bwd_noalloc",
 )
 
 _lib = None
@@ -70,6 +73,8 @@ def load_library():
     lib.monarch_bwd_traced.argtypes = [vp] * 10 + [sz] + shape + [c_int, c_int, vp,
                                                                    ctypes.POINTER(vp), c_int]
     lib.monarch_bwd_traced.restype = c_int
+    lib.monarch_bwd_noalloc.argtypes = [vp] * 9 + shape + [c_int, c_int, vp]
+    lib.monarch_bwd_noalloc.restype = c_int
     lib.monarch_describe.argtypes = [c_int] + shape + [c_int, c_int, ctypes.c_char_p, sz]
     lib.monarch_describe.restype = c_int
     lib.monarch_status_string.argtypes = [c_int]
@@ -192,6 +197,14 @@ def monarch_bwd(dy, x, w1, w2, z, y, dx, dw1, dw2, workspace, workspace_bytes, i
     else:
         arr, n = _events(events)
         _check(lib.monarch_bwd_traced(*args, arr, n))
+
+
+def monarch_bwd_noalloc(dy, x, w1, w2, z, y, dx, dw1, dw2, in_features, out_features, nblocks1,
+                        nblocks2, batch, dtype, act=ACT_NONE, stream=None) -> None:
+    lib = load_library()
+    _check(lib.monarch_bwd_noalloc(_ptr(dy), _ptr(x), _ptr(w1), _ptr(w2), _ptr(z), _ptr(y),
+                                   _ptr(dx), _ptr(dw1), _ptr(dw2), in_features, out_features,
+                                   nblocks1, nblocks2, batch, dtype, act, _stream(stream)))
 
 
 def monarch_project(m, w1, w2, in_features, out_features, nblocks1, nblocks2, dtype, iters=32,

@@ -11,11 +11,13 @@
 #include "kernels.h"
 #include "monarch.h"
 #include "plan.h"
+#include "api_internal.h"
 
 namespace monarch {
-namespace {
 
+namespace {
 thread_local char g_hip_error[256] = "no HIP error recorded";
+}  // namespace
 
 int record_hip(hipError_t e) {
   if (e == hipSuccess) return MONARCH_OK;
@@ -23,6 +25,8 @@ int record_hip(hipError_t e) {
            hipGetErrorString(e));
   return MONARCH_ERR_HIP;
 }
+
+namespace {
 
 bool misaligned(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) != 0; }
 
@@ -68,38 +72,6 @@ int fwd_impl(const Problem& pr, const void* x, const void* w1, const void* w2, c
   b.y_out = y;
   b.z_out = z;
   Plan plan = plan_fwd(pr);
-  return run_plan(plan, pr, b, static_cast<hipStream_t>(stream), events, n_events);
-}
-
-int bwd_impl(const Problem& pr, const void* dy, const void* x, const void* w1, const void* w2,
-             const void* z, const void* y, void* dx, void* dw1, void* dw2, void* dbias, void* ws,
-             size_t ws_bytes, void* stream, void* const* events, int n_events) {
-  if (!w1 || !w2 || !dw1 || !dw2) return MONARCH_ERR_NULL;
-  if (pr.bias && !dbias) return MONARCH_ERR_NULL;
-  if (pr.batch > 0) {
-    if (!dy || !x || !z || !dx) return MONARCH_ERR_NULL;
-    if (pr.act == MONARCH_ACT_RELU && !y) return MONARCH_ERR_NULL;
-  }
-  const size_t need = workspace_bytes(pr);
-  if (need > 0 && !ws) return MONARCH_ERR_NULL;
-  if (misaligned(dy) || misaligned(x) || misaligned(w1) || misaligned(w2) || misaligned(z) ||
-      misaligned(y) || misaligned(dx) || misaligned(dw1) || misaligned(dw2) ||
-      misaligned(dbias) || misaligned(ws))
-    return MONARCH_ERR_ALIGN;
-  if (ws_bytes < need) return MONARCH_ERR_WORKSPACE;
-  Buffers b;
-  b.dy = dy;
-  b.x = x;
-  b.w1 = w1;
-  b.w2 = w2;
-  b.z = z;
-  b.y = y;
-  b.dx = dx;
-  b.dw1 = dw1;
-  b.dw2 = dw2;
-  b.dbias = dbias;
-  b.ws = ws;
-  Plan plan = plan_bwd(pr);
   return run_plan(plan, pr, b, static_cast<hipStream_t>(stream), events, n_events);
 }
 
@@ -157,6 +129,47 @@ int describe_plan(const Problem& pr, int direction, char* buf, size_t buf_len) {
 }
 
 }  // namespace
+
+int bwd_check(const Problem& pr, const void* dy, const void* x, const void* w1, const void* w2,
+              const void* z, const void* y, const void* dx, const void* dw1, const void* dw2,
+              const void* dbias) {
+  if (!w1 || !w2 || !dw1 || !dw2) return MONARCH_ERR_NULL;
+  if (pr.bias && !dbias) return MONARCH_ERR_NULL;
+  if (pr.batch > 0) {
+    if (!dy || !x || !z || !dx) return MONARCH_ERR_NULL;
+    if (pr.act == MONARCH_ACT_RELU && !y) return MONARCH_ERR_NULL;
+  }
+  if (misaligned(dy) || misaligned(x) || misaligned(w1) || misaligned(w2) || misaligned(z) ||
+      misaligned(y) || misaligned(dx) || misaligned(dw1) || misaligned(dw2) || misaligned(dbias))
+    return MONARCH_ERR_ALIGN;
+  return MONARCH_OK;
+}
+
+int bwd_impl(const Problem& pr, const void* dy, const void* x, const void* w1, const void* w2,
+             const void* z, const void* y, void* dx, void* dw1, void* dw2, void* dbias, void* ws,
+             size_t ws_bytes, void* stream, void* const* events, int n_events) {
+  int st = bwd_check(pr, dy, x, w1, w2, z, y, dx, dw1, dw2, dbias);
+  if (st) return st;
+  const size_t need = workspace_bytes(pr);
+  if (need > 0 && !ws) return MONARCH_ERR_NULL;
+  if (misaligned(ws)) return MONARCH_ERR_ALIGN;
+  if (ws_bytes < need) return MONARCH_ERR_WORKSPACE;
+  Buffers b;
+  b.dy = dy;
+  b.x = x;
+  b.w1 = w1;
+  b.w2 = w2;
+  b.z = z;
+  b.y = y;
+  b.dx = dx;
+  b.dw1 = dw1;
+  b.dw2 = dw2;
+  b.dbias = dbias;
+  b.ws = ws;
+  Plan plan = plan_bwd(pr);
+  return run_plan(plan, pr, b, static_cast<hipStream_t>(stream), events, n_events);
+}
+
 }  // namespace monarch
 
 using namespace monarch;
@@ -457,6 +470,8 @@ const char* monarch_status_string(int status) {
     case MONARCH_ERR_ALIGN: return "a pointer is not 16-byte aligned";
     case MONARCH_ERR_WORKSPACE: return "workspace smaller than monarch_bwd_workspace_bytes()";
     case MONARCH_ERR_HIP: return g_hip_error;
+    case MONARCH_ERR_SCRATCH:
+      return "problem needs more than MONARCH_NOALLOC_SCRATCH_BYTES of scratch (use monarch_bwd)";
     default: return "unknown status";
   }
 }

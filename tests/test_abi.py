@@ -40,7 +40,7 @@ def test_abi_version_matches_header():
 
 
 def test_status_strings():
-    for st in (0, -1, -2, -3, -4, -5, -6, 7):
+    for st in (0, -1, -2, -3, -4, -5, -6, -7, 7):
         s = M.monarch_status_string(st)
         assert isinstance(s, str) and s
     assert "aligned" in M.monarch_status_string(B.MONARCH_ERR_ALIGN)
@@ -342,3 +342,36 @@ def test_dyad_plan_and_checks():
                                 0) == B.MONARCH_ERR_DTYPE
     assert lib.monarch_dyad_bwd(A, A, A, A, A2, A2, A2, A2, 0, 64, 32, 4, 8, B.F32, None, None,
                                 0) == B.MONARCH_ERR_WORKSPACE
+
+
+def bwd_noalloc(dy=A, x=A, w1=A, w2=A, z=A, y=A, dx=A2, dw1=A2, dw2=A2, fi=16, fo=16, nb1=4,
+                nb2=4, b=8, dt=B.F32, act=B.ACT_NONE):
+    lib = M.load_library()
+    return lib.monarch_bwd_noalloc(dy, x, w1, w2, z, y, dx, dw1, dw2, fi, fo, nb1, nb2, b, dt,
+                                   act, None)
+
+
+def test_noalloc_checks_before_any_hip_call():
+    # every rejection below happens before the library touches the device
+    assert bwd_noalloc(dt=2) == B.MONARCH_ERR_DTYPE
+    assert bwd_noalloc(fi=18) == B.MONARCH_ERR_SHAPE
+    assert bwd_noalloc(dx=0) == B.MONARCH_ERR_NULL
+    assert bwd_noalloc(y=0, act=B.ACT_RELU) == B.MONARCH_ERR_NULL
+    assert bwd_noalloc(w2=MIS) == B.MONARCH_ERR_ALIGN
+    # the largest square layer at full batch needs 4 GiB of workspace
+    big = dict(fi=16384, fo=16384, nb1=128, nb2=128, b=65536, dt=B.BF16)
+    need = M.monarch_bwd_workspace_bytes(16384, 16384, 128, 128, 65536, B.BF16)
+    assert need > B.NOALLOC_SCRATCH_BYTES
+    assert bwd_noalloc(**big) == B.MONARCH_ERR_SCRATCH
+    assert "scratch" in M.monarch_status_string(B.MONARCH_ERR_SCRATCH)
+
+
+def test_noalloc_scratch_size_matches_header():
+    text = open(HEADER).read()
+    m = re.search(r"#define MONARCH_NOALLOC_SCRATCH_BYTES \((\d+)ull << (\d+)\)", text)
+    assert m and (int(m.group(1)) << int(m.group(2))) == B.NOALLOC_SCRATCH_BYTES
+    # the workloads it is sized for fit: the 1024-feature square layer at 4096
+    # rows and both recommender layers at 10000 rows
+    for args in ((1024, 1024, 32, 32, 4096, B.BF16), (10000, 1024, 4, 4, 10000, B.F32),
+                 (1024, 512, 16, 16, 10000, B.F32)):
+        assert M.monarch_bwd_workspace_bytes(*args) <= B.NOALLOC_SCRATCH_BYTES
