@@ -60,9 +60,11 @@ def kernel_bytes(name: str, pr: dict) -> float:
         "stage1_bwd_data": e * B * (mid + inp) + e * p1,
         "stage1_bwd_weight": e * B * (mid + inp) + e * p1,
         "stage1_bwd": e * B * (mid + 2 * inp) + 2 * e * p1,
-        # square fast path: dY (and Y for the ReLU mask) -> block-major dV, then
-        # both stage-2 backward kernels read dV instead of dY
-        "sq128_dv_panels": e * B * out * (3 if relu else 2),
+        # square fast path: the dV pass (dY, and Y for the ReLU mask, ->
+        # block-major dV) is a layout pass with no algorithmic bytes of its
+        # own (its traffic is overhead against the two-pass count); both
+        # stage-2 backward kernels then read dV in place of dY
+        "sq128_dv_panels": 0.0,
         "sq128_stage2_bwd_data": e * B * (out + mid) + e * p2,
         "sq128_stage2_bwd_weight": e * B * (out + mid) + e * p2,
         # fused 32x32-block path: x -> z, y; dY (and Y for the ReLU mask) ->

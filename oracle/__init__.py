@@ -7,6 +7,7 @@ from .monarch_oracle import (  # noqa: F401
     derive_sizes, param_count, block_diag_dense, stride_permutation, output_permutation,
     dense_factors, monarch_matrix, forward, backward, mlp_forward, mlp_backward,
     forward_rows, backward_dx_rows, weight_grad_entries, rel_frobenius,
+    max_row_rel_error, parity_error,
 )
 from . import monarch_projection  # noqa: F401,E402
 from . import monarch_linear  # noqa: F401,E402

@@ -300,3 +300,42 @@ def rel_frobenius(a: np.ndarray, ref: np.ndarray) -> float:
     if den == 0.0:
         return 0.0 if num == 0.0 else float("inf")
     return float(num / den)
+
+
+def max_row_rel_error(a: np.ndarray, ref: np.ndarray, scale: Optional[np.ndarray] = None,
+                      floor: float = 1e-3) -> float:
+    """Largest relative error of one row, rows taken along the last axis
+    (batch rows of activations, block rows of weight gradients).
+
+    With `scale` (the same result computed from the absolute values of every
+    input, so each entry is the sum of the magnitudes of the terms it adds
+    up), row r is measured as ||a_r - ref_r|| / ||scale_r||: the standard
+    bound on the rounding error of a sum is proportional to the magnitudes
+    summed, and a row whose terms cancel is then not held to a bound relative
+    to its small result. Without cancellation scale_r = |ref_r| and this is
+    the plain row-relative error. Without `scale`, row r is measured against
+    ||ref_r||, or `floor` times the RMS row norm when that is larger."""
+    a = np.asarray(a, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    if ref.size == 0:
+        return 0.0
+    last = ref.shape[-1] if ref.ndim else 1
+    a2, r2 = a.reshape(-1, last), ref.reshape(-1, last)
+    num = np.linalg.norm(a2 - r2, axis=1)
+    if scale is not None:
+        den = np.linalg.norm(np.asarray(scale, dtype=np.float64).reshape(-1, last), axis=1)
+        with np.errstate(divide="ignore", invalid="ignore"):
+            e = np.where(num == 0.0, 0.0, num / den)
+        return float(np.max(e))
+    den = np.linalg.norm(r2, axis=1)
+    rms = np.linalg.norm(r2) / np.sqrt(r2.shape[0])
+    if rms == 0.0:
+        return 0.0 if not num.any() else float("inf")
+    return float(np.max(num / np.maximum(den, floor * rms)))
+
+
+def parity_error(a: np.ndarray, ref: np.ndarray, scale: Optional[np.ndarray] = None) -> float:
+    """The larger of the whole-tensor relative Frobenius error and the worst
+    row's error (max_row_rel_error, against `scale` when given): a result
+    passes a bound only if the tensor as a whole and every row of it do."""
+    return max(rel_frobenius(a, ref), max_row_rel_error(a, ref, scale))

@@ -8,7 +8,7 @@ import numpy as np
 import pytest
 
 from oracle import monarch_linear as ML
-from oracle.monarch_oracle import rel_frobenius
+from oracle.monarch_oracle import parity_error, rel_frobenius
 from monarch_block_diagonal_amd import synthetic as S
 
 pytestmark = pytest.mark.gpu
@@ -63,17 +63,22 @@ def check(api, inp, out, mid, b1, b2, batch, dtype, with_bias, relu, seed=7100):
     y, z = api.monarch_forward_ex(X, W1, W2, out, Bv, act)
     torch.cuda.synchronize()
     y_ref = ML.forward_ex(x, w1, w2, inp, out, mid, b, relu)
-    errs = {"y": rel_frobenius(host(y), y_ref)}
+    # row scales: the same results from the absolute values of every input
+    ab = np.abs(b) if with_bias else None
+    ys = ML.forward_ex(np.abs(x), np.abs(w1), np.abs(w2), inp, out, mid, ab, False)
+    errs = {"y": parity_error(host(y), y_ref, ys)}
     # the GPU backward masks with the oracle's forward output, so both sides
     # mask the same entries
     mask = dev(y_ref, dtype) if relu else None
     dx, dw1, dw2, db = api.monarch_backward_ex(dev(dy, dtype), X, W1, W2, z, mask, with_bias, act)
     torch.cuda.synchronize()
     rx, r1, r2, rb = ML.backward_ex(dy, x, w1, w2, inp, out, mid, b, relu, y=y_ref)
-    errs.update(dx=rel_frobenius(host(dx), rx), dw1=rel_frobenius(host(dw1), r1),
-                dw2=rel_frobenius(host(dw2), r2))
+    sx, s1, s2, sb = ML.backward_ex(np.abs(dy), np.abs(x), np.abs(w1), np.abs(w2), inp, out, mid,
+                                    ab, relu, y=y_ref)
+    errs.update(dx=parity_error(host(dx), rx, sx), dw1=parity_error(host(dw1), r1, s1),
+                dw2=parity_error(host(dw2), r2, s2))
     if with_bias:
-        errs["dbias"] = rel_frobenius(host(db), rb)
+        errs["dbias"] = parity_error(host(db), rb, sb)
     say(f"[linear]   errors {errs}")
     for k, e in errs.items():
         assert e <= TOL[dtype], (k, e)

@@ -421,6 +421,50 @@ def test_sampled_helpers_match_full():
             np.testing.assert_allclose(el, [dw2[i] for i in gpt], rtol=1e-11, atol=1e-12)
 
 
+def test_row_errors():
+    ref = np.array([[3.0, 4.0], [0.0, 10.0], [1.0, 0.0]])
+    a = ref.copy()
+    assert O.max_row_rel_error(a, ref) == 0.0 and O.parity_error(a, ref) == 0.0
+    # one row off by 10% of its own norm: the worst row reports 0.1 while the
+    # whole-tensor Frobenius error is diluted by the other rows
+    a[2] = [1.1, 0.0]
+    assert abs(O.max_row_rel_error(a, ref) - 0.1) < 1e-12
+    assert O.rel_frobenius(a, ref) < 0.02
+    assert abs(O.parity_error(a, ref) - 0.1) < 1e-12
+    # a zeroed row fails the row bound whatever the other rows hold
+    big = np.ones((4113, 8))
+    z = big.copy()
+    z[17] = 0.0
+    assert O.rel_frobenius(z, big) < 0.02 and O.max_row_rel_error(z, big) == 1.0
+    # a reference row of zeros is measured against the floor (1e-3 of the RMS row norm)
+    r0 = np.array([[1.0, 0.0], [0.0, 0.0]])
+    rms = np.linalg.norm(r0) / np.sqrt(2)
+    e = O.max_row_rel_error(np.array([[1.0, 0.0], [1e-6, 0.0]]), r0)
+    assert abs(e - 1e-6 / (1e-3 * rms)) < 1e-12
+    # weight-gradient blocks: rows along the last axis
+    g = np.arange(24, dtype=float).reshape(2, 3, 4) + 1
+    h = g.copy()
+    h[1, 2, 3] *= 1.5
+    row = g[1, 2]
+    assert abs(O.max_row_rel_error(h, g) - 0.5 * row[3] / np.linalg.norm(row)) < 1e-12
+
+
+def test_row_errors_against_absolute_scale():
+    # a row whose terms cancel: ref = 1 - 0.999, scale = 1 + 0.999
+    ref = np.array([[0.001, 5.0]])
+    scale = np.array([[1.999, 5.0]])
+    a = ref + np.array([[1e-3, 0.0]])
+    assert abs(O.max_row_rel_error(a, ref, scale) - 1e-3 / np.linalg.norm(scale)) < 1e-15
+    assert O.max_row_rel_error(a, ref) > O.max_row_rel_error(a, ref, scale)
+    # the scale of a sum is the same sum over magnitudes: for the Monarch
+    # product it is the oracle run on |X|, |w1|, |w2|
+    w1, w2 = _rand_factors(16, 16, 4, 4, seed=3)
+    x = _rng(4).standard_normal((5, 16))
+    sc = O.forward(np.abs(x), np.abs(w1), np.abs(w2), 16, 16)
+    assert np.all(sc >= np.abs(O.forward(x, w1, w2, 16, 16)) - 1e-12)
+    assert O.parity_error(O.forward(x, w1, w2, 16, 16), O.forward(x, w1, w2, 16, 16), sc) == 0.0
+
+
 def test_rel_frobenius():
     a = np.array([3.0, 4.0])
     assert O.rel_frobenius(a, a) == 0.0

@@ -16,7 +16,7 @@ import pytest
 
 import oracle as O
 from oracle import monarch_linear as ML
-from oracle.monarch_oracle import rel_frobenius
+from oracle.monarch_oracle import parity_error, rel_frobenius
 from monarch_block_diagonal_amd import synthetic as S
 
 pytestmark = pytest.mark.gpu
@@ -109,10 +109,15 @@ def test_sweep_general(api, case):
     dx, dw1, dw2, db = api.monarch_backward_ex(dev(dy, dtype), X, W1, W2, z, mask, with_bias, act)
     torch.cuda.synchronize()
     rx, r1, r2, rb = ML.backward_ex(dy, x, w1, w2, inp, out, mid, bias, relu, y=y_ref)
-    errs = {"y": rel_frobenius(host(y), y_ref), "dx": rel_frobenius(host(dx), rx),
-            "dw1": rel_frobenius(host(dw1), r1), "dw2": rel_frobenius(host(dw2), r2)}
+    # row scales: the same results from the absolute values of every input
+    ab = np.abs(bias) if with_bias else None
+    ys = ML.forward_ex(np.abs(x), np.abs(w1), np.abs(w2), inp, out, mid, ab, False)
+    sx, s1, s2, sb = ML.backward_ex(np.abs(dy), np.abs(x), np.abs(w1), np.abs(w2), inp, out, mid,
+                                    ab, relu, y=y_ref)
+    errs = {"y": parity_error(host(y), y_ref, ys), "dx": parity_error(host(dx), rx, sx),
+            "dw1": parity_error(host(dw1), r1, s1), "dw2": parity_error(host(dw2), r2, s2)}
     if with_bias:
-        errs["dbias"] = rel_frobenius(host(db), rb)
+        errs["dbias"] = parity_error(host(db), rb, sb)
     say(f"[sweep]   errors {errs}")
     for k, e in errs.items():
         assert e <= TOL[dtype], (case, k, e)
@@ -140,8 +145,12 @@ def test_sweep_square_paths(api, case):
     dx, dw1, dw2 = api.monarch_backward(dev(dy, "bf16"), X, W1, W2, z, mask, act)
     torch.cuda.synchronize()
     rx, r1, r2 = O.backward(dy, x, w1, w2, n, n, relu=relu, y=y_ref, factors=fac)
-    errs = {"y": rel_frobenius(host(y), y_ref), "dx": rel_frobenius(host(dx), rx),
-            "dw1": rel_frobenius(host(dw1), r1), "dw2": rel_frobenius(host(dw2), r2)}
+    afac = O.dense_factors(np.abs(w1), np.abs(w2), n, n, sparse=n * n > (1 << 22))
+    ys = O.forward(np.abs(x), np.abs(w1), np.abs(w2), n, n, factors=afac)
+    sx, s1, s2 = O.backward(np.abs(dy), np.abs(x), np.abs(w1), np.abs(w2), n, n, relu=relu,
+                            y=y_ref, factors=afac)
+    errs = {"y": parity_error(host(y), y_ref, ys), "dx": parity_error(host(dx), rx, sx),
+            "dw1": parity_error(host(dw1), r1, s1), "dw2": parity_error(host(dw2), r2, s2)}
     say(f"[sweep]   errors {errs}")
     for k, e in errs.items():
         assert e <= TOL["bf16"], (case, k, e)
