@@ -26,6 +26,9 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # dense MFMA, published
+# fp32 on the vector ALU without packed instructions: 256 CUs x 4 SIMDs x 16
+# lanes x 2 flops (FMA) x 2.4 GHz
+FP32_VALU_PEAK_TFLOPS = 78.6
 
 DEFAULT_WORKLOAD = "square_n16384_b128"
 
@@ -164,16 +167,18 @@ def bench_project(args) -> int:
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
     q = n // b
-    log(f"projection: {n} x {n} bf16, {b} x {b} slices of {q} x {q}, {args.iters} iterations")
+    log(f"projection: {n} x {n} bf16, {b} x {b} slices of {q} x {q}, "
+        f"at most {args.max_steps} products per slice")
     g = torch.Generator(device=dev)
     g.manual_seed(S.seed_for(4, S.TID_X) + 99)
     m = torch.randn((n, n), generator=g, device=dev, dtype=torch.float32).to(torch.bfloat16)
     w1 = torch.empty((b, b, q), dtype=torch.bfloat16, device=dev)
     w2 = torch.empty((b, q, b), dtype=torch.bfloat16, device=dev)
+    status = torch.empty((b * b,), dtype=torch.int32, device=dev)
     stream = torch.cuda.current_stream()
 
     def run():
-        M.monarch_project(m, w1, w2, n, n, b, b, M.BF16, args.iters, stream)
+        M.monarch_project(m, w1, w2, n, n, b, b, M.BF16, args.max_steps, status, stream)
 
     for _ in range(args.warmup):
         run()
@@ -189,11 +194,14 @@ def bench_project(args) -> int:
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t0) / K
     ms = e0.elapsed_time(e1) / K
-    # work per slice (bf16 128 x 128 slices): B = AᵀA on MFMA (2 q³ flops), then
-    # on the vector ALU the column sums, one product B v per iteration and the
-    # final A v (2 flops per multiply-add)
-    flops = b * b * 2.0 * q * q * (args.iters + 2)
-    mfma_flops = b * b * 2.0 * q * q * q
+    # work per slice: each product with AᵀA is u = A v, w = Aᵀ u on the vector
+    # ALU, 4 q² flops (2 per multiply-add); the status array holds the products
+    # each slice used. The reorthogonalisation (8 (j+1) q flops at step j) and
+    # the small tridiagonal solves are not counted.
+    st = status.cpu().numpy()
+    converged = int((st > 0).sum())
+    products = float(st[st > 0].sum())
+    flops = 4.0 * q * q * products
     hbm = 2.0 * n * n + 2 * 2.0 * b * b * q
     tflops = flops / (ms * 1e-3) / 1e12
     cpu = None
@@ -221,14 +229,15 @@ def bench_project(args) -> int:
         "metric": "Monarch projection slices/s", "value": round(b * b / (ms * 1e-3), 1),
         "unit": "slices/s", "n_gpus": 1, "steps": K, "warmup": args.warmup,
         "ms_per_step": round(ms, 4), "wall_ms_per_step": round(wall * 1e3, 4),
-        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "f32",
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
         "data": "synthetic (seeded N(0,1) matrix drawn on the device, stored bf16)",
-        "config": {"workload": f"project_n{n}_b{b}", "n": n, "nblocks": b, "iters": args.iters,
-                   "input": "bf16"},
-        "roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": 157.3,
-                     "unit": "TFLOP/s", "frac": round(tflops / 157.3, 4), "traffic": None,
-                     "hbm_bytes": hbm, "hbm_frac": round(hbm / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-                     "mfma_tflops": round(mfma_flops / (ms * 1e-3) / 1e12, 2)},
+        "config": {"workload": f"project_n{n}_b{b}", "n": n, "nblocks": b,
+                   "max_steps": args.max_steps, "input": "bf16", "compute": "fp32"},
+        "converged_slices": converged, "products_per_slice": round(products / max(converged, 1), 2),
+        "roofline": {"bound": "alu", "achieved": round(tflops, 2), "peak": FP32_VALU_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(tflops / FP32_VALU_PEAK_TFLOPS, 4),
+                     "traffic": None, "hbm_bytes": hbm,
+                     "hbm_frac": round(hbm / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)},
         "cpu_baseline": cpu,
     }
     print(json.dumps(result), flush=True)
@@ -461,7 +470,8 @@ def main() -> int:
     ap.add_argument("--rows", type=int, default=16384, help="tokens of --op hyper / dyad")
     ap.add_argument("--dtype", choices=("bf16", "f32"), default="bf16",
                     help="dtype of --op hyper / dyad")
-    ap.add_argument("--iters", type=int, default=32, help="power iterations (--op project)")
+    ap.add_argument("--max-steps", type=int, default=256,
+                    help="products with AᵀA each slice may use (--op project)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))

@@ -56,7 +56,7 @@
 extern "C" {
 #endif
 
-#define MONARCH_ABI_VERSION 3
+#define MONARCH_ABI_VERSION 4
 
 typedef enum {
   MONARCH_OK = 0,
@@ -145,17 +145,23 @@ int monarch_describe(int direction, int64_t in_features, int64_t out_features,
  *   m  [out, in] row-major, read;  w1 [b1, b2, q1i] and w2 [b2, q2o, b1],
  *   overwritten, in the layouts monarch_fwd takes.
  *
- * Each slice is fitted in fp32 by `iters` power iterations (1..4096) from the
- * column sums of the slice; the rate is (sigma2/sigma1)^2 per iteration and
- * an exactly rank-one slice is exact after one. The factors split sqrt(sigma)
- * evenly, with the sign making the largest-magnitude entry of w1[r, g, :]
- * (the first on ties) positive. A slice must fit in one workgroup's LDS:
- * q2o * (q1i + 1) + q1i + q2o + 16 <= 40960 fp32 values (128 x 128 slices
- * fit). Errors as for monarch_fwd; shapes outside the case, iters out of
- * range or a slice too large give MONARCH_ERR_SHAPE. */
+ * A slice A (q2o x q1i) is fitted by x, the unit vector maximising xᵀAᵀAx
+ * (the fit (A x) xᵀ leaves ||A||² - xᵀAᵀAx): Lanczos on AᵀA in fp32 with
+ * full reorthogonalisation, in cycles of up to 32 products restarted from the
+ * Ritz vector, until ||AᵀA x - theta x|| <= 1e-4 * theta (theta = xᵀAᵀAx) or
+ * max_steps (1..4096) products with AᵀA have been spent. The factors split
+ * sqrt(sigma) evenly (sigma = ||A x||), with the sign making the
+ * largest-magnitude entry of w1[r, g, :] (the first on ties) positive.
+ * converged (may be NULL): int32 [nb1 * nb2] device array; element
+ * r*nb2 + g is set to the number of products with AᵀA slice (g, r) used
+ * (> 0) when it met the tolerance, 0 when the budget ran out first (its
+ * factors are then the last Ritz vector's fit).
+ * Slices up to 128 x 128 (q1i, q2o <= 128). Errors as for monarch_fwd;
+ * shapes outside the case, max_steps out of range or a slice too large give
+ * MONARCH_ERR_SHAPE. */
 int monarch_project(const void* m, void* w1, void* w2, int64_t in_features,
                     int64_t out_features, int64_t nblocks1, int64_t nblocks2, int dtype,
-                    int iters, void* stream);
+                    int max_steps, int* converged, void* stream);
 
 /* ---------------------------------------------------------------------------
  * monarch_bwd without a workspace argument, for callers that cannot allocate

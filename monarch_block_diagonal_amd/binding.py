@@ -81,7 +81,7 @@ def load_library():
     lib.monarch_status_string.restype = ctypes.c_char_p
     lib.monarch_abi_version.argtypes = []
     lib.monarch_abi_version.restype = c_int
-    lib.monarch_project.argtypes = [vp] * 3 + [i64] * 4 + [c_int, c_int, vp]
+    lib.monarch_project.argtypes = [vp] * 3 + [i64] * 4 + [c_int, c_int, vp, vp]
     lib.monarch_project.restype = c_int
     ev = [ctypes.POINTER(vp), c_int]
     lib.monarch_linear_mid.argtypes = [i64] * 3
@@ -207,11 +207,11 @@ def monarch_bwd_noalloc(dy, x, w1, w2, z, y, dx, dw1, dw2, in_features, out_feat
                                    nblocks1, nblocks2, batch, dtype, act, _stream(stream)))
 
 
-def monarch_project(m, w1, w2, in_features, out_features, nblocks1, nblocks2, dtype, iters=32,
-                    stream=None) -> None:
+def monarch_project(m, w1, w2, in_features, out_features, nblocks1, nblocks2, dtype,
+                    max_steps=256, converged=None, stream=None) -> None:
     lib = load_library()
     _check(lib.monarch_project(_ptr(m), _ptr(w1), _ptr(w2), in_features, out_features, nblocks1,
-                               nblocks2, dtype, iters, _stream(stream)))
+                               nblocks2, dtype, max_steps, _ptr(converged), _stream(stream)))
 
 
 def monarch_describe(direction, in_features, out_features, nblocks1, nblocks2, batch, dtype,

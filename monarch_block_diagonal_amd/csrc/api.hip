@@ -279,19 +279,21 @@ int monarch_describe_ex(int direction, int64_t in_features, int64_t out_features
 
 int monarch_project(const void* m, void* w1, void* w2, int64_t in_features,
                     int64_t out_features, int64_t nblocks1, int64_t nblocks2, int dtype,
-                    int iters, void* stream) {
+                    int max_steps, int* converged, void* stream) {
   if (dtype != MONARCH_F32 && dtype != MONARCH_BF16) return MONARCH_ERR_DTYPE;
   const int64_t lim = int64_t(1) << 31;
   if (in_features <= 0 || out_features <= 0 || nblocks1 <= 0 || nblocks2 <= 0 ||
       in_features >= lim || out_features >= lim || in_features % nblocks1 != 0 ||
-      out_features != nblocks1 * nblocks2 || iters < 1 || iters > 4096)
+      out_features != nblocks1 * nblocks2 || max_steps < 1 || max_steps > 4096)
     return MONARCH_ERR_SHAPE;
   const int64_t q1i = in_features / nblocks1, q2o = out_features / nblocks2;
-  if (project_lds_bytes(q1i, q2o) > 40960 * sizeof(float)) return MONARCH_ERR_SHAPE;
+  if (!project_pad(q1i, q2o)) return MONARCH_ERR_SHAPE;
   if (!m || !w1 || !w2) return MONARCH_ERR_NULL;
   if (misaligned(m) || misaligned(w1) || misaligned(w2)) return MONARCH_ERR_ALIGN;
-  return record_hip(launch_project(m, w1, w2, in_features, nblocks1, nblocks2, q1i, q2o, iters,
-                                   dtype == MONARCH_BF16, static_cast<hipStream_t>(stream)));
+  if (reinterpret_cast<uintptr_t>(converged) & 3u) return MONARCH_ERR_ALIGN;
+  return record_hip(launch_project(m, w1, w2, converged, in_features, nblocks1, nblocks2, q1i,
+                                   q2o, max_steps, dtype == MONARCH_BF16,
+                                   static_cast<hipStream_t>(stream)));
 }
 
 int monarch_describe(int direction, int64_t in_features, int64_t out_features, int64_t nblocks1,

@@ -131,11 +131,14 @@ hipError_t launch_reduce_partials(const ReduceArgs& a, const ReduceArgs& b, cons
                                   bool bf16, hipStream_t s);
 
 // Dense -> Monarch projection: one workgroup per (g, r) slice of M
-// [out = nb1*nb2, in]; writes w1 [nb1, nb2, q1i] and w2 [nb2, q2o, nb1].
-// project_lds_bytes is the dynamic LDS one workgroup needs.
-size_t project_lds_bytes(int64_t q1i, int64_t q2o);
-hipError_t launch_project(const void* m, void* w1, void* w2, int64_t in, int64_t nb1,
-                          int64_t nb2, int64_t q1i, int64_t q2o, int iters, bool bf16,
-                          hipStream_t s);
+// [out = nb1*nb2, in]; writes w1 [nb1, nb2, q1i], w2 [nb2, q2o, nb1] and, when
+// status is set, status[r*nb2 + g] = the products with AᵀA a converged slice
+// used (> 0), or 0 when it did not converge.
+// project_pad is the padded slice size (16, 32, 64 or 128), 0 when a slice
+// side exceeds 128.
+int project_pad(int64_t q1i, int64_t q2o);
+hipError_t launch_project(const void* m, void* w1, void* w2, int* status, int64_t in,
+                          int64_t nb1, int64_t nb2, int64_t q1i, int64_t q2o, int max_steps,
+                          bool bf16, hipStream_t s);
 
 }  // namespace monarch

@@ -6,16 +6,38 @@
 // With w1 = R [b1, b2, q1i] and w2 = L [b2, q2o, b1], slice (g, r) over (p, s)
 // is A[p][s] = M[p*b2 + g][r*q1i + s] and the Monarch matrix holds
 // L[g, p, r] * R[r, g, s] there, so the nearest Monarch matrix takes each
-// slice's nearest rank-one matrix sigma * u * vᵀ (top singular triple).
+// slice's nearest rank-one matrix sigma * u * vᵀ (top singular triple,
+// Eckart-Young). For a unit vector x the rank-one fit (A x) xᵀ leaves the
+// error ||A||² - xᵀ B x with B = AᵀA, so the fit is optimal exactly when x
+// maximises the Rayleigh quotient of B.
 //
-// One workgroup per slice: the slice is read once from HBM into LDS (fp32),
-// then a fixed number of power iterations v <- normalize(Aᵀ (A v)) run in
-// LDS, starting from the column sums of A. The result is split evenly,
-// L[g, :, r] = u * sqrt(sigma) (u = A v / sigma), R[r, g, :] = v * sqrt(sigma),
-// with the sign chosen so that R's entry of largest magnitude (the first one
-// on ties) is positive. Power iteration converges to the top pair at the rate
-// (sigma2 / sigma1)^2 per iteration; an exactly rank-one slice is fitted
-// after one iteration.
+// Method: Lanczos on B = AᵀA (B never formed: each step is u = A v, w = Aᵀ u)
+// with full reorthogonalisation (classical Gram-Schmidt, twice) against the
+// cycle's basis, in fp32. A cycle of up to KC steps (fewer on breakdown, when
+// the Krylov space is exhausted) gives the tridiagonal T = VᵀBV; its top
+// eigenvalue is bracketed by multisection on Sturm counts (64 lanes, fp32),
+// and its eigenvector s by two steps of inverse iteration with the shift just
+// above that bracket, where shift·I - T is positive definite, so the
+// tridiagonal solve needs no pivoting (fp64). The Ritz vector x = V s is
+// accepted when ||B x - theta x|| <= kProjectTol * theta (theta = xᵀBx),
+// else the next cycle restarts from x, until the caller's step budget is
+// spent; each slice reports the products it used, or 0 if it did not converge. Lanczos reaches the top
+// pair at a rate set by the square root of the spectral gap, and a cluster
+// of near-equal top values is harmless: any unit vector in its span is a fit
+// within the cluster's width of the optimum.
+//
+// One workgroup per slice, the slice zero-padded to QP x QP (QP = 16, 32, 64
+// or 128; padding changes no singular triple) and held in registers: the 256
+// threads form a 16 x 16 grid, thread (tr, tc) holding the E x E sub-block
+// (E = QP/16) at rows tr*E.., columns tc*E... Vectors indexed by columns are
+// held by column strips (thread (tr, tc) keeps entries tc*E..), replicated
+// over tr; a row strip is 16 adjacent lanes (sums over it are DPP row sums),
+// sums over the 16 row strips take shuffles within a wave and one exchange
+// through LDS between the 4 waves. The Lanczos basis lives in LDS; in the
+// Gram-Schmidt passes row strip tr handles the basis vectors j = tr (mod 16).
+// The result is split evenly, L[g, :, r] = A x / sqrt(sigma),
+// R[r, g, :] = sqrt(sigma) x, with the sign chosen so that R's entry of
+// largest magnitude (the first one on ties) is positive.
 #include <math.h>
 
 #include <type_traits>
@@ -26,42 +48,10 @@
 namespace monarch {
 namespace {
 
-constexpr int PT = 256;   // threads per workgroup
-
-__device__ __forceinline__ float wave_sum(float x) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  return x;
-}
-
-// sum over the workgroup, returned to every thread (red: 8 floats of LDS)
-__device__ float block_sum(float x, float* red) {
-  x = wave_sum(x);
-  const int w = threadIdx.x >> 6;
-  __syncthreads();
-  if ((threadIdx.x & 63) == 0) red[w] = x;
-  __syncthreads();
-  float s = 0.f;
-#pragma unroll
-  for (int i = 0; i < PT / 64; ++i) s += red[i];
-  return s;
-}
-
-// y[i] = sum_j A(i, j) x[j] for n rows of length len; A(i, j) = base[i*si + j*sj].
-// A group of `tpr` adjacent lanes (a power of two <= 64) shares one row.
-__device__ void matvec(const float* base, int si, int sj, int n, int len, const float* x,
-                       float* y, int tpr) {
-  const int part = threadIdx.x & (tpr - 1);
-  const int rows_per_pass = PT / tpr;
-  for (int i0 = 0; i0 < n; i0 += rows_per_pass) {
-    const int i = i0 + static_cast<int>(threadIdx.x) / tpr;
-    float acc = 0.f;
-    if (i < n)
-      for (int j = part; j < len; j += tpr) acc += base[i * si + j * sj] * x[j];
-    for (int o = tpr >> 1; o > 0; o >>= 1) acc += __shfl_xor(acc, o);
-    if (i < n && part == 0) y[i] = acc;
-  }
-}
+constexpr int PT = 256;                 // threads per workgroup (16 x 16 grid)
+constexpr int KC = 32;                  // Lanczos steps per cycle at most
+constexpr float kProjectTol = 1e-4f;    // accept x when ||B x - theta x|| <= tol * theta
+constexpr float kBreakdown = 1e-6f;     // end a cycle when beta <= this * max |alpha|
 
 // Sum over the 16 lanes of a DPP row, returned to each of them: swaps within
 // quads (lane ^ 1, lane ^ 2), then the two quads of each half (row_half_mirror)
@@ -79,152 +69,104 @@ __device__ __forceinline__ float row16_sum(float x) {
   return x;
 }
 
-__device__ __forceinline__ int lanes_per_row(int n) {
-  int t = 1;
-  while (t < 64 && t * 2 * n <= PT) t *= 2;
-  return t;
+// Number of eigenvalues below x of the symmetric tridiagonal matrix with
+// diagonal al[0..m) and off-diagonal be[0..m-1): the negative pivots of the
+// LDLᵀ factorisation of T - x I (Sturm sequence), in fp32.
+__device__ int sturm_count(const float* al, const float* be, int m, float x) {
+  int cnt = 0;
+  float d = 1.f;
+  for (int i = 0; i < m; ++i) {
+    d = (al[i] - x) - (i ? be[i - 1] * be[i - 1] * __builtin_amdgcn_rcpf(d) : 0.f);
+    if (d == 0.f) d = -1e-30f;
+    cnt += d < 0.f ? 1 : 0;
+  }
+  return cnt;
 }
 
-template <typename T>
-__global__ __launch_bounds__(PT) void project_slices_kernel(const T* __restrict__ M,
-                                                            T* __restrict__ W1,
-                                                            T* __restrict__ W2, int64_t in,
-                                                            int b1, int b2, int q1i, int q2o,
-                                                            int iters) {
-  extern __shared__ float sm[];
-  const int pitch = q1i + 1;             // odd pitch: column walks hit distinct banks
-  float* A = sm;                         // [q2o][pitch]
-  float* v = A + q2o * pitch;            // [q1i]
-  float* u = v + q1i;                    // [q2o]
-  float* red = u + q2o;                  // 8 floats
-  int* ired = reinterpret_cast<int*>(red + 8);   // 8 ints
-  const int g = blockIdx.x % b2, r = blockIdx.x / b2;
-  const int tid = threadIdx.x;
-
-  // the slice, A[p][s] = M[p*b2 + g][r*q1i + s]
-  constexpr int VEC = 16 / sizeof(T);
-  const T* src = M + static_cast<int64_t>(g) * in + static_cast<int64_t>(r) * q1i;
-  if (q1i % VEC == 0 && in % VEC == 0) {
-    const int per_row = q1i / VEC;
-    for (int e = tid; e < q2o * per_row; e += PT) {
-      const int p = e / per_row, s0 = (e % per_row) * VEC;
-      const u32x4 raw = *reinterpret_cast<const u32x4*>(src + static_cast<int64_t>(p) * b2 * in + s0);
-      const T* el = reinterpret_cast<const T*>(&raw);
-#pragma unroll
-      for (int j = 0; j < VEC; ++j) A[p * pitch + s0 + j] = Io<T>::load(el, j);
+// Top eigenvector of the m x m tridiagonal T (al, be in LDS) into s[0..m),
+// by wave 0 (all 64 lanes call it). The top eigenvalue is bracketed by
+// multisection: each round the 64 lanes take Sturm counts at 64 points of
+// (lo, hi), keeping count(lo) < m = count(hi). Lane 0 then runs two steps of
+// inverse iteration with the shift just above hi, where shift·I - T is
+// positive definite (LDLᵀ without pivoting, fp64; tw: 2*KC doubles of LDS).
+__device__ void tridiag_top(const float* al, const float* be, int m, float* s, double* tw,
+                            int lane) {
+  if (m == 1) {
+    if (lane == 0) s[0] = 1.f;
+    return;
+  }
+  float lo = al[0], hi = -3.0e38f;
+  for (int i = 0; i < m; ++i) {
+    lo = fmaxf(lo, al[i]);
+    const float rad = (i ? fabsf(be[i - 1]) : 0.f) + (i + 1 < m ? fabsf(be[i]) : 0.f);
+    hi = fmaxf(hi, al[i] + rad);
+  }
+  hi += fmaxf(fabsf(hi) * 1e-6f, 1e-30f);          // strictly above every eigenvalue
+  for (int round = 0; round < 12; ++round) {
+    const float x = lo + (hi - lo) * static_cast<float>(lane + 1) * (1.f / 65.f);
+    const bool above = sturm_count(al, be, m, x) >= m;
+    const uint64_t mask = __ballot(above);
+    float nlo, nhi;
+    if (mask) {
+      const int l = __builtin_ctzll(mask);
+      nhi = __shfl(x, l);
+      nlo = l > 0 ? __shfl(x, l - 1) : lo;
+    } else {
+      nlo = __shfl(x, 63);
+      nhi = hi;
     }
-  } else {
-    for (int e = tid; e < q2o * q1i; e += PT) {
-      const int p = e / q1i, s = e % q1i;
-      A[p * pitch + s] = Io<T>::load(src, static_cast<int64_t>(p) * b2 * in + s);
+    lo = nlo, hi = nhi;
+    if (hi - lo <= fabsf(hi) * 2.4e-7f) break;
+  }
+  if (lane == 0) {
+    const double sh = static_cast<double>(hi) + fmax(fabs(static_cast<double>(hi)) * 1e-6, 1e-30);
+    double* c = tw;          // elimination multipliers
+    double* y = tw + KC;     // right-hand side, then solution
+    for (int i = 0; i < m; ++i) y[i] = 1.0;
+    for (int it = 0; it < 2; ++it) {
+      // (sh I - T) y = rhs: diagonal sh - al[i] > 0, off-diagonal -be[i]
+      double den = sh - al[0];
+      c[0] = -static_cast<double>(be[0]) / den;
+      y[0] = y[0] / den;
+      for (int i = 1; i < m; ++i) {
+        const double e = -static_cast<double>(be[i - 1]);
+        den = (sh - al[i]) - e * c[i - 1];
+        c[i] = i + 1 < m ? -static_cast<double>(be[i]) / den : 0.0;
+        y[i] = (y[i] - e * y[i - 1]) / den;
+      }
+      for (int i = m - 2; i >= 0; --i) y[i] -= c[i] * y[i + 1];
+      double n2 = 0.0;
+      for (int i = 0; i < m; ++i) n2 += y[i] * y[i];
+      const double inv = n2 > 0.0 ? 1.0 / sqrt(n2) : 0.0;
+      for (int i = 0; i < m; ++i) y[i] *= inv;
     }
+    for (int i = 0; i < m; ++i) s[i] = static_cast<float>(y[i]);
   }
-  __syncthreads();
-
-  const int tpr_rows = lanes_per_row(q2o), tpr_cols = lanes_per_row(q1i);
-  // start: column sums of A (the unit vector e_0 if they vanish)
-  for (int s = tid; s < q1i; s += PT) {
-    float acc = 0.f;
-    for (int p = 0; p < q2o; ++p) acc += A[p * pitch + s];
-    v[s] = acc;
-  }
-  __syncthreads();
-  float part = 0.f;
-  for (int s = tid; s < q1i; s += PT) part += v[s] * v[s];
-  float nrm = block_sum(part, red);
-  if (!(nrm > 0.f)) {
-    for (int s = tid; s < q1i; s += PT) v[s] = s == 0 ? 1.f : 0.f;
-    nrm = 1.f;
-  }
-  float inv = 1.f / sqrtf(nrm);
-  for (int s = tid; s < q1i; s += PT) v[s] *= inv;
-  __syncthreads();
-
-  for (int it = 0; it < iters; ++it) {
-    matvec(A, pitch, 1, q2o, q1i, v, u, tpr_rows);   // u = A v
-    __syncthreads();
-    matvec(A, 1, pitch, q1i, q2o, u, v, tpr_cols);   // v = Aᵀ u
-    __syncthreads();
-    part = 0.f;
-    for (int s = tid; s < q1i; s += PT) part += v[s] * v[s];
-    nrm = block_sum(part, red);
-    inv = nrm > 0.f ? 1.f / sqrtf(nrm) : 0.f;
-    for (int s = tid; s < q1i; s += PT) v[s] *= inv;
-    __syncthreads();
-  }
-
-  // u = A v, sigma = |u|
-  matvec(A, pitch, 1, q2o, q1i, v, u, tpr_rows);
-  __syncthreads();
-  part = 0.f;
-  for (int p = tid; p < q2o; p += PT) part += u[p] * u[p];
-  const float sigma = sqrtf(block_sum(part, red));
-
-  // sign: R's entry of largest magnitude (first on ties) is positive
-  float best = -1.f;
-  int besti = 0x7fffffff;
-  for (int s = tid; s < q1i; s += PT) {
-    const float a = fabsf(v[s]);
-    if (a > best) best = a, besti = s;     // s increases: the first maximum wins
-  }
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    const float ob = __shfl_xor(best, o);
-    const int oi = __shfl_xor(besti, o);
-    if (ob > best || (ob == best && oi < besti)) best = ob, besti = oi;
-  }
-  __syncthreads();
-  if ((tid & 63) == 0) red[tid >> 6] = best, ired[tid >> 6] = besti;
-  __syncthreads();
-  best = red[0];
-  besti = ired[0];
-  for (int w = 1; w < PT / 64; ++w)
-    if (red[w] > best || (red[w] == best && ired[w] < besti)) best = red[w], besti = ired[w];
-  const float sgn = v[besti] < 0.f ? -1.f : 1.f;
-
-  const float rs = sqrtf(sigma);
-  const float lscale = sigma > 0.f ? sgn / rs : 0.f;
-  T* R = W1 + (static_cast<int64_t>(r) * b2 + g) * q1i;
-  for (int s = tid; s < q1i; s += PT) Io<T>::store(R, s, sgn * rs * v[s]);
-  T* L = W2 + static_cast<int64_t>(g) * q2o * b1 + r;
-  for (int p = tid; p < q2o; p += PT) Io<T>::store(L, static_cast<int64_t>(p) * b1, lscale * u[p]);
 }
 
-// Square Q x Q slices (Q = 32, 64 or 128): the slice stays in registers. The
-// 256 threads form a 16 x 16 grid; thread (tr, tc) holds the E x E sub-block
-// (E = Q/16) at rows tr*E.., columns tc*E... A row strip is 16 adjacent
-// lanes, a column strip is 16 lanes 16 apart (4 in each wave).
-//  * u = A v: products against v's E entries, summed over the row strip
-//    with shuffles; every thread of the strip then holds its E entries of u,
-//    which is all the next product needs.
-//  * v = Aᵀ u: products against u's E entries, summed over the wave's 4 row
-//    strips with shuffles and over the 4 waves through LDS (double-buffered,
-//    so one barrier per iteration); every thread then holds its E entries of
-//    v, and |v|² is a shuffle sum over the 16 column strips of its wave.
-// Same start, iteration count, normalisation and sign rule as the general
-// kernel. bf16 slices of 64 or 128 instead form B = AᵀA once with MFMAs
-// (the slice written transposed to LDS; exact products, fp32 sums) and take
-// each power step as one product with B: w = B v by row strips, v = B w by
-// column strips (B is symmetric), so an exchange round through LDS covers
-// two steps; the final A v reads the bf16 copy in LDS.
-template <typename T, int Qs>
-__global__ __launch_bounds__(PT) void project_square_kernel(const T* __restrict__ M,
-                                                            T* __restrict__ W1,
-                                                            T* __restrict__ W2, int64_t in,
-                                                            int b1, int b2, int iters) {
-  constexpr int E = Qs / 16;
-  __shared__ float part[2][4][Qs];   // per-wave column partials, double-buffered
-  __shared__ float red[4];
+template <typename T, int QP>
+__global__ __launch_bounds__(PT) void project_lanczos_kernel(
+    const T* __restrict__ M, T* __restrict__ W1, T* __restrict__ W2, int* __restrict__ status,
+    int64_t in, int b1, int b2, int q1i, int q2o, int max_steps) {
+  constexpr int E = QP / 16;
+  __shared__ float part[2][4][QP];        // per-wave column partial sums, double-buffered
+  __shared__ float vb[KC + 1][QP];        // the cycle's Lanczos basis
+  __shared__ float tal[KC], tbe[KC], ts[KC];
+  __shared__ double tw[2 * KC];
   const int g = blockIdx.x % b2, r = blockIdx.x / b2;
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int tr = tid >> 4, tc = tid & 15;
+
+  // the slice A[p][s] = M[p*b2 + g][r*q1i + s], zero-padded to QP x QP
   float a[E][E];
-  const T* src = M + static_cast<int64_t>(g) * in + static_cast<int64_t>(r) * Qs + tc * E;
-  constexpr int VEC = 16 / sizeof(T);                 // elements per 16-byte load
+  const T* src = M + static_cast<int64_t>(g) * in + static_cast<int64_t>(r) * q1i;
+  constexpr int VEC = 16 / sizeof(T);
+  const bool vec = q1i == QP && q2o == QP && E % VEC == 0 && in % VEC == 0;
 #pragma unroll
   for (int i = 0; i < E; ++i) {
-    const T* rowp = src + static_cast<int64_t>(tr * E + i) * b2 * in;
-    if constexpr (E % VEC == 0) {
+    const int p = tr * E + i;
+    const T* rowp = src + static_cast<int64_t>(p) * b2 * in + tc * E;
+    if (vec) {
 #pragma unroll
       for (int j0 = 0; j0 < E; j0 += VEC) {
         const u32x4 raw = *reinterpret_cast<const u32x4*>(rowp + j0);
@@ -234,42 +176,38 @@ __global__ __launch_bounds__(PT) void project_square_kernel(const T* __restrict_
       }
     } else {
 #pragma unroll
-      for (int j = 0; j < E; ++j) a[i][j] = Io<T>::load(rowp, j);
+      for (int j = 0; j < E; ++j)
+        a[i][j] = (p < q2o && tc * E + j < q1i) ? Io<T>::load(rowp, j) : 0.f;
     }
   }
 
-  // v[tc*E + j] = sum_p x[p] A[p][tc*E + j], x given by this thread's rows
   int buf = 0;
-  auto colprod = [&](const float (&x)[E], float (&v)[E]) {
+  // x: this thread's partial over its rows -> the sums over all rows, per column
+  auto colsum = [&](float(&x)[E]) {
 #pragma unroll
     for (int j = 0; j < E; ++j) {
-      float acc = 0.f;
-#pragma unroll
-      for (int i = 0; i < E; ++i) acc += a[i][j] * x[i];
-      acc += __shfl_xor(acc, 16);
-      acc += __shfl_xor(acc, 32);
-      v[j] = acc;
+      x[j] += __shfl_xor(x[j], 16);
+      x[j] += __shfl_xor(x[j], 32);
     }
     if (lane < 16) {
 #pragma unroll
-      for (int j = 0; j < E; ++j) part[buf][wv][tc * E + j] = v[j];
+      for (int j = 0; j < E; ++j) part[buf][wv][tc * E + j] = x[j];
     }
     __syncthreads();
 #pragma unroll
-    for (int j = 0; j < E; ++j)
-      v[j] = part[buf][0][tc * E + j] + part[buf][1][tc * E + j] + part[buf][2][tc * E + j] +
-             part[buf][3][tc * E + j];
+    for (int j = 0; j < E; ++j) {
+      const int c = tc * E + j;
+      x[j] = part[buf][0][c] + part[buf][1][c] + part[buf][2][c] + part[buf][3][c];
+    }
     buf ^= 1;
   };
-  // |v|² over all Q entries (the 16 column strips of this wave)
-  auto norm2 = [&](const float (&v)[E]) {
-    float p2 = 0.f;
+  auto dot = [&](const float(&x)[E], const float(&y)[E]) {
+    float p = 0.f;
 #pragma unroll
-    for (int j = 0; j < E; ++j) p2 += v[j] * v[j];
-    return row16_sum(p2);
+    for (int j = 0; j < E; ++j) p += x[j] * y[j];
+    return row16_sum(p);
   };
-  // u = A v for this thread's rows
-  auto rowprod = [&](const float (&v)[E], float (&u)[E]) {
+  auto rowprod = [&](const float(&v)[E], float(&u)[E]) {   // u = A v (this thread's rows)
 #pragma unroll
     for (int i = 0; i < E; ++i) {
       float acc = 0.f;
@@ -278,191 +216,150 @@ __global__ __launch_bounds__(PT) void project_square_kernel(const T* __restrict_
       u[i] = row16_sum(acc);
     }
   };
-
-  float v[E], u[E];
-  {
-    float ones[E];
-#pragma unroll
-    for (int i = 0; i < E; ++i) ones[i] = 1.f;
-    colprod(ones, v);                          // start: column sums
-    const float nrm = norm2(v);
-    if (nrm > 0.f) {
-      const float inv = 1.f / sqrtf(nrm);
-#pragma unroll
-      for (int j = 0; j < E; ++j) v[j] *= inv;
-    } else {
-#pragma unroll
-      for (int j = 0; j < E; ++j) v[j] = (tc * E + j == 0) ? 1.f : 0.f;
-    }
-  }
-  if constexpr (std::is_same<T, uint16_t>::value && Qs >= 64) {
-    // bf16: B = AᵀA once on MFMA (exact products, fp32 sums), then power
-    // steps v <- B v, two per exchange round. Wave w keeps rows
-    // [32w, 32w + 32) (Q = 128; [16w, 16w + 16) for 64) of B in the MFMA
-    // result layout: lane holds B[16mt + 4lh + e][16nt + l15]. v lives by
-    // columns (lane: v[16nt + l15]); w = B v by rows (lane: w[16mt + 4lh + e],
-    // a 16-lane row sum); v = B w (B symmetric) sums over the wave's rows
-    // with shuffles and over the waves through LDS.
-    constexpr int AP = Qs + 8;           // LDS pitch of Aᵀ (bf16)
-    constexpr int NT = Qs / 16, MTW = NT / 4;
-    __shared__ __attribute__((aligned(16))) uint16_t ast[Qs * AP];   // Aᵀ[col][row]
-    __shared__ float vs[Qs];
-    const int l15 = lane & 15, lh = lane >> 4;
-    // Aᵀ: column tc*E + j, rows tr*E .. tr*E + E - 1 (the bf16 values exactly)
+  auto colprod = [&](const float(&u)[E], float(&w)[E]) {   // w = Aᵀ u
 #pragma unroll
     for (int j = 0; j < E; ++j) {
-      uint32_t pk[E / 2];
+      float acc = 0.f;
 #pragma unroll
-      for (int i = 0; i < E / 2; ++i)
-        pk[i] = (__float_as_uint(a[2 * i][j]) >> 16) | (__float_as_uint(a[2 * i + 1][j]) & 0xffff0000u);
-      uint16_t* dst = &ast[(tc * E + j) * AP + tr * E];
-      if constexpr (E == 8)
-        *reinterpret_cast<u32x4*>(dst) = u32x4{pk[0], pk[1], pk[2], pk[3]};
-      else
-        *reinterpret_cast<u32x2*>(dst) = u32x2{pk[0], pk[1]};
+      for (int i = 0; i < E; ++i) acc += a[i][j] * u[i];
+      w[j] = acc;
     }
+    colsum(w);
+  };
+  auto normalize = [&](float(&x)[E]) {
+    const float n2 = dot(x, x);
+    const float inv = n2 > 0.f ? 1.f / sqrtf(n2) : 0.f;
+#pragma unroll
+    for (int j = 0; j < E; ++j) x[j] *= inv;
+    return n2 > 0.f;
+  };
+
+  // ||A||² and the start vector: the column sums of |A| (nonzero when A is)
+  float x[E];
+  float fro2;
+  {
+    float f = 0.f;
+#pragma unroll
+    for (int j = 0; j < E; ++j) {
+      float acc = 0.f;
+#pragma unroll
+      for (int i = 0; i < E; ++i) {
+        acc += fabsf(a[i][j]);
+        f += a[i][j] * a[i][j];
+      }
+      x[j] = acc;
+    }
+    colsum(x);
+    float fx[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) fx[j] = j ? 0.f : row16_sum(f);
+    colsum(fx);
+    fro2 = fx[0];
+  }
+  if (!normalize(x)) {
+#pragma unroll
+    for (int j = 0; j < E; ++j) x[j] = tc * E + j == 0 ? 1.f : 0.f;
+  }
+
+  int steps = 0, cycle = 0;
+  bool conv = false;
+  float theta = 0.f, u[E];
+  for (;;) {
+    // one Lanczos cycle from x
+    const int kmax = min(KC, max(max_steps - steps, 1));
+    float v[E];
+#pragma unroll
+    for (int j = 0; j < E; ++j) v[j] = x[j];
     if (tr == 0) {
 #pragma unroll
-      for (int j = 0; j < E; ++j) vs[tc * E + j] = v[j];
+      for (int j = 0; j < E; ++j) vb[0][tc * E + j] = v[j];
     }
-    __syncthreads();
-    f32x4 bacc[MTW][NT];
+    float amax = 0.f;
+    int m = 0;
+    for (int i = 0; i < kmax; ++i) {
+      float uu[E], w[E];
+      rowprod(v, uu);
+      colprod(uu, w);
+      const float al = dot(v, w);
+      amax = fmaxf(amax, fabsf(al));
+      // w -= V (Vᵀ w), twice; row strip tr takes basis vectors tr, tr + 16
 #pragma unroll
-    for (int mt = 0; mt < MTW; ++mt)
+      for (int pass = 0; pass < 2; ++pass) {
+        float corr[E];
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) bacc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < E; ++j) corr[j] = 0.f;
+        for (int jj = tr; jj <= i; jj += 16) {
+          const float* vj = &vb[jj][tc * E];
+          float p = 0.f;
 #pragma unroll
-    for (int ks = 0; ks < Qs / 32; ++ks) {
-      bf16x8 fa[MTW], fb[NT];
+          for (int j = 0; j < E; ++j) p += vj[j] * w[j];
+          const float c = row16_sum(p);
 #pragma unroll
-      for (int mt = 0; mt < MTW; ++mt)
-        fa[mt] = as_bf16x8(*reinterpret_cast<const u16x8*>(
-            &ast[(16 * (MTW * wv + mt) + l15) * AP + 32 * ks + 8 * lh]));
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt)
-        fb[nt] = as_bf16x8(*reinterpret_cast<const u16x8*>(&ast[(16 * nt + l15) * AP + 32 * ks + 8 * lh]));
-#pragma unroll
-      for (int mt = 0; mt < MTW; ++mt)
-#pragma unroll
-        for (int nt = 0; nt < NT; ++nt)
-          bacc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mt], fb[nt], bacc[mt][nt], 0, 0, 0);
-    }
-    float vc[NT], wr[MTW][4];
-#pragma unroll
-    for (int nt = 0; nt < NT; ++nt) vc[nt] = vs[16 * nt + l15];
-    auto rowprod_b = [&]() {   // wr = B vc, rows of this wave
-#pragma unroll
-      for (int mt = 0; mt < MTW; ++mt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          float acc = 0.f;
-#pragma unroll
-          for (int nt = 0; nt < NT; ++nt) acc += bacc[mt][nt][e] * vc[nt];
-          wr[mt][e] = row16_sum(acc);
+          for (int j = 0; j < E; ++j) corr[j] += c * vj[j];
         }
-    };
-    auto colprod_b = [&]() {   // vc = B wr (B symmetric), then normalised
+        colsum(corr);
 #pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        float acc = 0.f;
-#pragma unroll
-        for (int mt = 0; mt < MTW; ++mt)
-#pragma unroll
-          for (int e = 0; e < 4; ++e) acc += bacc[mt][nt][e] * wr[mt][e];
-        acc += __shfl_xor(acc, 16);
-        acc += __shfl_xor(acc, 32);
-        vc[nt] = acc;
+        for (int j = 0; j < E; ++j) w[j] -= corr[j];
       }
-      if (lane < 16) {
+      const float be = sqrtf(dot(w, w));
+      if (tid == 0) tal[i] = al, tbe[i] = be;
+      m = i + 1;
+      ++steps;
+      if (i + 1 == kmax || !(be > kBreakdown * amax)) break;
+      const float inv = 1.f / be;
 #pragma unroll
-        for (int nt = 0; nt < NT; ++nt) part[buf][wv][16 * nt + l15] = vc[nt];
+      for (int j = 0; j < E; ++j) v[j] = w[j] * inv;
+      if (tr == 0) {
+#pragma unroll
+        for (int j = 0; j < E; ++j) vb[i + 1][tc * E + j] = v[j];
       }
-      __syncthreads();
-      float p2 = 0.f;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) {
-        const int c = 16 * nt + l15;
-        vc[nt] = part[buf][0][c] + part[buf][1][c] + part[buf][2][c] + part[buf][3][c];
-        p2 += vc[nt] * vc[nt];
-      }
-      buf ^= 1;
-      const float nrm = row16_sum(p2);
-      const float inv = nrm > 0.f ? 1.f / sqrtf(nrm) : 0.f;
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) vc[nt] *= inv;
-    };
-    int left = iters;
-    for (; left >= 2; left -= 2) {
-      rowprod_b();   // w = B v (not normalised: one step's growth)
-      colprod_b();   // v = B w, normalised
     }
-    if (left == 1) {
-      // one step: v by rows from the lanes that hold it by columns
-#pragma unroll
-      for (int mt = 0; mt < MTW; ++mt)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) wr[mt][e] = __shfl(vc[MTW * wv + mt], (lane & 48) | (4 * lh + e));
-      colprod_b();
-    }
-    __syncthreads();   // every lane has read vs
-    if (wv == 0 && lane < 16) {
-#pragma unroll
-      for (int nt = 0; nt < NT; ++nt) vs[16 * nt + l15] = vc[nt];
-    }
+    __syncthreads();   // T complete
+    if (wv == 0) tridiag_top(tal, tbe, m, ts, tw, lane);
     __syncthreads();
+    // Ritz vector x = V s
+    {
+      float xr[E];
 #pragma unroll
-    for (int j = 0; j < E; ++j) v[j] = vs[tc * E + j];
-    // u = A v from the bf16 copy (A's registers are free after the start):
-    // A[tr*E + i][tc*E + j] = Aᵀ[tc*E + j][tr*E + i]
-    float pu[E];
+      for (int j = 0; j < E; ++j) xr[j] = 0.f;
+      for (int jj = tr; jj < m; jj += 16) {
+        const float sj = ts[jj];
 #pragma unroll
-    for (int i = 0; i < E; ++i) pu[i] = 0.f;
-#pragma unroll
-    for (int j = 0; j < E; ++j) {
-      const uint16_t* col = &ast[(tc * E + j) * AP + tr * E];
-      uint32_t w32[E / 2];
-      if constexpr (E == 8) {
-        const u32x4 q = *reinterpret_cast<const u32x4*>(col);
-        w32[0] = q[0], w32[1] = q[1], w32[2] = q[2], w32[3] = q[3];
-      } else {
-        const u32x2 q = *reinterpret_cast<const u32x2*>(col);
-        w32[0] = q[0], w32[1] = q[1];
+        for (int j = 0; j < E; ++j) xr[j] += sj * vb[jj][tc * E + j];
       }
+      colsum(xr);
+      if (normalize(xr)) {
 #pragma unroll
-      for (int i = 0; i < E / 2; ++i) {
-        pu[2 * i] += __uint_as_float(w32[i] << 16) * v[j];
-        pu[2 * i + 1] += __uint_as_float(w32[i] & 0xffff0000u) * v[j];
+        for (int j = 0; j < E; ++j) x[j] = xr[j];
       }
     }
+    // accept x when B x is theta x to the tolerance
+    float w[E], res[E];
+    rowprod(x, u);
+    colprod(u, w);
+    theta = dot(x, w);
 #pragma unroll
-    for (int i = 0; i < E; ++i) u[i] = row16_sum(pu[i]);
-  } else {
-    for (int it = 0; it < iters; ++it) {
-      rowprod(v, u);                             // u = A v
-      colprod(u, v);                             // v = Aᵀ u
-      const float nrm = norm2(v);
-      const float inv = nrm > 0.f ? 1.f / sqrtf(nrm) : 0.f;
+    for (int j = 0; j < E; ++j) res[j] = w[j] - theta * x[j];
+    const float rho = sqrtf(dot(res, res));
+    ++steps;
+    ++cycle;
+    conv = theta > 0.f ? rho <= kProjectTol * theta : fro2 == 0.f;
+    if (conv || steps >= max_steps) break;
+    if (!(theta > 0.f)) {
+      // x fell in A's null space (only for contrived inputs): next unit vector
 #pragma unroll
-      for (int j = 0; j < E; ++j) v[j] *= inv;
+      for (int j = 0; j < E; ++j) x[j] = tc * E + j == cycle % q1i ? 1.f : 0.f;
     }
-    rowprod(v, u);
+    __syncthreads();   // every thread is done with vb and ts before the next cycle
   }
-  // sigma = |u|: this wave's 4 row strips, then the 4 waves
-  float p2 = 0.f;
-#pragma unroll
-  for (int i = 0; i < E; ++i) p2 += u[i] * u[i];
-  p2 += __shfl_xor(p2, 16);
-  p2 += __shfl_xor(p2, 32);
-  if (lane == 0) red[wv] = p2;
-  __syncthreads();
-  const float sigma = sqrtf(red[0] + red[1] + red[2] + red[3]);
 
-  // sign: the entry of v of largest magnitude (first on ties) is positive
+  const float sigma = theta > 0.f ? sqrtf(theta) : 0.f;   // ||A x||
+  // sign: the entry of x of largest magnitude (first on ties) is positive
   float best = -1.f;
   int besti = 0x7fffffff;
 #pragma unroll
   for (int j = 0; j < E; ++j) {
-    const float av = fabsf(v[j]);
+    const float av = fabsf(x[j]);
     if (av > best) best = av, besti = tc * E + j;
   }
 #pragma unroll
@@ -471,77 +368,61 @@ __global__ __launch_bounds__(PT) void project_square_kernel(const T* __restrict_
     const int oi = __shfl_xor(besti, o);
     if (ob > best || (ob == best && oi < besti)) best = ob, besti = oi;
   }
-  float vb = 0.f;
+  float vbest = 0.f;
 #pragma unroll
-  for (int j = 0; j < E; ++j) vb = (tc * E + j == besti) ? v[j] : vb;
-#pragma unroll
-  for (int o = 1; o < 16; o <<= 1) {
-    const float ov = __shfl_xor(vb, o);
-    vb = (ov != 0.f) ? ov : vb;   // only the owner's lane holds it (v has besti's value there)
-  }
-  const float sgn = vb < 0.f ? -1.f : 1.f;
+  for (int j = 0; j < E; ++j) vbest = tc * E + j == besti ? x[j] : vbest;
+  vbest = row16_sum(vbest);   // only the owning lane contributes
+  const float sgn = vbest < 0.f ? -1.f : 1.f;
   const float rs = sqrtf(sigma);
   const float lscale = sigma > 0.f ? sgn / rs : 0.f;
   if (tr == 0) {
-    T* R = W1 + (static_cast<int64_t>(r) * b2 + g) * Qs + tc * E;
+    T* R = W1 + (static_cast<int64_t>(r) * b2 + g) * q1i;
 #pragma unroll
-    for (int j = 0; j < E; ++j) Io<T>::store(R, j, sgn * rs * v[j]);
+    for (int j = 0; j < E; ++j)
+      if (tc * E + j < q1i) Io<T>::store(R, tc * E + j, sgn * rs * x[j]);
   }
   if (tc == 0) {
-    T* L = W2 + static_cast<int64_t>(g) * Qs * b1 + r;
+    T* L = W2 + static_cast<int64_t>(g) * q2o * b1 + r;
 #pragma unroll
-    for (int i = 0; i < E; ++i) Io<T>::store(L, static_cast<int64_t>(tr * E + i) * b1, lscale * u[i]);
+    for (int i = 0; i < E; ++i)
+      if (tr * E + i < q2o) Io<T>::store(L, static_cast<int64_t>(tr * E + i) * b1, lscale * u[i]);
   }
+  if (status && tid == 0) status[blockIdx.x] = conv ? steps : 0;
 }
 
 }  // namespace
 
-size_t project_lds_bytes(int64_t q1i, int64_t q2o) {
-  return static_cast<size_t>(q2o * (q1i + 1) + q1i + q2o + 16) * sizeof(float);
+int project_pad(int64_t q1i, int64_t q2o) {
+  const int64_t q = q1i > q2o ? q1i : q2o;
+  if (q <= 16) return 16;
+  if (q <= 32) return 32;
+  if (q <= 64) return 64;
+  if (q <= 128) return 128;
+  return 0;
 }
 
-hipError_t launch_project(const void* m, void* w1, void* w2, int64_t in, int64_t nb1,
-                          int64_t nb2, int64_t q1i, int64_t q2o, int iters, bool bf16,
-                          hipStream_t s) {
-  const size_t lds = project_lds_bytes(q1i, q2o);
+hipError_t launch_project(const void* m, void* w1, void* w2, int* status, int64_t in,
+                          int64_t nb1, int64_t nb2, int64_t q1i, int64_t q2o, int max_steps,
+                          bool bf16, hipStream_t s) {
   const dim3 grid(static_cast<unsigned>(nb1 * nb2)), block(PT);
-  if (q1i == q2o && (q1i == 32 || q1i == 64 || q1i == 128)) {
-    const int b1 = static_cast<int>(nb1), b2 = static_cast<int>(nb2);
-#define MONARCH_SQ_PROJECT(TT, QQ)                                                          \
-  hipLaunchKernelGGL((project_square_kernel<TT, QQ>), grid, block, 0, s,                     \
-                     static_cast<const TT*>(m), static_cast<TT*>(w1), static_cast<TT*>(w2), \
-                     in, b1, b2, iters)
-    if (bf16) {
-      if (q1i == 32) MONARCH_SQ_PROJECT(uint16_t, 32);
-      else if (q1i == 64) MONARCH_SQ_PROJECT(uint16_t, 64);
-      else MONARCH_SQ_PROJECT(uint16_t, 128);
-    } else {
-      if (q1i == 32) MONARCH_SQ_PROJECT(float, 32);
-      else if (q1i == 64) MONARCH_SQ_PROJECT(float, 64);
-      else MONARCH_SQ_PROJECT(float, 128);
-    }
-#undef MONARCH_SQ_PROJECT
-    return hipGetLastError();
+  const int b1 = static_cast<int>(nb1), b2 = static_cast<int>(nb2);
+  const int qi = static_cast<int>(q1i), qo = static_cast<int>(q2o);
+#define MONARCH_PROJECT(TT, QQ)                                                                 \
+  hipLaunchKernelGGL((project_lanczos_kernel<TT, QQ>), grid, block, 0, s,                        \
+                     static_cast<const TT*>(m), static_cast<TT*>(w1), static_cast<TT*>(w2),     \
+                     status, in, b1, b2, qi, qo, max_steps)
+  switch (project_pad(q1i, q2o) * (bf16 ? -1 : 1)) {
+    case 16: MONARCH_PROJECT(float, 16); break;
+    case 32: MONARCH_PROJECT(float, 32); break;
+    case 64: MONARCH_PROJECT(float, 64); break;
+    case 128: MONARCH_PROJECT(float, 128); break;
+    case -16: MONARCH_PROJECT(uint16_t, 16); break;
+    case -32: MONARCH_PROJECT(uint16_t, 32); break;
+    case -64: MONARCH_PROJECT(uint16_t, 64); break;
+    case -128: MONARCH_PROJECT(uint16_t, 128); break;
+    default: return hipErrorInvalidValue;
   }
-  if (bf16) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(project_slices_kernel<uint16_t>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(project_slices_kernel<uint16_t>, grid, block, lds, s,
-                       static_cast<const uint16_t*>(m), static_cast<uint16_t*>(w1),
-                       static_cast<uint16_t*>(w2), in, static_cast<int>(nb1),
-                       static_cast<int>(nb2), static_cast<int>(q1i), static_cast<int>(q2o), iters);
-  } else {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(project_slices_kernel<float>),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       static_cast<int>(lds));
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(project_slices_kernel<float>, grid, block, lds, s,
-                       static_cast<const float*>(m), static_cast<float*>(w1),
-                       static_cast<float*>(w2), in, static_cast<int>(nb1), static_cast<int>(nb2),
-                       static_cast<int>(q1i), static_cast<int>(q2o), iters);
-  }
+#undef MONARCH_PROJECT
   return hipGetLastError();
 }
 

@@ -95,9 +95,12 @@ def monarch_backward(dy, x, w1, w2, z, y=None, act: int = B.ACT_NONE, stream=Non
     return dx, dw1, dw2
 
 
-def monarch_project(m, nblocks1: int, nblocks2: int, iters: int = 32, stream=None):
+def monarch_project(m, nblocks1: int, nblocks2: int, max_steps: int = 256, stream=None,
+                    with_status: bool = False):
     """Nearest Monarch factors (w1 [b1, b2, in/b1], w2 [b2, out/b2, b1]) of a
-    dense [out, in] matrix; needs out = nblocks1 * nblocks2."""
+    dense [out, in] matrix; needs out = nblocks1 * nblocks2. With with_status,
+    also returns the int32 [b1 * b2] per-slice status (element r*b2 + g for
+    slice (g, r)): the products with AᵀA it used when converged, else 0."""
     _check(m)
     if m.dim() != 2:
         raise ValueError("m must be [out, in]")
@@ -106,8 +109,10 @@ def monarch_project(m, nblocks1: int, nblocks2: int, iters: int = 32, stream=Non
         raise ValueError("block counts must divide the matrix dimensions")
     w1 = torch.empty((nblocks1, nblocks2, fi // nblocks1), dtype=m.dtype, device=m.device)
     w2 = torch.empty((nblocks2, fo // nblocks2, nblocks1), dtype=m.dtype, device=m.device)
-    B.monarch_project(m, w1, w2, fi, fo, nblocks1, nblocks2, dtype_code(m), iters, stream)
-    return w1, w2
+    conv = torch.empty((nblocks1 * nblocks2,), dtype=torch.int32, device=m.device)
+    B.monarch_project(m, w1, w2, fi, fo, nblocks1, nblocks2, dtype_code(m), max_steps, conv,
+                      stream)
+    return (w1, w2, conv) if with_status else (w1, w2)
 
 
 class MonarchLinearFunction(torch.autograd.Function):

@@ -160,17 +160,19 @@ def test_path_selection():
         assert M.monarch_describe(0, *args)[0].startswith("generic")
 
 
-def proj(m=A, w1=A2, w2=A2, fi=16, fo=16, nb1=4, nb2=4, dt=B.F32, iters=8):
+def proj(m=A, w1=A2, w2=A2, fi=16, fo=16, nb1=4, nb2=4, dt=B.F32, steps=8, conv=None):
     lib = M.load_library()
-    return lib.monarch_project(m, w1, w2, fi, fo, nb1, nb2, dt, iters, None)
+    return lib.monarch_project(m, w1, w2, fi, fo, nb1, nb2, dt, steps, conv, None)
 
 
 @pytest.mark.parametrize("kw", [
     dict(fo=32),                      # out != nb1 * nb2
     dict(fi=18),                      # in % nb1
     dict(nb1=0), dict(fi=0),
-    dict(iters=0), dict(iters=5000),
-    dict(fi=256 * 512, fo=16, nb1=4, nb2=4),   # slice 4 x 32768 does not fit in LDS
+    dict(steps=0), dict(steps=5000),
+    dict(fi=256 * 512, fo=16, nb1=4, nb2=4),   # slice 4 x 32768: a side beyond 128
+    dict(fi=4 * 129, fo=16, nb1=4, nb2=4),     # 4 x 129
+    dict(fi=516, fo=516, nb1=129, nb2=4),      # slices 129 x 4
 ])
 def test_project_bad_shapes(kw):
     assert proj(**kw) == B.MONARCH_ERR_SHAPE
@@ -181,6 +183,7 @@ def test_project_bad_dtype_null_align():
     for name in ("m", "w1", "w2"):
         assert proj(**{name: None}) == B.MONARCH_ERR_NULL
         assert proj(**{name: MIS}) == B.MONARCH_ERR_ALIGN
+    assert proj(conv=A2 + 2) == B.MONARCH_ERR_ALIGN   # int32 status array
 
 
 # ---------------------------------------------------------------------------
