@@ -12,7 +12,10 @@ import ctypes
 import os
 from typing import Optional, Sequence
 
-LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libmonarch.so")
+# the in-tree build; MONARCH_LIBRARY may name another build of the same
+# sources (the host-sanitizer build of build_lib --sanitize)
+LIB_PATH = os.environ.get("MONARCH_LIBRARY") or os.path.join(
+    os.path.dirname(os.path.abspath(__file__)), "libmonarch.so")
 
 MONARCH_OK = 0
 MONARCH_ERR_NULL = -1

@@ -99,7 +99,7 @@ int make_dyad(int64_t in, int64_t out, int64_t nb, int64_t batch, int dtype, Dya
 int dyad_plan_fwd(const DyadProblem& dp, const DyadBuffers& b, SeqStep* steps) {
   if (dp.batch == 0) return 0;
   void* xp = b.ws;   // the forward's workspace: Xp, then term B's block-major rows
-  void* yp = static_cast<char*>(b.ws) + dp.ws_fwd_yp;
+  void* yp = byte_at(b.ws, dp.ws_fwd_yp);
   gather(steps[0], "dyad_gather_x", b.x, xp, dp.batch, dp.qi, dp.nb);
   steps[1].kind = SEQ_GEMM;
   steps[1].name = "dyad_term_b_fwd";
@@ -122,11 +122,10 @@ int dyad_plan_bwd(const DyadProblem& dp, const DyadBuffers& b, SeqStep* steps) {
     steps[1].zero_ptr = b.dwb, steps[1].zero_bytes = wbytes;
     return 2;
   }
-  char* ws = static_cast<char*>(b.ws);
-  float* pa = reinterpret_cast<float*>(ws + dp.ws_pa);
-  float* pb = reinterpret_cast<float*>(ws + dp.ws_pb);
-  void* xp = ws + dp.ws_xp;
-  void* dyp = ws + dp.ws_dyp;
+  float* pa = reinterpret_cast<float*>(byte_at(b.ws, dp.ws_pa));
+  float* pb = reinterpret_cast<float*>(byte_at(b.ws, dp.ws_pb));
+  void* xp = byte_at(b.ws, dp.ws_xp);
+  void* dyp = byte_at(b.ws, dp.ws_dyp);
   int n = 0;
   gather(steps[n++], "dyad_gather_x", b.x, xp, dp.batch, dp.qi, dp.nb);
   gather(steps[n++], "dyad_gather_dy", b.dy, dyp, dp.batch, dp.qo, dp.nb);

@@ -168,7 +168,7 @@ int hyper_plan_fwd(const HyperProblem& hp, const HyperBuffers& b, SeqStep* steps
   const int k = hp.k;
   const int64_t BN = hp.batch * hp.N;
   // saved slot j: the input of round j in L_j (slot 0 = x)
-  auto slot = [&](int sidx) { return static_cast<char*>(b.saved) + sidx * BN * hp.esize; };
+  auto slot = [&](int sidx) { return byte_at(b.saved, sidx * BN * hp.esize); };
   int ns = 0;
   const bool strided = strided_round0(hp);
   if (k > 1 && !strided) {
@@ -226,16 +226,17 @@ int hyper_plan_bwd(const HyperProblem& hp, const HyperBuffers& b, SeqStep* steps
     return ns;
   }
   const int64_t BN = hp.batch * hp.N;
-  char* ws = static_cast<char*>(b.ws);
-  const char* saved = static_cast<const char*>(b.saved_in);
+  void* ws = b.ws;
   // input of round j in L_j: the saved copies (slot j), or x itself when the
   // lattice has one dimension
-  auto input = [&](int j) -> const void* { return k > 1 ? saved + j * BN * hp.esize : b.x; };
+  auto input = [&](int j) -> const void* {
+    return k > 1 ? byte_at(b.saved_in, j * BN * hp.esize) : b.x;
+  };
   // g_{j+1} (gradient w.r.t. round j's output, in L_j) is dy for the last
   // round, else buffer 1; round j's data gradient goes to buffer 0 (in L_j)
   // and is swapped into buffer 1 (in L_{j-1})
-  void* g0 = ws + hp.ws_g[0];
-  void* g1 = ws + hp.ws_g[1];
+  void* g0 = byte_at(ws, hp.ws_g[0]);
+  void* g1 = byte_at(ws, hp.ws_g[1]);
   for (int j = k - 1; j >= 0; --j) {
     const int64_t n = hp.dims[j], nf = hp.N / n;
     const void* g = j == k - 1 ? b.dy : g1;
@@ -245,7 +246,7 @@ int hyper_plan_bwd(const HyperProblem& hp, const HyperBuffers& b, SeqStep* steps
       st.kind = SEQ_FIBER_WGRAD;
       st.name = "hyper_round_bwd_weight";
       st.t_in = g, st.f_in2 = input(j);
-      st.f_part = reinterpret_cast<float*>(ws + hp.ws_part[j]);
+      st.f_part = reinterpret_cast<float*>(byte_at(ws, hp.ws_part[j]));
       st.t_rows = hp.batch, st.f_N = hp.N, st.f_n = n, st.f_chunk = hp.chunk[j];
     } else {
       SeqStep& st = steps[ns++];
@@ -256,14 +257,14 @@ int hyper_plan_bwd(const HyperProblem& hp, const HyperBuffers& b, SeqStep* steps
       a.a_sb = n, a.a_si = 1, a.a_sk = hp.N;
       a.B = input(j);
       a.b_sb = n, a.b_sk = hp.N, a.b_sj = 1;
-      a.partial = reinterpret_cast<float*>(ws + hp.ws_part[j]);
+      a.partial = reinterpret_cast<float*>(byte_at(ws, hp.ws_part[j]));
       a.splits = hp.splits[j], a.k_chunk = hp.chunk[j];
       a.M = n, a.N = n, a.K = hp.batch, a.nblk = nf;
     }
     void* gout = k > 1 ? g0 : b.dx;                // L_j
     if (fib) {
       // per-fiber transposed weights, then the fiber products with them
-      void* wt = ws + hp.ws_wt;
+      void* wt = byte_at(ws, hp.ws_wt);
       SeqStep& sw = steps[ns++];
       sw.kind = SEQ_SWAP;
       sw.name = "hyper_weight_transpose";
@@ -313,7 +314,7 @@ int hyper_plan_bwd(const HyperProblem& hp, const HyperBuffers& b, SeqStep* steps
     st.name = "reduce_dw";
     for (int i = 0; i < 3 && j0 + i < k; ++i) {
       const int j = j0 + i;
-      st.r[i].partial = reinterpret_cast<const float*>(ws + hp.ws_part[j]);
+      st.r[i].partial = reinterpret_cast<const float*>(byte_at(ws, hp.ws_part[j]));
       st.r[i].out = b.dw[j];
       st.r[i].n = hp.N * hp.dims[j];
       st.r[i].splits = hp.splits[j];

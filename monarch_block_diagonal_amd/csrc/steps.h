@@ -11,6 +11,16 @@
 
 namespace monarch {
 
+// base + off bytes, or null when base is null: the planners also run with
+// null buffers (to name a call's kernels), and arithmetic on a null pointer is
+// undefined.
+inline char* byte_at(void* base, size_t off) {
+  return base ? static_cast<char*>(base) + off : nullptr;
+}
+inline const char* byte_at(const void* base, size_t off) {
+  return base ? static_cast<const char*>(base) + off : nullptr;
+}
+
 enum SeqKind {
   SEQ_GEMM, SEQ_REDUCE, SEQ_ZERO, SEQ_SWAP, SEQ_FIBER, SEQ_FIBER_WGRAD, SEQ_FIBER_SWAP,
   SEQ_FIBER_STRIDED
