@@ -306,6 +306,16 @@ int monarch_dyad_bwd(const void* dy, const void* x, const void* w_a, const void*
 int monarch_dyad_describe(int direction, int64_t in_features, int64_t out_features,
                           int64_t nblocks, int64_t batch, int dtype, char* buf, size_t buf_len);
 
+/* ---------------------------------------------------------------------------
+ * Stream copy: copies `bytes` bytes from src to dst (device buffers, 16-byte
+ * aligned, not overlapping), reading and writing each byte once with 16-byte
+ * non-temporal accesses. Not part of the Monarch operator: it is the
+ * reference for the HBM rooflines, the rate a kernel that streams its data
+ * through HBM can reach on this memory system (2 * bytes moved per call).
+ * bytes == 0 launches nothing. Errors: NULL -> MONARCH_ERR_NULL,
+ * misaligned -> MONARCH_ERR_ALIGN. */
+int monarch_stream_copy(const void* src, void* dst, size_t bytes, void* stream);
+
 /* Static text for a status code; for MONARCH_ERR_HIP the last HIP error
  * message recorded on the calling thread. Never NULL. */
 const char* monarch_status_string(int status);

@@ -15,4 +15,5 @@ from .binding import (  # noqa: F401
     monarch_hyper_fwd, monarch_hyper_bwd_workspace_bytes, monarch_hyper_bwd,
     monarch_hyper_describe, monarch_dyad_fwd_workspace_bytes, monarch_dyad_fwd,
     monarch_dyad_bwd_workspace_bytes, monarch_dyad_bwd, monarch_dyad_describe,
+    monarch_bwd_noalloc, monarch_stream_copy,
 )

@@ -41,7 +41,7 @@ EXPORTED = (
     "monarch_hyper_fwd", "monarch_hyper_bwd_workspace_bytes", "monarch_hyper_bwd",
     "monarch_hyper_describe", "monarch_dyad_fwd_workspace_bytes", "monarch_dyad_fwd",
     "monarch_dyad_bwd_workspace_bytes",
-    "monarch_dyad_bwd", "monarch_dyad_describe", "monarch_bwd_noalloc",
+    "monarch_dyad_bwd", "monarch_dyad_describe", "monarch_bwd_noalloc", "monarch_stream_copy",
 )
 
 _lib = None
@@ -78,6 +78,8 @@ def load_library():
     lib.monarch_bwd_traced.restype = c_int
     lib.monarch_bwd_noalloc.argtypes = [vp] * 9 + shape + [c_int, c_int, vp]
     lib.monarch_bwd_noalloc.restype = c_int
+    lib.monarch_stream_copy.argtypes = [vp, vp, sz, vp]
+    lib.monarch_stream_copy.restype = c_int
     lib.monarch_describe.argtypes = [c_int] + shape + [c_int, c_int, ctypes.c_char_p, sz]
     lib.monarch_describe.restype = c_int
     lib.monarch_status_string.argtypes = [c_int]
@@ -208,6 +210,11 @@ def monarch_bwd_noalloc(dy, x, w1, w2, z, y, dx, dw1, dw2, in_features, out_feat
     _check(lib.monarch_bwd_noalloc(_ptr(dy), _ptr(x), _ptr(w1), _ptr(w2), _ptr(z), _ptr(y),
                                    _ptr(dx), _ptr(dw1), _ptr(dw2), in_features, out_features,
                                    nblocks1, nblocks2, batch, dtype, act, _stream(stream)))
+
+
+def monarch_stream_copy(src, dst, nbytes, stream=None) -> None:
+    """Device copy of nbytes from src to dst (the HBM roofline reference)."""
+    _check(load_library().monarch_stream_copy(_ptr(src), _ptr(dst), nbytes, _stream(stream)))
 
 
 def monarch_project(m, w1, w2, in_features, out_features, nblocks1, nblocks2, dtype,

@@ -463,6 +463,13 @@ int monarch_dyad_describe(int direction, int64_t in_features, int64_t out_featur
   return write_names(names, n, buf, buf_len);
 }
 
+int monarch_stream_copy(const void* src, void* dst, size_t bytes, void* stream) {
+  if (bytes == 0) return MONARCH_OK;
+  if (!src || !dst) return MONARCH_ERR_NULL;
+  if (misaligned(src) || misaligned(dst)) return MONARCH_ERR_ALIGN;
+  return record_hip(launch_stream_copy(src, dst, bytes, static_cast<hipStream_t>(stream)));
+}
+
 const char* monarch_status_string(int status) {
   switch (status) {
     case MONARCH_OK: return "ok";

@@ -1,0 +1,53 @@
+// Stream copy: the measured-bandwidth reference for the HBM rooflines.
+//
+// A plain device-to-device copy moves every byte once each way, so its rate
+// is the most a kernel that streams its operands through HBM can reach on
+// this memory system. Each thread issues four 16-byte non-temporal loads
+// (256 threads apart, so a wave's access is contiguous) before its four
+// stores; the grid strides over the buffer.
+#include "common.h"
+#include "kernels.h"
+
+namespace monarch {
+namespace {
+
+constexpr int CT = 256;   // threads per workgroup
+constexpr int CU = 4;     // 16-byte pieces in flight per thread
+
+__global__ __launch_bounds__(CT) void stream_copy_kernel(const u32x4* __restrict__ src,
+                                                         u32x4* __restrict__ dst, int64_t n16,
+                                                         const uint8_t* __restrict__ src_tail,
+                                                         uint8_t* __restrict__ dst_tail,
+                                                         int tail) {
+  const int64_t step = static_cast<int64_t>(gridDim.x) * CT * CU;
+  for (int64_t base = static_cast<int64_t>(blockIdx.x) * CT * CU + threadIdx.x; base < n16;
+       base += step) {
+    u32x4 v[CU];
+#pragma unroll
+    for (int k = 0; k < CU; ++k)
+      if (base + k * CT < n16) v[k] = __builtin_nontemporal_load(src + base + k * CT);
+#pragma unroll
+    for (int k = 0; k < CU; ++k)
+      if (base + k * CT < n16) __builtin_nontemporal_store(v[k], dst + base + k * CT);
+  }
+  if (blockIdx.x == 0 && static_cast<int>(threadIdx.x) < tail)
+    dst_tail[threadIdx.x] = src_tail[threadIdx.x];
+}
+
+}  // namespace
+
+hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {
+  const int64_t n16 = static_cast<int64_t>(bytes / 16);
+  const int tail = static_cast<int>(bytes % 16);
+  int64_t grid = (n16 + CT * CU - 1) / (CT * CU);
+  if (grid > 2048) grid = 2048;   // 8 workgroups per CU
+  if (grid < 1) grid = 1;
+  const size_t done = static_cast<size_t>(n16) * 16;
+  hipLaunchKernelGGL(stream_copy_kernel, dim3(static_cast<unsigned>(grid)), dim3(CT), 0, s,
+                     static_cast<const u32x4*>(src), static_cast<u32x4*>(dst), n16,
+                     static_cast<const uint8_t*>(src) + done, static_cast<uint8_t*>(dst) + done,
+                     tail);
+  return hipGetLastError();
+}
+
+}  // namespace monarch

@@ -130,6 +130,10 @@ struct ReduceArgs {
 hipError_t launch_reduce_partials(const ReduceArgs& a, const ReduceArgs& b, const ReduceArgs& c,
                                   bool bf16, hipStream_t s);
 
+// Plain device copy of `bytes` bytes (16-byte aligned src and dst): the
+// measured-bandwidth reference of the HBM rooflines.
+hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s);
+
 // Dense -> Monarch projection: one workgroup per (g, r) slice of M
 // [out = nb1*nb2, in]; writes w1 [nb1, nb2, q1i], w2 [nb2, q2o, nb1] and, when
 // status is set, status[r*nb2 + g] = the products with AᵀA a converged slice

@@ -378,3 +378,11 @@ def test_noalloc_scratch_size_matches_header():
     for args in ((1024, 1024, 32, 32, 4096, B.BF16), (10000, 1024, 4, 4, 10000, B.F32),
                  (1024, 512, 16, 16, 10000, B.F32)):
         assert M.monarch_bwd_workspace_bytes(*args) <= B.NOALLOC_SCRATCH_BYTES
+
+
+def test_stream_copy_checks():
+    lib = M.load_library()
+    assert lib.monarch_stream_copy(A, A2, 0, None) == B.MONARCH_OK      # nothing to do
+    assert lib.monarch_stream_copy(None, A2, 64, None) == B.MONARCH_ERR_NULL
+    assert lib.monarch_stream_copy(A, None, 64, None) == B.MONARCH_ERR_NULL
+    assert lib.monarch_stream_copy(MIS, A2, 64, None) == B.MONARCH_ERR_ALIGN
