@@ -4,7 +4,7 @@
 // is the most a kernel that streams its operands through HBM can reach on
 // this memory system. Each thread issues four 16-byte non-temporal loads
 // (256 threads apart, so a wave's access is contiguous) before its four
-// stores; the grid strides over the buffer.
+// stores.
 #include "common.h"
 #include "kernels.h"
 
@@ -39,8 +39,12 @@ __global__ __launch_bounds__(CT) void stream_copy_kernel(const u32x4* __restrict
 hipError_t launch_stream_copy(const void* src, void* dst, size_t bytes, hipStream_t s) {
   const int64_t n16 = static_cast<int64_t>(bytes / 16);
   const int tail = static_cast<int>(bytes % 16);
+  // one pass over the buffer: of the grids tried (1K to 128K workgroups,
+  // 1 to 8 pieces per thread, plain or non-temporal accesses) this shape
+  // copied fastest, about 5.9 TB/s on 2 GiB. The cap keeps the launch's
+  // thread count (grid x 256) below 2^32; past 64 GiB the loop strides.
   int64_t grid = (n16 + CT * CU - 1) / (CT * CU);
-  if (grid > 2048) grid = 2048;   // 8 workgroups per CU
+  if (grid > (int64_t(1) << 22)) grid = int64_t(1) << 22;
   if (grid < 1) grid = 1;
   const size_t done = static_cast<size_t>(n16) * 16;
   hipLaunchKernelGGL(stream_copy_kernel, dim3(static_cast<unsigned>(grid)), dim3(CT), 0, s,
