@@ -63,7 +63,7 @@ enum StepKind {
   GEN_STAGE1_BWD_WEIGHT,
   REDUCE_DW,
   ZERO_DW,
-  SQ_RELU_MASK,
+  SQ_DV_PANELS,
   SQ_STAGE1_FWD,
   SQ_STAGE2_FWD,
   SQ_STAGE2_BWD_DATA,

@@ -119,9 +119,7 @@ int make_problem_ex(int64_t in, int64_t out, int64_t mid, int64_t nb1, int64_t n
     off = align_up(off + static_cast<size_t>(p.s2) * nb2 * p.q2o * p.q2i * 4, 256);
     p.ws_p1 = off;
     off = align_up(off + static_cast<size_t>(p.s1) * nb1 * p.q1o * p.q1i * 4, 256);
-    // dY in block-major order (generic and 32x32-block paths); the square
-    // path reads dY in place and keeps only the ReLU-masked dY here (reserved
-    // whatever the activation: the workspace query does not take it)
+    // dY in block-major order (sq path: panels, generic path: rows)
     p.ws_dv = off;
     off = align_up(off + static_cast<size_t>(batch) * p.out_ext * p.esize, 256);
     if (bias) {
@@ -174,7 +172,7 @@ Plan plan_bwd(const Problem& pr) {
     return p;
   }
   if (pr.path == PATH_SQ128) {
-    if (pr.act == MONARCH_ACT_RELU) p.add(SQ_RELU_MASK);
+    p.add(SQ_DV_PANELS);
     p.add(SQ_STAGE2_BWD_DATA);
     p.add(SQ_STAGE2_BWD_WEIGHT);
     p.add(SQ_STAGE1_BWD);
@@ -209,7 +207,7 @@ const char* step_name(StepKind k) {
     case GEN_STAGE1_BWD_WEIGHT: return "generic_stage1_bwd_weight";
     case REDUCE_DW: return "reduce_dw";
     case ZERO_DW: return "zero_dw";
-    case SQ_RELU_MASK: return "sq128_relu_mask";
+    case SQ_DV_PANELS: return "sq128_dv_panels";
     case SQ_STAGE1_FWD: return "sq128_stage1_fwd";
     case SQ_STAGE2_FWD: return "sq128_stage2_fwd";
     case SQ_STAGE2_BWD_DATA: return "sq128_stage2_bwd_data";
@@ -322,17 +320,17 @@ hipError_t launch_step(StepKind k, const Problem& pr, const Buffers& b, hipStrea
       if (pr.bias) rb.partial = pb, rb.out = b.dbias, rb.n = pr.out, rb.splits = pr.bias_chunks;
       return launch_reduce_partials(r2, r1, rb, bf16, s);
     }
-    case SQ_RELU_MASK:
-      return sq_launch_relu_mask(b.dy, b.y, dv, pr.batch, pr.b2, s);
+    case SQ_DV_PANELS:
+      return sq_launch_dv_panels(b.dy, mask, dv, pr.batch, pr.b2, s);
     case SQ_STAGE1_FWD:
       return sq_launch_stage1_fwd(b.x, b.w1, b.z_out, pr.batch, pr.b1, pr.sq, s);
     case SQ_STAGE2_FWD:
       return sq_launch_stage2_fwd(b.z_out, b.w2, b.y_out, pr.batch, pr.b2,
                                   pr.act == MONARCH_ACT_RELU, pr.sq, s);
     case SQ_STAGE2_BWD_DATA:
-      return sq_launch_stage2_bwd_data(mask ? dv : b.dy, b.w2, dz, pr.batch, pr.b2, pr.sq, s);
+      return sq_launch_stage2_bwd_data(dv, b.w2, dz, pr.batch, pr.b2, pr.sq, s);
     case SQ_STAGE2_BWD_WEIGHT:
-      return sq_launch_stage2_bwd_weight(mask ? dv : b.dy, b.z, p2, pr.batch, pr.b2, pr.sq, s);
+      return sq_launch_stage2_bwd_weight(dv, b.z, p2, pr.batch, pr.b2, pr.sq, s);
     case SQ_STAGE1_BWD:
       return sq_launch_stage1_bwd(dz, b.x, b.w1, b.dx, p1, pr.batch, pr.b1, pr.sq, s);
     case SM_FWD:

@@ -11,7 +11,7 @@ struct SqPlan {
   int64_t fwd1_chunks = 0, fwd1_rows = 0;  // stage-1 forward: row chunks per block
   int64_t s2_ranges = 0, s2_rows = 0;      // stage-2 forward: row ranges per block group
   int64_t d2_ranges = 0, d2_rows = 0;      // stage-2 backward data: row ranges per group
-  int64_t w2_chunks = 0, w2_rows = 0;      // stage-2 weight gradient: row ranges
+  int64_t w2_chunks = 0, w2_rows = 0;      // stage-2 weight gradient: batch chunks
   int64_t b1_chunks = 0, b1_rows = 0;      // stage-1 backward: batch chunks
 };
 
@@ -29,14 +29,14 @@ hipError_t sq_launch_stage1_fwd(const void* x, const void* w1, void* z, int64_t 
                                 const SqPlan& p, hipStream_t s);
 hipError_t sq_launch_stage2_fwd(const void* z, const void* w2, void* y, int64_t batch, int64_t nb,
                                 int relu, const SqPlan& p, hipStream_t s);
-// dye = dY where y > 0, else 0 (row-major, the ReLU backward's mask).
-hipError_t sq_launch_relu_mask(const void* dy, const void* y, void* dye, int64_t batch, int64_t nb,
-                               hipStream_t s);
-// Both stage-2 backward kernels read the caller's row-major dY (or dye).
-hipError_t sq_launch_stage2_bwd_data(const void* dy, const void* w2, void* dz, int64_t batch,
+// dv = dY (masked by ymask > 0 when ymask is set) in block-major panels:
+// feature g*128 + p of row b in the panel layout.
+hipError_t sq_launch_dv_panels(const void* dy, const void* ymask, void* dv, int64_t batch,
+                               int64_t nb, hipStream_t s);
+hipError_t sq_launch_stage2_bwd_data(const void* dv, const void* w2, void* dz, int64_t batch,
                                      int64_t nb, const SqPlan& p, hipStream_t s);
 // partial: [w2_chunks][nb][128][128] fp32
-hipError_t sq_launch_stage2_bwd_weight(const void* dy, const void* z, float* partial,
+hipError_t sq_launch_stage2_bwd_weight(const void* dv, const void* z, float* partial,
                                        int64_t batch, int64_t nb, const SqPlan& p, hipStream_t s);
 // partial: [b1_chunks][nb][128][128] fp32
 hipError_t sq_launch_stage1_bwd(const void* dz, const void* x, const void* w1, void* dx,

@@ -43,6 +43,7 @@ namespace {
 
 constexpr int Q = 128;        // block size
 constexpr int XLD = Q + 8;    // LDS pitch (elements) of [row][feature] tiles
+constexpr int TLD = 32 + 8;   // LDS pitch of [feature][32 rows] tiles
 
 __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
@@ -50,6 +51,9 @@ __device__ __forceinline__ u32x4 ldg16(const uint16_t* p) {
 // streaming load for the last reader of a tensor in the pass
 __device__ __forceinline__ u32x4 ldg16_nt(const uint16_t* p) {
   return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
+__device__ __forceinline__ void stg16(uint16_t* p, u32x4 v) {
+  *reinterpret_cast<u32x4*>(p) = v;
 }
 // streaming store for final outputs that no later kernel of the pass reads
 __device__ __forceinline__ void stg16_nt(uint16_t* p, u32x4 v) {
@@ -354,282 +358,252 @@ __global__ __launch_bounds__(512) void sq_stage2_fwd_kernel(const uint16_t* __re
 }
 
 // --------------------------------------------------------------------------
-// ReLU backward mask: dYe = dY where Y > 0, else 0 (element-wise, row-major)
+// dV panels: dV[b, g*128 + p] = dYe[b, p*b2 + g]  (block-major gradient of
+// stage 2's output; dYe = dY masked by Y > 0 after a fused ReLU)
 // --------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void sq_relu_mask_kernel(const u32x4* __restrict__ dY,
-                                                           const u32x4* __restrict__ Y,
-                                                           u32x4* __restrict__ dYe, int64_t n16) {
-  const int64_t step = static_cast<int64_t>(gridDim.x) * 256;
-  for (int64_t i = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x; i < n16; i += step)
-    dYe[i] = relu_mask_bf16(__builtin_nontemporal_load(dY + i), __builtin_nontemporal_load(Y + i));
+// The inverse stride permutation scatters one L block's outputs with stride
+// b2 through each row of Y, so a kernel owning a few blocks would read dY in
+// short runs. This pass reads dY rows in 256-byte runs (all blocks of 16 p at
+// once), transposes 8x8 bf16 blocks in registers and writes dV (feature
+// i = g*128 + p) in the panel layout through LDS in 256-byte runs. Both
+// backward stage-2 kernels then read dV contiguously.
+// Tile: RT = 256/GO rows x 16 p x 8*GO blocks (GO = min(16, b2/8) block
+// octets); 512 threads, one 8x8 block each; one tile per workgroup. The
+// staging row is XOR-swizzled with the block octet, so the 16-byte stores of
+// lanes with consecutive octets land on distinct banks.
+__global__ __launch_bounds__(512) void sq_dv_panels_kernel(const uint16_t* __restrict__ dY,
+                                                           const uint16_t* __restrict__ Ym,
+                                                           uint16_t* __restrict__ dV, int64_t B,
+                                                           int nb2) {
+  __shared__ __attribute__((aligned(16))) u32x4 st[4096];   // [g][po][row] 16-byte pieces
+  const int GO = nb2 >= 128 ? 16 : nb2 >> 3;
+  const int RT = 256 / GO;
+  const int n_gt = nb2 / (8 * GO);            // block groups per row
+  int bid = blockIdx.x;
+  const int gt = bid % n_gt;
+  bid /= n_gt;
+  const int pt = bid & 7;                     // 16-p tile
+  const int64_t b0 = static_cast<int64_t>(bid >> 3) * RT;
+  const int tid = threadIdx.x;
+  const int go = tid % GO, po = (tid / GO) & 1, row = tid / (2 * GO);
+  const uint32_t out = static_cast<uint32_t>(nb2) * Q;
+  const int64_t b = b0 + row < B ? b0 + row : B - 1;
+  const int64_t src = b * out + static_cast<int64_t>(16 * pt + 8 * po) * nb2 + (gt * GO + go) * 8;
+  u32x4 in[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) in[i] = ldg16_nt(dY + src + i * nb2);
+  if (Ym) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) in[i] = relu_mask_bf16(in[i], ldg16_nt(Ym + src + i * nb2));
+  }
+  u32x2 lo[8], hi[8];
+  transpose4x8(*reinterpret_cast<const u32x4(*)[4]>(&in[0]), lo);
+  transpose4x8(*reinterpret_cast<const u32x4(*)[4]>(&in[4]), hi);
+#pragma unroll
+  for (int e = 0; e < 8; ++e)
+    st[((go * 8 + e) * 2 + po) * RT + (row ^ go)] = u32x4{lo[e][0], lo[e][1], hi[e][0], hi[e][1]};
+  __syncthreads();
+  const int n_pieces = 8 * GO * 2 * RT;   // 4096
+  for (int id = tid; id < n_pieces; id += 512) {
+    const int r = id % RT, q = (id / RT) & 1, gl = id / (2 * RT);
+    const int64_t bb = b0 + r;
+    if (bb < B) {
+      const uint32_t panel = static_cast<uint32_t>(gt * GO * 8 + gl) * 16 + 2 * pt + q;
+      const PanelRow pr = panel_row(bb, out, static_cast<uint32_t>(B));
+      stg16(dV + pr.base + panel * pr.rt8, st[(gl * 2 + q) * RT + (r ^ (gl >> 3))]);
+    }
+  }
 }
 
 // --------------------------------------------------------------------------
-// stage 2 backward, data, from the caller's row-major dYe:
-//   dZ[b, t*b2 + g] = sum_p dYe[b, p*b2 + g] L[g,p,t]      (dZ in Z order, panels)
+// stage 2 backward, data: dZ[b, t*b2 + g] = sum_p dV[b, g*128 + p] L[g,p,t]
 // --------------------------------------------------------------------------
-// The inverse stride permutation puts the 128 p of one L block b2 elements
-// apart in a row of dY; a (row, p) of dY holds all blocks side by side. A
-// workgroup takes 32 blocks g0..g0+31 (one 64-byte run per (row, p)), a
-// 32-wide slice of t and a row range. 8 waves; wave w owns blocks
-// g0 + 8(w&3) .. +7 for the 16 t at t0 + 16(w>>2) (Lᵀ fragments gathered at
-// the start: 128 VGPRs). The range is read in 16-row tiles, each in 4 chunks
-// of 32 p. Per chunk every thread loads 4 runs' 16-byte pieces (4
-// consecutive p of 8 blocks), transposes them in registers and writes, per
-// block, the 4 p as one 8-byte half of a [block][p octet][row] LDS piece
-// (double-buffered: one barrier per chunk). The MFMA B operands (dV_g[b][8 p])
-// are then 16-byte LDS reads; the stored row is XOR-ed with the block octet
-// so that both the writes and the reads of 16 (32) lanes hit distinct banks.
-// C = dZᵀ[t x b] = Lᵀ[t x p] · dVᵀ[p x b]. A lane's results for its wave's 8
-// blocks at one (t, b) are one 16-byte piece of dZ, stored from registers:
-// 16 lanes write one 256-byte panel run.
-// The four t-slice workgroups of a block group read the same dY lines. They
-// take consecutive XCD slots (as do the block groups of a row range, which
-// share lines when b2 = 128), so the lines are fetched from HBM once and
-// served to the others by that XCD's L2; dY loads are plain, not streaming.
-constexpr int DZP = 32 * 4 * 16;   // 16-byte LDS pieces of one chunk
-
-__global__ __launch_bounds__(512) void sq_stage2_bwd_dz_kernel(const uint16_t* __restrict__ dY,
-                                                               const uint16_t* __restrict__ W2,
-                                                               uint16_t* __restrict__ dZ, int64_t B,
-                                                               int nb2, int64_t rows_per) {
+// 8 waves, 8 L blocks g0..g0+7 per workgroup; wave w owns block g0 + w (all
+// t; Lᵀ fragments gathered from L at the start: 128 VGPRs). Tile: 16 rows; the
+// MFMA B operands (dV_g[b][8 p]) are 16-byte pieces of the dV panels, loaded
+// straight into registers two tiles ahead. C = dZᵀ[t x b] = Lᵀ[t x p] ·
+// dVᵀ[p x b]; results -> LDS [t][row][g] -> dZ panels (256-byte runs).
+__global__ __launch_bounds__(512) void sq_stage2_bwd_data_kernel(
+    const uint16_t* __restrict__ dV, const uint16_t* __restrict__ W2,
+    uint16_t* __restrict__ dZ, int64_t B, int nb2, int64_t rows_per) {
   constexpr int T = 16;
-  __shared__ __attribute__((aligned(16))) u32x4 ds[2 * DZP];
-  const int n_gg = nb2 >> 5;
+  __shared__ __attribute__((aligned(16))) uint16_t zs[Q * XLD];
+  const int n_groups = nb2 >> 3;
   const int logical = xcd_logical(blockIdx.x, gridDim.x);
-  const int tg = logical & 3;
-  const int gg = (logical >> 2) % n_gg;
-  const int64_t row0 = static_cast<int64_t>((logical >> 2) / n_gg) * rows_per;
+  const int gg = logical % n_groups;
+  const int64_t row0 = static_cast<int64_t>(logical / n_groups) * rows_per;
   const int64_t row1 = row0 + rows_per < B ? row0 + rows_per : B;
   if (row0 >= row1) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l15 = lane & 15, lh = lane >> 4;
-  const int gow = w & 3;
-  const int g0 = gg * 32 + 8 * gow;          // the wave's first block
-  const int t0 = tg * 32 + 16 * (w >> 2);    // the wave's first t
-  const uint32_t out = static_cast<uint32_t>(nb2) * Q;
+  const int g = gg * 8 + w;
   const uint32_t Bu = static_cast<uint32_t>(B);
+  const uint32_t pstride = nb2 >> 3;
 
-  // A = Lᵀ[t x p] per block: lane holds L[g][p = 32ks + 8lh + e][t = t0 + l15]
+  // A = Lᵀ[t x p]: lane holds L[g][p = 32ks + 8lh + e][t = 16mt + l15]
   bf16x8 a[8][4];
+  const uint16_t* Lg = W2 + static_cast<int64_t>(g) * Q * Q;
 #pragma unroll
-  for (int k = 0; k < 8; ++k) {
-    const uint16_t* Lg = W2 + static_cast<int64_t>(g0 + k) * Q * Q;
+  for (int mt = 0; mt < 8; ++mt)
 #pragma unroll
-    for (int ks = 0; ks < 4; ++ks) a[k][ks] = frag_gather(Lg + (32 * ks + 8 * lh) * Q + t0 + l15);
-  }
+    for (int ks = 0; ks < 4; ++ks) a[mt][ks] = frag_gather(Lg + (32 * ks + 8 * lh) * Q + 16 * mt + l15);
 
-  // loader (every thread): row lrow of the tile, p = 32ks + 8lpo + 4lhalf + e
-  // (e < 4), blocks gg*32 + 8lgo .. +7; four lanes cover one 64-byte run
-  const int lgo = tid & 3, lhalf = (tid >> 2) & 1, lrow = (tid >> 3) & 15, lpo = tid >> 7;
-  const uint32_t lcol = static_cast<uint32_t>(8 * lpo + 4 * lhalf) * nb2 + gg * 32 + 8 * lgo;
-  // LDS piece of block 8lgo + j: (8lgo + j)*64 + lpo*16 + (lrow ^ 4lgo)
-  const int lslot = (32 * lgo + lpo) * 16 + (lrow ^ (4 * lgo));
-  // B operand piece k of the wave: block 8gow + k, p octet lh, row l15
-  const int rslot = (32 * gow + lh) * 16 + (l15 ^ (4 * gow));
+  const uint32_t F = static_cast<uint32_t>(nb2) * Q;
+  // operand pieces: panel g*16 + 4ks + lh, row b0 + l15
+  const uint32_t vpanel = g * 16 + lh;
+  // dZ pieces: t = (tid>>4) + 32i, row = tid&15; panel (t*b2 + g0)/8
+  const int zt = tid >> 4, zrow = tid & 15;
+  const uint32_t zpanel = zt * pstride + gg;
+  const uint32_t zstep = 32 * pstride;   // panels
 
-  const int64_t ntiles = (row1 - row0 + T - 1) / T;
-  const int64_t nchunks = ntiles * 4;
-  // chunk c: tile c >> 2, p chunk c & 3
-  auto gload = [&](u32x4(&pre)[4], int64_t c) {
-    const int64_t b0 = row0 + (c >> 2) * T;
+  auto gload = [&](u32x4(&pre)[4], int64_t b0) {
     const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
-    const uint16_t* base = dY + static_cast<uint32_t>(bc + clamp_row(lrow, lim)) * out +
-                           32 * static_cast<uint32_t>(c & 3) * nb2 + lcol;
+    const PanelRow pr = panel_row(bc + clamp_row(l15, lim), F, Bu);
+    const uint16_t* base = dV + pr.base + vpanel * pr.rt8;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) pre[e] = ldg16(base + e * nb2);
+    for (int ks = 0; ks < 4; ++ks) pre[ks] = ldg16_nt(base + 4 * ks * pr.rt8);   // +4 panels
+  };
+  auto body = [&](u32x4(&cur)[4], int64_t b0) {
+    pin(cur);
+    f32x4 acc[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) acc[mt] = zero4();
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+      bf16x8 bop;
+      __builtin_memcpy(&bop, &cur[ks], sizeof(bop));
+#pragma unroll
+      for (int mt = 0; mt < 8; ++mt) acc[mt] = mfma(a[mt][ks], bop, acc[mt]);
+    }
+    gload(cur, b0 + 2 * T);
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt)
+#pragma unroll
+      for (int v = 0; v < 4; v += 2) {
+        const uint32_t pk = pack_bf16x2(acc[mt][v], acc[mt][v + 1]);
+        zs[(16 * mt + 4 * lh + v) * XLD + l15 * 8 + w] = static_cast<uint16_t>(pk & 0xffffu);
+        zs[(16 * mt + 4 * lh + v + 1) * XLD + l15 * 8 + w] = static_cast<uint16_t>(pk >> 16);
+      }
+    __syncthreads();
+    const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
+    const PanelRow pr = panel_row(bc + clamp_row(zrow, lim), F, Bu);
+    uint16_t* zb = dZ + pr.base + zpanel * pr.rt8;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      stg16_nt(zb + i * zstep * pr.rt8,
+               *reinterpret_cast<const u32x4*>(&zs[(zt + 32 * i) * XLD + zrow * 8]));
+    __syncthreads();
   };
 
-  f32x4 acc[8];
+  const int64_t npairs = (row1 - row0 + 2 * T - 1) / (2 * T);
   u32x4 pa[4], pb[4];
-  gload(pa, 0);
-  gload(pb, 1);
+  gload(pa, row0);
+  gload(pb, row0 + T);
   pin(a);
   pin(pa);
   pin(pb);
-  auto step = [&](auto kc, u32x4(&cur)[4], int64_t tile) {
-    constexpr int ks = decltype(kc)::value;
-    const int64_t c = tile * 4 + ks;
-    pin(cur);
-    u32x2 tr[8];
-    transpose4x8(cur, tr);   // tr[j]: the 4 p of block 8lgo + j
-    u32x2* dst = reinterpret_cast<u32x2*>(ds + (ks & 1) * DZP);
-#pragma unroll
-    for (int j = 0; j < 8; ++j) dst[(lslot + 64 * j) * 2 + lhalf] = tr[j];
-    gload(cur, c + 2 < nchunks ? c + 2 : nchunks - 1);
-    __syncthreads();
-    if constexpr (ks == 0) {
-#pragma unroll
-      for (int k = 0; k < 8; ++k) acc[k] = zero4();
-    }
-    const u32x4* src = ds + (ks & 1) * DZP;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const u32x4 v = src[rslot + 64 * k];
-      bf16x8 bop;
-      __builtin_memcpy(&bop, &v, sizeof(bop));
-      acc[k] = mfma(a[k][ks], bop, acc[k]);
-    }
-    if constexpr (ks == 3) {
-      // lane: (t = t0 + 4lh + v, row l15) of blocks g0 .. g0+7 = one dZ piece
-      const int64_t b0 = row0 + tile * T;
-      const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
-      const PanelRow pr = panel_row(bc + clamp_row(l15, lim), out, Bu);
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const uint32_t panel = static_cast<uint32_t>(t0 + 4 * lh + v) * (nb2 >> 3) + (g0 >> 3);
-        stg16_nt(dZ + pr.base + panel * pr.rt8,
-                 u32x4{pack_bf16x2(acc[0][v], acc[1][v]), pack_bf16x2(acc[2][v], acc[3][v]),
-                       pack_bf16x2(acc[4][v], acc[5][v]), pack_bf16x2(acc[6][v], acc[7][v])});
-      }
-    }
-  };
-  for (int64_t tile = 0; tile < ntiles; ++tile) {
-    step(std::integral_constant<int, 0>{}, pa, tile);
-    step(std::integral_constant<int, 1>{}, pb, tile);
-    step(std::integral_constant<int, 2>{}, pa, tile);
-    step(std::integral_constant<int, 3>{}, pb, tile);
+  for (int64_t k = 0; k < npairs; ++k) {
+    body(pa, row0 + 2 * k * T);
+    body(pb, row0 + (2 * k + 1) * T);
   }
 }
 
 // --------------------------------------------------------------------------
-// stage 2 backward, weights, from the caller's row-major dYe:
-//   dL[g,p,t] = sum_b dYe[b, p*b2 + g] W[b, g*128 + t]     (fp32 partial per row range)
+// stage 2 backward, weights: dL[g,p,t] = sum_b dV[b, g*128 + p] W[b, g*128 + t]
 // --------------------------------------------------------------------------
-// Workgroup: 32 L blocks g0..g0+31 x a 32-wide slice of p x a 64-wide slice
-// of t x a row range. 8 waves; wave w owns blocks g0 + 4w .. +3: their dL
-// sums for the slice's p and t (4 x 2 x 4 16x16 tiles, 128 VGPRs). K step: 16
-// rows, 16x16x16 MFMAs with A = dYeᵀ[p x pos] and B = W[pos x t]. Each step
-// stages both operands in LDS with the batch rows as the contiguous
-// dimension, from loads that a 4x8 register transpose turns into 8-byte
-// writes:
-//  * dYe, [block][p][16 pos] (32 KB): a thread loads rows rq + 4i (i < 4) of
-//    one 16-byte piece (8 blocks at one p; four lanes cover one 64-byte run);
-//  * W, [block][t][16 pos] (64 KB): the same for two W panel pieces (8 t of
-//    one block).
-// pos 4rq + i holds row rq + 4i in both (a sum may take the rows in any
-// order that both operands share). The stored p row is XOR-ed with the
-// piece's block octet and t is rotated within its octet, and the two 8-byte
-// halves of a row swap places in every odd group of 8 rows: the 8-byte writes
-// of 32 lanes and the fragment reads of 32 lanes then touch 32 distinct bank
-// pairs. Rows past the range are loaded clamped; their dYe is zeroed.
-// The workgroups of a row range take consecutive XCD slots, so dY lines
-// (shared by block groups and t halves) and W panels (shared by p slices)
-// are fetched from HBM once; loads are plain, not streaming.
-typedef short s16x4 __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ f32x4 mfma16(u32x2 a, u32x2 b, f32x4 c) {
-  s16x4 x, y;
-  __builtin_memcpy(&x, &a, sizeof(x));
-  __builtin_memcpy(&y, &b, sizeof(y));
-  return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(x, y, c, 0, 0, 0);
-}
+// Workgroup: one L block x a batch chunk, all p and t. 4 waves; wave w owns
+// p in [32w, +32): accumulators dL[32 p x 128 t] in VGPRs. Tile: 32 rows =
+// one K step; two tiles in flight in registers. dV and W are both
+// block-major panels: waves 0-1 load dV, waves 2-3 load W, each thread 4
+// rows of one panel. Both MFMA operands need consecutive batch rows per
+// lane, so a 4x8 register transpose gives 8-byte LDS writes of
+// [feature][position] tiles. A sum over rows may take them in any order:
+// position 4rq + i holds row rq + 8i in both operands, so every load
+// instruction reads whole 128-byte lines (8 consecutive rows of a panel).
+// The chunk's sum is written as an fp32 partial.
+__device__ __forceinline__ int fl_row(int f) { return f * TLD + (f >> 3) * 8; }  // LDS row of feature f
 
-__global__ __launch_bounds__(512) void sq_stage2_bwd_dl_kernel(const uint16_t* __restrict__ dY,
-                                                               const uint16_t* __restrict__ Wz,
-                                                               float* __restrict__ partial,
-                                                               int64_t B, int nb2,
-                                                               int64_t rows_per) {
-  constexpr int T = 16;
-  __shared__ __attribute__((aligned(16))) u32x2 la[32 * 32 * 4];   // [block][p row][quad]
-  __shared__ __attribute__((aligned(16))) u32x2 lb[32 * 64 * 4];   // [block][t row][quad]
-  const int n_gg = nb2 >> 5;
-  const int logical = xcd_logical(blockIdx.x, gridDim.x);
-  const int th = logical & 1;
-  const int pg = (logical >> 1) & 3;
-  const int gg = (logical >> 3) % n_gg;
-  const int range = (logical >> 3) / n_gg;
-  const int64_t row0 = static_cast<int64_t>(range) * rows_per;
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void sq_stage2_bwd_weight_kernel(
+    const uint16_t* __restrict__ dV, const uint16_t* __restrict__ Wz, float* __restrict__ partial,
+    int64_t B, int nb2, int64_t rows_per) {
+  constexpr int T = 32;
+  constexpr int TS = Q * TLD + Q;   // one operand's [128][positions] tile (+ skew)
+  __shared__ __attribute__((aligned(16))) uint16_t ts[2 * TS];
+  const int g = blockIdx.x % nb2;
+  const int chunk = blockIdx.x / nb2;
+  const int64_t row0 = static_cast<int64_t>(chunk) * rows_per;
   const int64_t row1 = row0 + rows_per < B ? row0 + rows_per : B;
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l15 = lane & 15, lh = lane >> 4;
-  const uint32_t out = static_cast<uint32_t>(nb2) * Q, Bu = static_cast<uint32_t>(B);
-  const int g0 = gg * 32, p0 = pg * 32, t0 = th * 64;
 
-  f32x4 acc[4][2][4];
+  f32x4 acc[2][8];
 #pragma unroll
-  for (int gi = 0; gi < 4; ++gi)
+  for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int pt = 0; pt < 2; ++pt)
-#pragma unroll
-      for (int tt = 0; tt < 4; ++tt) acc[gi][pt][tt] = zero4();
+    for (int nt = 0; nt < 8; ++nt) acc[mt][nt] = zero4();
 
-  // dYe loader: rq, block octet ago, p = p0 + ap
-  const int rq = tid & 3, ago = (tid >> 2) & 3, ap = tid >> 4;
-  const uint32_t acol = static_cast<uint32_t>(p0 + ap) * nb2 + g0 + 8 * ago;
-  const int aprow = ap ^ (2 * ago);
-  // la index of block 8ago + j: + 128 j
-  const int aidx = (8 * ago * 32 + aprow) * 4 + (rq ^ (2 * ((aprow >> 3) & 1)));
-  // W loader: t octet bto of the half, blocks bgl and bgl + 16
-  const int bto = (tid >> 2) & 7, bgl = tid >> 5;
-  const uint32_t bpanel = static_cast<uint32_t>(g0 + bgl) * 16 + th * 8 + bto;
-  // lb index of t = 8bto + j, block bgl (+16): + 4 ((j + bto) & 7) (+ 16*64*4)
-  const int bidx = (bgl * 64 + 8 * bto) * 4 + (rq ^ (2 * (bto & 1)));
-  // fragment reads: A (block 4w + gi, p = 16pt + l15), B (block 4w + gi, t = 16tt + l15)
-  const int hq = lh ^ (2 * (l15 >> 3));
-  const int ra = ((4 * w) * 32 + (l15 ^ (2 * (w >> 1)))) * 4 + hq;   // + 128 gi + 64 pt
-  const int rb = (4 * w) * 64 * 4 + hq;                              // + 256 gi + row(tt)*4
+  // loader role: thread (rq = lt&7, pl = lt>>3) loads rows rq + 8i of panel
+  // g*16 + pl (features 8pl ..) of dV or W
+  const bool is_w = w >= 2;
+  const int lt = tid & 127, rq = lt & 7, pl = lt >> 3;
+  const uint16_t* src = is_w ? Wz : dV;
+  const uint32_t panel = g * 16 + pl;
+  const uint32_t F = static_cast<uint32_t>(nb2) * Q, Bu = static_cast<uint32_t>(B);
+  uint16_t* tdst = &ts[(is_w ? TS : 0) + fl_row(pl * 8) + 4 * rq];
 
-  auto gload = [&](u32x4(&pa)[4], u32x4(&pb)[8], int64_t b0) {
+  auto gload = [&](u32x4(&pre)[4], int64_t b0) {
     const int64_t bc = b0 < row1 ? b0 : row1 - 1, lim = row1 - bc;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int64_t row = bc + clamp_row(rq + 4 * i, lim);
-      pa[i] = ldg16(dY + static_cast<uint32_t>(row) * out + acol);
-      const PanelRow pr = panel_row(row, out, Bu);
-      pb[i] = ldg16(Wz + pr.base + bpanel * pr.rt8);
-      pb[4 + i] = ldg16(Wz + pr.base + (bpanel + 256) * pr.rt8);
+      const PanelRow pr = panel_row(bc + clamp_row(rq + 8 * i, lim), F, Bu);
+      pre[i] = ldg16_nt(src + pr.base + panel * pr.rt8);
     }
   };
-  auto body = [&](u32x4(&pa)[4], u32x4(&pb)[8], int64_t b0) {
-    pin(pa);
-    pin(pb);
+  auto body = [&](u32x4(&pre)[4], int64_t b0) {
+    pin(pre);
+    // dV rows past the range were loaded clamped: zero them (W rows stay)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) pa[i] = zero_unless(b0 + rq + 4 * i < row1, pa[i]);
+    for (int i = 0; i < 4; ++i) pre[i] = zero_unless(is_w || b0 + rq + 8 * i < row1, pre[i]);
     u32x2 tr[8];
-    transpose4x8(pa, tr);
+    transpose4x8(pre, tr);
 #pragma unroll
-    for (int j = 0; j < 8; ++j) la[aidx + 128 * j] = tr[j];
-#pragma unroll
-    for (int s = 0; s < 2; ++s) {
-      transpose4x8(*reinterpret_cast<const u32x4(*)[4]>(&pb[4 * s]), tr);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) lb[bidx + s * 16 * 64 * 4 + 4 * ((j + bto) & 7)] = tr[j];
-    }
+    for (int e = 0; e < 8; ++e) *reinterpret_cast<u32x2*>(tdst + e * TLD) = tr[e];
     __syncthreads();
-    gload(pa, pb, b0 + T);
+    gload(pre, b0 + 2 * T);
+    bf16x8 A[2];
 #pragma unroll
-    for (int gi = 0; gi < 4; ++gi) {
-      const u32x2 A0 = la[ra + 128 * gi], A1 = la[ra + 128 * gi + 64];
+    for (int mt = 0; mt < 2; ++mt) A[mt] = frag_ld(&ts[fl_row(32 * w + 16 * mt + l15) + 8 * lh]);
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt) {
-        // t = 16tt + l15: octet 2tt + (l15 >> 3), rotated row within it
-        const int to = 2 * tt + (l15 >> 3);
-        const int trow = 8 * to + (((l15 & 7) + to) & 7);
-        const u32x2 Bv = lb[rb + 256 * gi + 4 * trow];
-        acc[gi][0][tt] = mfma16(A0, Bv, acc[gi][0][tt]);
-        acc[gi][1][tt] = mfma16(A1, Bv, acc[gi][1][tt]);
-      }
+    for (int nt = 0; nt < 8; ++nt) {
+      const bf16x8 Bv = frag_ld(&ts[TS + fl_row(16 * nt + l15) + 8 * lh]);
+#pragma unroll
+      for (int mt = 0; mt < 2; ++mt) acc[mt][nt] = mfma(A[mt], Bv, acc[mt][nt]);
     }
     __syncthreads();
   };
 
   if (row0 < row1) {
-    u32x4 pa[4], pb[8];
-    gload(pa, pb, row0);
-    for (int64_t b0 = row0; b0 < row1; b0 += T) body(pa, pb, b0);
+    const int64_t npairs = (row1 - row0 + 2 * T - 1) / (2 * T);
+    u32x4 pa[4], pb[4];
+    gload(pa, row0);
+    gload(pb, row0 + T);
+    pin(pa);
+    pin(pb);
+    for (int64_t k = 0; k < npairs; ++k) {
+      body(pa, row0 + 2 * k * T);
+      body(pb, row0 + (2 * k + 1) * T);
+    }
   }
-  // partial[range][g][p][t]; lane: p = 16pt + 4lh + v, t = 16tt + l15
-  float* P = partial + (static_cast<int64_t>(range) * nb2 + g0 + 4 * w) * Q * Q;
+  // partial[chunk][g][p][t]
+  float* P = partial + (static_cast<int64_t>(chunk) * nb2 + g) * Q * Q;
 #pragma unroll
-  for (int gi = 0; gi < 4; ++gi)
+  for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
-    for (int pt = 0; pt < 2; ++pt)
+    for (int nt = 0; nt < 8; ++nt)
 #pragma unroll
-      for (int tt = 0; tt < 4; ++tt)
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-          P[gi * Q * Q + (p0 + 16 * pt + 4 * lh + v) * Q + t0 + 16 * tt + l15] = acc[gi][pt][tt][v];
+      for (int v = 0; v < 4; ++v)
+        P[(32 * w + 16 * mt + 4 * lh + v) * Q + 16 * nt + l15] = acc[mt][nt][v];
 }
 
 // --------------------------------------------------------------------------
@@ -787,14 +761,13 @@ SqPlan sq_plan(int64_t batch, int64_t nb) {
   p.s2_ranges = clamp64(256 / (groups * 4), 1, cdiv(batch, 16));
   p.s2_rows = round_up(cdiv(batch, p.s2_ranges), 16);
   p.s2_ranges = cdiv(batch, p.s2_rows);
-  // stage-2 backward data: groups x 4 t slices x row ranges ~ one workgroup per CU
-  p.d2_ranges = clamp64(256 / (groups * 4), 1, cdiv(batch, 16));
+  // stage-2 backward data: nb/8 block groups x row ranges ~ one workgroup per CU
+  p.d2_ranges = clamp64(256 / (nb / 8), 1, cdiv(batch, 16));
   p.d2_rows = round_up(cdiv(batch, p.d2_ranges), 16);
   p.d2_ranges = cdiv(batch, p.d2_rows);
-  // stage-2 weight gradient: groups x 4 p slices x 2 t halves x row ranges ~
-  // one workgroup per CU
-  p.w2_chunks = clamp64(256 / (groups * 8), 1, cdiv(batch, 16));
-  p.w2_rows = round_up(cdiv(batch, p.w2_chunks), 16);
+  // stage-2 weight gradient: nb blocks x chunks ~ three 4-wave workgroups per CU
+  p.w2_chunks = clamp64(768 / nb, 1, cdiv(batch, 32));
+  p.w2_rows = round_up(cdiv(batch, p.w2_chunks), 32);
   p.w2_chunks = cdiv(batch, p.w2_rows);
   // stage-1 backward: 2 workgroups of 8 waves per CU
   p.b1_chunks = clamp64(512 / nb, 1, cdiv(batch, T1));
@@ -827,32 +800,31 @@ hipError_t sq_launch_stage2_fwd(const void* z, const void* w2, void* y, int64_t 
   return hipGetLastError();
 }
 
-hipError_t sq_launch_relu_mask(const void* dy, const void* y, void* dye, int64_t batch, int64_t nb,
-                               hipStream_t s) {
-  const int64_t n16 = batch * nb * Q / 8;
-  int64_t grid = cdiv(n16, 256 * 4);
-  if (grid > 8192) grid = 8192;
-  if (grid < 1) grid = 1;
-  hipLaunchKernelGGL(sq_relu_mask_kernel, dim3(static_cast<unsigned>(grid)), dim3(256), 0, s,
-                     static_cast<const u32x4*>(dy), static_cast<const u32x4*>(y),
-                     static_cast<u32x4*>(dye), n16);
+hipError_t sq_launch_dv_panels(const void* dy, const void* ymask, void* dv, int64_t batch,
+                               int64_t nb, hipStream_t s) {
+  const int64_t GO = nb >= 128 ? 16 : nb / 8;
+  const int64_t RT = 256 / GO;
+  const int64_t grid = cdiv(batch, RT) * 8 * (nb / (8 * GO));
+  hipLaunchKernelGGL(sq_dv_panels_kernel, dim3(static_cast<unsigned>(grid)), dim3(512), 0, s,
+                     static_cast<const uint16_t*>(dy), static_cast<const uint16_t*>(ymask),
+                     static_cast<uint16_t*>(dv), batch, static_cast<int>(nb));
   return hipGetLastError();
 }
 
-hipError_t sq_launch_stage2_bwd_data(const void* dy, const void* w2, void* dz, int64_t batch,
+hipError_t sq_launch_stage2_bwd_data(const void* dv, const void* w2, void* dz, int64_t batch,
                                      int64_t nb, const SqPlan& p, hipStream_t s) {
-  hipLaunchKernelGGL(sq_stage2_bwd_dz_kernel, dim3(static_cast<unsigned>(nb / 32 * 4 * p.d2_ranges)),
-                     dim3(512), 0, s, static_cast<const uint16_t*>(dy),
+  hipLaunchKernelGGL(sq_stage2_bwd_data_kernel, dim3(static_cast<unsigned>(nb / 8 * p.d2_ranges)),
+                     dim3(512), 0, s, static_cast<const uint16_t*>(dv),
                      static_cast<const uint16_t*>(w2), static_cast<uint16_t*>(dz), batch,
                      static_cast<int>(nb), p.d2_rows);
   return hipGetLastError();
 }
 
-hipError_t sq_launch_stage2_bwd_weight(const void* dy, const void* z, float* partial,
+hipError_t sq_launch_stage2_bwd_weight(const void* dv, const void* z, float* partial,
                                        int64_t batch, int64_t nb, const SqPlan& p, hipStream_t s) {
-  hipLaunchKernelGGL(sq_stage2_bwd_dl_kernel,
-                     dim3(static_cast<unsigned>(nb / 32 * 8 * p.w2_chunks)), dim3(512), 0, s,
-                     static_cast<const uint16_t*>(dy), static_cast<const uint16_t*>(z), partial,
+  hipLaunchKernelGGL(sq_stage2_bwd_weight_kernel,
+                     dim3(static_cast<unsigned>(nb * p.w2_chunks)), dim3(256), 0, s,
+                     static_cast<const uint16_t*>(dv), static_cast<const uint16_t*>(z), partial,
                      batch, static_cast<int>(nb), p.w2_rows);
   return hipGetLastError();
 }
