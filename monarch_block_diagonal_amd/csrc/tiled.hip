@@ -267,7 +267,9 @@ void tiled_gemm_kernel(GemmArgs p, int64_t m_tiles,
   constexpr int TM = WM * FM * 16, TN = WN * FN * 16, TK = C::TK;
   static_assert(WM * WN == 4 || WM * WN == 8, "four or eight waves");
   constexpr int TT = WM * WN * 64;
-  constexpr int SL = kSlots<TM>, LB = kBufs<TM, TN>;
+  // the element-wise variants keep one K tile in registers: their per-element
+  // loads and masks need the room of the second slot
+  constexpr int SL = EW ? 1 : kSlots<TM>, LB = kBufs<TM, TN>;
   using TA = Tile<T, AM, TM, EW, SL, TT>;
   using TB = Tile<T, BMD, TN, EW, SL, TT>;
   __shared__ __attribute__((aligned(16))) T As[LB][TA::LDS];
@@ -680,6 +682,17 @@ Shape pick_shape(int64_t M, int64_t N, bool bf16) {
   return S32x32;
 }
 
+// Operands loaded element by element take the smaller tiles: the 256-row
+// tiles of the element-wise variant would not fit in 256 VGPRs per lane.
+Shape ew_shape(Shape s) {
+  switch (s) {
+    case S256x256:
+    case S256x192: return S128x128;
+    case S256x64: return S64x64;
+    default: return s;
+  }
+}
+
 void shape_tiles(Shape s, int* tm, int* tn) {
   switch (s) {
     case S256x256: *tm = 256, *tn = 256; return;
@@ -706,28 +719,34 @@ hipError_t launch_modes(const GemmArgs& a, Shape sh, dim3 g, int64_t mt, int64_t
   else                                                                                          \
     hipLaunchKernelGGL((tiled_gemm_kernel<T, AM, BMD, WM, WN, FM, FN, true>), g,               \
                        dim3(WM * WN * 64), 0, s, a, mt, nt, remap, avec, bvec)
+  // shapes that ew_shape() keeps away from the element-wise loads
+#define MONARCH_TILED_VEC(WM, WN, FM, FN)                                                     \
+  if (!(avec && bvec)) return hipErrorInvalidValue;                                            \
+  hipLaunchKernelGGL((tiled_gemm_kernel<T, AM, BMD, WM, WN, FM, FN, false>), g,                \
+                     dim3(WM * WN * 64), 0, s, a, mt, nt, remap, 1, 1)
   switch (sh) {
     case S256x256:
       if constexpr (std::is_same<T, uint16_t>::value) {
-        MONARCH_TILED(2, 4, 8, 4);
+        MONARCH_TILED_VEC(2, 4, 8, 4);
       } else {
         return hipErrorInvalidValue;
       }
       break;
     case S256x192:
       if constexpr (std::is_same<T, uint16_t>::value) {
-        MONARCH_TILED(2, 4, 8, 3);
+        MONARCH_TILED_VEC(2, 4, 8, 3);
       } else {
         return hipErrorInvalidValue;
       }
       break;
     case S128x128: MONARCH_TILED(2, 2, 4, 4); break;
-    case S256x64: MONARCH_TILED(4, 1, 4, 4); break;
+    case S256x64: MONARCH_TILED_VEC(4, 1, 4, 4); break;
     case S256x32: MONARCH_TILED(4, 1, 4, 2); break;
     case S64x64: MONARCH_TILED(2, 2, 2, 2); break;
     case S32x32: MONARCH_TILED(2, 2, 1, 1); break;
   }
 #undef MONARCH_TILED
+#undef MONARCH_TILED_VEC
   return hipGetLastError();
 }
 
@@ -758,7 +777,7 @@ hipError_t launch_gemm(const GemmArgs& a, bool bf16, hipStream_t s) {
   g4.cvec = !a.partial && (a.nsplit == 0 || (a.nsplit % 4 == 0 && a.c_sj_hi % 4 == 0)) &&
             a.c_sj == 1 && a.c_sb % 4 == 0 && a.c_si % 4 == 0 &&
             a.N % 4 == 0 && (a.c_cols < 0 || a.c_cols % 4 == 0);
-  const Shape sh = pick_shape(a.M, a.N, bf16);
+  const Shape sh = avec && bvec ? pick_shape(a.M, a.N, bf16) : ew_shape(pick_shape(a.M, a.N, bf16));
   int tm, tn;
   shape_tiles(sh, &tm, &tn);
   const int64_t mt = (a.M + tm - 1) / tm, nt = (a.N + tn - 1) / tn;
