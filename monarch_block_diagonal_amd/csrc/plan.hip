@@ -268,7 +268,7 @@ hipError_t launch_step(StepKind k, const Problem& pr, const Buffers& b, hipStrea
       a.B = b.w2;
       a.b_sb = pr.q2o * pr.q2i, a.b_sk = 1, a.b_sj = pr.q2i;
       a.C = b.y_out;
-      a.c_sb = 1, a.c_si = pr.out, a.c_sj = pr.b2, a.c_cols = pr.out;
+      a.c_sb = 1, a.c_si = pr.out, a.c_sj = pr.b2, a.c_cols = pr.out < pr.out_ext ? pr.out : -1;
       a.bias = b.bias;
       a.M = pr.batch, a.N = pr.q2o, a.K = pr.q2i, a.nblk = pr.b2;
       a.relu = pr.act == MONARCH_ACT_RELU;
@@ -300,7 +300,7 @@ hipError_t launch_step(StepKind k, const Problem& pr, const Buffers& b, hipStrea
       a.B = b.w1;
       a.b_sb = pr.q1o * pr.q1i, a.b_sk = pr.q1i, a.b_sj = 1;
       a.C = b.dx;
-      a.c_sb = pr.q1i, a.c_si = pr.in, a.c_sj = 1, a.c_cols = pr.in;
+      a.c_sb = pr.q1i, a.c_si = pr.in, a.c_sj = 1, a.c_cols = pr.in < pr.in_ext ? pr.in : -1;
       a.M = pr.batch, a.N = pr.q1i, a.K = pr.q1o, a.nblk = pr.b1;
       return launch_gemm(a, bf16, s);
     case GEN_STAGE1_BWD_WEIGHT:

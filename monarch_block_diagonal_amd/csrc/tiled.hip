@@ -258,6 +258,127 @@ template <> struct Vec4<uint16_t> {
   }
 };
 
+// Writes a workgroup's TM x TN result tile the way GemmArgs asks (plain,
+// 4-wide, fp32 partial, or with accumulation, bias, ReLU and the column
+// split). acc holds wave (wm, wn)'s FM x FN 16x16 MFMA tiles.
+template <typename T, int WM, int WN, int FM, int FN>
+__device__ __forceinline__ void write_tile(const GemmArgs& p, const f32x4 (&acc)[FM][FN],
+                                           int64_t blk, int64_t split, int64_t i0, int64_t j0,
+                                           int wm, int wn, int l15, int lh) {
+  constexpr int TM = WM * FM * 16, TN = WN * FN * 16;
+  // 16x16 result layout: lane holds rows 4*(lane/16)+v, column lane%16
+  const int64_t cblk = blk * p.c_sb;
+  // a whole tile of stores that keep every column (the common case) skips
+  // the per-element range checks and steps row offsets by the row stride;
+  // bias (one load per column) and ReLU fold in
+  const bool plain = !p.partial && !p.accum && p.c_cols < 0 && i0 + TM <= p.M && j0 + TN <= p.N;
+  // offset of this lane's first row (v = 0 of tile row 0)
+  const int64_t rb = (i0 + wm * FM * 16 + 4 * lh) * p.c_si;
+  if (p.cvec && plain) {
+    const int u = l15 & 3;
+#pragma unroll
+    for (int ni = 0; ni < FN; ++ni) {
+      const int64_t jb = j0 + (wn * FN + ni) * 16 + (l15 & ~3);
+      const int64_t cpos = cblk + (p.nsplit > 0 ? col_off(jb, p.nsplit, p.c_sj_hi, 1) : jb);
+      T* c = static_cast<T*>(p.C) + rb + u * p.c_si + cpos;
+      const f32x4 bv = p.bias ? Vec4<T>::load(p.bias, cpos) : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int mi = 0; mi < FM; ++mi) {
+        f32x4 o = quad_transpose4(acc[mi][ni], u) + bv;
+        if (p.relu) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = o[e] > 0.f ? o[e] : 0.f;
+        }
+        Vec4<T>::store(c, mi * 16 * p.c_si, o);
+      }
+    }
+    return;
+  }
+  if (p.partial && i0 + TM <= p.M && j0 + TN <= p.N) {
+    float* P = p.partial + ((split * p.nblk + blk) * p.M + i0 + wm * FM * 16 + 4 * lh) * p.N + j0 +
+               wn * FN * 16 + l15;
+#pragma unroll
+    for (int ni = 0; ni < FN; ++ni)
+#pragma unroll
+      for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) P[(mi * 16 + v) * p.N + ni * 16] = acc[mi][ni][v];
+    return;
+  }
+  if (plain) {
+#pragma unroll
+    for (int ni = 0; ni < FN; ++ni) {
+      const int64_t j = j0 + (wn * FN + ni) * 16 + l15;
+      const int64_t cpos = cblk + col_off(j, p.nsplit, p.c_sj_hi, p.c_sj);
+      T* c = static_cast<T*>(p.C) + rb + cpos;
+      const float bv = p.bias ? Io<T>::load(p.bias, cpos) : 0.f;
+#pragma unroll
+      for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          float o = acc[mi][ni][v] + bv;
+          if (p.relu) o = o > 0.f ? o : 0.f;
+          Io<T>::store(c, (mi * 16 + v) * p.c_si, o);
+        }
+    }
+    return;
+  }
+  if (p.cvec) {
+    // a 4x4 transpose within each quad of lanes (columns 4c..4c+3) leaves
+    // lane 4c+u with row 4*(lane/16)+u, columns 4c..4c+3: one 4-element
+    // load/store per row instead of four single elements. In rotation r
+    // lane u sends its row (u - r) & 3 and receives, by a DPP quad
+    // permutation (lane u reads lane (u + r) & 3), row u of column
+    // (u + r) & 3; the selections are two-level on the bits of a
+    // loop-invariant lane index, so they stay selects, not branches.
+    const int u = l15 & 3;
+#pragma unroll
+    for (int ni = 0; ni < FN; ++ni) {
+      const int64_t jb = j0 + (wn * FN + ni) * 16 + (l15 & ~3);
+      // with a column split the four columns stay within one piece
+      const int64_t cpos = cblk + (p.nsplit > 0 ? col_off(jb, p.nsplit, p.c_sj_hi, 1) : jb);
+#pragma unroll
+      for (int mi = 0; mi < FM; ++mi) {
+        f32x4 o = quad_transpose4(acc[mi][ni], u);
+        const int64_t i = i0 + (wm * FM + mi) * 16 + 4 * lh + u;
+        if (i < p.M && jb < p.N && (p.c_cols < 0 || cpos < p.c_cols)) {
+          const int64_t off = i * p.c_si + cpos;
+          if (p.accum) o += Vec4<T>::load(p.C, off);
+          if (p.bias) o += Vec4<T>::load(p.bias, cpos);
+          if (p.relu) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) o[e] = o[e] > 0.f ? o[e] : 0.f;
+          }
+          Vec4<T>::store(p.C, off, o);
+        }
+      }
+    }
+    return;
+  }
+#pragma unroll
+  for (int ni = 0; ni < FN; ++ni) {
+    const int64_t j = j0 + (wn * FN + ni) * 16 + l15;
+    const int64_t cpos = cblk + col_off(j, p.nsplit, p.c_sj_hi, p.c_sj);   // in-row offset
+#pragma unroll
+    for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int64_t i = i0 + (wm * FM + mi) * 16 + 4 * lh + v;
+        if (i < p.M && j < p.N) {
+          float val = acc[mi][ni][v];
+          if (p.partial) {
+            p.partial[((split * p.nblk + blk) * p.M + i) * p.N + j] = val;
+          } else if (p.c_cols < 0 || cpos < p.c_cols) {
+            if (p.accum) val += Io<T>::load(p.C, i * p.c_si + cpos);
+            if (p.bias) val += Io<T>::load(p.bias, cpos);
+            if (p.relu) val = val > 0.f ? val : 0.f;
+            Io<T>::store(p.C, i * p.c_si + cpos, val);
+          }
+        }
+      }
+  }
+}
+
 template <typename T, int AM, int BMD, int WM, int WN, int FM, int FN, bool EW>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void tiled_gemm_kernel(GemmArgs p, int64_t m_tiles,
@@ -450,105 +571,195 @@ void tiled_gemm_kernel(GemmArgs p, int64_t m_tiles,
     }
   }
 
-  // 16x16 result layout: lane holds rows 4*(lane/16)+v, column lane%16
-  const int64_t cblk = blk * p.c_sb;
-  // a whole tile of plain stores (the common case) skips the per-element
-  // range checks and flags and steps row offsets by the row stride
-  const bool plain = !p.partial && !p.accum && !p.bias && !p.relu && p.c_cols < 0 &&
-                     i0 + TM <= p.M && j0 + TN <= p.N;
-  // offset of this lane's first row (v = 0 of tile row 0)
-  const int64_t rb = (i0 + wm * FM * 16 + 4 * lh) * p.c_si;
-  if (p.cvec && plain) {
-    const int u = l15 & 3;
+  write_tile<T, WM, WN, FM, FN>(p, acc, blk, split, i0, j0, wm, wn, l15, lh);
+}
+
+// --------------------------------------------------------------------------
+// Pipelined variant: bf16, both operands K-contiguous with 16-byte aligned
+// pieces, the 256 x 256 and 256 x 192 tiles (8 waves, 128 x 64 or 128 x 48
+// per wave).
+// --------------------------------------------------------------------------
+// At these tile sizes the register-staged kernel above has room for one K
+// tile in flight, so each load has one multiply step to land. Here K tiles
+// of 32 go from global memory straight into LDS (global_load_lds_dwordx4: a
+// wave's 64 pieces land in 1 KB of LDS in lane order), PS stages deep: a
+// tile has PS - 1 multiply steps to land and takes no registers. A stage
+// holds 256 rows of A and 256 rows of B (the 192-wide tile loads 64 rows it
+// does not use) as 64-byte rows of four 16-byte pieces; piece q of row r
+// sits at position q ^ ((r >> 2) & 3), so the 16 rows of a fragment read
+// fall on distinct banks. Each step waits for this wave's loads of its tile
+// (vmcnt) and for its previous LDS reads, meets the other waves at a bare
+// s_barrier (a workgroup fence would also wait for the loads of the later
+// tiles), issues the loads of the tile PS - 1 steps ahead into the stage
+// the previous step read, and multiplies. Rows past M or N are loaded from
+// the last valid row and their results are not stored; the launcher checks
+// that every K range is a whole number of tiles and that zero padding cuts
+// no block.
+constexpr int PS = 4;    // LDS stages
+constexpr int PK = 32;   // K per stage
+
+#define MONARCH_GPTR(p) ((__attribute__((address_space(1))) void*)(p))
+#define MONARCH_LPTR(p) ((__attribute__((address_space(3))) void*)(p))
+// s_waitcnt: vector memory count <= n, LDS count 0, export count untouched
+#define MONARCH_WAIT_VM_LDS(n) (((n) & 0xF) | (((n) >> 4) << 14) | (0x7 << 4))
+
+// zero-padding limits are allowed when they cut no block (the last block's
+// valid range still covers K, or N)
+bool pipe_ok(const GemmArgs& a) {
+  const int64_t last = a.nblk - 1;
+  const bool kfull = a.k_lim < 0 || a.k_lim - last * a.k_lim_bs >= a.K;
+  const bool nfull = a.n_lim < 0 || a.n_lim - last * a.n_lim_bs >= a.N;
+  return a.K % PK == 0 && kfull && nfull && (!a.partial || a.k_chunk % PK == 0);
+}
+
+template <int FN>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2)))
+void pipe_gemm_kernel(GemmArgs p, int64_t m_tiles, int64_t n_tiles, int remap) {
+  constexpr int WM = 2, WN = 4, FM = 8;
+  constexpr int TM = WM * FM * 16, TN = WN * FN * 16;
+  static_assert(TM == 256 && TN <= 256, "tile");
+  __shared__ __attribute__((aligned(16))) u32x4 lds[PS][2][256 * 4];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / WN, wn = wave % WN;
+  const int l15 = lane & 15, lh = lane >> 4;
+
+  int64_t t = blockIdx.x;
+  if (remap) t = (t & 7) * (gridDim.x >> 3) + (t >> 3);
+  const int64_t blk = t % p.nblk;
+  t /= p.nblk;
+  const int64_t nt = t % n_tiles;
+  t /= n_tiles;
+  const int64_t mt = t % m_tiles;
+  const int64_t split = t / m_tiles;
+  const int64_t kb = p.partial ? split * p.k_chunk : 0;
+  const int64_t ke = p.partial ? (kb + p.k_chunk < p.K ? kb + p.k_chunk : p.K) : p.K;
+  const int64_t i0 = mt * TM, j0 = nt * TN;
+
+  // load instruction i of this wave: tile rows (2*wave + i)*16 + lane/4,
+  // LDS position lane % 4, global piece (lane % 4) ^ ((row >> 2) & 3)
+  const uint16_t* ap[2];
+  const uint16_t* bp[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int r = (2 * wave + i) * 16 + (lane >> 2);
+    const int q = (lane & 3) ^ ((r >> 2) & 3);
+    const int64_t ar = i0 + r < p.M ? i0 + r : p.M - 1;
+    const int64_t br = j0 + r < p.N ? j0 + r : p.N - 1;
+    ap[i] = static_cast<const uint16_t*>(p.A) + blk * p.a_sb + ar * p.a_si + 8 * q;
+    bp[i] = static_cast<const uint16_t*>(p.B) + blk * p.b_sb +
+            (p.nsplit > 0 ? (br / p.nsplit) * p.b_sj_hi + (br % p.nsplit) * p.b_sj : br * p.b_sj) +
+            8 * q;
+  }
+
+  f32x4 acc[FM][FN];
+#pragma unroll
+  for (int mi = 0; mi < FM; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < FN; ++ni) acc[mi][ni] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  const int64_t nsteps = kb < ke ? (ke - kb) / PK : 0;
+  auto issue = [&](int64_t s) {
+    const int st = static_cast<int>(s % PS);
+    const int64_t k0 = kb + s * PK;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      __builtin_amdgcn_global_load_lds(MONARCH_GPTR(ap[i] + k0),
+                                       MONARCH_LPTR(&lds[st][0][(2 * wave + i) * 64]), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(MONARCH_GPTR(bp[i] + k0),
+                                       MONARCH_LPTR(&lds[st][1][(2 * wave + i) * 64]), 16, 0, 0);
+    }
+  };
+  // fragment rows: (tile base multiple of 16) + l15, so the swizzle is lane-constant
+  const int sw = lh ^ ((l15 >> 2) & 3);
+  auto mult = [&](const u32x4* as, const u32x4* bs) {
+    bf16x8 fa[FM], fb[FN];
+#pragma unroll
+    for (int mi = 0; mi < FM; ++mi) {
+      const u32x4 v = as[((wm * FM + mi) * 16 + l15) * 4 + sw];
+      __builtin_memcpy(&fa[mi], &v, sizeof(v));
+    }
 #pragma unroll
     for (int ni = 0; ni < FN; ++ni) {
-      const int64_t jb = j0 + (wn * FN + ni) * 16 + (l15 & ~3);
-      const int64_t cpos = cblk + (p.nsplit > 0 ? col_off(jb, p.nsplit, p.c_sj_hi, 1) : jb);
-      T* c = static_cast<T*>(p.C) + rb + u * p.c_si + cpos;
-#pragma unroll
-      for (int mi = 0; mi < FM; ++mi)
-        Vec4<T>::store(c, mi * 16 * p.c_si, quad_transpose4(acc[mi][ni], u));
+      const u32x4 v = bs[((wn * FN + ni) * 16 + l15) * 4 + sw];
+      __builtin_memcpy(&fb[ni], &v, sizeof(v));
     }
-    return;
-  }
-  if (p.partial && i0 + TM <= p.M && j0 + TN <= p.N) {
-    float* P = p.partial + ((split * p.nblk + blk) * p.M + i0 + wm * FM * 16 + 4 * lh) * p.N + j0 +
-               wn * FN * 16 + l15;
-#pragma unroll
-    for (int ni = 0; ni < FN; ++ni)
-#pragma unroll
-      for (int mi = 0; mi < FM; ++mi)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) P[(mi * 16 + v) * p.N + ni * 16] = acc[mi][ni][v];
-    return;
-  }
-  if (plain) {
-#pragma unroll
-    for (int ni = 0; ni < FN; ++ni) {
-      const int64_t j = j0 + (wn * FN + ni) * 16 + l15;
-      T* c = static_cast<T*>(p.C) + rb + cblk + col_off(j, p.nsplit, p.c_sj_hi, p.c_sj);
-#pragma unroll
-      for (int mi = 0; mi < FM; ++mi)
-#pragma unroll
-        for (int v = 0; v < 4; ++v) Io<T>::store(c, (mi * 16 + v) * p.c_si, acc[mi][ni][v]);
-    }
-    return;
-  }
-  if (p.cvec) {
-    // a 4x4 transpose within each quad of lanes (columns 4c..4c+3) leaves
-    // lane 4c+u with row 4*(lane/16)+u, columns 4c..4c+3: one 4-element
-    // load/store per row instead of four single elements. In rotation r
-    // lane u sends its row (u - r) & 3 and receives, by a DPP quad
-    // permutation (lane u reads lane (u + r) & 3), row u of column
-    // (u + r) & 3; the selections are two-level on the bits of a
-    // loop-invariant lane index, so they stay selects, not branches.
-    const int u = l15 & 3;
-#pragma unroll
-    for (int ni = 0; ni < FN; ++ni) {
-      const int64_t jb = j0 + (wn * FN + ni) * 16 + (l15 & ~3);
-      // with a column split the four columns stay within one piece
-      const int64_t cpos = cblk + (p.nsplit > 0 ? col_off(jb, p.nsplit, p.c_sj_hi, 1) : jb);
-#pragma unroll
-      for (int mi = 0; mi < FM; ++mi) {
-        f32x4 o = quad_transpose4(acc[mi][ni], u);
-        const int64_t i = i0 + (wm * FM + mi) * 16 + 4 * lh + u;
-        if (i < p.M && jb < p.N && (p.c_cols < 0 || cpos < p.c_cols)) {
-          const int64_t off = i * p.c_si + cpos;
-          if (p.accum) o += Vec4<T>::load(p.C, off);
-          if (p.bias) o += Vec4<T>::load(p.bias, cpos);
-          if (p.relu) {
-#pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = o[e] > 0.f ? o[e] : 0.f;
-          }
-          Vec4<T>::store(p.C, off, o);
-        }
-      }
-    }
-    return;
-  }
-#pragma unroll
-  for (int ni = 0; ni < FN; ++ni) {
-    const int64_t j = j0 + (wn * FN + ni) * 16 + l15;
-    const int64_t cpos = cblk + col_off(j, p.nsplit, p.c_sj_hi, p.c_sj);   // in-row offset
 #pragma unroll
     for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int64_t i = i0 + (wm * FM + mi) * 16 + 4 * lh + v;
-        if (i < p.M && j < p.N) {
-          float val = acc[mi][ni][v];
-          if (p.partial) {
-            p.partial[((split * p.nblk + blk) * p.M + i) * p.N + j] = val;
-          } else if (p.c_cols < 0 || cpos < p.c_cols) {
-            if (p.accum) val += Io<T>::load(p.C, i * p.c_si + cpos);
-            if (p.bias) val += Io<T>::load(p.bias, cpos);
-            if (p.relu) val = val > 0.f ? val : 0.f;
-            Io<T>::store(p.C, i * p.c_si + cpos, val);
-          }
+      for (int ni = 0; ni < FN; ++ni)
+        acc[mi][ni] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[mi], fb[ni], acc[mi][ni], 0, 0, 0);
+  };
+
+  for (int64_t s = 0; s < PS - 1 && s < nsteps; ++s) issue(s);
+  for (int64_t s = 0; s < nsteps; ++s) {
+    // tiles issued after tile s (four loads each per wave)
+    const int64_t later = nsteps - 1 - s < PS - 2 ? nsteps - 1 - s : PS - 2;
+    asm volatile("" ::: "memory");
+    if (later >= 2)
+      __builtin_amdgcn_s_waitcnt(MONARCH_WAIT_VM_LDS(8));
+    else if (later == 1)
+      __builtin_amdgcn_s_waitcnt(MONARCH_WAIT_VM_LDS(4));
+    else
+      __builtin_amdgcn_s_waitcnt(MONARCH_WAIT_VM_LDS(0));
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    if (s + PS - 1 < nsteps) issue(s + PS - 1);
+    const int st = static_cast<int>(s % PS);
+    mult(lds[st][0], lds[st][1]);
+  }
+  // A whole tile of contiguous bf16 output (columns unit-stride, or runs of
+  // a column split that are whole 16-byte pieces) leaves through LDS: the
+  // stages are free after the last step and hold the 256 x TN tile. Written
+  // straight from the MFMA layout, a store instruction would cover 16 rows
+  // with 32 bytes each; from LDS every instruction writes two rows' whole
+  // 2*TN-byte segments. Tile row r keeps its 16-byte chunk c at c ^ (r & 7).
+  const bool staged = !p.partial && !p.accum && p.c_cols < 0 && p.c_sj == 1 &&
+                      i0 + TM <= p.M && j0 + TN <= p.N && p.c_si % 8 == 0 && p.c_sb % 8 == 0 &&
+                      (p.nsplit == 0 || (p.nsplit % 8 == 0 && p.c_sj_hi % 8 == 0)) &&
+                      (reinterpret_cast<uintptr_t>(p.C) & 15) == 0;
+  if (!staged) {
+    write_tile<uint16_t, WM, WN, FM, FN>(p, acc, blk, split, i0, j0, wm, wn, l15, lh);
+    return;
+  }
+  __syncthreads();
+  uint16_t* ct = reinterpret_cast<uint16_t*>(&lds[0][0][0]);
+  constexpr int NCH = TN / 8;   // 16-byte chunks per tile row
+  {
+    const int u = l15 & 3;
+#pragma unroll
+    for (int ni = 0; ni < FN; ++ni) {
+      const int jc = (wn * FN + ni) * 16 + (l15 & ~3);   // first of this lane's 4 columns
+      const f32x4 bv = p.bias ? Vec4<uint16_t>::load(p.bias, blk * p.c_sb +
+                                                    (p.nsplit > 0 ? col_off(j0 + jc, p.nsplit, p.c_sj_hi, 1) : j0 + jc))
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int mi = 0; mi < FM; ++mi) {
+        f32x4 o = quad_transpose4(acc[mi][ni], u) + bv;
+        if (p.relu) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = o[e] > 0.f ? o[e] : 0.f;
         }
+        const int r = (wm * FM + mi) * 16 + 4 * lh + u;
+        *reinterpret_cast<u32x2*>(&ct[r * TN + (((jc >> 3) ^ (r & 7)) << 3) + (jc & 7)]) =
+            u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
       }
+    }
+  }
+  __syncthreads();
+  uint16_t* C = static_cast<uint16_t*>(p.C) + blk * p.c_sb;
+#pragma unroll 4
+  for (int id = tid; id < TM * NCH; id += 512) {
+    const int r = id / NCH, c = id - r * NCH;
+    const int64_t j = j0 + 8 * c;
+    const int64_t col = p.nsplit > 0 ? col_off(j, p.nsplit, p.c_sj_hi, 1) : j;
+    *reinterpret_cast<u32x4*>(C + (i0 + r) * p.c_si + col) =
+        *reinterpret_cast<const u32x4*>(&ct[r * TN + ((c ^ (r & 7)) << 3)]);
   }
 }
+#undef MONARCH_GPTR
+#undef MONARCH_LPTR
+#undef MONARCH_WAIT_VM_LDS
 
 // keep v where m > 0 (ReLU derivative), element-wise on a 16-byte piece
 template <typename T>
@@ -726,6 +937,12 @@ hipError_t launch_modes(const GemmArgs& a, Shape sh, dim3 g, int64_t mt, int64_t
                      dim3(WM * WN * 64), 0, s, a, mt, nt, remap, 1, 1)
   switch (sh) {
     case S256x256:
+      if constexpr (std::is_same<T, uint16_t>::value && AM == 1 && BMD == 1) {
+        if (avec && bvec && pipe_ok(a)) {
+          hipLaunchKernelGGL(pipe_gemm_kernel<4>, g, dim3(512), 0, s, a, mt, nt, remap);
+          break;
+        }
+      }
       if constexpr (std::is_same<T, uint16_t>::value) {
         MONARCH_TILED_VEC(2, 4, 8, 4);
       } else {
@@ -733,6 +950,12 @@ hipError_t launch_modes(const GemmArgs& a, Shape sh, dim3 g, int64_t mt, int64_t
       }
       break;
     case S256x192:
+      if constexpr (std::is_same<T, uint16_t>::value && AM == 1 && BMD == 1) {
+        if (avec && bvec && pipe_ok(a)) {
+          hipLaunchKernelGGL(pipe_gemm_kernel<3>, g, dim3(512), 0, s, a, mt, nt, remap);
+          break;
+        }
+      }
       if constexpr (std::is_same<T, uint16_t>::value) {
         MONARCH_TILED_VEC(2, 4, 8, 3);
       } else {
