@@ -379,6 +379,63 @@ __device__ __forceinline__ void write_tile(const GemmArgs& p, const f32x4 (&acc)
   }
 }
 
+// A whole tile of contiguous bf16 output (columns unit-stride, or runs of a
+// column split that are whole 16-byte pieces) can leave through LDS once the
+// K loop is done (ct: TM x TN elements of free LDS). Written straight from the
+// MFMA layout, a store instruction covers 16 rows with 32 bytes each; from LDS
+// every instruction writes whole 2*TN-byte row segments, and those whole
+// lines leave with non-temporal stores (9% faster on the GPT-2 stage-1
+// forward; the strided two-byte stores of the other paths need L2 to merge
+// the blocks' lines and stay plain). Tile row r keeps its 16-byte chunk c at
+// c ^ (r & 7). Returns false, having done nothing, when the tile does not
+// qualify; every thread of the workgroup must call it.
+template <int WM, int WN, int FM, int FN>
+__device__ __forceinline__ bool write_tile_staged(const GemmArgs& p, const f32x4 (&acc)[FM][FN],
+                                                  int64_t blk, int64_t i0, int64_t j0, int wm,
+                                                  int wn, int l15, int lh, int tid, uint16_t* ct) {
+  constexpr int TM = WM * FM * 16, TN = WN * FN * 16, NT = WM * WN * 64;
+  static_assert(TN % 64 == 0, "the chunk swizzle needs whole groups of 8 chunks");
+  const bool staged = !p.partial && !p.accum && p.c_cols < 0 && p.c_sj == 1 &&
+                      i0 + TM <= p.M && j0 + TN <= p.N && p.c_si % 8 == 0 && p.c_sb % 8 == 0 &&
+                      (p.nsplit == 0 || (p.nsplit % 8 == 0 && p.c_sj_hi % 8 == 0)) &&
+                      (reinterpret_cast<uintptr_t>(p.C) & 15) == 0;
+  if (!staged) return false;
+  __syncthreads();
+  constexpr int NCH = TN / 8;   // 16-byte chunks per tile row
+  {
+    const int u = l15 & 3;
+#pragma unroll
+    for (int ni = 0; ni < FN; ++ni) {
+      const int jc = (wn * FN + ni) * 16 + (l15 & ~3);   // first of this lane's 4 columns
+      const f32x4 bv = p.bias ? Vec4<uint16_t>::load(p.bias, blk * p.c_sb +
+                                                    (p.nsplit > 0 ? col_off(j0 + jc, p.nsplit, p.c_sj_hi, 1) : j0 + jc))
+                              : f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int mi = 0; mi < FM; ++mi) {
+        f32x4 o = quad_transpose4(acc[mi][ni], u) + bv;
+        if (p.relu) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[e] = o[e] > 0.f ? o[e] : 0.f;
+        }
+        const int r = (wm * FM + mi) * 16 + 4 * lh + u;
+        *reinterpret_cast<u32x2*>(&ct[r * TN + (((jc >> 3) ^ (r & 7)) << 3) + (jc & 7)]) =
+            u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
+      }
+    }
+  }
+  __syncthreads();
+  uint16_t* C = static_cast<uint16_t*>(p.C) + blk * p.c_sb;
+#pragma unroll 4
+  for (int id = tid; id < TM * NCH; id += NT) {
+    const int r = id / NCH, c = id - r * NCH;
+    const int64_t j = j0 + 8 * c;
+    const int64_t col = p.nsplit > 0 ? col_off(j, p.nsplit, p.c_sj_hi, 1) : j;
+    __builtin_nontemporal_store(*reinterpret_cast<const u32x4*>(&ct[r * TN + ((c ^ (r & 7)) << 3)]),
+                                reinterpret_cast<u32x4*>(C + (i0 + r) * p.c_si + col));
+  }
+  return true;
+}
+
 template <typename T, int AM, int BMD, int WM, int WN, int FM, int FN, bool EW>
 __global__ __launch_bounds__(WM * WN * 64) __attribute__((amdgpu_waves_per_eu(2)))
 void tiled_gemm_kernel(GemmArgs p, int64_t m_tiles,
@@ -393,8 +450,11 @@ void tiled_gemm_kernel(GemmArgs p, int64_t m_tiles,
   constexpr int SL = EW ? 1 : kSlots<TM>, LB = kBufs<TM, TN>;
   using TA = Tile<T, AM, TM, EW, SL, TT>;
   using TB = Tile<T, BMD, TN, EW, SL, TT>;
-  __shared__ __attribute__((aligned(16))) T As[LB][TA::LDS];
-  __shared__ __attribute__((aligned(16))) T Bs[LB][TB::LDS];
+  // one LDS array for both operands' buffers, so that a bf16 output tile
+  // can be staged in it after the K loop
+  __shared__ __attribute__((aligned(16))) T smem[LB * (TA::LDS + TB::LDS)];
+  T (*As)[TA::LDS] = reinterpret_cast<T (*)[TA::LDS]>(smem);
+  T (*Bs)[TB::LDS] = reinterpret_cast<T (*)[TB::LDS]>(smem + LB * TA::LDS);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / WN, wn = wave % WN;
   const int l15 = lane & 15, lh = lane >> 4;
@@ -571,6 +631,9 @@ void tiled_gemm_kernel(GemmArgs p, int64_t m_tiles,
     }
   }
 
+  if constexpr (C::kBf16 && TM >= 128 && TN % 64 == 0 && LB * (TA::LDS + TB::LDS) >= TM * TN) {
+    if (write_tile_staged<WM, WN, FM, FN>(p, acc, blk, i0, j0, wm, wn, l15, lh, tid, smem)) return;
+  }
   write_tile<T, WM, WN, FM, FN>(p, acc, blk, split, i0, j0, wm, wn, l15, lh);
 }
 
@@ -708,54 +771,9 @@ void pipe_gemm_kernel(GemmArgs p, int64_t m_tiles, int64_t n_tiles, int remap) {
     const int st = static_cast<int>(s % PS);
     mult(lds[st][0], lds[st][1]);
   }
-  // A whole tile of contiguous bf16 output (columns unit-stride, or runs of
-  // a column split that are whole 16-byte pieces) leaves through LDS: the
-  // stages are free after the last step and hold the 256 x TN tile. Written
-  // straight from the MFMA layout, a store instruction would cover 16 rows
-  // with 32 bytes each; from LDS every instruction writes two rows' whole
-  // 2*TN-byte segments. Tile row r keeps its 16-byte chunk c at c ^ (r & 7).
-  const bool staged = !p.partial && !p.accum && p.c_cols < 0 && p.c_sj == 1 &&
-                      i0 + TM <= p.M && j0 + TN <= p.N && p.c_si % 8 == 0 && p.c_sb % 8 == 0 &&
-                      (p.nsplit == 0 || (p.nsplit % 8 == 0 && p.c_sj_hi % 8 == 0)) &&
-                      (reinterpret_cast<uintptr_t>(p.C) & 15) == 0;
-  if (!staged) {
+  if (!write_tile_staged<WM, WN, FM, FN>(p, acc, blk, i0, j0, wm, wn, l15, lh, tid,
+                                         reinterpret_cast<uint16_t*>(&lds[0][0][0])))
     write_tile<uint16_t, WM, WN, FM, FN>(p, acc, blk, split, i0, j0, wm, wn, l15, lh);
-    return;
-  }
-  __syncthreads();
-  uint16_t* ct = reinterpret_cast<uint16_t*>(&lds[0][0][0]);
-  constexpr int NCH = TN / 8;   // 16-byte chunks per tile row
-  {
-    const int u = l15 & 3;
-#pragma unroll
-    for (int ni = 0; ni < FN; ++ni) {
-      const int jc = (wn * FN + ni) * 16 + (l15 & ~3);   // first of this lane's 4 columns
-      const f32x4 bv = p.bias ? Vec4<uint16_t>::load(p.bias, blk * p.c_sb +
-                                                    (p.nsplit > 0 ? col_off(j0 + jc, p.nsplit, p.c_sj_hi, 1) : j0 + jc))
-                              : f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int mi = 0; mi < FM; ++mi) {
-        f32x4 o = quad_transpose4(acc[mi][ni], u) + bv;
-        if (p.relu) {
-#pragma unroll
-          for (int e = 0; e < 4; ++e) o[e] = o[e] > 0.f ? o[e] : 0.f;
-        }
-        const int r = (wm * FM + mi) * 16 + 4 * lh + u;
-        *reinterpret_cast<u32x2*>(&ct[r * TN + (((jc >> 3) ^ (r & 7)) << 3) + (jc & 7)]) =
-            u32x2{pack_bf16x2(o[0], o[1]), pack_bf16x2(o[2], o[3])};
-      }
-    }
-  }
-  __syncthreads();
-  uint16_t* C = static_cast<uint16_t*>(p.C) + blk * p.c_sb;
-#pragma unroll 4
-  for (int id = tid; id < TM * NCH; id += 512) {
-    const int r = id / NCH, c = id - r * NCH;
-    const int64_t j = j0 + 8 * c;
-    const int64_t col = p.nsplit > 0 ? col_off(j, p.nsplit, p.c_sj_hi, 1) : j;
-    *reinterpret_cast<u32x4*>(C + (i0 + r) * p.c_si + col) =
-        *reinterpret_cast<const u32x4*>(&ct[r * TN + ((c ^ (r & 7)) << 3)]);
-  }
 }
 #undef MONARCH_GPTR
 #undef MONARCH_LPTR
