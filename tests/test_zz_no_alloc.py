@@ -66,7 +66,7 @@ def test_noalloc_matches_monarch_bwd(fi, fo, nb1, nb2, dt, act, batches, path):
 
 
 def test_noalloc_matches_oracle():
-    # the same call checked against the fp64 oracle at the benchmark spec's bound
+    # the same call checked against the fp64 oracle at the bf16 bound (2e-2)
     fi, fo, nb, batch = 1024, 1024, 32, 600
     x, w1, w2, dy, y, z = _inputs(fi, fo, nb, nb, torch.bfloat16, B.ACT_NONE, batch, seed=77)
     got = _noalloc(dy, x, w1, w2, z, None, fi, fo, nb, nb, B.ACT_NONE)
