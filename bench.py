@@ -120,6 +120,28 @@ def measure_stream_copy(torch, dev, reps: int = 10, nbytes: int = 1 << 30) -> fl
     return 2.0 * nbytes / (ms * 1e-3) / 1e9
 
 
+def measure_gemm_peak(torch, dev, dtype: str, reps: int = 10, n: int = 8192) -> float:
+    """TFLOP/s of a large square GEMM (n x n x n) through torch's library GEMM
+    (hipBLASLt) in the workload's dtype, timed with HIP events: the measured
+    matrix-core reference beside the spec peak."""
+    tdt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    a = torch.randn((n, n), device=dev, dtype=torch.float32).to(tdt)
+    b = torch.randn((n, n), device=dev, dtype=torch.float32).to(tdt)
+    c = torch.empty((n, n), device=dev, dtype=tdt)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        torch.matmul(a, b, out=c)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        torch.matmul(a, b, out=c)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / reps
+    del a, b, c
+    return 2.0 * n ** 3 / (ms * 1e-3) / 1e12
+
+
 def load_traffic(kernel: str, workload: str, digest: str):
     """HBM bytes per launch from committed rocprofv3 --pmc summaries, or None
     when absent or taken on other kernel sources."""
@@ -737,12 +759,18 @@ def main() -> int:
             dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
+    # measured matrix-core reference: an 8192^3 GEMM in the workload's dtype
+    gemm_tflops = measure_gemm_peak(torch, dev, w.dtype)
     step_roofline["measured_peak_gbs"] = round(copy_gbs, 1)
+    step_roofline["measured_mfma_peak_tflops"] = round(gemm_tflops, 1)
     step_roofline["frac_measured"] = round(
-        max(flops / (mfma_peak * 1e12), b2p / (copy_gbs * 1e9)) * 1e3 / ms_per_step, 4)
+        max(flops / (gemm_tflops * 1e12), b2p / (copy_gbs * 1e9)) * 1e3 / ms_per_step, 4)
     if roofline.get("bound") == "hbm":
         roofline["measured_peak"] = round(copy_gbs, 1)
         roofline["frac_measured"] = round(roofline["achieved"] / copy_gbs, 4)
+    else:
+        roofline["measured_peak"] = round(gemm_tflops, 1)
+        roofline["frac_measured"] = round(roofline["achieved"] / gemm_tflops, 4)
 
     dense = None
     if not args.no_dense:
