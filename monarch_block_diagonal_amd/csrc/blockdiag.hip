@@ -1,24 +1,35 @@
-// Block-diagonal products with 256 x 256 weight blocks in bf16: the two
-// block-sparse terms of the DYAD-style layer (DYAD page, abstract) once
-// term B's operands are in block-major order, each multiplying nb
-// independent 256-feature segments of a row by one dense block:
-//   C[b, blk*cs + j] = sum_k A[b, blk*as + k] W_blk(k, j),   j, k < 256,
-// with W_blk(k, j) = W[blk][j][k] (the forward: rows of the stored block are
-// output features) or W[blk][k][j] (the data gradient: its transpose).
+// Block-diagonal products in bf16 whose weight blocks fit a CU's registers
+// when split into 256-column slices, with K = 192 or 256 per block:
+//   C[b, blk*cs + col(j)] = sum_k A[b, blk*as + k] W_blk(k, j),   k < K,
+// with W_blk(k, j) = W[blk][row(j)][k] (rows of the stored block are output
+// features) or, for 256 x 256 blocks only, W[blk][k][j] (the data gradient:
+// its transpose). row(j) and col(j) follow the optional column split of
+// GemmArgs: the stage-1 forward of a Monarch layer (Definition C.3 thread of
+// the scatterbrain issues page) stores block r's output k = tt*b2 + g at
+// stage 2's position g*q2i + r*n1 + tt, so its weight rows are gathered in
+// that order and its outputs leave as runs of n1 columns. Two users:
+//  * the two block-sparse terms of the DYAD-style layer (DYAD page,
+//    abstract), 256 x 256 blocks once term B's operands are block-major;
+//  * the stage-1 forward of Monarch layers with q1i = 192 or 256 and q1o a
+//    multiple of 256, e.g. the GPT-2 FFN up-projection 768 -> 3072 with 4
+//    blocks (768 x 192 blocks, taken as three 256-column slices).
 //
-// At K = N = 256 a product moves 1 KB per row (512 bytes in, 512 out) for
-// 64 Ki multiply-adds: 128 flop per byte, under the bf16 MFMA ridge of about
-// 310 (2.5 PFLOP/s over 8 TB/s), so it is bound by HBM. The generic tiled GEMM covers it with 256 x 256
-// tiles whose eight waves fill a CU's registers: a workgroup then loads,
-// multiplies and stores in turn (4 K steps) with nothing to overlap.
-// Here a workgroup owns one block and a row range:
-//  * each of its eight waves keeps a 32-column slice of the weight block in
-//    VGPRs (64 registers) for the whole launch;
+// A product moves (K + N) * 2 bytes per row for K * N multiply-adds: at
+// K = 192..256 that is 96..128 flop per byte, under the bf16 MFMA ridge of
+// about 310 (2.5 PFLOP/s over 8 TB/s), so it is bound by HBM. The generic
+// tiled GEMM covers it with 256 x 256 tiles whose eight waves fill a CU's
+// registers: a workgroup then loads, multiplies and stores in turn (6 or 8
+// K steps) with nothing to overlap. Here a workgroup owns one block, one
+// 256-column slice of it and a row range:
+//  * each of its eight waves keeps a 32-column piece of the slice in VGPRs
+//    (K/4 registers) for the whole launch;
 //  * 32-row tiles of A pass through LDS (double-buffered, loaded one tile
-//    ahead), results are staged in LDS and leave as whole 512-byte row
-//    segments, one barrier per tile;
-//  * 66 KB of LDS and at most 128 VGPRs per lane, so two workgroups share a
+//    ahead), results are staged in LDS and leave as 16-byte pieces of whole
+//    512-byte row segments (or of the split's runs), one barrier per tile;
+//  * at most 66 KB of LDS and 128 VGPRs per lane, so two workgroups share a
 //    CU and one's loads overlap the other's stores;
+//  * the slices of one block read the same A rows: they are given
+//    consecutive ids on one XCD, so those rows come from HBM once;
 //  * activations and results stream with non-temporal loads and stores
 //    (each is touched once per launch, far beyond the L2).
 // MFMA v_mfma_f32_16x16x32_bf16 computes Cᵀ[j x b] = Wᵀ-slice[j x k] · Aᵀ[k x b]
@@ -31,40 +42,60 @@
 namespace monarch {
 namespace {
 
-constexpr int BQ = 256;           // block size (N = K)
+constexpr int BQ = 256;           // columns per slice; block size of the transposed form
 constexpr int BT = 32;            // rows per tile
-constexpr int BP = BQ + 8;        // LDS pitch (elements) of a [row][feature] tile
+constexpr int BP = BQ + 8;        // LDS pitch (elements) of a [row][column] result tile
 constexpr int kBdThreads = 512;
 
 __device__ __forceinline__ bf16x8 bd_frag(const uint16_t* p) {
   return as_bf16x8(*reinterpret_cast<const u16x8*>(p));
 }
 
-template <bool TRANS>
+// Column offsets under the optional split (GemmArgs): j*lo, or
+// (j / ns)*hi + (j % ns)*lo when ns > 0.
+struct Split {
+  int64_t ns, hi, lo;
+  __device__ __forceinline__ int64_t operator()(int64_t j) const {
+    return ns > 0 ? (j / ns) * hi + (j % ns) * lo : j * lo;
+  }
+};
+
+template <bool TRANS, int KB>
 __global__ __launch_bounds__(kBdThreads) __attribute__((amdgpu_waves_per_eu(4)))
-void bd256_kernel(const uint16_t* __restrict__ A, int64_t a_sb, int64_t a_si,
-                  const uint16_t* __restrict__ W, int64_t w_sb, uint16_t* __restrict__ C,
-                  int64_t c_sb, int64_t c_si, int64_t rows, int64_t rows_per, int64_t nblk) {
+void bd_kernel(const uint16_t* __restrict__ A, int64_t a_sb, int64_t a_si,
+               const uint16_t* __restrict__ W, int64_t w_sb, Split wrow,
+               uint16_t* __restrict__ C, int64_t c_sb, int64_t c_si, Split ccol,
+               int64_t rows, int64_t rows_per, int64_t nblk, int nslices, int remap) {
+  static_assert(KB == 192 || KB == 256, "K per block");
+  static_assert(!TRANS || KB == BQ, "the transposed form takes 256 x 256 blocks");
+  constexpr int KP = KB + 8;               // LDS pitch of a [row][k] operand tile
+  constexpr int KS = KB / 32;              // MFMA K steps
+  constexpr int APR = KB / 8;              // 16-byte pieces per operand row
+  constexpr int NA = (BT * APR + kBdThreads - 1) / kBdThreads;   // pieces per thread
   // [A tile 0][A tile 1][C tile 0][C tile 1]; in the prologue of the
   // transposed form, 64 rows of the weight block, transposed
-  __shared__ __attribute__((aligned(16))) uint16_t lds[4 * BT * BP];
-  const int64_t blk = blockIdx.x % nblk;
-  const int64_t r0 = static_cast<int64_t>(blockIdx.x / nblk) * rows_per;
+  __shared__ __attribute__((aligned(16))) uint16_t lds[2 * BT * KP + 2 * BT * BP];
+  int64_t logical = blockIdx.x;
+  if (remap) logical = (logical & 7) * (gridDim.x >> 3) + (logical >> 3);
+  const int64_t blk = logical % nblk;
+  const int64_t rest = logical / nblk;
+  const int64_t j0 = (rest % nslices) * BQ;
+  const int64_t r0 = (rest / nslices) * rows_per;
   const int64_t r1 = r0 + rows_per < rows ? r0 + rows_per : rows;
   if (r0 >= r1) return;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l15 = lane & 15, lh = lane >> 4;
 
-  // MFMA A operand: lane holds W_blk(k = 32ks + 8lh .. +7, j = 32w + 16mt + l15)
-  bf16x8 wf[2][8];
+  // MFMA A operand: lane holds W_blk(k = 32ks + 8lh .. +7, j = j0 + 32w + 16mt + l15)
+  bf16x8 wf[2][KS];
   const uint16_t* Wb = W + blk * w_sb;
 #pragma unroll
   for (int mt = 0; mt < 2; ++mt) {
-    const int j = 32 * w + 16 * mt + l15;
+    const int64_t jr = wrow(j0 + 32 * w + 16 * mt + l15);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       const int k = 32 * ks + 8 * lh;
-      if constexpr (!TRANS) wf[mt][ks] = bd_frag(Wb + j * BQ + k);
+      if constexpr (!TRANS) wf[mt][ks] = bd_frag(Wb + jr + k);
     }
   }
   if constexpr (TRANS) {
@@ -79,16 +110,16 @@ void bd256_kernel(const uint16_t* __restrict__ A, int64_t a_sb, int64_t a_si,
       u32x4 v[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int p = tid + kBdThreads * i, kl = p & 63, j0 = (p >> 6) * 8;
-        v[i] = *reinterpret_cast<const u32x4*>(Wb + (64 * h + kl) * BQ + j0);
+        const int p = tid + kBdThreads * i, kl = p & 63, jg = (p >> 6) * 8;
+        v[i] = *reinterpret_cast<const u32x4*>(Wb + (64 * h + kl) * BQ + jg);
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int p = tid + kBdThreads * i, kl = p & 63, j0 = (p >> 6) * 8;
+        const int p = tid + kBdThreads * i, kl = p & 63, jg = (p >> 6) * 8;
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          lds[(j0 + 2 * q) * TP + kl] = static_cast<uint16_t>(v[i][q] & 0xffffu);
-          lds[(j0 + 2 * q + 1) * TP + kl] = static_cast<uint16_t>(v[i][q] >> 16);
+          lds[(jg + 2 * q) * TP + kl] = static_cast<uint16_t>(v[i][q] & 0xffffu);
+          lds[(jg + 2 * q + 1) * TP + kl] = static_cast<uint16_t>(v[i][q] >> 16);
         }
       }
       __syncthreads();
@@ -102,26 +133,40 @@ void bd256_kernel(const uint16_t* __restrict__ A, int64_t a_sb, int64_t a_si,
     }
   }
 
-  // tile pieces: thread moves pieces tid and tid + 512 of a 32 x 256 tile,
-  // piece p = (row p / 32, features 8 * (p % 32) .. +7)
+  // operand pieces: thread moves pieces tid + 512i of a 32 x KB tile, piece
+  // p = (row p / APR, k 8 * (p % APR) .. +7); result pieces: tid and tid +
+  // 512 of a 32 x 256 tile, piece (row tid / 32 + 16i, columns 8 * (tid % 32) .. +7)
+  int arow[NA], acol[NA];
+  bool aon[NA];
+#pragma unroll
+  for (int i = 0; i < NA; ++i) {
+    const int pc = tid + kBdThreads * i;
+    // every piece is real when the tile divides evenly (K = 256)
+    aon[i] = (BT * APR) % kBdThreads == 0 || pc < BT * APR;
+    arow[i] = aon[i] ? pc / APR : 0;
+    acol[i] = aon[i] ? (pc % APR) * 8 : 0;
+  }
   const int prow = tid >> 5, pcol = (tid & 31) * 8;
-  const uint16_t* Ab = A + blk * a_sb + pcol;
-  uint16_t* Cb = C + blk * c_sb + pcol;
+  const uint16_t* Ab = A + blk * a_sb;
+  // the 8 columns of a result piece lie in one run of the split
+  uint16_t* Cb = C + blk * c_sb + ccol(j0 + pcol);
   const int64_t ntiles = (r1 - r0 + BT - 1) / BT;
-  u32x4 pre[2];
+  u32x4 pre[NA];
   auto gload = [&](int64_t t) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      int64_t row = r0 + t * BT + prow + 16 * i;
+    for (int i = 0; i < NA; ++i) {
+      if (!aon[i]) continue;
+      int64_t row = r0 + t * BT + arow[i];
       row = row < r1 ? row : r1 - 1;
-      pre[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Ab + row * a_si));
+      pre[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(Ab + row * a_si + acol[i]));
     }
   };
   auto lstore = [&](uint16_t* x) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<u32x4*>(&x[(prow + 16 * i) * BP + pcol]) = pre[i];
+    for (int i = 0; i < NA; ++i)
+      if (aon[i]) *reinterpret_cast<u32x4*>(&x[arow[i] * KP + acol[i]]) = pre[i];
   };
+  uint16_t* const cst = lds + 2 * BT * KP;   // result tiles
 
   gload(0);
   lstore(lds);
@@ -129,25 +174,25 @@ void bd256_kernel(const uint16_t* __restrict__ A, int64_t a_sb, int64_t a_si,
   __syncthreads();
   for (int64_t t = 0; t < ntiles; ++t) {
     const int s = static_cast<int>(t & 1);
-    const uint16_t* x = lds + s * (BT * BP);
+    const uint16_t* x = lds + s * (BT * KP);
     f32x4 acc[2][2];
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
       for (int nt = 0; nt < 2; ++nt) acc[mt][nt] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
+    for (int ks = 0; ks < KS; ++ks) {
       bf16x8 fb[2];
 #pragma unroll
-      for (int nt = 0; nt < 2; ++nt) fb[nt] = bd_frag(&x[(16 * nt + l15) * BP + 32 * ks + 8 * lh]);
+      for (int nt = 0; nt < 2; ++nt) fb[nt] = bd_frag(&x[(16 * nt + l15) * KP + 32 * ks + 8 * lh]);
 #pragma unroll
       for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
         for (int nt = 0; nt < 2; ++nt)
           acc[mt][nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wf[mt][ks], fb[nt], acc[mt][nt], 0, 0, 0);
     }
-    // lane holds C[b = 16nt + l15][j = 32w + 16mt + 4lh .. +3]
-    uint16_t* y = lds + (2 + s) * (BT * BP);
+    // lane holds C[b = 16nt + l15][j = j0 + 32w + 16mt + 4lh .. +3]
+    uint16_t* y = cst + s * (BT * BP);
 #pragma unroll
     for (int mt = 0; mt < 2; ++mt)
 #pragma unroll
@@ -157,7 +202,7 @@ void bd256_kernel(const uint16_t* __restrict__ A, int64_t a_sb, int64_t a_si,
         *reinterpret_cast<u32x2*>(&y[(16 * nt + l15) * BP + 32 * w + 16 * mt + 4 * lh]) = v;
       }
     if (t + 1 < ntiles) {
-      lstore(lds + (1 - s) * (BT * BP));
+      lstore(lds + (1 - s) * (BT * KP));
       if (t + 2 < ntiles) gload(t + 2);
     }
     __syncthreads();
@@ -175,40 +220,63 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15) == 
 
 }  // namespace
 
-int bd256_mode(const GemmArgs& a, bool bf16) {
-  if (!bf16 || a.partial || a.accum || a.bias || a.relu || a.mask || a.nsplit > 0) return 0;
-  if (a.k_lim >= 0 || a.n_lim >= 0 || a.c_cols >= 0) return 0;
-  if (a.N != BQ || a.K != BQ || a.M <= 0 || a.nblk <= 0) return 0;
+int bd_mode(const GemmArgs& a, bool bf16) {
+  if (!bf16 || a.partial || a.accum || a.bias || a.relu || a.mask) return 0;
+  if (a.n_lim >= 0 || a.c_cols >= 0) return 0;
+  if (a.M <= 0 || a.nblk <= 0 || a.N <= 0 || a.N % BQ || (a.K != 192 && a.K != BQ)) return 0;
+  // zero padding is allowed when it cuts no block
+  if (a.k_lim >= 0 && a.k_lim - (a.nblk - 1) * a.k_lim_bs < a.K) return 0;
   if (a.a_sk != 1 || a.c_sj != 1) return 0;
   if (a.a_si % 8 || a.a_sb % 8 || a.c_si % 8 || a.c_sb % 8) return 0;
   if (a.a_si <= 0 || a.c_si <= 0 || a.a_sb < 0 || a.c_sb < 0 || a.b_sb < 0) return 0;
   if (!aligned16(a.A) || !aligned16(a.C)) return 0;
   if (!aligned16(a.B) || a.b_sb % 8) return 0;
-  if (a.b_sk == 1 && a.b_sj == BQ) return 1;
-  if (a.b_sk == BQ && a.b_sj == 1) return 2;
+  // a split keeps every 8-column piece (weights and results) in one run
+  if (a.nsplit > 0 && (a.nsplit % 8 || a.b_sj_hi < 0 || a.b_sj_hi % 8 || a.c_sj_hi < 0 ||
+                       a.c_sj_hi % 8))
+    return 0;
+  if (a.b_sk == 1 && a.b_sj > 0 && a.b_sj % 8 == 0) return a.K == BQ ? 1 : 3;
+  if (a.nsplit == 0 && a.K == BQ && a.N == BQ && a.b_sk == BQ && a.b_sj == 1) return 2;
   return 0;
 }
 
-hipError_t launch_bd256(const GemmArgs& a, int mode, hipStream_t s) {
+hipError_t launch_bd(const GemmArgs& a, int mode, hipStream_t s) {
   // about two workgroups per CU over the 256 CUs, each at least 4 tiles
+  const int64_t nslices = a.N / BQ;
+  const int64_t per_range = a.nblk * nslices;
   const int64_t tiles = (a.M + BT - 1) / BT;
-  int64_t ranges = (512 + a.nblk - 1) / a.nblk;
+  int64_t ranges = (512 + per_range - 1) / per_range;
   const int64_t rmax = (tiles + 3) / 4;
   if (ranges > rmax) ranges = rmax;
   if (ranges < 1) ranges = 1;
   const int64_t rows_per = (tiles + ranges - 1) / ranges * BT;
   ranges = (a.M + rows_per - 1) / rows_per;
-  const int64_t grid = ranges * a.nblk;
-  if (grid > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  const int64_t grid = ranges * per_range;
+  if (grid > 0x7fffffffLL || nslices > 0x7fffffffLL) return hipErrorInvalidConfiguration;
+  // the slices of a block share their A rows: one XCD for each run of ids
+  const int remap = nslices > 1 && grid % 8 == 0 ? 1 : 0;
   const auto* A = static_cast<const uint16_t*>(a.A);
   const auto* W = static_cast<const uint16_t*>(a.B);
   auto* C = static_cast<uint16_t*>(a.C);
-  if (mode == 1)
-    bd256_kernel<false><<<dim3(static_cast<unsigned>(grid)), dim3(kBdThreads), 0, s>>>(
-        A, a.a_sb, a.a_si, W, a.b_sb, C, a.c_sb, a.c_si, a.M, rows_per, a.nblk);
-  else
-    bd256_kernel<true><<<dim3(static_cast<unsigned>(grid)), dim3(kBdThreads), 0, s>>>(
-        A, a.a_sb, a.a_si, W, a.b_sb, C, a.c_sb, a.c_si, a.M, rows_per, a.nblk);
+  const Split wrow{a.nsplit, a.b_sj_hi, a.b_sj}, ccol{a.nsplit, a.c_sj_hi, 1};
+  const dim3 g(static_cast<unsigned>(grid)), blk(kBdThreads);
+  const int ns = static_cast<int>(nslices);
+  switch (mode) {
+    case 1:
+      bd_kernel<false, 256><<<g, blk, 0, s>>>(A, a.a_sb, a.a_si, W, a.b_sb, wrow, C, a.c_sb,
+                                               a.c_si, ccol, a.M, rows_per, a.nblk, ns, remap);
+      break;
+    case 2:
+      bd_kernel<true, 256><<<g, blk, 0, s>>>(A, a.a_sb, a.a_si, W, a.b_sb, wrow, C, a.c_sb,
+                                              a.c_si, ccol, a.M, rows_per, a.nblk, ns, remap);
+      break;
+    case 3:
+      bd_kernel<false, 192><<<g, blk, 0, s>>>(A, a.a_sb, a.a_si, W, a.b_sb, wrow, C, a.c_sb,
+                                               a.c_si, ccol, a.M, rows_per, a.nblk, ns, remap);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

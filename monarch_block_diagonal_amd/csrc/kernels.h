@@ -108,12 +108,15 @@ hipError_t launch_bias_partials(const void* dv, float* partial, int64_t rows, in
                                 int64_t chunks, int64_t out, int64_t b2, int64_t q2o, bool bf16,
                                 hipStream_t s);
 
-// bf16 block-diagonal products with 256 x 256 weight blocks (blockdiag.hip),
-// the form of both DYAD terms: bd256_mode returns 1 when W_blk(k, j) is
-// B[blk][j][k] (b_sk = 1, b_sj = 256), 2 when it is B[blk][k][j], and 0 when
-// the GemmArgs are not such a product (then launch_gemm's tiled kernel runs).
-int bd256_mode(const GemmArgs& a, bool bf16);
-hipError_t launch_bd256(const GemmArgs& a, int mode, hipStream_t s);
+// bf16 block-diagonal products with K = 192 or 256 per block and N a
+// multiple of 256, weights held in registers (blockdiag.hip): both DYAD
+// terms and the stage-1 forward at those block shapes. bd_mode returns 1
+// (K = 256) or 3 (K = 192) when W_blk(k, j) is B[blk][row(j)][k] (b_sk = 1,
+// rows under the optional column split), 2 when it is B[blk][k][j] with
+// K = N = 256, and 0 when the GemmArgs are not such a product (then
+// launch_gemm's tiled kernels run).
+int bd_mode(const GemmArgs& a, bool bf16);
+hipError_t launch_bd(const GemmArgs& a, int mode, hipStream_t s);
 
 // Writes `bytes` zero bytes (a plain kernel, not hipMemsetAsync, so callers may
 // capture it in a graph). p must be 2-byte aligned and bytes a multiple of 2.

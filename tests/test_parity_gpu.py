@@ -360,6 +360,13 @@ SHAPES = [
     (250, 100, 5, 2, 45),
     (36, 36, 6, 6, 17),
     (8, 8, 2, 4, 3),
+    # bf16 stage-1 forward with weights held in registers: K = 256 with two
+    # 256-column slices, K = 192 with one slice, one row, and K = 256 with a
+    # column split of 32 (runs of n1 = q1o / b2 columns in stage 2's order)
+    (1024, 2048, 4, 4, 333),
+    (768, 1024, 4, 4, 17),
+    (768, 3072, 4, 4, 1),
+    (2048, 2048, 8, 8, 77),
 ]
 
 
