@@ -36,6 +36,8 @@
 // with fp32 accumulation; each result is rounded once to bf16.
 #include <stdint.h>
 
+#include <numeric>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -249,12 +251,18 @@ hipError_t launch_bd(const GemmArgs& a, int mode, hipStream_t s) {
   const int64_t rmax = (tiles + 3) / 4;
   if (ranges > rmax) ranges = rmax;
   if (ranges < 1) ranges = 1;
+  // the slices of a block share their A rows: consecutive ids go to one XCD
+  // (workgroups are dispatched round-robin over the 8 XCDs), which needs a
+  // grid that is a multiple of 8; workgroups of trailing empty ranges exit
+  const int remap = nslices > 1 ? 1 : 0;
+  if (remap) {
+    const int64_t q = 8 / std::gcd(per_range, int64_t(8));
+    ranges = (ranges + q - 1) / q * q;
+  }
   const int64_t rows_per = (tiles + ranges - 1) / ranges * BT;
-  ranges = (a.M + rows_per - 1) / rows_per;
+  if (!remap) ranges = (a.M + rows_per - 1) / rows_per;
   const int64_t grid = ranges * per_range;
   if (grid > 0x7fffffffLL || nslices > 0x7fffffffLL) return hipErrorInvalidConfiguration;
-  // the slices of a block share their A rows: one XCD for each run of ids
-  const int remap = nslices > 1 && grid % 8 == 0 ? 1 : 0;
   const auto* A = static_cast<const uint16_t*>(a.A);
   const auto* W = static_cast<const uint16_t*>(a.B);
   auto* C = static_cast<uint16_t*>(a.C);
