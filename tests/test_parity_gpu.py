@@ -367,6 +367,10 @@ SHAPES = [
     (768, 1024, 4, 4, 17),
     (768, 3072, 4, 4, 1),
     (2048, 2048, 8, 8, 77),
+    # the same kernel with a column split of 16, and with the stage-1 output
+    # in its own order (q1o = 256 not a multiple of b2 = 512: no split)
+    (1024, 1024, 4, 16, 100),
+    (768, 1024, 4, 512, 33),
 ]
 
 
