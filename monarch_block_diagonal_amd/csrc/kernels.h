@@ -118,6 +118,15 @@ hipError_t launch_bias_partials(const void* dv, float* partial, int64_t rows, in
 int bd_mode(const GemmArgs& a, bool bf16);
 hipError_t launch_bd(const GemmArgs& a, int mode, hipStream_t s);
 
+// Products with at most 16 rows and K >= 128, both operands contiguous along
+// k (skinny.hip): each workgroup takes one block and 16 output columns and
+// splits K over its eight waves, summing their tiles in a fixed order.
+// skinny_ok says whether the GemmArgs are such a product (no batch-split
+// partials, no accumulation, no column limit); bias, ReLU, the column split
+// and the output column guard are applied in its epilogue.
+bool skinny_ok(const GemmArgs& a, bool bf16);
+hipError_t launch_skinny(const GemmArgs& a, bool bf16, hipStream_t s);
+
 // Writes `bytes` zero bytes (a plain kernel, not hipMemsetAsync, so callers may
 // capture it in a graph). p must be 2-byte aligned and bytes a multiple of 2.
 hipError_t launch_zero(void* p, size_t bytes, hipStream_t s);
