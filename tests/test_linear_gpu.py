@@ -94,6 +94,11 @@ SMALL = [
     (9, 6, 12, 4, 3, 130),
     (130, 200, 136, 8, 4, 300),       # several tiles, ragged, odd block sizes
     (1000, 333, 336, 3, 3, 257),      # q1i = 334, q2o = 111
+    # at most 16 rows and K >= 128 (the skinny form): a K tail in both dtypes
+    # with rows 8-byte aligned in bf16, bias and ReLU in its epilogue; and a
+    # padded input whose blocks start off 16-byte boundaries in fp32
+    (1000, 512, 512, 2, 2, 7),        # q1i = 500, q2i = 256
+    (2500, 1024, 1024, 16, 16, 3),    # q1i = 157, the last block cut by the padding
 ]
 
 
