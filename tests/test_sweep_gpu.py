@@ -2,8 +2,10 @@
 
 Covers the three paths with shapes the hand-picked cases do not: random
 block counts and block sizes, padded inputs and truncated outputs, bias,
-ReLU and ragged batches on the generic path (small layers, and bf16 layers
-of 256-1536 features that take the large tiles); random batches on the
+ReLU and ragged batches on the generic path (small layers, bf16 layers of
+256-1536 features that take the large tiles, bf16 layers whose stage-1
+blocks take the register-resident block-diagonal form, and batches of at
+most 16 rows with long stage-1 blocks); random batches on the
 fused 32x32-block and square 128x128-block paths. The shapes come from a fixed
 seed, so every run checks the same cases; the ids name them.
 """
@@ -82,12 +84,47 @@ def _large_cases():
     return cases
 
 
+def _blockdiag_cases():
+    # bf16 layers whose stage-1 blocks have 192 or 256 inputs and a multiple
+    # of 256 outputs (the register-resident block-diagonal form, one to three
+    # column slices, with or without stage 2's column split), sometimes with
+    # a padded input (the last block cut: the tiled form instead)
+    rng = random.Random(20221206)
+    cases = []
+    for _ in range(8):
+        b1 = rng.randint(1, 4)
+        q1i, q1o = rng.choice([192, 256]), 256 * rng.randint(1, 3)
+        mid = b1 * q1o
+        b2 = rng.choice([d for d in (1, 2, 3, 4, 6, 8, 16, 64) if mid % d == 0])
+        inp = b1 * q1i - (rng.randint(1, 40) if rng.random() < 0.25 else 0)
+        cases.append((inp, rng.randint(64, 1536), mid, b1, b2, rng.randint(1, 700), "bf16",
+                      rng.random() < 0.3, rng.random() < 0.3))
+    return cases
+
+
+def _skinny_cases():
+    # at most 16 rows with stage-1 blocks of 128 or more inputs (K split over
+    # the waves of a workgroup), odd and even strides, K tails
+    rng = random.Random(20221207)
+    cases = []
+    for _ in range(8):
+        b1, b2 = rng.randint(1, 4), rng.randint(1, 4)
+        lcm = b1 * b2 // math.gcd(b1, b2)
+        mid = lcm * rng.randint(max(1, 64 // lcm), max(2, 768 // lcm))
+        cases.append((b1 * rng.randint(128, 700), rng.randint(16, 600), mid, b1, b2,
+                      rng.randint(1, 16), rng.choice(["f32", "bf16"]), rng.random() < 0.5,
+                      rng.random() < 0.5))
+    return cases
+
+
 GENERAL = _general_cases()
 SQUARE = _square_cases()
 LARGE = _large_cases()
+BLOCKDIAG = _blockdiag_cases()
+SKINNY = _skinny_cases()
 
 
-@pytest.mark.parametrize("case", GENERAL + LARGE, ids=lambda c: "in%d-out%d-mid%d-b%dx%d-B%d-%s-bias%d-relu%d" % (
+@pytest.mark.parametrize("case", GENERAL + LARGE + BLOCKDIAG + SKINNY, ids=lambda c: "in%d-out%d-mid%d-b%dx%d-B%d-%s-bias%d-relu%d" % (
     c[0], c[1], c[2], c[3], c[4], c[5], c[6], c[7], c[8]))
 def test_sweep_general(api, case):
     inp, out, mid, b1, b2, batch, dtype, with_bias, relu = case
