@@ -118,14 +118,16 @@ hipError_t launch_bias_partials(const void* dv, float* partial, int64_t rows, in
 int bd_mode(const GemmArgs& a, bool bf16);
 hipError_t launch_bd(const GemmArgs& a, int mode, hipStream_t s);
 
-// Products with at most 16 rows and K >= 128, both operands contiguous along
-// k (skinny.hip): each workgroup takes one block and 16 output columns and
-// splits K over its eight waves, summing their tiles in a fixed order.
-// skinny_ok says whether the GemmArgs are such a product (no batch-split
-// partials, no accumulation, no column limit); bias, ReLU, the column split
-// and the output column guard are applied in its epilogue.
-bool skinny_ok(const GemmArgs& a, bool bf16);
-hipError_t launch_skinny(const GemmArgs& a, bool bf16, hipStream_t s);
+// Products whose K is split over the eight waves of a workgroup, both
+// operands contiguous along k (skinny.hip), the waves' tiles summed in a
+// fixed order: skinny_mode returns 1 for at most 16 rows and K >= 128 (one
+// block and 16 output columns per workgroup), 2 for fp32 products with
+// K >= 512 and at most 512 tiles of 64 x 64 (one such tile per workgroup),
+// and 0 otherwise (also with batch-split partials, accumulation or a column
+// limit). Bias, ReLU, the column split and the output column guard are
+// applied in the epilogue.
+int skinny_mode(const GemmArgs& a, bool bf16);
+hipError_t launch_skinny(const GemmArgs& a, int mode, bool bf16, hipStream_t s);
 
 // Writes `bytes` zero bytes (a plain kernel, not hipMemsetAsync, so callers may
 // capture it in a graph). p must be 2-byte aligned and bytes a multiple of 2.

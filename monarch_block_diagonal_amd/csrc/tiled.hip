@@ -997,7 +997,7 @@ int64_t iabs(int64_t v) { return v < 0 ? -v : v; }
 
 hipError_t launch_gemm(const GemmArgs& a, bool bf16, hipStream_t s) {
   if (const int bdm = bd_mode(a, bf16)) return launch_bd(a, bdm, s);
-  if (skinny_ok(a, bf16)) return launch_skinny(a, bf16, s);
+  if (const int skm = skinny_mode(a, bf16)) return launch_skinny(a, skm, bf16, s);
   const int vec = bf16 ? 8 : 4;
   // A: K-major units when K is its faster dimension, row-major otherwise
   const int am = a.a_sk == 1 ? 1 : (a.a_si == 1 ? 2 : (iabs(a.a_sk) <= iabs(a.a_si) ? 1 : 2));

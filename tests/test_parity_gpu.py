@@ -371,6 +371,11 @@ SHAPES = [
     # in its own order (q1o = 256 not a multiple of b2 = 512: no split)
     (1024, 1024, 4, 16, 100),
     (768, 1024, 4, 512, 33),
+    # fp32 stage-1 forwards with K >= 512 and few 64 x 64 tiles (K split over
+    # the eight waves of a workgroup): K = 512, and K = 525 with a tail and
+    # rows starting off 16-byte boundaries
+    (2048, 256, 4, 4, 300),
+    (2100, 512, 4, 4, 100),
 ]
 
 
