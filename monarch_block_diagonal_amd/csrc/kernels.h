@@ -54,9 +54,11 @@ struct GemmArgs {
 // kernels' K steps).
 constexpr int kSplitK = 64;
 
-// The tiled GEMM (tiled.hip) runs every GemmArgs: operands move as 16-byte
-// pieces when they are contiguous along a tile dimension with 16-byte
-// aligned rows, element by element otherwise.
+// Runs any GemmArgs: the block-diagonal kernel (bd_mode) or the K-split
+// kernel (skinny_mode) where those take the product, otherwise the tiled
+// GEMM (tiled.hip), whose operands move as 16-byte pieces when they are
+// contiguous along a tile dimension with 16-byte aligned rows, element by
+// element otherwise.
 hipError_t launch_gemm(const GemmArgs& a, bool bf16, hipStream_t s);
 
 // dV[b, g*q2o + p] = dY[b, p*b2 + g] for p*b2 + g < out, else 0, times

@@ -49,20 +49,11 @@ __device__ __forceinline__ float sk_to_f32(T v) {
   else return bf16_to_f32(v);
 }
 
-template <typename T>
-__device__ __forceinline__ f32x4 sk_mfma(u32x4 a, u32x4 b, f32x4 c) {
-  if constexpr (std::is_same<T, float>::value) {
-#pragma unroll
-    for (int e = 0; e < 4; ++e)
-      c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[e]), __uint_as_float(b[e]), c,
-                                               0, 0, 0);
-    return c;
-  } else {
-    bf16x8 x, y;
-    __builtin_memcpy(&x, &a, sizeof(x));
-    __builtin_memcpy(&y, &b, sizeof(y));
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c, 0, 0, 0);
-  }
+__device__ __forceinline__ f32x4 sk_mfma_bf16(u32x4 a, u32x4 b, f32x4 c) {
+  bf16x8 x, y;
+  __builtin_memcpy(&x, &a, sizeof(x));
+  __builtin_memcpy(&y, &b, sizeof(y));
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(x, y, c, 0, 0, 0);
 }
 
 template <typename T, int FM, int FN>
@@ -125,7 +116,7 @@ __global__ __launch_bounds__(kSkWaves * 64) void skinny_kernel(GemmArgs p, int64
 #pragma unroll
       for (int mi = 0; mi < FM; ++mi)
 #pragma unroll
-        for (int ni = 0; ni < FN; ++ni) acc[mi][ni] = sk_mfma<T>(va[mi], vb[ni], acc[mi][ni]);
+        for (int ni = 0; ni < FN; ++ni) acc[mi][ni] = sk_mfma_bf16(va[mi], vb[ni], acc[mi][ni]);
     }
   };
   int64_t c = c0;
