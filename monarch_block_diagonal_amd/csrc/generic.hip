@@ -185,6 +185,48 @@ __global__ __launch_bounds__(256) void swap_lds_kernel(const T* __restrict__ in,
   }
 }
 
+// Rows of A x 4 two-byte elements (M = 1, C = 4, A a multiple of 8) swapped
+// to 4 x A in registers: a lane loads one 16-byte piece (positions 2k and
+// 2k+1, all four c; the lanes of a wave read 1 KB contiguous), packs it into
+// one 32-bit word per c (the two positions side by side), and a 4 x 4
+// transpose within its quad of lanes (DPP moves, bit-exact) gives lane c of
+// the quad the words of c for the quad's 8 consecutive positions: one
+// 16-byte store, and 16 quads of a wave write 256-byte runs per c. No LDS.
+// A quad's four pieces lie in one row (A/2 pieces per row, a multiple of 4)
+// and quads are in or out of range as a whole, so the transpose runs with
+// all four lanes of a quad active. Each thread takes up to 4 quads' worth
+// of pieces, 1024 threads apart, loading all of them first.
+__global__ __launch_bounds__(256) void swap_c4_kernel(const u32x4* __restrict__ in,
+                                                      u32x4* __restrict__ out, int64_t rows,
+                                                      int64_t A) {
+  constexpr int U = 4;
+  const int64_t ppr = A / 2;   // pieces per row
+  const int64_t total = rows * ppr;
+  const int u = threadIdx.x & 3;
+  const int64_t p0 = static_cast<int64_t>(blockIdx.x) * 256 * U + threadIdx.x;
+  u32x4 v[U];
+#pragma unroll
+  for (int j = 0; j < U; ++j)
+    if (p0 + 256 * j < total) v[j] = __builtin_nontemporal_load(in + p0 + 256 * j);
+#pragma unroll
+  for (int j = 0; j < U; ++j) {
+    const int64_t p = p0 + 256 * j;
+    if (p >= total) continue;
+    // words of c: (position 2k, c) in the low half, (2k + 1, c) in the high half
+    f32x4 w;
+    w[0] = __uint_as_float((v[j][0] & 0xffffu) | (v[j][2] << 16));
+    w[1] = __uint_as_float((v[j][0] >> 16) | (v[j][2] & 0xffff0000u));
+    w[2] = __uint_as_float((v[j][1] & 0xffffu) | (v[j][3] << 16));
+    w[3] = __uint_as_float((v[j][1] >> 16) | (v[j][3] & 0xffff0000u));
+    const f32x4 o = quad_transpose4(w, u);   // lane u: c = u, quad lanes' words in order
+    const int64_t row = p / ppr, q = (p - row * ppr) >> 2;
+    const u32x4 r{__float_as_uint(o[0]), __float_as_uint(o[1]), __float_as_uint(o[2]),
+                  __float_as_uint(o[3])};
+    // element offset row*4A + u*A + 8q, in 16-byte pieces
+    __builtin_nontemporal_store(r, out + row * ppr + u * (A / 8) + q);
+  }
+}
+
 // Larger arrays: 32 x 32 (a, c) tiles of one (b, m) through LDS; reads run
 // along c and writes along a.
 template <typename T>
@@ -235,6 +277,16 @@ hipError_t launch_swap(const void* in, void* out, int64_t rows, int64_t A, int64
                        bool bf16, hipStream_t s, bool accum) {
   const int acc = accum ? 1 : 0;
   if (rows <= 0 || A <= 0 || M <= 0 || C <= 0) return hipSuccess;
+  if (bf16 && !accum && M == 1 && C == 4 && A % 8 == 0 &&
+      (reinterpret_cast<uintptr_t>(in) & 15) == 0 && (reinterpret_cast<uintptr_t>(out) & 15) == 0) {
+    const int64_t quads = rows * (A / 2) / 4;   // whole quads of pieces
+    const int64_t blocks = (rows * (A / 2) + 1023) / 1024;
+    if (quads > 0 && blocks <= 0x7fffffffLL) {
+      hipLaunchKernelGGL(swap_c4_kernel, dim3(static_cast<unsigned>(blocks)), dim3(256), 0, s,
+                         static_cast<const u32x4*>(in), static_cast<u32x4*>(out), rows, A);
+      return hipGetLastError();
+    }
+  }
   const int64_t esz = bf16 ? 2 : 4, V = 16 / esz, n = A * M * C;
   constexpr int64_t kLds = 49 * 1024;
   // arrays per workgroup: about 4K elements of them (fewer, larger
