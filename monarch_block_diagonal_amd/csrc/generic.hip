@@ -194,8 +194,9 @@ __global__ __launch_bounds__(256) void swap_lds_kernel(const T* __restrict__ in,
 // 16-byte store, and 16 quads of a wave write 256-byte runs per c. No LDS.
 // A quad's four pieces lie in one row (A/2 pieces per row, a multiple of 4)
 // and quads are in or out of range as a whole, so the transpose runs with
-// all four lanes of a quad active. Each thread takes up to 4 quads' worth
-// of pieces, 1024 threads apart, loading all of them first.
+// all four lanes of a quad active. A workgroup covers 1024 consecutive
+// pieces: each thread takes up to four of them, 256 apart, loading all of
+// them first.
 __global__ __launch_bounds__(256) void swap_c4_kernel(const u32x4* __restrict__ in,
                                                       u32x4* __restrict__ out, int64_t rows,
                                                       int64_t A) {
